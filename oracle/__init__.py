@@ -1,0 +1,14 @@
+"""CPU oracle of the melded FP8 LoRA linear step (FALQON).
+
+TEST INFRASTRUCTURE ONLY: imported by tests/, by the smoke check and by the
+CPU-baseline leg of bench.py, never by the HIP library or its binding.  It
+shares no code with fp8_quantized_lora_amd/.
+"""
+from . import e4m3
+from .melded import (fp8_quantize, dequantize, melded_linear_fwd, melded_linear_bwd,
+                     adapter_step, rowwise_proxy_update, row_scores, select_rows,
+                     rank_delta, num_threads)
+
+__all__ = ["e4m3", "fp8_quantize", "dequantize", "melded_linear_fwd", "melded_linear_bwd",
+           "adapter_step", "rowwise_proxy_update", "row_scores", "select_rows",
+           "rank_delta", "num_threads"]

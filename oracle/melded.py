@@ -1,0 +1,273 @@
+"""CPU oracle of FALQON's melded FP8 LoRA linear step.
+
+TEST INFRASTRUCTURE ONLY.  Only `tests/`, the smoke check in
+`__graft_entry__.py` and the CPU-baseline leg of `bench.py` may import this
+package; the HIP library never calls it and shares no code with it.
+
+Every function is the plain definition of one call of the step, on host
+NumPy arrays, in float64 unless a rounding is part of the definition.
+Pages cited (by address and section):
+
+* [P1] FALQON summary, shd-paper.top (arXiv 2510.24061): key-points list and
+  the "key design" paragraph on the row-wise proxy update.
+* [P2] FALQON introduction, luneresearch.com: the method paragraph (melded
+  LoRA, reformulated forward/backward, row-wise proxy update).
+* [P4] FALQON OpenReview rebuttal, paperhub.cn/paper/yPXOfBoQL7: thread 2
+  replies W2 (per-tensor scaling), W7 (top-k row selection), W8 (DQ),
+  Q3/Q4 (Eq. 8/9: DQ(W~) + Delta_Q W = W); thread 3 replies Q1 (top-k) and
+  W3.1 (optimizer); thread 4 reply Q1 (gradient of A).
+
+Readings of points the pages leave open are stated where they are used.
+
+Parity pins: every function here is checked in tests/test_oracle_*.py against
+closed forms, brute force on tiny inputs, finite differences, exact rational
+arithmetic or an independent library routine.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import numpy as np
+
+from . import e4m3
+
+FLT_MAX = np.float32(np.finfo(np.float32).max)
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_CHAIN_LIB = os.path.join(_HERE, "liborchain.so")
+_lib = None
+
+
+def _chain_lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_CHAIN_LIB):
+            from . import build as _b
+            _b.build()
+        lib = ctypes.CDLL(_CHAIN_LIB)
+        lib.orc_rank_chain.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p,
+                                       ctypes.c_int64, ctypes.c_int64, ctypes.c_int64,
+                                       ctypes.c_void_p]
+        lib.orc_rank_chain.restype = None
+        lib.orc_num_threads.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def num_threads() -> int:
+    return int(_chain_lib().orc_num_threads())
+
+
+# ----------------------------------------------------------------------------
+# fp8_quantize
+# ----------------------------------------------------------------------------
+def fp8_quantize(x: np.ndarray, scale_in: Optional[float] = None
+                 ) -> Tuple[np.ndarray, np.float32, np.float32, int]:
+    """Per-tensor current-scaled quantization to E4M3 ([P4] thread 2, W2: a
+    high-precision tensor X is multiplied by a per-tensor factor s_X and the
+    product s_X * X is rounded to FP8).
+
+    The formula after "as follows" is missing from the page; reading used:
+      amax = max |x| over the finite elements (non-finite ones are counted);
+      s    = 448 / amax in float32 (IEEE division); amax == 0 gives s = 1 and
+             a quotient that overflows gives s = FLT_MAX;
+      v    = fl32(x * s)            (one float32 rounding)
+      q    = E4M3 encode of v       (nearest, ties to even, saturating)
+    When `scale_in` is given, s = scale_in and amax is still reported.
+
+    `x` is float32, or uint16 holding bfloat16 bit patterns (widened exactly).
+    Returns (codes uint8, s float32, amax float32, number of non-finite inputs).
+    """
+    x = np.asarray(x)
+    if x.dtype == np.uint16:
+        xf = (x.astype(np.uint32) << 16).view(np.float32)
+    else:
+        xf = np.ascontiguousarray(x, dtype=np.float32)
+    finite = np.isfinite(xf)
+    n_bad = int(xf.size - np.count_nonzero(finite))
+    amax = np.float32(np.max(np.abs(xf[finite]))) if np.any(finite) else np.float32(0.0)
+    if scale_in is not None:
+        s = np.float32(scale_in)
+    elif amax == 0:
+        s = np.float32(1.0)
+    else:
+        with np.errstate(over="ignore"):
+            s = np.float32(448.0) / amax
+        if not np.isfinite(s):
+            s = FLT_MAX
+    with np.errstate(over="ignore", invalid="ignore"):
+        v = (xf * s).astype(np.float32)
+    return e4m3.encode(v), np.float32(s), np.float32(amax), n_bad
+
+
+def dequantize(q: np.ndarray, s: float) -> np.ndarray:
+    """DQ(q) = dec(q) / s in float64 ([P4] thread 2, W8: DQ reconstructs the
+    high-precision approximation of a quantized tensor)."""
+    return e4m3.decode(q) / np.float64(np.float32(s))
+
+
+# ----------------------------------------------------------------------------
+# melded_linear_fwd
+# ----------------------------------------------------------------------------
+def melded_linear_fwd(xq: np.ndarray, s_x: float, wq: np.ndarray, s_w: float) -> np.ndarray:
+    """Y = DQ(X~) DQ(W~)^T as ONE FP8 product, with no separate LoRA path
+    ([P2] method paragraph: the adapter is merged into the FP8 backbone;
+    abstract: eliminates the separate LoRA computational path).
+
+    Y[t,o] = (sum_k dec(X~[t,k]) dec(W~[o,k])) / (s_x s_w), stored as float32.
+    Products of E4M3 values and their sums are exact in float64 at these sizes
+    (multiples of 2**-18 below 2**35), so the matrix product is exact and the
+    only roundings are the division and the final float32 store.  The pending
+    adapter delta B.A is not part of Y until a proxy update merges it.
+    """
+    xd = e4m3.decode(xq)
+    wd = e4m3.decode(wq)
+    acc = xd @ wd.T
+    return (acc / (np.float64(np.float32(s_x)) * np.float64(np.float32(s_w)))).astype(np.float32)
+
+
+# ----------------------------------------------------------------------------
+# melded_linear_bwd
+# ----------------------------------------------------------------------------
+def melded_linear_bwd(gq: np.ndarray, s_g: float, xq: np.ndarray, s_x: float,
+                      wq: np.ndarray, s_w: float, A: np.ndarray, B: np.ndarray,
+                      want_dx: bool = True, want_da: bool = True
+                      ) -> Tuple[Optional[np.ndarray], Optional[np.ndarray], np.ndarray]:
+    """Reformulated backward of the melded layer ([P2] method paragraph;
+    [P4] thread 4, Q1: dL/dA = B^T (dL/dO) x^T, while the X A^T factor that
+    dL/dB needs can be computed ahead).
+
+    G^ = DQ(G~) (the quantized upstream gradient), X^ = DQ(X~) (the saved
+    quantized activation: no separate quantized LoRA path is formed).
+      dX = G^ DQ(W~)            straight-through: Q is treated as identity
+      dB = G^T (X^ A^T)         [d_out x r]
+      dA = (G^ B)^T X^          [r x d_in]
+    Adapter layout: A [r x d_in], B [d_out x r], so that row i of B A is the
+    delta of backbone row i.  All sums in float64, stored as float32.
+    """
+    gd = e4m3.decode(gq)
+    xd = e4m3.decode(xq)
+    sg = np.float64(np.float32(s_g))
+    sx = np.float64(np.float32(s_x))
+    sw = np.float64(np.float32(s_w))
+    dx = None
+    if want_dx:
+        wd = e4m3.decode(wq)
+        dx = ((gd @ wd) / (sg * sw)).astype(np.float32)
+    g_hat = gd / sg
+    x_hat = xd / sx
+    A64 = np.asarray(A, dtype=np.float64)
+    B64 = np.asarray(B, dtype=np.float64)
+    U = x_hat @ A64.T                    # [T x r]
+    dB = (g_hat.T @ U).astype(np.float32)
+    dA = None
+    if want_da:
+        V = g_hat @ B64                  # [T x r]
+        dA = (V.T @ x_hat).astype(np.float32)
+    return dx, dA, dB
+
+
+# ----------------------------------------------------------------------------
+# adapter_step
+# ----------------------------------------------------------------------------
+def adapter_step(A: np.ndarray, B: np.ndarray, dA: Optional[np.ndarray], dB: np.ndarray,
+                 lr: float) -> Tuple[np.ndarray, np.ndarray]:
+    """Plain SGD on the adapter factors: p <- fl(p - fl(lr * g)) elementwise in
+    float32 (two roundings, no fused multiply-add).  dA = None keeps A frozen.
+    The pages train with 32-bit AdamW ([P4] thread 3, W3.1); the workloads
+    here ask for SGD with lr 1e-3."""
+    lr32 = np.float32(lr)
+    A2 = np.array(A, dtype=np.float32, copy=True)
+    if dA is not None:
+        A2 = (A2 - (lr32 * np.asarray(dA, np.float32)).astype(np.float32)).astype(np.float32)
+    B2 = (np.asarray(B, np.float32) - (lr32 * np.asarray(dB, np.float32)).astype(np.float32)
+          ).astype(np.float32)
+    return A2, B2
+
+
+# ----------------------------------------------------------------------------
+# rowwise_proxy_update
+# ----------------------------------------------------------------------------
+def rank_delta(B: np.ndarray, A: np.ndarray, rows: Optional[np.ndarray] = None) -> np.ndarray:
+    """u = B[rows] . A with the fixed fp32 fmaf chain of oracle/chain.c."""
+    B = np.ascontiguousarray(B, dtype=np.float32)
+    A = np.ascontiguousarray(A, dtype=np.float32)
+    d_out, r = B.shape
+    d_in = A.shape[1]
+    if rows is None:
+        n = d_out
+        rp = None
+    else:
+        rows = np.ascontiguousarray(rows, dtype=np.int64)
+        n = rows.size
+        rp = rows.ctypes.data
+    u = np.empty((n, d_in), dtype=np.float32)
+    if n and d_in:
+        _chain_lib().orc_rank_chain(B.ctypes.data, A.ctypes.data, rp, n, r, d_in,
+                                    u.ctypes.data)
+    return u
+
+
+def row_scores(wq: np.ndarray, s_w: float, A: np.ndarray, B: np.ndarray
+               ) -> Tuple[np.ndarray, np.ndarray]:
+    """Score of every backbone row: how many of the row's FP8 steps its pending
+    delta would move its largest element.
+
+      m_i   = max_j |dec(W~[i,j])|;  step_i = E4M3 spacing at m_i (2**-9 below 2**-6)
+      t_ij  = fl32(s_w * u_ij),  u = B A (fixed fmaf chain)
+      rho_i = fl32(max_j |t_ij| / step_i)     (a power-of-two scaling, exact)
+
+    Returns (rho float32 [d_out], t float32 [d_out x d_in]).
+    """
+    wq = np.asarray(wq, dtype=np.uint8)
+    u = rank_delta(B, A)
+    t = (np.float32(s_w) * u).astype(np.float32)
+    m = np.max(np.abs(e4m3.decode(wq)), axis=1) if wq.shape[1] else np.zeros(wq.shape[0])
+    inv_step = (1.0 / e4m3.step_of(m)).astype(np.float32)   # powers of two
+    tmax = np.max(np.abs(t), axis=1) if t.shape[1] else np.zeros(t.shape[0], np.float32)
+    rho = (tmax.astype(np.float32) * inv_step).astype(np.float32)
+    return rho, t
+
+
+def select_rows(rho: np.ndarray, tau: float, k_max: int) -> np.ndarray:
+    """Rows to merge: rho_i >= tau; with k_max > 0 and more candidates than
+    k_max, the k_max largest rho, equal rho going to the lower row index.
+    Returned in ascending row order ([P4] thread 2, W7 and thread 3, Q1:
+    the update is migrated into the weight through top-k row selection)."""
+    rho = np.asarray(rho, dtype=np.float32)
+    cand = np.nonzero(rho >= np.float32(tau))[0]
+    if k_max > 0 and cand.size > k_max:
+        order = sorted(cand.tolist(), key=lambda i: (-float(rho[i]), i))
+        cand = np.array(sorted(order[:k_max]), dtype=np.int64)
+    return cand.astype(np.int32)
+
+
+def rowwise_proxy_update(wq: np.ndarray, s_w: float, A: np.ndarray, B: np.ndarray,
+                         tau: float, k_max: int = 0
+                         ) -> Tuple[np.ndarray, np.ndarray, np.ndarray, np.ndarray]:
+    """Row-wise proxy update ([P1] key design: a row-wise proxy accumulates the
+    adapter updates and is merged into the quantized backbone from time to
+    time; [P2]: only substantial updates are applied, since small ones vanish
+    under low-bit rounding; [P4] thread 2, W7: the update is merged into the
+    weight by top-k row selection).
+
+    Reading used: the rows of B are the proxy (row i's pending delta is
+    B_i . A).  For every selected row i (see row_scores / select_rows):
+        W~[i,j] <- encode(fl32(dec(W~[i,j]) + t_ij))   for all j
+        B[i,:]  <- 0
+    i.e. dequantize, add and requantize in the scaled domain of the fixed
+    backbone scale s_w.  Unselected rows and their B rows are left as they are.
+
+    Returns (new codes, new B, selected rows int32 ascending, rho).
+    """
+    wq2 = np.array(wq, dtype=np.uint8, copy=True)
+    B2 = np.array(B, dtype=np.float32, copy=True)
+    rho, t = row_scores(wq, s_w, A, B)
+    sel = select_rows(rho, tau, k_max)
+    if sel.size:
+        merged = (e4m3.decode_f32(wq2[sel]) + t[sel]).astype(np.float32)
+        wq2[sel] = e4m3.encode(merged)
+        B2[sel] = 0.0
+    return wq2, B2, sel, rho

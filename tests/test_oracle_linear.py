@@ -1,0 +1,261 @@
+"""Pins of the oracle's quantize / forward / backward / SGD calls.
+
+Each check uses something the oracle does not: exact rational arithmetic
+(`fractions`), closed forms, finite differences of the loss the gradients
+belong to, or invariants of the FP8 format.  Shapes are non-square with
+distinct dimensions so that a transposed operand or a swapped index fails.
+"""
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import e4m3
+from tests.exact import round_to_f32
+
+DEC = e4m3.DECODE_F64
+
+
+def rand_codes(rng, shape, lo=0x00, hi=0x7E):
+    """Random finite codes with random signs."""
+    mag = rng.integers(lo, hi + 1, size=shape)
+    sgn = rng.integers(0, 2, size=shape) << 7
+    return (mag | sgn).astype(np.uint8)
+
+
+# ---------------------------------------------------------------- quantize --
+def test_quantize_amax_element_maps_to_448():
+    rng = np.random.default_rng(1)
+    x = rng.standard_normal((37, 53)).astype(np.float32)
+    q, s, amax, bad = oracle.fp8_quantize(x)
+    i = np.unravel_index(np.argmax(np.abs(x)), x.shape)
+    assert bad == 0
+    assert amax == np.abs(x).max()
+    assert q[i] & 0x7F == 0x7E
+    assert (q[i] >> 7) == (x[i] < 0)
+    # no scaled value exceeds 448 by more than one float32 rounding
+    v = np.abs(x.astype(np.float64) * np.float64(s))
+    assert v.max() <= 448.0 * (1 + 2.0 ** -23)
+
+
+def test_quantize_exact_on_scaled_codes():
+    """x = dec(q) * 2**-5 with max |x| = 448 * 2**-5 -> s = 2**5 exactly and the
+    codes come back unchanged (closed form)."""
+    rng = np.random.default_rng(2)
+    q0 = rand_codes(rng, (64, 48))
+    q0[3, 7] = 0x7E
+    x = (DEC[q0] * 2.0 ** -5).astype(np.float32)
+    q, s, amax, _ = oracle.fp8_quantize(x)
+    assert s == np.float32(32.0) and amax == np.float32(14.0)
+    # -0 codes stay -0
+    assert np.array_equal(q, q0)
+
+
+def test_quantize_error_bound_eq8_9():
+    """Eq. 8/9 of the rebuttal (DQ(W~) + Delta_Q W = W): the quantization error
+    of every non-saturated element is at most half an E4M3 step (in the scaled
+    domain) plus the float32 rounding of x*s."""
+    rng = np.random.default_rng(3)
+    w = (rng.standard_normal((96, 80)) * 0.02).astype(np.float32)
+    q, s, _, _ = oracle.fp8_quantize(w)
+    dq = oracle.dequantize(q, s)
+    delta = w.astype(np.float64) - dq                   # Delta_Q W
+    assert np.array_equal(dq + delta, w.astype(np.float64))
+    step = e4m3.step_of(np.abs(DEC[q]))
+    xs = np.abs(w.astype(np.float64)) * np.float64(s)
+    bound = 0.5 * step + xs * 2.0 ** -23
+    assert np.all(np.abs(delta) * np.float64(s) <= bound * (1 + 1e-12))
+
+
+def test_quantize_degenerate_cases():
+    q, s, amax, bad = oracle.fp8_quantize(np.zeros(10, np.float32))
+    assert s == 1.0 and amax == 0.0 and bad == 0 and not q.any()
+    q, s, amax, _ = oracle.fp8_quantize(np.array([-0.0, 0.0], np.float32))
+    assert list(q) == [0x80, 0x00] and s == 1.0
+    q, s, amax, bad = oracle.fp8_quantize(np.zeros(0, np.float32))
+    assert q.size == 0 and s == 1.0 and amax == 0.0
+    # tiny amax: quotient overflows -> FLT_MAX
+    q, s, amax, _ = oracle.fp8_quantize(np.array([1e-45, -1e-45], np.float32))
+    assert s == np.finfo(np.float32).max
+    # non-finite inputs are counted and left out of amax
+    x = np.array([1.0, np.nan, -2.0, np.inf, 0.5], np.float32)
+    q, s, amax, bad = oracle.fp8_quantize(x)
+    assert bad == 2 and amax == 2.0 and s == 224.0
+    assert q[2] == 0xFE and q[0] == e4m3.encode(np.array([224.0], np.float32))[0]
+
+
+def test_quantize_static_scale_and_bf16():
+    rng = np.random.default_rng(4)
+    x = rng.standard_normal(1000).astype(np.float32)
+    q, s, amax, _ = oracle.fp8_quantize(x, scale_in=16.0)
+    assert s == 16.0 and amax == np.abs(x).max()
+    assert np.array_equal(q, e4m3.encode((x * np.float32(16.0)).astype(np.float32)))
+    # bf16 bit patterns widen exactly: same codes as the float32 values they hold
+    xb = (x.view(np.uint32) >> 16).astype(np.uint16)
+    xw = (xb.astype(np.uint32) << 16).view(np.float32)
+    qa, sa, _, _ = oracle.fp8_quantize(xb)
+    qb, sb, _, _ = oracle.fp8_quantize(xw)
+    assert np.array_equal(qa, qb) and sa == sb
+
+
+# ----------------------------------------------------------------- forward --
+def test_forward_exact_rationals_tiny():
+    rng = np.random.default_rng(5)
+    T, d_in, d_out = 3, 5, 4
+    xq = rand_codes(rng, (T, d_in))
+    wq = rand_codes(rng, (d_out, d_in))
+    s_x, s_w = np.float32(3.7), np.float32(0.61)
+    y = oracle.melded_linear_fwd(xq, s_x, wq, s_w)
+    assert y.shape == (T, d_out) and y.dtype == np.float32
+    for t in range(T):
+        for o in range(d_out):
+            acc = sum(Fraction(DEC[xq[t, k]]) * Fraction(DEC[wq[o, k]]) for k in range(d_in))
+            ref = round_to_f32(acc / (Fraction(float(s_x)) * Fraction(float(s_w))))
+            assert abs(y[t, o] - ref) <= abs(ref) * 2.0 ** -23, (t, o, y[t, o], ref)
+
+
+def test_forward_scaled_identity_weight():
+    """W~ = c I (square) -> Y = dec(X~) dec(c) / (s_x s_w) elementwise."""
+    rng = np.random.default_rng(6)
+    d = 24
+    xq = rand_codes(rng, (7, d))
+    c = 0x3C  # 1.5
+    wq = np.zeros((d, d), np.uint8)
+    wq[np.arange(d), np.arange(d)] = c
+    y = oracle.melded_linear_fwd(xq, 2.0, wq, 4.0)
+    ref = (DEC[xq] * 1.5 / 8.0).astype(np.float32)
+    assert np.array_equal(y, ref)
+
+
+# ---------------------------------------------------------------- backward --
+def tiny_problem(seed, T=5, d_in=7, d_out=6, r=3):
+    rng = np.random.default_rng(seed)
+    xq = rand_codes(rng, (T, d_in), hi=0x60)
+    gq = rand_codes(rng, (T, d_out), hi=0x60)
+    wq = rand_codes(rng, (d_out, d_in), hi=0x60)
+    A = rng.standard_normal((r, d_in)).astype(np.float32)
+    B = rng.standard_normal((d_out, r)).astype(np.float32)
+    return xq, gq, wq, A, B, np.float32(1.75), np.float32(0.3), np.float32(5.5)
+
+
+def test_dx_exact_rationals_tiny():
+    xq, gq, wq, A, B, s_x, s_g, s_w = tiny_problem(7)
+    dx, _, _ = oracle.melded_linear_bwd(gq, s_g, xq, s_x, wq, s_w, A, B)
+    T, d_out = gq.shape
+    d_in = wq.shape[1]
+    assert dx.shape == (T, d_in)
+    for t in range(T):
+        for k in range(d_in):
+            acc = sum(Fraction(DEC[gq[t, o]]) * Fraction(DEC[wq[o, k]]) for o in range(d_out))
+            ref = round_to_f32(acc / (Fraction(float(s_g)) * Fraction(float(s_w))))
+            assert abs(dx[t, k] - ref) <= abs(ref) * 2.0 ** -23
+
+
+def loss(g_hat, x_hat, A, B):
+    """L(A, B) = <G^, X^ (B A)^T>, written as an explicit sum of products."""
+    T, d_out = g_hat.shape
+    d_in = x_hat.shape[1]
+    r = A.shape[0]
+    total = 0.0
+    for t in range(T):
+        for o in range(d_out):
+            for j in range(d_in):
+                w = 0.0
+                for k in range(r):
+                    w += B[o, k] * A[k, j]
+                total += g_hat[t, o] * x_hat[t, j] * w
+    return total
+
+
+def test_adapter_grads_match_finite_differences():
+    xq, gq, wq, A, B, s_x, s_g, s_w = tiny_problem(8)
+    _, dA, dB = oracle.melded_linear_bwd(gq, s_g, xq, s_x, wq, s_w, A, B)
+    g_hat = DEC[gq] / float(s_g)
+    x_hat = DEC[xq] / float(s_x)
+    A64, B64 = A.astype(np.float64), B.astype(np.float64)
+    h = 1e-3
+    fdA = np.zeros_like(A64)
+    for k in range(A.shape[0]):
+        for j in range(A.shape[1]):
+            Ap, Am = A64.copy(), A64.copy()
+            Ap[k, j] += h
+            Am[k, j] -= h
+            fdA[k, j] = (loss(g_hat, x_hat, Ap, B64) - loss(g_hat, x_hat, Am, B64)) / (2 * h)
+    fdB = np.zeros_like(B64)
+    for o in range(B.shape[0]):
+        for k in range(B.shape[1]):
+            Bp, Bm = B64.copy(), B64.copy()
+            Bp[o, k] += h
+            Bm[o, k] -= h
+            fdB[o, k] = (loss(g_hat, x_hat, A64, Bp) - loss(g_hat, x_hat, A64, Bm)) / (2 * h)
+    # L is linear in A and in B separately: central differences are exact up to rounding
+    assert np.allclose(dA, fdA, rtol=1e-5, atol=1e-6 * np.abs(fdA).max())
+    assert np.allclose(dB, fdB, rtol=1e-5, atol=1e-6 * np.abs(fdB).max())
+
+
+def test_dx_matches_finite_differences():
+    xq, gq, wq, A, B, s_x, s_g, s_w = tiny_problem(9)
+    dx, _, _ = oracle.melded_linear_bwd(gq, s_g, xq, s_x, wq, s_w, A, B)
+    g_hat = DEC[gq] / float(s_g)
+    w_hat = DEC[wq] / float(s_w)
+
+    def L(xh):  # <G^, X^ DQ(W~)^T>
+        return float(np.sum(g_hat * (xh @ w_hat.T)))
+    x_hat = DEC[xq] / float(s_x)
+    fd = np.zeros_like(x_hat)
+    h = 1e-3
+    for t in range(x_hat.shape[0]):
+        for k in range(x_hat.shape[1]):
+            p, m = x_hat.copy(), x_hat.copy()
+            p[t, k] += h
+            m[t, k] -= h
+            fd[t, k] = (L(p) - L(m)) / (2 * h)
+    assert np.allclose(dx, fd, rtol=1e-5, atol=1e-7 * np.abs(fd).max())
+
+
+def test_adapter_grads_closed_forms():
+    xq, gq, wq, A, B, s_x, s_g, s_w = tiny_problem(10)
+    # B = 0  =>  dA == 0 exactly
+    _, dA, _ = oracle.melded_linear_bwd(gq, s_g, xq, s_x, wq, s_w, A, np.zeros_like(B))
+    assert not dA.any()
+    # only row k of A nonzero  =>  dB[:, k] = G^T (X a_k), other columns 0
+    k = 1
+    A1 = np.zeros_like(A)
+    A1[k] = A[k]
+    _, _, dB = oracle.melded_linear_bwd(gq, s_g, xq, s_x, wq, s_w, A1, B)
+    g_hat = DEC[gq] / float(s_g)
+    x_hat = DEC[xq] / float(s_x)
+    col = np.array([sum(g_hat[t, o] * sum(x_hat[t, j] * float(A[k, j]) for j in range(A.shape[1]))
+                        for t in range(gq.shape[0])) for o in range(gq.shape[1])])
+    assert np.allclose(dB[:, k], col, rtol=1e-6)
+    assert not np.delete(dB, k, axis=1).any()
+
+
+def test_backward_frozen_a_and_empty_tokens():
+    xq, gq, wq, A, B, s_x, s_g, s_w = tiny_problem(11)
+    dx, dA, dB = oracle.melded_linear_bwd(gq, s_g, xq, s_x, wq, s_w, A, B, want_da=False)
+    assert dA is None and dB is not None
+    # no tokens: gradients of the adapter are exactly zero, dX is empty
+    dx, dA, dB = oracle.melded_linear_bwd(gq[:0], s_g, xq[:0], s_x, wq, s_w, A, B)
+    assert dx.shape == (0, wq.shape[1]) and not dA.any() and not dB.any()
+
+
+# --------------------------------------------------------------------- SGD --
+def test_sgd_two_roundings():
+    rng = np.random.default_rng(12)
+    A = rng.standard_normal((3, 8)).astype(np.float32)
+    B = rng.standard_normal((5, 3)).astype(np.float32)
+    dA = rng.standard_normal(A.shape).astype(np.float32)
+    dB = rng.standard_normal(B.shape).astype(np.float32)
+    lr = 1e-3
+    A2, B2 = oracle.adapter_step(A, B, dA, dB, lr)
+    lrf = Fraction(float(np.float32(lr)))
+    for p, g, p2 in ((A, dA, A2), (B, dB, B2)):
+        for idx in np.ndindex(p.shape):
+            step = round_to_f32(lrf * Fraction(float(g[idx])))
+            ref = round_to_f32(Fraction(float(p[idx])) - Fraction(step))
+            assert p2[idx] == np.float32(ref)
+    # frozen A
+    A3, _ = oracle.adapter_step(A, B, None, dB, lr)
+    assert np.array_equal(A3, A)

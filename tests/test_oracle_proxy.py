@@ -1,0 +1,171 @@
+"""Pins of the oracle's row-wise proxy update.
+
+* brute force on tiny inputs: every fused multiply-add of the rank-r chain is
+  done on exact rationals and rounded once (IEEE definition), the row's FP8
+  step is read off the code table (distance to the next code), the merge is
+  re-encoded with the brute-force nearest-value encoder;
+* invariants on larger inputs: unselected rows untouched, merged elements
+  within half a step of dec(q) + t, tau = inf selects nothing, tau = 0 selects
+  every row, B = 0 selects nothing, the selection shrinks as tau grows, equal
+  scores are broken toward the lower row index under a k_max cap.
+"""
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+from oracle import e4m3
+from tests.exact import fmaf_exact, round_to_f32
+from tests.test_oracle_e4m3 import brute_force_encode, torch_decode_all
+
+TABLE = torch_decode_all()
+
+
+def table_step(code_mag: int) -> float:
+    """FP8 step at the magnitude of code `code_mag` (0..0x7E): the distance to
+    the next code up; at the top code, the distance to the one below."""
+    if code_mag == 0x7E:
+        return TABLE[0x7E] - TABLE[0x7D]
+    return TABLE[code_mag + 1] - TABLE[code_mag]
+
+
+def brute_force_update(wq, s_w, A, B, tau, k_max):
+    d_out, d_in = wq.shape
+    r = A.shape[0]
+    t = np.zeros((d_out, d_in), np.float32)
+    rho = np.zeros(d_out, np.float32)
+    for i in range(d_out):
+        for j in range(d_in):
+            acc = 0.0
+            for k in range(r):
+                acc = fmaf_exact(float(B[i, k]), float(A[k, j]), acc)
+            t[i, j] = round_to_f32(Fraction(float(np.float32(s_w))) * Fraction(acc))
+        top = max(int(c) & 0x7F for c in wq[i])                  # largest magnitude code
+        step = table_step(top)
+        rho[i] = round_to_f32(Fraction(float(np.max(np.abs(t[i])))) / Fraction(step))
+    cand = [i for i in range(d_out) if rho[i] >= np.float32(tau)]
+    if k_max > 0 and len(cand) > k_max:
+        cand = sorted(sorted(cand, key=lambda i: (-rho[i], i))[:k_max])
+    wq2 = wq.copy()
+    B2 = B.copy()
+    for i in cand:
+        for j in range(d_in):
+            v = round_to_f32(Fraction(float(TABLE[wq[i, j]])) + Fraction(float(t[i, j])))
+            wq2[i, j] = brute_force_encode(np.array([v], np.float32))[0]
+        B2[i, :] = 0.0
+    return wq2, B2, np.array(cand, np.int32), rho
+
+
+def problem(seed, d_out=6, d_in=8, r=3, b_scale=0.004):
+    rng = np.random.default_rng(seed)
+    w = (rng.standard_normal((d_out, d_in)) * 0.02).astype(np.float32)
+    wq, s_w, _, _ = oracle.fp8_quantize(w)
+    A = (rng.standard_normal((r, d_in)) / np.sqrt(r)).astype(np.float32)
+    B = (rng.standard_normal((d_out, r)) * b_scale).astype(np.float32)
+    B *= rng.choice(np.array([0.05, 0.5, 1.0, 3.0], np.float32), size=(d_out, 1))
+    return wq, np.float32(s_w), A, B
+
+
+@pytest.mark.parametrize("seed,k_max", [(0, 0), (1, 0), (2, 2), (3, 1), (4, 0)])
+def test_proxy_update_brute_force(seed, k_max):
+    wq, s_w, A, B = problem(seed)
+    got = oracle.rowwise_proxy_update(wq, s_w, A, B, tau=0.5, k_max=k_max)
+    ref = brute_force_update(wq, s_w, A, B, 0.5, k_max)
+    assert np.array_equal(got[2], ref[2]), (got[2], ref[2])
+    assert np.array_equal(got[3], ref[3])
+    assert np.array_equal(got[0], ref[0])
+    assert np.array_equal(got[1].view(np.uint32), ref[1].view(np.uint32))
+    if seed == 0:
+        assert 0 < got[2].size < wq.shape[0], "fixture should select some rows, not all"
+
+
+def test_rank_chain_against_exact_fmaf():
+    rng = np.random.default_rng(21)
+    B = rng.standard_normal((4, 9)).astype(np.float32)
+    A = rng.standard_normal((9, 5)).astype(np.float32)
+    u = oracle.rank_delta(B, A)
+    for i in range(4):
+        for j in range(5):
+            acc = 0.0
+            for k in range(9):
+                acc = fmaf_exact(float(B[i, k]), float(A[k, j]), acc)
+            assert u[i, j] == np.float32(acc)
+    # a subset of rows gives the same rows
+    assert np.array_equal(oracle.rank_delta(B, A, rows=np.array([3, 1])), u[[3, 1]])
+
+
+def bigger(seed=30):
+    return problem(seed, d_out=64, d_in=96, r=8)
+
+
+def test_invariants_unselected_untouched_and_half_step():
+    wq, s_w, A, B = bigger()
+    wq2, B2, sel, rho = oracle.rowwise_proxy_update(wq, s_w, A, B, 0.5)
+    assert 0 < sel.size < wq.shape[0]
+    assert np.all(np.diff(sel) > 0)
+    uns = np.setdiff1d(np.arange(wq.shape[0]), sel)
+    assert np.array_equal(wq2[uns], wq[uns])
+    assert np.array_equal(B2[uns].view(np.uint32), B[uns].view(np.uint32))
+    assert not B2[sel].any()
+    # merged elements: within half an FP8 step of dec(q) + t, or saturated
+    _, t = oracle.row_scores(wq, s_w, A, B)
+    target = e4m3.DECODE_F64[wq[sel]] + t[sel].astype(np.float64)
+    got = e4m3.DECODE_F64[wq2[sel]]
+    sat = np.abs(target) >= 448.0
+    assert np.all(np.abs(got[sat]) == 448.0) and np.all(np.sign(got[sat]) == np.sign(target[sat]))
+    ok = ~sat
+    assert ok.sum() > 0.9 * ok.size
+    tol = 0.5 * e4m3.step_of(np.abs(got)) + np.abs(target) * 2.0 ** -23
+    assert np.all(np.abs(got - target)[ok] <= tol[ok])
+    # the effective weight DQ(W~) + B A is preserved up to that rounding
+    weff0 = e4m3.DECODE_F64[wq] / s_w + B.astype(np.float64) @ A.astype(np.float64)
+    weff1 = e4m3.DECODE_F64[wq2] / s_w + B2.astype(np.float64) @ A.astype(np.float64)
+    err = np.abs(weff1 - weff0) * s_w
+    assert np.all(err[uns] == 0)
+    assert np.all(err[sel][ok] <= 0.5 * e4m3.step_of(np.abs(got))[ok] + 1e-5)
+
+
+def test_selection_limits_and_monotonicity():
+    wq, s_w, A, B = bigger(31)
+    _, _, none, _ = oracle.rowwise_proxy_update(wq, s_w, A, B, np.inf)
+    assert none.size == 0
+    _, _, every, _ = oracle.rowwise_proxy_update(wq, s_w, A, B, 0.0)
+    assert np.array_equal(every, np.arange(wq.shape[0]))
+    wq2, B2, sel, rho = oracle.rowwise_proxy_update(wq, s_w, A, np.zeros_like(B), 0.5)
+    assert sel.size == 0 and not rho.any() and np.array_equal(wq2, wq)
+    prev = None
+    for tau in [0.0, 0.1, 0.25, 0.5, 1.0, 2.0, 8.0]:
+        s = set(oracle.rowwise_proxy_update(wq, s_w, A, B, tau)[2].tolist())
+        if prev is not None:
+            assert s <= prev
+        prev = s
+
+
+def test_k_max_tie_break_prefers_lower_row():
+    wq, s_w, A, B = bigger(32)
+    # rows 5, 9, 40 identical (codes and proxy) -> identical scores
+    for i in (9, 40):
+        wq[i] = wq[5]
+        B[i] = B[5]
+    B[5] *= np.float32(40.0)
+    B[9] = B[5]
+    B[40] = B[5]
+    rho, _ = oracle.row_scores(wq, s_w, A, B)
+    assert rho[5] == rho[9] == rho[40] and rho[5] == rho.max()
+    _, _, sel, _ = oracle.rowwise_proxy_update(wq, s_w, A, B, 0.0, k_max=2)
+    assert list(sel) == [5, 9]
+    _, _, sel, _ = oracle.rowwise_proxy_update(wq, s_w, A, B, 0.0, k_max=1)
+    assert list(sel) == [5]
+
+
+def test_saturating_merge_and_zero_rank():
+    wq, s_w, A, B = problem(33, d_out=4, d_in=8, r=2)
+    B[0] = 1e6                                     # pushes row 0 past 448
+    wq2, _, sel, _ = oracle.rowwise_proxy_update(wq, s_w, A, B, 0.5)
+    assert 0 in sel
+    assert np.all((wq2[0] & 0x7F) <= 0x7E)
+    # r = 0: no delta; tau = 0 merges every row, codes change only -0 -> +0
+    wq3, _, sel, rho = oracle.rowwise_proxy_update(wq, s_w, A[:0], B[:, :0], 0.0)
+    assert sel.size == 4 and not rho.any()
+    assert np.array_equal(wq3, np.where(wq == 0x80, 0, wq))
