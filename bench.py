@@ -1,0 +1,207 @@
+"""Benchmark of the melded FP8 LoRA linear training step on one MI355X.
+
+Workload (the 7B attention projection): W 4096 x 4096 in E4M3, 4096 tokens
+(batch 4 x sequence 1024) of N(0,1) activations with 1% outlier channels
+scaled x20, dY ~ N(0, 1e-3), rank 64, SGD lr 1e-3, row-wise proxy update
+every step.  One step = fp8_quantize(X) + melded_linear_fwd +
+fp8_quantize(dY) + melded_linear_bwd (dX, dA, dB) + adapter_step +
+rowwise_proxy_update, all on one HIP stream, inputs resident in HBM.
+
+Prints ONE JSON line.  `value` is whole-step TFLOP/s over the algorithmic
+flops of a step (forward and dX FP8 GEMMs, the four rank-r adapter
+contractions and the rank-r row delta); tokens/s is reported beside it.
+`roofline` describes the dominant kernel (the forward FP8 GEMM), timed with
+HIP events on the stream it runs on.  `cpu_baseline` times the CPU oracle on
+a token sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "melded FP8 LoRA linear fwd+bwd TFLOP/s and tokens/s; % FP8 MFMA / HBM peak"
+FP8_PEAK_TFLOPS = 5000.0      # MI355X dense FP8 MFMA
+HBM_PEAK_GBS = 8000.0         # MI355X HBM3E
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--batches", type=int, default=4, help="distinct (X, dY) batches cycled")
+    ap.add_argument("--cpu-tokens", type=int, default=2048,
+                    help="token sample for the CPU-oracle baseline (0 = skip)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(the per-GPU shard of the step is what one GPU runs); use --gpus 1",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import fp8_quantized_lora_amd as fq
+    import workloads as wl
+
+    fq.load()
+    torch.cuda.set_device(0)
+    cfg = wl.WORKLOADS[2]
+    spec = cfg.linears[0]
+    T, d_in, d_out, r = spec.tokens, spec.d_in, spec.d_out, spec.rank
+
+    d0 = wl.make_linear(2, 0, spec, step=0)
+    m = fq.MeldedLinear(d_out, d_in, r, T)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    m.init_state(t(d0["W"]), t(d0["A"]), t(d0["B"]))
+    batches = []
+    for b in range(max(1, args.batches)):
+        d = d0 if b == 0 else wl.step_activations(2, 0, spec, b)
+        batches.append((t(d["X"]), t(d["dY"])))
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+    names = ["quantize_x", "fwd_gemm", "quantize_dy", "bwd", "adapter_step", "proxy_update"]
+
+    def one_step(i, ev=None):
+        X, dY = batches[i % len(batches)]
+        marks = []
+
+        def mark():
+            if ev is not None:
+                e = torch.cuda.Event(enable_timing=True)
+                e.record(stream)
+                marks.append(e)
+        mark()
+        fq.fp8_quantize(X, m.xq, m.s_x, ws=m.ws_q, stream=stream)
+        mark()
+        fq.melded_linear_fwd(m.xq, m.s_x, m.wq, m.s_w, m.y, stream=stream)
+        mark()
+        fq.fp8_quantize(dY, m.gq, m.s_g, ws=m.ws_q, stream=stream)
+        mark()
+        fq.melded_linear_bwd(m.gq, m.s_g, m.xq, m.s_x, m.wq, m.s_w, m.A, m.B, m.dx, m.dA, m.dB,
+                             ws=m.ws_bwd, stream=stream)
+        mark()
+        fq.adapter_step(m.A, m.B, m.dA, m.dB, spec.lr, stream=stream)
+        mark()
+        fq.rowwise_proxy_update(m.wq, m.s_w, m.A, m.B, spec.tau, spec.k_max, m.sel, m.n_sel,
+                                rho=m.rho, ws=m.ws_px, stream=stream)
+        mark()
+        if ev is not None:
+            ev.append(marks)
+
+    for i in range(args.warmup):
+        one_step(i)
+    torch.cuda.synchronize()
+
+    # timed region: K whole steps, with an event between calls
+    evs = []
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    sel_counts = []
+    for i in range(args.steps):
+        one_step(args.warmup + i, evs)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(stop)
+    ms_per_step = total_ms / args.steps
+    per_call_us = {n: 0.0 for n in names}
+    for marks in evs:
+        for j, n in enumerate(names):
+            per_call_us[n] += marks[j].elapsed_time(marks[j + 1]) * 1e3 / len(evs)
+    n_sel = int(m.n_sel.cpu()[0])
+
+    flops = wl.step_flops(T, d_in, d_out, r)
+    tflops = flops / (ms_per_step * 1e-3) / 1e12
+    tokens_per_s = T / (ms_per_step * 1e-3)
+    gemm_flops = 2 * T * d_in * d_out
+    gemm_us = per_call_us["fwd_gemm"]
+    gemm_tflops = gemm_flops / (gemm_us * 1e-6) / 1e12
+    quant_bytes = T * d_in * 5 + 4
+    out = {
+        "metric": METRIC,
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8e4m3",
+        "data": "synthetic",
+        "config": {"workload": "7B attention projection: W 4096x4096 E4M3, 4096 tokens "
+                               "(4 x 1024), 1% outlier channels x20, rank 64, SGD lr 1e-3, "
+                               "proxy update every step",
+                   "tokens": T, "d_in": d_in, "d_out": d_out, "rank": r,
+                   "parallelism": "single GPU"},
+        "tokens_per_s": round(tokens_per_s, 1),
+        "roofline": {"kernel": "melded_linear_fwd FP8 GEMM (4096 x 4096 x 4096)",
+                     "bound": "mfma", "achieved": round(gemm_tflops, 1),
+                     "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(gemm_tflops / FP8_PEAK_TFLOPS, 4), "traffic": None},
+        "per_call_us": {k: round(v, 2) for k, v in per_call_us.items()},
+        "quantize_x_GBps": round(quant_bytes / (per_call_us["quantize_x"] * 1e-6) / 1e9, 1),
+        "selected_rows_last_step": n_sel,
+    }
+
+    if not args.no_cpu_baseline and args.cpu_tokens > 0:
+        out["cpu_baseline"] = cpu_baseline(spec, d0, args.cpu_tokens)
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(spec, d0, Ts):
+    """The CPU oracle, as it is, on a token sample of the same workload:
+    quantize X and dY, forward, backward (dX, dA, dB), SGD, and the proxy
+    update over the full 4096 x 4096 backbone."""
+    import numpy as np
+
+    import oracle
+    import workloads as wl
+
+    X = d0["X"][:Ts]
+    dY = d0["dY"][:Ts]
+    t0 = time.perf_counter()
+    wq, s_w, _, _ = oracle.fp8_quantize(d0["W"])
+    t1 = time.perf_counter()
+    xq, s_x, _, _ = oracle.fp8_quantize(X)
+    oracle.melded_linear_fwd(xq, s_x, wq, s_w)
+    gq, s_g, _, _ = oracle.fp8_quantize(dY)
+    _, dA, dB = oracle.melded_linear_bwd(gq, s_g, xq, s_x, wq, s_w, d0["A"], d0["B"])
+    A, B = oracle.adapter_step(d0["A"], d0["B"], dA, dB, spec.lr)
+    oracle.rowwise_proxy_update(wq, s_w, A, B, spec.tau, spec.k_max)
+    t2 = time.perf_counter()
+    step_s = t2 - t1
+    flops = wl.step_flops(Ts, spec.d_in, spec.d_out, spec.rank)
+    try:
+        import threadpoolctl
+        blas = threadpoolctl.threadpool_info()
+        blas_threads = max([b.get("num_threads", 1) for b in blas] or [1])
+    except Exception:
+        blas_threads = os.cpu_count()
+    return {"value": round(flops / step_s / 1e12, 5), "unit": "TFLOP/s", "cores": int(max(
+        blas_threads, oracle.num_threads())), "kind": "oracle",
+        "tokens_per_s": round(Ts / step_s, 1),
+        "sample": f"one step on the first {Ts} of 4096 tokens (full 4096 x 4096 weight, r=64, "
+                  f"full proxy update), {step_s:.1f} s; the initial weight quantization "
+                  f"({t1 - t0:.1f} s) is not part of the step"}
+
+
+if __name__ == "__main__":
+    main()

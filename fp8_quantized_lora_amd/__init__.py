@@ -1,0 +1,199 @@
+"""Python binding of libfalqon.so, the gfx950 HIP library of FALQON's melded
+FP8 LoRA linear step.
+
+Argument marshalling only: every function takes device tensors, checks
+dtype/shape/contiguity, passes their device pointers and sizes to the C
+function of the same name (include/falqon.h) and raises FalqError on a
+non-zero status.  All computation runs in the library's HIP kernels on the
+stream given (default: torch's current stream).  There is no fallback: if
+the library is missing, load() raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+__all__ = ["load", "FalqError", "fp8_quantize", "fp8_quantize_workspace_bytes",
+           "melded_linear_fwd", "melded_linear_bwd", "melded_linear_bwd_workspace_bytes",
+           "adapter_step", "rowwise_proxy_update", "rowwise_proxy_update_workspace_bytes",
+           "version", "LIB_PATH"]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfalqon.so")
+_lib = None
+
+_c_p = ctypes.c_void_p
+_i64 = ctypes.c_int64
+_sz = ctypes.c_size_t
+_f32 = ctypes.c_float
+_i32 = ctypes.c_int
+
+_SIGS = {
+    "falq_status_string": (ctypes.c_char_p, [_i32]),
+    "falq_version": (ctypes.c_char_p, []),
+    "fp8_quantize_workspace_bytes": (_sz, [_i64]),
+    "fp8_quantize": (_i32, [_c_p, _i32, _i64, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _sz, _c_p]),
+    "melded_linear_fwd": (_i32, [_c_p, _c_p, _c_p, _c_p, _i64, _i64, _i64, _c_p, _c_p]),
+    "melded_linear_bwd_workspace_bytes": (_sz, [_i64, _i64, _i64, _i64]),
+    "melded_linear_bwd": (_i32, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _i64, _i64,
+                                 _i64, _i64, _c_p, _c_p, _c_p, _c_p, _sz, _c_p]),
+    "adapter_step": (_i32, [_c_p, _c_p, _c_p, _c_p, _i64, _i64, _i64, _f32, _c_p]),
+    "rowwise_proxy_update_workspace_bytes": (_sz, [_i64, _i64, _i64]),
+    "rowwise_proxy_update": (_i32, [_c_p, _c_p, _c_p, _c_p, _i64, _i64, _i64, _f32, _i64, _c_p,
+                                    _c_p, _c_p, _c_p, _sz, _c_p]),
+}
+
+
+class FalqError(RuntimeError):
+    pass
+
+
+def load(path: Optional[str] = None):
+    """Load libfalqon.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise FalqError(f"{p} not found: build it with `python -c 'import __graft_entry__ as g; "
+                        f"g.build()'` or `python fp8_quantized_lora_amd/build.py`")
+    lib = ctypes.CDLL(p)
+    for name, (res, args) in _SIGS.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def version() -> str:
+    return load().falq_version().decode()
+
+
+def _check(status: int, what: str):
+    if status != 0:
+        msg = load().falq_status_string(status).decode()
+        raise FalqError(f"{what}: {msg}")
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise FalqError("tensor arguments must live on the GPU")
+    if not t.is_contiguous():
+        raise FalqError("tensor arguments must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _req(t: torch.Tensor, dtype, shape, name):
+    if t.dtype != dtype:
+        raise FalqError(f"{name}: expected dtype {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise FalqError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+# ---------------------------------------------------------------------------
+def fp8_quantize_workspace_bytes(n: int) -> int:
+    return int(load().fp8_quantize_workspace_bytes(n))
+
+
+def fp8_quantize(x: torch.Tensor, q: torch.Tensor, scale: torch.Tensor,
+                 scale_in: Optional[torch.Tensor] = None, amax: Optional[torch.Tensor] = None,
+                 nonfinite: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None,
+                 stream=None) -> None:
+    lib = load()
+    if x.dtype == torch.float32:
+        dt = 0
+    elif x.dtype == torch.bfloat16:
+        dt = 1
+    else:
+        raise FalqError("fp8_quantize: x must be float32 or bfloat16")
+    n = x.numel()
+    _req(q, torch.uint8, x.shape, "q")
+    wsb = fp8_quantize_workspace_bytes(n)
+    if ws is None:
+        ws = torch.empty(wsb, dtype=torch.uint8, device=x.device)
+    _check(lib.fp8_quantize(_ptr(x), dt, n, _ptr(scale_in), _ptr(q), _ptr(scale), _ptr(amax),
+                            _ptr(nonfinite), _ptr(ws), ws.numel(), _stream(stream)),
+           "fp8_quantize")
+
+
+def melded_linear_fwd(xq: torch.Tensor, s_x: torch.Tensor, wq: torch.Tensor, s_w: torch.Tensor,
+                      y: torch.Tensor, stream=None) -> None:
+    T, d_in = xq.shape
+    d_out = wq.shape[0]
+    _req(wq, torch.uint8, (d_out, d_in), "wq")
+    _req(y, torch.float32, (T, d_out), "y")
+    _check(load().melded_linear_fwd(_ptr(xq), _ptr(s_x), _ptr(wq), _ptr(s_w), T, d_in, d_out,
+                                    _ptr(y), _stream(stream)), "melded_linear_fwd")
+
+
+def melded_linear_bwd_workspace_bytes(T: int, d_in: int, d_out: int, r: int) -> int:
+    return int(load().melded_linear_bwd_workspace_bytes(T, d_in, d_out, r))
+
+
+def melded_linear_bwd(gq, s_g, xq, s_x, wq, s_w, A, B, dx, dA, dB, ws=None, stream=None) -> None:
+    T, d_out = gq.shape
+    d_in = xq.shape[1]
+    r = A.shape[0]
+    _req(xq, torch.uint8, (T, d_in), "xq")
+    _req(wq, torch.uint8, (d_out, d_in), "wq")
+    _req(A, torch.float32, (r, d_in), "A")
+    _req(B, torch.float32, (d_out, r), "B")
+    _req(dB, torch.float32, (d_out, r), "dB")
+    if dx is not None:
+        _req(dx, torch.float32, (T, d_in), "dx")
+    if dA is not None:
+        _req(dA, torch.float32, (r, d_in), "dA")
+    wsb = melded_linear_bwd_workspace_bytes(T, d_in, d_out, r)
+    if ws is None:
+        ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=gq.device)
+    _check(load().melded_linear_bwd(_ptr(gq), _ptr(s_g), _ptr(xq), _ptr(s_x), _ptr(wq), _ptr(s_w),
+                                    _ptr(A), _ptr(B), T, d_in, d_out, r, _ptr(dx), _ptr(dA),
+                                    _ptr(dB), _ptr(ws), ws.numel(), _stream(stream)),
+           "melded_linear_bwd")
+
+
+def adapter_step(A, B, dA, dB, lr: float, stream=None) -> None:
+    r, d_in = A.shape
+    d_out = B.shape[0]
+    _req(B, torch.float32, (d_out, r), "B")
+    _req(dB, torch.float32, (d_out, r), "dB")
+    if dA is not None:
+        _req(dA, torch.float32, (r, d_in), "dA")
+    _check(load().adapter_step(_ptr(A), _ptr(B), _ptr(dA), _ptr(dB), r, d_in, d_out, lr,
+                               _stream(stream)), "adapter_step")
+
+
+def rowwise_proxy_update_workspace_bytes(d_in: int, d_out: int, r: int) -> int:
+    return int(load().rowwise_proxy_update_workspace_bytes(d_in, d_out, r))
+
+
+def rowwise_proxy_update(wq, s_w, A, B, tau: float, k_max: int, sel_idx, n_sel, rho=None, ws=None,
+                         stream=None) -> None:
+    d_out, d_in = wq.shape
+    r = A.shape[0]
+    _req(A, torch.float32, (r, d_in), "A")
+    _req(B, torch.float32, (d_out, r), "B")
+    _req(sel_idx, torch.int32, (d_out,), "sel_idx")
+    if rho is not None:
+        _req(rho, torch.float32, (d_out,), "rho")
+    wsb = rowwise_proxy_update_workspace_bytes(d_in, d_out, r)
+    if ws is None:
+        ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=wq.device)
+    _check(load().rowwise_proxy_update(_ptr(wq), _ptr(s_w), _ptr(A), _ptr(B), d_in, d_out, r, tau,
+                                       k_max, _ptr(sel_idx), _ptr(n_sel), _ptr(rho), _ptr(ws),
+                                       ws.numel(), _stream(stream)), "rowwise_proxy_update")
+
+
+from .step import MeldedLinear  # noqa: E402  (buffers + the step's call sequence)
+__all__.append("MeldedLinear")

@@ -1,0 +1,440 @@
+// Rank-r adapter gradients of the melded layer on gfx950 matrix cores.
+//
+// With X^ = dec(X~)/s_x and G^ = dec(G~)/s_g (the FP8 tensors the forward and
+// the dX product already hold: no second quantized LoRA path), the FALQON
+// rebuttal (thread 4, reply Q1) gives dL/dA = B^T (dL/dO) x^T, and dL/dB uses
+// the factor x A^T.  In row-major form:
+//     U  = X^ A^T   [T x r]        V  = G^ B   [T x r]
+//     dB = G^^T U   [d_out x r]    dA = V^T X^ [r x d_in]
+//
+// All four are "skinny" contractions: one operand is FP8 codes (T x d), the
+// other a rank-r float operand.  One kernel does all of them:
+//     P[s][m][n] = sum_{k in split s} dec(Q)[m][k] * H[n][k]
+// where Q is read either row-wise (Q[m][k] = codes[m*ld + k]: U, V) or
+// column-wise (Q[m][k] = codes[k*ld + m]: dB, dA, contracting over tokens),
+// on v_mfma_f32_32x32x16_bf16.  Precision:
+//  * an E4M3 code decodes exactly to bf16 (3 mantissa bits, fp32 exponent
+//    range), so the FP8 operand is exact;
+//  * the float operand H is split as H = hi + lo with hi = bf16(H),
+//    lo = bf16(H - hi); two MFMAs per block, fp32 accumulation.  The relative
+//    error per product is about 2^-17, far inside the 1e-3 parity bound;
+//  * U and V are stored as hi/lo bf16 pairs as well (transposed to [r x T],
+//    tokens padded with zeros to a multiple of 64) for the second pass.
+// Work is split over K (d for U/V, T for dB/dA) so that every shape launches
+// a few hundred workgroups; the partial sums are added in a fixed order by
+// a reduction kernel (no atomics: the result is the same on every run).
+// U and V are T x r: a few MiB, consumed at once, cache resident.
+#include "common.hpp"
+#include "kernels.hpp"
+
+#include <algorithm>
+
+namespace falq {
+namespace {
+
+constexpr int TM = 128, TN = 64, TK = 64;      // skinny tile
+constexpr int ROWB = TK * 2 + 16;              // LDS row bytes (bf16 + pad)
+constexpr int kThreads = 256;
+
+__device__ __forceinline__ uint16_t bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+// two floats that hold E4M3 values (<= 4 significant bits) -> packed bf16x2 (exact)
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
+}
+
+// 4 E4M3 codes in a dword -> 4 bf16 in two dwords (element order preserved)
+__device__ __forceinline__ uint2 dec4_bf16(uint32_t w) {
+  float2 a = dec2(w, false), b = dec2(w, true);
+  return make_uint2(pack_bf16x2(a.x, a.y), pack_bf16x2(b.x, b.y));
+}
+
+struct Prob {
+  const uint8_t* Q;      // FP8 codes
+  int64_t ldq;           // row stride of Q in bytes
+  const uint16_t* Hhi;   // [N x ldh] bf16 bits, K contiguous
+  const uint16_t* Hlo;
+  int64_t ldh;
+  float* P;              // [S][M][N] partial sums
+  int M, N, K;           // contraction over K
+  int kchunk;            // K range of split s: [s*kchunk, min(K, (s+1)*kchunk))
+  int tilesM, tilesN;
+};
+
+template <bool TRANS>
+__global__ __launch_bounds__(kThreads) void skinny_kernel(Prob p0, Prob p1) {
+  const Prob p = blockIdx.z == 0 ? p0 : p1;
+  const int tile = blockIdx.x;
+  if (tile >= p.tilesM * p.tilesN) return;
+  const int m0 = (tile % p.tilesM) * TM;
+  const int n0 = (tile / p.tilesM) * TN;
+  const int s = blockIdx.y;
+  const int kb = s * p.kchunk;
+  const int ke = min(p.K, kb + p.kchunk);
+
+  __shared__ __attribute__((aligned(16))) uint8_t sQ[2][TM * ROWB];
+  __shared__ __attribute__((aligned(16))) uint8_t sH[2][2][TN * ROWB];
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  v16f acc[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[j][v] = 0.0f;
+
+  // staging registers
+  uint4 rq[2];               // TRANS=false: 2 x 16 codes;  TRANS=true: 8 dwords
+  uint4 rh[2][2];            // [hi/lo][chunk]
+
+  auto gload = [&](int k0) {
+    if (!TRANS) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int c = tid + i * kThreads;
+        const int row = c >> 2, col = (c & 3) * 16;
+        const int gm = m0 + row, gk = k0 + col;
+        const bool ok = gm < p.M && gk < ke;
+        uint4 v = *reinterpret_cast<const uint4*>(p.Q + (int64_t)min(gm, p.M - 1) * p.ldq +
+                                                  min(gk, p.K - 16));
+        rq[i] = ok ? v : make_uint4(0, 0, 0, 0);
+      }
+    } else {
+      const int mo = (tid & 31) * 4, to = (tid >> 5) * 8;
+      const int gm = m0 + mo;
+      uint32_t d[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int gk = k0 + to + i;
+        const bool ok = gm < p.M && gk < ke;
+        uint32_t v = *reinterpret_cast<const uint32_t*>(p.Q + (int64_t)min(gk, p.K - 1) * p.ldq +
+                                                        min(gm, p.M - 4));
+        d[i] = ok ? v : 0u;
+      }
+      rq[0] = make_uint4(d[0], d[1], d[2], d[3]);
+      rq[1] = make_uint4(d[4], d[5], d[6], d[7]);
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int c = tid + i * kThreads;
+      const int row = c >> 3, col = (c & 7) * 8;   // bf16 elements
+      const int gn = n0 + row, gk = k0 + col;
+      const bool ok = gn < p.N && gk < ke;
+      const int64_t off = ok ? (int64_t)gn * p.ldh + gk : 0;   // H rows may be padded past K
+      uint4 h = *reinterpret_cast<const uint4*>(p.Hhi + off);
+      uint4 l = *reinterpret_cast<const uint4*>(p.Hlo + off);
+      rh[0][i] = ok ? h : make_uint4(0, 0, 0, 0);
+      rh[1][i] = ok ? l : make_uint4(0, 0, 0, 0);
+    }
+  };
+
+  auto sstore = [&](int buf) {
+    if (!TRANS) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int c = tid + i * kThreads;
+        const int row = c >> 2, col = (c & 3) * 16;
+        uint8_t* dst = sQ[buf] + row * ROWB + col * 2;
+        uint2 a = dec4_bf16(rq[i].x), b = dec4_bf16(rq[i].y);
+        uint2 cc = dec4_bf16(rq[i].z), dd = dec4_bf16(rq[i].w);
+        *reinterpret_cast<uint4*>(dst) = make_uint4(a.x, a.y, b.x, b.y);
+        *reinterpret_cast<uint4*>(dst + 16) = make_uint4(cc.x, cc.y, dd.x, dd.y);
+      }
+    } else {
+      const int mo = (tid & 31) * 4, to = (tid >> 5) * 8;
+      const uint32_t d[8] = {rq[0].x, rq[0].y, rq[0].z, rq[0].w, rq[1].x, rq[1].y, rq[1].z, rq[1].w};
+      uint32_t out[4][4];   // [column][dword of 2 bf16 along k]
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {          // token pair (2i, 2i+1)
+        // bytes: [col0 t, col0 t+1, col2 t, col2 t+1] and the same for cols 1, 3
+        const uint32_t w02 = __builtin_amdgcn_perm(d[2 * i + 1], d[2 * i], 0x06020400u);
+        const uint32_t w13 = __builtin_amdgcn_perm(d[2 * i + 1], d[2 * i], 0x07030501u);
+        float2 c0 = dec2(w02, false), c2 = dec2(w02, true);
+        float2 c1 = dec2(w13, false), c3 = dec2(w13, true);
+        out[0][i] = pack_bf16x2(c0.x, c0.y);
+        out[1][i] = pack_bf16x2(c1.x, c1.y);
+        out[2][i] = pack_bf16x2(c2.x, c2.y);
+        out[3][i] = pack_bf16x2(c3.x, c3.y);
+      }
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        *reinterpret_cast<uint4*>(sQ[buf] + (mo + c) * ROWB + to * 2) =
+            make_uint4(out[c][0], out[c][1], out[c][2], out[c][3]);
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int c = tid + i * kThreads;
+      const int row = c >> 3, col = (c & 7) * 8;
+      *reinterpret_cast<uint4*>(sH[buf][0] + row * ROWB + col * 2) = rh[0][i];
+      *reinterpret_cast<uint4*>(sH[buf][1] + row * ROWB + col * 2) = rh[1][i];
+    }
+  };
+
+  const int nk = ke > kb ? (ke - kb + TK - 1) / TK : 0;
+  if (nk > 0) {
+    gload(kb);
+    sstore(0);
+  }
+  __syncthreads();
+  const int qoff = (w * 32 + (lane & 31)) * ROWB + (lane >> 5) * 16;
+  const int hoff = (lane & 31) * ROWB + (lane >> 5) * 16;
+  for (int it = 0; it < nk; ++it) {
+    const int cur = it & 1;
+    if (it + 1 < nk) gload(kb + (it + 1) * TK);
+#pragma unroll
+    for (int kk = 0; kk < TK; kk += 16) {
+      const v8bf a = __builtin_bit_cast(v8bf, *reinterpret_cast<const uint4*>(sQ[cur] + qoff + kk * 2));
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const v8bf bh = __builtin_bit_cast(
+            v8bf, *reinterpret_cast<const uint4*>(sH[cur][0] + hoff + j * 32 * ROWB + kk * 2));
+        const v8bf bl = __builtin_bit_cast(
+            v8bf, *reinterpret_cast<const uint4*>(sH[cur][1] + hoff + j * 32 * ROWB + kk * 2));
+        acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bh, acc[j], 0, 0, 0);
+        acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bl, acc[j], 0, 0, 0);
+      }
+    }
+    if (it + 1 < nk) sstore(cur ^ 1);
+    __syncthreads();
+  }
+
+  float* P = p.P + (int64_t)s * p.M * p.N;
+  const int rbase = m0 + w * 32 + 4 * (lane >> 5);
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int n = n0 + j * 32 + (lane & 31);
+    if (n >= p.N) continue;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int m = rbase + 8 * (v >> 2) + (v & 3);
+      if (m < p.M) P[(int64_t)m * p.N + n] = acc[j][v];
+    }
+  }
+}
+
+// fp32 [rows x cols] -> bf16 hi/lo, optionally transposed ([cols x ld_out]).
+__global__ __launch_bounds__(256) void split_bf16_kernel(const float* __restrict__ src, int rows,
+                                                         int cols, bool transpose, int64_t ld_out,
+                                                         uint16_t* __restrict__ hi,
+                                                         uint16_t* __restrict__ lo) {
+  __shared__ float t[32][33];
+  const int r0 = blockIdx.y * 32, c0 = blockIdx.x * 32;
+  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;   // 32 x 8
+  if (!transpose) {
+    for (int rr = ty; rr < 32; rr += 8) {
+      const int r = r0 + rr, c = c0 + tx;
+      if (r < rows && c < cols) {
+        const float x = src[(int64_t)r * cols + c];
+        const uint16_t h = bf16_rne(x);
+        hi[(int64_t)r * ld_out + c] = h;
+        lo[(int64_t)r * ld_out + c] = bf16_rne(x - bf16_to_f32(h));
+      }
+    }
+    return;
+  }
+  for (int rr = ty; rr < 32; rr += 8) {
+    const int r = r0 + rr, c = c0 + tx;
+    t[rr][tx] = (r < rows && c < cols) ? src[(int64_t)r * cols + c] : 0.0f;
+  }
+  __syncthreads();
+  for (int cc = ty; cc < 32; cc += 8) {
+    const int c = c0 + cc, r = r0 + tx;
+    if (c < cols && r < rows) {
+      const float x = t[tx][cc];
+      const uint16_t h = bf16_rne(x);
+      hi[(int64_t)c * ld_out + r] = h;
+      lo[(int64_t)c * ld_out + r] = bf16_rne(x - bf16_to_f32(h));
+    }
+  }
+}
+
+// out = (1/ *sc) * sum_s P[s] with P[s] of shape [M x N].
+//   mode 0: out_f32[m * ldo + n]           (dB)
+//   mode 1: out_f32[n * ldo + m]           (dA)
+//   mode 2: hi/lo bf16 [n * ldo + m], and zeros for M <= m < Mpad   (U^T, V^T)
+__global__ __launch_bounds__(256) void reduce_kernel(const float* __restrict__ P, int S, int M, int N,
+                                                     int Mpad, const float* __restrict__ sc, int mode,
+                                                     float* __restrict__ out, int64_t ldo,
+                                                     uint16_t* __restrict__ ohi,
+                                                     uint16_t* __restrict__ olo) {
+  __shared__ float t[32][33];
+  const int m0 = blockIdx.y * 32, n0 = blockIdx.x * 32;
+  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
+  const float scale = 1.0f / sc[0];
+  const int64_t plane = (int64_t)M * N;
+  for (int mm = ty; mm < 32; mm += 8) {
+    const int m = m0 + mm, n = n0 + tx;
+    float v = 0.0f;
+    if (m < M && n < N) {
+      for (int s = 0; s < S; ++s) v += P[s * plane + (int64_t)m * N + n];
+      v *= scale;
+    }
+    if (mode == 0) {
+      if (m < M && n < N) out[(int64_t)m * ldo + n] = v;
+    } else {
+      t[mm][tx] = v;
+    }
+  }
+  if (mode == 0) return;
+  __syncthreads();
+  for (int nn = ty; nn < 32; nn += 8) {
+    const int n = n0 + nn, m = m0 + tx;
+    if (n >= N) continue;
+    const float v = t[tx][nn];
+    if (mode == 1) {
+      if (m < M) out[(int64_t)n * ldo + m] = v;
+    } else if (m < Mpad) {
+      const uint16_t h = bf16_rne(v);
+      ohi[(int64_t)n * ldo + m] = h;
+      olo[(int64_t)n * ldo + m] = bf16_rne(v - bf16_to_f32(h));
+    }
+  }
+}
+
+__global__ void fill_kernel(float* p, int64_t n, float v) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = v;
+}
+
+// ---------------------------------------------------------------------------
+// Host-side plan: split counts and workspace layout (identical for the size
+// query and the launch).
+// ---------------------------------------------------------------------------
+struct Plan {
+  int64_t Tp;            // tokens padded to TK
+  int S1, S2;            // K splits of pass 1 (U, V) and pass 2 (dB, dA)
+  int kc1u, kc1v, kc2;   // K chunk per split
+  size_t off_ahi, off_alo, off_bhi, off_blo, off_p1u, off_p1v, off_uhi, off_ulo, off_vhi, off_vlo,
+      off_p2b, off_p2a, total;
+};
+
+int ceil_div(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
+
+int pick_splits(int64_t tiles, int64_t K, int64_t per_split_bytes, int64_t cap_bytes) {
+  int s = 1;
+  while (tiles * s < 512 && K / (int64_t)(s * 2) >= 4 * TK && per_split_bytes * (s * 2) <= cap_bytes)
+    s *= 2;
+  return s;
+}
+
+int chunk_for(int64_t K, int S) { return ceil_div(ceil_div(K, S), TK) * TK; }
+
+Plan make_plan(int64_t T, int64_t d_in, int64_t d_out, int64_t r) {
+  Plan p{};
+  p.Tp = (T + TK - 1) / TK * TK;
+  const int64_t nT = ceil_div(r, TN);
+  const int64_t tiles1 = (int64_t)ceil_div(T, TM) * nT * 2;
+  const int64_t tiles2 = ((int64_t)ceil_div(d_in, TM) + ceil_div(d_out, TM)) * nT;
+  const int64_t cap = 256ll << 20;
+  p.S1 = pick_splits(tiles1, std::min(d_in, d_out), T * r * 4 * 2, cap);
+  p.S2 = pick_splits(tiles2, T, (d_in + d_out) * r * 4, cap);
+  p.kc1u = chunk_for(d_in, p.S1);
+  p.kc1v = chunk_for(d_out, p.S1);
+  p.kc2 = chunk_for(T, p.S2);
+  size_t o = 0;
+  auto take = [&](size_t bytes) { size_t at = o; o = align_up(o + bytes, 256); return at; };
+  p.off_ahi = take((size_t)r * d_in * 2);
+  p.off_alo = take((size_t)r * d_in * 2);
+  p.off_bhi = take((size_t)r * d_out * 2);
+  p.off_blo = take((size_t)r * d_out * 2);
+  p.off_p1u = take((size_t)p.S1 * T * r * 4);
+  p.off_p1v = take((size_t)p.S1 * T * r * 4);
+  p.off_uhi = take((size_t)r * p.Tp * 2);
+  p.off_ulo = take((size_t)r * p.Tp * 2);
+  p.off_vhi = take((size_t)r * p.Tp * 2);
+  p.off_vlo = take((size_t)r * p.Tp * 2);
+  p.off_p2b = take((size_t)p.S2 * d_out * r * 4);
+  p.off_p2a = take((size_t)p.S2 * d_in * r * 4);
+  p.total = o;
+  return p;
+}
+
+Prob prob(const uint8_t* Q, int64_t ldq, const uint16_t* hi, const uint16_t* lo, int64_t ldh,
+          float* P, int64_t M, int64_t N, int64_t K, int kchunk) {
+  Prob q;
+  q.Q = Q; q.ldq = ldq; q.Hhi = hi; q.Hlo = lo; q.ldh = ldh; q.P = P;
+  q.M = (int)M; q.N = (int)N; q.K = (int)K; q.kchunk = kchunk;
+  q.tilesM = ceil_div(M, TM);
+  q.tilesN = ceil_div(N, TN);
+  return q;
+}
+
+}  // namespace
+
+size_t adapter_grad_ws_bytes(int64_t T, int64_t d_in, int64_t d_out, int64_t r) {
+  if (r == 0 || T == 0) return 0;
+  return make_plan(T, d_in, d_out, r).total;
+}
+
+hipError_t launch_fill_f32(float* p, int64_t n, float v, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  int blocks = (int)std::min<int64_t>((n + 255) / 256, 4096);
+  fill_kernel<<<blocks, 256, 0, s>>>(p, n, v);
+  return hipGetLastError();
+}
+
+hipError_t launch_adapter_grads(const uint8_t* gq, const float* s_g, const uint8_t* xq,
+                                const float* s_x, const float* A, const float* B, int64_t T,
+                                int64_t d_in, int64_t d_out, int64_t r, float* dA, float* dB,
+                                void* ws, hipStream_t s) {
+  if (r == 0) return hipSuccess;
+  if (T == 0) {
+    hipError_t e = launch_fill_f32(dB, d_out * r, 0.0f, s);
+    if (e == hipSuccess && dA) e = launch_fill_f32(dA, r * d_in, 0.0f, s);
+    return e;
+  }
+  const Plan pl = make_plan(T, d_in, d_out, r);
+  uint8_t* base = reinterpret_cast<uint8_t*>(ws);
+  auto u16 = [&](size_t off) { return reinterpret_cast<uint16_t*>(base + off); };
+  auto f32 = [&](size_t off) { return reinterpret_cast<float*>(base + off); };
+  const bool want_da = dA != nullptr;
+
+  // 0. float operands -> bf16 hi/lo: A as is [r x d_in]; B transposed [r x d_out]
+  split_bf16_kernel<<<dim3(ceil_div(d_in, 32), ceil_div(r, 32)), 256, 0, s>>>(
+      A, (int)r, (int)d_in, false, d_in, u16(pl.off_ahi), u16(pl.off_alo));
+  if (want_da)
+    split_bf16_kernel<<<dim3(ceil_div(r, 32), ceil_div(d_out, 32)), 256, 0, s>>>(
+        B, (int)d_out, (int)r, true, d_out, u16(pl.off_bhi), u16(pl.off_blo));
+
+  // 1. U = dec(X~) A^T, V = dec(G~) B  (partials over d)
+  Prob pu = prob(xq, d_in, u16(pl.off_ahi), u16(pl.off_alo), d_in, f32(pl.off_p1u), T, r, d_in,
+                 pl.kc1u);
+  Prob pv = prob(gq, d_out, u16(pl.off_bhi), u16(pl.off_blo), d_out, f32(pl.off_p1v), T, r, d_out,
+                 pl.kc1v);
+  {
+    dim3 grid(pu.tilesM * pu.tilesN, pl.S1, want_da ? 2 : 1);
+    skinny_kernel<false><<<grid, kThreads, 0, s>>>(pu, pv);
+  }
+  // reduce -> U^T, V^T as bf16 hi/lo [r x Tp], scaled by 1/s_x, 1/s_g
+  reduce_kernel<<<dim3(ceil_div(r, 32), ceil_div(pl.Tp, 32)), 256, 0, s>>>(
+      f32(pl.off_p1u), pl.S1, (int)T, (int)r, (int)pl.Tp, s_x, 2, nullptr, pl.Tp, u16(pl.off_uhi),
+      u16(pl.off_ulo));
+  if (want_da)
+    reduce_kernel<<<dim3(ceil_div(r, 32), ceil_div(pl.Tp, 32)), 256, 0, s>>>(
+        f32(pl.off_p1v), pl.S1, (int)T, (int)r, (int)pl.Tp, s_g, 2, nullptr, pl.Tp,
+        u16(pl.off_vhi), u16(pl.off_vlo));
+
+  // 2. dB = dec(G~)^T U, dA^T = dec(X~)^T V  (contract over tokens, partials over T)
+  Prob pb = prob(gq, d_out, u16(pl.off_uhi), u16(pl.off_ulo), pl.Tp, f32(pl.off_p2b), d_out, r,
+                 T, pl.kc2);
+  Prob pa = prob(xq, d_in, u16(pl.off_vhi), u16(pl.off_vlo), pl.Tp, f32(pl.off_p2a), d_in, r, T,
+                 pl.kc2);
+  {
+    const int tiles = std::max(pb.tilesM * pb.tilesN, want_da ? pa.tilesM * pa.tilesN : 0);
+    dim3 grid(tiles, pl.S2, want_da ? 2 : 1);
+    skinny_kernel<true><<<grid, kThreads, 0, s>>>(pb, pa);
+  }
+  reduce_kernel<<<dim3(ceil_div(r, 32), ceil_div(d_out, 32)), 256, 0, s>>>(
+      f32(pl.off_p2b), pl.S2, (int)d_out, (int)r, (int)d_out, s_g, 0, dB, r, nullptr, nullptr);
+  if (want_da)
+    reduce_kernel<<<dim3(ceil_div(r, 32), ceil_div(d_in, 32)), 256, 0, s>>>(
+        f32(pl.off_p2a), pl.S2, (int)d_in, (int)r, (int)d_in, s_x, 1, dA, d_in, nullptr, nullptr);
+  return hipGetLastError();
+}
+
+}  // namespace falq

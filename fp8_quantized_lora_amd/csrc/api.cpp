@@ -1,0 +1,165 @@
+// C ABI of the melded FP8 LoRA step: argument validation and dispatch to the
+// gfx950 kernels.  Every argument error is reported before anything is
+// launched; launches are asynchronous on the caller's stream.
+#include "../../include/falqon.h"
+#include "kernels.hpp"
+
+#include <hip/hip_runtime.h>
+
+namespace {
+
+using falq::align_up;
+
+inline bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// a required device pointer: non-null and 16-byte aligned
+inline bool need(const void* p) { return p != nullptr && aligned(p, 16); }
+// an optional device pointer: null, or 16-byte aligned
+inline bool opt(const void* p) { return p == nullptr || aligned(p, 16); }
+// a device scalar (float / int32): non-null and 4-byte aligned
+inline bool scalar(const void* p) { return p != nullptr && aligned(p, 4); }
+
+inline bool dims_ok(int64_t d) { return d >= 0 && d % 16 == 0 && d <= (int64_t)1 << 30; }
+
+inline falq_status hip_status(hipError_t e) { return e == hipSuccess ? FALQ_OK : FALQ_EHIP; }
+
+inline bool ws_ok(const void* ws, size_t have, size_t need_bytes) {
+  if (need_bytes == 0) return true;
+  return ws != nullptr && aligned(ws, 256) && have >= need_bytes;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* falq_status_string(falq_status s) {
+  switch (s) {
+    case FALQ_OK: return "FALQ_OK";
+    case FALQ_EINVAL: return "FALQ_EINVAL: invalid argument";
+    case FALQ_EHIP: return "FALQ_EHIP: HIP launch or runtime error";
+    case FALQ_EUNSUPPORTED: return "FALQ_EUNSUPPORTED: not supported by this build";
+  }
+  return "unknown falq_status";
+}
+
+const char* falq_version(void) { return "0.1.0"; }
+
+size_t fp8_quantize_workspace_bytes(int64_t n) {
+  (void)n;
+  return falq::quantize_ws_bytes();
+}
+
+falq_status fp8_quantize(const void* x, int dtype, int64_t n, const float* scale_in, uint8_t* q,
+                         float* scale, float* amax, int32_t* nonfinite, void* ws, size_t ws_bytes,
+                         falq_stream stream) {
+  if (n < 0 || (dtype != FALQ_F32 && dtype != FALQ_BF16)) return FALQ_EINVAL;
+  if (n > 0 && (!need(x) || !need(q))) return FALQ_EINVAL;
+  if (!scalar(scale) || (scale_in && !aligned(scale_in, 4)) || (amax && !aligned(amax, 4)) ||
+      (nonfinite && !aligned(nonfinite, 4)))
+    return FALQ_EINVAL;
+  if (!ws_ok(ws, ws_bytes, falq::quantize_ws_bytes())) return FALQ_EINVAL;
+  return hip_status(falq::launch_quantize(x, dtype, n, scale_in, q, scale, amax, nonfinite, ws,
+                                          reinterpret_cast<hipStream_t>(stream)));
+}
+
+falq_status melded_linear_fwd(const uint8_t* xq, const float* s_x, const uint8_t* wq,
+                              const float* s_w, int64_t T, int64_t d_in, int64_t d_out, float* y,
+                              falq_stream stream) {
+  if (T < 0 || T > ((int64_t)1 << 30) || !dims_ok(d_in) || !dims_ok(d_out)) return FALQ_EINVAL;
+  if (!scalar(s_x) || !scalar(s_w)) return FALQ_EINVAL;
+  if (T * d_in > 0 && !need(xq)) return FALQ_EINVAL;
+  if (d_out * d_in > 0 && !need(wq)) return FALQ_EINVAL;
+  if (T * d_out > 0 && !need(y)) return FALQ_EINVAL;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (T == 0 || d_out == 0) return FALQ_OK;
+  if (d_in == 0) return hip_status(falq::launch_fill_f32(y, T * d_out, 0.0f, s));
+  return hip_status(
+      falq::launch_gemm_fp8_nt(xq, d_in, wq, d_in, y, d_out, T, d_out, d_in, s_x, s_w, s));
+}
+
+size_t melded_linear_bwd_workspace_bytes(int64_t T, int64_t d_in, int64_t d_out, int64_t r) {
+  if (T < 0 || d_in < 0 || d_out < 0 || r < 0) return 0;
+  const size_t wt = align_up((size_t)d_in * (size_t)d_out, 256);      // W~^T for dX
+  return wt + falq::adapter_grad_ws_bytes(T, d_in, d_out, r);
+}
+
+falq_status melded_linear_bwd(const uint8_t* gq, const float* s_g, const uint8_t* xq,
+                              const float* s_x, const uint8_t* wq, const float* s_w,
+                              const float* A, const float* B, int64_t T, int64_t d_in,
+                              int64_t d_out, int64_t r, float* dx, float* dA, float* dB, void* ws,
+                              size_t ws_bytes, falq_stream stream) {
+  if (T < 0 || T > ((int64_t)1 << 30) || !dims_ok(d_in) || !dims_ok(d_out) || r < 0 ||
+      r > ((int64_t)1 << 20))
+    return FALQ_EINVAL;
+  if (!scalar(s_g) || !scalar(s_x) || !scalar(s_w)) return FALQ_EINVAL;
+  if (T * d_out > 0 && !need(gq)) return FALQ_EINVAL;
+  if (T * d_in > 0 && !need(xq)) return FALQ_EINVAL;
+  if (d_out * d_in > 0 && dx && !need(wq)) return FALQ_EINVAL;
+  if (!opt(dx) || !opt(dA)) return FALQ_EINVAL;
+  if (r * d_in > 0 && !need(A)) return FALQ_EINVAL;
+  if (r * d_out > 0 && (!need(B) || !need(dB))) return FALQ_EINVAL;
+  if (r * d_in > 0 && dA && !need(dA)) return FALQ_EINVAL;
+  if (!ws_ok(ws, ws_bytes, melded_linear_bwd_workspace_bytes(T, d_in, d_out, r)))
+    return FALQ_EINVAL;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  uint8_t* base = reinterpret_cast<uint8_t*>(ws);
+  const size_t wt_bytes = align_up((size_t)d_in * (size_t)d_out, 256);
+  hipError_t e = hipSuccess;
+  if (dx && T * d_in > 0) {
+    if (d_out == 0) {
+      e = falq::launch_fill_f32(dx, T * d_in, 0.0f, s);
+    } else {
+      e = falq::launch_transpose_u8(wq, d_out, d_in, base, s);
+      if (e == hipSuccess)
+        e = falq::launch_gemm_fp8_nt(gq, d_out, base, d_out, dx, d_in, T, d_in, d_out, s_g, s_w, s);
+    }
+    if (e != hipSuccess) return FALQ_EHIP;
+  }
+  if (r > 0) {
+    if (d_in == 0 || d_out == 0) {
+      if (d_out > 0) e = falq::launch_fill_f32(dB, d_out * r, 0.0f, s);
+      if (e == hipSuccess && dA && d_in > 0) e = falq::launch_fill_f32(dA, r * d_in, 0.0f, s);
+    } else {
+      e = falq::launch_adapter_grads(gq, s_g, xq, s_x, A, B, T, d_in, d_out, r, dA, dB,
+                                     base + wt_bytes, s);
+    }
+  }
+  return hip_status(e);
+}
+
+falq_status adapter_step(float* A, float* B, const float* dA, const float* dB, int64_t r,
+                         int64_t d_in, int64_t d_out, float lr, falq_stream stream) {
+  if (r < 0 || d_in < 0 || d_out < 0) return FALQ_EINVAL;
+  if (r * d_in > 0 && (!need(A) || !opt(dA))) return FALQ_EINVAL;
+  if (r * d_out > 0 && (!need(B) || !need(dB))) return FALQ_EINVAL;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  hipError_t e = hipSuccess;
+  if (dA && r * d_in > 0) e = falq::launch_sgd(A, dA, r * d_in, lr, s);
+  if (e == hipSuccess && r * d_out > 0) e = falq::launch_sgd(B, dB, r * d_out, lr, s);
+  return hip_status(e);
+}
+
+size_t rowwise_proxy_update_workspace_bytes(int64_t d_in, int64_t d_out, int64_t r) {
+  if (d_in < 0 || d_out < 0 || r < 0) return 0;
+  return falq::proxy_ws_bytes(d_in, d_out, r);
+}
+
+falq_status rowwise_proxy_update(uint8_t* wq, const float* s_w, const float* A, float* B,
+                                 int64_t d_in, int64_t d_out, int64_t r, float tau, int64_t k_max,
+                                 int32_t* sel_idx, int32_t* n_sel, float* rho, void* ws,
+                                 size_t ws_bytes, falq_stream stream) {
+  if (!dims_ok(d_in) || !dims_ok(d_out) || r < 0 || r > ((int64_t)1 << 20) || k_max < 0)
+    return FALQ_EINVAL;
+  if (!scalar(s_w) || !scalar(n_sel)) return FALQ_EINVAL;
+  if (d_out * d_in > 0 && !need(wq)) return FALQ_EINVAL;
+  if (r * d_in > 0 && !need(A)) return FALQ_EINVAL;
+  if (r * d_out > 0 && !need(B)) return FALQ_EINVAL;
+  if (d_out > 0 && !need(sel_idx)) return FALQ_EINVAL;
+  if (!opt(rho)) return FALQ_EINVAL;
+  if (!ws_ok(ws, ws_bytes, rowwise_proxy_update_workspace_bytes(d_in, d_out, r)))
+    return FALQ_EINVAL;
+  return hip_status(falq::launch_proxy_update(wq, s_w, A, B, d_in, d_out, r, tau, k_max, sel_idx,
+                                              n_sel, rho, ws, reinterpret_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

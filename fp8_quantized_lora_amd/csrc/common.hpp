@@ -1,0 +1,91 @@
+// Device helpers shared by the gfx950 kernels of the melded FP8 LoRA step.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace falq {
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+
+constexpr float kE4M3Max = 448.0f;
+
+// ---------------------------------------------------------------------------
+// E4M3 (OCP e4m3fn) conversions on the gfx950 conversion unit.
+//
+// v_cvt_pk_fp8_f32 rounds to nearest even.  Inputs are clamped to +-448 first
+// so that overflow saturates whatever the instruction does past the largest
+// finite value; NaN lanes are patched to 0x7F | sign afterwards (fmin/fmax
+// would turn NaN into a finite bound).  Signed zero passes through.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float clamp448(float v) {
+  return fminf(fmaxf(v, -kE4M3Max), kE4M3Max);
+}
+
+__device__ __forceinline__ uint32_t nan_patch(uint32_t codes, float a, float b, float c, float d) {
+  if (__builtin_expect(__builtin_isnan(a) | __builtin_isnan(b) | __builtin_isnan(c) |
+                       __builtin_isnan(d), 0)) {
+    float v[4] = {a, b, c, d};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (__builtin_isnan(v[i])) {
+        uint32_t sgn = (__float_as_uint(v[i]) >> 31) << 7;
+        codes = (codes & ~(0xFFu << (8 * i))) | ((0x7Fu | sgn) << (8 * i));
+      }
+    }
+  }
+  return codes;
+}
+
+// four floats -> four E4M3 codes packed little-endian (a in the low byte)
+__device__ __forceinline__ uint32_t enc4(float a, float b, float c, float d) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(clamp448(a), clamp448(b), 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(clamp448(c), clamp448(d), w, true);
+  return nan_patch((uint32_t)w, a, b, c, d);
+}
+
+// one float -> one E4M3 code
+__device__ __forceinline__ uint32_t enc1(float a) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(clamp448(a), 0.0f, 0, false);
+  uint32_t c = (uint32_t)w & 0xFFu;
+  if (__builtin_isnan(a)) c = 0x7Fu | ((__float_as_uint(a) >> 31) << 7);
+  return c;
+}
+
+// E4M3 bytes 0,1 (hi = false) or 2,3 (hi = true) of a dword -> two floats (exact)
+__device__ __forceinline__ float2 dec2(uint32_t w, bool hi) {
+  typedef float v2f __attribute__((ext_vector_type(2)));
+  v2f r = hi ? __builtin_amdgcn_cvt_pk_f32_fp8((int)w, true)
+             : __builtin_amdgcn_cvt_pk_f32_fp8((int)w, false);
+  return make_float2(r.x, r.y);
+}
+
+// ---------------------------------------------------------------------------
+// Wavefront (64 lanes) reductions.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    uint32_t o = __shfl_xor(v, off, 64);
+    v = v > o ? v : o;
+  }
+  return v;
+}
+
+__device__ __forceinline__ int wave_sum_i32(int v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+__device__ __forceinline__ float wave_max_f32(float v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+  return v;
+}
+
+}  // namespace falq

@@ -1,0 +1,49 @@
+// Internal launchers of the gfx950 kernels (host side).  Each returns
+// hipSuccess or the launch error; arguments are validated by api.cpp.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace falq {
+
+// ---- fp8_quantize: amax partials + cast ---------------------------------
+constexpr int kQzMaxParts = 1024;
+size_t quantize_ws_bytes();
+hipError_t launch_quantize(const void* x, int dtype, int64_t n, const float* scale_in,
+                           uint8_t* q, float* scale, float* amax, int32_t* nonfinite,
+                           void* ws, hipStream_t s);
+
+// ---- FP8 GEMMs ------------------------------------------------------------
+// C[M x N] (fp32, row stride ldc) = dec(A)[M x K] . dec(B)[N x K]^T / (sa * sb)
+hipError_t launch_gemm_fp8_nt(const uint8_t* A, int64_t lda, const uint8_t* B, int64_t ldb,
+                              float* C, int64_t ldc, int64_t M, int64_t N, int64_t K,
+                              const float* sa, const float* sb, hipStream_t s);
+// out[cols x rows] = in[rows x cols]^T (bytes)
+hipError_t launch_transpose_u8(const uint8_t* in, int64_t rows, int64_t cols, uint8_t* out,
+                               hipStream_t s);
+
+// ---- adapter gradients ----------------------------------------------------
+size_t adapter_grad_ws_bytes(int64_t T, int64_t d_in, int64_t d_out, int64_t r);
+hipError_t launch_adapter_grads(const uint8_t* gq, const float* s_g, const uint8_t* xq,
+                                const float* s_x, const float* A, const float* B,
+                                int64_t T, int64_t d_in, int64_t d_out, int64_t r,
+                                float* dA, float* dB, void* ws, hipStream_t s);
+
+// ---- SGD ------------------------------------------------------------------
+hipError_t launch_sgd(float* p, const float* g, int64_t n, float lr, hipStream_t s);
+
+// ---- row-wise proxy update -------------------------------------------------
+size_t proxy_ws_bytes(int64_t d_in, int64_t d_out, int64_t r);
+hipError_t launch_proxy_update(uint8_t* wq, const float* s_w, const float* A, float* B,
+                               int64_t d_in, int64_t d_out, int64_t r, float tau,
+                               int64_t k_max, int32_t* sel_idx, int32_t* n_sel, float* rho,
+                               void* ws, hipStream_t s);
+
+// ---- misc -----------------------------------------------------------------
+hipError_t launch_fill_f32(float* p, int64_t n, float v, hipStream_t s);
+
+inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+}  // namespace falq

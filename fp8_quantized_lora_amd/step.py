@@ -1,0 +1,83 @@
+"""One melded linear layer's training state and the call sequence of a step.
+
+State (all device tensors, owned here): the E4M3 backbone codes W~ with its
+fixed per-tensor scale s_w, and the adapter factors A [r x d_in] and
+B [d_out x r] (B doubles as the row-wise proxy).  A step is
+
+    fp8_quantize(X) -> melded_linear_fwd -> fp8_quantize(dY)
+    -> melded_linear_bwd -> adapter_step -> rowwise_proxy_update
+
+with every buffer and workspace allocated once up front, so a step makes no
+allocation and no host synchronisation.  This module only sequences calls
+into the HIP library; it computes nothing itself.
+"""
+from __future__ import annotations
+
+from typing import Optional
+
+import torch
+
+from . import (fp8_quantize, fp8_quantize_workspace_bytes, melded_linear_fwd, melded_linear_bwd,
+               melded_linear_bwd_workspace_bytes, adapter_step, rowwise_proxy_update,
+               rowwise_proxy_update_workspace_bytes)
+
+
+class MeldedLinear:
+    def __init__(self, d_out: int, d_in: int, rank: int, tokens: int, device="cuda",
+                 x_dtype=torch.float32, train_a: bool = True):
+        self.d_out, self.d_in, self.r, self.T = d_out, d_in, rank, tokens
+        self.train_a = train_a
+        dev = torch.device(device)
+        u8, f32, i32 = torch.uint8, torch.float32, torch.int32
+        self.wq = torch.empty((d_out, d_in), dtype=u8, device=dev)
+        self.s_w = torch.empty(1, dtype=f32, device=dev)
+        self.A = torch.empty((rank, d_in), dtype=f32, device=dev)
+        self.B = torch.empty((d_out, rank), dtype=f32, device=dev)
+        # per-step buffers
+        self.xq = torch.empty((tokens, d_in), dtype=u8, device=dev)
+        self.gq = torch.empty((tokens, d_out), dtype=u8, device=dev)
+        self.s_x = torch.empty(1, dtype=f32, device=dev)
+        self.s_g = torch.empty(1, dtype=f32, device=dev)
+        self.y = torch.empty((tokens, d_out), dtype=f32, device=dev)
+        self.dx = torch.empty((tokens, d_in), dtype=f32, device=dev)
+        self.dA = torch.empty((rank, d_in), dtype=f32, device=dev) if train_a else None
+        self.dB = torch.empty((d_out, rank), dtype=f32, device=dev)
+        self.sel = torch.empty(d_out, dtype=i32, device=dev)
+        self.n_sel = torch.zeros(1, dtype=i32, device=dev)
+        self.rho = torch.empty(d_out, dtype=f32, device=dev)
+        # workspaces
+        nq = max(tokens * max(d_in, d_out), d_out * d_in)
+        self.ws_q = torch.empty(fp8_quantize_workspace_bytes(nq), dtype=u8, device=dev)
+        self.ws_bwd = torch.empty(max(1, melded_linear_bwd_workspace_bytes(tokens, d_in, d_out, rank)),
+                                  dtype=u8, device=dev)
+        self.ws_px = torch.empty(max(1, rowwise_proxy_update_workspace_bytes(d_in, d_out, rank)),
+                                 dtype=u8, device=dev)
+
+    def init_state(self, W: torch.Tensor, A: torch.Tensor, B: torch.Tensor, stream=None):
+        """W~ = E4M3(W * s_w), s_w = 448 / max|W| (the initial quantization
+        error is the implicit adapter); A and B copied in."""
+        fp8_quantize(W, self.wq, self.s_w, ws=self.ws_q, stream=stream)
+        self.A.copy_(A)
+        self.B.copy_(B)
+
+    def forward(self, X: torch.Tensor, stream=None):
+        fp8_quantize(X, self.xq, self.s_x, ws=self.ws_q, stream=stream)
+        melded_linear_fwd(self.xq, self.s_x, self.wq, self.s_w, self.y, stream=stream)
+        return self.y
+
+    def backward(self, dY: torch.Tensor, stream=None):
+        fp8_quantize(dY, self.gq, self.s_g, ws=self.ws_q, stream=stream)
+        melded_linear_bwd(self.gq, self.s_g, self.xq, self.s_x, self.wq, self.s_w, self.A, self.B,
+                          self.dx, self.dA, self.dB, ws=self.ws_bwd, stream=stream)
+        return self.dx
+
+    def update(self, lr: float, tau: float, k_max: int = 0, stream=None):
+        adapter_step(self.A, self.B, self.dA, self.dB, lr, stream=stream)
+        rowwise_proxy_update(self.wq, self.s_w, self.A, self.B, tau, k_max, self.sel, self.n_sel,
+                             rho=self.rho, ws=self.ws_px, stream=stream)
+
+    def step(self, X: torch.Tensor, dY: torch.Tensor, lr: float = 1e-3, tau: float = 0.5,
+             k_max: int = 0, stream=None):
+        self.forward(X, stream)
+        self.backward(dY, stream)
+        self.update(lr, tau, k_max, stream)

@@ -1,0 +1,192 @@
+/*
+ * falqon.h — C ABI of the melded FP8 LoRA linear-layer training step
+ * (FALQON, arXiv 2510.24061) for AMD Instinct MI355X (gfx950).
+ *
+ * One training step of one melded linear layer is five calls, in this order:
+ *
+ *   fp8_quantize(X)        -> X~, s_x        per-tensor E4M3 activations
+ *   melded_linear_fwd      -> Y              one FP8 GEMM, no LoRA branch
+ *   fp8_quantize(dY)       -> G~, s_g        per-tensor E4M3 upstream gradient
+ *   melded_linear_bwd      -> dX, dA, dB     dX through the FP8 weight; rank-r
+ *                                            adapter gradients from G~ and X~
+ *   adapter_step           -> A, B           SGD on the adapter factors
+ *   rowwise_proxy_update   -> W~, B, rows    merge rows whose pending delta
+ *                                            survives FP8 rounding
+ *
+ * Pages the calls follow (cited by address and section):
+ *   [summary]  shd-paper.top summary of arXiv 2510.24061, "key design"
+ *              paragraph (row-wise proxy that accumulates updates and is
+ *              merged into the quantized backbone);
+ *   [intro]    luneresearch.com introduction, method paragraph (adapter merged
+ *              into the FP8 backbone; initial quantization error as implicit
+ *              LoRA initialisation; reformulated forward/backward; row-wise
+ *              proxy update applying only substantial updates);
+ *   [rebuttal] paperhub.cn OpenReview rebuttal: thread 2 W2 (per-tensor scale
+ *              s_X, s_X*X rounded to FP8), W7 (top-k row selection), W8 (DQ),
+ *              Q3 (Eq. 8/9); thread 3 Q1 (top-k cost); thread 4 Q1 (dL/dA).
+ *
+ * Conventions for every call:
+ *   - Tensor arguments are DEVICE pointers into memory the caller owns,
+ *     row-major and contiguous, 16-byte aligned.  The library allocates
+ *     nothing and keeps no state between calls; scratch memory comes from the
+ *     caller (`ws`, at least the size the matching *_workspace_bytes returns,
+ *     256-byte aligned).  Scalars that a step produces (scales, counts) stay
+ *     on the device, so a step needs no host synchronisation.
+ *   - `stream` is a hipStream_t (NULL = the null stream).  Calls are
+ *     asynchronous and stream-ordered; they may be captured in a HIP graph.
+ *   - Argument errors return FALQ_EINVAL before anything is launched; a failed
+ *     launch returns FALQ_EHIP.  Nothing is printed and nothing aborts.
+ *   - Shapes: T tokens, d_in input features, d_out output features, r rank.
+ *     d_in and d_out must be multiples of 16 (16-byte rows of FP8 codes);
+ *     T and r may be any value >= 0; zero sizes are valid and well defined.
+ *   - FP8 is OCP E4M3 ("e4m3fn": bias 7, max 448, no infinities, NaN 0x7F /
+ *     0xFF).  Casts round to nearest even and saturate to +-448.
+ *   - Output floats are fp32; products of FP8 values accumulate in fp32.
+ */
+#ifndef FALQON_H
+#define FALQON_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    FALQ_OK = 0,
+    FALQ_EINVAL = 1,        /* bad argument: null pointer, size, alignment, workspace */
+    FALQ_EHIP = 2,          /* a HIP launch or runtime call failed */
+    FALQ_EUNSUPPORTED = 3   /* valid request this build does not implement */
+} falq_status;
+
+typedef enum {
+    FALQ_F32 = 0,           /* float32 input */
+    FALQ_BF16 = 1           /* bfloat16 input (uint16 bit patterns) */
+} falq_dtype;
+
+typedef void *falq_stream;  /* a hipStream_t */
+
+/* Human-readable name of a status code (static string). */
+const char *falq_status_string(falq_status s);
+
+/* Library version, e.g. "0.1.0". */
+const char *falq_version(void);
+
+/*
+ * fp8_quantize — per-tensor current-scaled cast to E4M3 ([rebuttal] thread 2,
+ * W2: a higher-precision tensor is multiplied by one per-tensor factor s and
+ * s*X is rounded to FP8).  The page's formula is missing; this call computes
+ *     amax = max |x| over the finite elements,
+ *     s    = 448 / amax (IEEE fp32 division; amax == 0 gives 1, an overflowing
+ *            quotient gives FLT_MAX),
+ *     q[i] = E4M3(fl32(x[i] * s)).
+ *
+ *   x          [n] float32 or bfloat16 (dtype), device
+ *   scale_in   device float or NULL.  Non-NULL: use *scale_in as s (static
+ *              scaling, e.g. to requantize with a fixed backbone scale);
+ *              amax is still computed.
+ *   q          [n] uint8 codes, device (output)
+ *   scale      device float (output): s
+ *   amax       device float or NULL (output): amax
+ *   nonfinite  device int32 or NULL (output): number of NaN/inf inputs; they
+ *              are left out of amax, inf encodes to +-448, NaN to 0x7F|sign
+ *   ws         workspace of fp8_quantize_workspace_bytes(n) bytes
+ * Errors: FALQ_EINVAL for n < 0, a NULL required pointer, misalignment, a
+ * bad dtype or a short workspace.
+ */
+size_t fp8_quantize_workspace_bytes(int64_t n);
+falq_status fp8_quantize(const void *x, int dtype, int64_t n, const float *scale_in,
+                         uint8_t *q, float *scale, float *amax, int32_t *nonfinite,
+                         void *ws, size_t ws_bytes, falq_stream stream);
+
+/*
+ * melded_linear_fwd — the forward of the melded layer as one FP8 GEMM with
+ * no separate LoRA path ([intro] method paragraph; abstract):
+ *     Y[t,o] = (sum_k dec(xq[t,k]) * dec(wq[o,k])) / (s_x * s_w)
+ *
+ *   xq  [T x d_in]     E4M3 codes of X, device;   s_x  device float
+ *   wq  [d_out x d_in] E4M3 backbone codes, device; s_w device float
+ *   y   [T x d_out]    float32, device (output)
+ * The pending adapter delta B.A is not part of Y until a proxy update merges
+ * it into wq.  No workspace.
+ */
+falq_status melded_linear_fwd(const uint8_t *xq, const float *s_x,
+                              const uint8_t *wq, const float *s_w,
+                              int64_t T, int64_t d_in, int64_t d_out,
+                              float *y, falq_stream stream);
+
+/*
+ * melded_linear_bwd — reformulated backward ([intro] method paragraph;
+ * [rebuttal] thread 4, Q1: dL/dA = B^T (dL/dO) x^T, while the x A^T factor
+ * of dL/dB can be computed ahead).  With G^ = dec(gq)/s_g, X^ = dec(xq)/s_x:
+ *     dX = G^ . dec(wq)/s_w          (straight-through: Q taken as identity)
+ *     dB = G^^T (X^ A^T)             [d_out x r]
+ *     dA = (G^ B)^T X^               [r x d_in]
+ * The saved FP8 activations X~ are reused: no second quantized LoRA path.
+ *
+ *   gq [T x d_out], xq [T x d_in], wq [d_out x d_in]: E4M3 codes, device
+ *   s_g, s_x, s_w: device floats
+ *   A  [r x d_in] float32, B [d_out x r] float32, device (inputs)
+ *   dx [T x d_in] float32 or NULL (skip), dA [r x d_in] float32 or NULL
+ *   (frozen A), dB [d_out x r] float32: device outputs
+ *   ws workspace of melded_linear_bwd_workspace_bytes(T, d_in, d_out, r)
+ * With T == 0 the adapter gradients are written as zeros.
+ */
+size_t melded_linear_bwd_workspace_bytes(int64_t T, int64_t d_in, int64_t d_out, int64_t r);
+falq_status melded_linear_bwd(const uint8_t *gq, const float *s_g,
+                              const uint8_t *xq, const float *s_x,
+                              const uint8_t *wq, const float *s_w,
+                              const float *A, const float *B,
+                              int64_t T, int64_t d_in, int64_t d_out, int64_t r,
+                              float *dx, float *dA, float *dB,
+                              void *ws, size_t ws_bytes, falq_stream stream);
+
+/*
+ * adapter_step — SGD on the adapter factors, in place, elementwise in fp32
+ * with two roundings and no fused multiply-add:
+ *     A <- fl(A - fl(lr * dA))   (skipped when dA is NULL: frozen A)
+ *     B <- fl(B - fl(lr * dB))
+ * (The pages train with 32-bit AdamW, [rebuttal] thread 3 W3.1.)
+ *   A [r x d_in], B [d_out x r], dA, dB of the same shapes: float32, device
+ */
+falq_status adapter_step(float *A, float *B, const float *dA, const float *dB,
+                         int64_t r, int64_t d_in, int64_t d_out, float lr,
+                         falq_stream stream);
+
+/*
+ * rowwise_proxy_update — row-wise proxy update ([summary] key design; [intro]:
+ * only substantial updates are applied because small ones vanish under
+ * low-bit rounding; [rebuttal] thread 2 W7: merge by top-k row selection).
+ * The rows of B are the proxy: row i's pending delta is u_i = B_i . A, summed
+ * as the fixed fp32 chain acc = +0; acc = fmaf(B[i,k], A[k,j], acc) for
+ * k = 0..r-1.  With t = fl(s_w * u):
+ *     step_i = E4M3 spacing at m_i = max_j |dec(wq[i,j])| (2^-9 below 2^-6)
+ *     rho_i  = max_j |t_ij| / step_i
+ *     selected rows: rho_i >= tau; with k_max > 0 and more candidates, the
+ *                    k_max largest rho, equal rho going to the lower index
+ *     for each selected row: wq[i,j] <- E4M3(fl(dec(wq[i,j]) + t_ij)), B[i,:] <- 0
+ *
+ *   wq [d_out x d_in] E4M3 codes, device, updated in place
+ *   s_w device float (the fixed backbone scale)
+ *   A  [r x d_in] float32, device;  B [d_out x r] float32, device, in place
+ *   tau  threshold in units of the row's FP8 step (0.5 = half a step)
+ *   k_max  0 = no cap
+ *   sel_idx [d_out] int32, device (output): selected rows, ascending, in the
+ *           first n_sel entries
+ *   n_sel   device int32 (output)
+ *   rho     [d_out] float32 or NULL, device (output): every row's score
+ *   ws      workspace of rowwise_proxy_update_workspace_bytes(d_in, d_out, r)
+ */
+size_t rowwise_proxy_update_workspace_bytes(int64_t d_in, int64_t d_out, int64_t r);
+falq_status rowwise_proxy_update(uint8_t *wq, const float *s_w, const float *A, float *B,
+                                 int64_t d_in, int64_t d_out, int64_t r,
+                                 float tau, int64_t k_max,
+                                 int32_t *sel_idx, int32_t *n_sel, float *rho,
+                                 void *ws, size_t ws_bytes, falq_stream stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FALQON_H */

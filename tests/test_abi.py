@@ -1,0 +1,106 @@
+"""The C-ABI library loads and exports every function include/falqon.h
+declares, and rejects bad arguments before launching anything (these calls
+never reach the GPU, so they run on a host without one)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import fp8_quantized_lora_amd as fq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "falqon.h")
+
+EINVAL = 1
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[a-z_][a-z0-9_]*\s*\*?\s*([a-z_][a-z0-9_]*)\s*\(", src, re.M)
+    return sorted(set(n for n in names if n not in ("if", "return")))
+
+
+def test_header_declares_the_five_calls():
+    names = declared_functions()
+    for n in ["fp8_quantize", "melded_linear_fwd", "melded_linear_bwd", "adapter_step",
+              "rowwise_proxy_update"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_function():
+    lib = ctypes.CDLL(fq.LIB_PATH)
+    missing = [n for n in declared_functions() if not hasattr(lib, n)]
+    assert not missing, missing
+
+
+def test_binding_covers_every_call():
+    for n in declared_functions():
+        if n.startswith("falq_"):
+            continue
+        assert hasattr(fq, n), n
+
+
+def test_status_strings_and_version():
+    lib = fq.load()
+    assert lib.falq_status_string(0) == b"FALQ_OK"
+    assert b"EINVAL" in lib.falq_status_string(1)
+    assert fq.version().count(".") == 2
+
+
+def test_workspace_queries():
+    assert fq.fp8_quantize_workspace_bytes(1 << 24) >= 8 * 1024
+    b = fq.melded_linear_bwd_workspace_bytes(4096, 4096, 4096, 64)
+    assert b >= 4096 * 4096                    # at least W~^T for the dX product
+    assert fq.melded_linear_bwd_workspace_bytes(0, 512, 512, 16) == 512 * 512
+    assert fq.rowwise_proxy_update_workspace_bytes(4096, 4096, 64) >= 4096 * 4
+    assert fq.melded_linear_bwd_workspace_bytes(-1, 16, 16, 1) == 0
+
+
+# Argument errors: FALQ_EINVAL before any launch.  Pointers are fake host
+# addresses with the stated alignment; they are never dereferenced.
+P = 1 << 20        # a 16-byte aligned fake address
+MIS = P + 1        # misaligned
+
+
+def test_quantize_rejects_bad_arguments():
+    lib = fq.load()
+    ws = fq.fp8_quantize_workspace_bytes(16)
+    assert lib.fp8_quantize(P, 0, -1, None, P, P, None, None, P, ws, None) == EINVAL
+    assert lib.fp8_quantize(P, 7, 16, None, P, P, None, None, P, ws, None) == EINVAL      # dtype
+    assert lib.fp8_quantize(None, 0, 16, None, P, P, None, None, P, ws, None) == EINVAL   # x null
+    assert lib.fp8_quantize(MIS, 0, 16, None, P, P, None, None, P, ws, None) == EINVAL    # align
+    assert lib.fp8_quantize(P, 0, 16, None, P, None, None, None, P, ws, None) == EINVAL   # scale
+    assert lib.fp8_quantize(P, 0, 16, None, P, P, None, None, P, ws - 1, None) == EINVAL  # short ws
+    assert lib.fp8_quantize(P, 0, 16, None, P, P, None, None, MIS, ws, None) == EINVAL    # ws align
+
+
+def test_linear_rejects_bad_arguments():
+    lib = fq.load()
+    # d_in not a multiple of 16
+    assert lib.melded_linear_fwd(P, P, P, P, 8, 24, 32, P, None) == EINVAL
+    assert lib.melded_linear_fwd(P, P, P, P, -1, 32, 32, P, None) == EINVAL
+    assert lib.melded_linear_fwd(P, None, P, P, 8, 32, 32, P, None) == EINVAL             # s_x
+    assert lib.melded_linear_fwd(P, P, P, P, 8, 32, 32, None, None) == EINVAL             # y
+    ws = fq.melded_linear_bwd_workspace_bytes(8, 32, 32, 4)
+    args = [P, P, P, P, P, P, P, P, 8, 32, 32, 4, P, P, P, P, ws, None]
+    bad_r = list(args); bad_r[11] = -1
+    assert lib.melded_linear_bwd(*bad_r) == EINVAL
+    short = list(args); short[16] = ws - 1
+    assert lib.melded_linear_bwd(*short) == EINVAL
+    no_db = list(args); no_db[14] = None
+    assert lib.melded_linear_bwd(*no_db) == EINVAL
+    assert lib.adapter_step(P, P, P, None, 4, 32, 32, 1e-3, None) == EINVAL               # dB null
+    assert lib.adapter_step(P, P, P, P, -4, 32, 32, 1e-3, None) == EINVAL
+
+
+def test_proxy_rejects_bad_arguments():
+    lib = fq.load()
+    ws = fq.rowwise_proxy_update_workspace_bytes(32, 32, 4)
+    ok = [P, P, P, P, 32, 32, 4, 0.5, 0, P, P, None, P, ws, None]
+    for idx, val in [(4, 20), (6, -1), (8, -2), (9, None), (10, None), (13, ws - 1), (12, MIS),
+                     (1, None)]:
+        a = list(ok)
+        a[idx] = val
+        assert lib.rowwise_proxy_update(*a) == EINVAL, idx

@@ -1,0 +1,172 @@
+"""melded_linear_fwd / melded_linear_bwd / adapter_step on the GPU against the
+oracle: rel-L2 <= 1e-3 for Y, dX, dA, dB (fp32 accumulation); SGD bit-exact."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from tests.gpu_util import TOL, announce, dev, host, rel_l2, scalar
+import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+
+def quantized_problem(seed, T, d_in, d_out, r, x_std=1.0, dy_std=1e-2, b_std=1e-3):
+    rng = np.random.default_rng(seed)
+    W = (rng.standard_normal((d_out, d_in)) * 0.02).astype(np.float32)
+    X = (rng.standard_normal((T, d_in)) * x_std).astype(np.float32)
+    dY = (rng.standard_normal((T, d_out)) * dy_std).astype(np.float32)
+    A = (rng.standard_normal((r, d_in)) / np.sqrt(max(r, 1))).astype(np.float32)
+    B = (rng.standard_normal((d_out, r)) * b_std).astype(np.float32)
+    wq, s_w, _, _ = oracle.fp8_quantize(W)
+    xq, s_x, _, _ = oracle.fp8_quantize(X)
+    gq, s_g, _, _ = oracle.fp8_quantize(dY)
+    return dict(wq=wq, s_w=s_w, xq=xq, s_x=s_x, gq=gq, s_g=s_g, A=A, B=B)
+
+
+def gpu_fwd(fq, p):
+    T, d_out = p["xq"].shape[0], p["wq"].shape[0]
+    y = torch.empty((T, d_out), dtype=torch.float32, device="cuda")
+    fq.melded_linear_fwd(dev(p["xq"]), scalar(p["s_x"]), dev(p["wq"]), scalar(p["s_w"]), y)
+    return host(y)
+
+
+def gpu_bwd(fq, p, want_dx=True, want_da=True):
+    T, d_out = p["gq"].shape
+    d_in = p["xq"].shape[1]
+    r = p["A"].shape[0]
+    dx = torch.full((T, d_in), np.nan, dtype=torch.float32, device="cuda") if want_dx else None
+    dA = torch.full((r, d_in), np.nan, dtype=torch.float32, device="cuda") if want_da else None
+    dB = torch.full((d_out, r), np.nan, dtype=torch.float32, device="cuda")
+    fq.melded_linear_bwd(dev(p["gq"]), scalar(p["s_g"]), dev(p["xq"]), scalar(p["s_x"]),
+                         dev(p["wq"]), scalar(p["s_w"]), dev(p["A"]), dev(p["B"]), dx, dA, dB)
+    return (host(dx) if want_dx else None), (host(dA) if want_da else None), host(dB)
+
+
+SHAPES = [  # (T, d_in, d_out, r): full tiles, ragged tails in every dimension, tiny
+    (256, 512, 512, 16),
+    (257, 400, 272, 5),
+    (600, 1040, 784, 64),
+    (1, 16, 16, 1),
+    (3, 48, 32, 70),
+    (1000, 256, 1536, 128),
+]
+
+
+@pytest.mark.parametrize("T,d_in,d_out,r", SHAPES)
+def test_forward_parity(gpu_lib, T, d_in, d_out, r):
+    announce(f"fwd T={T} d_in={d_in} d_out={d_out}")
+    p = quantized_problem(T + d_in, T, d_in, d_out, r)
+    y = gpu_fwd(gpu_lib, p)
+    ref = oracle.melded_linear_fwd(p["xq"], p["s_x"], p["wq"], p["s_w"])
+    err = rel_l2(y, ref)
+    print(f"fwd rel-L2 {err:.3e}")
+    assert err <= TOL
+
+
+@pytest.mark.parametrize("T,d_in,d_out,r", SHAPES)
+def test_backward_parity(gpu_lib, T, d_in, d_out, r):
+    announce(f"bwd T={T} d_in={d_in} d_out={d_out} r={r}")
+    p = quantized_problem(T + d_out, T, d_in, d_out, r)
+    dx, dA, dB = gpu_bwd(gpu_lib, p)
+    rdx, rdA, rdB = oracle.melded_linear_bwd(p["gq"], p["s_g"], p["xq"], p["s_x"], p["wq"],
+                                             p["s_w"], p["A"], p["B"])
+    e = (rel_l2(dx, rdx), rel_l2(dA, rdA), rel_l2(dB, rdB))
+    print("bwd rel-L2 dX %.3e dA %.3e dB %.3e" % e)
+    assert max(e) <= TOL
+
+
+def test_backward_frozen_a_and_no_dx(gpu_lib):
+    announce("bwd frozen A, no dX")
+    p = quantized_problem(3, 300, 512, 384, 32)
+    _, _, dB = gpu_bwd(gpu_lib, p, want_dx=False, want_da=False)
+    _, _, rdB = oracle.melded_linear_bwd(p["gq"], p["s_g"], p["xq"], p["s_x"], p["wq"], p["s_w"],
+                                         p["A"], p["B"], want_dx=False, want_da=False)
+    assert rel_l2(dB, rdB) <= TOL
+
+
+def test_backward_degenerate(gpu_lib):
+    announce("bwd degenerate: T=0, B=0, r=0")
+    p = quantized_problem(4, 0, 64, 48, 8)
+    dx, dA, dB = gpu_bwd(gpu_lib, p)
+    assert dx.shape == (0, 64) and not dA.any() and not dB.any()
+    p = quantized_problem(5, 100, 64, 48, 8, b_std=0.0)
+    _, dA, dB = gpu_bwd(gpu_lib, p)
+    assert not dA.any()            # B = 0 => dA = 0 exactly
+    p = quantized_problem(6, 100, 64, 48, 0)
+    dx, dA, dB = gpu_bwd(gpu_lib, p)
+    rdx, _, _ = oracle.melded_linear_bwd(p["gq"], p["s_g"], p["xq"], p["s_x"], p["wq"], p["s_w"],
+                                         p["A"], p["B"])
+    assert dA.size == 0 and dB.size == 0 and rel_l2(dx, rdx) <= TOL
+
+
+def test_full_size_attention_projection(gpu_lib):
+    """4096 x 4096 weight, 4096 tokens with outlier channels, r = 64 (the 7B
+    attention projection workload): Y and dX on 96 sampled token rows, dA and
+    dB in full."""
+    spec = wl.WORKLOADS[2].linears[0]
+    announce("full-size 4096^3 fwd/bwd, sampled rows")
+    d = wl.make_linear(2, 0, spec, step=0)
+    wq, s_w, _, _ = oracle.fp8_quantize(d["W"])
+    xq, s_x, _, _ = oracle.fp8_quantize(d["X"])
+    gq, s_g, _, _ = oracle.fp8_quantize(d["dY"])
+    p = dict(wq=wq, s_w=s_w, xq=xq, s_x=s_x, gq=gq, s_g=s_g, A=d["A"], B=d["B"])
+    y = gpu_fwd(gpu_lib, p)
+    dx, dA, dB = gpu_bwd(gpu_lib, p)
+    rows = np.sort(np.random.default_rng(0).choice(spec.tokens, 96, replace=False))
+    rows = np.concatenate([[0], rows, [spec.tokens - 1]])
+    ry = oracle.melded_linear_fwd(xq[rows], s_x, wq, s_w)
+    rdx, _, _ = oracle.melded_linear_bwd(gq[rows], s_g, xq[rows], s_x, wq, s_w, d["A"], d["B"],
+                                         want_da=False)
+    _, rdA, rdB = oracle.melded_linear_bwd(gq, s_g, xq, s_x, wq, s_w, d["A"], d["B"], want_dx=False)
+    e = (rel_l2(y[rows], ry), rel_l2(dx[rows], rdx), rel_l2(dA, rdA), rel_l2(dB, rdB))
+    print("full-size rel-L2 Y %.3e dX %.3e dA %.3e dB %.3e" % e)
+    assert max(e) <= TOL
+
+
+def test_max_size_mlp_down(gpu_lib):
+    """The largest single GEMM of the workloads: 7B MLP down projection,
+    W 4096 x 11008, 8192 tokens.  Sampled rows of Y and dX."""
+    announce("max-size fwd/bwd 8192 x 11008 -> 4096, sampled rows")
+    rng = np.random.default_rng(77)
+    T, d_in, d_out = 8192, 11008, 4096
+    wq = rng.integers(0, 0x7F, size=(d_out, d_in), dtype=np.uint8) | \
+        (rng.integers(0, 2, size=(d_out, d_in), dtype=np.uint8) << 7)
+    xq = rng.integers(0, 0x7F, size=(T, d_in), dtype=np.uint8)
+    gq = rng.integers(0, 0x7F, size=(T, d_out), dtype=np.uint8)
+    p = dict(wq=wq, s_w=np.float32(2000.0), xq=xq, s_x=np.float32(30.0), gq=gq,
+             s_g=np.float32(5e4), A=np.zeros((1, d_in), np.float32), B=np.zeros((d_out, 1), np.float32))
+    y = gpu_fwd(gpu_lib, p)
+    dx, _, _ = gpu_bwd(gpu_lib, p, want_da=False)
+    rows = np.array([0, 1, 4095, 4096, 5000, 8191])
+    ry = oracle.melded_linear_fwd(xq[rows], p["s_x"], wq, p["s_w"])
+    rdx, _, _ = oracle.melded_linear_bwd(gq[rows], p["s_g"], xq[rows], p["s_x"], wq, p["s_w"],
+                                         p["A"], p["B"], want_da=False)
+    assert rel_l2(y[rows], ry) <= TOL and rel_l2(dx[rows], rdx) <= TOL
+
+
+def test_adapter_step_bit_exact(gpu_lib):
+    announce("adapter_step")
+    rng = np.random.default_rng(11)
+    for r, d_in, d_out in [(16, 512, 512), (5, 48, 80), (64, 4096, 4096)]:
+        A = rng.standard_normal((r, d_in)).astype(np.float32)
+        B = rng.standard_normal((d_out, r)).astype(np.float32)
+        dA = rng.standard_normal((r, d_in)).astype(np.float32)
+        dB = rng.standard_normal((d_out, r)).astype(np.float32)
+        tA, tB = dev(A), dev(B)
+        gpu_lib.adapter_step(tA, tB, dev(dA), dev(dB), 1e-3)
+        rA, rB = oracle.adapter_step(A, B, dA, dB, 1e-3)
+        assert np.array_equal(host(tA).view(np.uint32), rA.view(np.uint32))
+        assert np.array_equal(host(tB).view(np.uint32), rB.view(np.uint32))
+        tA2 = dev(A)
+        gpu_lib.adapter_step(tA2, dev(B), None, dev(dB), 1e-3)     # frozen A
+        assert np.array_equal(host(tA2), A)
+
+
+def test_backward_is_deterministic(gpu_lib):
+    announce("bwd twice, bitwise equal")
+    p = quantized_problem(12, 777, 512, 640, 64)
+    a = gpu_bwd(gpu_lib, p)
+    b = gpu_bwd(gpu_lib, p)
+    for u, v in zip(a, b):
+        assert np.array_equal(u.view(np.uint32), v.view(np.uint32))

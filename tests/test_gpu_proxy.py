@@ -1,0 +1,98 @@
+"""rowwise_proxy_update on the GPU against the oracle: new codes, new B,
+scores, selected rows and their count all bit-exact."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from tests.gpu_util import announce, dev, host, scalar
+import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+
+def proxy_problem(seed, d_out, d_in, r, b_scale=0.004, a_std=None):
+    rng = np.random.default_rng(seed)
+    W = (rng.standard_normal((d_out, d_in)) * 0.02).astype(np.float32)
+    wq, s_w, _, _ = oracle.fp8_quantize(W)
+    A = (rng.standard_normal((r, d_in)) * (a_std or 1.0 / np.sqrt(max(r, 1)))).astype(np.float32)
+    B = (rng.standard_normal((d_out, r)) * b_scale).astype(np.float32)
+    if d_out:
+        B *= rng.choice(np.array([0.05, 0.5, 1.0, 3.0], np.float32), size=(d_out, 1))
+    return wq, np.float32(s_w), A, B
+
+
+def run_gpu(fq, wq, s_w, A, B, tau, k_max):
+    d_out = wq.shape[0]
+    twq, tB = dev(wq), dev(B)
+    sel = torch.full((d_out,), -1, dtype=torch.int32, device="cuda")
+    n = torch.full((1,), -1, dtype=torch.int32, device="cuda")
+    rho = torch.full((d_out,), np.nan, dtype=torch.float32, device="cuda")
+    fq.rowwise_proxy_update(twq, scalar(s_w), dev(A), tB, tau, k_max, sel, n, rho=rho)
+    n_sel = int(host(n)[0])
+    return host(twq), host(tB), host(sel)[:n_sel], host(rho)
+
+
+def check(fq, wq, s_w, A, B, tau=0.5, k_max=0, expect_some=True):
+    g_wq, g_B, g_sel, g_rho = run_gpu(fq, wq, s_w, A, B, tau, k_max)
+    r_wq, r_B, r_sel, r_rho = oracle.rowwise_proxy_update(wq, s_w, A, B, tau, k_max)
+    assert np.array_equal(g_rho.view(np.uint32), r_rho.view(np.uint32)), \
+        f"rho differs at rows {np.nonzero(g_rho != r_rho)[0][:8]}"
+    assert np.array_equal(g_sel, r_sel), (g_sel[:10], r_sel[:10])
+    bad = np.nonzero(g_wq != r_wq)
+    assert bad[0].size == 0, f"{bad[0].size} code mismatches at rows {np.unique(bad[0])[:8]}"
+    assert np.array_equal(g_B.view(np.uint32), r_B.view(np.uint32))
+    if expect_some:
+        assert 0 < r_sel.size, "fixture selects nothing"
+    return r_sel
+
+
+@pytest.mark.parametrize("d_out,d_in,r", [(512, 512, 16), (272, 400, 5), (9, 16, 1),
+                                          (1000, 1040, 64), (64, 2048, 130)])
+def test_proxy_parity(gpu_lib, d_out, d_in, r):
+    announce(f"proxy d_out={d_out} d_in={d_in} r={r}")
+    wq, s_w, A, B = proxy_problem(d_out + r, d_out, d_in, r)
+    sel = check(gpu_lib, wq, s_w, A, B)
+    print(f"selected {sel.size}/{d_out}")
+
+
+def test_proxy_k_max_and_ties(gpu_lib):
+    announce("proxy k_max cap with tied scores")
+    wq, s_w, A, B = proxy_problem(7, 300, 256, 8)
+    for i in (40, 41, 200, 299):        # four identical rows with the top score
+        wq[i] = wq[3]
+        B[i] = B[3] * np.float32(30.0)
+    B[3] *= np.float32(30.0)
+    for k in (1, 2, 3, 5, 17, 299, 300, 1000):
+        check(gpu_lib, wq, s_w, A, B, tau=0.5, k_max=k)
+    check(gpu_lib, wq, s_w, A, B, tau=0.0, k_max=2)
+
+
+def test_proxy_limits(gpu_lib):
+    announce("proxy tau=inf, tau=0, B=0, r=0, d_out=0")
+    wq, s_w, A, B = proxy_problem(8, 200, 128, 4)
+    check(gpu_lib, wq, s_w, A, B, tau=np.inf, expect_some=False)
+    check(gpu_lib, wq, s_w, A, B, tau=0.0)
+    check(gpu_lib, wq, s_w, A, np.zeros_like(B), tau=0.5, expect_some=False)
+    check(gpu_lib, wq, s_w, A[:0], B[:, :0], tau=0.0)          # r = 0: -0 codes become +0
+    check(gpu_lib, wq[:0], s_w, A, B[:0], tau=0.5, expect_some=False)
+    big = B.copy()
+    big[::7] = 1e4                                              # saturating merges
+    check(gpu_lib, wq, s_w, A, big, tau=0.5)
+
+
+def test_proxy_full_size_attention_projection(gpu_lib):
+    """4096 x 4096 backbone, r = 64, A ~ N(0, 1/r) (variance), B ~ N(0, 1e-3):
+    every row scored and merged exactly as the oracle does."""
+    announce("proxy full size 4096 x 4096 r=64")
+    spec = wl.WORKLOADS[2].linears[0]
+    d = wl.make_linear(2, 0, spec)
+    wq, s_w, _, _ = oracle.fp8_quantize(d["W"])
+    sel = check(gpu_lib, wq, np.float32(s_w), d["A"], d["B"])
+    print(f"selected {sel.size}/4096")
+
+
+def test_proxy_large_rank(gpu_lib):
+    announce("proxy 1024 x 4096, r=2048")
+    wq, s_w, A, B = proxy_problem(13, 1024, 4096, 2048, b_scale=0.0005)
+    check(gpu_lib, wq, s_w, A, B)
