@@ -148,7 +148,9 @@ falq_status rowwise_proxy_update(uint8_t* wq, const float* s_w, const float* A, 
                                  int64_t d_in, int64_t d_out, int64_t r, float tau, int64_t k_max,
                                  int32_t* sel_idx, int32_t* n_sel, float* rho, void* ws,
                                  size_t ws_bytes, falq_stream stream) {
-  if (!dims_ok(d_in) || !dims_ok(d_out) || r < 0 || r > ((int64_t)1 << 20) || k_max < 0)
+  // rows are independent: only d_in needs 16-byte rows of codes
+  if (!dims_ok(d_in) || d_out < 0 || d_out > ((int64_t)1 << 30) || r < 0 ||
+      r > ((int64_t)1 << 20) || k_max < 0)
     return FALQ_EINVAL;
   if (!scalar(s_w) || !scalar(n_sel)) return FALQ_EINVAL;
   if (d_out * d_in > 0 && !need(wq)) return FALQ_EINVAL;

@@ -37,8 +37,9 @@
  *   - Argument errors return FALQ_EINVAL before anything is launched; a failed
  *     launch returns FALQ_EHIP.  Nothing is printed and nothing aborts.
  *   - Shapes: T tokens, d_in input features, d_out output features, r rank.
- *     d_in and d_out must be multiples of 16 (16-byte rows of FP8 codes);
- *     T and r may be any value >= 0; zero sizes are valid and well defined.
+ *     d_in and d_out must be multiples of 16 (16-byte rows of FP8 codes;
+ *     rowwise_proxy_update accepts any d_out); T and r may be any value >= 0;
+ *     zero sizes are valid and well defined.
  *   - FP8 is OCP E4M3 ("e4m3fn": bias 7, max 448, no infinities, NaN 0x7F /
  *     0xFF).  Casts round to nearest even and saturate to +-448.
  *   - Output floats are fp32; products of FP8 values accumulate in fp32.
@@ -167,7 +168,8 @@ falq_status adapter_step(float *A, float *B, const float *dA, const float *dB,
  *                    k_max largest rho, equal rho going to the lower index
  *     for each selected row: wq[i,j] <- E4M3(fl(dec(wq[i,j]) + t_ij)), B[i,:] <- 0
  *
- *   wq [d_out x d_in] E4M3 codes, device, updated in place
+ *   wq [d_out x d_in] E4M3 codes, device, updated in place (d_out may be any
+ *      value >= 0 here; d_in a multiple of 16)
  *   s_w device float (the fixed backbone scale)
  *   A  [r x d_in] float32, device;  B [d_out x r] float32, device, in place
  *   tau  threshold in units of the row's FP8 step (0.5 = half a step)

@@ -1,15 +1,19 @@
 """Whole steps chained on the GPU (MeldedLinear) against the oracle's chain.
 
 Per call on identical inputs the results are bit-exact (codes, rows) or within
-rel-L2 1e-3 (floats); chained over steps, tolerance-level differences in dA/dB
-move B, so a row whose score sits at the threshold may flip.  These tests
-assert that every differing selection is such a borderline row and that all
-other state agrees."""
+rel-L2 1e-3 (floats).  Within a step, the oracle's dA/dB differ from the
+GPU's at the 1e-6 level, so after SGD its B differs by as little, and two
+things may then legitimately differ: a row whose score sits at the threshold
+may be selected by one side only, and a merged element whose dec(q) + t sits
+at a rounding midpoint may round to the neighbouring code.  The test asserts
+that every difference is of one of these two kinds, and that Y, dX, dA, dB
+stay within 1e-3.  Each step restarts the oracle from the GPU's state, so the
+comparison does not compound."""
 import numpy as np
 import pytest
-import torch
 
 import oracle
+from oracle import e4m3
 from tests.gpu_util import TOL, announce, dev, host, rel_l2
 import workloads as wl
 
@@ -22,11 +26,13 @@ def oracle_step(st, X, dY, lr, tau, k_max=0):
     gq, s_g, _, _ = oracle.fp8_quantize(dY)
     dx, dA, dB = oracle.melded_linear_bwd(gq, s_g, xq, s_x, st["wq"], st["s_w"], st["A"], st["B"])
     A, B = oracle.adapter_step(st["A"], st["B"], dA, dB, lr)
+    _, t = oracle.row_scores(st["wq"], st["s_w"], A, B)
     wq, B, sel, rho = oracle.rowwise_proxy_update(st["wq"], st["s_w"], A, B, tau, k_max)
-    return dict(wq=wq, s_w=st["s_w"], A=A, B=B), dict(y=y, dx=dx, dA=dA, dB=dB, sel=sel, rho=rho)
+    return dict(wq=wq, s_w=st["s_w"], A=A, B=B), dict(y=y, dx=dx, dA=dA, dB=dB, sel=sel, rho=rho,
+                                                      t=t)
 
 
-def run_chain(fq, cfg_id, steps, tol_rows_frac=0.01):
+def run_chain(fq, cfg_id, steps):
     spec = wl.WORKLOADS[cfg_id].linears[0]
     d0 = wl.make_linear(cfg_id, 0, spec, step=0)
     m = fq.MeldedLinear(spec.d_out, spec.d_in, spec.rank, spec.tokens)
@@ -36,26 +42,35 @@ def run_chain(fq, cfg_id, steps, tol_rows_frac=0.01):
     st = dict(wq=wq0, s_w=np.float32(s_w), A=d0["A"], B=d0["B"])
     for step in range(steps):
         d = wl.step_activations(cfg_id, 0, spec, step)
-        X, dY = dev(d["X"]), dev(d["dY"])
-        m.step(X, dY, lr=spec.lr, tau=spec.tau, k_max=spec.k_max)
+        m.step(dev(d["X"]), dev(d["dY"]), lr=spec.lr, tau=spec.tau, k_max=spec.k_max)
+        wq_before = st["wq"]
         st, out = oracle_step(st, d["X"], d["dY"], spec.lr, spec.tau, spec.k_max)
         e = (rel_l2(host(m.y), out["y"]), rel_l2(host(m.dx), out["dx"]),
              rel_l2(host(m.dA), out["dA"]), rel_l2(host(m.dB), out["dB"]))
         n_sel = int(host(m.n_sel)[0])
         g_sel = host(m.sel)[:n_sel]
         flips = np.setxor1d(g_sel, out["sel"])
-        rho = out["rho"]
-        margin = np.abs(rho[flips] - spec.tau) / spec.tau if flips.size else np.zeros(0)
-        code_rows = np.nonzero(np.any(host(m.wq) != st["wq"], axis=1))[0]
+        margin = np.abs(out["rho"][flips] - spec.tau) / spec.tau
+        both = np.intersect1d(g_sel, out["sel"])
+        g_wq = host(m.wq)
+        di, dj = np.nonzero(g_wq[both] != st["wq"][both])
+        rows, cols = both[di], dj
+        qg, qo = g_wq[rows, cols], st["wq"][rows, cols]
+        vg, vo = e4m3.DECODE_F64[qg], e4m3.DECODE_F64[qo]
+        v = e4m3.DECODE_F64[wq_before[rows, cols]] + out["t"][rows, cols].astype(np.float64)
+        mid = 0.5 * (vg + vo)
+        step_at = e4m3.step_of(np.abs(mid))
+        adjacent = np.abs(vg - vo) <= step_at * 1.0000001 + 0.0
+        near_mid = np.abs(v - mid) <= 1e-3 * (np.abs(out["t"][rows, cols]) + step_at)
         print(f"step {step}: rel-L2 Y {e[0]:.2e} dX {e[1]:.2e} dA {e[2]:.2e} dB {e[3]:.2e}; "
-              f"selected {n_sel}/{spec.d_out}, flips {flips.size}, rows with code drift "
-              f"{code_rows.size}")
-        assert max(e[:2]) <= TOL
-        assert e[2] <= TOL and e[3] <= TOL
+              f"selected {n_sel}/{spec.d_out}, threshold flips {flips.size}, midpoint "
+              f"re-roundings {rows.size} in {np.unique(rows).size} rows")
+        assert max(e) <= TOL
         assert np.all(margin < 1e-3), (flips, margin)
-        assert code_rows.size <= max(1, int(tol_rows_frac * spec.d_out))
-        # continue both chains from the GPU's state so that drift does not compound
-        st = dict(wq=host(m.wq), s_w=st["s_w"], A=host(m.A), B=host(m.B))
+        assert np.all(adjacent), "a merged code differs by more than one step"
+        assert np.all(near_mid), "a merged code differs away from a rounding midpoint"
+        assert rows.size <= 1e-4 * max(1, both.size) * spec.d_in
+        st = dict(wq=g_wq, s_w=st["s_w"], A=host(m.A), B=host(m.B))
 
 
 def test_single_linear_step(gpu_lib):
