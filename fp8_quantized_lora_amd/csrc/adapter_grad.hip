@@ -252,7 +252,10 @@ __global__ __launch_bounds__(256) void split_bf16_kernel(const float* __restrict
   }
 }
 
-// out = (1/ *sc) * sum_s P[s] with P[s] of shape [M x N].
+// out = (1/ *sc) * sum_s P[s] with P[s] of shape [M x N], folded in split
+// order s = 0, 1, ... (deterministic).  A workgroup owns a 64 (m) x 64 (n)
+// tile: float4 loads along n, the tile transposed through LDS when the output
+// is n-major.
 //   mode 0: out_f32[m * ldo + n]           (dB)
 //   mode 1: out_f32[n * ldo + m]           (dA)
 //   mode 2: hi/lo bf16 [n * ldo + m], and zeros for M <= m < Mpad   (U^T, V^T)
@@ -261,30 +264,59 @@ __global__ __launch_bounds__(256) void reduce_kernel(const float* __restrict__ P
                                                      float* __restrict__ out, int64_t ldo,
                                                      uint16_t* __restrict__ ohi,
                                                      uint16_t* __restrict__ olo) {
-  __shared__ float t[32][33];
-  const int m0 = blockIdx.y * 32, n0 = blockIdx.x * 32;
-  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
+  __shared__ float t[64][65];
+  const int m0 = blockIdx.y * 64, n0 = blockIdx.x * 64;
+  const int tid = threadIdx.x;
   const float scale = 1.0f / sc[0];
   const int64_t plane = (int64_t)M * N;
-  for (int mm = ty; mm < 32; mm += 8) {
-    const int m = m0 + mm, n = n0 + tx;
-    float v = 0.0f;
-    if (m < M && n < N) {
-      for (int s = 0; s < S; ++s) v += P[s * plane + (int64_t)m * N + n];
-      v *= scale;
+  const bool vec = (N % 4) == 0;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int idx = tid + u * 256;            // 0..1023: 64 rows x 16 float4
+    const int mm = idx >> 4, nn = (idx & 15) * 4;
+    const int m = m0 + mm, n = n0 + nn;
+    float v[4] = {0.f, 0.f, 0.f, 0.f};
+    if (m < M) {
+      const int64_t off = (int64_t)m * N + n;
+      if (vec && n + 3 < N) {
+        for (int s = 0; s < S; ++s) {
+          const float4 x = *reinterpret_cast<const float4*>(P + s * plane + off);
+          v[0] += x.x; v[1] += x.y; v[2] += x.z; v[3] += x.w;
+        }
+      } else {
+        for (int s = 0; s < S; ++s)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (n + e < N) v[e] += P[s * plane + off + e];
+      }
     }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] *= scale;
     if (mode == 0) {
-      if (m < M && n < N) out[(int64_t)m * ldo + n] = v;
+      if (m < M) {
+        if (vec && n + 3 < N && (ldo % 4) == 0) {
+          *reinterpret_cast<float4*>(out + (int64_t)m * ldo + n) = make_float4(v[0], v[1], v[2], v[3]);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (n + e < N) out[(int64_t)m * ldo + n + e] = v[e];
+        }
+      }
     } else {
-      t[mm][tx] = v;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) t[nn + e][mm] = v[e];
     }
   }
   if (mode == 0) return;
   __syncthreads();
-  for (int nn = ty; nn < 32; nn += 8) {
-    const int n = n0 + nn, m = m0 + tx;
+  // write n-major rows: 64 consecutive m per row
+#pragma unroll
+  for (int u = 0; u < 16; ++u) {
+    const int idx = tid + u * 256;            // 0..4095: 64 rows (n) x 64 m
+    const int nn = idx >> 6, mm = idx & 63;
+    const int n = n0 + nn, m = m0 + mm;
     if (n >= N) continue;
-    const float v = t[tx][nn];
+    const float v = t[nn][mm];
     if (mode == 1) {
       if (m < M) out[(int64_t)n * ldo + m] = v;
     } else if (m < Mpad) {
@@ -411,11 +443,11 @@ hipError_t launch_adapter_grads(const uint8_t* gq, const float* s_g, const uint8
     skinny_kernel<false><<<grid, kThreads, 0, s>>>(pu, pv);
   }
   // reduce -> U^T, V^T as bf16 hi/lo [r x Tp], scaled by 1/s_x, 1/s_g
-  reduce_kernel<<<dim3(ceil_div(r, 32), ceil_div(pl.Tp, 32)), 256, 0, s>>>(
+  reduce_kernel<<<dim3(ceil_div(r, 64), ceil_div(pl.Tp, 64)), 256, 0, s>>>(
       f32(pl.off_p1u), pl.S1, (int)T, (int)r, (int)pl.Tp, s_x, 2, nullptr, pl.Tp, u16(pl.off_uhi),
       u16(pl.off_ulo));
   if (want_da)
-    reduce_kernel<<<dim3(ceil_div(r, 32), ceil_div(pl.Tp, 32)), 256, 0, s>>>(
+    reduce_kernel<<<dim3(ceil_div(r, 64), ceil_div(pl.Tp, 64)), 256, 0, s>>>(
         f32(pl.off_p1v), pl.S1, (int)T, (int)r, (int)pl.Tp, s_g, 2, nullptr, pl.Tp,
         u16(pl.off_vhi), u16(pl.off_vlo));
 
@@ -429,10 +461,10 @@ hipError_t launch_adapter_grads(const uint8_t* gq, const float* s_g, const uint8
     dim3 grid(tiles, pl.S2, want_da ? 2 : 1);
     skinny_kernel<true><<<grid, kThreads, 0, s>>>(pb, pa);
   }
-  reduce_kernel<<<dim3(ceil_div(r, 32), ceil_div(d_out, 32)), 256, 0, s>>>(
+  reduce_kernel<<<dim3(ceil_div(r, 64), ceil_div(d_out, 64)), 256, 0, s>>>(
       f32(pl.off_p2b), pl.S2, (int)d_out, (int)r, (int)d_out, s_g, 0, dB, r, nullptr, nullptr);
   if (want_da)
-    reduce_kernel<<<dim3(ceil_div(r, 32), ceil_div(d_in, 32)), 256, 0, s>>>(
+    reduce_kernel<<<dim3(ceil_div(r, 64), ceil_div(d_in, 64)), 256, 0, s>>>(
         f32(pl.off_p2a), pl.S2, (int)d_in, (int)r, (int)d_in, s_x, 1, dA, d_in, nullptr, nullptr);
   return hipGetLastError();
 }

@@ -1,0 +1,307 @@
+// FP8 GEMM kernel template (C = A . B^T, both operands K-contiguous) for
+// gfx950; instantiated by gemm_fp8.hip.  See that file for the design notes.
+#pragma once
+
+#include "common.hpp"
+
+namespace falq {
+namespace gemm {
+
+template <int BM_, int BN_, int BK_, int WGM_, int WGN_>
+struct Cfg {
+  static constexpr int BM = BM_, BN = BN_, BK = BK_, WGM = WGM_, WGN = WGN_;
+  static constexpr int kThreads = WGM * WGN * 64;
+  static constexpr int WTM = BM / WGM, WTN = BN / WGN;
+  static constexpr int MB = WTM / 32, NB = WTN / 32;
+  static constexpr int ROW = BK + 16;                    // padded LDS row (bytes)
+  static constexpr int CPR = BK / 16;                    // 16-byte chunks per row
+  static constexpr int A_CH = BM * CPR / kThreads;
+  static constexpr int B_CH = BN * CPR / kThreads;
+  static constexpr int LDS_BYTES = 2 * (BM + BN) * ROW;
+  static_assert(BM * CPR % kThreads == 0 && BN * CPR % kThreads == 0, "tile/threads");
+  static_assert(WTM % 32 == 0 && WTN % 32 == 0 && BK % 64 == 0, "mfma shape");
+};
+
+__device__ __forceinline__ v8i join(uint4 lo, uint4 hi) {
+  v8i r;
+  r[0] = lo.x; r[1] = lo.y; r[2] = lo.z; r[3] = lo.w;
+  r[4] = hi.x; r[5] = hi.y; r[6] = hi.z; r[7] = hi.w;
+  return r;
+}
+
+__device__ __forceinline__ void tile_coords(int tilesM, int tilesN, int& tm, int& tn) {
+  const int nt = tilesM * tilesN;
+  const int bid = blockIdx.x;
+  const int per = nt / 8;
+  int logical = bid;
+  if (bid < per * 8) logical = (bid % 8) * per + bid / 8;   // 8 XCDs, round-robin dispatch
+  constexpr int G = 8;                                       // tile rows per group
+  const int gsz = G * tilesN;
+  const int g = logical / gsz;
+  const int first = g * G;
+  const int gm = min(tilesM - first, G);
+  const int rem = logical - g * gsz;
+  tm = first + rem % gm;
+  tn = rem / gm;
+}
+
+template <class C>
+__global__ __launch_bounds__(C::kThreads, 1) void gemm_fp8_nt_kernel(
+    const uint8_t* __restrict__ A, int64_t lda, const uint8_t* __restrict__ B, int64_t ldb,
+    float* __restrict__ Cm, int64_t ldc, int M, int N, int K, const float* __restrict__ sa,
+    const float* __restrict__ sb, int tilesM, int tilesN) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[C::LDS_BYTES];
+  uint8_t* sA = smem;
+  uint8_t* sB = smem + 2 * C::BM * C::ROW;
+
+  int tm, tn;
+  tile_coords(tilesM, tilesN, tm, tn);
+  const int m0 = tm * C::BM, n0 = tn * C::BN;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int wm = wid / C::WGN, wn = wid % C::WGN;
+
+  v16f acc[C::MB][C::NB];
+#pragma unroll
+  for (int i = 0; i < C::MB; ++i)
+#pragma unroll
+    for (int j = 0; j < C::NB; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+
+  uint4 ra[C::A_CH], rb[C::B_CH];
+  auto gload = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < C::A_CH; ++i) {
+      const int c = tid + i * C::kThreads;
+      const int row = c / C::CPR, col = (c % C::CPR) * 16;
+      const int gr = m0 + row, gk = k0 + col;
+      const bool ok = gr < M && gk < K;
+      // branch-free edge handling: read a valid address, zero the value
+      uint4 v = *reinterpret_cast<const uint4*>(A + (int64_t)min(gr, M - 1) * lda + min(gk, K - 16));
+      ra[i] = ok ? v : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < C::B_CH; ++i) {
+      const int c = tid + i * C::kThreads;
+      const int row = c / C::CPR, col = (c % C::CPR) * 16;
+      const int gr = n0 + row, gk = k0 + col;
+      const bool ok = gr < N && gk < K;
+      uint4 v = *reinterpret_cast<const uint4*>(B + (int64_t)min(gr, N - 1) * ldb + min(gk, K - 16));
+      rb[i] = ok ? v : make_uint4(0, 0, 0, 0);
+    }
+  };
+  auto sstore = [&](int buf) {
+    uint8_t* a = sA + buf * C::BM * C::ROW;
+    uint8_t* b = sB + buf * C::BN * C::ROW;
+#pragma unroll
+    for (int i = 0; i < C::A_CH; ++i) {
+      const int c = tid + i * C::kThreads;
+      *reinterpret_cast<uint4*>(a + (c / C::CPR) * C::ROW + (c % C::CPR) * 16) = ra[i];
+    }
+#pragma unroll
+    for (int i = 0; i < C::B_CH; ++i) {
+      const int c = tid + i * C::kThreads;
+      *reinterpret_cast<uint4*>(b + (c / C::CPR) * C::ROW + (c % C::CPR) * 16) = rb[i];
+    }
+  };
+
+  const int nk = (K + C::BK - 1) / C::BK;
+  if (nk > 0) {
+    gload(0);
+    sstore(0);
+  }
+  __syncthreads();
+  const int a_off = (wm * C::WTM + (lane & 31)) * C::ROW + (lane >> 5) * 32;
+  const int b_off = (wn * C::WTN + (lane & 31)) * C::ROW + (lane >> 5) * 32;
+  for (int kt = 0; kt < nk; ++kt) {
+    const int cur = kt & 1;
+    if (kt + 1 < nk) gload((kt + 1) * C::BK);
+    const uint8_t* a_base = sA + cur * C::BM * C::ROW + a_off;
+    const uint8_t* b_base = sB + cur * C::BN * C::ROW + b_off;
+#pragma unroll
+    for (int kk = 0; kk < C::BK; kk += 64) {
+      v8i af[C::MB], bf[C::NB];
+#pragma unroll
+      for (int i = 0; i < C::MB; ++i) {
+        const uint8_t* p = a_base + i * 32 * C::ROW + kk;
+        af[i] = join(*reinterpret_cast<const uint4*>(p), *reinterpret_cast<const uint4*>(p + 16));
+      }
+#pragma unroll
+      for (int j = 0; j < C::NB; ++j) {
+        const uint8_t* p = b_base + j * 32 * C::ROW + kk;
+        bf[j] = join(*reinterpret_cast<const uint4*>(p), *reinterpret_cast<const uint4*>(p + 16));
+      }
+#pragma unroll
+      for (int i = 0; i < C::MB; ++i)
+#pragma unroll
+        for (int j = 0; j < C::NB; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[i], bf[j], acc[i][j], 0, 0,
+                                                                      0, 0, 0, 0);
+    }
+    if (kt + 1 < nk) sstore(cur ^ 1);
+    __syncthreads();
+  }
+
+  const float scale = 1.0f / (sa[0] * sb[0]);
+  const int rbase = m0 + wm * C::WTM + 4 * (lane >> 5);
+  const int cbase = n0 + wn * C::WTN + (lane & 31);
+#pragma unroll
+  for (int i = 0; i < C::MB; ++i)
+#pragma unroll
+    for (int j = 0; j < C::NB; ++j) {
+      const int col = cbase + j * 32;
+      if (col >= N) continue;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int row = rbase + i * 32 + 8 * (v >> 2) + (v & 3);
+        if (row < M) Cm[(int64_t)row * ldc + col] = acc[i][j][v] * scale;
+      }
+    }
+}
+
+
+// ---------------------------------------------------------------------------
+// Fast path for K a multiple of 128: direct-to-LDS loads and a two-stage LDS
+// ring, v_mfma_f32_16x16x128_f8f6f4, 8 waves (2 per SIMD) on a 256 x 256
+// tile.
+//
+//  * global_load_lds_dwordx4 moves 16 bytes per lane from global memory
+//    straight into LDS (no staging registers, no LDS write instructions);
+//    it is issued from inline asm so that the compiler does not serialise it
+//    with a full vmcnt wait before every LDS read: completion is tracked with
+//    explicit vmcnt waits, then a bare s_barrier.
+//  * one DMA instruction fills 1 KB = 8 rows of 128 K-bytes; within a row the
+//    16-byte chunk c is stored at slot c ^ ((row >> 1) & 7) so that the 16
+//    lanes that read one fragment column spread over the LDS banks.
+//  * each wave owns a 128 x 64 sub-tile: 8 x 4 blocks of 16 x 16, four fp32
+//    accumulators per lane per block.  A fragment lane l holds row l % 16 and
+//    32 bytes at K offset 32 * (l / 16) of the 128-byte K step; B the same.
+// ---------------------------------------------------------------------------
+namespace dma {
+
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+
+__device__ __forceinline__ void load16_to_lds(const uint8_t* g, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds_addr)
+               : "memory", "m0");
+}
+__device__ __forceinline__ uint32_t lds_offset(const void* p) {
+  return (uint32_t)(uintptr_t)(const lds_u8*)p;
+}
+// wait until at most n vector-memory instructions of this wave are in flight
+__device__ __forceinline__ void wait_vmem(int n) {
+#define FALQ_WVM(k) \
+  case k: __builtin_amdgcn_s_waitcnt(((k) & 0xF) | (((k) >> 4) << 14) | (0x7 << 4) | (0xF << 8)); break;
+  switch (n) {
+    FALQ_WVM(0) FALQ_WVM(8) FALQ_WVM(16) FALQ_WVM(24)
+    default: __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xF << 8)); break;
+  }
+#undef FALQ_WVM
+}
+
+constexpr int BM = 256, BN = 256, BK = 128, WGM = 2, WGN = 4, S = 2;
+constexpr int NW = WGM * WGN, kThreads = NW * 64;
+constexpr int WTM = BM / WGM, WTN = BN / WGN, MB = WTM / 16, NB = WTN / 16;
+constexpr int STAGE = (BM + BN) * BK;
+constexpr int AI = BM * BK / 1024 / NW, BI = BN * BK / 1024 / NW;   // DMA instructions / wave / stage
+constexpr int LPS = AI + BI;
+static_assert(S * STAGE <= 160 * 1024, "LDS");
+
+__global__ __launch_bounds__(kThreads, 1) void gemm_fp8_nt_dma(
+    const uint8_t* __restrict__ A, int64_t lda, const uint8_t* __restrict__ B, int64_t ldb,
+    float* __restrict__ C, int64_t ldc, int M, int N, int K, const float* __restrict__ sa,
+    const float* __restrict__ sb, int tilesM, int tilesN) {
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[S * STAGE];
+  int tm, tn;
+  tile_coords(tilesM, tilesN, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, wm = w / WGN, wn = w % WGN;
+
+  v4f acc[MB][NB];
+#pragma unroll
+  for (int i = 0; i < MB; ++i)
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) acc[i][j][v] = 0.0f;
+
+  // per-lane source of each DMA instruction: row (clamped into the matrix;
+  // rows past M or N are computed and discarded) and the swizzled chunk
+  const int lrow = lane >> 3, lslot = lane & 7;
+  const uint8_t* gA[AI];
+  const uint8_t* gB[BI];
+#pragma unroll
+  for (int j = 0; j < AI; ++j) {
+    const int row = (w * AI + j) * 8 + lrow;
+    gA[j] = A + (int64_t)min(m0 + row, M - 1) * lda + ((lslot ^ ((row >> 1) & 7)) * 16);
+  }
+#pragma unroll
+  for (int j = 0; j < BI; ++j) {
+    const int row = (w * BI + j) * 8 + lrow;
+    gB[j] = B + (int64_t)min(n0 + row, N - 1) * ldb + ((lslot ^ ((row >> 1) & 7)) * 16);
+  }
+  auto issue = [&](int stage, int k0) {
+    const uint32_t base = lds_offset(smem + stage * STAGE);
+    const uint32_t la = __builtin_amdgcn_readfirstlane(base + w * AI * 1024);
+    const uint32_t lb = __builtin_amdgcn_readfirstlane(base + BM * BK + w * BI * 1024);
+#pragma unroll
+    for (int j = 0; j < AI; ++j) load16_to_lds(gA[j] + k0, la + j * 1024);
+#pragma unroll
+    for (int j = 0; j < BI; ++j) load16_to_lds(gB[j] + k0, lb + j * 1024);
+  };
+
+  const int nk = K / BK;
+#pragma unroll
+  for (int s = 0; s < S - 1; ++s)
+    if (s < nk) issue(s, s * BK);
+
+  const int r16 = lane & 15, g = lane >> 4;
+  const int sw = (r16 >> 1) & 7;
+  const int o0 = ((2 * g) ^ sw) * 16, o1 = ((2 * g + 1) ^ sw) * 16;
+  const int offA = (wm * WTM + r16) * BK, offB = BM * BK + (wn * WTN + r16) * BK;
+  for (int kt = 0; kt < nk; ++kt) {
+    // stage kt has landed once at most (stages issued after it) * LPS loads are in flight
+    wait_vmem(min(S - 2, nk - 1 - kt) * LPS);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (kt + S - 1 < nk) issue((kt + S - 1) % S, (kt + S - 1) * BK);
+    const uint8_t* st = smem + (kt % S) * STAGE;
+    v8i bf[NB];
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      const uint8_t* p = st + offB + j * 16 * BK;
+      bf[j] = join(*reinterpret_cast<const uint4*>(p + o0), *reinterpret_cast<const uint4*>(p + o1));
+    }
+#pragma unroll
+    for (int i = 0; i < MB; ++i) {
+      const uint8_t* p = st + offA + i * 16 * BK;
+      const v8i af =
+          join(*reinterpret_cast<const uint4*>(p + o0), *reinterpret_cast<const uint4*>(p + o1));
+#pragma unroll
+      for (int j = 0; j < NB; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af, bf[j], acc[i][j], 0, 0, 0,
+                                                                     0, 0, 0);
+    }
+  }
+
+  const float scale = 1.0f / (sa[0] * sb[0]);
+  const int rbase = m0 + wm * WTM + 4 * (lane >> 4);
+  const int cbase = n0 + wn * WTN + (lane & 15);
+#pragma unroll
+  for (int i = 0; i < MB; ++i)
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+      const int col = cbase + j * 16;
+      if (col >= N) continue;
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int row = rbase + i * 16 + v;
+        if (row < M) C[(int64_t)row * ldc + col] = acc[i][j][v] * scale;
+      }
+    }
+}
+
+}  // namespace dma
+}  // namespace gemm
+}  // namespace falq

@@ -4,38 +4,49 @@
 // rows whose update is large enough to survive FP8 rounding (summary page,
 // key-design paragraph; introduction, method paragraph; rebuttal thread 2,
 // reply W7: merge by top-k row selection).  The rows of B are the proxy: the
-// pending delta of backbone row i is u_i = B_i . A.  Three launches:
+// pending delta of backbone row i is u_i = B_i . A.  Four launches:
 //
-//  proxy_rows<score>  every row: the rank-r chain acc = fmaf(B[i,k], A[k,j],
-//                     acc) for k = 0..r-1 from +0 (the fixed order makes the
-//                     later FP8 rounding reproducible bit for bit), then
-//                     t = fl(s_w * acc), and
-//                     rho_i = max_j |t_ij| * 2^-log2(step_i), where step_i is
-//                     the E4M3 spacing at the row's largest code magnitude;
-//  proxy_select       one workgroup: rho_i >= tau, optionally capped to the
-//                     k_max largest (radix select on the float bits, equal
-//                     scores to the lower row), compacted in row order;
-//  proxy_rows<apply>  selected rows only: recompute t, requantize
-//                     E4M3(fl(dec(q) + t)) in the scaled domain of the fixed
-//                     backbone scale, then zero the row of B.
+//  proxy_clear    zero the per-row maxima (a kernel, not a memset, so that
+//                 the sequence can be captured in a graph);
+//  proxy_score    every element once: the rank-r chain acc = fmaf(B[i,k],
+//                 A[k,j], acc) for k = 0..r-1 from +0 (the fixed order makes
+//                 the FP8 rounding below reproducible bit for bit), then
+//                 t = fl(s_w * acc).  Per row it folds max |t| and the largest
+//                 code magnitude into two arrays with atomicMax on the
+//                 non-negative bit patterns (order independent), and it
+//                 stages the candidate codes E4M3(fl(dec(q) + t)) for every
+//                 element in a workspace copy of the backbone;
+//  proxy_select   one workgroup: rho_i = max|t| / step_i (a power-of-two
+//                 scaling), rho_i >= tau, optionally capped to the k_max
+//                 largest (radix select on the float bits, equal scores to the
+//                 lower row), compacted in row order;
+//  proxy_apply    selected rows only: copy the staged codes into the backbone
+//                 and zero the row of B.
 //
-// Each workgroup owns PR rows; its 256 threads own 4 columns each per
-// 1024-column pass, so every A element loaded (16 B per lane, coalesced) feeds
-// 4 * PR fused multiply-adds and the B values are wave-uniform scalar loads.
-// The chain is VALU work: 2 r flops per backbone byte.
+// proxy_score tiles 64 rows x 256 columns per workgroup: each wave owns 16
+// rows, each lane 4 columns, so a lane keeps 64 accumulators.  A is staged in
+// LDS in slabs of 16 ranks and read as one float4 per rank; the 16 B values
+// of a rank are read as LDS broadcasts.  That is 64 fused multiply-adds per
+// 16 bytes of LDS traffic: the kernel is bound by fp32 VALU issue (2 r flops
+// per backbone byte), which is what the exact, ordered chain costs.
 #include "common.hpp"
 #include "kernels.hpp"
+
+#include <algorithm>
 
 namespace falq {
 namespace {
 
-constexpr int PR = 8;          // rows per workgroup
 constexpr int kThreads = 256;
 constexpr int kSelThreads = 1024;
+constexpr int PRB = 64;          // rows per score workgroup (16 per wave)
+constexpr int PRW = 16;          // rows per wave
+constexpr int PCB = 256;         // columns per score workgroup (4 per lane)
+constexpr int KC = 16;           // ranks per LDS slab
 
 __device__ __forceinline__ uint32_t max_code_mag(uint32_t w, uint32_t m) {
-  uint32_t a = w & 0x7F7F7F7Fu;
-  uint32_t b0 = a & 0xFF, b1 = (a >> 8) & 0xFF, b2 = (a >> 16) & 0xFF, b3 = a >> 24;
+  const uint32_t a = w & 0x7F7F7F7Fu;
+  const uint32_t b0 = a & 0xFF, b1 = (a >> 8) & 0xFF, b2 = (a >> 16) & 0xFF, b3 = a >> 24;
   m = m > b0 ? m : b0;
   m = m > b1 ? m : b1;
   m = m > b2 ? m : b2;
@@ -50,100 +61,116 @@ __device__ __forceinline__ float inv_step_of_code(uint32_t c) {
   return __uint_as_float((uint32_t)(127 + 10 - e) << 23);
 }
 
-template <bool APPLY>
-__global__ __launch_bounds__(kThreads) void proxy_rows(uint8_t* __restrict__ wq,
-                                                       const float* __restrict__ s_w_ptr,
-                                                       const float* __restrict__ A,
-                                                       float* __restrict__ B, int d_in, int d_out,
-                                                       int r, const int32_t* __restrict__ sel,
-                                                       const int32_t* __restrict__ n_sel,
-                                                       float* __restrict__ rho) {
-  int rows[PR];
-  int nrows;
-  if (!APPLY) {
-    const int i0 = blockIdx.x * PR;
-    nrows = min(PR, d_out - i0);
+__global__ void proxy_clear(uint32_t* __restrict__ p, int n) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = 0u;
+}
+
+__global__ __launch_bounds__(kThreads) void proxy_score(const uint8_t* __restrict__ wq,
+                                                        const float* __restrict__ s_w_ptr,
+                                                        const float* __restrict__ A,
+                                                        const float* __restrict__ B, int d_in,
+                                                        int d_out, int r,
+                                                        uint32_t* __restrict__ tmax_bits,
+                                                        uint32_t* __restrict__ cmax,
+                                                        uint8_t* __restrict__ staged) {
+  __shared__ __attribute__((aligned(16))) float sA[2][KC][PCB];         // 32 KB
+  __shared__ __attribute__((aligned(16))) float sB[2][KC][PRB];         // 8 KB, [k][row]
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int row0 = blockIdx.x * PRB, col0 = blockIdx.y * PCB;
+  const int c = col0 + lane * 4;                  // this lane's 4 columns
+  const bool col_ok = c < d_in;
+
+  float acc[PRW][4];
 #pragma unroll
-    for (int ii = 0; ii < PR; ++ii) rows[ii] = i0 + (ii < nrows ? ii : 0);
-  } else {
-    const int n = *n_sel;
-    const int b0 = blockIdx.x * PR;
-    if (b0 >= n) return;
-    nrows = min(PR, n - b0);
+  for (int i = 0; i < PRW; ++i)
 #pragma unroll
-    for (int ii = 0; ii < PR; ++ii) rows[ii] = sel[b0 + (ii < nrows ? ii : 0)];
+    for (int e = 0; e < 4; ++e) acc[i][e] = 0.0f;
+
+  // slab loaders: A[k0..k0+KC) x [col0, col0+256) and B[row0..row0+64) x [k0..k0+KC)
+  float4 ra[4];
+  float rb[4];
+  auto gload = [&](int k0) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int idx = tid + u * kThreads;                    // 0..1023 float4 slots
+      const int kk = idx >> 6, cc = (idx & 63) * 4;
+      const int gk = k0 + kk, gc = col0 + cc;
+      ra[u] = (gk < r && gc < d_in)
+                  ? *reinterpret_cast<const float4*>(A + (int64_t)gk * d_in + gc)
+                  : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int idx = tid + u * kThreads;                    // 0..1023 = 64 rows x 16 k
+      const int rr = idx >> 4, kk = idx & 15;
+      const int gr = row0 + rr, gk = k0 + kk;
+      rb[u] = (gr < d_out && gk < r) ? B[(int64_t)gr * r + gk] : 0.0f;
+    }
+  };
+  auto sstore = [&](int buf) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int idx = tid + u * kThreads;
+      *reinterpret_cast<float4*>(&sA[buf][idx >> 6][(idx & 63) * 4]) = ra[u];
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int idx = tid + u * kThreads;
+      sB[buf][idx & 15][idx >> 4] = rb[u];
+    }
+  };
+
+  const int nslab = (r + KC - 1) / KC;
+  if (nslab > 0) {
+    gload(0);
+    sstore(0);
   }
-  const float s_w = *s_w_ptr;
-  const int tid = threadIdx.x;
-  float tmax[PR];
-  uint32_t cmax[PR];
+  __syncthreads();
+  for (int s = 0; s < nslab; ++s) {
+    const int cur = s & 1;
+    if (s + 1 < nslab) gload((s + 1) * KC);
+    const int kn = min(KC, r - s * KC);                      // ranks in this slab (ascending k)
+    for (int kk = 0; kk < kn; ++kk) {
+      const float4 a = *reinterpret_cast<const float4*>(&sA[cur][kk][lane * 4]);
+      const float4* bp = reinterpret_cast<const float4*>(&sB[cur][kk][w * PRW]);
+      const float4 b0 = bp[0], b1 = bp[1], b2 = bp[2], b3 = bp[3];
+      const float bv[PRW] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w,
+                             b2.x, b2.y, b2.z, b2.w, b3.x, b3.y, b3.z, b3.w};
 #pragma unroll
-  for (int ii = 0; ii < PR; ++ii) { tmax[ii] = 0.0f; cmax[ii] = 0; }
-
-  const float* Brow[PR];
-#pragma unroll
-  for (int ii = 0; ii < PR; ++ii) Brow[ii] = B + (int64_t)rows[ii] * r;
-
-  for (int c0 = tid * 4; c0 < d_in; c0 += kThreads * 4) {
-    float acc[PR][4];
-#pragma unroll
-    for (int ii = 0; ii < PR; ++ii)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) acc[ii][e] = 0.0f;
-    const float* Ac = A + c0;
-    for (int k = 0; k < r; ++k) {
-      const float4 a = *reinterpret_cast<const float4*>(Ac + (int64_t)k * d_in);
-#pragma unroll
-      for (int ii = 0; ii < PR; ++ii) {
-        const float b = Brow[ii][k];
-        acc[ii][0] = __builtin_fmaf(b, a.x, acc[ii][0]);
-        acc[ii][1] = __builtin_fmaf(b, a.y, acc[ii][1]);
-        acc[ii][2] = __builtin_fmaf(b, a.z, acc[ii][2]);
-        acc[ii][3] = __builtin_fmaf(b, a.w, acc[ii][3]);
+      for (int i = 0; i < PRW; ++i) {
+        acc[i][0] = __builtin_fmaf(bv[i], a.x, acc[i][0]);
+        acc[i][1] = __builtin_fmaf(bv[i], a.y, acc[i][1]);
+        acc[i][2] = __builtin_fmaf(bv[i], a.z, acc[i][2]);
+        acc[i][3] = __builtin_fmaf(bv[i], a.w, acc[i][3]);
       }
     }
-#pragma unroll
-    for (int ii = 0; ii < PR; ++ii) {
-      if (ii >= nrows) break;
-      uint32_t* qp = reinterpret_cast<uint32_t*>(wq + (int64_t)rows[ii] * d_in + c0);
-      const uint32_t codes = *qp;
-      const float t0 = s_w * acc[ii][0], t1 = s_w * acc[ii][1];
-      const float t2 = s_w * acc[ii][2], t3 = s_w * acc[ii][3];
-      if (!APPLY) {
-        tmax[ii] = fmaxf(tmax[ii], fmaxf(fmaxf(fabsf(t0), fabsf(t1)), fmaxf(fabsf(t2), fabsf(t3))));
-        cmax[ii] = max_code_mag(codes, cmax[ii]);
-      } else {
-        const float2 lo = dec2(codes, false), hi = dec2(codes, true);
-        *qp = enc4(lo.x + t0, lo.y + t1, hi.x + t2, hi.y + t3);
-      }
-    }
-  }
-
-  if (!APPLY) {
-    __shared__ float st[kThreads / 64][PR];
-    __shared__ uint32_t sc[kThreads / 64][PR];
-    const int w = tid >> 6;
-#pragma unroll
-    for (int ii = 0; ii < PR; ++ii) {
-      const float tm = wave_max_f32(tmax[ii]);
-      const uint32_t cm = wave_max_u32(cmax[ii]);
-      if ((tid & 63) == 0) { st[w][ii] = tm; sc[w][ii] = cm; }
-    }
+    if (s + 1 < nslab) sstore(cur ^ 1);
     __syncthreads();
-    if (tid < nrows) {
-      float tm = st[0][tid];
-      uint32_t cm = sc[0][tid];
+  }
+
+  const float s_w = *s_w_ptr;
 #pragma unroll
-      for (int k = 1; k < kThreads / 64; ++k) {
-        tm = fmaxf(tm, st[k][tid]);
-        cm = cm > sc[k][tid] ? cm : sc[k][tid];
-      }
-      rho[rows[0] + tid] = tm * inv_step_of_code(cm);
+  for (int i = 0; i < PRW; ++i) {
+    const int row = row0 + w * PRW + i;
+    if (row >= d_out) break;                                 // wave-uniform
+    float tm = 0.0f;
+    uint32_t cm = 0;
+    if (col_ok) {
+      const uint32_t codes = *reinterpret_cast<const uint32_t*>(wq + (int64_t)row * d_in + c);
+      const float t0 = s_w * acc[i][0], t1 = s_w * acc[i][1];
+      const float t2 = s_w * acc[i][2], t3 = s_w * acc[i][3];
+      tm = fmaxf(fmaxf(fabsf(t0), fabsf(t1)), fmaxf(fabsf(t2), fabsf(t3)));
+      cm = max_code_mag(codes, 0u);
+      const float2 lo = dec2(codes, false), hi = dec2(codes, true);
+      *reinterpret_cast<uint32_t*>(staged + (int64_t)row * d_in + c) =
+          enc4(lo.x + t0, lo.y + t1, hi.x + t2, hi.y + t3);
     }
-  } else {
-    __syncthreads();                       // every wave is done reading these B rows
-    for (int ii = 0; ii < nrows; ++ii)
-      for (int k = tid; k < r; k += kThreads) B[(int64_t)rows[ii] * r + k] = 0.0f;
+    const uint32_t tb = wave_max_u32(__float_as_uint(tm));   // |t| >= 0: bit order = value order
+    const uint32_t cb = wave_max_u32(cm);
+    if (lane == 0) {
+      atomicMax(&tmax_bits[row], tb);
+      atomicMax(&cmax[row], cb);
+    }
   }
 }
 
@@ -169,7 +196,10 @@ __device__ int block_excl_scan(int v, int* smem16, int* total) {
   return base + x - v;
 }
 
-__global__ __launch_bounds__(kSelThreads) void proxy_select(const float* __restrict__ rho, int d_out,
+// rho_i from the folded maxima; written to rho[] for every row
+__global__ __launch_bounds__(kSelThreads) void proxy_select(const uint32_t* __restrict__ tmax_bits,
+                                                            const uint32_t* __restrict__ cmax,
+                                                            float* __restrict__ rho, int d_out,
                                                             float tau, int k_max,
                                                             int32_t* __restrict__ sel,
                                                             int32_t* __restrict__ n_sel) {
@@ -179,14 +209,18 @@ __global__ __launch_bounds__(kSelThreads) void proxy_select(const float* __restr
   __shared__ int s_need;
   const int tid = threadIdx.x;
 
-  // candidates: rho >= tau (false for NaN)
   int cnt = 0;
-  for (int i = tid; i < d_out; i += kSelThreads) cnt += (rho[i] >= tau) ? 1 : 0;
+  for (int i = tid; i < d_out; i += kSelThreads) {
+    const float x = __uint_as_float(tmax_bits[i]) * inv_step_of_code(cmax[i]);
+    rho[i] = x;
+    cnt += (x >= tau) ? 1 : 0;
+  }
+  __syncthreads();                     // rho[] written by this workgroup, read back below
   int total;
   block_excl_scan(cnt, s16, &total);
 
-  uint32_t key_star = 0;    // k-th largest key (cap case)
-  int need_eq = 0;          // how many rows with key == key_star to keep
+  uint32_t key_star = 0;               // k-th largest score (cap case)
+  int need_eq = 0;                     // rows with score == key_star to keep
   const bool capped = k_max > 0 && total > k_max;
   if (capped) {
     if (tid == 0) { s_prefix = 0; s_need = k_max; }
@@ -247,6 +281,23 @@ __global__ __launch_bounds__(kSelThreads) void proxy_select(const float* __restr
   if (tid == 0) *n_sel = written;
 }
 
+// one selected row per wave: copy the staged codes, zero the B row
+__global__ __launch_bounds__(kThreads) void proxy_apply(uint8_t* __restrict__ wq,
+                                                        const uint8_t* __restrict__ staged,
+                                                        float* __restrict__ B, int d_in, int r,
+                                                        const int32_t* __restrict__ sel,
+                                                        const int32_t* __restrict__ n_sel) {
+  const int n = *n_sel;
+  const int lane = threadIdx.x & 63;
+  const int e = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+  if (e >= n) return;
+  const int64_t row = sel[e];
+  const uint4* src = reinterpret_cast<const uint4*>(staged + row * d_in);
+  uint4* dst = reinterpret_cast<uint4*>(wq + row * d_in);
+  for (int j = lane; j < d_in / 16; j += 64) dst[j] = src[j];
+  for (int k = lane; k < r; k += 64) B[row * r + k] = 0.0f;
+}
+
 __global__ __launch_bounds__(256) void sgd_kernel(float* __restrict__ p, const float* __restrict__ g,
                                                   int64_t n, float lr) {
   const int64_t n4 = n / 4;
@@ -264,28 +315,55 @@ __global__ __launch_bounds__(256) void sgd_kernel(float* __restrict__ p, const f
     for (int64_t i = n4 * 4 + threadIdx.x; i < n; i += blockDim.x) p[i] = p[i] - lr * g[i];
 }
 
+struct ProxyWs {
+  size_t off_tmax, off_cmax, off_rho, off_staged, total;
+};
+
+ProxyWs proxy_layout(int64_t d_in, int64_t d_out) {
+  ProxyWs p{};
+  size_t o = 0;
+  auto take = [&](size_t bytes) { size_t at = o; o = align_up(o + bytes, 256); return at; };
+  p.off_tmax = take((size_t)d_out * 4);
+  p.off_cmax = take((size_t)d_out * 4);
+  p.off_rho = take((size_t)d_out * 4);
+  p.off_staged = take((size_t)d_out * (size_t)d_in);
+  p.total = o;
+  return p;
+}
+
 }  // namespace
 
 size_t proxy_ws_bytes(int64_t d_in, int64_t d_out, int64_t r) {
-  (void)d_in;
   (void)r;
-  return align_up((size_t)d_out * 4, 256);
+  return proxy_layout(d_in, d_out).total;
 }
 
 hipError_t launch_proxy_update(uint8_t* wq, const float* s_w, const float* A, float* B,
                                int64_t d_in, int64_t d_out, int64_t r, float tau, int64_t k_max,
                                int32_t* sel_idx, int32_t* n_sel, float* rho, void* ws,
                                hipStream_t s) {
-  float* rr = rho ? rho : reinterpret_cast<float*>(ws);
-  const int blocks = (int)((d_out + PR - 1) / PR);
+  const ProxyWs L = proxy_layout(d_in, d_out);
+  uint8_t* base = reinterpret_cast<uint8_t*>(ws);
+  uint32_t* tmax = reinterpret_cast<uint32_t*>(base + L.off_tmax);
+  uint32_t* cmax = reinterpret_cast<uint32_t*>(base + L.off_cmax);
+  float* rr = rho ? rho : reinterpret_cast<float*>(base + L.off_rho);
+  uint8_t* staged = base + L.off_staged;
   if (d_out > 0) {
-    proxy_rows<false><<<blocks, kThreads, 0, s>>>(wq, s_w, A, B, (int)d_in, (int)d_out, (int)r,
-                                                  nullptr, nullptr, rr);
+    // tmax and cmax are adjacent: one clear covers both (the gap is padding)
+    const int nclear = (int)((L.off_cmax - L.off_tmax) / 4 + d_out);
+    proxy_clear<<<std::min(64, (nclear + 255) / 256), 256, 0, s>>>(tmax, nclear);
+    if (d_in > 0) {
+      dim3 grid((unsigned)((d_out + PRB - 1) / PRB), (unsigned)((d_in + PCB - 1) / PCB));
+      proxy_score<<<grid, kThreads, 0, s>>>(wq, s_w, A, B, (int)d_in, (int)d_out, (int)r, tmax,
+                                            cmax, staged);
+    }
   }
-  proxy_select<<<1, kSelThreads, 0, s>>>(rr, (int)d_out, tau, (int)k_max, sel_idx, n_sel);
+  proxy_select<<<1, kSelThreads, 0, s>>>(tmax, cmax, rr, (int)d_out, tau, (int)k_max, sel_idx,
+                                         n_sel);
   if (d_out > 0) {
-    proxy_rows<true><<<blocks, kThreads, 0, s>>>(wq, s_w, A, B, (int)d_in, (int)d_out, (int)r,
-                                                 sel_idx, n_sel, nullptr);
+    const int rows_per_block = kThreads / 64;
+    proxy_apply<<<(unsigned)((d_out + rows_per_block - 1) / rows_per_block), kThreads, 0, s>>>(
+        wq, staged, B, (int)d_in, (int)r, sel_idx, n_sel);
   }
   return hipGetLastError();
 }

@@ -22,7 +22,7 @@ namespace falq {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kUnroll = 4;
+constexpr int kUnroll = 8;
 
 template <int DT> struct Vec;
 template <> struct Vec<0> {  // float32: 4 elements per 16-byte load

@@ -50,6 +50,8 @@ SHAPES = [  # (T, d_in, d_out, r): full tiles, ragged tails in every dimension, 
     (1, 16, 16, 1),
     (3, 48, 32, 70),
     (1000, 256, 1536, 128),
+    (300, 384, 640, 8),      # K % 128 == 0 in both products: fast path with ragged M and N
+    (513, 1152, 1280, 64),
 ]
 
 
