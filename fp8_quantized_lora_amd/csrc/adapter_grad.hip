@@ -217,114 +217,146 @@ __global__ __launch_bounds__(kThreads) void skinny_kernel(Prob p0, Prob p1) {
 }
 
 // fp32 [rows x cols] -> bf16 hi/lo, optionally transposed ([cols x ld_out]).
-__global__ __launch_bounds__(256) void split_bf16_kernel(const float* __restrict__ src, int rows,
-                                                         int cols, bool transpose, int64_t ld_out,
-                                                         uint16_t* __restrict__ hi,
-                                                         uint16_t* __restrict__ lo) {
+// Two problems per launch (blockIdx.z), 32 x 32 tiles.
+struct Split {
+  const float* src;
+  int rows, cols;
+  bool transpose;
+  int64_t ld_out;
+  uint16_t* hi;
+  uint16_t* lo;
+  int tx, ty;          // tiles along cols, rows
+};
+
+__global__ __launch_bounds__(256) void split_bf16_kernel(Split p0, Split p1) {
+  const Split p = blockIdx.z == 0 ? p0 : p1;
+  if ((int)blockIdx.x >= p.tx * p.ty) return;
   __shared__ float t[32][33];
-  const int r0 = blockIdx.y * 32, c0 = blockIdx.x * 32;
+  const int r0 = ((int)blockIdx.x / p.tx) * 32, c0 = ((int)blockIdx.x % p.tx) * 32;
   const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;   // 32 x 8
-  if (!transpose) {
+  if (!p.transpose) {
     for (int rr = ty; rr < 32; rr += 8) {
       const int r = r0 + rr, c = c0 + tx;
-      if (r < rows && c < cols) {
-        const float x = src[(int64_t)r * cols + c];
+      if (r < p.rows && c < p.cols) {
+        const float x = p.src[(int64_t)r * p.cols + c];
         const uint16_t h = bf16_rne(x);
-        hi[(int64_t)r * ld_out + c] = h;
-        lo[(int64_t)r * ld_out + c] = bf16_rne(x - bf16_to_f32(h));
+        p.hi[(int64_t)r * p.ld_out + c] = h;
+        p.lo[(int64_t)r * p.ld_out + c] = bf16_rne(x - bf16_to_f32(h));
       }
     }
     return;
   }
   for (int rr = ty; rr < 32; rr += 8) {
     const int r = r0 + rr, c = c0 + tx;
-    t[rr][tx] = (r < rows && c < cols) ? src[(int64_t)r * cols + c] : 0.0f;
+    t[rr][tx] = (r < p.rows && c < p.cols) ? p.src[(int64_t)r * p.cols + c] : 0.0f;
   }
   __syncthreads();
   for (int cc = ty; cc < 32; cc += 8) {
     const int c = c0 + cc, r = r0 + tx;
-    if (c < cols && r < rows) {
+    if (c < p.cols && r < p.rows) {
       const float x = t[tx][cc];
       const uint16_t h = bf16_rne(x);
-      hi[(int64_t)c * ld_out + r] = h;
-      lo[(int64_t)c * ld_out + r] = bf16_rne(x - bf16_to_f32(h));
+      p.hi[(int64_t)c * p.ld_out + r] = h;
+      p.lo[(int64_t)c * p.ld_out + r] = bf16_rne(x - bf16_to_f32(h));
     }
   }
 }
 
 // out = (1/ *sc) * sum_s P[s] with P[s] of shape [M x N], folded in split
-// order s = 0, 1, ... (deterministic).  A workgroup owns a 64 (m) x 64 (n)
-// tile: float4 loads along n, the tile transposed through LDS when the output
-// is n-major.
+// order s = 0, 1, ... (deterministic).  A workgroup owns a 16 (m) x 64 (n)
+// tile, one float4 of it per thread, transposed through LDS when the output
+// is n-major.  Two problems per launch (blockIdx.z).
 //   mode 0: out_f32[m * ldo + n]           (dB)
 //   mode 1: out_f32[n * ldo + m]           (dA)
 //   mode 2: hi/lo bf16 [n * ldo + m], and zeros for M <= m < Mpad   (U^T, V^T)
-__global__ __launch_bounds__(256) void reduce_kernel(const float* __restrict__ P, int S, int M, int N,
-                                                     int Mpad, const float* __restrict__ sc, int mode,
-                                                     float* __restrict__ out, int64_t ldo,
-                                                     uint16_t* __restrict__ ohi,
-                                                     uint16_t* __restrict__ olo) {
-  __shared__ float t[64][65];
-  const int m0 = blockIdx.y * 64, n0 = blockIdx.x * 64;
+struct Red {
+  const float* P;
+  int S, M, N, Mpad;
+  const float* sc;
+  int mode;
+  float* out;
+  int64_t ldo;
+  uint16_t* ohi;
+  uint16_t* olo;
+  int tilesM, tilesN;
+};
+
+constexpr int RM = 16;   // rows of a reduction tile
+
+__global__ __launch_bounds__(256) void reduce_kernel(Red r0, Red r1) {
+  const Red R = blockIdx.z == 0 ? r0 : r1;
+  const int tile = blockIdx.x;
+  if (tile >= R.tilesM * R.tilesN) return;
+  const int m0 = (tile % R.tilesM) * RM, n0 = (tile / R.tilesM) * 64;
+  __shared__ float t[64][RM + 1];
   const int tid = threadIdx.x;
-  const float scale = 1.0f / sc[0];
-  const int64_t plane = (int64_t)M * N;
-  const bool vec = (N % 4) == 0;
-#pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int idx = tid + u * 256;            // 0..1023: 64 rows x 16 float4
-    const int mm = idx >> 4, nn = (idx & 15) * 4;
-    const int m = m0 + mm, n = n0 + nn;
-    float v[4] = {0.f, 0.f, 0.f, 0.f};
-    if (m < M) {
-      const int64_t off = (int64_t)m * N + n;
-      if (vec && n + 3 < N) {
-        for (int s = 0; s < S; ++s) {
-          const float4 x = *reinterpret_cast<const float4*>(P + s * plane + off);
-          v[0] += x.x; v[1] += x.y; v[2] += x.z; v[3] += x.w;
-        }
-      } else {
-        for (int s = 0; s < S; ++s)
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (n + e < N) v[e] += P[s * plane + off + e];
-      }
-    }
-#pragma unroll
-    for (int e = 0; e < 4; ++e) v[e] *= scale;
-    if (mode == 0) {
-      if (m < M) {
-        if (vec && n + 3 < N && (ldo % 4) == 0) {
-          *reinterpret_cast<float4*>(out + (int64_t)m * ldo + n) = make_float4(v[0], v[1], v[2], v[3]);
-        } else {
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (n + e < N) out[(int64_t)m * ldo + n + e] = v[e];
-        }
+  const float scale = 1.0f / R.sc[0];
+  const int64_t plane = (int64_t)R.M * R.N;
+  const bool vec = (R.N % 4) == 0;
+  const int mm = tid >> 4, nn = (tid & 15) * 4;
+  const int m = m0 + mm, n = n0 + nn;
+  float v[4] = {0.f, 0.f, 0.f, 0.f};
+  if (m < R.M && n < R.N) {
+    const int64_t off = (int64_t)m * R.N + n;
+    if (vec) {
+      for (int s = 0; s < R.S; ++s) {
+        const float4 x = *reinterpret_cast<const float4*>(R.P + s * plane + off);
+        v[0] += x.x; v[1] += x.y; v[2] += x.z; v[3] += x.w;
       }
     } else {
+      for (int s = 0; s < R.S; ++s)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) t[nn + e][mm] = v[e];
+        for (int e = 0; e < 4; ++e)
+          if (n + e < R.N) v[e] += R.P[s * plane + off + e];
     }
   }
-  if (mode == 0) return;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) v[e] *= scale;
+  if (R.mode == 0) {
+    if (m < R.M) {
+      if (vec && n < R.N && (R.ldo % 4) == 0) {
+        *reinterpret_cast<float4*>(R.out + (int64_t)m * R.ldo + n) = make_float4(v[0], v[1], v[2], v[3]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (n + e < R.N) R.out[(int64_t)m * R.ldo + n + e] = v[e];
+      }
+    }
+    return;
+  }
+#pragma unroll
+  for (int e = 0; e < 4; ++e) t[nn + e][mm] = v[e];
   __syncthreads();
-  // write n-major rows: 64 consecutive m per row
 #pragma unroll
-  for (int u = 0; u < 16; ++u) {
-    const int idx = tid + u * 256;            // 0..4095: 64 rows (n) x 64 m
-    const int nn = idx >> 6, mm = idx & 63;
-    const int n = n0 + nn, m = m0 + mm;
-    if (n >= N) continue;
-    const float v = t[nn][mm];
-    if (mode == 1) {
-      if (m < M) out[(int64_t)n * ldo + m] = v;
-    } else if (m < Mpad) {
-      const uint16_t h = bf16_rne(v);
-      ohi[(int64_t)n * ldo + m] = h;
-      olo[(int64_t)n * ldo + m] = bf16_rne(v - bf16_to_f32(h));
+  for (int u = 0; u < 4; ++u) {
+    const int idx = tid + u * 256;            // 64 rows (n) x 16 m
+    const int tn = idx >> 4, tm = idx & 15;
+    const int nn2 = n0 + tn, mm2 = m0 + tm;
+    if (nn2 >= R.N) continue;
+    const float x = t[tn][tm];
+    if (R.mode == 1) {
+      if (mm2 < R.M) R.out[(int64_t)nn2 * R.ldo + mm2] = x;
+    } else if (mm2 < R.Mpad) {
+      const uint16_t h = bf16_rne(x);
+      R.ohi[(int64_t)nn2 * R.ldo + mm2] = h;
+      R.olo[(int64_t)nn2 * R.ldo + mm2] = bf16_rne(x - bf16_to_f32(h));
     }
   }
+}
+
+Red red(const float* P, int S, int64_t M, int64_t N, int64_t Mpad, const float* sc, int mode,
+        float* out, int64_t ldo, uint16_t* ohi, uint16_t* olo) {
+  Red r;
+  r.P = P; r.S = S; r.M = (int)M; r.N = (int)N; r.Mpad = (int)Mpad; r.sc = sc; r.mode = mode;
+  r.out = out; r.ldo = ldo; r.ohi = ohi; r.olo = olo;
+  r.tilesM = (int)((std::max(M, Mpad) + RM - 1) / RM);
+  r.tilesN = (int)((N + 63) / 64);
+  return r;
+}
+
+void launch_reduce(const Red& a, const Red* b, hipStream_t s) {
+  const int tiles = std::max(a.tilesM * a.tilesN, b ? b->tilesM * b->tilesN : 0);
+  reduce_kernel<<<dim3(tiles, 1, b ? 2 : 1), 256, 0, s>>>(a, b ? *b : a);
 }
 
 __global__ void fill_kernel(float* p, int64_t n, float v) {
@@ -427,11 +459,14 @@ hipError_t launch_adapter_grads(const uint8_t* gq, const float* s_g, const uint8
   const bool want_da = dA != nullptr;
 
   // 0. float operands -> bf16 hi/lo: A as is [r x d_in]; B transposed [r x d_out]
-  split_bf16_kernel<<<dim3(ceil_div(d_in, 32), ceil_div(r, 32)), 256, 0, s>>>(
-      A, (int)r, (int)d_in, false, d_in, u16(pl.off_ahi), u16(pl.off_alo));
-  if (want_da)
-    split_bf16_kernel<<<dim3(ceil_div(r, 32), ceil_div(d_out, 32)), 256, 0, s>>>(
-        B, (int)d_out, (int)r, true, d_out, u16(pl.off_bhi), u16(pl.off_blo));
+  {
+    Split sa{A, (int)r, (int)d_in, false, d_in, u16(pl.off_ahi), u16(pl.off_alo),
+             ceil_div(d_in, 32), ceil_div(r, 32)};
+    Split sb{B, (int)d_out, (int)r, true, d_out, u16(pl.off_bhi), u16(pl.off_blo),
+             ceil_div(r, 32), ceil_div(d_out, 32)};
+    const int tiles = std::max(sa.tx * sa.ty, want_da ? sb.tx * sb.ty : 0);
+    split_bf16_kernel<<<dim3(tiles, 1, want_da ? 2 : 1), 256, 0, s>>>(sa, sb);
+  }
 
   // 1. U = dec(X~) A^T, V = dec(G~) B  (partials over d)
   Prob pu = prob(xq, d_in, u16(pl.off_ahi), u16(pl.off_alo), d_in, f32(pl.off_p1u), T, r, d_in,
@@ -443,13 +478,13 @@ hipError_t launch_adapter_grads(const uint8_t* gq, const float* s_g, const uint8
     skinny_kernel<false><<<grid, kThreads, 0, s>>>(pu, pv);
   }
   // reduce -> U^T, V^T as bf16 hi/lo [r x Tp], scaled by 1/s_x, 1/s_g
-  reduce_kernel<<<dim3(ceil_div(r, 64), ceil_div(pl.Tp, 64)), 256, 0, s>>>(
-      f32(pl.off_p1u), pl.S1, (int)T, (int)r, (int)pl.Tp, s_x, 2, nullptr, pl.Tp, u16(pl.off_uhi),
-      u16(pl.off_ulo));
-  if (want_da)
-    reduce_kernel<<<dim3(ceil_div(r, 64), ceil_div(pl.Tp, 64)), 256, 0, s>>>(
-        f32(pl.off_p1v), pl.S1, (int)T, (int)r, (int)pl.Tp, s_g, 2, nullptr, pl.Tp,
-        u16(pl.off_vhi), u16(pl.off_vlo));
+  {
+    const Red ru = red(f32(pl.off_p1u), pl.S1, T, r, pl.Tp, s_x, 2, nullptr, pl.Tp,
+                       u16(pl.off_uhi), u16(pl.off_ulo));
+    const Red rv = red(f32(pl.off_p1v), pl.S1, T, r, pl.Tp, s_g, 2, nullptr, pl.Tp,
+                       u16(pl.off_vhi), u16(pl.off_vlo));
+    launch_reduce(ru, want_da ? &rv : nullptr, s);
+  }
 
   // 2. dB = dec(G~)^T U, dA^T = dec(X~)^T V  (contract over tokens, partials over T)
   Prob pb = prob(gq, d_out, u16(pl.off_uhi), u16(pl.off_ulo), pl.Tp, f32(pl.off_p2b), d_out, r,
@@ -461,11 +496,11 @@ hipError_t launch_adapter_grads(const uint8_t* gq, const float* s_g, const uint8
     dim3 grid(tiles, pl.S2, want_da ? 2 : 1);
     skinny_kernel<true><<<grid, kThreads, 0, s>>>(pb, pa);
   }
-  reduce_kernel<<<dim3(ceil_div(r, 64), ceil_div(d_out, 64)), 256, 0, s>>>(
-      f32(pl.off_p2b), pl.S2, (int)d_out, (int)r, (int)d_out, s_g, 0, dB, r, nullptr, nullptr);
-  if (want_da)
-    reduce_kernel<<<dim3(ceil_div(r, 64), ceil_div(d_in, 64)), 256, 0, s>>>(
-        f32(pl.off_p2a), pl.S2, (int)d_in, (int)r, (int)d_in, s_x, 1, dA, d_in, nullptr, nullptr);
+  {
+    const Red rb = red(f32(pl.off_p2b), pl.S2, d_out, r, d_out, s_g, 0, dB, r, nullptr, nullptr);
+    const Red ra = red(f32(pl.off_p2a), pl.S2, d_in, r, d_in, s_x, 1, dA, d_in, nullptr, nullptr);
+    launch_reduce(rb, want_da ? &ra : nullptr, s);
+  }
   return hipGetLastError();
 }
 

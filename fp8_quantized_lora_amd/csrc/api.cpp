@@ -133,10 +133,8 @@ falq_status adapter_step(float* A, float* B, const float* dA, const float* dB, i
   if (r * d_in > 0 && (!need(A) || !opt(dA))) return FALQ_EINVAL;
   if (r * d_out > 0 && (!need(B) || !need(dB))) return FALQ_EINVAL;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  hipError_t e = hipSuccess;
-  if (dA && r * d_in > 0) e = falq::launch_sgd(A, dA, r * d_in, lr, s);
-  if (e == hipSuccess && r * d_out > 0) e = falq::launch_sgd(B, dB, r * d_out, lr, s);
-  return hip_status(e);
+  const int64_t na = dA ? r * d_in : 0;
+  return hip_status(falq::launch_sgd2(A, dA, na, B, dB, r * d_out, lr, s));
 }
 
 size_t rowwise_proxy_update_workspace_bytes(int64_t d_in, int64_t d_out, int64_t r) {

@@ -9,7 +9,7 @@
 namespace falq {
 
 // ---- fp8_quantize: amax partials + cast ---------------------------------
-constexpr int kQzMaxParts = 1024;
+constexpr int kQzMaxParts = 2048;
 size_t quantize_ws_bytes();
 hipError_t launch_quantize(const void* x, int dtype, int64_t n, const float* scale_in,
                            uint8_t* q, float* scale, float* amax, int32_t* nonfinite,
@@ -32,7 +32,9 @@ hipError_t launch_adapter_grads(const uint8_t* gq, const float* s_g, const uint8
                                 float* dA, float* dB, void* ws, hipStream_t s);
 
 // ---- SGD ------------------------------------------------------------------
-hipError_t launch_sgd(float* p, const float* g, int64_t n, float lr, hipStream_t s);
+// two tensors in one launch (either may be empty); 16-byte aligned pointers
+hipError_t launch_sgd2(float* pa, const float* ga, int64_t na, float* pb, const float* gb,
+                       int64_t nb, float lr, hipStream_t s);
 
 // ---- row-wise proxy update -------------------------------------------------
 size_t proxy_ws_bytes(int64_t d_in, int64_t d_out, int64_t r);

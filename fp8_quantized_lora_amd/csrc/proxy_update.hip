@@ -4,19 +4,18 @@
 // rows whose update is large enough to survive FP8 rounding (summary page,
 // key-design paragraph; introduction, method paragraph; rebuttal thread 2,
 // reply W7: merge by top-k row selection).  The rows of B are the proxy: the
-// pending delta of backbone row i is u_i = B_i . A.  Four launches:
+// pending delta of backbone row i is u_i = B_i . A.  Three launches:
 //
-//  proxy_clear    zero the per-row maxima (a kernel, not a memset, so that
-//                 the sequence can be captured in a graph);
 //  proxy_score    every element once: the rank-r chain acc = fmaf(B[i,k],
 //                 A[k,j], acc) for k = 0..r-1 from +0 (the fixed order makes
 //                 the FP8 rounding below reproducible bit for bit), then
-//                 t = fl(s_w * acc).  Per row it folds max |t| and the largest
-//                 code magnitude into two arrays with atomicMax on the
-//                 non-negative bit patterns (order independent), and it
-//                 stages the candidate codes E4M3(fl(dec(q) + t)) for every
+//                 t = fl(s_w * acc).  Each workgroup writes, per row, the max
+//                 |t| and the largest code magnitude of its 256 columns, and
+//                 it stages the candidate codes E4M3(fl(dec(q) + t)) for every
 //                 element in a workspace copy of the backbone;
-//  proxy_select   one workgroup: rho_i = max|t| / step_i (a power-of-two
+//  proxy_select   one workgroup: folds the per-column-block maxima (a max of
+//                 non-negative bit patterns, order independent), then
+//                 rho_i = max|t| / step_i (a power-of-two
 //                 scaling), rho_i >= tau, optionally capped to the k_max
 //                 largest (radix select on the float bits, equal scores to the
 //                 lower row), compacted in row order;
@@ -61,17 +60,13 @@ __device__ __forceinline__ float inv_step_of_code(uint32_t c) {
   return __uint_as_float((uint32_t)(127 + 10 - e) << 23);
 }
 
-__global__ void proxy_clear(uint32_t* __restrict__ p, int n) {
-  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) p[i] = 0u;
-}
-
 __global__ __launch_bounds__(kThreads) void proxy_score(const uint8_t* __restrict__ wq,
                                                         const float* __restrict__ s_w_ptr,
                                                         const float* __restrict__ A,
                                                         const float* __restrict__ B, int d_in,
                                                         int d_out, int r,
-                                                        uint32_t* __restrict__ tmax_bits,
-                                                        uint32_t* __restrict__ cmax,
+                                                        uint32_t* __restrict__ tmax_part,
+                                                        uint32_t* __restrict__ cmax_part,
                                                         uint8_t* __restrict__ staged) {
   __shared__ __attribute__((aligned(16))) float sA[2][KC][PCB];         // 32 KB
   __shared__ __attribute__((aligned(16))) float sB[2][KC][PRB];         // 8 KB, [k][row]
@@ -167,9 +162,9 @@ __global__ __launch_bounds__(kThreads) void proxy_score(const uint8_t* __restric
     }
     const uint32_t tb = wave_max_u32(__float_as_uint(tm));   // |t| >= 0: bit order = value order
     const uint32_t cb = wave_max_u32(cm);
-    if (lane == 0) {
-      atomicMax(&tmax_bits[row], tb);
-      atomicMax(&cmax[row], cb);
+    if (lane == 0) {                                         // this column block's share of the row
+      tmax_part[(int64_t)blockIdx.y * d_out + row] = tb;
+      cmax_part[(int64_t)blockIdx.y * d_out + row] = cb;
     }
   }
 }
@@ -196,11 +191,13 @@ __device__ int block_excl_scan(int v, int* smem16, int* total) {
   return base + x - v;
 }
 
-// rho_i from the folded maxima; written to rho[] for every row
-__global__ __launch_bounds__(kSelThreads) void proxy_select(const uint32_t* __restrict__ tmax_bits,
-                                                            const uint32_t* __restrict__ cmax,
-                                                            float* __restrict__ rho, int d_out,
-                                                            float tau, int k_max,
+// rho_i from the per-column-block maxima, written to rho[] for every row;
+// then the selection.  Thread t owns rows [t*R, t*R + R), R = ceil(d_out/1024),
+// so one block-wide scan orders the uncapped selection.
+__global__ __launch_bounds__(kSelThreads) void proxy_select(const uint32_t* __restrict__ tmax_part,
+                                                            const uint32_t* __restrict__ cmax_part,
+                                                            int ncb, float* __restrict__ rho,
+                                                            int d_out, float tau, int k_max,
                                                             int32_t* __restrict__ sel,
                                                             int32_t* __restrict__ n_sel) {
   __shared__ int hist[256];
@@ -208,77 +205,98 @@ __global__ __launch_bounds__(kSelThreads) void proxy_select(const uint32_t* __re
   __shared__ uint32_t s_prefix;
   __shared__ int s_need;
   const int tid = threadIdx.x;
-
-  int cnt = 0;
+  // fold the column-block maxima: rows strided over the threads (coalesced),
+  // the partial loads of a row issued together
   for (int i = tid; i < d_out; i += kSelThreads) {
-    const float x = __uint_as_float(tmax_bits[i]) * inv_step_of_code(cmax[i]);
-    rho[i] = x;
-    cnt += (x >= tau) ? 1 : 0;
+    uint32_t tb = 0, cb = 0;
+    int b = 0;
+    for (; b + 4 <= ncb; b += 4) {
+      uint32_t x[4], y[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        x[u] = tmax_part[(int64_t)(b + u) * d_out + i];
+        y[u] = cmax_part[(int64_t)(b + u) * d_out + i];
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        tb = x[u] > tb ? x[u] : tb;
+        cb = y[u] > cb ? y[u] : cb;
+      }
+    }
+    for (; b < ncb; ++b) {
+      const uint32_t x = tmax_part[(int64_t)b * d_out + i], y = cmax_part[(int64_t)b * d_out + i];
+      tb = x > tb ? x : tb;
+      cb = y > cb ? y : cb;
+    }
+    rho[i] = __uint_as_float(tb) * inv_step_of_code(cb);
   }
-  __syncthreads();                     // rho[] written by this workgroup, read back below
+  __syncthreads();                     // rho[] of every row written, read back below
+
+  const int R = (d_out + kSelThreads - 1) / kSelThreads;
+  const int i0 = tid * R, i1 = min(d_out, i0 + R);
+  int cnt = 0;
+  for (int i = i0; i < i1; ++i) cnt += (rho[i] >= tau) ? 1 : 0;
   int total;
-  block_excl_scan(cnt, s16, &total);
-
-  uint32_t key_star = 0;               // k-th largest score (cap case)
-  int need_eq = 0;                     // rows with score == key_star to keep
+  const int base = block_excl_scan(cnt, s16, &total);
   const bool capped = k_max > 0 && total > k_max;
-  if (capped) {
-    if (tid == 0) { s_prefix = 0; s_need = k_max; }
-    __syncthreads();
-    for (int shift = 24; shift >= 0; shift -= 8) {
-      for (int b = tid; b < 256; b += kSelThreads) hist[b] = 0;
-      __syncthreads();
-      const uint32_t prefix = s_prefix;
-      const uint32_t hmask = shift == 24 ? 0u : (0xFFFFFFFFu << (shift + 8));
-      for (int i = tid; i < d_out; i += kSelThreads) {
-        const float x = rho[i];
-        if (!(x >= tau)) continue;
-        const uint32_t key = __float_as_uint(x);
-        if ((key & hmask) == (prefix & hmask)) atomicAdd(&hist[(key >> shift) & 0xFF], 1);
-      }
-      __syncthreads();
-      if (tid == 0) {
-        int need = s_need, cum = 0, digit = 0;
-        for (int b = 255; b >= 0; --b) {
-          if (cum + hist[b] >= need) { digit = b; break; }
-          cum += hist[b];
-        }
-        s_need = need - cum;
-        s_prefix = prefix | ((uint32_t)digit << shift);
-      }
-      __syncthreads();
-    }
-    key_star = s_prefix;
-    need_eq = s_need;
+  if (!capped) {
+    int pos = base;
+    for (int i = i0; i < i1; ++i)
+      if (rho[i] >= tau) sel[pos++] = i;
+    if (tid == 0) *n_sel = total;
+    return;
   }
 
-  // compaction in row order
-  int written = 0, eq_seen = 0;
-  for (int base = 0; base < d_out; base += kSelThreads) {
-    const int i = base + tid;
-    bool take = false, eq = false;
-    if (i < d_out) {
+  // k_max largest scores: radix select of the k-th largest key, then a
+  // row-order compaction that keeps the lowest rows among equal scores
+  if (tid == 0) { s_prefix = 0; s_need = k_max; }
+  __syncthreads();
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    for (int b = tid; b < 256; b += kSelThreads) hist[b] = 0;
+    __syncthreads();
+    const uint32_t prefix = s_prefix;
+    const uint32_t hmask = shift == 24 ? 0u : (0xFFFFFFFFu << (shift + 8));
+    for (int i = tid; i < d_out; i += kSelThreads) {
       const float x = rho[i];
-      if (x >= tau) {
-        if (!capped) {
-          take = true;
-        } else {
-          const uint32_t key = __float_as_uint(x);
-          eq = key == key_star;
-          take = key > key_star;
-        }
-      }
+      if (!(x >= tau)) continue;
+      const uint32_t key = __float_as_uint(x);
+      if ((key & hmask) == (prefix & hmask)) atomicAdd(&hist[(key >> shift) & 0xFF], 1);
     }
-    int eq_total;
-    const int eq_rank = eq_seen + block_excl_scan(eq ? 1 : 0, s16, &eq_total);
-    if (eq && eq_rank < need_eq) take = true;
-    eq_seen += eq_total;
-    int tk_total;
-    const int pos = written + block_excl_scan(take ? 1 : 0, s16, &tk_total);
-    if (take) sel[pos] = i;
-    written += tk_total;
+    __syncthreads();
+    if (tid == 0) {
+      int need = s_need, cum = 0, digit = 0;
+      for (int b = 255; b >= 0; --b) {
+        if (cum + hist[b] >= need) { digit = b; break; }
+        cum += hist[b];
+      }
+      s_need = need - cum;
+      s_prefix = prefix | ((uint32_t)digit << shift);
+    }
+    __syncthreads();
   }
-  if (tid == 0) *n_sel = written;
+  const uint32_t key_star = s_prefix;  // k-th largest score
+  const int need_eq = s_need;          // rows with score == key_star to keep
+  int n_eq = 0, n_gt = 0;
+  for (int i = i0; i < i1; ++i) {
+    const float x = rho[i];
+    if (!(x >= tau)) continue;
+    const uint32_t key = __float_as_uint(x);
+    n_eq += key == key_star;
+    n_gt += key > key_star;
+  }
+  int eq_total;
+  int eq_rank = block_excl_scan(n_eq, s16, &eq_total);
+  const int eq_take = max(0, min(n_eq, need_eq - eq_rank));   // lowest rows first
+  int tk_total;
+  int pos = block_excl_scan(n_gt + eq_take, s16, &tk_total);
+  int eq_left = eq_take;
+  for (int i = i0; i < i1; ++i) {
+    const float x = rho[i];
+    if (!(x >= tau)) continue;
+    const uint32_t key = __float_as_uint(x);
+    if (key > key_star || (key == key_star && eq_left-- > 0)) sel[pos++] = i;
+  }
+  if (tid == 0) *n_sel = tk_total;
 }
 
 // one selected row per wave: copy the staged codes, zero the B row
@@ -298,33 +316,45 @@ __global__ __launch_bounds__(kThreads) void proxy_apply(uint8_t* __restrict__ wq
   for (int k = lane; k < r; k += 64) B[row * r + k] = 0.0f;
 }
 
-__global__ __launch_bounds__(256) void sgd_kernel(float* __restrict__ p, const float* __restrict__ g,
-                                                  int64_t n, float lr) {
-  const int64_t n4 = n / 4;
+// p <- fl(p - fl(lr * g)) for two tensors in one launch: float4 slots
+// [0, na4) belong to the first, [na4, na4 + nb4) to the second; scalar tails
+// are done by workgroup 0.
+__global__ __launch_bounds__(256) void sgd_kernel(float* __restrict__ pa, const float* __restrict__ ga,
+                                                  int64_t na, float* __restrict__ pb,
+                                                  const float* __restrict__ gb, int64_t nb,
+                                                  float lr) {
+  const int64_t na4 = na / 4, nb4 = nb / 4;
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += stride) {
-    float4 a = reinterpret_cast<float4*>(p)[i];
-    const float4 b = reinterpret_cast<const float4*>(g)[i];
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < na4 + nb4; i += stride) {
+    float* p = i < na4 ? pa : pb;
+    const float* g = i < na4 ? ga : gb;
+    const int64_t j = i < na4 ? i : i - na4;
+    float4 a = reinterpret_cast<float4*>(p)[j];
+    const float4 b = reinterpret_cast<const float4*>(g)[j];
     a.x = a.x - lr * b.x;     // two roundings: built without fp contraction
     a.y = a.y - lr * b.y;
     a.z = a.z - lr * b.z;
     a.w = a.w - lr * b.w;
-    reinterpret_cast<float4*>(p)[i] = a;
+    reinterpret_cast<float4*>(p)[j] = a;
   }
-  if (blockIdx.x == 0)
-    for (int64_t i = n4 * 4 + threadIdx.x; i < n; i += blockDim.x) p[i] = p[i] - lr * g[i];
+  if (blockIdx.x == 0) {
+    for (int64_t i = na4 * 4 + threadIdx.x; i < na; i += blockDim.x) pa[i] = pa[i] - lr * ga[i];
+    for (int64_t i = nb4 * 4 + threadIdx.x; i < nb; i += blockDim.x) pb[i] = pb[i] - lr * gb[i];
+  }
 }
 
 struct ProxyWs {
   size_t off_tmax, off_cmax, off_rho, off_staged, total;
+  int ncb;                                  // column blocks of the score kernel
 };
 
 ProxyWs proxy_layout(int64_t d_in, int64_t d_out) {
   ProxyWs p{};
+  p.ncb = (int)((d_in + PCB - 1) / PCB);
   size_t o = 0;
   auto take = [&](size_t bytes) { size_t at = o; o = align_up(o + bytes, 256); return at; };
-  p.off_tmax = take((size_t)d_out * 4);
-  p.off_cmax = take((size_t)d_out * 4);
+  p.off_tmax = take((size_t)p.ncb * d_out * 4);
+  p.off_cmax = take((size_t)p.ncb * d_out * 4);
   p.off_rho = take((size_t)d_out * 4);
   p.off_staged = take((size_t)d_out * (size_t)d_in);
   p.total = o;
@@ -348,18 +378,13 @@ hipError_t launch_proxy_update(uint8_t* wq, const float* s_w, const float* A, fl
   uint32_t* cmax = reinterpret_cast<uint32_t*>(base + L.off_cmax);
   float* rr = rho ? rho : reinterpret_cast<float*>(base + L.off_rho);
   uint8_t* staged = base + L.off_staged;
-  if (d_out > 0) {
-    // tmax and cmax are adjacent: one clear covers both (the gap is padding)
-    const int nclear = (int)((L.off_cmax - L.off_tmax) / 4 + d_out);
-    proxy_clear<<<std::min(64, (nclear + 255) / 256), 256, 0, s>>>(tmax, nclear);
-    if (d_in > 0) {
-      dim3 grid((unsigned)((d_out + PRB - 1) / PRB), (unsigned)((d_in + PCB - 1) / PCB));
-      proxy_score<<<grid, kThreads, 0, s>>>(wq, s_w, A, B, (int)d_in, (int)d_out, (int)r, tmax,
-                                            cmax, staged);
-    }
+  if (d_out > 0 && d_in > 0) {
+    dim3 grid((unsigned)((d_out + PRB - 1) / PRB), (unsigned)L.ncb);
+    proxy_score<<<grid, kThreads, 0, s>>>(wq, s_w, A, B, (int)d_in, (int)d_out, (int)r, tmax,
+                                          cmax, staged);
   }
-  proxy_select<<<1, kSelThreads, 0, s>>>(tmax, cmax, rr, (int)d_out, tau, (int)k_max, sel_idx,
-                                         n_sel);
+  proxy_select<<<1, kSelThreads, 0, s>>>(tmax, cmax, L.ncb, rr, (int)d_out, tau, (int)k_max,
+                                         sel_idx, n_sel);
   if (d_out > 0) {
     const int rows_per_block = kThreads / 64;
     proxy_apply<<<(unsigned)((d_out + rows_per_block - 1) / rows_per_block), kThreads, 0, s>>>(
@@ -368,10 +393,13 @@ hipError_t launch_proxy_update(uint8_t* wq, const float* s_w, const float* A, fl
   return hipGetLastError();
 }
 
-hipError_t launch_sgd(float* p, const float* g, int64_t n, float lr, hipStream_t s) {
-  if (n <= 0) return hipSuccess;
-  const int64_t blocks = std::min<int64_t>((n / 4 + 255) / 256 + 1, 4096);
-  sgd_kernel<<<(int)blocks, 256, 0, s>>>(p, g, n, lr);
+hipError_t launch_sgd2(float* pa, const float* ga, int64_t na, float* pb, const float* gb,
+                       int64_t nb, float lr, hipStream_t s) {
+  if (na <= 0) { pa = nullptr; ga = nullptr; na = 0; }
+  if (nb <= 0) { pb = nullptr; gb = nullptr; nb = 0; }
+  if (na + nb == 0) return hipSuccess;
+  const int64_t blocks = std::min<int64_t>(((na + nb) / 4 + 255) / 256 + 1, 4096);
+  sgd_kernel<<<(int)blocks, 256, 0, s>>>(pa, ga, na, pb, gb, nb, lr);
   return hipGetLastError();
 }
 

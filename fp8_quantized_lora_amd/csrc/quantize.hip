@@ -11,8 +11,10 @@
 //                  the hardware E4M3 converter.  Workgroup 0 writes s, amax
 //                  and the non-finite count.
 // No atomics and no zero-initialised counters: the result is bit-identical
-// from run to run and the pair can be captured in a graph.  The second read of
-// x normally hits the 256 MB Infinity Cache for activations up to that size.
+// from run to run and the pair can be captured in a graph.
+// (A single cooperative launch that keeps x in registers across a grid
+// barrier was measured at several times the cost of these two launches on
+// this runtime, so it is not used.)
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -57,6 +59,82 @@ __device__ __forceinline__ void absorb(float f, uint32_t& m, int& bad) {
   else m = a > m ? a : m;
 }
 
+// every workgroup: fold the per-workgroup partials into amax and the scale;
+// workgroup 0 publishes s, amax and the non-finite count
+__device__ float fold_scale(const uint32_t* __restrict__ part_max, const int* __restrict__ part_bad,
+                            int nparts, const float* __restrict__ scale_in,
+                            float* __restrict__ scale_out, float* __restrict__ amax_out,
+                            int32_t* __restrict__ nonfinite_out) {
+  __shared__ uint32_t sm[kThreads / 64];
+  __shared__ int sb[kThreads / 64];
+  __shared__ float s_scale;
+  uint32_t m = 0;
+  int bad = 0;
+  for (int i = threadIdx.x; i < nparts; i += kThreads) {
+    const uint32_t p = part_max[i];
+    m = p > m ? p : m;
+    bad += part_bad[i];
+  }
+  m = wave_max_u32(m);
+  bad = wave_sum_i32(bad);
+  if ((threadIdx.x & 63) == 0) { sm[threadIdx.x >> 6] = m; sb[threadIdx.x >> 6] = bad; }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t mm = sm[0];
+    int bb = sb[0];
+#pragma unroll
+    for (int k = 1; k < kThreads / 64; ++k) { mm = sm[k] > mm ? sm[k] : mm; bb += sb[k]; }
+    const float amax = __uint_as_float(mm);
+    float sc;
+    if (scale_in) {
+      sc = *scale_in;
+    } else if (amax == 0.0f) {
+      sc = 1.0f;
+    } else {
+      sc = kE4M3Max / amax;                // IEEE-correct fp32 division
+      if (__builtin_isinf(sc)) sc = FLT_MAX;
+    }
+    s_scale = sc;
+    if (blockIdx.x == 0) {
+      *scale_out = sc;
+      if (amax_out) *amax_out = amax;
+      if (nonfinite_out) *nonfinite_out = bb;
+    }
+  }
+  __syncthreads();
+  return s_scale;
+}
+
+template <int DT>
+__device__ __forceinline__ void store_codes(uint8_t* __restrict__ q, int64_t i, const float (&v)[8],
+                                            float s) {
+  if (DT == 0) {
+    reinterpret_cast<uint32_t*>(q)[i] = enc4(v[0] * s, v[1] * s, v[2] * s, v[3] * s);
+  } else {
+    const uint32_t c0 = enc4(v[0] * s, v[1] * s, v[2] * s, v[3] * s);
+    const uint32_t c1 = enc4(v[4] * s, v[5] * s, v[6] * s, v[7] * s);
+    reinterpret_cast<uint2*>(q)[i] = make_uint2(c0, c1);
+  }
+}
+
+__device__ __forceinline__ void block_partials(uint32_t m, int bad, uint32_t* __restrict__ part_max,
+                                               int* __restrict__ part_bad) {
+  __shared__ uint32_t sm[kThreads / 64];
+  __shared__ int sb[kThreads / 64];
+  m = wave_max_u32(m);
+  bad = wave_sum_i32(bad);
+  if ((threadIdx.x & 63) == 0) { sm[threadIdx.x >> 6] = m; sb[threadIdx.x >> 6] = bad; }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t mm = sm[0];
+    int bb = sb[0];
+#pragma unroll
+    for (int k = 1; k < kThreads / 64; ++k) { mm = sm[k] > mm ? sm[k] : mm; bb += sb[k]; }
+    part_max[blockIdx.x] = mm;
+    part_bad[blockIdx.x] = bb;
+  }
+}
+
 template <int DT>
 __global__ __launch_bounds__(kThreads) void qz_amax(const void* __restrict__ x, int64_t n,
                                                     uint32_t* __restrict__ part_max,
@@ -81,21 +159,7 @@ __global__ __launch_bounds__(kThreads) void qz_amax(const void* __restrict__ x, 
   if (blockIdx.x == 0)
     for (int64_t i = nvec * V::N + threadIdx.x; i < n; i += kThreads) absorb(V::scalar(x, i), m, bad);
 
-  __shared__ uint32_t sm[kThreads / 64];
-  __shared__ int sb[kThreads / 64];
-  m = wave_max_u32(m);
-  bad = wave_sum_i32(bad);
-  const int w = threadIdx.x >> 6;
-  if ((threadIdx.x & 63) == 0) { sm[w] = m; sb[w] = bad; }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    uint32_t mm = sm[0];
-    int bb = sb[0];
-#pragma unroll
-    for (int k = 1; k < kThreads / 64; ++k) { mm = sm[k] > mm ? sm[k] : mm; bb += sb[k]; }
-    part_max[blockIdx.x] = mm;
-    part_bad[blockIdx.x] = bb;
-  }
+  block_partials(m, bad, part_max, part_bad);
 }
 
 template <int DT>
@@ -108,44 +172,8 @@ __global__ __launch_bounds__(kThreads) void qz_cast(const void* __restrict__ x, 
                                                     float* __restrict__ amax_out,
                                                     int32_t* __restrict__ nonfinite_out) {
   using V = Vec<DT>;
-  __shared__ uint32_t sm[kThreads / 64];
-  __shared__ int sb[kThreads / 64];
-  __shared__ float s_scale;
-  uint32_t m = 0;
-  int bad = 0;
-  for (int i = threadIdx.x; i < nparts; i += kThreads) {
-    uint32_t p = part_max[i];
-    m = p > m ? p : m;
-    bad += part_bad[i];
-  }
-  m = wave_max_u32(m);
-  bad = wave_sum_i32(bad);
-  if ((threadIdx.x & 63) == 0) { sm[threadIdx.x >> 6] = m; sb[threadIdx.x >> 6] = bad; }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    uint32_t mm = sm[0];
-    int bb = sb[0];
-#pragma unroll
-    for (int k = 1; k < kThreads / 64; ++k) { mm = sm[k] > mm ? sm[k] : mm; bb += sb[k]; }
-    const float amax = __uint_as_float(mm);
-    float s;
-    if (scale_in) {
-      s = *scale_in;
-    } else if (amax == 0.0f) {
-      s = 1.0f;
-    } else {
-      s = kE4M3Max / amax;                 // IEEE-correct fp32 division
-      if (__builtin_isinf(s)) s = FLT_MAX;
-    }
-    s_scale = s;
-    if (blockIdx.x == 0) {
-      *scale_out = s;
-      if (amax_out) *amax_out = amax;
-      if (nonfinite_out) *nonfinite_out = bb;
-    }
-  }
-  __syncthreads();
-  const float s = s_scale;
+  const float s = fold_scale(part_max, part_bad, nparts, scale_in, scale_out, amax_out,
+                             nonfinite_out);
 
   const int64_t nvec = n / V::N;
   const int64_t stride = (int64_t)gridDim.x * kThreads;
@@ -158,16 +186,7 @@ __global__ __launch_bounds__(kThreads) void qz_cast(const void* __restrict__ x, 
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       const int64_t i = i0 + u * stride;
-      if (i < nvec) {
-        if (DT == 0) {
-          uint32_t c = enc4(v[u][0] * s, v[u][1] * s, v[u][2] * s, v[u][3] * s);
-          reinterpret_cast<uint32_t*>(q)[i] = c;
-        } else {
-          uint32_t c0 = enc4(v[u][0] * s, v[u][1] * s, v[u][2] * s, v[u][3] * s);
-          uint32_t c1 = enc4(v[u][4] * s, v[u][5] * s, v[u][6] * s, v[u][7] * s);
-          reinterpret_cast<uint2*>(q)[i] = make_uint2(c0, c1);
-        }
-      }
+      if (i < nvec) store_codes<DT>(q, i, v[u], s);
     }
   }
   if (blockIdx.x == 0)
@@ -193,7 +212,7 @@ hipError_t launch_quantize(const void* x, int dtype, int64_t n, const float* sca
   int* part_bad = reinterpret_cast<int*>(part_max + kQzMaxParts);
   const int vecn = dtype == 0 ? 4 : 8;
   const int64_t nvec = n / vecn;
-  const int g1 = blocks_for(nvec, kQzMaxParts);
+  const int g1 = blocks_for(nvec, 512);            // few partials: every cast workgroup folds them
   const int g2 = blocks_for(nvec, 2048);
   if (dtype == 0) {
     qz_amax<0><<<g1, kThreads, 0, s>>>(x, n, part_max, part_bad);
