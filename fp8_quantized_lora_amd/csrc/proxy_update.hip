@@ -143,14 +143,20 @@ __global__ __launch_bounds__(kThreads) void proxy_score(const uint8_t* __restric
     __syncthreads();
   }
 
+  // Epilogue.  Per row this lane has max |t| and the largest code magnitude
+  // of its 4 columns; the row maxima over the 64 lanes go through LDS (the A
+  // slabs are free now): every lane writes its 16 pairs, then lanes 0..15
+  // reduce one row each.  (Wave shuffles would be 16 x 2 chains of 6
+  // dependent cross-lane steps.)
   const float s_w = *s_w_ptr;
+  float* red_t = &sA[0][0][0] + w * (2 * PRW * 64);               // [16 rows][64 lanes]
+  uint32_t* red_c = reinterpret_cast<uint32_t*>(red_t + PRW * 64);
 #pragma unroll
   for (int i = 0; i < PRW; ++i) {
     const int row = row0 + w * PRW + i;
-    if (row >= d_out) break;                                 // wave-uniform
     float tm = 0.0f;
     uint32_t cm = 0;
-    if (col_ok) {
+    if (col_ok && row < d_out) {
       const uint32_t codes = *reinterpret_cast<const uint32_t*>(wq + (int64_t)row * d_in + c);
       const float t0 = s_w * acc[i][0], t1 = s_w * acc[i][1];
       const float t2 = s_w * acc[i][2], t3 = s_w * acc[i][3];
@@ -160,10 +166,30 @@ __global__ __launch_bounds__(kThreads) void proxy_score(const uint8_t* __restric
       *reinterpret_cast<uint32_t*>(staged + (int64_t)row * d_in + c) =
           enc4(lo.x + t0, lo.y + t1, hi.x + t2, hi.y + t3);
     }
-    const uint32_t tb = wave_max_u32(__float_as_uint(tm));   // |t| >= 0: bit order = value order
-    const uint32_t cb = wave_max_u32(cm);
-    if (lane == 0) {                                         // this column block's share of the row
-      tmax_part[(int64_t)blockIdx.y * d_out + row] = tb;
+    // 16-byte chunk of row i rotated by i: the per-row float4 reads below
+    // then touch 16 distinct chunk positions (no bank conflicts)
+    const int slot = i * 64 + ((((lane >> 2) ^ i) << 2) | (lane & 3));
+    red_t[slot] = tm;
+    red_c[slot] = cm;
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  if (lane < PRW) {
+    const int row = row0 + w * PRW + lane;
+    if (row < d_out) {
+      const float4* rt = reinterpret_cast<const float4*>(red_t + lane * 64);
+      const uint4* rc = reinterpret_cast<const uint4*>(red_c + lane * 64);
+      uint32_t tb = 0, cb = 0;                               // |t| >= 0: bit order = value order
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const float4 x = rt[j ^ lane];
+        const uint4 y = rc[j ^ lane];
+        tb = max(tb, max(max(__float_as_uint(x.x), __float_as_uint(x.y)),
+                         max(__float_as_uint(x.z), __float_as_uint(x.w))));
+        cb = max(cb, max(max(y.x, y.y), max(y.z, y.w)));
+      }
+      tmax_part[(int64_t)blockIdx.y * d_out + row] = tb;    // this column block's share
       cmax_part[(int64_t)blockIdx.y * d_out + row] = cb;
     }
   }

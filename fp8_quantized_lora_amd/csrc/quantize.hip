@@ -25,6 +25,7 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kUnroll = 8;
+constexpr int kAmaxUnroll = 16;
 
 template <int DT> struct Vec;
 template <> struct Vec<0> {  // float32: 4 elements per 16-byte load
@@ -144,14 +145,16 @@ __global__ __launch_bounds__(kThreads) void qz_amax(const void* __restrict__ x, 
   const int64_t stride = (int64_t)gridDim.x * kThreads;
   uint32_t m = 0;
   int bad = 0;
+  // kAmaxUnroll independent 16-byte loads in flight per lane: the pass reads
+  // x cold from HBM, so bytes in flight, not arithmetic, set its speed
   for (int64_t i0 = (int64_t)blockIdx.x * kThreads + threadIdx.x; i0 < nvec;
-       i0 += stride * kUnroll) {
-    float v[kUnroll][8];
+       i0 += stride * kAmaxUnroll) {
+    float v[kAmaxUnroll][8];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u)
+    for (int u = 0; u < kAmaxUnroll; ++u)
       if (i0 + u * stride < nvec) V::load(x, i0 + u * stride, v[u]);
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u)
+    for (int u = 0; u < kAmaxUnroll; ++u)
       if (i0 + u * stride < nvec)
 #pragma unroll
         for (int e = 0; e < V::N; ++e) absorb(v[u][e], m, bad);
@@ -172,30 +175,36 @@ __global__ __launch_bounds__(kThreads) void qz_cast(const void* __restrict__ x, 
                                                     float* __restrict__ amax_out,
                                                     int32_t* __restrict__ nonfinite_out) {
   using V = Vec<DT>;
-  const float s = fold_scale(part_max, part_bad, nparts, scale_in, scale_out, amax_out,
-                             nonfinite_out);
-
   const int64_t nvec = n / V::N;
   const int64_t stride = (int64_t)gridDim.x * kThreads;
-  for (int64_t i0 = (int64_t)blockIdx.x * kThreads + threadIdx.x; i0 < nvec;
-       i0 += stride * kUnroll) {
-    float v[kUnroll][8];
+  int64_t i0 = (int64_t)blockIdx.x * kThreads + threadIdx.x;
+  // the first batch of x is requested before the partials are folded, so the
+  // fold's latency overlaps the loads
+  float v[kUnroll][8];
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u)
-      if (i0 + u * stride < nvec) V::load(x, i0 + u * stride, v[u]);
+  for (int u = 0; u < kUnroll; ++u)
+    if (i0 + u * stride < nvec) V::load(x, i0 + u * stride, v[u]);
+  const float s = fold_scale(part_max, part_bad, nparts, scale_in, scale_out, amax_out,
+                             nonfinite_out);
+  while (true) {
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       const int64_t i = i0 + u * stride;
       if (i < nvec) store_codes<DT>(q, i, v[u], s);
     }
+    i0 += stride * kUnroll;
+    if (i0 >= nvec) break;
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u)
+      if (i0 + u * stride < nvec) V::load(x, i0 + u * stride, v[u]);
   }
   if (blockIdx.x == 0)
     for (int64_t i = nvec * V::N + threadIdx.x; i < n; i += kThreads)
       q[i] = (uint8_t)enc1(V::scalar(x, i) * s);
 }
 
-int blocks_for(int64_t nvec, int cap) {
-  int64_t b = (nvec + (int64_t)kThreads * kUnroll - 1) / ((int64_t)kThreads * kUnroll);
+int blocks_for(int64_t nvec, int unroll, int cap) {
+  int64_t b = (nvec + (int64_t)kThreads * unroll - 1) / ((int64_t)kThreads * unroll);
   if (b < 1) b = 1;
   if (b > cap) b = cap;
   return (int)b;
@@ -212,8 +221,8 @@ hipError_t launch_quantize(const void* x, int dtype, int64_t n, const float* sca
   int* part_bad = reinterpret_cast<int*>(part_max + kQzMaxParts);
   const int vecn = dtype == 0 ? 4 : 8;
   const int64_t nvec = n / vecn;
-  const int g1 = blocks_for(nvec, 512);            // few partials: every cast workgroup folds them
-  const int g2 = blocks_for(nvec, 2048);
+  const int g1 = blocks_for(nvec, kAmaxUnroll, 1024);   // every cast workgroup folds these partials
+  const int g2 = blocks_for(nvec, kUnroll, 2048);
   if (dtype == 0) {
     qz_amax<0><<<g1, kThreads, 0, s>>>(x, n, part_max, part_bad);
     qz_cast<0><<<g2, kThreads, 0, s>>>(x, n, part_max, part_bad, g1, scale_in, q, scale, amax,
