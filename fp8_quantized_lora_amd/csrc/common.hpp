@@ -65,6 +65,42 @@ __device__ __forceinline__ float2 dec2(uint32_t w, bool hi) {
 }
 
 // ---------------------------------------------------------------------------
+// Direct global -> LDS loads (global_load_lds_dwordx4): each lane moves 16
+// bytes from its own global address to LDS byte m0 + 16 * lane, without
+// passing through VGPRs.  Written as inline asm with no outputs, so the
+// compiler tracks nothing: completion is waited for with wait_vmem (vmcnt
+// counts these loads), and a workgroup barrier then makes every wave's data
+// visible.  The LDS address must be wave-uniform (m0).
+// ---------------------------------------------------------------------------
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+
+__device__ __forceinline__ void load16_to_lds(const void* g, uint32_t lds_addr) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds_addr)
+               : "memory", "m0");
+}
+__device__ __forceinline__ uint32_t lds_offset(const void* p) {
+  return (uint32_t)(uintptr_t)(const lds_u8*)p;
+}
+// wait until at most n vector-memory instructions of this wave are in flight
+// (n in {0, 2, 4, 8, 16, 24}; other values wait for all)
+__device__ __forceinline__ void wait_vmem(int n) {
+#define FALQ_WVM(k) \
+  case k: __builtin_amdgcn_s_waitcnt(((k) & 0xF) | (((k) >> 4) << 14) | (0x7 << 4) | (0xF << 8)); break;
+  switch (n) {
+    FALQ_WVM(0) FALQ_WVM(2) FALQ_WVM(4) FALQ_WVM(8) FALQ_WVM(16) FALQ_WVM(24)
+    default: __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xF << 8)); break;
+  }
+#undef FALQ_WVM
+}
+// workgroup barrier that does not wait for outstanding memory operations
+// (__syncthreads would drain vmcnt first and serialise the direct loads)
+__device__ __forceinline__ void barrier_no_drain() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// ---------------------------------------------------------------------------
 // Wavefront (64 lanes) reductions.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {

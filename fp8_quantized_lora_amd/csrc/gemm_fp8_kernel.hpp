@@ -171,35 +171,19 @@ __global__ __launch_bounds__(C::kThreads, 1) void gemm_fp8_nt_kernel(
 //    with a full vmcnt wait before every LDS read: completion is tracked with
 //    explicit vmcnt waits, then a bare s_barrier.
 //  * one DMA instruction fills 1 KB = 8 rows of 128 K-bytes; within a row the
-//    16-byte chunk c is stored at slot c ^ ((row >> 1) & 7) so that the 16
-//    lanes that read one fragment column spread over the LDS banks.
+//    16-byte chunk c is stored at slot c ^ swz(row), swz(r) = (r ^ (r >> 3)) & 7
+//    over the row's index within its 16-row fragment.  Of the XOR swizzles
+//    measured with the LDS bank-conflict counter on gfx950 this is one of the
+//    two with no conflicts for the 16 x 16-byte fragment reads (the plain
+//    (r >> 1) & 7 pattern costs an extra cycle per ds_read_b128).
 //  * each wave owns a 128 x 64 sub-tile: 8 x 4 blocks of 16 x 16, four fp32
 //    accumulators per lane per block.  A fragment lane l holds row l % 16 and
 //    32 bytes at K offset 32 * (l / 16) of the 128-byte K step; B the same.
 // ---------------------------------------------------------------------------
 namespace dma {
 
-typedef __attribute__((address_space(3))) uint8_t lds_u8;
-
-__device__ __forceinline__ void load16_to_lds(const uint8_t* g, uint32_t lds_addr) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds_addr)
-               : "memory", "m0");
-}
-__device__ __forceinline__ uint32_t lds_offset(const void* p) {
-  return (uint32_t)(uintptr_t)(const lds_u8*)p;
-}
-// wait until at most n vector-memory instructions of this wave are in flight
-__device__ __forceinline__ void wait_vmem(int n) {
-#define FALQ_WVM(k) \
-  case k: __builtin_amdgcn_s_waitcnt(((k) & 0xF) | (((k) >> 4) << 14) | (0x7 << 4) | (0xF << 8)); break;
-  switch (n) {
-    FALQ_WVM(0) FALQ_WVM(8) FALQ_WVM(16) FALQ_WVM(24)
-    default: __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xF << 8)); break;
-  }
-#undef FALQ_WVM
-}
-
 constexpr int BM = 256, BN = 256, BK = 128, WGM = 2, WGN = 4, S = 2;
+__device__ __forceinline__ int swz(int row) { return (row ^ ((row >> 3) & 1)) & 7; }
 constexpr int NW = WGM * WGN, kThreads = NW * 64;
 constexpr int WTM = BM / WGM, WTN = BN / WGN, MB = WTM / 16, NB = WTN / 16;
 constexpr int STAGE = (BM + BN) * BK;
@@ -233,12 +217,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_nt_dma(
 #pragma unroll
   for (int j = 0; j < AI; ++j) {
     const int row = (w * AI + j) * 8 + lrow;
-    gA[j] = A + (int64_t)min(m0 + row, M - 1) * lda + ((lslot ^ ((row >> 1) & 7)) * 16);
+    gA[j] = A + (int64_t)min(m0 + row, M - 1) * lda + ((lslot ^ swz(row)) * 16);
   }
 #pragma unroll
   for (int j = 0; j < BI; ++j) {
     const int row = (w * BI + j) * 8 + lrow;
-    gB[j] = B + (int64_t)min(n0 + row, N - 1) * ldb + ((lslot ^ ((row >> 1) & 7)) * 16);
+    gB[j] = B + (int64_t)min(n0 + row, N - 1) * ldb + ((lslot ^ swz(row)) * 16);
   }
   auto issue = [&](int stage, int k0) {
     const uint32_t base = lds_offset(smem + stage * STAGE);
@@ -256,7 +240,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_nt_dma(
     if (s < nk) issue(s, s * BK);
 
   const int r16 = lane & 15, g = lane >> 4;
-  const int sw = (r16 >> 1) & 7;
+  const int sw = swz(r16);
   const int o0 = ((2 * g) ^ sw) * 16, o1 = ((2 * g + 1) ^ sw) * 16;
   const int offA = (wm * WTM + r16) * BK, offB = BM * BK + (wn * WTN + r16) * BK;
   for (int kt = 0; kt < nk; ++kt) {

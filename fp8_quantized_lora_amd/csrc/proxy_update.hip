@@ -22,12 +22,15 @@
 //  proxy_apply    selected rows only: copy the staged codes into the backbone
 //                 and zero the row of B.
 //
-// proxy_score tiles 64 rows x 256 columns per workgroup: each wave owns 16
-// rows, each lane 4 columns, so a lane keeps 64 accumulators.  A is staged in
-// LDS in slabs of 16 ranks and read as one float4 per rank; the 16 B values
-// of a rank are read as LDS broadcasts.  That is 64 fused multiply-adds per
-// 16 bytes of LDS traffic: the kernel is bound by fp32 VALU issue (2 r flops
-// per backbone byte), which is what the exact, ordered chain costs.
+// proxy_score tiles 32 rows x 512 columns per workgroup: each wave owns 8
+// rows, each lane 8 columns (two groups of 4, 256 apart), so a lane keeps 64
+// accumulators.  A reaches LDS by direct global->LDS loads in stages of 8
+// ranks and is read as two float4 per rank; B is wave-uniform (a wave's rows
+// are the same for all its lanes), so its values come through the scalar
+// cache into SGPRs and feed v_fmac as the scalar operand.  That is 64 fused
+// multiply-adds per 32 bytes of LDS traffic, and no VGPRs or LDS broadcasts
+// for B: the kernel is bound by fp32 VALU issue (2 r flops per backbone
+// byte), which is what the exact, ordered chain costs.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -38,10 +41,11 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kSelThreads = 1024;
-constexpr int PRB = 64;          // rows per score workgroup (16 per wave)
-constexpr int PRW = 16;          // rows per wave
-constexpr int PCB = 256;         // columns per score workgroup (4 per lane)
-constexpr int KC = 16;           // ranks per LDS slab
+constexpr int PRW = 8;           // rows per wave
+constexpr int PRB = 4 * PRW;     // rows per score workgroup
+constexpr int PCB = 512;         // columns per score workgroup (8 per lane)
+constexpr int KC = 8;            // ranks per LDS stage
+constexpr int KG = 4;            // ranks per batch of scalar B loads
 
 __device__ __forceinline__ uint32_t max_code_mag(uint32_t w, uint32_t m) {
   const uint32_t a = w & 0x7F7F7F7Fu;
@@ -68,103 +72,107 @@ __global__ __launch_bounds__(kThreads) void proxy_score(const uint8_t* __restric
                                                         uint32_t* __restrict__ tmax_part,
                                                         uint32_t* __restrict__ cmax_part,
                                                         uint8_t* __restrict__ staged) {
-  __shared__ __attribute__((aligned(16))) float sA[2][KC][PCB];         // 32 KB
-  __shared__ __attribute__((aligned(16))) float sB[2][KC][PRB];         // 8 KB, [k][row]
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int row0 = blockIdx.x * PRB, col0 = blockIdx.y * PCB;
-  const int c = col0 + lane * 4;                  // this lane's 4 columns
-  const bool col_ok = c < d_in;
+  __shared__ __attribute__((aligned(1024))) float sA[2][KC][PCB];       // 32 KB
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wrow0 = blockIdx.x * PRB + w * PRW;            // this wave's first row
+  const int col0 = blockIdx.y * PCB;
+  const int c0 = col0 + lane * 4, c1 = c0 + 256;           // this lane's two column groups
+  const bool ok0 = c0 < d_in, ok1 = c1 < d_in;
 
-  float acc[PRW][4];
+  float acc[PRW][8];
 #pragma unroll
   for (int i = 0; i < PRW; ++i)
 #pragma unroll
-    for (int e = 0; e < 4; ++e) acc[i][e] = 0.0f;
+    for (int e = 0; e < 8; ++e) acc[i][e] = 0.0f;
 
-  // slab loaders: A[k0..k0+KC) x [col0, col0+256) and B[row0..row0+64) x [k0..k0+KC)
-  float4 ra[4];
-  float rb[4];
-  auto gload = [&](int k0) {
+  // B row pointers of this wave (rows past d_out read the last row; their
+  // results are discarded)
+  const float* brow[PRW];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int idx = tid + u * kThreads;                    // 0..1023 float4 slots
-      const int kk = idx >> 6, cc = (idx & 63) * 4;
-      const int gk = k0 + kk, gc = col0 + cc;
-      ra[u] = (gk < r && gc < d_in)
-                  ? *reinterpret_cast<const float4*>(A + (int64_t)gk * d_in + gc)
-                  : make_float4(0.f, 0.f, 0.f, 0.f);
-    }
+  for (int i = 0; i < PRW; ++i) brow[i] = B + (int64_t)min(wrow0 + i, d_out - 1) * r;
+
+  // stage `buf` <- A[k0 .. k0+KC) x [col0, col0+512): 16 half rows of 1 KB,
+  // four per wave; rows past r and columns past d_in are clamped into A
+  auto issue = [&](int buf, int k0) {
+    const uint32_t lbase = lds_offset(&sA[buf][0][0]);
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int idx = tid + u * kThreads;                    // 0..1023 = 64 rows x 16 k
-      const int rr = idx >> 4, kk = idx & 15;
-      const int gr = row0 + rr, gk = k0 + kk;
-      rb[u] = (gr < d_out && gk < r) ? B[(int64_t)gr * r + gk] : 0.0f;
+    for (int j = 0; j < 4; ++j) {
+      const int c = w * 4 + j, kk = c >> 1, h = c & 1;
+      const int gk = min(k0 + kk, r - 1);
+      const int gc = min(col0 + h * 256 + lane * 4, d_in - 4);
+      load16_to_lds(A + (int64_t)gk * d_in + gc, __builtin_amdgcn_readfirstlane(lbase + c * 1024));
     }
   };
-  auto sstore = [&](int buf) {
+  auto rank = [&](const float (&bv)[PRW], int buf, int kk) {
+    const float4 a0 = *reinterpret_cast<const float4*>(&sA[buf][kk][lane * 4]);
+    const float4 a1 = *reinterpret_cast<const float4*>(&sA[buf][kk][256 + lane * 4]);
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int idx = tid + u * kThreads;
-      *reinterpret_cast<float4*>(&sA[buf][idx >> 6][(idx & 63) * 4]) = ra[u];
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int idx = tid + u * kThreads;
-      sB[buf][idx & 15][idx >> 4] = rb[u];
+    for (int i = 0; i < PRW; ++i) {
+      acc[i][0] = __builtin_fmaf(bv[i], a0.x, acc[i][0]);
+      acc[i][1] = __builtin_fmaf(bv[i], a0.y, acc[i][1]);
+      acc[i][2] = __builtin_fmaf(bv[i], a0.z, acc[i][2]);
+      acc[i][3] = __builtin_fmaf(bv[i], a0.w, acc[i][3]);
+      acc[i][4] = __builtin_fmaf(bv[i], a1.x, acc[i][4]);
+      acc[i][5] = __builtin_fmaf(bv[i], a1.y, acc[i][5]);
+      acc[i][6] = __builtin_fmaf(bv[i], a1.z, acc[i][6]);
+      acc[i][7] = __builtin_fmaf(bv[i], a1.w, acc[i][7]);
     }
   };
 
   const int nslab = (r + KC - 1) / KC;
-  if (nslab > 0) {
-    gload(0);
-    sstore(0);
-  }
-  __syncthreads();
+  if (nslab > 0) issue(0, 0);
   for (int s = 0; s < nslab; ++s) {
-    const int cur = s & 1;
-    if (s + 1 < nslab) gload((s + 1) * KC);
-    const int kn = min(KC, r - s * KC);                      // ranks in this slab (ascending k)
-    for (int kk = 0; kk < kn; ++kk) {
-      const float4 a = *reinterpret_cast<const float4*>(&sA[cur][kk][lane * 4]);
-      const float4* bp = reinterpret_cast<const float4*>(&sB[cur][kk][w * PRW]);
-      const float4 b0 = bp[0], b1 = bp[1], b2 = bp[2], b3 = bp[3];
-      const float bv[PRW] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w,
-                             b2.x, b2.y, b2.z, b2.w, b3.x, b3.y, b3.z, b3.w};
+    const int buf = s & 1, k0 = s * KC;
+    wait_vmem(0);                  // this wave's part of stage s has landed
+    barrier_no_drain();            // all of stage s landed; stage s-1 no longer read
+    if (s + 1 < nslab) issue(buf ^ 1, k0 + KC);
+    const int kn = min(KC, r - k0);                          // ranks of this stage, ascending
+    int kk = 0;
+    for (; kk + KG <= kn; kk += KG) {
+      float bq[KG][PRW];
 #pragma unroll
-      for (int i = 0; i < PRW; ++i) {
-        acc[i][0] = __builtin_fmaf(bv[i], a.x, acc[i][0]);
-        acc[i][1] = __builtin_fmaf(bv[i], a.y, acc[i][1]);
-        acc[i][2] = __builtin_fmaf(bv[i], a.z, acc[i][2]);
-        acc[i][3] = __builtin_fmaf(bv[i], a.w, acc[i][3]);
-      }
+      for (int u = 0; u < KG; ++u)
+#pragma unroll
+        for (int i = 0; i < PRW; ++i) bq[u][i] = brow[i][k0 + kk + u];
+#pragma unroll
+      for (int u = 0; u < KG; ++u) rank(bq[u], buf, kk + u);
     }
-    if (s + 1 < nslab) sstore(cur ^ 1);
-    __syncthreads();
+    for (; kk < kn; ++kk) {
+      float bv[PRW];
+#pragma unroll
+      for (int i = 0; i < PRW; ++i) bv[i] = brow[i][k0 + kk];
+      rank(bv, buf, kk);
+    }
   }
 
   // Epilogue.  Per row this lane has max |t| and the largest code magnitude
-  // of its 4 columns; the row maxima over the 64 lanes go through LDS (the A
-  // slabs are free now): every lane writes its 16 pairs, then lanes 0..15
-  // reduce one row each.  (Wave shuffles would be 16 x 2 chains of 6
-  // dependent cross-lane steps.)
+  // of its 8 columns; the row maxima over the 64 lanes go through LDS (the A
+  // stages are free once every wave has passed the barrier below): every
+  // lane writes its 8 pairs, then lanes 0..7 reduce one row each.
+  __syncthreads();
   const float s_w = *s_w_ptr;
-  float* red_t = &sA[0][0][0] + w * (2 * PRW * 64);               // [16 rows][64 lanes]
+  float* red_t = &sA[0][0][0] + w * (2 * PRW * 64);               // [8 rows][64 lanes]
   uint32_t* red_c = reinterpret_cast<uint32_t*>(red_t + PRW * 64);
 #pragma unroll
   for (int i = 0; i < PRW; ++i) {
-    const int row = row0 + w * PRW + i;
+    const int row = wrow0 + i;
     float tm = 0.0f;
     uint32_t cm = 0;
-    if (col_ok && row < d_out) {
-      const uint32_t codes = *reinterpret_cast<const uint32_t*>(wq + (int64_t)row * d_in + c);
-      const float t0 = s_w * acc[i][0], t1 = s_w * acc[i][1];
-      const float t2 = s_w * acc[i][2], t3 = s_w * acc[i][3];
-      tm = fmaxf(fmaxf(fabsf(t0), fabsf(t1)), fmaxf(fabsf(t2), fabsf(t3)));
-      cm = max_code_mag(codes, 0u);
-      const float2 lo = dec2(codes, false), hi = dec2(codes, true);
-      *reinterpret_cast<uint32_t*>(staged + (int64_t)row * d_in + c) =
-          enc4(lo.x + t0, lo.y + t1, hi.x + t2, hi.y + t3);
+    if (row < d_out) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int c = h ? c1 : c0;
+        if (!(h ? ok1 : ok0)) continue;
+        const uint32_t codes = *reinterpret_cast<const uint32_t*>(wq + (int64_t)row * d_in + c);
+        const float t0 = s_w * acc[i][4 * h + 0], t1 = s_w * acc[i][4 * h + 1];
+        const float t2 = s_w * acc[i][4 * h + 2], t3 = s_w * acc[i][4 * h + 3];
+        tm = fmaxf(tm, fmaxf(fmaxf(fabsf(t0), fabsf(t1)), fmaxf(fabsf(t2), fabsf(t3))));
+        cm = max_code_mag(codes, cm);
+        const float2 lo = dec2(codes, false), hi = dec2(codes, true);
+        *reinterpret_cast<uint32_t*>(staged + (int64_t)row * d_in + c) =
+            enc4(lo.x + t0, lo.y + t1, hi.x + t2, hi.y + t3);
+      }
     }
     // 16-byte chunk of row i rotated by i: the per-row float4 reads below
     // then touch 16 distinct chunk positions (no bank conflicts)
@@ -176,7 +184,7 @@ __global__ __launch_bounds__(kThreads) void proxy_score(const uint8_t* __restric
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   if (lane < PRW) {
-    const int row = row0 + w * PRW + lane;
+    const int row = wrow0 + lane;
     if (row < d_out) {
       const float4* rt = reinterpret_cast<const float4*>(red_t + lane * 64);
       const uint4* rc = reinterpret_cast<const uint4*>(red_c + lane * 64);
