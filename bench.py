@@ -5,7 +5,8 @@ Workload (the 7B attention projection): W 4096 x 4096 in E4M3, 4096 tokens
 scaled x20, dY ~ N(0, 1e-3), rank 64, SGD lr 1e-3, row-wise proxy update
 every step.  One step = fp8_quantize(X) + melded_linear_fwd +
 fp8_quantize(dY) + melded_linear_bwd (dX, dA, dB) + adapter_step +
-rowwise_proxy_update, all on one HIP stream, inputs resident in HBM.
+rowwise_proxy_update, launched eagerly on one HIP stream, inputs resident in
+HBM.
 
 Prints ONE JSON line.  `value` is whole-step TFLOP/s over the algorithmic
 flops of a step (forward and dX FP8 GEMMs, the four rank-r adapter
@@ -40,8 +41,9 @@ def parse():
     ap.add_argument("--cpu-tokens", type=int, default=2048,
                     help="token sample for the CPU-oracle baseline (0 = skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-graph", action="store_true",
-                    help="launch every call from Python instead of replaying a captured step")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="run one plain device copy of this many MiB before the timed steps "
+                         "(calibrates the HBM byte counters of a profiler run)")
     return ap.parse_args()
 
 
@@ -78,85 +80,85 @@ def main():
     stream = torch.cuda.current_stream()
     names = ["quantize_x", "fwd_gemm", "quantize_dy", "bwd", "adapter_step", "proxy_update"]
 
-    def one_step(i, ev=None):
+    def calls(i):
+        """The step's six boundary calls for batch i, in order."""
         X, dY = batches[i % len(batches)]
-        marks = []
-
-        def mark():
-            if ev is not None:
-                e = torch.cuda.Event(enable_timing=True)
-                e.record(stream)
-                marks.append(e)
-        mark()
-        fq.fp8_quantize(X, m.xq, m.s_x, ws=m.ws_q, stream=stream)
-        mark()
-        fq.melded_linear_fwd(m.xq, m.s_x, m.wq, m.s_w, m.y, stream=stream)
-        mark()
-        fq.fp8_quantize(dY, m.gq, m.s_g, ws=m.ws_q, stream=stream)
-        mark()
-        fq.melded_linear_bwd(m.gq, m.s_g, m.xq, m.s_x, m.wq, m.s_w, m.A, m.B, m.dx, m.dA, m.dB,
-                             ws=m.ws_bwd, stream=stream)
-        mark()
-        fq.adapter_step(m.A, m.B, m.dA, m.dB, spec.lr, stream=stream)
-        mark()
-        fq.rowwise_proxy_update(m.wq, m.s_w, m.A, m.B, spec.tau, spec.k_max, m.sel, m.n_sel,
-                                rho=m.rho, ws=m.ws_px, stream=stream)
-        mark()
-        if ev is not None:
-            ev.append(marks)
+        return [
+            lambda: fq.fp8_quantize(X, m.xq, m.s_x, ws=m.ws_q, stream=stream),
+            lambda: fq.melded_linear_fwd(m.xq, m.s_x, m.wq, m.s_w, m.y, stream=stream),
+            lambda: fq.fp8_quantize(dY, m.gq, m.s_g, ws=m.ws_q, stream=stream),
+            lambda: fq.melded_linear_bwd(m.gq, m.s_g, m.xq, m.s_x, m.wq, m.s_w, m.A, m.B, m.dx,
+                                         m.dA, m.dB, ws=m.ws_bwd, stream=stream),
+            lambda: fq.adapter_step(m.A, m.B, m.dA, m.dB, spec.lr, stream=stream),
+            lambda: fq.rowwise_proxy_update(m.wq, m.s_w, m.A, m.B, spec.tau, spec.k_max, m.sel,
+                                            m.n_sel, rho=m.rho, ws=m.ws_px, stream=stream),
+        ]
 
     for i in range(args.warmup):
-        one_step(i)
+        for c in calls(i):
+            c()
     torch.cuda.synchronize()
 
-    # Per-call durations: HIP events between the calls of eager steps, on the
-    # stream the kernels run on (this pass is not part of the timed region).
-    evs = []
-    for i in range(max(3, min(args.steps, 10))):
-        one_step(args.warmup + i, evs)
+    # Per-call durations (reported beside the result, not part of the timed
+    # region): HIP events between the calls of a few eager steps.
+    n_pc = max(3, min(args.steps, 10))
+    pc = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
+          for _ in range(n_pc)]
+    for i in range(n_pc):
+        for k, c in enumerate(calls(args.warmup + i)):
+            pc[i][k].record(stream)
+            c()
+        pc[i][len(names)].record(stream)
     torch.cuda.synchronize()
-    per_call_us = {n: 0.0 for n in names}
-    for marks in evs:
-        for j, n in enumerate(names):
-            per_call_us[n] += marks[j].elapsed_time(marks[j + 1]) * 1e3 / len(evs)
+    per_call_us = {n: sum(pc[i][k].elapsed_time(pc[i][k + 1]) for i in range(n_pc)) * 1e3 / n_pc
+                   for k, n in enumerate(names)}
 
-    # Timed region: K whole steps.  By default each step is a replay of a HIP
-    # graph holding the step's launches (one per batch), so host launch
-    # latency does not idle the GPU; the kernels and their work are the same.
-    graphs = []
-    if not args.no_graph:
-        cap = torch.cuda.Stream()
-        cap.wait_stream(torch.cuda.current_stream())
-        for b in range(len(batches)):
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g, stream=cap):
-                stream = torch.cuda.current_stream()
-                one_step(b)
-            graphs.append(g)
-        stream = torch.cuda.current_stream()
+    # A plain device copy of known size, for scaling the HBM byte counters of
+    # a profiler run (not part of the timed region).
+    # The source is written, then 1 GiB of other data is written so that the
+    # copy reads its source from HBM rather than from the 256 MB last-level
+    # cache.
+    if args.copy_probe_mib > 0:
+        n = args.copy_probe_mib << 18                       # float32 elements
+        src = torch.ones(n, device="cuda")
+        dst = torch.empty_like(src)
+        evict = torch.empty(1 << 28, device="cuda")
+        evict.fill_(2.0)
         torch.cuda.synchronize()
-        for i in range(args.warmup):
-            graphs[i % len(graphs)].replay()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst, evict
+
+    # Timed region: K steps, launched eagerly on one stream (back-to-back
+    # launches keep the GPU busy: a captured-graph replay of the step measured
+    # no faster).  The forward FP8 GEMM, the dominant kernel, is bracketed by
+    # HIP events on the stream it runs on, so its launch duration is measured
+    # in the same region.
+    g_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            for _ in range(args.steps)]
     start = torch.cuda.Event(enable_timing=True)
     stop = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record(stream)
     for i in range(args.steps):
-        if graphs:
-            graphs[(args.warmup + i) % len(graphs)].replay()
-        else:
-            one_step(args.warmup + i)
+        for k, c in enumerate(calls(args.warmup + n_pc + i)):
+            if k == 1:
+                g_ev[i][0].record(stream)
+                c()
+                g_ev[i][1].record(stream)
+            else:
+                c()
     stop.record(stream)
     torch.cuda.synchronize()
-    total_ms = start.elapsed_time(stop)
-    ms_per_step = total_ms / args.steps
+    ms_per_step = start.elapsed_time(stop) / args.steps
+    gemm_timed_us = sum(a.elapsed_time(b) for a, b in g_ev) * 1e3 / args.steps
     n_sel = int(m.n_sel.cpu()[0])
 
     flops = wl.step_flops(T, d_in, d_out, r)
     tflops = flops / (ms_per_step * 1e-3) / 1e12
     tokens_per_s = T / (ms_per_step * 1e-3)
     gemm_flops = 2 * T * d_in * d_out
-    gemm_us = per_call_us["fwd_gemm"]
+    gemm_us = gemm_timed_us
     gemm_tflops = gemm_flops / (gemm_us * 1e-6) / 1e12
     quant_bytes = T * d_in * 5 + 4
     out = {
@@ -181,9 +183,11 @@ def main():
         "roofline": {"kernel": "melded_linear_fwd FP8 GEMM (4096 x 4096 x 4096)",
                      "bound": "mfma", "achieved": round(gemm_tflops, 1),
                      "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(gemm_tflops / FP8_PEAK_TFLOPS, 4), "traffic": None},
+                     "frac": round(gemm_tflops / FP8_PEAK_TFLOPS, 4),
+                     "traffic": gemm_traffic_bytes()},
         "per_call_us": {k: round(v, 2) for k, v in per_call_us.items()},
-        "launch": "hip graph replay per step" if graphs else "eager launches",
+        "launch": "eager launches on one HIP stream",
+        "fwd_gemm_us_timed": round(gemm_timed_us, 2),
         "quantize_x_GBps": round(quant_bytes / (per_call_us["quantize_x"] * 1e-6) / 1e9, 1),
         "selected_rows_last_step": n_sel,
     }
@@ -191,6 +195,42 @@ def main():
     if not args.no_cpu_baseline and args.cpu_tokens > 0:
         out["cpu_baseline"] = cpu_baseline(spec, d0, args.cpu_tokens)
     print(json.dumps(out), flush=True)
+
+
+GEMM_SOURCES = ("fp8_quantized_lora_amd/csrc/gemm_fp8_kernel.hpp",
+                "fp8_quantized_lora_amd/csrc/gemm_fp8.hip",
+                "fp8_quantized_lora_amd/csrc/common.hpp")
+TRAFFIC_SUMMARY = "profiles/gemm_fp8_nt_dma_4096x4096x4096_hbm_traffic.md"
+
+
+def gemm_sources_digest():
+    import hashlib
+    h = hashlib.sha256()
+    for f in GEMM_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def gemm_traffic_bytes():
+    """HBM bytes per launch of the 4096^3 FP8 GEMM from the committed
+    FETCH_SIZE / WRITE_SIZE counter summary, or None when that summary is
+    missing or was taken on other kernel sources than the ones built here."""
+    path = os.path.join(ROOT, TRAFFIC_SUMMARY)
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    with open(path) as fh:
+        for line in fh:
+            if line.startswith("- ") and ": " in line:
+                k, v = line[2:].strip().split(": ", 1)
+                vals[k.strip("`")] = v.strip().strip("`")
+    if vals.get("sources_sha256") != gemm_sources_digest():
+        return None
+    try:
+        return int(vals["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def cpu_baseline(spec, d0, Ts):

@@ -32,9 +32,9 @@
 namespace falq {
 namespace {
 
-constexpr int TM = 128, TN = 64, TK = 64;      // skinny tile
-constexpr int ROWB = TK * 2 + 16;              // LDS row bytes (bf16 + pad)
-constexpr int kThreads = 256;
+constexpr int TM = 256, TN = 64, TK = 128;     // skinny tile: M x N outputs, K step
+constexpr int kThreads = 256;                  // split / reduce kernels
+constexpr int kSkThreads = 512;                // skinny kernel: 8 waves, 64 x 32 outputs each
 
 __device__ __forceinline__ uint16_t bf16_rne(float f) {
   uint32_t u = __float_as_uint(f);
@@ -54,6 +54,11 @@ __device__ __forceinline__ uint2 dec4_bf16(uint32_t w) {
   return make_uint2(pack_bf16x2(a.x, a.y), pack_bf16x2(b.x, b.y));
 }
 
+// 16-byte chunk slot of chunk c in an LDS row of 128 bytes: the XOR by
+// swz(row) makes the 16-row fragment reads conflict-free (same geometry as
+// the FP8 GEMM's stages)
+__device__ __forceinline__ int swz(int row) { return (row ^ ((row >> 3) & 1)) & 7; }
+
 struct Prob {
   const uint8_t* Q;      // FP8 codes
   int64_t ldq;           // row stride of Q in bytes
@@ -62,12 +67,26 @@ struct Prob {
   int64_t ldh;
   float* P;              // [S][M][N] partial sums
   int M, N, K;           // contraction over K
-  int kchunk;            // K range of split s: [s*kchunk, min(K, (s+1)*kchunk))
+  int kchunk;            // K range of split s: [s*kchunk, min(K, (s+1)*kchunk)), a multiple of TK
   int tilesM, tilesN;
 };
 
+// One K step of the skinny kernel, staged in registers between the global
+// loads and the LDS stores (two steps are in flight).
+struct Stage {
+  uint4 q[4];            // FP8 operand: 64 bytes per thread
+  uint4 h[4];            // bf16 hi/lo operand: 64 bytes per thread
+  uint32_t ok;           // in-range bits: q (0..3, or 0..15 column-wise), h (16..19)
+};
+
+// P[s][m][n] = sum over k in split s of dec(Q)[m][k] * (Hhi + Hlo)[n][k].
+// Q is read row-wise (Q[m][k] = codes[m * ldq + k]) or, with TRANS,
+// column-wise (Q[m][k] = codes[k * ldq + m]: contraction over tokens, the
+// 4 x 16-byte transpose done in registers).  LDS holds the FP8 codes
+// ([256 rows][128 k], 32 KB) and H ([hi/lo][k half][64 n][64 k], 32 KB) per
+// stage; the codes are decoded to bf16 when a fragment is read.
 template <bool TRANS>
-__global__ __launch_bounds__(kThreads) void skinny_kernel(Prob p0, Prob p1) {
+__global__ __launch_bounds__(kSkThreads, 1) void skinny_kernel(Prob p0, Prob p1) {
   const Prob p = blockIdx.z == 0 ? p0 : p1;
   const int tile = blockIdx.x;
   if (tile >= p.tilesM * p.tilesN) return;
@@ -77,141 +96,187 @@ __global__ __launch_bounds__(kThreads) void skinny_kernel(Prob p0, Prob p1) {
   const int kb = s * p.kchunk;
   const int ke = min(p.K, kb + p.kchunk);
 
-  __shared__ __attribute__((aligned(16))) uint8_t sQ[2][TM * ROWB];
-  __shared__ __attribute__((aligned(16))) uint8_t sH[2][2][TN * ROWB];
+  __shared__ __attribute__((aligned(16))) uint8_t sQ[2][TM * TK];          // 64 KB
+  __shared__ __attribute__((aligned(16))) uint8_t sH[2][2][2][TN * 128];   // 64 KB
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int wm = w >> 1, wn = w & 1;             // wave tile: rows wm*64.., cols wn*32..
   v16f acc[2];
 #pragma unroll
-  for (int j = 0; j < 2; ++j)
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int v = 0; v < 16; ++v) acc[j][v] = 0.0f;
+    for (int v = 0; v < 16; ++v) acc[i][v] = 0.0f;
 
-  // staging registers
-  uint4 rq[2];               // TRANS=false: 2 x 16 codes;  TRANS=true: 8 dwords
-  uint4 rh[2][2];            // [hi/lo][chunk]
-
-  auto gload = [&](int k0) {
+  // Every load is issued unconditionally from a clamped in-bounds address;
+  // the out-of-range parts are zeroed only when the stage is written to LDS,
+  // so nothing waits for a stage's loads before the step that stores it.
+  auto gload = [&](int k0, Stage& R) {
+    uint32_t ok = 0;
     if (!TRANS) {
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int c = tid + i * kThreads;
-        const int row = c >> 2, col = (c & 3) * 16;
+      for (int u = 0; u < 4; ++u) {
+        const int c = tid + u * kSkThreads;                  // 2048 chunks of 16 codes
+        const int row = c >> 3, col = (c & 7) * 16;
         const int gm = m0 + row, gk = k0 + col;
-        const bool ok = gm < p.M && gk < ke;
-        uint4 v = *reinterpret_cast<const uint4*>(p.Q + (int64_t)min(gm, p.M - 1) * p.ldq +
-                                                  min(gk, p.K - 16));
-        rq[i] = ok ? v : make_uint4(0, 0, 0, 0);
+        R.q[u] = *reinterpret_cast<const uint4*>(p.Q + (int64_t)min(gm, p.M - 1) * p.ldq +
+                                                 min(gk, p.K - 16));
+        ok |= (gm < p.M && gk < ke) ? 1u << u : 0u;
       }
     } else {
-      const int mo = (tid & 31) * 4, to = (tid >> 5) * 8;
-      const int gm = m0 + mo;
-      uint32_t d[8];
+      const int m4 = (tid & 63) * 4, tg = tid >> 6;         // 4 columns x 16 tokens
+      const int gm = m0 + m4;
+      uint32_t d[16];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int gk = k0 + to + i;
-        const bool ok = gm < p.M && gk < ke;
-        uint32_t v = *reinterpret_cast<const uint32_t*>(p.Q + (int64_t)min(gk, p.K - 1) * p.ldq +
-                                                        min(gm, p.M - 4));
-        d[i] = ok ? v : 0u;
+      for (int i = 0; i < 16; ++i) {
+        const int gk = k0 + tg * 16 + i;
+        d[i] = *reinterpret_cast<const uint32_t*>(p.Q + (int64_t)min(gk, p.K - 1) * p.ldq +
+                                                  min(gm, p.M - 4));
+        ok |= (gm < p.M && gk < ke) ? 1u << i : 0u;
       }
-      rq[0] = make_uint4(d[0], d[1], d[2], d[3]);
-      rq[1] = make_uint4(d[4], d[5], d[6], d[7]);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) R.q[u] = make_uint4(d[4 * u], d[4 * u + 1], d[4 * u + 2], d[4 * u + 3]);
     }
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int c = tid + i * kThreads;
-      const int row = c >> 3, col = (c & 7) * 8;   // bf16 elements
-      const int gn = n0 + row, gk = k0 + col;
-      const bool ok = gn < p.N && gk < ke;
-      const int64_t off = ok ? (int64_t)gn * p.ldh + gk : 0;   // H rows may be padded past K
-      uint4 h = *reinterpret_cast<const uint4*>(p.Hhi + off);
-      uint4 l = *reinterpret_cast<const uint4*>(p.Hlo + off);
-      rh[0][i] = ok ? h : make_uint4(0, 0, 0, 0);
-      rh[1][i] = ok ? l : make_uint4(0, 0, 0, 0);
+    for (int u = 0; u < 4; ++u) {
+      const int c = tid + u * kSkThreads;                    // [hi/lo][64 n][16 chunks of 8]
+      const int h = c >> 10, rem = c & 1023;
+      const int n = rem >> 4, k8 = (rem & 15) * 8;
+      const int gn = n0 + n, gk = k0 + k8;
+      // H rows may be padded past K; out-of-range lanes read row 0
+      const bool in = gn < p.N && gk < ke;
+      const int64_t off = in ? (int64_t)gn * p.ldh + gk : 0;
+      R.h[u] = *reinterpret_cast<const uint4*>((h ? p.Hlo : p.Hhi) + off);
+      ok |= in ? 1u << (16 + u) : 0u;
+    }
+    R.ok = ok;
+  };
+  auto keep = [](uint4 v, uint32_t ok, int bit) {
+    const uint32_t m = 0u - ((ok >> bit) & 1u);
+    return make_uint4(v.x & m, v.y & m, v.z & m, v.w & m);
+  };
+
+  auto sstore = [&](int buf, const Stage& R) {
+    if (!TRANS) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int c = tid + u * kSkThreads;
+        const int row = c >> 3, ch = c & 7;
+        *reinterpret_cast<uint4*>(sQ[buf] + row * TK + ((ch ^ swz(row)) * 16)) = keep(R.q[u], R.ok, u);
+      }
+    } else {
+      const int m4 = (tid & 63) * 4, tg = tid >> 6;
+      uint32_t out[4][4];                                    // [column][4 tokens]
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {                          // tokens 4g .. 4g+3
+        uint4 v = R.q[g];
+        v.x &= 0u - ((R.ok >> (4 * g)) & 1u);
+        v.y &= 0u - ((R.ok >> (4 * g + 1)) & 1u);
+        v.z &= 0u - ((R.ok >> (4 * g + 2)) & 1u);
+        v.w &= 0u - ((R.ok >> (4 * g + 3)) & 1u);
+        const uint32_t t01a = __builtin_amdgcn_perm(v.y, v.x, 0x05010400u);
+        const uint32_t t01b = __builtin_amdgcn_perm(v.y, v.x, 0x07030602u);
+        const uint32_t t23a = __builtin_amdgcn_perm(v.w, v.z, 0x05010400u);
+        const uint32_t t23b = __builtin_amdgcn_perm(v.w, v.z, 0x07030602u);
+        out[0][g] = __builtin_amdgcn_perm(t23a, t01a, 0x05040100u);
+        out[1][g] = __builtin_amdgcn_perm(t23a, t01a, 0x07060302u);
+        out[2][g] = __builtin_amdgcn_perm(t23b, t01b, 0x05040100u);
+        out[3][g] = __builtin_amdgcn_perm(t23b, t01b, 0x07060302u);
+      }
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int row = m4 + c;
+        *reinterpret_cast<uint4*>(sQ[buf] + row * TK + ((tg ^ swz(row)) * 16)) =
+            make_uint4(out[c][0], out[c][1], out[c][2], out[c][3]);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int c = tid + u * kSkThreads;
+      const int h = c >> 10, rem = c & 1023;
+      const int n = rem >> 4, k8 = rem & 15;
+      *reinterpret_cast<uint4*>(sH[buf][h][k8 >> 3] + n * 128 + (((k8 & 7) ^ swz(n)) * 16)) =
+          keep(R.h[u], R.ok, 16 + u);
     }
   };
 
-  auto sstore = [&](int buf) {
-    if (!TRANS) {
+  // fragments: 32x32x16 bf16 MFMA, lane l: row/col l % 32, K half l / 32.
+  // A 16-byte LDS chunk holds the codes of two consecutive MFMA steps: step
+  // 2*q2 + sub of the stage uses k = q2*32 + half*16 + sub*8 + 0..7 for both
+  // operands (a fixed permutation of the stage's 128 k).
+  const int r32 = lane & 31, half = lane >> 5;
+  auto compute = [&](int buf) {
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int c = tid + i * kThreads;
-        const int row = c >> 2, col = (c & 3) * 16;
-        uint8_t* dst = sQ[buf] + row * ROWB + col * 2;
-        uint2 a = dec4_bf16(rq[i].x), b = dec4_bf16(rq[i].y);
-        uint2 cc = dec4_bf16(rq[i].z), dd = dec4_bf16(rq[i].w);
-        *reinterpret_cast<uint4*>(dst) = make_uint4(a.x, a.y, b.x, b.y);
-        *reinterpret_cast<uint4*>(dst + 16) = make_uint4(cc.x, cc.y, dd.x, dd.y);
+    for (int q2 = 0; q2 < TK / 32; ++q2) {
+      v8bf a[2][2];                                          // [m block][sub]
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+        const int row = wm * 64 + mb * 32 + r32;
+        const uint4 c = *reinterpret_cast<const uint4*>(sQ[buf] + row * TK +
+                                                        (((q2 * 2 + half) ^ swz(row)) * 16));
+        const uint2 c0 = dec4_bf16(c.x), c1 = dec4_bf16(c.y), c2 = dec4_bf16(c.z), c3 = dec4_bf16(c.w);
+        a[mb][0] = __builtin_bit_cast(v8bf, make_uint4(c0.x, c0.y, c1.x, c1.y));
+        a[mb][1] = __builtin_bit_cast(v8bf, make_uint4(c2.x, c2.y, c3.x, c3.y));
       }
-    } else {
-      const int mo = (tid & 31) * 4, to = (tid >> 5) * 8;
-      const uint32_t d[8] = {rq[0].x, rq[0].y, rq[0].z, rq[0].w, rq[1].x, rq[1].y, rq[1].z, rq[1].w};
-      uint32_t out[4][4];   // [column][dword of 2 bf16 along k]
+      const int n = wn * 32 + r32;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {          // token pair (2i, 2i+1)
-        // bytes: [col0 t, col0 t+1, col2 t, col2 t+1] and the same for cols 1, 3
-        const uint32_t w02 = __builtin_amdgcn_perm(d[2 * i + 1], d[2 * i], 0x06020400u);
-        const uint32_t w13 = __builtin_amdgcn_perm(d[2 * i + 1], d[2 * i], 0x07030501u);
-        float2 c0 = dec2(w02, false), c2 = dec2(w02, true);
-        float2 c1 = dec2(w13, false), c3 = dec2(w13, true);
-        out[0][i] = pack_bf16x2(c0.x, c0.y);
-        out[1][i] = pack_bf16x2(c1.x, c1.y);
-        out[2][i] = pack_bf16x2(c2.x, c2.y);
-        out[3][i] = pack_bf16x2(c3.x, c3.y);
+      for (int sub = 0; sub < 2; ++sub) {
+        const int ch = ((q2 & 1) * 4 + half * 2 + sub) ^ swz(n);
+        const v8bf bh = __builtin_bit_cast(
+            v8bf, *reinterpret_cast<const uint4*>(sH[buf][0][q2 >> 1] + n * 128 + ch * 16));
+        const v8bf bl = __builtin_bit_cast(
+            v8bf, *reinterpret_cast<const uint4*>(sH[buf][1][q2 >> 1] + n * 128 + ch * 16));
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) {
+          acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mb][sub], bh, acc[mb], 0, 0, 0);
+          acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mb][sub], bl, acc[mb], 0, 0, 0);
+        }
       }
-#pragma unroll
-      for (int c = 0; c < 4; ++c)
-        *reinterpret_cast<uint4*>(sQ[buf] + (mo + c) * ROWB + to * 2) =
-            make_uint4(out[c][0], out[c][1], out[c][2], out[c][3]);
     }
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int c = tid + i * kThreads;
-      const int row = c >> 3, col = (c & 7) * 8;
-      *reinterpret_cast<uint4*>(sH[buf][0] + row * ROWB + col * 2) = rh[0][i];
-      *reinterpret_cast<uint4*>(sH[buf][1] + row * ROWB + col * 2) = rh[1][i];
-    }
+  };
+  // LDS stores of this wave complete, then a barrier that does not wait for
+  // the global loads still in flight
+  auto sync = [] {
+    __builtin_amdgcn_s_waitcnt(0xC07F);                     // lgkmcnt(0)
+    barrier_no_drain();
   };
 
   const int nk = ke > kb ? (ke - kb + TK - 1) / TK : 0;
-  if (nk > 0) {
-    gload(kb);
-    sstore(0);
+  Stage R0, R1;
+  gload(kb, R0);
+  gload(kb + TK, R1);
+  if (nk > 0) sstore(0, R0);
+  sync();
+  // step it: stage it is in LDS buffer it & 1, stage it+1 in registers; the
+  // loads of stage it+2 go into the register set that stage it came from
+  // (the loads of stage it+2 are issued even past the last stage, from
+  // clamped addresses and never stored: a fixed number of loads in flight
+  // lets the compiler wait for exactly one stage)
+  auto step = [&](int it, Stage& Rcur, Stage& Rnext) {
+    gload(kb + (it + 2) * TK, Rcur);
+    __builtin_amdgcn_sched_barrier(0);
+    compute(it & 1);
+    __builtin_amdgcn_sched_barrier(0);
+    if (it + 1 < nk) sstore((it + 1) & 1, Rnext);
+    sync();
+  };
+  int it = 0;
+  for (; it + 1 < nk; it += 2) {
+    step(it, R0, R1);
+    step(it + 1, R1, R0);
   }
-  __syncthreads();
-  const int qoff = (w * 32 + (lane & 31)) * ROWB + (lane >> 5) * 16;
-  const int hoff = (lane & 31) * ROWB + (lane >> 5) * 16;
-  for (int it = 0; it < nk; ++it) {
-    const int cur = it & 1;
-    if (it + 1 < nk) gload(kb + (it + 1) * TK);
-#pragma unroll
-    for (int kk = 0; kk < TK; kk += 16) {
-      const v8bf a = __builtin_bit_cast(v8bf, *reinterpret_cast<const uint4*>(sQ[cur] + qoff + kk * 2));
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const v8bf bh = __builtin_bit_cast(
-            v8bf, *reinterpret_cast<const uint4*>(sH[cur][0] + hoff + j * 32 * ROWB + kk * 2));
-        const v8bf bl = __builtin_bit_cast(
-            v8bf, *reinterpret_cast<const uint4*>(sH[cur][1] + hoff + j * 32 * ROWB + kk * 2));
-        acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bh, acc[j], 0, 0, 0);
-        acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bl, acc[j], 0, 0, 0);
-      }
-    }
-    if (it + 1 < nk) sstore(cur ^ 1);
-    __syncthreads();
-  }
+  if (it < nk) step(it, R0, R1);
 
   float* P = p.P + (int64_t)s * p.M * p.N;
-  const int rbase = m0 + w * 32 + 4 * (lane >> 5);
+  const int n = n0 + wn * 32 + r32;
+  if (n < p.N) {
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int n = n0 + j * 32 + (lane & 31);
-    if (n >= p.N) continue;
+    for (int mb = 0; mb < 2; ++mb) {
+      const int rbase = m0 + wm * 64 + mb * 32 + 4 * half;
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int m = rbase + 8 * (v >> 2) + (v & 3);
-      if (m < p.M) P[(int64_t)m * p.N + n] = acc[j][v];
+      for (int v = 0; v < 16; ++v) {
+        const int m = rbase + 8 * (v >> 2) + (v & 3);
+        if (m < p.M) P[(int64_t)m * p.N + n] = acc[mb][v];
+      }
     }
   }
 }
@@ -379,9 +444,11 @@ struct Plan {
 
 int ceil_div(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
 
+// splits of K so that about one skinny workgroup per CU (256) runs, each
+// with at least two K steps
 int pick_splits(int64_t tiles, int64_t K, int64_t per_split_bytes, int64_t cap_bytes) {
   int s = 1;
-  while (tiles * s < 512 && K / (int64_t)(s * 2) >= 4 * TK && per_split_bytes * (s * 2) <= cap_bytes)
+  while (tiles * s < 256 && K / (int64_t)(s * 2) >= 2 * TK && per_split_bytes * (s * 2) <= cap_bytes)
     s *= 2;
   return s;
 }
@@ -475,7 +542,7 @@ hipError_t launch_adapter_grads(const uint8_t* gq, const float* s_g, const uint8
                  pl.kc1v);
   {
     dim3 grid(pu.tilesM * pu.tilesN, pl.S1, want_da ? 2 : 1);
-    skinny_kernel<false><<<grid, kThreads, 0, s>>>(pu, pv);
+    skinny_kernel<false><<<grid, kSkThreads, 0, s>>>(pu, pv);
   }
   // reduce -> U^T, V^T as bf16 hi/lo [r x Tp], scaled by 1/s_x, 1/s_g
   {
@@ -494,7 +561,7 @@ hipError_t launch_adapter_grads(const uint8_t* gq, const float* s_g, const uint8
   {
     const int tiles = std::max(pb.tilesM * pb.tilesN, want_da ? pa.tilesM * pa.tilesN : 0);
     dim3 grid(tiles, pl.S2, want_da ? 2 : 1);
-    skinny_kernel<true><<<grid, kThreads, 0, s>>>(pb, pa);
+    skinny_kernel<true><<<grid, kSkThreads, 0, s>>>(pb, pa);
   }
   {
     const Red rb = red(f32(pl.off_p2b), pl.S2, d_out, r, d_out, s_g, 0, dB, r, nullptr, nullptr);

@@ -33,31 +33,36 @@ namespace falq {
 namespace {
 
 // in [rows x cols] -> out [cols x rows], bytes; rows and cols multiples of 16
+// out[cols x rows] = in[rows x cols]^T for byte matrices whose sizes are
+// multiples of 16.  A workgroup transposes a 128 x 128 tile without LDS:
+// each thread loads 16 rows x 4 bytes (a wave reads two 128-byte row
+// segments per load), transposes them in registers with byte permutes, and
+// stores 4 output rows x 16 bytes.
 __global__ __launch_bounds__(256) void transpose_u8_kernel(const uint8_t* __restrict__ in,
                                                            int64_t rows, int64_t cols,
                                                            uint8_t* __restrict__ out) {
-  __shared__ uint8_t t[64][64 + 4];
-  const int64_t r0 = (int64_t)blockIdx.y * 64, c0 = (int64_t)blockIdx.x * 64;
-  const int tid = threadIdx.x;
-  {
-    const int rr = tid >> 2, cc = (tid & 3) * 16;
-    uint4 v = make_uint4(0, 0, 0, 0);
-    if (r0 + rr < rows && c0 + cc < cols)
-      v = *reinterpret_cast<const uint4*>(in + (r0 + rr) * cols + c0 + cc);
-    uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  const int tid = threadIdx.x, cg = tid & 31, rg = tid >> 5;
+  const int64_t c = (int64_t)blockIdx.x * 128 + cg * 4;    // 4 input columns
+  const int64_t r = (int64_t)blockIdx.y * 128 + rg * 16;   // 16 input rows
+  if (c >= cols || r >= rows) return;                       // whole 16 x 4 blocks only
+  uint32_t d[16];
 #pragma unroll
-    for (int b = 0; b < 16; ++b) t[rr][cc + b] = (uint8_t)(w[b >> 2] >> (8 * (b & 3)));
-  }
-  __syncthreads();
-  {
-    const int oc = tid >> 2, orr = (tid & 3) * 16;  // output row = input column
-    if (c0 + oc < cols && r0 + orr < rows) {
-      uint32_t w[4] = {0, 0, 0, 0};
+  for (int i = 0; i < 16; ++i) d[i] = *reinterpret_cast<const uint32_t*>(in + (r + i) * cols + c);
+  uint32_t o[4][4];                                         // [column][4 rows]
 #pragma unroll
-      for (int b = 0; b < 16; ++b) w[b >> 2] |= (uint32_t)t[orr + b][oc] << (8 * (b & 3));
-      *reinterpret_cast<uint4*>(out + (c0 + oc) * rows + r0 + orr) = make_uint4(w[0], w[1], w[2], w[3]);
-    }
+  for (int g = 0; g < 4; ++g) {                             // rows 4g .. 4g+3
+    const uint32_t t01a = __builtin_amdgcn_perm(d[4 * g + 1], d[4 * g], 0x05010400u);
+    const uint32_t t01b = __builtin_amdgcn_perm(d[4 * g + 1], d[4 * g], 0x07030602u);
+    const uint32_t t23a = __builtin_amdgcn_perm(d[4 * g + 3], d[4 * g + 2], 0x05010400u);
+    const uint32_t t23b = __builtin_amdgcn_perm(d[4 * g + 3], d[4 * g + 2], 0x07030602u);
+    o[0][g] = __builtin_amdgcn_perm(t23a, t01a, 0x05040100u);
+    o[1][g] = __builtin_amdgcn_perm(t23a, t01a, 0x07060302u);
+    o[2][g] = __builtin_amdgcn_perm(t23b, t01b, 0x05040100u);
+    o[3][g] = __builtin_amdgcn_perm(t23b, t01b, 0x07060302u);
   }
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+    *reinterpret_cast<uint4*>(out + (c + k) * rows + r) = make_uint4(o[k][0], o[k][1], o[k][2], o[k][3]);
 }
 
 }  // namespace
@@ -84,7 +89,8 @@ hipError_t launch_gemm_fp8_nt(const uint8_t* A, int64_t lda, const uint8_t* B, i
 hipError_t launch_transpose_u8(const uint8_t* in, int64_t rows, int64_t cols, uint8_t* out,
                                hipStream_t s) {
   if (rows == 0 || cols == 0) return hipSuccess;
-  dim3 grid((unsigned)((cols + 63) / 64), (unsigned)((rows + 63) / 64));
+  if (rows % 16 != 0 || cols % 16 != 0) return hipErrorInvalidValue;
+  dim3 grid((unsigned)((cols + 127) / 128), (unsigned)((rows + 127) / 128));
   transpose_u8_kernel<<<grid, 256, 0, s>>>(in, rows, cols, out);
   return hipGetLastError();
 }

@@ -20,7 +20,7 @@ hipError_t launch_quantize(const void* x, int dtype, int64_t n, const float* sca
 hipError_t launch_gemm_fp8_nt(const uint8_t* A, int64_t lda, const uint8_t* B, int64_t ldb,
                               float* C, int64_t ldc, int64_t M, int64_t N, int64_t K,
                               const float* sa, const float* sb, hipStream_t s);
-// out[cols x rows] = in[rows x cols]^T (bytes)
+// out[cols x rows] = in[rows x cols]^T (bytes; rows and cols multiples of 16)
 hipError_t launch_transpose_u8(const uint8_t* in, int64_t rows, int64_t cols, uint8_t* out,
                                hipStream_t s);
 

@@ -239,30 +239,34 @@ __global__ __launch_bounds__(kSelThreads) void proxy_select(const uint32_t* __re
   __shared__ uint32_t s_prefix;
   __shared__ int s_need;
   const int tid = threadIdx.x;
-  // fold the column-block maxima: rows strided over the threads (coalesced),
-  // the partial loads of a row issued together
-  for (int i = tid; i < d_out; i += kSelThreads) {
-    uint32_t tb = 0, cb = 0;
-    int b = 0;
-    for (; b + 4 <= ncb; b += 4) {
-      uint32_t x[4], y[4];
+  // fold the column-block maxima: rows strided over the threads (coalesced);
+  // a thread folds four rows at once with the loads of four column blocks
+  // (32 loads) in flight, so the fold takes ncb / 4 round trips
+  for (int i0 = tid; i0 < d_out; i0 += 4 * kSelThreads) {
+    uint32_t tb[4] = {0, 0, 0, 0}, cb[4] = {0, 0, 0, 0};
+    for (int b = 0; b < ncb; b += 4) {
+      uint32_t x[4][4], y[4][4];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        x[u] = tmax_part[(int64_t)(b + u) * d_out + i];
-        y[u] = cmax_part[(int64_t)(b + u) * d_out + i];
-      }
+      for (int u = 0; u < 4; ++u)
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        tb = x[u] > tb ? x[u] : tb;
-        cb = y[u] > cb ? y[u] : cb;
-      }
+        for (int j = 0; j < 4; ++j) {
+          const int i = min(i0 + j * kSelThreads, d_out - 1), bb = min(b + u, ncb - 1);
+          x[u][j] = tmax_part[(int64_t)bb * d_out + i];    // clamped repeats fold harmlessly
+          y[u][j] = cmax_part[(int64_t)bb * d_out + i];
+        }
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          tb[j] = x[u][j] > tb[j] ? x[u][j] : tb[j];
+          cb[j] = y[u][j] > cb[j] ? y[u][j] : cb[j];
+        }
     }
-    for (; b < ncb; ++b) {
-      const uint32_t x = tmax_part[(int64_t)b * d_out + i], y = cmax_part[(int64_t)b * d_out + i];
-      tb = x > tb ? x : tb;
-      cb = y > cb ? y : cb;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int i = i0 + j * kSelThreads;
+      if (i < d_out) rho[i] = __uint_as_float(tb[j]) * inv_step_of_code(cb[j]);
     }
-    rho[i] = __uint_as_float(tb) * inv_step_of_code(cb);
   }
   __syncthreads();                     // rho[] of every row written, read back below
 
