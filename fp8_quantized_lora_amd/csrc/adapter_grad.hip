@@ -364,9 +364,16 @@ __global__ __launch_bounds__(256) void reduce_kernel(Red r0, Red r1) {
   if (m < R.M && n < R.N) {
     const int64_t off = (int64_t)m * R.N + n;
     if (vec) {
-      for (int s = 0; s < R.S; ++s) {
-        const float4 x = *reinterpret_cast<const float4*>(R.P + s * plane + off);
-        v[0] += x.x; v[1] += x.y; v[2] += x.z; v[3] += x.w;
+      // eight planes' loads in flight, added in plane order
+      for (int s0 = 0; s0 < R.S; s0 += 8) {
+        float4 x[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          x[u] = s0 + u < R.S ? *reinterpret_cast<const float4*>(R.P + (s0 + u) * plane + off)
+                              : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          if (s0 + u < R.S) { v[0] += x[u].x; v[1] += x[u].y; v[2] += x[u].z; v[3] += x[u].w; }
       }
     } else {
       for (int s = 0; s < R.S; ++s)

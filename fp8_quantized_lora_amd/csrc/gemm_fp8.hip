@@ -7,7 +7,9 @@
 // Both are C = A . B^T with A and B K-contiguous ("NT"), fp32 accumulation,
 // and the per-tensor scales folded into the epilogue: C *= 1 / (sa * sb).
 //
-// Kernel shape (CDNA4):
+// Two kernels.  K a multiple of 128 (every shape of the workloads) takes the
+// direct-to-LDS kernel described in gemm_fp8_kernel.hpp (namespace dma).
+// Other K take the general kernel below:
 //  * workgroup tile BM x BN x BK = 256 x 256 x 128 bytes, 4 waves in 2 x 2,
 //    each wave a 128 x 128 sub-tile of 4 x 4 blocks of
 //    v_mfma_f32_32x32x64_f8f6f4 (16 fp32 accumulators per lane per block);
@@ -32,7 +34,6 @@
 namespace falq {
 namespace {
 
-// in [rows x cols] -> out [cols x rows], bytes; rows and cols multiples of 16
 // out[cols x rows] = in[rows x cols]^T for byte matrices whose sizes are
 // multiples of 16.  A workgroup transposes a 128 x 128 tile without LDS:
 // each thread loads 16 rows x 4 bytes (a wave reads two 128-byte row

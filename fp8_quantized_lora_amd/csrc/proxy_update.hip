@@ -10,7 +10,7 @@
 //                 A[k,j], acc) for k = 0..r-1 from +0 (the fixed order makes
 //                 the FP8 rounding below reproducible bit for bit), then
 //                 t = fl(s_w * acc).  Each workgroup writes, per row, the max
-//                 |t| and the largest code magnitude of its 256 columns, and
+//                 |t| and the largest code magnitude of its 512 columns, and
 //                 it stages the candidate codes E4M3(fl(dec(q) + t)) for every
 //                 element in a workspace copy of the backbone;
 //  proxy_select   one workgroup: folds the per-column-block maxima (a max of
@@ -41,6 +41,7 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kSelThreads = 1024;
+constexpr int kSelRhoLds = 16384;  // rows whose scores proxy_select keeps in LDS
 constexpr int PRW = 8;           // rows per wave
 constexpr int PRB = 4 * PRW;     // rows per score workgroup
 constexpr int PCB = 512;         // columns per score workgroup (8 per lane)
@@ -238,16 +239,18 @@ __global__ __launch_bounds__(kSelThreads) void proxy_select(const uint32_t* __re
   __shared__ int s16[kSelThreads / 64];
   __shared__ uint32_t s_prefix;
   __shared__ int s_need;
+  __shared__ float s_rho[kSelRhoLds];  // rho read back from LDS when d_out fits
   const int tid = threadIdx.x;
+  float* rv = d_out <= kSelRhoLds ? s_rho : rho;
   // fold the column-block maxima: rows strided over the threads (coalesced);
-  // a thread folds four rows at once with the loads of four column blocks
-  // (32 loads) in flight, so the fold takes ncb / 4 round trips
+  // a thread folds four rows at once with the loads of eight column blocks
+  // (64 loads) in flight, so the fold takes ncb / 8 round trips
   for (int i0 = tid; i0 < d_out; i0 += 4 * kSelThreads) {
     uint32_t tb[4] = {0, 0, 0, 0}, cb[4] = {0, 0, 0, 0};
-    for (int b = 0; b < ncb; b += 4) {
-      uint32_t x[4][4], y[4][4];
+    for (int b = 0; b < ncb; b += 8) {
+      uint32_t x[8][4], y[8][4];
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
+      for (int u = 0; u < 8; ++u)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int i = min(i0 + j * kSelThreads, d_out - 1), bb = min(b + u, ncb - 1);
@@ -255,7 +258,7 @@ __global__ __launch_bounds__(kSelThreads) void proxy_select(const uint32_t* __re
           y[u][j] = cmax_part[(int64_t)bb * d_out + i];
         }
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
+      for (int u = 0; u < 8; ++u)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           tb[j] = x[u][j] > tb[j] ? x[u][j] : tb[j];
@@ -265,22 +268,26 @@ __global__ __launch_bounds__(kSelThreads) void proxy_select(const uint32_t* __re
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int i = i0 + j * kSelThreads;
-      if (i < d_out) rho[i] = __uint_as_float(tb[j]) * inv_step_of_code(cb[j]);
+      if (i < d_out) {
+        const float x = __uint_as_float(tb[j]) * inv_step_of_code(cb[j]);
+        rho[i] = x;
+        if (rv != rho) rv[i] = x;
+      }
     }
   }
-  __syncthreads();                     // rho[] of every row written, read back below
+  __syncthreads();                     // every row's rho written, read back below
 
   const int R = (d_out + kSelThreads - 1) / kSelThreads;
   const int i0 = tid * R, i1 = min(d_out, i0 + R);
   int cnt = 0;
-  for (int i = i0; i < i1; ++i) cnt += (rho[i] >= tau) ? 1 : 0;
+  for (int i = i0; i < i1; ++i) cnt += (rv[i] >= tau) ? 1 : 0;
   int total;
   const int base = block_excl_scan(cnt, s16, &total);
   const bool capped = k_max > 0 && total > k_max;
   if (!capped) {
     int pos = base;
     for (int i = i0; i < i1; ++i)
-      if (rho[i] >= tau) sel[pos++] = i;
+      if (rv[i] >= tau) sel[pos++] = i;
     if (tid == 0) *n_sel = total;
     return;
   }
@@ -295,7 +302,7 @@ __global__ __launch_bounds__(kSelThreads) void proxy_select(const uint32_t* __re
     const uint32_t prefix = s_prefix;
     const uint32_t hmask = shift == 24 ? 0u : (0xFFFFFFFFu << (shift + 8));
     for (int i = tid; i < d_out; i += kSelThreads) {
-      const float x = rho[i];
+      const float x = rv[i];
       if (!(x >= tau)) continue;
       const uint32_t key = __float_as_uint(x);
       if ((key & hmask) == (prefix & hmask)) atomicAdd(&hist[(key >> shift) & 0xFF], 1);
@@ -316,7 +323,7 @@ __global__ __launch_bounds__(kSelThreads) void proxy_select(const uint32_t* __re
   const int need_eq = s_need;          // rows with score == key_star to keep
   int n_eq = 0, n_gt = 0;
   for (int i = i0; i < i1; ++i) {
-    const float x = rho[i];
+    const float x = rv[i];
     if (!(x >= tau)) continue;
     const uint32_t key = __float_as_uint(x);
     n_eq += key == key_star;
@@ -329,7 +336,7 @@ __global__ __launch_bounds__(kSelThreads) void proxy_select(const uint32_t* __re
   int pos = block_excl_scan(n_gt + eq_take, s16, &tk_total);
   int eq_left = eq_take;
   for (int i = i0; i < i1; ++i) {
-    const float x = rho[i];
+    const float x = rv[i];
     if (!(x >= tau)) continue;
     const uint32_t key = __float_as_uint(x);
     if (key > key_star || (key == key_star && eq_left-- > 0)) sel[pos++] = i;
