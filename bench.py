@@ -204,11 +204,17 @@ TRAFFIC_SUMMARY = "profiles/gemm_fp8_nt_dma_4096x4096x4096_hbm_traffic.md"
 
 
 def gemm_sources_digest():
+    """sha256 over the GEMM sources with comments and blank space removed, so
+    that only code changes invalidate a traffic measurement."""
     import hashlib
+    import re
     h = hashlib.sha256()
     for f in GEMM_SOURCES:
-        with open(os.path.join(ROOT, f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, f), encoding="utf-8") as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()
 
 
