@@ -243,33 +243,47 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_nt_dma(
   const int sw = swz(r16);
   const int o0 = ((2 * g) ^ sw) * 16, o1 = ((2 * g + 1) ^ sw) * 16;
   const int offA = (wm * WTM + r16) * BK, offB = BM * BK + (wn * WTN + r16) * BK;
+  auto frag = [&](const uint8_t* p) {
+    return join(*reinterpret_cast<const uint4*>(p + o0), *reinterpret_cast<const uint4*>(p + o1));
+  };
+  // No scalar load may be pending when the loop starts: the compiler then
+  // treats each step's LDS reads as returning in order and waits only for the
+  // fragments the next MFMA needs.
+  const float scale = 1.0f / (sa[0] * sb[0]);
+  __builtin_amdgcn_s_waitcnt(0xC07F);                        // lgkmcnt(0)
   for (int kt = 0; kt < nk; ++kt) {
     // stage kt has landed once at most (stages issued after it) * LPS loads are in flight
     wait_vmem(min(S - 2, nk - 1 - kt) * LPS);
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-    if (kt + S - 1 < nk) issue((kt + S - 1) % S, (kt + S - 1) * BK);
+    barrier_no_drain();
     const uint8_t* st = smem + (kt % S) * STAGE;
-    v8i bf[NB];
+    // Fragment reads in the order the MFMAs consume them (A0, B0..B3, then
+    // A(i+1) ahead of the MFMAs on A(i)); scheduling barriers keep the
+    // compiler from reordering them, so the first MFMA waits for 4 reads,
+    // not 12.
+    v8i bf[NB], af[2];
+    af[0] = frag(st + offA);
 #pragma unroll
     for (int j = 0; j < NB; ++j) {
-      const uint8_t* p = st + offB + j * 16 * BK;
-      bf[j] = join(*reinterpret_cast<const uint4*>(p + o0), *reinterpret_cast<const uint4*>(p + o1));
+      bf[j] = frag(st + offB + j * 16 * BK);
+      __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
     for (int i = 0; i < MB; ++i) {
-      const uint8_t* p = st + offA + i * 16 * BK;
-      const v8i af =
-          join(*reinterpret_cast<const uint4*>(p + o0), *reinterpret_cast<const uint4*>(p + o1));
+      if (i + 1 < MB) af[(i + 1) & 1] = frag(st + offA + (i + 1) * 16 * BK);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int j = 0; j < NB; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af, bf[j], acc[i][j], 0, 0, 0,
-                                                                     0, 0, 0);
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[i & 1], bf[j], acc[i][j], 0,
+                                                                     0, 0, 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+      // the next stage's direct loads go out once this step's first
+      // fragments are in registers (an inline-asm load ahead of the first
+      // reads makes the compiler wait for all twelve of them)
+      if (i == 0 && kt + S - 1 < nk) issue((kt + S - 1) % S, (kt + S - 1) * BK);
+      __builtin_amdgcn_sched_barrier(0);
     }
   }
 
-  const float scale = 1.0f / (sa[0] * sb[0]);
   const int rbase = m0 + wm * WTM + 4 * (lane >> 4);
   const int cbase = n0 + wn * WTN + (lane & 15);
 #pragma unroll
