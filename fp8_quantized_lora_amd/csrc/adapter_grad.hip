@@ -85,14 +85,23 @@ struct Stage {
 // 4 x 16-byte transpose done in registers).  LDS holds the FP8 codes
 // ([256 rows][128 k], 32 KB) and H ([hi/lo][k half][64 n][64 k], 32 KB) per
 // stage; the codes are decoded to bf16 when a fragment is read.
+//
+// The grid is 1-D over (problem, split, tile) with the tile fastest.  The
+// dispatcher deals consecutive workgroup ids round-robin to the 8 XCDs; the
+// id is remapped so that each XCD gets a run of consecutive logical ids, i.e.
+// whole (problem, split) groups, whose tiles all read the same K chunk of H:
+// that chunk then comes from HBM into one XCD's L2 once, not once per tile.
 template <bool TRANS>
-__global__ __launch_bounds__(kSkThreads, 1) void skinny_kernel(Prob p0, Prob p1) {
-  const Prob p = blockIdx.z == 0 ? p0 : p1;
-  const int tile = blockIdx.x;
+__global__ __launch_bounds__(kSkThreads, 1) void skinny_kernel(Prob p0, Prob p1, int tiles_max,
+                                                               int splits) {
+  const int nblk = gridDim.x, per = nblk / 8, b = blockIdx.x;
+  const int lid = b < per * 8 ? (b % 8) * per + b / 8 : b;
+  const int tile = lid % tiles_max, rest = lid / tiles_max;
+  const int s = rest % splits;
+  const Prob p = rest / splits == 0 ? p0 : p1;
   if (tile >= p.tilesM * p.tilesN) return;
   const int m0 = (tile % p.tilesM) * TM;
   const int n0 = (tile / p.tilesM) * TN;
-  const int s = blockIdx.y;
   const int kb = s * p.kchunk;
   const int ke = min(p.K, kb + p.kchunk);
 
@@ -548,8 +557,9 @@ hipError_t launch_adapter_grads(const uint8_t* gq, const float* s_g, const uint8
   Prob pv = prob(gq, d_out, u16(pl.off_bhi), u16(pl.off_blo), d_out, f32(pl.off_p1v), T, r, d_out,
                  pl.kc1v);
   {
-    dim3 grid(pu.tilesM * pu.tilesN, pl.S1, want_da ? 2 : 1);
-    skinny_kernel<false><<<grid, kSkThreads, 0, s>>>(pu, pv);
+    const int tiles = pu.tilesM * pu.tilesN;
+    skinny_kernel<false><<<tiles * pl.S1 * (want_da ? 2 : 1), kSkThreads, 0, s>>>(pu, pv, tiles,
+                                                                                  pl.S1);
   }
   // reduce -> U^T, V^T as bf16 hi/lo [r x Tp], scaled by 1/s_x, 1/s_g
   {
@@ -567,8 +577,8 @@ hipError_t launch_adapter_grads(const uint8_t* gq, const float* s_g, const uint8
                  pl.kc2);
   {
     const int tiles = std::max(pb.tilesM * pb.tilesN, want_da ? pa.tilesM * pa.tilesN : 0);
-    dim3 grid(tiles, pl.S2, want_da ? 2 : 1);
-    skinny_kernel<true><<<grid, kSkThreads, 0, s>>>(pb, pa);
+    skinny_kernel<true><<<tiles * pl.S2 * (want_da ? 2 : 1), kSkThreads, 0, s>>>(pb, pa, tiles,
+                                                                                 pl.S2);
   }
   {
     const Red rb = red(f32(pl.off_p2b), pl.S2, d_out, r, d_out, s_g, 0, dB, r, nullptr, nullptr);
