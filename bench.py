@@ -160,7 +160,12 @@ def main():
     gemm_flops = 2 * T * d_in * d_out
     gemm_us = gemm_timed_us
     gemm_tflops = gemm_flops / (gemm_us * 1e-6) / 1e12
-    quant_bytes = T * d_in * 5 + 4
+    quant_bytes = T * d_in * 5 + 4                  # fp32 in, E4M3 out, the scale
+    quant_gbs = quant_bytes / (per_call_us["quantize_x"] * 1e-6) / 1e9
+    # proxy update: read the codes, A and B; write the selected rows' codes,
+    # zero their B rows, write the indices
+    proxy_bytes = d_out * d_in + 4 * r * (d_in + d_out) + n_sel * (d_in + 4 * r + 4)
+    proxy_gbs = proxy_bytes / (per_call_us["proxy_update"] * 1e-6) / 1e9
     out = {
         "metric": METRIC,
         "value": round(tflops, 2),
@@ -188,7 +193,10 @@ def main():
         "per_call_us": {k: round(v, 2) for k, v in per_call_us.items()},
         "launch": "eager launches on one HIP stream",
         "fwd_gemm_us_timed": round(gemm_timed_us, 2),
-        "quantize_x_GBps": round(quant_bytes / (per_call_us["quantize_x"] * 1e-6) / 1e9, 1),
+        "quantize_x_GBps": round(quant_gbs, 1),
+        "quantize_x_hbm_frac": round(quant_gbs / HBM_PEAK_GBS, 4),
+        "proxy_update_GBps": round(proxy_gbs, 1),
+        "proxy_update_hbm_frac": round(proxy_gbs / HBM_PEAK_GBS, 4),
         "selected_rows_last_step": n_sel,
     }
 
