@@ -26,6 +26,7 @@ arithmetic or an independent library routine.
 from __future__ import annotations
 
 import ctypes
+import math
 import os
 from typing import Optional, Tuple
 
@@ -185,6 +186,68 @@ def adapter_step(A: np.ndarray, B: np.ndarray, dA: Optional[np.ndarray], dB: np.
     B2 = (np.asarray(B, np.float32) - (lr32 * np.asarray(dB, np.float32)).astype(np.float32)
           ).astype(np.float32)
     return A2, B2
+
+
+def adamw_scalars(lr: float, beta1: float, beta2: float, eps: float, weight_decay: float,
+                  step: int) -> dict:
+    """The float32 scalars of AdamW step number `step` (>= 1).  Each is computed
+    in float64 from the float32 values of the arguments and rounded to float32
+    once:
+        decay     = 1 - lr*wd                     (decoupled weight decay)
+        step_size = lr / (1 - beta1**step)        (first-moment bias correction)
+        inv_bc2   = 1 / sqrt(1 - beta2**step)     (second-moment bias correction)
+        omb1, omb2 = 1 - beta1, 1 - beta2
+    """
+    lr, b1, b2, eps, wd = (float(np.float32(v)) for v in (lr, beta1, beta2, eps, weight_decay))
+    t = int(step)
+    return {
+        "b1": np.float32(b1), "b2": np.float32(b2), "eps": np.float32(eps),
+        "omb1": np.float32(1.0 - b1), "omb2": np.float32(1.0 - b2),
+        "decay": np.float32(1.0 - lr * wd),
+        "step_size": np.float32(lr / (1.0 - b1 ** t)),
+        "inv_bc2": np.float32(1.0 / math.sqrt(1.0 - b2 ** t)),
+    }
+
+
+def adamw_update(p: np.ndarray, g: np.ndarray, m: np.ndarray, v: np.ndarray, sc: dict
+                 ) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """One AdamW update of one tensor, elementwise in float32 with every
+    operation rounded on its own (no fused multiply-add):
+        m'  = b1*m + omb1*g
+        v'  = b2*v + (omb2*g)*g
+        den = sqrt(v')*inv_bc2 + eps
+        p'  = decay*p - step_size*(m'/den)
+    Returns (p', m', v')."""
+    f = np.float32
+    p, g, m, v = (np.asarray(a, dtype=f) for a in (p, g, m, v))
+    with np.errstate(over="ignore", under="ignore"):
+        m2 = (sc["b1"] * m).astype(f) + (sc["omb1"] * g).astype(f)
+        v2 = (sc["b2"] * v).astype(f) + ((sc["omb2"] * g).astype(f) * g).astype(f)
+        den = (np.sqrt(v2).astype(f) * sc["inv_bc2"]).astype(f) + sc["eps"]
+        p2 = (sc["decay"] * p).astype(f) - (sc["step_size"] * (m2 / den).astype(f)).astype(f)
+    return p2.astype(f), m2.astype(f), v2.astype(f)
+
+
+def adapter_step_adamw(A: np.ndarray, B: np.ndarray, dA: Optional[np.ndarray], dB: np.ndarray,
+                       mA: Optional[np.ndarray], vA: Optional[np.ndarray],
+                       mB: np.ndarray, vB: np.ndarray, lr: float, beta1: float, beta2: float,
+                       eps: float, weight_decay: float, step: int):
+    """32-bit AdamW on the adapter factors ([P4] thread 3, W3.1: every run of
+    the pages trains with a 32-bit AdamW optimizer; the pages give no
+    hyper-parameters, so they are arguments).  AdamW is Adam with the weight
+    decay applied to the weights directly rather than added to the gradient
+    (decoupled weight decay, Loshchilov and Hutter); moments and weights are
+    float32.  dA = None keeps A (and its moments) frozen.
+    Returns (A', B', mA', vA', mB', vB')."""
+    sc = adamw_scalars(lr, beta1, beta2, eps, weight_decay, step)
+    if dA is None:
+        A2 = np.array(A, dtype=np.float32, copy=True)
+        mA2 = None if mA is None else np.array(mA, dtype=np.float32, copy=True)
+        vA2 = None if vA is None else np.array(vA, dtype=np.float32, copy=True)
+    else:
+        A2, mA2, vA2 = adamw_update(A, dA, mA, vA, sc)
+    B2, mB2, vB2 = adamw_update(B, dB, mB, vB, sc)
+    return A2, B2, mA2, vA2, mB2, vB2
 
 
 # ----------------------------------------------------------------------------
