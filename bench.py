@@ -4,7 +4,8 @@ Workload (the 7B attention projection): W 4096 x 4096 in E4M3, 4096 tokens
 (batch 4 x sequence 1024) of N(0,1) activations with 1% outlier channels
 scaled x20, dY ~ N(0, 1e-3), rank 64, SGD lr 1e-3, row-wise proxy update
 every step.  One step = fp8_quantize(X) + melded_linear_fwd +
-fp8_quantize(dY) + melded_linear_bwd (dX, dA, dB) + adapter_step +
+fp8_quantize(dY) + melded_linear_bwd (dX, dA, dB) + adapter_step (SGD, or
+adapter_step_adamw with --optimizer adamw) +
 rowwise_proxy_update, launched eagerly on one HIP stream, inputs resident in
 HBM.
 
@@ -41,6 +42,9 @@ def parse():
     ap.add_argument("--cpu-tokens", type=int, default=2048,
                     help="token sample for the CPU-oracle baseline (0 = skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--optimizer", choices=["sgd", "adamw"], default="sgd",
+                    help="adapter optimizer: SGD lr 1e-3 (the workload's) or 32-bit AdamW "
+                         "(the pages' training runs)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB before the timed steps "
                          "(calibrates the HBM byte counters of a profiler run)")
@@ -68,7 +72,7 @@ def main():
     T, d_in, d_out, r = spec.tokens, spec.d_in, spec.d_out, spec.rank
 
     d0 = wl.make_linear(2, 0, spec, step=0)
-    m = fq.MeldedLinear(d_out, d_in, r, T)
+    m = fq.MeldedLinear(d_out, d_in, r, T, optimizer=args.optimizer)
     t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
     m.init_state(t(d0["W"]), t(d0["A"]), t(d0["B"]))
     batches = []
@@ -89,7 +93,7 @@ def main():
             lambda: fq.fp8_quantize(dY, m.gq, m.s_g, ws=m.ws_q, stream=stream),
             lambda: fq.melded_linear_bwd(m.gq, m.s_g, m.xq, m.s_x, m.wq, m.s_w, m.A, m.B, m.dx,
                                          m.dA, m.dB, ws=m.ws_bwd, stream=stream),
-            lambda: fq.adapter_step(m.A, m.B, m.dA, m.dB, spec.lr, stream=stream),
+            lambda: m.adapter_update(spec.lr, stream=stream),
             lambda: fq.rowwise_proxy_update(m.wq, m.s_w, m.A, m.B, spec.tau, spec.k_max, m.sel,
                                             m.n_sel, rho=m.rho, ws=m.ws_px, stream=stream),
         ]
@@ -180,9 +184,11 @@ def main():
         "dtype": "fp8e4m3",
         "data": "synthetic",
         "config": {"workload": "7B attention projection: W 4096x4096 E4M3, 4096 tokens "
-                               "(4 x 1024), 1% outlier channels x20, rank 64, SGD lr 1e-3, "
-                               "proxy update every step",
+                               "(4 x 1024), 1% outlier channels x20, rank 64, "
+                               + ("SGD" if args.optimizer == "sgd" else "32-bit AdamW")
+                               + " lr 1e-3, proxy update every step",
                    "tokens": T, "d_in": d_in, "d_out": d_out, "rank": r,
+                   "optimizer": args.optimizer,
                    "parallelism": "single GPU"},
         "tokens_per_s": round(tokens_per_s, 1),
         "roofline": {"kernel": "melded_linear_fwd FP8 GEMM (4096 x 4096 x 4096)",
@@ -201,7 +207,7 @@ def main():
     }
 
     if not args.no_cpu_baseline and args.cpu_tokens > 0:
-        out["cpu_baseline"] = cpu_baseline(spec, d0, args.cpu_tokens)
+        out["cpu_baseline"] = cpu_baseline(spec, d0, args.cpu_tokens, args.optimizer)
     print(json.dumps(out), flush=True)
 
 
@@ -247,10 +253,10 @@ def gemm_traffic_bytes():
         return None
 
 
-def cpu_baseline(spec, d0, Ts):
+def cpu_baseline(spec, d0, Ts, optimizer="sgd"):
     """The CPU oracle, as it is, on a token sample of the same workload:
-    quantize X and dY, forward, backward (dX, dA, dB), SGD, and the proxy
-    update over the full 4096 x 4096 backbone."""
+    quantize X and dY, forward, backward (dX, dA, dB), the adapter step (SGD
+    or AdamW) and the proxy update over the full 4096 x 4096 backbone."""
     import numpy as np
 
     import oracle
@@ -265,7 +271,12 @@ def cpu_baseline(spec, d0, Ts):
     oracle.melded_linear_fwd(xq, s_x, wq, s_w)
     gq, s_g, _, _ = oracle.fp8_quantize(dY)
     _, dA, dB = oracle.melded_linear_bwd(gq, s_g, xq, s_x, wq, s_w, d0["A"], d0["B"])
-    A, B = oracle.adapter_step(d0["A"], d0["B"], dA, dB, spec.lr)
+    if optimizer == "sgd":
+        A, B = oracle.adapter_step(d0["A"], d0["B"], dA, dB, spec.lr)
+    else:
+        z = [np.zeros_like(d0["A"]), np.zeros_like(d0["B"])]
+        A, B, _, _, _, _ = oracle.adapter_step_adamw(d0["A"], d0["B"], dA, dB, z[0], z[0], z[1],
+                                                     z[1], spec.lr, 0.9, 0.999, 1e-8, 0.0, 1)
     oracle.rowwise_proxy_update(wq, s_w, A, B, spec.tau, spec.k_max)
     t2 = time.perf_counter()
     step_s = t2 - t1

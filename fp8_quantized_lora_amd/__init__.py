@@ -18,7 +18,7 @@ import torch
 
 __all__ = ["load", "FalqError", "fp8_quantize", "fp8_quantize_workspace_bytes",
            "melded_linear_fwd", "melded_linear_bwd", "melded_linear_bwd_workspace_bytes",
-           "adapter_step", "rowwise_proxy_update", "rowwise_proxy_update_workspace_bytes",
+           "adapter_step", "adapter_step_adamw", "rowwise_proxy_update", "rowwise_proxy_update_workspace_bytes",
            "version", "LIB_PATH"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfalqon.so")
@@ -40,6 +40,8 @@ _SIGS = {
     "melded_linear_bwd": (_i32, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _i64, _i64,
                                  _i64, _i64, _c_p, _c_p, _c_p, _c_p, _sz, _c_p]),
     "adapter_step": (_i32, [_c_p, _c_p, _c_p, _c_p, _i64, _i64, _i64, _f32, _c_p]),
+    "adapter_step_adamw": (_i32, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _i64, _i64,
+                                  _i64, _f32, _f32, _f32, _f32, _f32, _i64, _c_p]),
     "rowwise_proxy_update_workspace_bytes": (_sz, [_i64, _i64, _i64]),
     "rowwise_proxy_update": (_i32, [_c_p, _c_p, _c_p, _c_p, _i64, _i64, _i64, _f32, _i64, _c_p,
                                     _c_p, _c_p, _c_p, _sz, _c_p]),
@@ -172,6 +174,23 @@ def adapter_step(A, B, dA, dB, lr: float, stream=None) -> None:
         _req(dA, torch.float32, (r, d_in), "dA")
     _check(load().adapter_step(_ptr(A), _ptr(B), _ptr(dA), _ptr(dB), r, d_in, d_out, lr,
                                _stream(stream)), "adapter_step")
+
+
+def adapter_step_adamw(A, B, dA, dB, mA, vA, mB, vB, lr: float, step: int, beta1: float = 0.9,
+                       beta2: float = 0.999, eps: float = 1e-8, weight_decay: float = 0.0,
+                       stream=None) -> None:
+    """AdamW step number `step` (>= 1) on A and B, moments mA, vA, mB, vB in
+    place; dA = None freezes A (mA and vA may then be None)."""
+    r, d_in = A.shape
+    d_out = B.shape[0]
+    for t, name in ((B, "B"), (dB, "dB"), (mB, "mB"), (vB, "vB")):
+        _req(t, torch.float32, (d_out, r), name)
+    if dA is not None:
+        for t, name in ((A, "A"), (dA, "dA"), (mA, "mA"), (vA, "vA")):
+            _req(t, torch.float32, (r, d_in), name)
+    _check(load().adapter_step_adamw(_ptr(A), _ptr(B), _ptr(dA), _ptr(dB), _ptr(mA), _ptr(vA),
+                                     _ptr(mB), _ptr(vB), r, d_in, d_out, lr, beta1, beta2, eps,
+                                     weight_decay, step, _stream(stream)), "adapter_step_adamw")
 
 
 def rowwise_proxy_update_workspace_bytes(d_in: int, d_out: int, r: int) -> int:

@@ -36,6 +36,23 @@ hipError_t launch_adapter_grads(const uint8_t* gq, const float* s_g, const uint8
 hipError_t launch_sgd2(float* pa, const float* ga, int64_t na, float* pb, const float* gb,
                        int64_t nb, float lr, hipStream_t s);
 
+// ---- AdamW ----------------------------------------------------------------
+// float32 scalars of one AdamW step (derived on the host, see api.cpp)
+struct AdamWScalars {
+  float b1, b2, omb1, omb2, eps, decay, step_size, inv_bc2;
+};
+// one tensor: parameters, gradient, first and second moments (in place)
+struct AdamWTensor {
+  float* p;
+  const float* g;
+  float* m;
+  float* v;
+  int64_t n;
+};
+// two tensors in one launch (either may be empty: n == 0); 16-byte aligned
+hipError_t launch_adamw2(const AdamWTensor& a, const AdamWTensor& b, const AdamWScalars& c,
+                         hipStream_t s);
+
 // ---- row-wise proxy update -------------------------------------------------
 size_t proxy_ws_bytes(int64_t d_in, int64_t d_out, int64_t r);
 hipError_t launch_proxy_update(uint8_t* wq, const float* s_w, const float* A, float* B,

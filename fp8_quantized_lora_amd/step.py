@@ -5,7 +5,8 @@ fixed per-tensor scale s_w, and the adapter factors A [r x d_in] and
 B [d_out x r] (B doubles as the row-wise proxy).  A step is
 
     fp8_quantize(X) -> melded_linear_fwd -> fp8_quantize(dY)
-    -> melded_linear_bwd -> adapter_step -> rowwise_proxy_update
+    -> melded_linear_bwd -> adapter_step (SGD) or adapter_step_adamw
+    -> rowwise_proxy_update
 
 with every buffer and workspace allocated once up front, so a step makes no
 allocation and no host synchronisation.  This module only sequences calls
@@ -18,15 +19,24 @@ from typing import Optional
 import torch
 
 from . import (fp8_quantize, fp8_quantize_workspace_bytes, melded_linear_fwd, melded_linear_bwd,
-               melded_linear_bwd_workspace_bytes, adapter_step, rowwise_proxy_update,
-               rowwise_proxy_update_workspace_bytes)
+               melded_linear_bwd_workspace_bytes, adapter_step, adapter_step_adamw,
+               rowwise_proxy_update, rowwise_proxy_update_workspace_bytes)
 
 
 class MeldedLinear:
     def __init__(self, d_out: int, d_in: int, rank: int, tokens: int, device="cuda",
-                 x_dtype=torch.float32, train_a: bool = True):
+                 x_dtype=torch.float32, train_a: bool = True, optimizer: str = "sgd",
+                 adamw: Optional[dict] = None):
+        """optimizer "sgd" (adapter_step) or "adamw" (adapter_step_adamw, with
+        hyper-parameters `adamw`: beta1, beta2, eps, weight_decay)."""
+        if optimizer not in ("sgd", "adamw"):
+            raise ValueError(f"optimizer must be 'sgd' or 'adamw', not {optimizer!r}")
         self.d_out, self.d_in, self.r, self.T = d_out, d_in, rank, tokens
         self.train_a = train_a
+        self.optimizer = optimizer
+        self.adamw = {"beta1": 0.9, "beta2": 0.999, "eps": 1e-8, "weight_decay": 0.0,
+                      **(adamw or {})}
+        self.opt_step = 0
         dev = torch.device(device)
         u8, f32, i32 = torch.uint8, torch.float32, torch.int32
         self.wq = torch.empty((d_out, d_in), dtype=u8, device=dev)
@@ -42,6 +52,11 @@ class MeldedLinear:
         self.dx = torch.empty((tokens, d_in), dtype=f32, device=dev)
         self.dA = torch.empty((rank, d_in), dtype=f32, device=dev) if train_a else None
         self.dB = torch.empty((d_out, rank), dtype=f32, device=dev)
+        if optimizer == "adamw":          # first and second moments, zero at the start
+            self.mA = torch.zeros((rank, d_in), dtype=f32, device=dev) if train_a else None
+            self.vA = torch.zeros((rank, d_in), dtype=f32, device=dev) if train_a else None
+            self.mB = torch.zeros((d_out, rank), dtype=f32, device=dev)
+            self.vB = torch.zeros((d_out, rank), dtype=f32, device=dev)
         self.sel = torch.empty(d_out, dtype=i32, device=dev)
         self.n_sel = torch.zeros(1, dtype=i32, device=dev)
         self.rho = torch.empty(d_out, dtype=f32, device=dev)
@@ -71,8 +86,16 @@ class MeldedLinear:
                           self.dx, self.dA, self.dB, ws=self.ws_bwd, stream=stream)
         return self.dx
 
+    def adapter_update(self, lr: float, stream=None):
+        if self.optimizer == "sgd":
+            adapter_step(self.A, self.B, self.dA, self.dB, lr, stream=stream)
+        else:
+            self.opt_step += 1
+            adapter_step_adamw(self.A, self.B, self.dA, self.dB, self.mA, self.vA, self.mB,
+                               self.vB, lr, self.opt_step, stream=stream, **self.adamw)
+
     def update(self, lr: float, tau: float, k_max: int = 0, stream=None):
-        adapter_step(self.A, self.B, self.dA, self.dB, lr, stream=stream)
+        self.adapter_update(lr, stream)
         rowwise_proxy_update(self.wq, self.s_w, self.A, self.B, tau, k_max, self.sel, self.n_sel,
                              rho=self.rho, ws=self.ws_px, stream=stream)
 

@@ -10,6 +10,7 @@
  *   melded_linear_bwd      -> dX, dA, dB     dX through the FP8 weight; rank-r
  *                                            adapter gradients from G~ and X~
  *   adapter_step           -> A, B           SGD on the adapter factors
+ *     (or adapter_step_adamw                    32-bit AdamW, the pages' optimizer)
  *   rowwise_proxy_update   -> W~, B, rows    merge rows whose pending delta
  *                                            survives FP8 rounding
  *
@@ -154,6 +155,34 @@ falq_status melded_linear_bwd(const uint8_t *gq, const float *s_g,
 falq_status adapter_step(float *A, float *B, const float *dA, const float *dB,
                          int64_t r, int64_t d_in, int64_t d_out, float lr,
                          falq_stream stream);
+
+/*
+ * adapter_step_adamw — 32-bit AdamW on the adapter factors, in place
+ * ([rebuttal] thread 3 W3.1: the runs train with a 32-bit AdamW optimizer;
+ * the pages give no hyper-parameters).  Adam with decoupled weight decay
+ * (the decay scales the weights; it is not added to the gradient); weights
+ * and moments are float32.  Step number `step` (>= 1) sets the bias
+ * corrections.  From the float arguments, in double, each rounded to float
+ * once:
+ *     omb1 = 1 - beta1, omb2 = 1 - beta2, decay = 1 - lr*weight_decay,
+ *     step_size = lr / (1 - beta1^step), inv_bc2 = 1 / sqrt(1 - beta2^step)
+ * then per element, every float operation rounded on its own (no fused
+ * multiply-add; sqrt and division correctly rounded):
+ *     m <- beta1*m + omb1*g
+ *     v <- beta2*v + (omb2*g)*g
+ *     p <- decay*p - step_size*(m / (sqrt(v)*inv_bc2 + eps))
+ *
+ *   A [r x d_in], mA, vA: float32, device, in place; B [d_out x r], mB, vB
+ *   likewise; dA, dB gradients of the same shapes.  dA = NULL freezes A:
+ *   A, mA and vA are then not touched and may be NULL.  Moments start at 0.
+ *   Errors: FALQ_EINVAL for step < 1, beta outside [0, 1), eps <= 0, a
+ *   non-finite lr / eps / weight_decay, or a null or misaligned pointer.
+ */
+falq_status adapter_step_adamw(float *A, float *B, const float *dA, const float *dB,
+                               float *mA, float *vA, float *mB, float *vB,
+                               int64_t r, int64_t d_in, int64_t d_out,
+                               float lr, float beta1, float beta2, float eps,
+                               float weight_decay, int64_t step, falq_stream stream);
 
 /*
  * rowwise_proxy_update — row-wise proxy update ([summary] key design; [intro]:

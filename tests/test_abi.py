@@ -95,6 +95,22 @@ def test_linear_rejects_bad_arguments():
     assert lib.adapter_step(P, P, P, P, -4, 32, 32, 1e-3, None) == EINVAL
 
 
+def test_adamw_rejects_bad_arguments():
+    lib = fq.load()
+    ok = [P, P, P, P, P, P, P, P, 4, 32, 32, 1e-3, 0.9, 0.999, 1e-8, 0.0, 1, None]
+    for idx, val in [(3, None), (6, None), (7, MIS), (0, None), (4, None), (8, -1), (16, 0),
+                     (12, 1.0), (13, -0.1), (14, 0.0), (14, float("inf")), (11, float("nan")),
+                     (15, float("inf"))]:
+        a = list(ok)
+        a[idx] = val
+        assert lib.adapter_step_adamw(*a) == EINVAL, idx
+    # frozen A: A, mA and vA may be null
+    frozen = list(ok)
+    frozen[0] = frozen[2] = frozen[4] = frozen[5] = None
+    a = list(frozen); a[7] = None
+    assert lib.adapter_step_adamw(*a) == EINVAL                  # vB is still required
+
+
 def test_proxy_rejects_bad_arguments():
     lib = fq.load()
     ws = fq.rowwise_proxy_update_workspace_bytes(32, 32, 4)
@@ -104,3 +120,18 @@ def test_proxy_rejects_bad_arguments():
         a = list(ok)
         a[idx] = val
         assert lib.rowwise_proxy_update(*a) == EINVAL, idx
+
+
+def test_melded_linear_buffers_on_host():
+    """MeldedLinear allocates every buffer up front (built here on the CPU
+    device only to check shapes; its calls need the GPU)."""
+    m = fq.MeldedLinear(64, 32, 4, 16, device="cpu", optimizer="adamw",
+                        adamw={"beta1": 0.8, "weight_decay": 0.1})
+    assert m.adamw == {"beta1": 0.8, "beta2": 0.999, "eps": 1e-8, "weight_decay": 0.1}
+    assert m.mA.shape == m.vA.shape == (4, 32) and m.mB.shape == m.vB.shape == (64, 4)
+    assert not m.mB.any() and not m.vB.any()
+    frozen = fq.MeldedLinear(64, 32, 4, 16, device="cpu", optimizer="adamw", train_a=False)
+    assert frozen.dA is None and frozen.mA is None and frozen.vA is None
+    assert fq.MeldedLinear(64, 32, 4, 16, device="cpu").optimizer == "sgd"
+    with pytest.raises(ValueError):
+        fq.MeldedLinear(64, 32, 4, 16, device="cpu", optimizer="adam")

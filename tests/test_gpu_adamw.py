@@ -1,0 +1,73 @@
+"""adapter_step_adamw on the GPU against the oracle: weights and both moments
+bit-exact over consecutive steps (every float operation of the update is
+rounded on its own on both sides; sqrt and division are correctly rounded)."""
+import numpy as np
+import pytest
+
+import oracle
+from tests.gpu_util import announce, dev, host
+
+pytestmark = pytest.mark.gpu
+
+
+def bits(a):
+    return np.asarray(a, np.float32).view(np.uint32)
+
+
+def grads(rng, shape):
+    """gradients over many decades, with zeros and values whose squares are
+    subnormal or underflow"""
+    g = rng.standard_normal(shape) * 10.0 ** rng.uniform(-24, 1, shape)
+    g[rng.random(shape) < 0.02] = 0.0
+    return g.astype(np.float32)
+
+
+@pytest.mark.parametrize("r,d_in,d_out", [(16, 512, 512), (3, 37, 13), (64, 4096, 4096),
+                                          (1, 1, 5)])
+def test_adamw_bit_exact_over_steps(gpu_lib, r, d_in, d_out):
+    announce(f"adapter_step_adamw r {r} d_in {d_in} d_out {d_out}")
+    rng = np.random.default_rng(r * 1000 + d_in)
+    hp = dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01)
+    A = (rng.standard_normal((r, d_in)) / np.sqrt(r)).astype(np.float32)
+    B = (rng.standard_normal((d_out, r)) * 1e-3).astype(np.float32)
+    st = [A, B, np.zeros_like(A), np.zeros_like(A), np.zeros_like(B), np.zeros_like(B)]
+    tA, tB, tmA, tvA, tmB, tvB = (dev(x) for x in st)
+    for step in (1, 2, 3, 1000):
+        dA, dB = grads(rng, A.shape), grads(rng, B.shape)
+        gpu_lib.adapter_step_adamw(tA, tB, dev(dA), dev(dB), tmA, tvA, tmB, tvB, step=step, **hp)
+        A2, B2, mA2, vA2, mB2, vB2 = oracle.adapter_step_adamw(
+            st[0], st[1], dA, dB, st[2], st[3], st[4], st[5], hp["lr"], hp["beta1"],
+            hp["beta2"], hp["eps"], hp["weight_decay"], step)
+        st = [A2, B2, mA2, vA2, mB2, vB2]
+        for name, t, ref in zip(["A", "B", "mA", "vA", "mB", "vB"],
+                                [tA, tB, tmA, tvA, tmB, tvB], st):
+            got = host(t)
+            assert np.array_equal(bits(got), bits(ref)), (step, name)
+
+
+def test_adamw_frozen_a_and_hyper_parameters(gpu_lib):
+    announce("adapter_step_adamw frozen A, beta2 0.95, wd 0.1")
+    rng = np.random.default_rng(7)
+    r, d_in, d_out = 8, 64, 96
+    A = rng.standard_normal((r, d_in)).astype(np.float32)
+    B = rng.standard_normal((d_out, r)).astype(np.float32)
+    mB = (rng.standard_normal((d_out, r)) * 1e-3).astype(np.float32)
+    vB = (rng.random((d_out, r)) * 1e-6).astype(np.float32)
+    dB = grads(rng, B.shape)
+    tA, tB, tmB, tvB = dev(A), dev(B), dev(mB), dev(vB)
+    hp = dict(lr=3e-4, beta1=0.8, beta2=0.95, eps=1e-6, weight_decay=0.1)
+    gpu_lib.adapter_step_adamw(tA, tB, None, dev(dB), None, None, tmB, tvB, step=17, **hp)
+    _, B2, _, _, mB2, vB2 = oracle.adapter_step_adamw(A, B, None, dB, None, None, mB, vB,
+                                                      hp["lr"], hp["beta1"], hp["beta2"],
+                                                      hp["eps"], hp["weight_decay"], 17)
+    assert np.array_equal(host(tA), A)
+    for t, ref in ((tB, B2), (tmB, mB2), (tvB, vB2)):
+        assert np.array_equal(bits(host(t)), bits(ref))
+
+
+def test_adamw_empty(gpu_lib):
+    announce("adapter_step_adamw r = 0")
+    import torch
+    z = torch.zeros((0, 32), device="cuda")
+    zb = torch.zeros((48, 0), device="cuda")
+    gpu_lib.adapter_step_adamw(z, zb, z, zb, z, z, zb, zb, lr=1e-3, step=1)

@@ -2,7 +2,7 @@
 
 Per call on identical inputs the results are bit-exact (codes, rows) or within
 rel-L2 1e-3 (floats).  Within a step, the oracle's dA/dB differ from the
-GPU's at the 1e-6 level, so after SGD its B differs by as little, and two
+GPU's at the 1e-6 level, so after SGD (or AdamW) its B differs by as little, and two
 things may then legitimately differ: a row whose score sits at the threshold
 may be selected by one side only, and a merged element whose dec(q) + t sits
 at a rounding midpoint may round to the neighbouring code.  The test asserts
@@ -20,31 +20,55 @@ import workloads as wl
 pytestmark = pytest.mark.gpu
 
 
-def oracle_step(st, X, dY, lr, tau, k_max=0):
+ADAMW = dict(beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.0)
+
+
+def oracle_step(st, X, dY, lr, tau, k_max=0, opt_step=0, grads=None):
+    """One oracle step from state st; with `grads` = (dA, dB) the adapter
+    optimizer takes those gradients instead of the oracle's own."""
     xq, s_x, _, _ = oracle.fp8_quantize(X)
     y = oracle.melded_linear_fwd(xq, s_x, st["wq"], st["s_w"])
     gq, s_g, _, _ = oracle.fp8_quantize(dY)
     dx, dA, dB = oracle.melded_linear_bwd(gq, s_g, xq, s_x, st["wq"], st["s_w"], st["A"], st["B"])
-    A, B = oracle.adapter_step(st["A"], st["B"], dA, dB, lr)
+    new = {}
+    uA, uB = (dA, dB) if grads is None else grads
+    if opt_step == 0:
+        A, B = oracle.adapter_step(st["A"], st["B"], uA, uB, lr)
+    else:
+        A, B, mA, vA, mB, vB = oracle.adapter_step_adamw(
+            st["A"], st["B"], uA, uB, st["mA"], st["vA"], st["mB"], st["vB"], lr,
+            ADAMW["beta1"], ADAMW["beta2"], ADAMW["eps"], ADAMW["weight_decay"], opt_step)
+        new = dict(mA=mA, vA=vA, mB=mB, vB=vB)
     _, t = oracle.row_scores(st["wq"], st["s_w"], A, B)
     wq, B, sel, rho = oracle.rowwise_proxy_update(st["wq"], st["s_w"], A, B, tau, k_max)
-    return dict(wq=wq, s_w=st["s_w"], A=A, B=B), dict(y=y, dx=dx, dA=dA, dB=dB, sel=sel, rho=rho,
-                                                      t=t)
+    return dict(wq=wq, s_w=st["s_w"], A=A, B=B, **new), dict(y=y, dx=dx, dA=dA, dB=dB, sel=sel,
+                                                             rho=rho, t=t)
 
 
-def run_chain(fq, cfg_id, steps):
+def run_chain(fq, cfg_id, steps, optimizer="sgd"):
     spec = wl.WORKLOADS[cfg_id].linears[0]
     d0 = wl.make_linear(cfg_id, 0, spec, step=0)
-    m = fq.MeldedLinear(spec.d_out, spec.d_in, spec.rank, spec.tokens)
+    m = fq.MeldedLinear(spec.d_out, spec.d_in, spec.rank, spec.tokens, optimizer=optimizer,
+                        adamw=ADAMW)
     m.init_state(dev(d0["W"]), dev(d0["A"]), dev(d0["B"]))
     wq0, s_w, _, _ = oracle.fp8_quantize(d0["W"])
     assert np.array_equal(host(m.wq), wq0)
     st = dict(wq=wq0, s_w=np.float32(s_w), A=d0["A"], B=d0["B"])
+    if optimizer == "adamw":
+        st.update(mA=np.zeros_like(d0["A"]), vA=np.zeros_like(d0["A"]),
+                  mB=np.zeros_like(d0["B"]), vB=np.zeros_like(d0["B"]))
     for step in range(steps):
         d = wl.step_activations(cfg_id, 0, spec, step)
         m.step(dev(d["X"]), dev(d["dY"]), lr=spec.lr, tau=spec.tau, k_max=spec.k_max)
         wq_before = st["wq"]
-        st, out = oracle_step(st, d["X"], d["dY"], spec.lr, spec.tau, spec.k_max)
+        # AdamW's first steps move each element by about lr * sign(g), so a
+        # gradient entry within rounding of zero may step either way: its
+        # optimizer takes the GPU's gradients (checked against the oracle's
+        # below), after which the adapters, moments, scores and codes must
+        # agree bit for bit
+        grads = (host(m.dA), host(m.dB)) if optimizer == "adamw" else None
+        st, out = oracle_step(st, d["X"], d["dY"], spec.lr, spec.tau, spec.k_max,
+                              opt_step=0 if optimizer == "sgd" else step + 1, grads=grads)
         e = (rel_l2(host(m.y), out["y"]), rel_l2(host(m.dx), out["dx"]),
              rel_l2(host(m.dA), out["dA"]), rel_l2(host(m.dB), out["dB"]))
         n_sel = int(host(m.n_sel)[0])
@@ -70,7 +94,15 @@ def run_chain(fq, cfg_id, steps):
         assert np.all(adjacent), "a merged code differs by more than one step"
         assert np.all(near_mid), "a merged code differs away from a rounding midpoint"
         assert rows.size <= 1e-4 * max(1, both.size) * spec.d_in
+        if optimizer == "adamw":
+            assert flips.size == 0 and rows.size == 0
+            for k, t in (("A", m.A), ("B", m.B), ("mA", m.mA), ("vA", m.vA), ("mB", m.mB),
+                         ("vB", m.vB)):
+                assert np.array_equal(host(t).view(np.uint32), st[k].view(np.uint32)), k
+            assert np.array_equal(host(m.rho).view(np.uint32), out["rho"].view(np.uint32))
         st = dict(wq=g_wq, s_w=st["s_w"], A=host(m.A), B=host(m.B))
+        if optimizer == "adamw":
+            st.update(mA=host(m.mA), vA=host(m.vA), mB=host(m.mB), vB=host(m.vB))
 
 
 def test_single_linear_step(gpu_lib):
@@ -81,3 +113,8 @@ def test_single_linear_step(gpu_lib):
 def test_attention_projection_ten_steps(gpu_lib):
     announce("chained steps: 7B attention projection, 10 steps")
     run_chain(gpu_lib, 2, 10)
+
+
+def test_attention_projection_adamw_three_steps(gpu_lib):
+    announce("chained steps: 7B attention projection, 32-bit AdamW, 3 steps")
+    run_chain(gpu_lib, 2, 3, optimizer="adamw")
