@@ -6,11 +6,13 @@ shares no code with fp8_quantized_lora_amd/.
 """
 from . import e4m3
 from .melded import (fp8_quantize, dequantize, melded_linear_fwd, melded_linear_bwd,
-                     adapter_step, adapter_step_adamw, adamw_scalars, adamw_update,
+                     melded_linear_fwd_frozen_a,
+                     melded_linear_bwd_frozen_a, fp8_dequantize, adapter_step, adapter_step_adamw, adamw_scalars, adamw_update,
                      rowwise_proxy_update, row_scores, select_rows,
                      rank_delta, num_threads)
 
 __all__ = ["e4m3", "fp8_quantize", "dequantize", "melded_linear_fwd", "melded_linear_bwd",
+           "melded_linear_fwd_frozen_a", "melded_linear_bwd_frozen_a", "fp8_dequantize",
            "adapter_step", "adapter_step_adamw", "adamw_scalars", "adamw_update",
            "rowwise_proxy_update", "row_scores", "select_rows",
            "rank_delta", "num_threads"]

@@ -171,6 +171,47 @@ def melded_linear_bwd(gq: np.ndarray, s_g: float, xq: np.ndarray, s_x: float,
 
 
 # ----------------------------------------------------------------------------
+# the pages' training setup: frozen FP8 factor A~
+# ----------------------------------------------------------------------------
+def fp8_dequantize(q: np.ndarray, s: float) -> np.ndarray:
+    """DQ(q) = dec(q) / s rounded once to float32 ([P4] thread 2, W8).  The
+    float64 quotient of two float32 values rounded to float32 equals the
+    correctly rounded float32 quotient (53 >= 2*24 + 2 bits)."""
+    return (e4m3.decode(q) / np.float64(np.float32(s))).astype(np.float32)
+
+
+def melded_linear_fwd_frozen_a(xq: np.ndarray, s_x: float, wq: np.ndarray, s_w: float,
+                               aq: np.ndarray, s_a: float) -> Tuple[np.ndarray, np.ndarray]:
+    """Forward of the pages' training setup, where the adapter factor A is
+    frozen and held in FP8 (A~, scale s_a): Y as in melded_linear_fwd, plus
+    the rank-r product that dL/dB needs,
+        U[t,k] = (sum_j dec(X~[t,j]) dec(A~[k,j])) / (s_x s_a)    [T x r]
+    formed while X~ is at hand ([P4] thread 4, Q1: unlike dL/dA, the factor
+    of dL/dB can be computed ahead; thread 2, W1/W9: Figure 2 joins X~ to W~
+    and to A~ by matrix products).  The sums are exact in float64; one
+    division; stored as float32."""
+    y = melded_linear_fwd(xq, s_x, wq, s_w)
+    acc = e4m3.decode(xq) @ e4m3.decode(aq).T
+    u = (acc / (np.float64(np.float32(s_x)) * np.float64(np.float32(s_a)))).astype(np.float32)
+    return y, u
+
+
+def melded_linear_bwd_frozen_a(gq: np.ndarray, s_g: float, wq: np.ndarray, s_w: float,
+                               U: np.ndarray, want_dx: bool = True
+                               ) -> Tuple[Optional[np.ndarray], np.ndarray]:
+    """Backward with A frozen: dX = G^ DQ(W~) as in melded_linear_bwd, and
+    dB = G^^T U with the U of the forward (float32 as given); no dA, so no
+    product with X~ is needed here.  Sums in float64, stored as float32."""
+    gd = e4m3.decode(gq)
+    sg = np.float64(np.float32(s_g))
+    dx = None
+    if want_dx:
+        dx = ((gd @ e4m3.decode(wq)) / (sg * np.float64(np.float32(s_w)))).astype(np.float32)
+    dB = ((gd / sg).T @ np.asarray(U, dtype=np.float64)).astype(np.float32)
+    return dx, dB
+
+
+# ----------------------------------------------------------------------------
 # adapter_step
 # ----------------------------------------------------------------------------
 def adapter_step(A: np.ndarray, B: np.ndarray, dA: Optional[np.ndarray], dB: np.ndarray,
