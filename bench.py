@@ -42,6 +42,9 @@ def parse():
     ap.add_argument("--cpu-tokens", type=int, default=2048,
                     help="token sample for the CPU-oracle baseline (0 = skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--adapter", choices=["trained", "frozen-fp8"], default="trained",
+                    help="A trained in fp32 (dA computed), or the pages' training setup: A "
+                         "frozen in FP8, X~A~^T formed in the forward, no dA")
     ap.add_argument("--optimizer", choices=["sgd", "adamw"], default="sgd",
                     help="adapter optimizer: SGD lr 1e-3 (the workload's) or 32-bit AdamW "
                          "(the pages' training runs)")
@@ -72,7 +75,8 @@ def main():
     T, d_in, d_out, r = spec.tokens, spec.d_in, spec.d_out, spec.rank
 
     d0 = wl.make_linear(2, 0, spec, step=0)
-    m = fq.MeldedLinear(d_out, d_in, r, T, optimizer=args.optimizer)
+    frozen = args.adapter == "frozen-fp8"
+    m = fq.MeldedLinear(d_out, d_in, r, T, optimizer=args.optimizer, fp8_a=frozen)
     t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
     m.init_state(t(d0["W"]), t(d0["A"]), t(d0["B"]))
     batches = []
@@ -87,12 +91,20 @@ def main():
     def calls(i):
         """The step's six boundary calls for batch i, in order."""
         X, dY = batches[i % len(batches)]
+        if frozen:
+            fwd = lambda: fq.melded_linear_fwd_frozen_a(m.xq, m.s_x, m.wq, m.s_w, m.aq, m.s_a,  # noqa: E731
+                                                        m.y, m.u, ws=m.ws_fwd, stream=stream)
+            bwd = lambda: fq.melded_linear_bwd_frozen_a(m.gq, m.s_g, m.wq, m.s_w, m.u, m.dx,  # noqa: E731
+                                                        m.dB, ws=m.ws_bwd, stream=stream)
+        else:
+            fwd = lambda: fq.melded_linear_fwd(m.xq, m.s_x, m.wq, m.s_w, m.y, stream=stream)  # noqa: E731
+            bwd = lambda: fq.melded_linear_bwd(m.gq, m.s_g, m.xq, m.s_x, m.wq, m.s_w, m.A, m.B,  # noqa: E731
+                                               m.dx, m.dA, m.dB, ws=m.ws_bwd, stream=stream)
         return [
             lambda: fq.fp8_quantize(X, m.xq, m.s_x, ws=m.ws_q, stream=stream),
-            lambda: fq.melded_linear_fwd(m.xq, m.s_x, m.wq, m.s_w, m.y, stream=stream),
+            fwd,
             lambda: fq.fp8_quantize(dY, m.gq, m.s_g, ws=m.ws_q, stream=stream),
-            lambda: fq.melded_linear_bwd(m.gq, m.s_g, m.xq, m.s_x, m.wq, m.s_w, m.A, m.B, m.dx,
-                                         m.dA, m.dB, ws=m.ws_bwd, stream=stream),
+            bwd,
             lambda: m.adapter_update(spec.lr, stream=stream),
             lambda: fq.rowwise_proxy_update(m.wq, m.s_w, m.A, m.B, spec.tau, spec.k_max, m.sel,
                                             m.n_sel, rho=m.rho, ws=m.ws_px, stream=stream),
@@ -158,10 +170,10 @@ def main():
     gemm_timed_us = sum(a.elapsed_time(b) for a, b in g_ev) * 1e3 / args.steps
     n_sel = int(m.n_sel.cpu()[0])
 
-    flops = wl.step_flops(T, d_in, d_out, r)
+    flops = wl.step_flops(T, d_in, d_out, r, frozen_a=frozen)
     tflops = flops / (ms_per_step * 1e-3) / 1e12
     tokens_per_s = T / (ms_per_step * 1e-3)
-    gemm_flops = 2 * T * d_in * d_out
+    gemm_flops = 2 * T * d_in * d_out + (2 * T * d_in * r if frozen else 0)
     gemm_us = gemm_timed_us
     gemm_tflops = gemm_flops / (gemm_us * 1e-6) / 1e12
     quant_bytes = T * d_in * 5 + 4                  # fp32 in, E4M3 out, the scale
@@ -186,16 +198,20 @@ def main():
         "config": {"workload": "7B attention projection: W 4096x4096 E4M3, 4096 tokens "
                                "(4 x 1024), 1% outlier channels x20, rank 64, "
                                + ("SGD" if args.optimizer == "sgd" else "32-bit AdamW")
-                               + " lr 1e-3, proxy update every step",
+                               + " lr 1e-3, proxy update every step"
+                               + (", A frozen in FP8 (X~A~^T formed in the forward, no dA)"
+                                  if frozen else ""),
                    "tokens": T, "d_in": d_in, "d_out": d_out, "rank": r,
-                   "optimizer": args.optimizer,
+                   "optimizer": args.optimizer, "adapter": args.adapter,
                    "parallelism": "single GPU"},
         "tokens_per_s": round(tokens_per_s, 1),
-        "roofline": {"kernel": "melded_linear_fwd FP8 GEMM (4096 x 4096 x 4096)",
+        "roofline": {"kernel": ("melded_linear_fwd_frozen_a call (FP8 GEMM 4096 x 4096 x 4096 "
+                                "+ X~A~^T)" if frozen else
+                                "melded_linear_fwd FP8 GEMM (4096 x 4096 x 4096)"),
                      "bound": "mfma", "achieved": round(gemm_tflops, 1),
                      "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(gemm_tflops / FP8_PEAK_TFLOPS, 4),
-                     "traffic": gemm_traffic_bytes()},
+                     "traffic": None if frozen else gemm_traffic_bytes()},
         "per_call_us": {k: round(v, 2) for k, v in per_call_us.items()},
         "launch": "eager launches on one HIP stream",
         "fwd_gemm_us_timed": round(gemm_timed_us, 2),
@@ -207,7 +223,7 @@ def main():
     }
 
     if not args.no_cpu_baseline and args.cpu_tokens > 0:
-        out["cpu_baseline"] = cpu_baseline(spec, d0, args.cpu_tokens, args.optimizer)
+        out["cpu_baseline"] = cpu_baseline(spec, d0, args.cpu_tokens, args.optimizer, frozen)
     print(json.dumps(out), flush=True)
 
 
@@ -253,10 +269,11 @@ def gemm_traffic_bytes():
         return None
 
 
-def cpu_baseline(spec, d0, Ts, optimizer="sgd"):
+def cpu_baseline(spec, d0, Ts, optimizer="sgd", frozen=False):
     """The CPU oracle, as it is, on a token sample of the same workload:
-    quantize X and dY, forward, backward (dX, dA, dB), the adapter step (SGD
-    or AdamW) and the proxy update over the full 4096 x 4096 backbone."""
+    quantize X and dY, forward, backward (dX, dA, dB; or with A frozen in FP8,
+    X~A~^T in the forward and dX, dB), the adapter step (SGD or AdamW) and
+    the proxy update over the full 4096 x 4096 backbone."""
     import numpy as np
 
     import oracle
@@ -266,21 +283,30 @@ def cpu_baseline(spec, d0, Ts, optimizer="sgd"):
     dY = d0["dY"][:Ts]
     t0 = time.perf_counter()
     wq, s_w, _, _ = oracle.fp8_quantize(d0["W"])
+    A0 = d0["A"]
+    if frozen:
+        aq, s_a, _, _ = oracle.fp8_quantize(A0)
+        A0 = oracle.fp8_dequantize(aq, s_a)
     t1 = time.perf_counter()
     xq, s_x, _, _ = oracle.fp8_quantize(X)
-    oracle.melded_linear_fwd(xq, s_x, wq, s_w)
     gq, s_g, _, _ = oracle.fp8_quantize(dY)
-    _, dA, dB = oracle.melded_linear_bwd(gq, s_g, xq, s_x, wq, s_w, d0["A"], d0["B"])
-    if optimizer == "sgd":
-        A, B = oracle.adapter_step(d0["A"], d0["B"], dA, dB, spec.lr)
+    if frozen:
+        _, U = oracle.melded_linear_fwd_frozen_a(xq, s_x, wq, s_w, aq, s_a)
+        _, dB = oracle.melded_linear_bwd_frozen_a(gq, s_g, wq, s_w, U)
+        dA = None
     else:
-        z = [np.zeros_like(d0["A"]), np.zeros_like(d0["B"])]
-        A, B, _, _, _, _ = oracle.adapter_step_adamw(d0["A"], d0["B"], dA, dB, z[0], z[0], z[1],
+        oracle.melded_linear_fwd(xq, s_x, wq, s_w)
+        _, dA, dB = oracle.melded_linear_bwd(gq, s_g, xq, s_x, wq, s_w, A0, d0["B"])
+    if optimizer == "sgd":
+        A, B = oracle.adapter_step(A0, d0["B"], dA, dB, spec.lr)
+    else:
+        z = [np.zeros_like(A0), np.zeros_like(d0["B"])]
+        A, B, _, _, _, _ = oracle.adapter_step_adamw(A0, d0["B"], dA, dB, z[0], z[0], z[1],
                                                      z[1], spec.lr, 0.9, 0.999, 1e-8, 0.0, 1)
     oracle.rowwise_proxy_update(wq, s_w, A, B, spec.tau, spec.k_max)
     t2 = time.perf_counter()
     step_s = t2 - t1
-    flops = wl.step_flops(Ts, spec.d_in, spec.d_out, spec.rank)
+    flops = wl.step_flops(Ts, spec.d_in, spec.d_out, spec.rank, frozen_a=frozen)
     try:
         import threadpoolctl
         blas = threadpoolctl.threadpool_info()
@@ -291,8 +317,8 @@ def cpu_baseline(spec, d0, Ts, optimizer="sgd"):
         blas_threads, oracle.num_threads())), "kind": "oracle",
         "tokens_per_s": round(Ts / step_s, 1),
         "sample": f"one step on the first {Ts} of 4096 tokens (full 4096 x 4096 weight, r=64, "
-                  f"full proxy update), {step_s:.1f} s; the initial weight quantization "
-                  f"({t1 - t0:.1f} s) is not part of the step"}
+                  f"full proxy update), {step_s:.1f} s; the initial quantization of W"
+                  f"{' and A' if frozen else ''} ({t1 - t0:.1f} s) is not part of the step"}
 
 
 if __name__ == "__main__":

@@ -18,7 +18,10 @@ import torch
 
 __all__ = ["load", "FalqError", "fp8_quantize", "fp8_quantize_workspace_bytes",
            "melded_linear_fwd", "melded_linear_bwd", "melded_linear_bwd_workspace_bytes",
-           "adapter_step", "adapter_step_adamw", "rowwise_proxy_update", "rowwise_proxy_update_workspace_bytes",
+           "adapter_step", "adapter_step_adamw", "rowwise_proxy_update",
+           "fp8_dequantize", "melded_linear_fwd_frozen_a",
+           "melded_linear_fwd_frozen_a_workspace_bytes", "melded_linear_bwd_frozen_a",
+           "melded_linear_bwd_frozen_a_workspace_bytes", "rowwise_proxy_update_workspace_bytes",
            "version", "LIB_PATH"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfalqon.so")
@@ -42,6 +45,13 @@ _SIGS = {
     "adapter_step": (_i32, [_c_p, _c_p, _c_p, _c_p, _i64, _i64, _i64, _f32, _c_p]),
     "adapter_step_adamw": (_i32, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _i64, _i64,
                                   _i64, _f32, _f32, _f32, _f32, _f32, _i64, _c_p]),
+    "fp8_dequantize": (_i32, [_c_p, _c_p, _i64, _c_p, _c_p]),
+    "melded_linear_fwd_frozen_a_workspace_bytes": (_sz, [_i64, _i64, _i64]),
+    "melded_linear_fwd_frozen_a": (_i32, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _i64, _i64, _i64,
+                                          _i64, _c_p, _c_p, _c_p, _sz, _c_p]),
+    "melded_linear_bwd_frozen_a_workspace_bytes": (_sz, [_i64, _i64, _i64, _i64]),
+    "melded_linear_bwd_frozen_a": (_i32, [_c_p, _c_p, _c_p, _c_p, _c_p, _i64, _i64, _i64, _i64,
+                                          _c_p, _c_p, _c_p, _sz, _c_p]),
     "rowwise_proxy_update_workspace_bytes": (_sz, [_i64, _i64, _i64]),
     "rowwise_proxy_update": (_i32, [_c_p, _c_p, _c_p, _c_p, _i64, _i64, _i64, _f32, _i64, _c_p,
                                     _c_p, _c_p, _c_p, _sz, _c_p]),
@@ -163,6 +173,62 @@ def melded_linear_bwd(gq, s_g, xq, s_x, wq, s_w, A, B, dx, dA, dB, ws=None, stre
                                     _ptr(A), _ptr(B), T, d_in, d_out, r, _ptr(dx), _ptr(dA),
                                     _ptr(dB), _ptr(ws), ws.numel(), _stream(stream)),
            "melded_linear_bwd")
+
+
+def fp8_dequantize(q: torch.Tensor, scale: torch.Tensor, out: torch.Tensor, stream=None) -> None:
+    """out = dec(q) / scale (float32), elementwise."""
+    _req(q, torch.uint8, tuple(q.shape), "q")
+    _req(out, torch.float32, tuple(q.shape), "out")
+    _req(scale, torch.float32, (1,), "scale")
+    _check(load().fp8_dequantize(_ptr(q), _ptr(scale), q.numel(), _ptr(out), _stream(stream)),
+           "fp8_dequantize")
+
+
+def melded_linear_fwd_frozen_a_workspace_bytes(T: int, d_in: int, r: int) -> int:
+    return int(load().melded_linear_fwd_frozen_a_workspace_bytes(T, d_in, r))
+
+
+def melded_linear_fwd_frozen_a(xq, s_x, wq, s_w, aq, s_a, y, u, ws=None, stream=None) -> None:
+    """y = X~ W~^T / (s_x s_w) and u = X~ A~^T / (s_x s_a)."""
+    T, d_in = xq.shape
+    d_out = wq.shape[0]
+    r = aq.shape[0]
+    _req(xq, torch.uint8, (T, d_in), "xq")
+    _req(wq, torch.uint8, (d_out, d_in), "wq")
+    _req(aq, torch.uint8, (r, d_in), "aq")
+    _req(y, torch.float32, (T, d_out), "y")
+    _req(u, torch.float32, (T, r), "u")
+    need = melded_linear_fwd_frozen_a_workspace_bytes(T, d_in, r)
+    if ws is None:
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=xq.device)
+    _check(load().melded_linear_fwd_frozen_a(_ptr(xq), _ptr(s_x), _ptr(wq), _ptr(s_w), _ptr(aq),
+                                             _ptr(s_a), T, d_in, d_out, r, _ptr(y), _ptr(u),
+                                             _ptr(ws), ws.numel(), _stream(stream)),
+           "melded_linear_fwd_frozen_a")
+
+
+def melded_linear_bwd_frozen_a_workspace_bytes(T: int, d_in: int, d_out: int, r: int) -> int:
+    return int(load().melded_linear_bwd_frozen_a_workspace_bytes(T, d_in, d_out, r))
+
+
+def melded_linear_bwd_frozen_a(gq, s_g, wq, s_w, u, dx, dB, ws=None, stream=None) -> None:
+    """dx = G~ W~ / (s_g s_w) (dx may be None) and dB = G^^T u."""
+    T, d_out = gq.shape
+    d_in = wq.shape[1]
+    r = u.shape[1]
+    _req(gq, torch.uint8, (T, d_out), "gq")
+    _req(wq, torch.uint8, (d_out, d_in), "wq")
+    _req(u, torch.float32, (T, r), "u")
+    _req(dB, torch.float32, (d_out, r), "dB")
+    if dx is not None:
+        _req(dx, torch.float32, (T, d_in), "dx")
+    need = melded_linear_bwd_frozen_a_workspace_bytes(T, d_in, d_out, r)
+    if ws is None:
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=gq.device)
+    _check(load().melded_linear_bwd_frozen_a(_ptr(gq), _ptr(s_g), _ptr(wq), _ptr(s_w), _ptr(u),
+                                             T, d_in, d_out, r, _ptr(dx), _ptr(dB), _ptr(ws),
+                                             ws.numel(), _stream(stream)),
+           "melded_linear_bwd_frozen_a")
 
 
 def adapter_step(A, B, dA, dB, lr: float, stream=None) -> None:

@@ -79,7 +79,9 @@ struct Stage {
   uint32_t ok;           // in-range bits: q (0..3, or 0..15 column-wise), h (16..19)
 };
 
-// P[s][m][n] = sum over k in split s of dec(Q)[m][k] * (Hhi + Hlo)[n][k].
+// P[s][m][n] = sum over k in split s of dec(Q)[m][k] * (Hhi + Hlo)[n][k]
+// (NPL = 2), or of dec(Q)[m][k] * Hhi[n][k] alone (NPL = 1: H exact in bf16,
+// e.g. decoded E4M3 codes).
 // Q is read row-wise (Q[m][k] = codes[m * ldq + k]) or, with TRANS,
 // column-wise (Q[m][k] = codes[k * ldq + m]: contraction over tokens, the
 // 4 x 16-byte transpose done in registers).  LDS holds the FP8 codes
@@ -91,9 +93,10 @@ struct Stage {
 // id is remapped so that each XCD gets a run of consecutive logical ids, i.e.
 // whole (problem, split) groups, whose tiles all read the same K chunk of H:
 // that chunk then comes from HBM into one XCD's L2 once, not once per tile.
-template <bool TRANS>
+template <bool TRANS, int NPL>
 __global__ __launch_bounds__(kSkThreads, 1) void skinny_kernel(Prob p0, Prob p1, int tiles_max,
                                                                int splits) {
+  static_assert(NPL == 1 || NPL == 2, "one or two bf16 planes of H");
   const int nblk = gridDim.x, per = nblk / 8, b = blockIdx.x;
   const int lid = b < per * 8 ? (b % 8) * per + b / 8 : b;
   const int tile = lid % tiles_max, rest = lid / tiles_max;
@@ -146,7 +149,7 @@ __global__ __launch_bounds__(kSkThreads, 1) void skinny_kernel(Prob p0, Prob p1,
       for (int u = 0; u < 4; ++u) R.q[u] = make_uint4(d[4 * u], d[4 * u + 1], d[4 * u + 2], d[4 * u + 3]);
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < 2 * NPL; ++u) {
       const int c = tid + u * kSkThreads;                    // [hi/lo][64 n][16 chunks of 8]
       const int h = c >> 10, rem = c & 1023;
       const int n = rem >> 4, k8 = (rem & 15) * 8;
@@ -199,7 +202,7 @@ __global__ __launch_bounds__(kSkThreads, 1) void skinny_kernel(Prob p0, Prob p1,
       }
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < 2 * NPL; ++u) {
       const int c = tid + u * kSkThreads;
       const int h = c >> 10, rem = c & 1023;
       const int n = rem >> 4, k8 = rem & 15;
@@ -232,12 +235,15 @@ __global__ __launch_bounds__(kSkThreads, 1) void skinny_kernel(Prob p0, Prob p1,
         const int ch = ((q2 & 1) * 4 + half * 2 + sub) ^ swz(n);
         const v8bf bh = __builtin_bit_cast(
             v8bf, *reinterpret_cast<const uint4*>(sH[buf][0][q2 >> 1] + n * 128 + ch * 16));
-        const v8bf bl = __builtin_bit_cast(
-            v8bf, *reinterpret_cast<const uint4*>(sH[buf][1][q2 >> 1] + n * 128 + ch * 16));
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb) {
+        for (int mb = 0; mb < 2; ++mb)
           acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mb][sub], bh, acc[mb], 0, 0, 0);
-          acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mb][sub], bl, acc[mb], 0, 0, 0);
+        if (NPL == 2) {
+          const v8bf bl = __builtin_bit_cast(
+              v8bf, *reinterpret_cast<const uint4*>(sH[buf][1][q2 >> 1] + n * 128 + ch * 16));
+#pragma unroll
+          for (int mb = 0; mb < 2; ++mb)
+            acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[mb][sub], bl, acc[mb], 0, 0, 0);
         }
       }
     }
@@ -336,7 +342,8 @@ __global__ __launch_bounds__(256) void split_bf16_kernel(Split p0, Split p1) {
   }
 }
 
-// out = (1/ *sc) * sum_s P[s] with P[s] of shape [M x N], folded in split
+// out = sum_s P[s] / (*sc * *sc2) with P[s] of shape [M x N] (a null sc or
+// sc2 stands for 1), folded in split
 // order s = 0, 1, ... (deterministic).  A workgroup owns a 16 (m) x 64 (n)
 // tile, one float4 of it per thread, transposed through LDS when the output
 // is n-major.  Two problems per launch (blockIdx.z).
@@ -347,6 +354,7 @@ struct Red {
   const float* P;
   int S, M, N, Mpad;
   const float* sc;
+  const float* sc2;
   int mode;
   float* out;
   int64_t ldo;
@@ -364,7 +372,7 @@ __global__ __launch_bounds__(256) void reduce_kernel(Red r0, Red r1) {
   const int m0 = (tile % R.tilesM) * RM, n0 = (tile / R.tilesM) * 64;
   __shared__ float t[64][RM + 1];
   const int tid = threadIdx.x;
-  const float scale = 1.0f / R.sc[0];
+  const float scale = 1.0f / ((R.sc ? R.sc[0] : 1.0f) * (R.sc2 ? R.sc2[0] : 1.0f));
   const int64_t plane = (int64_t)R.M * R.N;
   const bool vec = (R.N % 4) == 0;
   const int mm = tid >> 4, nn = (tid & 15) * 4;
@@ -428,7 +436,8 @@ __global__ __launch_bounds__(256) void reduce_kernel(Red r0, Red r1) {
 Red red(const float* P, int S, int64_t M, int64_t N, int64_t Mpad, const float* sc, int mode,
         float* out, int64_t ldo, uint16_t* ohi, uint16_t* olo) {
   Red r;
-  r.P = P; r.S = S; r.M = (int)M; r.N = (int)N; r.Mpad = (int)Mpad; r.sc = sc; r.mode = mode;
+  r.P = P; r.S = S; r.M = (int)M; r.N = (int)N; r.Mpad = (int)Mpad; r.sc = sc; r.sc2 = nullptr;
+  r.mode = mode;
   r.out = out; r.ldo = ldo; r.ohi = ohi; r.olo = olo;
   r.tilesM = (int)((std::max(M, Mpad) + RM - 1) / RM);
   r.tilesN = (int)((N + 63) / 64);
@@ -444,6 +453,20 @@ __global__ void fill_kernel(float* p, int64_t n, float v) {
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
        i += (int64_t)gridDim.x * blockDim.x)
     p[i] = v;
+}
+
+// E4M3 codes -> bf16 (exact: 3 mantissa bits), 16 codes per thread; n is a
+// multiple of 16
+__global__ __launch_bounds__(256) void decode_bf16_kernel(const uint8_t* __restrict__ q, int64_t n,
+                                                          uint16_t* __restrict__ out) {
+  const int64_t n16 = n / 16;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const uint4 c = reinterpret_cast<const uint4*>(q)[i];
+    const uint2 a = dec4_bf16(c.x), b = dec4_bf16(c.y), d = dec4_bf16(c.z), e = dec4_bf16(c.w);
+    reinterpret_cast<uint4*>(out)[2 * i] = make_uint4(a.x, a.y, b.x, b.y);
+    reinterpret_cast<uint4*>(out)[2 * i + 1] = make_uint4(d.x, d.y, e.x, e.y);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -511,7 +534,96 @@ Prob prob(const uint8_t* Q, int64_t ldq, const uint16_t* hi, const uint16_t* lo,
   return q;
 }
 
+// Frozen FP8 factor A~: U = dec(X~) dec(A~)^T (one skinny problem, H = the
+// decoded codes, one bf16 plane) and dB = dec(G~)^T U (one problem, H = U^T
+// as bf16 hi/lo).
+struct FrozenPlan {
+  int64_t Tp;
+  int S;                 // K splits
+  int kc;                // K chunk per split
+  size_t off_h, off_lo, off_p, total;
+};
+
+FrozenPlan frozen_u_plan(int64_t T, int64_t d_in, int64_t r) {
+  FrozenPlan p{};
+  const int64_t tiles = (int64_t)ceil_div(T, TM) * ceil_div(r, TN);
+  p.S = pick_splits(tiles, d_in, T * r * 4, 256ll << 20);
+  p.kc = chunk_for(d_in, p.S);
+  size_t o = 0;
+  auto take = [&](size_t bytes) { size_t at = o; o = align_up(o + bytes, 256); return at; };
+  p.off_h = take((size_t)r * d_in * 2);        // decoded A~ [r x d_in] bf16
+  p.off_p = take((size_t)p.S * T * r * 4);     // partials [S][T][r]
+  p.total = o;
+  return p;
+}
+
+FrozenPlan frozen_db_plan(int64_t T, int64_t d_out, int64_t r) {
+  FrozenPlan p{};
+  p.Tp = (T + TK - 1) / TK * TK;
+  const int64_t tiles = (int64_t)ceil_div(d_out, TM) * ceil_div(r, TN);
+  p.S = pick_splits(tiles, T, d_out * r * 4, 256ll << 20);
+  p.kc = chunk_for(T, p.S);
+  size_t o = 0;
+  auto take = [&](size_t bytes) { size_t at = o; o = align_up(o + bytes, 256); return at; };
+  p.off_h = take((size_t)r * p.Tp * 2);        // U^T hi [r x Tp]
+  p.off_lo = take((size_t)r * p.Tp * 2);       // U^T lo
+  p.off_p = take((size_t)p.S * d_out * r * 4); // partials [S][d_out][r]
+  p.total = o;
+  return p;
+}
+
 }  // namespace
+
+size_t frozen_u_ws_bytes(int64_t T, int64_t d_in, int64_t r) {
+  if (r == 0 || T == 0) return 0;
+  return frozen_u_plan(T, d_in, r).total;
+}
+
+size_t frozen_db_ws_bytes(int64_t T, int64_t d_out, int64_t r) {
+  if (r == 0 || T == 0) return 0;
+  return frozen_db_plan(T, d_out, r).total;
+}
+
+hipError_t launch_frozen_u(const uint8_t* xq, const float* s_x, const uint8_t* aq,
+                           const float* s_a, int64_t T, int64_t d_in, int64_t r, float* u,
+                           void* ws, hipStream_t s) {
+  if (r == 0 || T == 0) return hipSuccess;
+  if (d_in == 0) return launch_fill_f32(u, T * r, 0.0f, s);
+  const FrozenPlan pl = frozen_u_plan(T, d_in, r);
+  uint8_t* base = reinterpret_cast<uint8_t*>(ws);
+  uint16_t* h = reinterpret_cast<uint16_t*>(base + pl.off_h);
+  float* part = reinterpret_cast<float*>(base + pl.off_p);
+  {
+    const int64_t n16 = r * d_in / 16;
+    const int blocks = (int)std::min<int64_t>((n16 + 255) / 256, 2048);
+    decode_bf16_kernel<<<blocks, 256, 0, s>>>(aq, r * d_in, h);
+  }
+  const Prob pu = prob(xq, d_in, h, nullptr, d_in, part, T, r, d_in, pl.kc);
+  const int tiles = pu.tilesM * pu.tilesN;
+  skinny_kernel<false, 1><<<tiles * pl.S, kSkThreads, 0, s>>>(pu, pu, tiles, pl.S);
+  Red ru = red(part, pl.S, T, r, T, s_x, 0, u, r, nullptr, nullptr);
+  ru.sc2 = s_a;
+  launch_reduce(ru, nullptr, s);
+  return hipGetLastError();
+}
+
+hipError_t launch_frozen_db(const uint8_t* gq, const float* s_g, const float* u, int64_t T,
+                            int64_t d_out, int64_t r, float* dB, void* ws, hipStream_t s) {
+  if (r == 0 || d_out == 0) return hipSuccess;
+  if (T == 0) return launch_fill_f32(dB, d_out * r, 0.0f, s);
+  const FrozenPlan pl = frozen_db_plan(T, d_out, r);
+  uint8_t* base = reinterpret_cast<uint8_t*>(ws);
+  uint16_t* hi = reinterpret_cast<uint16_t*>(base + pl.off_h);
+  uint16_t* lo = reinterpret_cast<uint16_t*>(base + pl.off_lo);
+  float* part = reinterpret_cast<float*>(base + pl.off_p);
+  // U [T x r] -> U^T as bf16 hi/lo [r x Tp], tokens T..Tp-1 zero (one plane, no scale)
+  launch_reduce(red(u, 1, T, r, pl.Tp, nullptr, 2, nullptr, pl.Tp, hi, lo), nullptr, s);
+  const Prob pb = prob(gq, d_out, hi, lo, pl.Tp, part, d_out, r, T, pl.kc);
+  const int tiles = pb.tilesM * pb.tilesN;
+  skinny_kernel<true, 2><<<tiles * pl.S, kSkThreads, 0, s>>>(pb, pb, tiles, pl.S);
+  launch_reduce(red(part, pl.S, d_out, r, d_out, s_g, 0, dB, r, nullptr, nullptr), nullptr, s);
+  return hipGetLastError();
+}
 
 size_t adapter_grad_ws_bytes(int64_t T, int64_t d_in, int64_t d_out, int64_t r) {
   if (r == 0 || T == 0) return 0;
@@ -558,7 +670,7 @@ hipError_t launch_adapter_grads(const uint8_t* gq, const float* s_g, const uint8
                  pl.kc1v);
   {
     const int tiles = pu.tilesM * pu.tilesN;
-    skinny_kernel<false><<<tiles * pl.S1 * (want_da ? 2 : 1), kSkThreads, 0, s>>>(pu, pv, tiles,
+    skinny_kernel<false, 2><<<tiles * pl.S1 * (want_da ? 2 : 1), kSkThreads, 0, s>>>(pu, pv, tiles,
                                                                                   pl.S1);
   }
   // reduce -> U^T, V^T as bf16 hi/lo [r x Tp], scaled by 1/s_x, 1/s_g
@@ -577,7 +689,7 @@ hipError_t launch_adapter_grads(const uint8_t* gq, const float* s_g, const uint8
                  pl.kc2);
   {
     const int tiles = std::max(pb.tilesM * pb.tilesN, want_da ? pa.tilesM * pa.tilesN : 0);
-    skinny_kernel<true><<<tiles * pl.S2 * (want_da ? 2 : 1), kSkThreads, 0, s>>>(pb, pa, tiles,
+    skinny_kernel<true, 2><<<tiles * pl.S2 * (want_da ? 2 : 1), kSkThreads, 0, s>>>(pb, pa, tiles,
                                                                                  pl.S2);
   }
   {

@@ -30,6 +30,17 @@ inline bool ws_ok(const void* ws, size_t have, size_t need_bytes) {
   return ws != nullptr && aligned(ws, 256) && have >= need_bytes;
 }
 
+// dX = dec(G~) dec(W~) / (s_g s_w) as an NT FP8 GEMM against W~^T, which is
+// written to the first d_in * d_out bytes of the workspace
+hipError_t run_dx(const uint8_t* gq, const float* s_g, const uint8_t* wq, const float* s_w,
+                  int64_t T, int64_t d_in, int64_t d_out, float* dx, uint8_t* wt, hipStream_t s) {
+  if (T * d_in == 0) return hipSuccess;
+  if (d_out == 0) return falq::launch_fill_f32(dx, T * d_in, 0.0f, s);
+  hipError_t e = falq::launch_transpose_u8(wq, d_out, d_in, wt, s);
+  if (e != hipSuccess) return e;
+  return falq::launch_gemm_fp8_nt(gq, d_out, wt, d_out, dx, d_in, T, d_in, d_out, s_g, s_w, s);
+}
+
 }  // namespace
 
 extern "C" {
@@ -107,16 +118,7 @@ falq_status melded_linear_bwd(const uint8_t* gq, const float* s_g, const uint8_t
   uint8_t* base = reinterpret_cast<uint8_t*>(ws);
   const size_t wt_bytes = align_up((size_t)d_in * (size_t)d_out, 256);
   hipError_t e = hipSuccess;
-  if (dx && T * d_in > 0) {
-    if (d_out == 0) {
-      e = falq::launch_fill_f32(dx, T * d_in, 0.0f, s);
-    } else {
-      e = falq::launch_transpose_u8(wq, d_out, d_in, base, s);
-      if (e == hipSuccess)
-        e = falq::launch_gemm_fp8_nt(gq, d_out, base, d_out, dx, d_in, T, d_in, d_out, s_g, s_w, s);
-    }
-    if (e != hipSuccess) return FALQ_EHIP;
-  }
+  if (dx && run_dx(gq, s_g, wq, s_w, T, d_in, d_out, dx, base, s) != hipSuccess) return FALQ_EHIP;
   if (r > 0) {
     if (d_in == 0 || d_out == 0) {
       if (d_out > 0) e = falq::launch_fill_f32(dB, d_out * r, 0.0f, s);
@@ -127,6 +129,66 @@ falq_status melded_linear_bwd(const uint8_t* gq, const float* s_g, const uint8_t
     }
   }
   return hip_status(e);
+}
+
+falq_status fp8_dequantize(const uint8_t* q, const float* scale, int64_t n, float* out,
+                           falq_stream stream) {
+  if (n < 0 || !scalar(scale)) return FALQ_EINVAL;
+  if (n > 0 && (!need(q) || !need(out))) return FALQ_EINVAL;
+  return hip_status(falq::launch_dequantize(q, n, scale, out, reinterpret_cast<hipStream_t>(stream)));
+}
+
+size_t melded_linear_fwd_frozen_a_workspace_bytes(int64_t T, int64_t d_in, int64_t r) {
+  if (T < 0 || d_in < 0 || r < 0) return 0;
+  return falq::frozen_u_ws_bytes(T, d_in, r);
+}
+
+falq_status melded_linear_fwd_frozen_a(const uint8_t* xq, const float* s_x, const uint8_t* wq,
+                                       const float* s_w, const uint8_t* aq, const float* s_a,
+                                       int64_t T, int64_t d_in, int64_t d_out, int64_t r,
+                                       float* y, float* u, void* ws, size_t ws_bytes,
+                                       falq_stream stream) {
+  if (T < 0 || T > ((int64_t)1 << 30) || !dims_ok(d_in) || !dims_ok(d_out) || r < 0 ||
+      r > ((int64_t)1 << 20))
+    return FALQ_EINVAL;
+  if (!scalar(s_a)) return FALQ_EINVAL;
+  if (r * d_in > 0 && !need(aq)) return FALQ_EINVAL;
+  if (T * r > 0 && !need(u)) return FALQ_EINVAL;
+  if (!ws_ok(ws, ws_bytes, melded_linear_fwd_frozen_a_workspace_bytes(T, d_in, r)))
+    return FALQ_EINVAL;
+  const falq_status st = melded_linear_fwd(xq, s_x, wq, s_w, T, d_in, d_out, y, stream);
+  if (st != FALQ_OK) return st;
+  return hip_status(falq::launch_frozen_u(xq, s_x, aq, s_a, T, d_in, r, u, ws,
+                                          reinterpret_cast<hipStream_t>(stream)));
+}
+
+size_t melded_linear_bwd_frozen_a_workspace_bytes(int64_t T, int64_t d_in, int64_t d_out,
+                                                  int64_t r) {
+  if (T < 0 || d_in < 0 || d_out < 0 || r < 0) return 0;
+  const size_t wt = align_up((size_t)d_in * (size_t)d_out, 256);      // W~^T for dX
+  return wt + falq::frozen_db_ws_bytes(T, d_out, r);
+}
+
+falq_status melded_linear_bwd_frozen_a(const uint8_t* gq, const float* s_g, const uint8_t* wq,
+                                       const float* s_w, const float* u, int64_t T, int64_t d_in,
+                                       int64_t d_out, int64_t r, float* dx, float* dB, void* ws,
+                                       size_t ws_bytes, falq_stream stream) {
+  if (T < 0 || T > ((int64_t)1 << 30) || !dims_ok(d_in) || !dims_ok(d_out) || r < 0 ||
+      r > ((int64_t)1 << 20))
+    return FALQ_EINVAL;
+  if (!scalar(s_g) || !scalar(s_w)) return FALQ_EINVAL;
+  if (T * d_out > 0 && !need(gq)) return FALQ_EINVAL;
+  if (d_out * d_in > 0 && dx && !need(wq)) return FALQ_EINVAL;
+  if (!opt(dx)) return FALQ_EINVAL;
+  if (T * r > 0 && !need(u)) return FALQ_EINVAL;
+  if (r * d_out > 0 && !need(dB)) return FALQ_EINVAL;
+  if (!ws_ok(ws, ws_bytes, melded_linear_bwd_frozen_a_workspace_bytes(T, d_in, d_out, r)))
+    return FALQ_EINVAL;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  uint8_t* base = reinterpret_cast<uint8_t*>(ws);
+  const size_t wt_bytes = align_up((size_t)d_in * (size_t)d_out, 256);
+  if (dx && run_dx(gq, s_g, wq, s_w, T, d_in, d_out, dx, base, s) != hipSuccess) return FALQ_EHIP;
+  return hip_status(falq::launch_frozen_db(gq, s_g, u, T, d_out, r, dB, base + wt_bytes, s));
 }
 
 falq_status adapter_step(float* A, float* B, const float* dA, const float* dB, int64_t r,

@@ -15,6 +15,10 @@ hipError_t launch_quantize(const void* x, int dtype, int64_t n, const float* sca
                            uint8_t* q, float* scale, float* amax, int32_t* nonfinite,
                            void* ws, hipStream_t s);
 
+// out[i] = dec(q[i]) / *s (float32, correctly rounded division)
+hipError_t launch_dequantize(const uint8_t* q, int64_t n, const float* s, float* out,
+                             hipStream_t st);
+
 // ---- FP8 GEMMs ------------------------------------------------------------
 // C[M x N] (fp32, row stride ldc) = dec(A)[M x K] . dec(B)[N x K]^T / (sa * sb)
 hipError_t launch_gemm_fp8_nt(const uint8_t* A, int64_t lda, const uint8_t* B, int64_t ldb,
@@ -30,6 +34,16 @@ hipError_t launch_adapter_grads(const uint8_t* gq, const float* s_g, const uint8
                                 const float* s_x, const float* A, const float* B,
                                 int64_t T, int64_t d_in, int64_t d_out, int64_t r,
                                 float* dA, float* dB, void* ws, hipStream_t s);
+
+// frozen FP8 factor A~: u [T x r] = dec(X~) dec(A~)^T / (s_x s_a)
+size_t frozen_u_ws_bytes(int64_t T, int64_t d_in, int64_t r);
+hipError_t launch_frozen_u(const uint8_t* xq, const float* s_x, const uint8_t* aq,
+                           const float* s_a, int64_t T, int64_t d_in, int64_t r, float* u,
+                           void* ws, hipStream_t s);
+// dB [d_out x r] = dec(G~)^T u / s_g
+size_t frozen_db_ws_bytes(int64_t T, int64_t d_out, int64_t r);
+hipError_t launch_frozen_db(const uint8_t* gq, const float* s_g, const float* u, int64_t T,
+                            int64_t d_out, int64_t r, float* dB, void* ws, hipStream_t s);
 
 // ---- SGD ------------------------------------------------------------------
 // two tensors in one launch (either may be empty); 16-byte aligned pointers

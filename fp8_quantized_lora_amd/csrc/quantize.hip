@@ -210,7 +210,38 @@ int blocks_for(int64_t nvec, int unroll, int cap) {
   return (int)b;
 }
 
+// out[i] = dec(q[i]) / s, the float32 division correctly rounded; 16 codes a
+// thread, a scalar tail for n % 16
+__global__ __launch_bounds__(kThreads) void dq_kernel(const uint8_t* __restrict__ q, int64_t n,
+                                                      const float* __restrict__ scale,
+                                                      float* __restrict__ out) {
+  const float s = scale[0];
+  const int64_t n16 = n / 16;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const uint4 c = reinterpret_cast<const uint4*>(q)[i];
+    const uint32_t w[4] = {c.x, c.y, c.z, c.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const float2 a = dec2(w[k], false), b = dec2(w[k], true);
+      reinterpret_cast<float4*>(out)[4 * i + k] = make_float4(a.x / s, a.y / s, b.x / s, b.y / s);
+    }
+  }
+  if (blockIdx.x == 0) {
+    for (int64_t i = n16 * 16 + threadIdx.x; i < n; i += blockDim.x)
+      out[i] = dec2(q[i], false).x / s;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_dequantize(const uint8_t* q, int64_t n, const float* s, float* out,
+                             hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  const int blocks = (int)std::min<int64_t>((n / 16 + kThreads - 1) / kThreads + 1, 2048);
+  dq_kernel<<<blocks, kThreads, 0, st>>>(q, n, s, out);
+  return hipGetLastError();
+}
 
 size_t quantize_ws_bytes() { return (size_t)kQzMaxParts * 8; }
 

@@ -8,7 +8,12 @@ B [d_out x r] (B doubles as the row-wise proxy).  A step is
     -> melded_linear_bwd -> adapter_step (SGD) or adapter_step_adamw
     -> rowwise_proxy_update
 
-with every buffer and workspace allocated once up front, so a step makes no
+With fp8_a=True (the pages' training setup: A frozen and held in FP8), A is
+quantized once to A~ at init, the forward is melded_linear_fwd_frozen_a (Y and
+U = X~ A~^T), the backward melded_linear_bwd_frozen_a (dX and dB from U), and
+the proxy update's A is DQ(A~).
+
+Every buffer and workspace is allocated once up front, so a step makes no
 allocation and no host synchronisation.  This module only sequences calls
 into the HIP library; it computes nothing itself.
 """
@@ -18,19 +23,25 @@ from typing import Optional
 
 import torch
 
-from . import (fp8_quantize, fp8_quantize_workspace_bytes, melded_linear_fwd, melded_linear_bwd,
-               melded_linear_bwd_workspace_bytes, adapter_step, adapter_step_adamw,
+from . import (fp8_quantize, fp8_quantize_workspace_bytes, fp8_dequantize, melded_linear_fwd,
+               melded_linear_bwd, melded_linear_bwd_workspace_bytes, melded_linear_fwd_frozen_a,
+               melded_linear_fwd_frozen_a_workspace_bytes, melded_linear_bwd_frozen_a,
+               melded_linear_bwd_frozen_a_workspace_bytes, adapter_step, adapter_step_adamw,
                rowwise_proxy_update, rowwise_proxy_update_workspace_bytes)
 
 
 class MeldedLinear:
     def __init__(self, d_out: int, d_in: int, rank: int, tokens: int, device="cuda",
                  x_dtype=torch.float32, train_a: bool = True, optimizer: str = "sgd",
-                 adamw: Optional[dict] = None):
+                 adamw: Optional[dict] = None, fp8_a: bool = False):
         """optimizer "sgd" (adapter_step) or "adamw" (adapter_step_adamw, with
-        hyper-parameters `adamw`: beta1, beta2, eps, weight_decay)."""
+        hyper-parameters `adamw`: beta1, beta2, eps, weight_decay); fp8_a
+        freezes A in FP8 (implies train_a=False)."""
         if optimizer not in ("sgd", "adamw"):
             raise ValueError(f"optimizer must be 'sgd' or 'adamw', not {optimizer!r}")
+        if fp8_a:
+            train_a = False
+        self.fp8_a = fp8_a
         self.d_out, self.d_in, self.r, self.T = d_out, d_in, rank, tokens
         self.train_a = train_a
         self.optimizer = optimizer
@@ -52,6 +63,10 @@ class MeldedLinear:
         self.dx = torch.empty((tokens, d_in), dtype=f32, device=dev)
         self.dA = torch.empty((rank, d_in), dtype=f32, device=dev) if train_a else None
         self.dB = torch.empty((d_out, rank), dtype=f32, device=dev)
+        if fp8_a:                         # A~, its scale, and U = X~ A~^T of the forward
+            self.aq = torch.empty((rank, d_in), dtype=u8, device=dev)
+            self.s_a = torch.empty(1, dtype=f32, device=dev)
+            self.u = torch.empty((tokens, rank), dtype=f32, device=dev)
         if optimizer == "adamw":          # first and second moments, zero at the start
             self.mA = torch.zeros((rank, d_in), dtype=f32, device=dev) if train_a else None
             self.vA = torch.zeros((rank, d_in), dtype=f32, device=dev) if train_a else None
@@ -63,8 +78,13 @@ class MeldedLinear:
         # workspaces
         nq = max(tokens * max(d_in, d_out), d_out * d_in)
         self.ws_q = torch.empty(fp8_quantize_workspace_bytes(nq), dtype=u8, device=dev)
-        self.ws_bwd = torch.empty(max(1, melded_linear_bwd_workspace_bytes(tokens, d_in, d_out, rank)),
-                                  dtype=u8, device=dev)
+        if fp8_a:
+            fw = melded_linear_fwd_frozen_a_workspace_bytes(tokens, d_in, rank)
+            bw = melded_linear_bwd_frozen_a_workspace_bytes(tokens, d_in, d_out, rank)
+            self.ws_fwd = torch.empty(max(1, fw), dtype=u8, device=dev)
+        else:
+            bw = melded_linear_bwd_workspace_bytes(tokens, d_in, d_out, rank)
+        self.ws_bwd = torch.empty(max(1, bw), dtype=u8, device=dev)
         self.ws_px = torch.empty(max(1, rowwise_proxy_update_workspace_bytes(d_in, d_out, rank)),
                                  dtype=u8, device=dev)
 
@@ -72,16 +92,29 @@ class MeldedLinear:
         """W~ = E4M3(W * s_w), s_w = 448 / max|W| (the initial quantization
         error is the implicit adapter); A and B copied in."""
         fp8_quantize(W, self.wq, self.s_w, ws=self.ws_q, stream=stream)
-        self.A.copy_(A)
         self.B.copy_(B)
+        if self.fp8_a:                    # A~ = E4M3(A * s_a); the proxy's A is DQ(A~)
+            self.A.copy_(A)
+            fp8_quantize(self.A, self.aq, self.s_a, ws=self.ws_q, stream=stream)
+            fp8_dequantize(self.aq, self.s_a, self.A, stream=stream)
+        else:
+            self.A.copy_(A)
 
     def forward(self, X: torch.Tensor, stream=None):
         fp8_quantize(X, self.xq, self.s_x, ws=self.ws_q, stream=stream)
-        melded_linear_fwd(self.xq, self.s_x, self.wq, self.s_w, self.y, stream=stream)
+        if self.fp8_a:
+            melded_linear_fwd_frozen_a(self.xq, self.s_x, self.wq, self.s_w, self.aq, self.s_a,
+                                       self.y, self.u, ws=self.ws_fwd, stream=stream)
+        else:
+            melded_linear_fwd(self.xq, self.s_x, self.wq, self.s_w, self.y, stream=stream)
         return self.y
 
     def backward(self, dY: torch.Tensor, stream=None):
         fp8_quantize(dY, self.gq, self.s_g, ws=self.ws_q, stream=stream)
+        if self.fp8_a:
+            melded_linear_bwd_frozen_a(self.gq, self.s_g, self.wq, self.s_w, self.u, self.dx,
+                                       self.dB, ws=self.ws_bwd, stream=stream)
+            return self.dx
         melded_linear_bwd(self.gq, self.s_g, self.xq, self.s_x, self.wq, self.s_w, self.A, self.B,
                           self.dx, self.dA, self.dB, ws=self.ws_bwd, stream=stream)
         return self.dx

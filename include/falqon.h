@@ -14,6 +14,10 @@
  *   rowwise_proxy_update   -> W~, B, rows    merge rows whose pending delta
  *                                            survives FP8 rounding
  *
+ * With A frozen in FP8 (the pages' training setup), melded_linear_fwd_frozen_a
+ * and melded_linear_bwd_frozen_a take the place of the forward and backward
+ * calls, and fp8_dequantize gives the proxy update its A.
+ *
  * Pages the calls follow (cited by address and section):
  *   [summary]  shd-paper.top summary of arXiv 2510.24061, "key design"
  *              paragraph (row-wise proxy that accumulates updates and is
@@ -143,6 +147,58 @@ falq_status melded_linear_bwd(const uint8_t *gq, const float *s_g,
                               int64_t T, int64_t d_in, int64_t d_out, int64_t r,
                               float *dx, float *dA, float *dB,
                               void *ws, size_t ws_bytes, falq_stream stream);
+
+/*
+ * The pages' training setup: A frozen and held in FP8 ([rebuttal] thread 4,
+ * Q1: A is frozen, and the x A^T factor of dL/dB, unlike dL/dA, can be
+ * computed ahead; thread 2, W1/W9: Figure 2 joins X~ to W~ and to A~ by
+ * matrix products; thread 2 W2: the adapters are FP8 as well).  A~ is the
+ * E4M3 quantization of A (fp8_quantize, scale s_a), made once.  The forward
+ * then also forms U = X^ A^^T while X~ is at hand, and the backward takes U
+ * for dB instead of contracting X~ again.
+ *
+ * fp8_dequantize — out[i] = dec(q[i]) / s in float32, the division correctly
+ * rounded ([rebuttal] thread 2 W8: DQ).  For the proxy update, whose delta
+ * B . A then uses A = DQ(A~).
+ *   q [n] E4M3 codes, out [n] float32: device, 16-byte aligned; s device float
+ */
+falq_status fp8_dequantize(const uint8_t *q, const float *s, int64_t n, float *out,
+                           falq_stream stream);
+
+/*
+ * melded_linear_fwd_frozen_a — Y exactly as melded_linear_fwd, plus
+ *     U[t,k] = (sum_j dec(xq[t,j]) * dec(aq[k,j])) / (s_x * s_a)   [T x r]
+ * (products of E4M3 values are exact; fp32 accumulation).
+ *   aq [r x d_in] E4M3 codes of A, device; s_a device float
+ *   u  [T x r] float32, device (output), 16-byte aligned
+ *   ws workspace of melded_linear_fwd_frozen_a_workspace_bytes(T, d_in, r)
+ * Other arguments as melded_linear_fwd.
+ */
+size_t melded_linear_fwd_frozen_a_workspace_bytes(int64_t T, int64_t d_in, int64_t r);
+falq_status melded_linear_fwd_frozen_a(const uint8_t *xq, const float *s_x,
+                                       const uint8_t *wq, const float *s_w,
+                                       const uint8_t *aq, const float *s_a,
+                                       int64_t T, int64_t d_in, int64_t d_out, int64_t r,
+                                       float *y, float *u, void *ws, size_t ws_bytes,
+                                       falq_stream stream);
+
+/*
+ * melded_linear_bwd_frozen_a — backward with A frozen:
+ *     dX = G^ . dec(wq)/s_w          (as melded_linear_bwd)
+ *     dB = G^^T U                    [d_out x r], U from the forward
+ * No dA, and no contraction over X~.
+ *   u  [T x r] float32, device (input, as melded_linear_fwd_frozen_a wrote it)
+ *   dx [T x d_in] float32 or NULL (skip); dB [d_out x r] float32 (output)
+ *   ws workspace of melded_linear_bwd_frozen_a_workspace_bytes(T, d_in, d_out, r)
+ * Other arguments as melded_linear_bwd.  With T == 0, dB is written as zeros.
+ */
+size_t melded_linear_bwd_frozen_a_workspace_bytes(int64_t T, int64_t d_in, int64_t d_out,
+                                                  int64_t r);
+falq_status melded_linear_bwd_frozen_a(const uint8_t *gq, const float *s_g,
+                                       const uint8_t *wq, const float *s_w, const float *u,
+                                       int64_t T, int64_t d_in, int64_t d_out, int64_t r,
+                                       float *dx, float *dB, void *ws, size_t ws_bytes,
+                                       falq_stream stream);
 
 /*
  * adapter_step — SGD on the adapter factors, in place, elementwise in fp32

@@ -111,6 +111,26 @@ def test_adamw_rejects_bad_arguments():
     assert lib.adapter_step_adamw(*a) == EINVAL                  # vB is still required
 
 
+def test_frozen_a_calls_reject_bad_arguments():
+    lib = fq.load()
+    assert lib.fp8_dequantize(P, None, 16, P, None) == EINVAL
+    assert lib.fp8_dequantize(MIS, P, 16, P, None) == EINVAL
+    assert lib.fp8_dequantize(P, P, -1, P, None) == EINVAL
+    fw = fq.melded_linear_fwd_frozen_a_workspace_bytes(64, 32, 4)
+    ok = [P, P, P, P, P, P, 64, 32, 48, 4, P, P, P, fw, None]
+    for idx, val in [(4, None), (5, None), (11, None), (11, MIS), (7, 20), (9, -1), (13, fw - 1)]:
+        a = list(ok)
+        a[idx] = val
+        assert lib.melded_linear_fwd_frozen_a(*a) == EINVAL, idx
+    bw = fq.melded_linear_bwd_frozen_a_workspace_bytes(64, 32, 48, 4)
+    assert bw >= 32 * 48
+    ok = [P, P, P, P, P, 64, 32, 48, 4, P, P, P, bw, None]
+    for idx, val in [(4, None), (10, None), (1, None), (9, MIS), (12, bw - 1), (6, 17)]:
+        a = list(ok)
+        a[idx] = val
+        assert lib.melded_linear_bwd_frozen_a(*a) == EINVAL, idx
+
+
 def test_proxy_rejects_bad_arguments():
     lib = fq.load()
     ws = fq.rowwise_proxy_update_workspace_bytes(32, 32, 4)

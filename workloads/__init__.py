@@ -153,7 +153,9 @@ WORKLOADS = {
 RANK_SWEEP = (8, 64, 512, 2048, 8192)
 
 
-def step_flops(T: int, d_in: int, d_out: int, r: int) -> int:
+def step_flops(T: int, d_in: int, d_out: int, r: int, frozen_a: bool = False) -> int:
     """Algorithmic flops of one melded-linear step: forward and dX FP8 GEMMs,
-    the four rank-r adapter contractions, and the rank-r row delta B.A."""
-    return 4 * T * d_in * d_out + 4 * T * r * (d_in + d_out) + 2 * d_out * d_in * r
+    the four rank-r adapter contractions (two with A frozen: X A^T and the dB
+    product), and the rank-r row delta B.A."""
+    adapter = (2 if frozen_a else 4) * T * r * (d_in + d_out)
+    return 4 * T * d_in * d_out + adapter + 2 * d_out * d_in * r
