@@ -156,10 +156,16 @@ falq_status melded_linear_fwd_frozen_a(const uint8_t* xq, const float* s_x, cons
   if (T * r > 0 && !need(u)) return FALQ_EINVAL;
   if (!ws_ok(ws, ws_bytes, melded_linear_fwd_frozen_a_workspace_bytes(T, d_in, r)))
     return FALQ_EINVAL;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (T > 0 && d_in > 0 && falq::gemm_fp8_nt_fuses_second(d_out, d_in, r)) {
+    // U from the forward GEMM's own X~ tiles (one launch)
+    if (!scalar(s_x) || !scalar(s_w) || !need(xq) || !need(wq) || !need(y)) return FALQ_EINVAL;
+    return hip_status(falq::launch_gemm_fp8_nt_second(xq, d_in, wq, d_in, y, d_out, T, d_out, d_in,
+                                                      s_x, s_w, aq, d_in, r, u, r, s_a, s));
+  }
   const falq_status st = melded_linear_fwd(xq, s_x, wq, s_w, T, d_in, d_out, y, stream);
   if (st != FALQ_OK) return st;
-  return hip_status(falq::launch_frozen_u(xq, s_x, aq, s_a, T, d_in, r, u, ws,
-                                          reinterpret_cast<hipStream_t>(stream)));
+  return hip_status(falq::launch_frozen_u(xq, s_x, aq, s_a, T, d_in, r, u, ws, s));
 }
 
 size_t melded_linear_bwd_frozen_a_workspace_bytes(int64_t T, int64_t d_in, int64_t d_out,

@@ -75,8 +75,8 @@ hipError_t launch_gemm_fp8_nt(const uint8_t* A, int64_t lda, const uint8_t* B, i
   if (K % gemm::dma::BK == 0) {
     const int tM = (int)((M + gemm::dma::BM - 1) / gemm::dma::BM);
     const int tN = (int)((N + gemm::dma::BN - 1) / gemm::dma::BN);
-    gemm::dma::gemm_fp8_nt_dma<<<tM * tN, gemm::dma::kThreads, 0, s>>>(
-        A, lda, B, ldb, C, ldc, (int)M, (int)N, (int)K, sa, sb, tM, tN);
+    gemm::dma::gemm_fp8_nt_dma<false><<<tM * tN, gemm::dma::kThreads, 0, s>>>(
+        A, lda, B, ldb, C, ldc, (int)M, (int)N, (int)K, sa, sb, tM, tN, gemm::dma::SecondB{});
     return hipGetLastError();
   }
   using Cf = gemm::Cfg<256, 256, 128, 2, 2>;
@@ -84,6 +84,27 @@ hipError_t launch_gemm_fp8_nt(const uint8_t* A, int64_t lda, const uint8_t* B, i
   const int tilesN = (int)((N + Cf::BN - 1) / Cf::BN);
   gemm::gemm_fp8_nt_kernel<Cf><<<tilesM * tilesN, Cf::kThreads, 0, s>>>(
       A, lda, B, ldb, C, ldc, (int)M, (int)N, (int)K, sa, sb, tilesM, tilesN);
+  return hipGetLastError();
+}
+
+bool gemm_fp8_nt_fuses_second(int64_t N, int64_t K, int64_t R) {
+  if (R <= 0 || K <= 0 || K % gemm::dma::BK != 0) return false;
+  const int64_t tN = (N + gemm::dma::BN - 1) / gemm::dma::BN;
+  return 4 * ((R + gemm::dma::UR - 1) / gemm::dma::UR) <= tN;
+}
+
+hipError_t launch_gemm_fp8_nt_second(const uint8_t* A, int64_t lda, const uint8_t* B, int64_t ldb,
+                                     float* C, int64_t ldc, int64_t M, int64_t N, int64_t K,
+                                     const float* sa, const float* sb, const uint8_t* Bu,
+                                     int64_t ldbu, int64_t R, float* Cu, int64_t ldcu,
+                                     const float* sbu, hipStream_t s) {
+  if (M == 0) return hipSuccess;
+  if (!gemm_fp8_nt_fuses_second(N, K, R)) return hipErrorInvalidValue;
+  const int tM = (int)((M + gemm::dma::BM - 1) / gemm::dma::BM);
+  const int tN = (int)((N + gemm::dma::BN - 1) / gemm::dma::BN);
+  gemm::dma::gemm_fp8_nt_dma<true><<<tM * tN, gemm::dma::kThreads, 0, s>>>(
+      A, lda, B, ldb, C, ldc, (int)M, (int)N, (int)K, sa, sb, tM, tN,
+      gemm::dma::SecondB{Bu, ldbu, (int)R, Cu, ldcu, sbu});
   return hipGetLastError();
 }
 

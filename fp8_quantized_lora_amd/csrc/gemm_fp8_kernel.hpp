@@ -186,20 +186,45 @@ constexpr int BM = 256, BN = 256, BK = 128, WGM = 2, WGN = 4, S = 2;
 __device__ __forceinline__ int swz(int row) { return (row ^ ((row >> 3) & 1)) & 7; }
 constexpr int NW = WGM * WGN, kThreads = NW * 64;
 constexpr int WTM = BM / WGM, WTN = BN / WGN, MB = WTM / 16, NB = WTN / 16;
-constexpr int STAGE = (BM + BN) * BK;
+constexpr int UR = 16;                                  // rank rows of the second B operand
+constexpr int STAGE = (BM + BN) * BK, STAGE_U = STAGE + UR * BK;
 constexpr int AI = BM * BK / 1024 / NW, BI = BN * BK / 1024 / NW;   // DMA instructions / wave / stage
 constexpr int LPS = AI + BI;
-static_assert(S * STAGE <= 160 * 1024, "LDS");
+static_assert(S * STAGE_U <= 160 * 1024, "LDS");
 
+// Optional second product against a small second B operand (the frozen
+// adapter factor A~ in the forward: U = dec(X~) dec(A~)^T / (sa * su)).  Its
+// 16-rank blocks times 64-row quarters of a tile are "units"; the tile in
+// column tn < 4 * ceil(R / 16) takes unit tn: block tn / 4, quarter tn % 4.
+// The quarter's rows are held by the four waves of row group wm = quarter / 2,
+// so each of them issues one more MFMA per K step (on its fragment
+// i = (quarter % 2) * 4 + wn), one per SIMD.
+struct SecondB {
+  const uint8_t* B;      // [R x K] codes, row stride ldb
+  int64_t ldb;
+  int R;
+  float* C;              // [M x R] fp32 output, row stride ldc
+  int64_t ldc;
+  const float* sb;
+};
+
+template <bool FU>
 __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_nt_dma(
     const uint8_t* __restrict__ A, int64_t lda, const uint8_t* __restrict__ B, int64_t ldb,
     float* __restrict__ C, int64_t ldc, int M, int N, int K, const float* __restrict__ sa,
-    const float* __restrict__ sb, int tilesM, int tilesN) {
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[S * STAGE];
+    const float* __restrict__ sb, int tilesM, int tilesN, SecondB u) {
+  constexpr int SB = FU ? STAGE_U : STAGE;                 // bytes per LDS stage
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[S * SB];
   int tm, tn;
   tile_coords(tilesM, tilesN, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, wm = w / WGN, wn = w % WGN;
+  // second product: this tile's unit (block ub, quarter uq), if any
+  const bool has_u = FU && tn < 4 * ((u.R + UR - 1) / UR);
+  const int ub = tn >> 2, uq = tn & 3;
+  // wave-uniform (read from lane 0), so the extra MFMA sits behind a scalar branch
+  const bool wave_u = __builtin_amdgcn_readfirstlane((int)(has_u && wm == (uq >> 1))) != 0;
+  const int iu = __builtin_amdgcn_readfirstlane((uq & 1) * 4 + wn);   // the wave's fragment
 
   v4f acc[MB][NB];
 #pragma unroll
@@ -224,14 +249,23 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_nt_dma(
     const int row = (w * BI + j) * 8 + lrow;
     gB[j] = B + (int64_t)min(n0 + row, N - 1) * ldb + ((lslot ^ swz(row)) * 16);
   }
+  // the 16 rank rows of the unit's block: waves 0 and 1 load 8 rows each
+  const bool load_u = __builtin_amdgcn_readfirstlane((int)(has_u && w < 2)) != 0;
+  const uint8_t* gU = nullptr;
+  if (FU && load_u) {
+    const int row = w * 8 + lrow;
+    gU = u.B + (int64_t)min(ub * UR + row, u.R - 1) * u.ldb + ((lslot ^ swz(row)) * 16);
+  }
   auto issue = [&](int stage, int k0) {
-    const uint32_t base = lds_offset(smem + stage * STAGE);
+    const uint32_t base = lds_offset(smem + stage * SB);
     const uint32_t la = __builtin_amdgcn_readfirstlane(base + w * AI * 1024);
     const uint32_t lb = __builtin_amdgcn_readfirstlane(base + BM * BK + w * BI * 1024);
 #pragma unroll
     for (int j = 0; j < AI; ++j) load16_to_lds(gA[j] + k0, la + j * 1024);
 #pragma unroll
     for (int j = 0; j < BI; ++j) load16_to_lds(gB[j] + k0, lb + j * 1024);
+    if (FU && load_u)
+      load16_to_lds(gU + k0, __builtin_amdgcn_readfirstlane(base + (BM + BN) * BK + w * 1024));
   };
 
   const int nk = K / BK;
@@ -250,23 +284,30 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_nt_dma(
   // treats each step's LDS reads as returning in order and waits only for the
   // fragments the next MFMA needs.
   const float scale = 1.0f / (sa[0] * sb[0]);
+  const float scale_u = FU ? 1.0f / (sa[0] * u.sb[0]) : 0.0f;
+  v4f accu;
+#pragma unroll
+  for (int v = 0; v < 4; ++v) accu[v] = 0.0f;
+  const int offU = (BM + BN) * BK + r16 * BK;
   __builtin_amdgcn_s_waitcnt(0xC07F);                        // lgkmcnt(0)
   for (int kt = 0; kt < nk; ++kt) {
     // stage kt has landed once at most (stages issued after it) * LPS loads are in flight
     wait_vmem(min(S - 2, nk - 1 - kt) * LPS);
     barrier_no_drain();
-    const uint8_t* st = smem + (kt % S) * STAGE;
+    const uint8_t* st = smem + (kt % S) * SB;
     // Fragment reads in the order the MFMAs consume them (A0, B0..B3, then
     // A(i+1) ahead of the MFMAs on A(i)); scheduling barriers keep the
     // compiler from reordering them, so the first MFMA waits for 4 reads,
     // not 12.
-    v8i bf[NB], af[2];
+    v8i bf[NB], af[2], bu;
     af[0] = frag(st + offA);
 #pragma unroll
     for (int j = 0; j < NB; ++j) {
       bf[j] = frag(st + offB + j * 16 * BK);
       __builtin_amdgcn_sched_barrier(0);
     }
+    if (FU && wave_u) bu = frag(st + offU);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < MB; ++i) {
       if (i + 1 < MB) af[(i + 1) & 1] = frag(st + offA + (i + 1) * 16 * BK);
@@ -275,6 +316,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_nt_dma(
       for (int j = 0; j < NB; ++j)
         acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[i & 1], bf[j], acc[i][j], 0,
                                                                      0, 0, 0, 0, 0);
+      if (FU && wave_u && i == iu)
+        accu = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[i & 1], bu, accu, 0, 0, 0, 0, 0,
+                                                                0);
       __builtin_amdgcn_sched_barrier(0);
       // the next stage's direct loads go out once this step's first
       // fragments are in registers (an inline-asm load ahead of the first
@@ -298,6 +342,16 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_nt_dma(
         if (row < M) C[(int64_t)row * ldc + col] = acc[i][j][v] * scale;
       }
     }
+  if (FU && wave_u) {
+    const int rank = ub * UR + (lane & 15);
+    if (rank < u.R) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int row = m0 + uq * 64 + wn * 16 + 4 * (lane >> 4) + v;
+        if (row < M) u.C[(int64_t)row * u.ldc + rank] = accu[v] * scale_u;
+      }
+    }
+  }
 }
 
 }  // namespace dma

@@ -24,6 +24,15 @@ hipError_t launch_dequantize(const uint8_t* q, int64_t n, const float* s, float*
 hipError_t launch_gemm_fp8_nt(const uint8_t* A, int64_t lda, const uint8_t* B, int64_t ldb,
                               float* C, int64_t ldc, int64_t M, int64_t N, int64_t K,
                               const float* sa, const float* sb, hipStream_t s);
+// The same product plus Cu[M x R] = dec(A) . dec(Bu)[R x K]^T / (sa * sbu) in
+// the same launch (the DMA kernel's extra units); only where
+// gemm_fp8_nt_fuses_second(N, K, R) holds
+bool gemm_fp8_nt_fuses_second(int64_t N, int64_t K, int64_t R);
+hipError_t launch_gemm_fp8_nt_second(const uint8_t* A, int64_t lda, const uint8_t* B, int64_t ldb,
+                                     float* C, int64_t ldc, int64_t M, int64_t N, int64_t K,
+                                     const float* sa, const float* sb, const uint8_t* Bu,
+                                     int64_t ldbu, int64_t R, float* Cu, int64_t ldcu,
+                                     const float* sbu, hipStream_t s);
 // out[cols x rows] = in[rows x cols]^T (bytes; rows and cols multiples of 16)
 hipError_t launch_transpose_u8(const uint8_t* in, int64_t rows, int64_t cols, uint8_t* out,
                                hipStream_t s);

@@ -38,8 +38,14 @@ def test_dequantize_bit_exact(gpu_lib):
         assert np.array_equal(host(out).view(np.uint32), ref.view(np.uint32)), n
 
 
+# the forward forms U inside the FP8 GEMM when d_in % 128 == 0 and the tile
+# columns (d_out / 256) number at least 4 * ceil(r / 16): the 4096, (300, 256,
+# 1024, 13), (512, 384, 2048, 32) and (200, 128, 1040, 16) cases; the others
+# take the separate kernels
 @pytest.mark.parametrize("T,d_in,d_out,r", [(256, 512, 512, 16), (777, 48, 80, 5),
-                                            (300, 128, 64, 70), (4096, 4096, 4096, 64)])
+                                            (300, 128, 64, 70), (300, 256, 1024, 13),
+                                            (512, 384, 2048, 32), (200, 128, 1040, 16),
+                                            (4096, 4096, 4096, 64)])
 def test_frozen_fwd_bwd(gpu_lib, T, d_in, d_out, r):
     announce(f"frozen-A fwd/bwd T {T} d_in {d_in} d_out {d_out} r {r}")
     q = problem(T + d_in + r, T, d_in, d_out, r)
