@@ -45,6 +45,9 @@ def parse():
     ap.add_argument("--adapter", choices=["trained", "frozen-fp8"], default="trained",
                     help="A trained in fp32 (dA computed), or the pages' training setup: A "
                          "frozen in FP8, X~A~^T formed in the forward, no dA")
+    ap.add_argument("--merge-every", type=int, default=1,
+                    help="run the row-wise proxy update on every N-th step (B accumulates "
+                         "the adapter updates in between)")
     ap.add_argument("--optimizer", choices=["sgd", "adamw"], default="sgd",
                     help="adapter optimizer: SGD lr 1e-3 (the workload's) or 32-bit AdamW "
                          "(the pages' training runs)")
@@ -88,8 +91,16 @@ def main():
     stream = torch.cuda.current_stream()
     names = ["quantize_x", "fwd_gemm", "quantize_dy", "bwd", "adapter_step", "proxy_update"]
 
+    if args.merge_every < 1:
+        sys.exit("--merge-every must be >= 1")
+
+    def merges(i):
+        """whether step i (0-based) ends with the proxy update"""
+        return (i + 1) % args.merge_every == 0
+
     def calls(i):
-        """The step's six boundary calls for batch i, in order."""
+        """The step's six boundary calls for batch i, in order (the last one a
+        no-op on steps without a merge)."""
         X, dY = batches[i % len(batches)]
         if frozen:
             fwd = lambda: fq.melded_linear_fwd_frozen_a(m.xq, m.s_x, m.wq, m.s_w, m.aq, m.s_a,  # noqa: E731
@@ -106,8 +117,9 @@ def main():
             lambda: fq.fp8_quantize(dY, m.gq, m.s_g, ws=m.ws_q, stream=stream),
             bwd,
             lambda: m.adapter_update(spec.lr, stream=stream),
-            lambda: fq.rowwise_proxy_update(m.wq, m.s_w, m.A, m.B, spec.tau, spec.k_max, m.sel,
-                                            m.n_sel, rho=m.rho, ws=m.ws_px, stream=stream),
+            (lambda: fq.rowwise_proxy_update(m.wq, m.s_w, m.A, m.B, spec.tau, spec.k_max, m.sel,
+                                             m.n_sel, rho=m.rho, ws=m.ws_px, stream=stream))
+            if merges(i) else (lambda: None),
         ]
 
     for i in range(args.warmup):
@@ -117,7 +129,7 @@ def main():
 
     # Per-call durations (reported beside the result, not part of the timed
     # region): HIP events between the calls of a few eager steps.
-    n_pc = max(3, min(args.steps, 10))
+    n_pc = max(3, min(args.steps, 10), args.merge_every)
     pc = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
           for _ in range(n_pc)]
     for i in range(n_pc):
@@ -128,6 +140,11 @@ def main():
     torch.cuda.synchronize()
     per_call_us = {n: sum(pc[i][k].elapsed_time(pc[i][k + 1]) for i in range(n_pc)) * 1e3 / n_pc
                    for k, n in enumerate(names)}
+    # the proxy update's own duration: averaged over the steps that ran it
+    n_merge = sum(merges(args.warmup + i) for i in range(n_pc))
+    per_call_us["proxy_update"] = sum(
+        pc[i][5].elapsed_time(pc[i][6]) for i in range(n_pc) if merges(args.warmup + i)
+    ) * 1e3 / max(1, n_merge)
 
     # A plain device copy of known size, for scaling the HBM byte counters of
     # a profiler run (not part of the timed region).
@@ -170,7 +187,10 @@ def main():
     gemm_timed_us = sum(a.elapsed_time(b) for a, b in g_ev) * 1e3 / args.steps
     n_sel = int(m.n_sel.cpu()[0])
 
-    flops = wl.step_flops(T, d_in, d_out, r, frozen_a=frozen)
+    # the rank-r row delta B.A is computed on merge steps only
+    n_merge_timed = sum(merges(args.warmup + n_pc + i) for i in range(args.steps))
+    flops = (wl.step_flops(T, d_in, d_out, r, frozen_a=frozen)
+             - 2 * d_out * d_in * r * (1 - n_merge_timed / args.steps))
     tflops = flops / (ms_per_step * 1e-3) / 1e12
     tokens_per_s = T / (ms_per_step * 1e-3)
     gemm_flops = 2 * T * d_in * d_out + (2 * T * d_in * r if frozen else 0)
@@ -198,11 +218,13 @@ def main():
         "config": {"workload": "7B attention projection: W 4096x4096 E4M3, 4096 tokens "
                                "(4 x 1024), 1% outlier channels x20, rank 64, "
                                + ("SGD" if args.optimizer == "sgd" else "32-bit AdamW")
-                               + " lr 1e-3, proxy update every step"
+                               + " lr 1e-3, proxy update every "
+                               + ("step" if args.merge_every == 1 else f"{args.merge_every} steps")
                                + (", A frozen in FP8 (X~A~^T formed in the forward, no dA)"
                                   if frozen else ""),
                    "tokens": T, "d_in": d_in, "d_out": d_out, "rank": r,
                    "optimizer": args.optimizer, "adapter": args.adapter,
+                   "merge_every": args.merge_every,
                    "parallelism": "single GPU"},
         "tokens_per_s": round(tokens_per_s, 1),
         "roofline": {"kernel": ("melded_linear_fwd_frozen_a call (FP8 GEMM 4096 x 4096 x 4096 "

@@ -127,13 +127,25 @@ class MeldedLinear:
             adapter_step_adamw(self.A, self.B, self.dA, self.dB, self.mA, self.vA, self.mB,
                                self.vB, lr, self.opt_step, stream=stream, **self.adamw)
 
-    def update(self, lr: float, tau: float, k_max: int = 0, stream=None):
-        self.adapter_update(lr, stream)
+    def merge(self, tau: float, k_max: int = 0, stream=None):
         rowwise_proxy_update(self.wq, self.s_w, self.A, self.B, tau, k_max, self.sel, self.n_sel,
                              rho=self.rho, ws=self.ws_px, stream=stream)
 
+    def update(self, lr: float, tau: float, k_max: int = 0, stream=None, merge: bool = True):
+        """Adapter step, then (if `merge`) the row-wise proxy update.  Between
+        merges B keeps accumulating the adapter updates: B is the proxy, merged
+        into W~ periodically."""
+        self.adapter_update(lr, stream)
+        if merge:
+            self.merge(tau, k_max, stream)
+
     def step(self, X: torch.Tensor, dY: torch.Tensor, lr: float = 1e-3, tau: float = 0.5,
-             k_max: int = 0, stream=None):
+             k_max: int = 0, stream=None, merge_every: int = 1):
+        """One training step; the proxy is merged into W~ on every
+        `merge_every`-th step (counted by this layer)."""
+        if merge_every < 1:
+            raise ValueError("merge_every must be >= 1")
+        self.n_steps = getattr(self, "n_steps", 0) + 1
         self.forward(X, stream)
         self.backward(dY, stream)
-        self.update(lr, tau, k_max, stream)
+        self.update(lr, tau, k_max, stream, merge=self.n_steps % merge_every == 0)

@@ -118,3 +118,39 @@ def test_attention_projection_ten_steps(gpu_lib):
 def test_attention_projection_adamw_three_steps(gpu_lib):
     announce("chained steps: 7B attention projection, 32-bit AdamW, 3 steps")
     run_chain(gpu_lib, 2, 3, optimizer="adamw")
+
+
+def test_merge_interval(gpu_lib):
+    """Proxy merged every third step (the pages merge the accumulated proxy
+    into the backbone periodically): between merges W~ is untouched and B
+    accumulates the SGD updates; on merge steps the oracle's proxy update,
+    given the GPU's adapter gradients, yields the same rows, codes and B bit
+    for bit."""
+    announce("merge every 3 steps: 512 x 512 single linear, 6 steps")
+    spec = wl.WORKLOADS[1].linears[0]
+    d0 = wl.make_linear(1, 0, spec, step=0)
+    m = gpu_lib.MeldedLinear(spec.d_out, spec.d_in, spec.rank, spec.tokens)
+    m.init_state(dev(d0["W"]), dev(d0["A"]), dev(d0["B"]))
+    wq, s_w, _, _ = oracle.fp8_quantize(d0["W"])
+    A, B = d0["A"], d0["B"]
+    merged_rows = 0
+    for step in range(6):
+        d = wl.step_activations(1, 0, spec, step)
+        m.step(dev(d["X"]), dev(d["dY"]), lr=spec.lr, tau=spec.tau, k_max=spec.k_max,
+               merge_every=3)
+        xq, s_x, _, _ = oracle.fp8_quantize(d["X"])
+        gq, s_g, _, _ = oracle.fp8_quantize(d["dY"])
+        _, rdA, rdB = oracle.melded_linear_bwd(gq, s_g, xq, s_x, wq, s_w, A, B, want_dx=False)
+        gdA, gdB = host(m.dA), host(m.dB)
+        assert rel_l2(gdA, rdA) <= TOL and rel_l2(gdB, rdB) <= TOL
+        A, B = oracle.adapter_step(A, B, gdA, gdB, spec.lr)
+        if (step + 1) % 3 == 0:
+            wq, B, sel, _ = oracle.rowwise_proxy_update(wq, s_w, A, B, spec.tau, spec.k_max)
+            n_sel = int(host(m.n_sel)[0])
+            assert np.array_equal(host(m.sel)[:n_sel], sel)
+            merged_rows += n_sel
+        assert np.array_equal(host(m.wq), wq), step
+        assert np.array_equal(host(m.A).view(np.uint32), A.view(np.uint32)), step
+        assert np.array_equal(host(m.B).view(np.uint32), B.view(np.uint32)), step
+    print(f"rows merged over 2 merges: {merged_rows}")
+    assert merged_rows > 0
