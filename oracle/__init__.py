@@ -4,14 +4,14 @@ TEST INFRASTRUCTURE ONLY: imported by tests/, by the smoke check and by the
 CPU-baseline leg of bench.py, never by the HIP library or its binding.  It
 shares no code with fp8_quantized_lora_amd/.
 """
-from . import e4m3
+from . import e4m3, e5m2
 from .melded import (fp8_quantize, dequantize, melded_linear_fwd, melded_linear_bwd,
                      melded_linear_fwd_frozen_a,
                      melded_linear_bwd_frozen_a, fp8_dequantize, adapter_step, adapter_step_adamw, adamw_scalars, adamw_update,
                      rowwise_proxy_update, row_scores, select_rows,
                      rank_delta, num_threads)
 
-__all__ = ["e4m3", "fp8_quantize", "dequantize", "melded_linear_fwd", "melded_linear_bwd",
+__all__ = ["e4m3", "e5m2", "fp8_quantize", "dequantize", "melded_linear_fwd", "melded_linear_bwd",
            "melded_linear_fwd_frozen_a", "melded_linear_bwd_frozen_a", "fp8_dequantize",
            "adapter_step", "adapter_step_adamw", "adamw_scalars", "adamw_update",
            "rowwise_proxy_update", "row_scores", "select_rows",

@@ -32,7 +32,9 @@ from typing import Optional, Tuple
 
 import numpy as np
 
-from . import e4m3
+from . import e4m3, e5m2
+
+FORMATS = {"e4m3": (e4m3, 448.0), "e5m2": (e5m2, 57344.0)}
 
 FLT_MAX = np.float32(np.finfo(np.float32).max)
 
@@ -64,7 +66,7 @@ def num_threads() -> int:
 # ----------------------------------------------------------------------------
 # fp8_quantize
 # ----------------------------------------------------------------------------
-def fp8_quantize(x: np.ndarray, scale_in: Optional[float] = None
+def fp8_quantize(x: np.ndarray, scale_in: Optional[float] = None, fmt: str = "e4m3"
                  ) -> Tuple[np.ndarray, np.float32, np.float32, int]:
     """Per-tensor current-scaled quantization to E4M3 ([P4] thread 2, W2: a
     high-precision tensor X is multiplied by a per-tensor factor s_X and the
@@ -77,6 +79,8 @@ def fp8_quantize(x: np.ndarray, scale_in: Optional[float] = None
       v    = fl32(x * s)            (one float32 rounding)
       q    = E4M3 encode of v       (nearest, ties to even, saturating)
     When `scale_in` is given, s = scale_in and amax is still reported.
+    fmt = "e5m2" uses E5M2 codes and 57344 in place of 448 (the largest
+    finite value of each format).
 
     `x` is float32, or uint16 holding bfloat16 bit patterns (widened exactly).
     Returns (codes uint8, s float32, amax float32, number of non-finite inputs).
@@ -95,12 +99,12 @@ def fp8_quantize(x: np.ndarray, scale_in: Optional[float] = None
         s = np.float32(1.0)
     else:
         with np.errstate(over="ignore"):
-            s = np.float32(448.0) / amax
+            s = np.float32(FORMATS[fmt][1]) / amax
         if not np.isfinite(s):
             s = FLT_MAX
     with np.errstate(over="ignore", invalid="ignore"):
         v = (xf * s).astype(np.float32)
-    return e4m3.encode(v), np.float32(s), np.float32(amax), n_bad
+    return FORMATS[fmt][0].encode(v), np.float32(s), np.float32(amax), n_bad
 
 
 def dequantize(q: np.ndarray, s: float) -> np.ndarray:
@@ -134,7 +138,7 @@ def melded_linear_fwd(xq: np.ndarray, s_x: float, wq: np.ndarray, s_w: float) ->
 # ----------------------------------------------------------------------------
 def melded_linear_bwd(gq: np.ndarray, s_g: float, xq: np.ndarray, s_x: float,
                       wq: np.ndarray, s_w: float, A: np.ndarray, B: np.ndarray,
-                      want_dx: bool = True, want_da: bool = True
+                      want_dx: bool = True, want_da: bool = True, g_fmt: str = "e4m3"
                       ) -> Tuple[Optional[np.ndarray], Optional[np.ndarray], np.ndarray]:
     """Reformulated backward of the melded layer ([P2] method paragraph;
     [P4] thread 4, Q1: dL/dA = B^T (dL/dO) x^T, while the X A^T factor that
@@ -147,8 +151,9 @@ def melded_linear_bwd(gq: np.ndarray, s_g: float, xq: np.ndarray, s_x: float,
       dA = (G^ B)^T X^          [r x d_in]
     Adapter layout: A [r x d_in], B [d_out x r], so that row i of B A is the
     delta of backbone row i.  All sums in float64, stored as float32.
+    g_fmt = "e5m2" reads gq as E5M2 codes.
     """
-    gd = e4m3.decode(gq)
+    gd = FORMATS[g_fmt][0].decode(gq)
     xd = e4m3.decode(xq)
     sg = np.float64(np.float32(s_g))
     sx = np.float64(np.float32(s_x))
@@ -197,12 +202,13 @@ def melded_linear_fwd_frozen_a(xq: np.ndarray, s_x: float, wq: np.ndarray, s_w: 
 
 
 def melded_linear_bwd_frozen_a(gq: np.ndarray, s_g: float, wq: np.ndarray, s_w: float,
-                               U: np.ndarray, want_dx: bool = True
+                               U: np.ndarray, want_dx: bool = True, g_fmt: str = "e4m3"
                                ) -> Tuple[Optional[np.ndarray], np.ndarray]:
     """Backward with A frozen: dX = G^ DQ(W~) as in melded_linear_bwd, and
     dB = G^^T U with the U of the forward (float32 as given); no dA, so no
-    product with X~ is needed here.  Sums in float64, stored as float32."""
-    gd = e4m3.decode(gq)
+    product with X~ is needed here.  Sums in float64, stored as float32.
+    g_fmt = "e5m2" reads gq as E5M2 codes."""
+    gd = FORMATS[g_fmt][0].decode(gq)
     sg = np.float64(np.float32(s_g))
     dx = None
     if want_dx:
