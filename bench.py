@@ -45,6 +45,8 @@ def parse():
     ap.add_argument("--adapter", choices=["trained", "frozen-fp8"], default="trained",
                     help="A trained in fp32 (dA computed), or the pages' training setup: A "
                          "frozen in FP8, X~A~^T formed in the forward, no dA")
+    ap.add_argument("--grad-format", choices=["e4m3", "e5m2"], default="e4m3",
+                    help="FP8 format of the upstream gradient dY")
     ap.add_argument("--merge-every", type=int, default=1,
                     help="run the row-wise proxy update on every N-th step (B accumulates "
                          "the adapter updates in between)")
@@ -79,7 +81,8 @@ def main():
 
     d0 = wl.make_linear(2, 0, spec, step=0)
     frozen = args.adapter == "frozen-fp8"
-    m = fq.MeldedLinear(d_out, d_in, r, T, optimizer=args.optimizer, fp8_a=frozen)
+    m = fq.MeldedLinear(d_out, d_in, r, T, optimizer=args.optimizer, fp8_a=frozen,
+                        g_fmt=args.grad_format)
     t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
     m.init_state(t(d0["W"]), t(d0["A"]), t(d0["B"]))
     batches = []
@@ -106,15 +109,18 @@ def main():
             fwd = lambda: fq.melded_linear_fwd_frozen_a(m.xq, m.s_x, m.wq, m.s_w, m.aq, m.s_a,  # noqa: E731
                                                         m.y, m.u, ws=m.ws_fwd, stream=stream)
             bwd = lambda: fq.melded_linear_bwd_frozen_a(m.gq, m.s_g, m.wq, m.s_w, m.u, m.dx,  # noqa: E731
-                                                        m.dB, ws=m.ws_bwd, stream=stream)
+                                                        m.dB, ws=m.ws_bwd, stream=stream,
+                                                        g_fmt=args.grad_format)
         else:
             fwd = lambda: fq.melded_linear_fwd(m.xq, m.s_x, m.wq, m.s_w, m.y, stream=stream)  # noqa: E731
             bwd = lambda: fq.melded_linear_bwd(m.gq, m.s_g, m.xq, m.s_x, m.wq, m.s_w, m.A, m.B,  # noqa: E731
-                                               m.dx, m.dA, m.dB, ws=m.ws_bwd, stream=stream)
+                                               m.dx, m.dA, m.dB, ws=m.ws_bwd, stream=stream,
+                                               g_fmt=args.grad_format)
         return [
             lambda: fq.fp8_quantize(X, m.xq, m.s_x, ws=m.ws_q, stream=stream),
             fwd,
-            lambda: fq.fp8_quantize(dY, m.gq, m.s_g, ws=m.ws_q, stream=stream),
+            lambda: fq.fp8_quantize(dY, m.gq, m.s_g, ws=m.ws_q, stream=stream,
+                                    fmt=args.grad_format),
             bwd,
             lambda: m.adapter_update(spec.lr, stream=stream),
             (lambda: fq.rowwise_proxy_update(m.wq, m.s_w, m.A, m.B, spec.tau, spec.k_max, m.sel,
@@ -221,10 +227,11 @@ def main():
                                + " lr 1e-3, proxy update every "
                                + ("step" if args.merge_every == 1 else f"{args.merge_every} steps")
                                + (", A frozen in FP8 (X~A~^T formed in the forward, no dA)"
-                                  if frozen else ""),
+                                  if frozen else "")
+                               + (", dY in E5M2" if args.grad_format == "e5m2" else ""),
                    "tokens": T, "d_in": d_in, "d_out": d_out, "rank": r,
                    "optimizer": args.optimizer, "adapter": args.adapter,
-                   "merge_every": args.merge_every,
+                   "merge_every": args.merge_every, "grad_format": args.grad_format,
                    "parallelism": "single GPU"},
         "tokens_per_s": round(tokens_per_s, 1),
         "roofline": {"kernel": ("melded_linear_fwd_frozen_a call (FP8 GEMM 4096 x 4096 x 4096 "
@@ -245,7 +252,8 @@ def main():
     }
 
     if not args.no_cpu_baseline and args.cpu_tokens > 0:
-        out["cpu_baseline"] = cpu_baseline(spec, d0, args.cpu_tokens, args.optimizer, frozen)
+        out["cpu_baseline"] = cpu_baseline(spec, d0, args.cpu_tokens, args.optimizer, frozen,
+                                           args.grad_format)
     print(json.dumps(out), flush=True)
 
 
@@ -291,7 +299,7 @@ def gemm_traffic_bytes():
         return None
 
 
-def cpu_baseline(spec, d0, Ts, optimizer="sgd", frozen=False):
+def cpu_baseline(spec, d0, Ts, optimizer="sgd", frozen=False, g_fmt="e4m3"):
     """The CPU oracle, as it is, on a token sample of the same workload:
     quantize X and dY, forward, backward (dX, dA, dB; or with A frozen in FP8,
     X~A~^T in the forward and dX, dB), the adapter step (SGD or AdamW) and
@@ -311,14 +319,14 @@ def cpu_baseline(spec, d0, Ts, optimizer="sgd", frozen=False):
         A0 = oracle.fp8_dequantize(aq, s_a)
     t1 = time.perf_counter()
     xq, s_x, _, _ = oracle.fp8_quantize(X)
-    gq, s_g, _, _ = oracle.fp8_quantize(dY)
+    gq, s_g, _, _ = oracle.fp8_quantize(dY, fmt=g_fmt)
     if frozen:
         _, U = oracle.melded_linear_fwd_frozen_a(xq, s_x, wq, s_w, aq, s_a)
-        _, dB = oracle.melded_linear_bwd_frozen_a(gq, s_g, wq, s_w, U)
+        _, dB = oracle.melded_linear_bwd_frozen_a(gq, s_g, wq, s_w, U, g_fmt=g_fmt)
         dA = None
     else:
         oracle.melded_linear_fwd(xq, s_x, wq, s_w)
-        _, dA, dB = oracle.melded_linear_bwd(gq, s_g, xq, s_x, wq, s_w, A0, d0["B"])
+        _, dA, dB = oracle.melded_linear_bwd(gq, s_g, xq, s_x, wq, s_w, A0, d0["B"], g_fmt=g_fmt)
     if optimizer == "sgd":
         A, B = oracle.adapter_step(A0, d0["B"], dA, dB, spec.lr)
     else:

@@ -19,7 +19,8 @@ import torch
 __all__ = ["load", "FalqError", "fp8_quantize", "fp8_quantize_workspace_bytes",
            "melded_linear_fwd", "melded_linear_bwd", "melded_linear_bwd_workspace_bytes",
            "adapter_step", "adapter_step_adamw", "rowwise_proxy_update",
-           "fp8_dequantize", "melded_linear_fwd_frozen_a",
+           "fp8_dequantize", "melded_linear_fwd_frozen_a", "fp8_quantize_fmt",
+           "melded_linear_bwd_fmt", "melded_linear_bwd_frozen_a_fmt", "FORMATS",
            "melded_linear_fwd_frozen_a_workspace_bytes", "melded_linear_bwd_frozen_a",
            "melded_linear_bwd_frozen_a_workspace_bytes", "rowwise_proxy_update_workspace_bytes",
            "version", "LIB_PATH"]
@@ -46,6 +47,12 @@ _SIGS = {
     "adapter_step_adamw": (_i32, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _i64, _i64,
                                   _i64, _f32, _f32, _f32, _f32, _f32, _i64, _c_p]),
     "fp8_dequantize": (_i32, [_c_p, _c_p, _i64, _c_p, _c_p]),
+    "fp8_quantize_fmt": (_i32, [_c_p, _i32, _i64, _i32, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _sz,
+                                _c_p]),
+    "melded_linear_bwd_fmt": (_i32, [_c_p, _i32, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _i64,
+                                     _i64, _i64, _i64, _c_p, _c_p, _c_p, _c_p, _sz, _c_p]),
+    "melded_linear_bwd_frozen_a_fmt": (_i32, [_c_p, _i32, _c_p, _c_p, _c_p, _c_p, _i64, _i64,
+                                              _i64, _i64, _c_p, _c_p, _c_p, _sz, _c_p]),
     "melded_linear_fwd_frozen_a_workspace_bytes": (_sz, [_i64, _i64, _i64]),
     "melded_linear_fwd_frozen_a": (_i32, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _i64, _i64, _i64,
                                           _i64, _c_p, _c_p, _c_p, _sz, _c_p]),
@@ -60,6 +67,16 @@ _SIGS = {
 
 class FalqError(RuntimeError):
     pass
+
+
+#: FP8 code formats (falq_fp8_format): OCP E4M3 and OCP E5M2
+FORMATS = {"e4m3": 0, "e5m2": 1}
+
+
+def _fmt(f) -> int:
+    if f not in FORMATS:
+        raise FalqError(f"format must be one of {sorted(FORMATS)}, not {f!r}")
+    return FORMATS[f]
 
 
 def load(path: Optional[str] = None):
@@ -121,7 +138,9 @@ def fp8_quantize_workspace_bytes(n: int) -> int:
 def fp8_quantize(x: torch.Tensor, q: torch.Tensor, scale: torch.Tensor,
                  scale_in: Optional[torch.Tensor] = None, amax: Optional[torch.Tensor] = None,
                  nonfinite: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None,
-                 stream=None) -> None:
+                 stream=None, fmt: str = "e4m3") -> None:
+    """q = FP8(x * s), s = max / amax(x); fmt "e4m3" (fp8_quantize) or "e5m2"
+    (fp8_quantize_fmt)."""
     lib = load()
     if x.dtype == torch.float32:
         dt = 0
@@ -134,9 +153,19 @@ def fp8_quantize(x: torch.Tensor, q: torch.Tensor, scale: torch.Tensor,
     wsb = fp8_quantize_workspace_bytes(n)
     if ws is None:
         ws = torch.empty(wsb, dtype=torch.uint8, device=x.device)
-    _check(lib.fp8_quantize(_ptr(x), dt, n, _ptr(scale_in), _ptr(q), _ptr(scale), _ptr(amax),
-                            _ptr(nonfinite), _ptr(ws), ws.numel(), _stream(stream)),
-           "fp8_quantize")
+    f = _fmt(fmt)
+    if f == 0:
+        _check(lib.fp8_quantize(_ptr(x), dt, n, _ptr(scale_in), _ptr(q), _ptr(scale), _ptr(amax),
+                                _ptr(nonfinite), _ptr(ws), ws.numel(), _stream(stream)),
+               "fp8_quantize")
+    else:
+        _check(lib.fp8_quantize_fmt(_ptr(x), dt, n, f, _ptr(scale_in), _ptr(q), _ptr(scale),
+                                    _ptr(amax), _ptr(nonfinite), _ptr(ws), ws.numel(),
+                                    _stream(stream)), "fp8_quantize_fmt")
+
+
+def fp8_quantize_fmt(x, q, scale, fmt: str, **kw) -> None:
+    fp8_quantize(x, q, scale, fmt=fmt, **kw)
 
 
 def melded_linear_fwd(xq: torch.Tensor, s_x: torch.Tensor, wq: torch.Tensor, s_w: torch.Tensor,
@@ -153,7 +182,8 @@ def melded_linear_bwd_workspace_bytes(T: int, d_in: int, d_out: int, r: int) -> 
     return int(load().melded_linear_bwd_workspace_bytes(T, d_in, d_out, r))
 
 
-def melded_linear_bwd(gq, s_g, xq, s_x, wq, s_w, A, B, dx, dA, dB, ws=None, stream=None) -> None:
+def melded_linear_bwd(gq, s_g, xq, s_x, wq, s_w, A, B, dx, dA, dB, ws=None, stream=None,
+                      g_fmt: str = "e4m3") -> None:
     T, d_out = gq.shape
     d_in = xq.shape[1]
     r = A.shape[0]
@@ -169,10 +199,14 @@ def melded_linear_bwd(gq, s_g, xq, s_x, wq, s_w, A, B, dx, dA, dB, ws=None, stre
     wsb = melded_linear_bwd_workspace_bytes(T, d_in, d_out, r)
     if ws is None:
         ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=gq.device)
-    _check(load().melded_linear_bwd(_ptr(gq), _ptr(s_g), _ptr(xq), _ptr(s_x), _ptr(wq), _ptr(s_w),
-                                    _ptr(A), _ptr(B), T, d_in, d_out, r, _ptr(dx), _ptr(dA),
-                                    _ptr(dB), _ptr(ws), ws.numel(), _stream(stream)),
-           "melded_linear_bwd")
+    _check(load().melded_linear_bwd_fmt(_ptr(gq), _fmt(g_fmt), _ptr(s_g), _ptr(xq), _ptr(s_x),
+                                        _ptr(wq), _ptr(s_w), _ptr(A), _ptr(B), T, d_in, d_out, r,
+                                        _ptr(dx), _ptr(dA), _ptr(dB), _ptr(ws), ws.numel(),
+                                        _stream(stream)), "melded_linear_bwd")
+
+
+def melded_linear_bwd_fmt(gq, g_fmt: str, s_g, xq, s_x, wq, s_w, A, B, dx, dA, dB, **kw) -> None:
+    melded_linear_bwd(gq, s_g, xq, s_x, wq, s_w, A, B, dx, dA, dB, g_fmt=g_fmt, **kw)
 
 
 def fp8_dequantize(q: torch.Tensor, scale: torch.Tensor, out: torch.Tensor, stream=None) -> None:
@@ -211,7 +245,8 @@ def melded_linear_bwd_frozen_a_workspace_bytes(T: int, d_in: int, d_out: int, r:
     return int(load().melded_linear_bwd_frozen_a_workspace_bytes(T, d_in, d_out, r))
 
 
-def melded_linear_bwd_frozen_a(gq, s_g, wq, s_w, u, dx, dB, ws=None, stream=None) -> None:
+def melded_linear_bwd_frozen_a(gq, s_g, wq, s_w, u, dx, dB, ws=None, stream=None,
+                               g_fmt: str = "e4m3") -> None:
     """dx = G~ W~ / (s_g s_w) (dx may be None) and dB = G^^T u."""
     T, d_out = gq.shape
     d_in = wq.shape[1]
@@ -225,10 +260,14 @@ def melded_linear_bwd_frozen_a(gq, s_g, wq, s_w, u, dx, dB, ws=None, stream=None
     need = melded_linear_bwd_frozen_a_workspace_bytes(T, d_in, d_out, r)
     if ws is None:
         ws = torch.empty(max(need, 1), dtype=torch.uint8, device=gq.device)
-    _check(load().melded_linear_bwd_frozen_a(_ptr(gq), _ptr(s_g), _ptr(wq), _ptr(s_w), _ptr(u),
-                                             T, d_in, d_out, r, _ptr(dx), _ptr(dB), _ptr(ws),
-                                             ws.numel(), _stream(stream)),
+    _check(load().melded_linear_bwd_frozen_a_fmt(_ptr(gq), _fmt(g_fmt), _ptr(s_g), _ptr(wq),
+                                                 _ptr(s_w), _ptr(u), T, d_in, d_out, r, _ptr(dx),
+                                                 _ptr(dB), _ptr(ws), ws.numel(), _stream(stream)),
            "melded_linear_bwd_frozen_a")
+
+
+def melded_linear_bwd_frozen_a_fmt(gq, g_fmt: str, s_g, wq, s_w, u, dx, dB, **kw) -> None:
+    melded_linear_bwd_frozen_a(gq, s_g, wq, s_w, u, dx, dB, g_fmt=g_fmt, **kw)
 
 
 def adapter_step(A, B, dA, dB, lr: float, stream=None) -> None:

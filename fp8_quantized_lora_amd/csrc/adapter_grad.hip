@@ -54,6 +54,12 @@ __device__ __forceinline__ uint2 dec4_bf16(uint32_t w) {
   return make_uint2(pack_bf16x2(a.x, a.y), pack_bf16x2(b.x, b.y));
 }
 
+// the same for E5M2 codes (2 mantissa bits, exponents 2^-16 .. 2^15: exact in bf16)
+__device__ __forceinline__ uint2 dec4_bf16_e5m2(uint32_t w) {
+  float2 a = dec2_e5m2(w, false), b = dec2_e5m2(w, true);
+  return make_uint2(pack_bf16x2(a.x, a.y), pack_bf16x2(b.x, b.y));
+}
+
 // 16-byte chunk slot of chunk c in an LDS row of 128 bytes: the XOR by
 // swz(row) makes the 16-row fragment reads conflict-free (same geometry as
 // the FP8 GEMM's stages)
@@ -93,23 +99,18 @@ struct Stage {
 // id is remapped so that each XCD gets a run of consecutive logical ids, i.e.
 // whole (problem, split) groups, whose tiles all read the same K chunk of H:
 // that chunk then comes from HBM into one XCD's L2 once, not once per tile.
-template <bool TRANS, int NPL>
-__global__ __launch_bounds__(kSkThreads, 1) void skinny_kernel(Prob p0, Prob p1, int tiles_max,
-                                                               int splits) {
+typedef uint8_t SkQ[TM * TK];             // one stage of FP8 codes
+typedef uint8_t SkH[2][2][TN * 128];      // one stage of H: [hi/lo][k half][64 n x 64 k]
+
+// One workgroup: tile `tile` of problem p over K split s.  QF is the format
+// of p's codes (0 E4M3, 1 E5M2: both decode exactly to bf16).
+template <bool TRANS, int NPL, int QF>
+__device__ __forceinline__ void skinny_tile(const Prob& p, int tile, int s, SkQ* sQ, SkH* sH) {
   static_assert(NPL == 1 || NPL == 2, "one or two bf16 planes of H");
-  const int nblk = gridDim.x, per = nblk / 8, b = blockIdx.x;
-  const int lid = b < per * 8 ? (b % 8) * per + b / 8 : b;
-  const int tile = lid % tiles_max, rest = lid / tiles_max;
-  const int s = rest % splits;
-  const Prob p = rest / splits == 0 ? p0 : p1;
-  if (tile >= p.tilesM * p.tilesN) return;
   const int m0 = (tile % p.tilesM) * TM;
   const int n0 = (tile / p.tilesM) * TN;
   const int kb = s * p.kchunk;
   const int ke = min(p.K, kb + p.kchunk);
-
-  __shared__ __attribute__((aligned(16))) uint8_t sQ[2][TM * TK];          // 64 KB
-  __shared__ __attribute__((aligned(16))) uint8_t sH[2][2][2][TN * 128];   // 64 KB
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int wm = w >> 1, wn = w & 1;             // wave tile: rows wm*64.., cols wn*32..
@@ -225,7 +226,13 @@ __global__ __launch_bounds__(kSkThreads, 1) void skinny_kernel(Prob p0, Prob p1,
         const int row = wm * 64 + mb * 32 + r32;
         const uint4 c = *reinterpret_cast<const uint4*>(sQ[buf] + row * TK +
                                                         (((q2 * 2 + half) ^ swz(row)) * 16));
-        const uint2 c0 = dec4_bf16(c.x), c1 = dec4_bf16(c.y), c2 = dec4_bf16(c.z), c3 = dec4_bf16(c.w);
+        uint2 c0, c1, c2, c3;
+        if (QF == 0) {
+          c0 = dec4_bf16(c.x); c1 = dec4_bf16(c.y); c2 = dec4_bf16(c.z); c3 = dec4_bf16(c.w);
+        } else {
+          c0 = dec4_bf16_e5m2(c.x); c1 = dec4_bf16_e5m2(c.y);
+          c2 = dec4_bf16_e5m2(c.z); c3 = dec4_bf16_e5m2(c.w);
+        }
         a[mb][0] = __builtin_bit_cast(v8bf, make_uint4(c0.x, c0.y, c1.x, c1.y));
         a[mb][1] = __builtin_bit_cast(v8bf, make_uint4(c2.x, c2.y, c3.x, c3.y));
       }
@@ -293,6 +300,30 @@ __global__ __launch_bounds__(kSkThreads, 1) void skinny_kernel(Prob p0, Prob p1,
         if (m < p.M) P[(int64_t)m * p.N + n] = acc[mb][v];
       }
     }
+  }
+}
+
+// Grid: (problem, split, tile) with the tile fastest; problem 0 uses codes of
+// format QF0, problem 1 of format QF1.
+template <bool TRANS, int NPL, int QF0, int QF1>
+__global__ __launch_bounds__(kSkThreads, 1) void skinny_kernel(Prob p0, Prob p1, int tiles_max,
+                                                               int splits) {
+  __shared__ __attribute__((aligned(16))) SkQ sQ[2];     // 64 KB
+  __shared__ __attribute__((aligned(16))) SkH sH[2];     // 64 KB
+  const int nblk = gridDim.x, per = nblk / 8, b = blockIdx.x;
+  const int lid = b < per * 8 ? (b % 8) * per + b / 8 : b;
+  const int tile = lid % tiles_max, rest = lid / tiles_max;
+  const int s = rest % splits;
+  if constexpr (QF0 == QF1) {
+    const Prob p = rest / splits == 0 ? p0 : p1;           // a copy: selected in SGPRs
+    if (tile >= p.tilesM * p.tilesN) return;
+    skinny_tile<TRANS, NPL, QF0>(p, tile, s, sQ, sH);
+  } else if (rest / splits == 0) {
+    if (tile >= p0.tilesM * p0.tilesN) return;
+    skinny_tile<TRANS, NPL, QF0>(p0, tile, s, sQ, sH);
+  } else {
+    if (tile >= p1.tilesM * p1.tilesN) return;
+    skinny_tile<TRANS, NPL, QF1>(p1, tile, s, sQ, sH);
   }
 }
 
@@ -600,7 +631,7 @@ hipError_t launch_frozen_u(const uint8_t* xq, const float* s_x, const uint8_t* a
   }
   const Prob pu = prob(xq, d_in, h, nullptr, d_in, part, T, r, d_in, pl.kc);
   const int tiles = pu.tilesM * pu.tilesN;
-  skinny_kernel<false, 1><<<tiles * pl.S, kSkThreads, 0, s>>>(pu, pu, tiles, pl.S);
+  skinny_kernel<false, 1, 0, 0><<<tiles * pl.S, kSkThreads, 0, s>>>(pu, pu, tiles, pl.S);
   Red ru = red(part, pl.S, T, r, T, s_x, 0, u, r, nullptr, nullptr);
   ru.sc2 = s_a;
   launch_reduce(ru, nullptr, s);
@@ -608,7 +639,8 @@ hipError_t launch_frozen_u(const uint8_t* xq, const float* s_x, const uint8_t* a
 }
 
 hipError_t launch_frozen_db(const uint8_t* gq, const float* s_g, const float* u, int64_t T,
-                            int64_t d_out, int64_t r, float* dB, void* ws, hipStream_t s) {
+                            int64_t d_out, int64_t r, float* dB, void* ws, hipStream_t s,
+                            int g_fmt) {
   if (r == 0 || d_out == 0) return hipSuccess;
   if (T == 0) return launch_fill_f32(dB, d_out * r, 0.0f, s);
   const FrozenPlan pl = frozen_db_plan(T, d_out, r);
@@ -620,7 +652,10 @@ hipError_t launch_frozen_db(const uint8_t* gq, const float* s_g, const float* u,
   launch_reduce(red(u, 1, T, r, pl.Tp, nullptr, 2, nullptr, pl.Tp, hi, lo), nullptr, s);
   const Prob pb = prob(gq, d_out, hi, lo, pl.Tp, part, d_out, r, T, pl.kc);
   const int tiles = pb.tilesM * pb.tilesN;
-  skinny_kernel<true, 2><<<tiles * pl.S, kSkThreads, 0, s>>>(pb, pb, tiles, pl.S);
+  if (g_fmt == 0)
+    skinny_kernel<true, 2, 0, 0><<<tiles * pl.S, kSkThreads, 0, s>>>(pb, pb, tiles, pl.S);
+  else
+    skinny_kernel<true, 2, 1, 1><<<tiles * pl.S, kSkThreads, 0, s>>>(pb, pb, tiles, pl.S);
   launch_reduce(red(part, pl.S, d_out, r, d_out, s_g, 0, dB, r, nullptr, nullptr), nullptr, s);
   return hipGetLastError();
 }
@@ -640,7 +675,7 @@ hipError_t launch_fill_f32(float* p, int64_t n, float v, hipStream_t s) {
 hipError_t launch_adapter_grads(const uint8_t* gq, const float* s_g, const uint8_t* xq,
                                 const float* s_x, const float* A, const float* B, int64_t T,
                                 int64_t d_in, int64_t d_out, int64_t r, float* dA, float* dB,
-                                void* ws, hipStream_t s) {
+                                void* ws, hipStream_t s, int g_fmt) {
   if (r == 0) return hipSuccess;
   if (T == 0) {
     hipError_t e = launch_fill_f32(dB, d_out * r, 0.0f, s);
@@ -670,8 +705,11 @@ hipError_t launch_adapter_grads(const uint8_t* gq, const float* s_g, const uint8
                  pl.kc1v);
   {
     const int tiles = pu.tilesM * pu.tilesN;
-    skinny_kernel<false, 2><<<tiles * pl.S1 * (want_da ? 2 : 1), kSkThreads, 0, s>>>(pu, pv, tiles,
-                                                                                  pl.S1);
+    const int grid = tiles * pl.S1 * (want_da ? 2 : 1);
+    if (g_fmt == 0)
+      skinny_kernel<false, 2, 0, 0><<<grid, kSkThreads, 0, s>>>(pu, pv, tiles, pl.S1);
+    else
+      skinny_kernel<false, 2, 0, 1><<<grid, kSkThreads, 0, s>>>(pu, pv, tiles, pl.S1);
   }
   // reduce -> U^T, V^T as bf16 hi/lo [r x Tp], scaled by 1/s_x, 1/s_g
   {
@@ -689,8 +727,11 @@ hipError_t launch_adapter_grads(const uint8_t* gq, const float* s_g, const uint8
                  pl.kc2);
   {
     const int tiles = std::max(pb.tilesM * pb.tilesN, want_da ? pa.tilesM * pa.tilesN : 0);
-    skinny_kernel<true, 2><<<tiles * pl.S2 * (want_da ? 2 : 1), kSkThreads, 0, s>>>(pb, pa, tiles,
-                                                                                 pl.S2);
+    const int grid = tiles * pl.S2 * (want_da ? 2 : 1);
+    if (g_fmt == 0)
+      skinny_kernel<true, 2, 0, 0><<<grid, kSkThreads, 0, s>>>(pb, pa, tiles, pl.S2);
+    else
+      skinny_kernel<true, 2, 1, 0><<<grid, kSkThreads, 0, s>>>(pb, pa, tiles, pl.S2);
   }
   {
     const Red rb = red(f32(pl.off_p2b), pl.S2, d_out, r, d_out, s_g, 0, dB, r, nullptr, nullptr);

@@ -32,14 +32,18 @@ inline bool ws_ok(const void* ws, size_t have, size_t need_bytes) {
 
 // dX = dec(G~) dec(W~) / (s_g s_w) as an NT FP8 GEMM against W~^T, which is
 // written to the first d_in * d_out bytes of the workspace
-hipError_t run_dx(const uint8_t* gq, const float* s_g, const uint8_t* wq, const float* s_w,
-                  int64_t T, int64_t d_in, int64_t d_out, float* dx, uint8_t* wt, hipStream_t s) {
+hipError_t run_dx(const uint8_t* gq, int g_fmt, const float* s_g, const uint8_t* wq,
+                  const float* s_w, int64_t T, int64_t d_in, int64_t d_out, float* dx, uint8_t* wt,
+                  hipStream_t s) {
   if (T * d_in == 0) return hipSuccess;
   if (d_out == 0) return falq::launch_fill_f32(dx, T * d_in, 0.0f, s);
   hipError_t e = falq::launch_transpose_u8(wq, d_out, d_in, wt, s);
   if (e != hipSuccess) return e;
-  return falq::launch_gemm_fp8_nt(gq, d_out, wt, d_out, dx, d_in, T, d_in, d_out, s_g, s_w, s);
+  return falq::launch_gemm_fp8_nt(gq, d_out, wt, d_out, dx, d_in, T, d_in, d_out, s_g, s_w, s,
+                                  g_fmt);
 }
+
+inline bool fmt_ok(int f) { return f == FALQ_E4M3 || f == FALQ_E5M2; }
 
 }  // namespace
 
@@ -65,14 +69,21 @@ size_t fp8_quantize_workspace_bytes(int64_t n) {
 falq_status fp8_quantize(const void* x, int dtype, int64_t n, const float* scale_in, uint8_t* q,
                          float* scale, float* amax, int32_t* nonfinite, void* ws, size_t ws_bytes,
                          falq_stream stream) {
-  if (n < 0 || (dtype != FALQ_F32 && dtype != FALQ_BF16)) return FALQ_EINVAL;
+  return fp8_quantize_fmt(x, dtype, n, FALQ_E4M3, scale_in, q, scale, amax, nonfinite, ws,
+                          ws_bytes, stream);
+}
+
+falq_status fp8_quantize_fmt(const void* x, int dtype, int64_t n, int fmt, const float* scale_in,
+                             uint8_t* q, float* scale, float* amax, int32_t* nonfinite, void* ws,
+                             size_t ws_bytes, falq_stream stream) {
+  if (n < 0 || (dtype != FALQ_F32 && dtype != FALQ_BF16) || !fmt_ok(fmt)) return FALQ_EINVAL;
   if (n > 0 && (!need(x) || !need(q))) return FALQ_EINVAL;
   if (!scalar(scale) || (scale_in && !aligned(scale_in, 4)) || (amax && !aligned(amax, 4)) ||
       (nonfinite && !aligned(nonfinite, 4)))
     return FALQ_EINVAL;
   if (!ws_ok(ws, ws_bytes, falq::quantize_ws_bytes())) return FALQ_EINVAL;
-  return hip_status(falq::launch_quantize(x, dtype, n, scale_in, q, scale, amax, nonfinite, ws,
-                                          reinterpret_cast<hipStream_t>(stream)));
+  return hip_status(falq::launch_quantize(x, dtype, fmt, n, scale_in, q, scale, amax, nonfinite,
+                                          ws, reinterpret_cast<hipStream_t>(stream)));
 }
 
 falq_status melded_linear_fwd(const uint8_t* xq, const float* s_x, const uint8_t* wq,
@@ -101,6 +112,16 @@ falq_status melded_linear_bwd(const uint8_t* gq, const float* s_g, const uint8_t
                               const float* A, const float* B, int64_t T, int64_t d_in,
                               int64_t d_out, int64_t r, float* dx, float* dA, float* dB, void* ws,
                               size_t ws_bytes, falq_stream stream) {
+  return melded_linear_bwd_fmt(gq, FALQ_E4M3, s_g, xq, s_x, wq, s_w, A, B, T, d_in, d_out, r, dx,
+                               dA, dB, ws, ws_bytes, stream);
+}
+
+falq_status melded_linear_bwd_fmt(const uint8_t* gq, int g_fmt, const float* s_g,
+                                  const uint8_t* xq, const float* s_x, const uint8_t* wq,
+                                  const float* s_w, const float* A, const float* B, int64_t T,
+                                  int64_t d_in, int64_t d_out, int64_t r, float* dx, float* dA,
+                                  float* dB, void* ws, size_t ws_bytes, falq_stream stream) {
+  if (!fmt_ok(g_fmt)) return FALQ_EINVAL;
   if (T < 0 || T > ((int64_t)1 << 30) || !dims_ok(d_in) || !dims_ok(d_out) || r < 0 ||
       r > ((int64_t)1 << 20))
     return FALQ_EINVAL;
@@ -118,14 +139,15 @@ falq_status melded_linear_bwd(const uint8_t* gq, const float* s_g, const uint8_t
   uint8_t* base = reinterpret_cast<uint8_t*>(ws);
   const size_t wt_bytes = align_up((size_t)d_in * (size_t)d_out, 256);
   hipError_t e = hipSuccess;
-  if (dx && run_dx(gq, s_g, wq, s_w, T, d_in, d_out, dx, base, s) != hipSuccess) return FALQ_EHIP;
+  if (dx && run_dx(gq, g_fmt, s_g, wq, s_w, T, d_in, d_out, dx, base, s) != hipSuccess)
+    return FALQ_EHIP;
   if (r > 0) {
     if (d_in == 0 || d_out == 0) {
       if (d_out > 0) e = falq::launch_fill_f32(dB, d_out * r, 0.0f, s);
       if (e == hipSuccess && dA && d_in > 0) e = falq::launch_fill_f32(dA, r * d_in, 0.0f, s);
     } else {
       e = falq::launch_adapter_grads(gq, s_g, xq, s_x, A, B, T, d_in, d_out, r, dA, dB,
-                                     base + wt_bytes, s);
+                                     base + wt_bytes, s, g_fmt);
     }
   }
   return hip_status(e);
@@ -179,6 +201,16 @@ falq_status melded_linear_bwd_frozen_a(const uint8_t* gq, const float* s_g, cons
                                        const float* s_w, const float* u, int64_t T, int64_t d_in,
                                        int64_t d_out, int64_t r, float* dx, float* dB, void* ws,
                                        size_t ws_bytes, falq_stream stream) {
+  return melded_linear_bwd_frozen_a_fmt(gq, FALQ_E4M3, s_g, wq, s_w, u, T, d_in, d_out, r, dx, dB,
+                                        ws, ws_bytes, stream);
+}
+
+falq_status melded_linear_bwd_frozen_a_fmt(const uint8_t* gq, int g_fmt, const float* s_g,
+                                           const uint8_t* wq, const float* s_w, const float* u,
+                                           int64_t T, int64_t d_in, int64_t d_out, int64_t r,
+                                           float* dx, float* dB, void* ws, size_t ws_bytes,
+                                           falq_stream stream) {
+  if (!fmt_ok(g_fmt)) return FALQ_EINVAL;
   if (T < 0 || T > ((int64_t)1 << 30) || !dims_ok(d_in) || !dims_ok(d_out) || r < 0 ||
       r > ((int64_t)1 << 20))
     return FALQ_EINVAL;
@@ -193,8 +225,10 @@ falq_status melded_linear_bwd_frozen_a(const uint8_t* gq, const float* s_g, cons
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   uint8_t* base = reinterpret_cast<uint8_t*>(ws);
   const size_t wt_bytes = align_up((size_t)d_in * (size_t)d_out, 256);
-  if (dx && run_dx(gq, s_g, wq, s_w, T, d_in, d_out, dx, base, s) != hipSuccess) return FALQ_EHIP;
-  return hip_status(falq::launch_frozen_db(gq, s_g, u, T, d_out, r, dB, base + wt_bytes, s));
+  if (dx && run_dx(gq, g_fmt, s_g, wq, s_w, T, d_in, d_out, dx, base, s) != hipSuccess)
+    return FALQ_EHIP;
+  return hip_status(
+      falq::launch_frozen_db(gq, s_g, u, T, d_out, r, dB, base + wt_bytes, s, g_fmt));
 }
 
 falq_status adapter_step(float* A, float* B, const float* dA, const float* dB, int64_t r,

@@ -13,6 +13,7 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 
 constexpr float kE4M3Max = 448.0f;
+constexpr float kE5M2Max = 57344.0f;      // OCP E5M2: 1.75 * 2^15 (0x7B)
 
 // ---------------------------------------------------------------------------
 // E4M3 (OCP e4m3fn) conversions on the gfx950 conversion unit.
@@ -54,6 +55,34 @@ __device__ __forceinline__ uint32_t enc1(float a) {
   uint32_t c = (uint32_t)w & 0xFFu;
   if (__builtin_isnan(a)) c = 0x7Fu | ((__float_as_uint(a) >> 31) << 7);
   return c;
+}
+
+// E5M2 casts, the same scheme: v_cvt_pk_bf8_f32 rounds to nearest even; the
+// clamp to +-57344 saturates finite overflow and infinities (so no code
+// reaches the infinity pattern 0x7C); NaN lanes become 0x7F | sign
+__device__ __forceinline__ float clamp_e5(float v) {
+  return fminf(fmaxf(v, -kE5M2Max), kE5M2Max);
+}
+
+__device__ __forceinline__ uint32_t enc4_e5m2(float a, float b, float c, float d) {
+  int w = __builtin_amdgcn_cvt_pk_bf8_f32(clamp_e5(a), clamp_e5(b), 0, false);
+  w = __builtin_amdgcn_cvt_pk_bf8_f32(clamp_e5(c), clamp_e5(d), w, true);
+  return nan_patch((uint32_t)w, a, b, c, d);
+}
+
+__device__ __forceinline__ uint32_t enc1_e5m2(float a) {
+  int w = __builtin_amdgcn_cvt_pk_bf8_f32(clamp_e5(a), 0.0f, 0, false);
+  uint32_t c = (uint32_t)w & 0xFFu;
+  if (__builtin_isnan(a)) c = 0x7Fu | ((__float_as_uint(a) >> 31) << 7);
+  return c;
+}
+
+// E5M2 bytes 0,1 (hi = false) or 2,3 (hi = true) of a dword -> two floats (exact)
+__device__ __forceinline__ float2 dec2_e5m2(uint32_t w, bool hi) {
+  typedef float v2f __attribute__((ext_vector_type(2)));
+  v2f r = hi ? __builtin_amdgcn_cvt_pk_f32_bf8((int)w, true)
+             : __builtin_amdgcn_cvt_pk_f32_bf8((int)w, false);
+  return make_float2(r.x, r.y);
 }
 
 // E4M3 bytes 0,1 (hi = false) or 2,3 (hi = true) of a dword -> two floats (exact)

@@ -68,23 +68,33 @@ __global__ __launch_bounds__(256) void transpose_u8_kernel(const uint8_t* __rest
 
 }  // namespace
 
-hipError_t launch_gemm_fp8_nt(const uint8_t* A, int64_t lda, const uint8_t* B, int64_t ldb,
-                              float* C, int64_t ldc, int64_t M, int64_t N, int64_t K,
-                              const float* sa, const float* sb, hipStream_t s) {
-  if (M == 0 || N == 0) return hipSuccess;
+namespace {
+template <int FA>
+hipError_t gemm_nt(const uint8_t* A, int64_t lda, const uint8_t* B, int64_t ldb, float* C,
+                   int64_t ldc, int64_t M, int64_t N, int64_t K, const float* sa, const float* sb,
+                   hipStream_t s) {
   if (K % gemm::dma::BK == 0) {
     const int tM = (int)((M + gemm::dma::BM - 1) / gemm::dma::BM);
     const int tN = (int)((N + gemm::dma::BN - 1) / gemm::dma::BN);
-    gemm::dma::gemm_fp8_nt_dma<false><<<tM * tN, gemm::dma::kThreads, 0, s>>>(
+    gemm::dma::gemm_fp8_nt_dma<false, FA><<<tM * tN, gemm::dma::kThreads, 0, s>>>(
         A, lda, B, ldb, C, ldc, (int)M, (int)N, (int)K, sa, sb, tM, tN, gemm::dma::SecondB{});
     return hipGetLastError();
   }
   using Cf = gemm::Cfg<256, 256, 128, 2, 2>;
   const int tilesM = (int)((M + Cf::BM - 1) / Cf::BM);
   const int tilesN = (int)((N + Cf::BN - 1) / Cf::BN);
-  gemm::gemm_fp8_nt_kernel<Cf><<<tilesM * tilesN, Cf::kThreads, 0, s>>>(
+  gemm::gemm_fp8_nt_kernel<Cf, FA><<<tilesM * tilesN, Cf::kThreads, 0, s>>>(
       A, lda, B, ldb, C, ldc, (int)M, (int)N, (int)K, sa, sb, tilesM, tilesN);
   return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_gemm_fp8_nt(const uint8_t* A, int64_t lda, const uint8_t* B, int64_t ldb,
+                              float* C, int64_t ldc, int64_t M, int64_t N, int64_t K,
+                              const float* sa, const float* sb, hipStream_t s, int a_fmt) {
+  if (M == 0 || N == 0) return hipSuccess;
+  return a_fmt == 0 ? gemm_nt<0>(A, lda, B, ldb, C, ldc, M, N, K, sa, sb, s)
+                    : gemm_nt<1>(A, lda, B, ldb, C, ldc, M, N, K, sa, sb, s);
 }
 
 bool gemm_fp8_nt_fuses_second(int64_t N, int64_t K, int64_t R) {
@@ -102,7 +112,7 @@ hipError_t launch_gemm_fp8_nt_second(const uint8_t* A, int64_t lda, const uint8_
   if (!gemm_fp8_nt_fuses_second(N, K, R)) return hipErrorInvalidValue;
   const int tM = (int)((M + gemm::dma::BM - 1) / gemm::dma::BM);
   const int tN = (int)((N + gemm::dma::BN - 1) / gemm::dma::BN);
-  gemm::dma::gemm_fp8_nt_dma<true><<<tM * tN, gemm::dma::kThreads, 0, s>>>(
+  gemm::dma::gemm_fp8_nt_dma<true, 0><<<tM * tN, gemm::dma::kThreads, 0, s>>>(
       A, lda, B, ldb, C, ldc, (int)M, (int)N, (int)K, sa, sb, tM, tN,
       gemm::dma::SecondB{Bu, ldbu, (int)R, Cu, ldcu, sbu});
   return hipGetLastError();

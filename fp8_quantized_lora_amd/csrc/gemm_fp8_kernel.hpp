@@ -45,7 +45,9 @@ __device__ __forceinline__ void tile_coords(int tilesM, int tilesN, int& tm, int
   tn = rem / gm;
 }
 
-template <class C>
+// FA: format of the A codes (0 = E4M3, 1 = E5M2: the MFMA's A-format field);
+// B is E4M3
+template <class C, int FA>
 __global__ __launch_bounds__(C::kThreads, 1) void gemm_fp8_nt_kernel(
     const uint8_t* __restrict__ A, int64_t lda, const uint8_t* __restrict__ B, int64_t ldb,
     float* __restrict__ Cm, int64_t ldc, int M, int N, int K, const float* __restrict__ sa,
@@ -135,8 +137,8 @@ __global__ __launch_bounds__(C::kThreads, 1) void gemm_fp8_nt_kernel(
       for (int i = 0; i < C::MB; ++i)
 #pragma unroll
         for (int j = 0; j < C::NB; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[i], bf[j], acc[i][j], 0, 0,
-                                                                      0, 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[i], bf[j], acc[i][j], FA,
+                                                                      0, 0, 0, 0, 0);
     }
     if (kt + 1 < nk) sstore(cur ^ 1);
     __syncthreads();
@@ -208,7 +210,8 @@ struct SecondB {
   const float* sb;
 };
 
-template <bool FU>
+// FA: format of the A codes (0 = E4M3, 1 = E5M2); B (and the second B) E4M3
+template <bool FU, int FA>
 __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_nt_dma(
     const uint8_t* __restrict__ A, int64_t lda, const uint8_t* __restrict__ B, int64_t ldb,
     float* __restrict__ C, int64_t ldc, int M, int N, int K, const float* __restrict__ sa,
@@ -314,10 +317,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_nt_dma(
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int j = 0; j < NB; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[i & 1], bf[j], acc[i][j], 0,
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[i & 1], bf[j], acc[i][j], FA,
                                                                      0, 0, 0, 0, 0);
       if (FU && wave_u && i == iu)
-        accu = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[i & 1], bu, accu, 0, 0, 0, 0, 0,
+        accu = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[i & 1], bu, accu, FA, 0, 0, 0, 0,
                                                                 0);
       __builtin_amdgcn_sched_barrier(0);
       // the next stage's direct loads go out once this step's first

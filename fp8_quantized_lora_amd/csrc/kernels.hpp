@@ -11,7 +11,8 @@ namespace falq {
 // ---- fp8_quantize: amax partials + cast ---------------------------------
 constexpr int kQzMaxParts = 2048;
 size_t quantize_ws_bytes();
-hipError_t launch_quantize(const void* x, int dtype, int64_t n, const float* scale_in,
+// fmt 0: E4M3 (s = 448 / amax), 1: E5M2 (s = 57344 / amax)
+hipError_t launch_quantize(const void* x, int dtype, int fmt, int64_t n, const float* scale_in,
                            uint8_t* q, float* scale, float* amax, int32_t* nonfinite,
                            void* ws, hipStream_t s);
 
@@ -20,10 +21,11 @@ hipError_t launch_dequantize(const uint8_t* q, int64_t n, const float* s, float*
                              hipStream_t st);
 
 // ---- FP8 GEMMs ------------------------------------------------------------
-// C[M x N] (fp32, row stride ldc) = dec(A)[M x K] . dec(B)[N x K]^T / (sa * sb)
+// C[M x N] (fp32, row stride ldc) = dec(A)[M x K] . dec(B)[N x K]^T / (sa * sb);
+// A in E4M3 (a_fmt 0) or E5M2 (a_fmt 1), B in E4M3
 hipError_t launch_gemm_fp8_nt(const uint8_t* A, int64_t lda, const uint8_t* B, int64_t ldb,
                               float* C, int64_t ldc, int64_t M, int64_t N, int64_t K,
-                              const float* sa, const float* sb, hipStream_t s);
+                              const float* sa, const float* sb, hipStream_t s, int a_fmt = 0);
 // The same product plus Cu[M x R] = dec(A) . dec(Bu)[R x K]^T / (sa * sbu) in
 // the same launch (the DMA kernel's extra units); only where
 // gemm_fp8_nt_fuses_second(N, K, R) holds
@@ -42,7 +44,7 @@ size_t adapter_grad_ws_bytes(int64_t T, int64_t d_in, int64_t d_out, int64_t r);
 hipError_t launch_adapter_grads(const uint8_t* gq, const float* s_g, const uint8_t* xq,
                                 const float* s_x, const float* A, const float* B,
                                 int64_t T, int64_t d_in, int64_t d_out, int64_t r,
-                                float* dA, float* dB, void* ws, hipStream_t s);
+                                float* dA, float* dB, void* ws, hipStream_t s, int g_fmt = 0);
 
 // frozen FP8 factor A~: u [T x r] = dec(X~) dec(A~)^T / (s_x s_a)
 size_t frozen_u_ws_bytes(int64_t T, int64_t d_in, int64_t r);
@@ -52,7 +54,8 @@ hipError_t launch_frozen_u(const uint8_t* xq, const float* s_x, const uint8_t* a
 // dB [d_out x r] = dec(G~)^T u / s_g
 size_t frozen_db_ws_bytes(int64_t T, int64_t d_out, int64_t r);
 hipError_t launch_frozen_db(const uint8_t* gq, const float* s_g, const float* u, int64_t T,
-                            int64_t d_out, int64_t r, float* dB, void* ws, hipStream_t s);
+                            int64_t d_out, int64_t r, float* dB, void* ws, hipStream_t s,
+                            int g_fmt = 0);
 
 // ---- SGD ------------------------------------------------------------------
 // two tensors in one launch (either may be empty); 16-byte aligned pointers

@@ -1,7 +1,8 @@
-// fp8_quantize: per-tensor current scaling to OCP E4M3 on gfx950.
+// fp8_quantize: per-tensor current scaling to OCP E4M3 (or E5M2) on gfx950.
 //
-// The scale is s = 448 / max|x| (the per-tensor factor s_X of the FALQON
-// rebuttal, thread 2 reply W2), so every cast depends on one global maximum.
+// The scale is s = 448 / max|x| (57344 / max|x| for E5M2; the per-tensor
+// factor s_X of the FALQON rebuttal, thread 2 reply W2), so every cast
+// depends on one global maximum.
 // Two launches, both streaming and fully coalesced:
 //   1. qz_amax   : grid-stride max of |x| over finite elements (as the ordered
 //                  uint32 bit pattern of a non-negative float) and a count of
@@ -63,7 +64,7 @@ __device__ __forceinline__ void absorb(float f, uint32_t& m, int& bad) {
 // every workgroup: fold the per-workgroup partials into amax and the scale;
 // workgroup 0 publishes s, amax and the non-finite count
 __device__ float fold_scale(const uint32_t* __restrict__ part_max, const int* __restrict__ part_bad,
-                            int nparts, const float* __restrict__ scale_in,
+                            int nparts, float fmt_max, const float* __restrict__ scale_in,
                             float* __restrict__ scale_out, float* __restrict__ amax_out,
                             int32_t* __restrict__ nonfinite_out) {
   __shared__ uint32_t sm[kThreads / 64];
@@ -92,7 +93,7 @@ __device__ float fold_scale(const uint32_t* __restrict__ part_max, const int* __
     } else if (amax == 0.0f) {
       sc = 1.0f;
     } else {
-      sc = kE4M3Max / amax;                // IEEE-correct fp32 division
+      sc = fmt_max / amax;                 // IEEE-correct fp32 division
       if (__builtin_isinf(sc)) sc = FLT_MAX;
     }
     s_scale = sc;
@@ -106,14 +107,20 @@ __device__ float fold_scale(const uint32_t* __restrict__ part_max, const int* __
   return s_scale;
 }
 
-template <int DT>
+// F = 0: E4M3, F = 1: E5M2
+template <int F>
+__device__ __forceinline__ uint32_t enc4f(float a, float b, float c, float d) {
+  return F == 0 ? enc4(a, b, c, d) : enc4_e5m2(a, b, c, d);
+}
+
+template <int DT, int F>
 __device__ __forceinline__ void store_codes(uint8_t* __restrict__ q, int64_t i, const float (&v)[8],
                                             float s) {
   if (DT == 0) {
-    reinterpret_cast<uint32_t*>(q)[i] = enc4(v[0] * s, v[1] * s, v[2] * s, v[3] * s);
+    reinterpret_cast<uint32_t*>(q)[i] = enc4f<F>(v[0] * s, v[1] * s, v[2] * s, v[3] * s);
   } else {
-    const uint32_t c0 = enc4(v[0] * s, v[1] * s, v[2] * s, v[3] * s);
-    const uint32_t c1 = enc4(v[4] * s, v[5] * s, v[6] * s, v[7] * s);
+    const uint32_t c0 = enc4f<F>(v[0] * s, v[1] * s, v[2] * s, v[3] * s);
+    const uint32_t c1 = enc4f<F>(v[4] * s, v[5] * s, v[6] * s, v[7] * s);
     reinterpret_cast<uint2*>(q)[i] = make_uint2(c0, c1);
   }
 }
@@ -165,7 +172,7 @@ __global__ __launch_bounds__(kThreads) void qz_amax(const void* __restrict__ x, 
   block_partials(m, bad, part_max, part_bad);
 }
 
-template <int DT>
+template <int DT, int F>
 __global__ __launch_bounds__(kThreads) void qz_cast(const void* __restrict__ x, int64_t n,
                                                     const uint32_t* __restrict__ part_max,
                                                     const int* __restrict__ part_bad, int nparts,
@@ -184,13 +191,13 @@ __global__ __launch_bounds__(kThreads) void qz_cast(const void* __restrict__ x, 
 #pragma unroll
   for (int u = 0; u < kUnroll; ++u)
     if (i0 + u * stride < nvec) V::load(x, i0 + u * stride, v[u]);
-  const float s = fold_scale(part_max, part_bad, nparts, scale_in, scale_out, amax_out,
-                             nonfinite_out);
+  const float s = fold_scale(part_max, part_bad, nparts, F == 0 ? kE4M3Max : kE5M2Max, scale_in,
+                             scale_out, amax_out, nonfinite_out);
   while (true) {
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
       const int64_t i = i0 + u * stride;
-      if (i < nvec) store_codes<DT>(q, i, v[u], s);
+      if (i < nvec) store_codes<DT, F>(q, i, v[u], s);
     }
     i0 += stride * kUnroll;
     if (i0 >= nvec) break;
@@ -200,7 +207,7 @@ __global__ __launch_bounds__(kThreads) void qz_cast(const void* __restrict__ x, 
   }
   if (blockIdx.x == 0)
     for (int64_t i = nvec * V::N + threadIdx.x; i < n; i += kThreads)
-      q[i] = (uint8_t)enc1(V::scalar(x, i) * s);
+      q[i] = (uint8_t)(F == 0 ? enc1(V::scalar(x, i) * s) : enc1_e5m2(V::scalar(x, i) * s));
 }
 
 int blocks_for(int64_t nvec, int unroll, int cap) {
@@ -245,7 +252,7 @@ hipError_t launch_dequantize(const uint8_t* q, int64_t n, const float* s, float*
 
 size_t quantize_ws_bytes() { return (size_t)kQzMaxParts * 8; }
 
-hipError_t launch_quantize(const void* x, int dtype, int64_t n, const float* scale_in,
+hipError_t launch_quantize(const void* x, int dtype, int fmt, int64_t n, const float* scale_in,
                            uint8_t* q, float* scale, float* amax, int32_t* nonfinite,
                            void* ws, hipStream_t s) {
   uint32_t* part_max = reinterpret_cast<uint32_t*>(ws);
@@ -254,15 +261,18 @@ hipError_t launch_quantize(const void* x, int dtype, int64_t n, const float* sca
   const int64_t nvec = n / vecn;
   const int g1 = blocks_for(nvec, kAmaxUnroll, 1024);   // every cast workgroup folds these partials
   const int g2 = blocks_for(nvec, kUnroll, 2048);
-  if (dtype == 0) {
+  if (dtype == 0)
     qz_amax<0><<<g1, kThreads, 0, s>>>(x, n, part_max, part_bad);
-    qz_cast<0><<<g2, kThreads, 0, s>>>(x, n, part_max, part_bad, g1, scale_in, q, scale, amax,
-                                       nonfinite);
-  } else {
+  else
     qz_amax<1><<<g1, kThreads, 0, s>>>(x, n, part_max, part_bad);
-    qz_cast<1><<<g2, kThreads, 0, s>>>(x, n, part_max, part_bad, g1, scale_in, q, scale, amax,
-                                       nonfinite);
-  }
+#define FALQ_CAST(DT, F)                                                                        \
+  qz_cast<DT, F><<<g2, kThreads, 0, s>>>(x, n, part_max, part_bad, g1, scale_in, q, scale, amax, \
+                                         nonfinite)
+  if (dtype == 0 && fmt == 0) FALQ_CAST(0, 0);
+  else if (dtype == 0) FALQ_CAST(0, 1);
+  else if (fmt == 0) FALQ_CAST(1, 0);
+  else FALQ_CAST(1, 1);
+#undef FALQ_CAST
   return hipGetLastError();
 }
 

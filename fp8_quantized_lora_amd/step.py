@@ -33,15 +33,17 @@ from . import (fp8_quantize, fp8_quantize_workspace_bytes, fp8_dequantize, melde
 class MeldedLinear:
     def __init__(self, d_out: int, d_in: int, rank: int, tokens: int, device="cuda",
                  x_dtype=torch.float32, train_a: bool = True, optimizer: str = "sgd",
-                 adamw: Optional[dict] = None, fp8_a: bool = False):
+                 adamw: Optional[dict] = None, fp8_a: bool = False, g_fmt: str = "e4m3"):
         """optimizer "sgd" (adapter_step) or "adamw" (adapter_step_adamw, with
         hyper-parameters `adamw`: beta1, beta2, eps, weight_decay); fp8_a
-        freezes A in FP8 (implies train_a=False)."""
+        freezes A in FP8 (implies train_a=False); g_fmt is the FP8 format of the
+        upstream gradient dY ("e4m3" or "e5m2")."""
         if optimizer not in ("sgd", "adamw"):
             raise ValueError(f"optimizer must be 'sgd' or 'adamw', not {optimizer!r}")
         if fp8_a:
             train_a = False
         self.fp8_a = fp8_a
+        self.g_fmt = g_fmt
         self.d_out, self.d_in, self.r, self.T = d_out, d_in, rank, tokens
         self.train_a = train_a
         self.optimizer = optimizer
@@ -110,13 +112,13 @@ class MeldedLinear:
         return self.y
 
     def backward(self, dY: torch.Tensor, stream=None):
-        fp8_quantize(dY, self.gq, self.s_g, ws=self.ws_q, stream=stream)
+        fp8_quantize(dY, self.gq, self.s_g, ws=self.ws_q, stream=stream, fmt=self.g_fmt)
         if self.fp8_a:
             melded_linear_bwd_frozen_a(self.gq, self.s_g, self.wq, self.s_w, self.u, self.dx,
-                                       self.dB, ws=self.ws_bwd, stream=stream)
+                                       self.dB, ws=self.ws_bwd, stream=stream, g_fmt=self.g_fmt)
             return self.dx
         melded_linear_bwd(self.gq, self.s_g, self.xq, self.s_x, self.wq, self.s_w, self.A, self.B,
-                          self.dx, self.dA, self.dB, ws=self.ws_bwd, stream=stream)
+                          self.dx, self.dA, self.dB, ws=self.ws_bwd, stream=stream, g_fmt=self.g_fmt)
         return self.dx
 
     def adapter_update(self, lr: float, stream=None):

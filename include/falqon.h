@@ -71,6 +71,11 @@ typedef enum {
     FALQ_BF16 = 1           /* bfloat16 input (uint16 bit patterns) */
 } falq_dtype;
 
+typedef enum {
+    FALQ_E4M3 = 0,          /* OCP E4M3 ("e4m3fn"): bias 7, max 448, NaN 0x7F/0xFF */
+    FALQ_E5M2 = 1           /* OCP E5M2: bias 15, max 57344, inf 0x7C, NaN 0x7D-0x7F */
+} falq_fp8_format;
+
 typedef void *falq_stream;  /* a hipStream_t */
 
 /* Human-readable name of a status code (static string). */
@@ -105,6 +110,19 @@ size_t fp8_quantize_workspace_bytes(int64_t n);
 falq_status fp8_quantize(const void *x, int dtype, int64_t n, const float *scale_in,
                          uint8_t *q, float *scale, float *amax, int32_t *nonfinite,
                          void *ws, size_t ws_bytes, falq_stream stream);
+
+/*
+ * fp8_quantize_fmt — fp8_quantize with the code format as an argument:
+ * fmt = FALQ_E4M3 is fp8_quantize; fmt = FALQ_E5M2 casts to OCP E5M2 with
+ * s = 57344 / amax (the pages name the formats as "E4M3 or E5M2", [rebuttal]
+ * thread 2 W2; E5M2 is the usual format of an upstream gradient).  E5M2 casts
+ * round to nearest even and saturate to +-57344 (infinities included); NaN
+ * becomes 0x7F | sign.  FALQ_EINVAL for any other fmt.
+ */
+falq_status fp8_quantize_fmt(const void *x, int dtype, int64_t n, int fmt,
+                             const float *scale_in, uint8_t *q, float *scale, float *amax,
+                             int32_t *nonfinite, void *ws, size_t ws_bytes,
+                             falq_stream stream);
 
 /*
  * melded_linear_fwd — the forward of the melded layer as one FP8 GEMM with
@@ -147,6 +165,20 @@ falq_status melded_linear_bwd(const uint8_t *gq, const float *s_g,
                               int64_t T, int64_t d_in, int64_t d_out, int64_t r,
                               float *dx, float *dA, float *dB,
                               void *ws, size_t ws_bytes, falq_stream stream);
+
+/*
+ * melded_linear_bwd_fmt — melded_linear_bwd with gq in the format g_fmt
+ * (FALQ_E4M3 or FALQ_E5M2, as fp8_quantize_fmt wrote it); xq and wq stay
+ * E4M3.  The dX product then runs on the matrix cores with an E5M2 A
+ * operand, and the adapter contractions decode E5M2 exactly.
+ */
+falq_status melded_linear_bwd_fmt(const uint8_t *gq, int g_fmt, const float *s_g,
+                                  const uint8_t *xq, const float *s_x,
+                                  const uint8_t *wq, const float *s_w,
+                                  const float *A, const float *B,
+                                  int64_t T, int64_t d_in, int64_t d_out, int64_t r,
+                                  float *dx, float *dA, float *dB,
+                                  void *ws, size_t ws_bytes, falq_stream stream);
 
 /*
  * The pages' training setup: A frozen and held in FP8 ([rebuttal] thread 4,
@@ -199,6 +231,12 @@ falq_status melded_linear_bwd_frozen_a(const uint8_t *gq, const float *s_g,
                                        int64_t T, int64_t d_in, int64_t d_out, int64_t r,
                                        float *dx, float *dB, void *ws, size_t ws_bytes,
                                        falq_stream stream);
+/* the same with gq in the format g_fmt (FALQ_E4M3 or FALQ_E5M2) */
+falq_status melded_linear_bwd_frozen_a_fmt(const uint8_t *gq, int g_fmt, const float *s_g,
+                                           const uint8_t *wq, const float *s_w, const float *u,
+                                           int64_t T, int64_t d_in, int64_t d_out, int64_t r,
+                                           float *dx, float *dB, void *ws, size_t ws_bytes,
+                                           falq_stream stream);
 
 /*
  * adapter_step — SGD on the adapter factors, in place, elementwise in fp32

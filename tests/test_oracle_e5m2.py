@@ -106,3 +106,23 @@ def test_backward_with_e5m2_gradient_exact_rationals():
     x_hat = oracle.e4m3.decode(xq) / float(s_x)
     np.testing.assert_allclose(dB, g_hat.T @ (x_hat @ A.astype(np.float64).T), rtol=1e-6)
     np.testing.assert_allclose(dA, (g_hat @ B.astype(np.float64)).T @ x_hat, rtol=1e-6)
+
+
+def test_encode_matches_torch_cast_in_range():
+    """torch's float8_e5m2 cast (round to nearest even) agrees wherever it does
+    not overflow (it does not saturate: past 57344 it gives infinity)."""
+    import torch
+    from tests.test_oracle_e4m3 import structured_f32_patterns
+    rng = np.random.default_rng(7)
+    v = np.concatenate([
+        structured_f32_patterns(),
+        rng.uniform(-57343.0, 57343.0, 300_000).astype(np.float32),
+        (rng.standard_normal(300_000) * 2.0 ** -14).astype(np.float32),
+    ])
+    with np.errstate(invalid="ignore"):
+        v = v[np.isfinite(v) & (np.abs(v) <= 57344.0)]
+    ref = torch.from_numpy(v).to(torch.float8_e5m2).view(torch.uint8).numpy()
+    ours = e5m2.encode(v)
+    nan = np.isnan(v)
+    bad = np.nonzero((ours != ref) & ~nan)[0]
+    assert bad.size == 0, f"{bad.size} mismatches, first {v[bad[:5]]} {ours[bad[:5]]} {ref[bad[:5]]}"
