@@ -241,18 +241,24 @@ def adamw_scalars(lr: float, beta1: float, beta2: float, eps: float, weight_deca
     in float64 from the float32 values of the arguments and rounded to float32
     once:
         decay     = 1 - lr*wd                     (decoupled weight decay)
-        step_size = lr / (1 - beta1**step)        (first-moment bias correction)
-        inv_bc2   = 1 / sqrt(1 - beta2**step)     (second-moment bias correction)
+        step_size = lr / (1 - P1)                 (first-moment bias correction)
+        inv_bc2   = 1 / sqrt(1 - P2)              (second-moment bias correction)
         omb1, omb2 = 1 - beta1, 1 - beta2
+    where P = beta**step is formed as the running float64 product of beta over
+    the steps (one rounding per step: the value an optimizer state carries
+    from step to step, so that the step count can live in device memory).
     """
     lr, b1, b2, eps, wd = (float(np.float32(v)) for v in (lr, beta1, beta2, eps, weight_decay))
-    t = int(step)
+    p1 = p2 = 1.0
+    for _ in range(int(step)):
+        p1 *= b1
+        p2 *= b2
     return {
         "b1": np.float32(b1), "b2": np.float32(b2), "eps": np.float32(eps),
         "omb1": np.float32(1.0 - b1), "omb2": np.float32(1.0 - b2),
         "decay": np.float32(1.0 - lr * wd),
-        "step_size": np.float32(lr / (1.0 - b1 ** t)),
-        "inv_bc2": np.float32(1.0 / math.sqrt(1.0 - b2 ** t)),
+        "step_size": np.float32(lr / (1.0 - p1)),
+        "inv_bc2": np.float32(1.0 / math.sqrt(1.0 - p2)),
     }
 
 
