@@ -18,7 +18,8 @@ import torch
 
 __all__ = ["load", "FalqError", "fp8_quantize", "fp8_quantize_workspace_bytes",
            "melded_linear_fwd", "melded_linear_bwd", "melded_linear_bwd_workspace_bytes",
-           "adapter_step", "adapter_step_adamw", "rowwise_proxy_update",
+           "adapter_step", "adapter_step_adamw", "adamw_state", "ADAMW_STATE_BYTES",
+           "rowwise_proxy_update",
            "fp8_dequantize", "melded_linear_fwd_frozen_a", "fp8_quantize_fmt",
            "melded_linear_bwd_fmt", "melded_linear_bwd_frozen_a_fmt", "FORMATS",
            "melded_linear_fwd_frozen_a_workspace_bytes", "melded_linear_bwd_frozen_a",
@@ -45,7 +46,7 @@ _SIGS = {
                                  _i64, _i64, _c_p, _c_p, _c_p, _c_p, _sz, _c_p]),
     "adapter_step": (_i32, [_c_p, _c_p, _c_p, _c_p, _i64, _i64, _i64, _f32, _c_p]),
     "adapter_step_adamw": (_i32, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _i64, _i64,
-                                  _i64, _f32, _f32, _f32, _f32, _f32, _i64, _c_p]),
+                                  _i64, _f32, _f32, _f32, _f32, _f32, _c_p, _c_p]),
     "fp8_dequantize": (_i32, [_c_p, _c_p, _i64, _c_p, _c_p]),
     "fp8_quantize_fmt": (_i32, [_c_p, _i32, _i64, _i32, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _sz,
                                 _c_p]),
@@ -281,11 +282,21 @@ def adapter_step(A, B, dA, dB, lr: float, stream=None) -> None:
                                _stream(stream)), "adapter_step")
 
 
-def adapter_step_adamw(A, B, dA, dB, mA, vA, mB, vB, lr: float, step: int, beta1: float = 0.9,
+#: bytes of the AdamW optimizer state (zero-filled before the first step)
+ADAMW_STATE_BYTES = 64
+
+
+def adamw_state(device="cuda") -> torch.Tensor:
+    """A fresh AdamW state: zeros, before step 1 (int64 step count first)."""
+    return torch.zeros(ADAMW_STATE_BYTES // 8, dtype=torch.int64, device=device)
+
+
+def adapter_step_adamw(A, B, dA, dB, mA, vA, mB, vB, state, lr: float, beta1: float = 0.9,
                        beta2: float = 0.999, eps: float = 1e-8, weight_decay: float = 0.0,
                        stream=None) -> None:
-    """AdamW step number `step` (>= 1) on A and B, moments mA, vA, mB, vB in
-    place; dA = None freezes A (mA and vA may then be None)."""
+    """One AdamW step on A and B with moments mA, vA, mB, vB, in place; `state`
+    (adamw_state()) carries the step count and is advanced by the call.  dA =
+    None freezes A (mA and vA may then be None)."""
     r, d_in = A.shape
     d_out = B.shape[0]
     for t, name in ((B, "B"), (dB, "dB"), (mB, "mB"), (vB, "vB")):
@@ -293,9 +304,12 @@ def adapter_step_adamw(A, B, dA, dB, mA, vA, mB, vB, lr: float, step: int, beta1
     if dA is not None:
         for t, name in ((A, "A"), (dA, "dA"), (mA, "mA"), (vA, "vA")):
             _req(t, torch.float32, (r, d_in), name)
+    if state.numel() * state.element_size() != ADAMW_STATE_BYTES:
+        raise FalqError(f"state must be {ADAMW_STATE_BYTES} bytes (adamw_state())")
     _check(load().adapter_step_adamw(_ptr(A), _ptr(B), _ptr(dA), _ptr(dB), _ptr(mA), _ptr(vA),
                                      _ptr(mB), _ptr(vB), r, d_in, d_out, lr, beta1, beta2, eps,
-                                     weight_decay, step, _stream(stream)), "adapter_step_adamw")
+                                     weight_decay, _ptr(state), _stream(stream)),
+           "adapter_step_adamw")
 
 
 def rowwise_proxy_update_workspace_bytes(d_in: int, d_out: int, r: int) -> int:

@@ -10,8 +10,13 @@
 //     den = sqrt(v')*inv_bc2 + eps
 //     p'  = decay*p - step_size*(m'/den)
 // with sqrt and the division correctly rounded.  The step-dependent scalars
-// (bias corrections, decay) come from the host.  Memory: 16 bytes read and
-// 12 bytes written per element, float4 at a time.
+// come from a 64-byte optimizer state in device memory, advanced by a
+// one-thread kernel before the update: step t, the running float64 products
+// beta1^t and beta2^t, and the float32 scalars of the step (decay =
+// 1 - lr*wd, step_size = lr / (1 - beta1^t), inv_bc2 = 1 / sqrt(1 -
+// beta2^t), each computed in float64 and rounded once).  Nothing comes from
+// the host per step, so a captured graph replays consecutive steps.
+// Memory: 16 bytes read and 12 bytes written per element, float4 at a time.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -21,6 +26,27 @@ namespace falq {
 namespace {
 
 constexpr int kThreads = 256;
+
+// the optimizer state (AdamWState in kernels.hpp): all zero = before step 1
+__global__ void adamw_advance_kernel(AdamWState* st, float lr, float beta1, float beta2, float eps,
+                                     float wd) {
+  const bool first = st->t == 0;
+  const double p1 = (first ? 1.0 : st->pow1) * (double)beta1;
+  const double p2 = (first ? 1.0 : st->pow2) * (double)beta2;
+  st->t += 1;
+  st->pow1 = p1;
+  st->pow2 = p2;
+  AdamWScalars c;
+  c.b1 = beta1;
+  c.b2 = beta2;
+  c.omb1 = (float)(1.0 - (double)beta1);
+  c.omb2 = (float)(1.0 - (double)beta2);
+  c.eps = eps;
+  c.decay = (float)(1.0 - (double)lr * (double)wd);
+  c.step_size = (float)((double)lr / (1.0 - p1));
+  c.inv_bc2 = (float)(1.0 / sqrt(1.0 - p2));
+  st->sc = c;
+}
 
 __device__ __forceinline__ void adam1(float& p, float g, float& m, float& v,
                                       const AdamWScalars& c) {
@@ -35,7 +61,8 @@ __device__ __forceinline__ void adam1(float& p, float g, float& m, float& v,
 // grid-stride over the float4 items of a, then of b; the scalar tails (n % 4)
 // are done by workgroup 0
 __global__ __launch_bounds__(kThreads) void adamw_kernel(AdamWTensor a, AdamWTensor b,
-                                                         AdamWScalars c) {
+                                                         const AdamWState* __restrict__ st) {
+  const AdamWScalars c = st->sc;
   const int64_t na4 = a.n / 4, nb4 = b.n / 4;
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < na4 + nb4; i += stride) {
@@ -64,14 +91,16 @@ __global__ __launch_bounds__(kThreads) void adamw_kernel(AdamWTensor a, AdamWTen
 
 }  // namespace
 
-hipError_t launch_adamw2(const AdamWTensor& a, const AdamWTensor& b, const AdamWScalars& c,
-                         hipStream_t s) {
+hipError_t launch_adamw2(const AdamWTensor& a, const AdamWTensor& b, AdamWState* st, float lr,
+                         float beta1, float beta2, float eps, float wd, hipStream_t s) {
+  adamw_advance_kernel<<<1, 1, 0, s>>>(st, lr, beta1, beta2, eps, wd);
   const AdamWTensor none{nullptr, nullptr, nullptr, nullptr, 0};
   const AdamWTensor ta = a.n > 0 ? a : none, tb = b.n > 0 ? b : none;
-  if (ta.n + tb.n == 0) return hipSuccess;
-  const int64_t blocks = std::min<int64_t>((ta.n / 4 + tb.n / 4 + kThreads - 1) / kThreads + 1,
-                                           4096);
-  adamw_kernel<<<(int)blocks, kThreads, 0, s>>>(ta, tb, c);
+  if (ta.n + tb.n > 0) {
+    const int64_t blocks =
+        std::min<int64_t>((ta.n / 4 + tb.n / 4 + kThreads - 1) / kThreads + 1, 4096);
+    adamw_kernel<<<(int)blocks, kThreads, 0, s>>>(ta, tb, st);
+  }
   return hipGetLastError();
 }
 

@@ -244,29 +244,21 @@ falq_status adapter_step(float* A, float* B, const float* dA, const float* dB, i
 falq_status adapter_step_adamw(float* A, float* B, const float* dA, const float* dB, float* mA,
                                float* vA, float* mB, float* vB, int64_t r, int64_t d_in,
                                int64_t d_out, float lr, float beta1, float beta2, float eps,
-                               float weight_decay, int64_t step, falq_stream stream) {
-  if (r < 0 || d_in < 0 || d_out < 0 || step < 1) return FALQ_EINVAL;
+                               float weight_decay, void* state, falq_stream stream) {
+  if (r < 0 || d_in < 0 || d_out < 0) return FALQ_EINVAL;
   if (!std::isfinite(lr) || !std::isfinite(weight_decay) || !(beta1 >= 0.0f && beta1 < 1.0f) ||
       !(beta2 >= 0.0f && beta2 < 1.0f) || !(eps > 0.0f) || !std::isfinite(eps))
     return FALQ_EINVAL;
+  if (state == nullptr || !aligned(state, 8)) return FALQ_EINVAL;
   const bool train_a = dA != nullptr && r * d_in > 0;
   if (train_a && (!need(A) || !need(dA) || !need(mA) || !need(vA))) return FALQ_EINVAL;
   if (r * d_in > 0 && !opt(dA)) return FALQ_EINVAL;
   if (r * d_out > 0 && (!need(B) || !need(dB) || !need(mB) || !need(vB))) return FALQ_EINVAL;
-  // step scalars in double from the float arguments, each rounded to float once
-  const double lr_d = lr, b1 = beta1, b2 = beta2, t = (double)step;
-  falq::AdamWScalars c;
-  c.b1 = beta1;
-  c.b2 = beta2;
-  c.omb1 = (float)(1.0 - b1);
-  c.omb2 = (float)(1.0 - b2);
-  c.eps = eps;
-  c.decay = (float)(1.0 - lr_d * (double)weight_decay);
-  c.step_size = (float)(lr_d / (1.0 - std::pow(b1, t)));
-  c.inv_bc2 = (float)(1.0 / std::sqrt(1.0 - std::pow(b2, t)));
   const falq::AdamWTensor ta{A, dA, mA, vA, train_a ? r * d_in : 0};
   const falq::AdamWTensor tb{B, dB, mB, vB, r * d_out};
-  return hip_status(falq::launch_adamw2(ta, tb, c, reinterpret_cast<hipStream_t>(stream)));
+  return hip_status(falq::launch_adamw2(ta, tb, reinterpret_cast<falq::AdamWState*>(state), lr,
+                                        beta1, beta2, eps, weight_decay,
+                                        reinterpret_cast<hipStream_t>(stream)));
 }
 
 size_t rowwise_proxy_update_workspace_bytes(int64_t d_in, int64_t d_out, int64_t r) {

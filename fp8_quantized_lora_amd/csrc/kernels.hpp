@@ -75,9 +75,18 @@ struct AdamWTensor {
   float* v;
   int64_t n;
 };
-// two tensors in one launch (either may be empty: n == 0); 16-byte aligned
-hipError_t launch_adamw2(const AdamWTensor& a, const AdamWTensor& b, const AdamWScalars& c,
-                         hipStream_t s);
+// optimizer state in device memory (64 bytes; all zero before the first step)
+struct AdamWState {
+  int64_t t;             // steps taken
+  double pow1, pow2;     // beta1^t, beta2^t (running products)
+  AdamWScalars sc;       // the float32 scalars of step t
+  uint32_t pad[2];
+};
+static_assert(sizeof(AdamWState) == 64, "64-byte AdamW state");
+// advance the state one step, then update the two tensors (either may be
+// empty: n == 0); 16-byte aligned
+hipError_t launch_adamw2(const AdamWTensor& a, const AdamWTensor& b, AdamWState* st, float lr,
+                         float beta1, float beta2, float eps, float wd, hipStream_t s);
 
 // ---- row-wise proxy update -------------------------------------------------
 size_t proxy_ws_bytes(int64_t d_in, int64_t d_out, int64_t r);

@@ -27,6 +27,7 @@ from . import (fp8_quantize, fp8_quantize_workspace_bytes, fp8_dequantize, melde
                melded_linear_bwd, melded_linear_bwd_workspace_bytes, melded_linear_fwd_frozen_a,
                melded_linear_fwd_frozen_a_workspace_bytes, melded_linear_bwd_frozen_a,
                melded_linear_bwd_frozen_a_workspace_bytes, adapter_step, adapter_step_adamw,
+               adamw_state,
                rowwise_proxy_update, rowwise_proxy_update_workspace_bytes)
 
 
@@ -49,7 +50,7 @@ class MeldedLinear:
         self.optimizer = optimizer
         self.adamw = {"beta1": 0.9, "beta2": 0.999, "eps": 1e-8, "weight_decay": 0.0,
                       **(adamw or {})}
-        self.opt_step = 0
+
         dev = torch.device(device)
         u8, f32, i32 = torch.uint8, torch.float32, torch.int32
         self.wq = torch.empty((d_out, d_in), dtype=u8, device=dev)
@@ -74,6 +75,7 @@ class MeldedLinear:
             self.vA = torch.zeros((rank, d_in), dtype=f32, device=dev) if train_a else None
             self.mB = torch.zeros((d_out, rank), dtype=f32, device=dev)
             self.vB = torch.zeros((d_out, rank), dtype=f32, device=dev)
+            self.adam_state = adamw_state(dev)   # step count and beta powers, on the device
         self.sel = torch.empty(d_out, dtype=i32, device=dev)
         self.n_sel = torch.zeros(1, dtype=i32, device=dev)
         self.rho = torch.empty(d_out, dtype=f32, device=dev)
@@ -125,9 +127,8 @@ class MeldedLinear:
         if self.optimizer == "sgd":
             adapter_step(self.A, self.B, self.dA, self.dB, lr, stream=stream)
         else:
-            self.opt_step += 1
             adapter_step_adamw(self.A, self.B, self.dA, self.dB, self.mA, self.vA, self.mB,
-                               self.vB, lr, self.opt_step, stream=stream, **self.adamw)
+                               self.vB, self.adam_state, lr, stream=stream, **self.adamw)
 
     def merge(self, tau: float, k_max: int = 0, stream=None):
         rowwise_proxy_update(self.wq, self.s_w, self.A, self.B, tau, k_max, self.sel, self.n_sel,

@@ -255,28 +255,35 @@ falq_status adapter_step(float *A, float *B, const float *dA, const float *dB,
  * ([rebuttal] thread 3 W3.1: the runs train with a 32-bit AdamW optimizer;
  * the pages give no hyper-parameters).  Adam with decoupled weight decay
  * (the decay scales the weights; it is not added to the gradient); weights
- * and moments are float32.  Step number `step` (>= 1) sets the bias
- * corrections.  From the float arguments, in double, each rounded to float
- * once:
+ * and moments are float32.
+ *
+ * `state` is FALQ_ADAMW_STATE_BYTES of device memory (8-byte aligned) that
+ * the caller zero-fills once before the first step and then leaves to the
+ * library: each call first advances it (step t = t + 1; P1 = beta1^t and
+ * P2 = beta2^t as running float64 products, starting from 1) and derives,
+ * in float64 from the float arguments, each rounded to float once:
  *     omb1 = 1 - beta1, omb2 = 1 - beta2, decay = 1 - lr*weight_decay,
- *     step_size = lr / (1 - beta1^step), inv_bc2 = 1 / sqrt(1 - beta2^step)
+ *     step_size = lr / (1 - P1), inv_bc2 = 1 / sqrt(1 - P2)
  * then per element, every float operation rounded on its own (no fused
  * multiply-add; sqrt and division correctly rounded):
  *     m <- beta1*m + omb1*g
  *     v <- beta2*v + (omb2*g)*g
  *     p <- decay*p - step_size*(m / (sqrt(v)*inv_bc2 + eps))
+ * The step count lives in `state`, so a captured graph replays consecutive
+ * steps.  The first 8 bytes of `state` hold t as int64.
  *
  *   A [r x d_in], mA, vA: float32, device, in place; B [d_out x r], mB, vB
  *   likewise; dA, dB gradients of the same shapes.  dA = NULL freezes A:
  *   A, mA and vA are then not touched and may be NULL.  Moments start at 0.
- *   Errors: FALQ_EINVAL for step < 1, beta outside [0, 1), eps <= 0, a
- *   non-finite lr / eps / weight_decay, or a null or misaligned pointer.
+ *   Errors: FALQ_EINVAL for beta outside [0, 1), eps <= 0, a non-finite
+ *   lr / eps / weight_decay, a null state, or a null or misaligned pointer.
  */
+#define FALQ_ADAMW_STATE_BYTES 64
 falq_status adapter_step_adamw(float *A, float *B, const float *dA, const float *dB,
                                float *mA, float *vA, float *mB, float *vB,
                                int64_t r, int64_t d_in, int64_t d_out,
                                float lr, float beta1, float beta2, float eps,
-                               float weight_decay, int64_t step, falq_stream stream);
+                               float weight_decay, void *state, falq_stream stream);
 
 /*
  * rowwise_proxy_update — row-wise proxy update ([summary] key design; [intro]:

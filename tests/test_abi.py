@@ -97,10 +97,10 @@ def test_linear_rejects_bad_arguments():
 
 def test_adamw_rejects_bad_arguments():
     lib = fq.load()
-    ok = [P, P, P, P, P, P, P, P, 4, 32, 32, 1e-3, 0.9, 0.999, 1e-8, 0.0, 1, None]
-    for idx, val in [(3, None), (6, None), (7, MIS), (0, None), (4, None), (8, -1), (16, 0),
-                     (12, 1.0), (13, -0.1), (14, 0.0), (14, float("inf")), (11, float("nan")),
-                     (15, float("inf"))]:
+    ok = [P, P, P, P, P, P, P, P, 4, 32, 32, 1e-3, 0.9, 0.999, 1e-8, 0.0, P, None]
+    for idx, val in [(3, None), (6, None), (7, MIS), (0, None), (4, None), (8, -1), (16, None),
+                     (16, P + 4), (12, 1.0), (13, -0.1), (14, 0.0), (14, float("inf")),
+                     (11, float("nan")), (15, float("inf"))]:
         a = list(ok)
         a[idx] = val
         assert lib.adapter_step_adamw(*a) == EINVAL, idx
@@ -149,6 +149,8 @@ def test_melded_linear_buffers_on_host():
                         adamw={"beta1": 0.8, "weight_decay": 0.1})
     assert m.adamw == {"beta1": 0.8, "beta2": 0.999, "eps": 1e-8, "weight_decay": 0.1}
     assert m.mA.shape == m.vA.shape == (4, 32) and m.mB.shape == m.vB.shape == (64, 4)
+    assert m.adam_state.numel() * m.adam_state.element_size() == fq.ADAMW_STATE_BYTES
+    assert not m.adam_state.any()
     assert not m.mB.any() and not m.vB.any()
     frozen = fq.MeldedLinear(64, 32, 4, 16, device="cpu", optimizer="adamw", train_a=False)
     assert frozen.dA is None and frozen.mA is None and frozen.vA is None

@@ -1,13 +1,31 @@
 """adapter_step_adamw on the GPU against the oracle: weights and both moments
 bit-exact over consecutive steps (every float operation of the update is
-rounded on its own on both sides; sqrt and division are correctly rounded)."""
+rounded on its own on both sides; sqrt and division are correctly rounded),
+the step count advanced in the device-side state."""
 import numpy as np
 import pytest
+import torch
 
 import oracle
 from tests.gpu_util import announce, dev, host
 
 pytestmark = pytest.mark.gpu
+
+
+def state_at(gpu_lib, t, beta1, beta2):
+    """An AdamW state after t steps: t and the running float64 products of the
+    float32 betas (the scalar fields are rewritten by the next call)."""
+    st = gpu_lib.adamw_state()
+    b1, b2 = float(np.float32(beta1)), float(np.float32(beta2))
+    p1 = p2 = 1.0
+    for _ in range(t):
+        p1 *= b1
+        p2 *= b2
+    h = np.zeros(8, np.int64)
+    h[0] = t
+    h[1:3] = np.array([p1, p2], np.float64).view(np.int64)
+    st.copy_(torch.from_numpy(h))
+    return st
 
 
 def bits(a):
@@ -32,9 +50,13 @@ def test_adamw_bit_exact_over_steps(gpu_lib, r, d_in, d_out):
     B = (rng.standard_normal((d_out, r)) * 1e-3).astype(np.float32)
     st = [A, B, np.zeros_like(A), np.zeros_like(A), np.zeros_like(B), np.zeros_like(B)]
     tA, tB, tmA, tvA, tmB, tvB = (dev(x) for x in st)
+    state = gpu_lib.adamw_state()
     for step in (1, 2, 3, 1000):
         dA, dB = grads(rng, A.shape), grads(rng, B.shape)
-        gpu_lib.adapter_step_adamw(tA, tB, dev(dA), dev(dB), tmA, tvA, tmB, tvB, step=step, **hp)
+        if step == 1000:                    # jump ahead: the state after 999 steps
+            state = state_at(gpu_lib, 999, hp["beta1"], hp["beta2"])
+        gpu_lib.adapter_step_adamw(tA, tB, dev(dA), dev(dB), tmA, tvA, tmB, tvB, state, **hp)
+        assert int(host(state)[0]) == step
         A2, B2, mA2, vA2, mB2, vB2 = oracle.adapter_step_adamw(
             st[0], st[1], dA, dB, st[2], st[3], st[4], st[5], hp["lr"], hp["beta1"],
             hp["beta2"], hp["eps"], hp["weight_decay"], step)
@@ -56,7 +78,8 @@ def test_adamw_frozen_a_and_hyper_parameters(gpu_lib):
     dB = grads(rng, B.shape)
     tA, tB, tmB, tvB = dev(A), dev(B), dev(mB), dev(vB)
     hp = dict(lr=3e-4, beta1=0.8, beta2=0.95, eps=1e-6, weight_decay=0.1)
-    gpu_lib.adapter_step_adamw(tA, tB, None, dev(dB), None, None, tmB, tvB, step=17, **hp)
+    state = state_at(gpu_lib, 16, hp["beta1"], hp["beta2"])
+    gpu_lib.adapter_step_adamw(tA, tB, None, dev(dB), None, None, tmB, tvB, state, **hp)
     _, B2, _, _, mB2, vB2 = oracle.adapter_step_adamw(A, B, None, dB, None, None, mB, vB,
                                                       hp["lr"], hp["beta1"], hp["beta2"],
                                                       hp["eps"], hp["weight_decay"], 17)
@@ -67,7 +90,8 @@ def test_adamw_frozen_a_and_hyper_parameters(gpu_lib):
 
 def test_adamw_empty(gpu_lib):
     announce("adapter_step_adamw r = 0")
-    import torch
     z = torch.zeros((0, 32), device="cuda")
     zb = torch.zeros((48, 0), device="cuda")
-    gpu_lib.adapter_step_adamw(z, zb, z, zb, z, z, zb, zb, lr=1e-3, step=1)
+    state = gpu_lib.adamw_state()
+    gpu_lib.adapter_step_adamw(z, zb, z, zb, z, z, zb, zb, state, lr=1e-3)
+    assert int(host(state)[0]) == 1                 # the step is counted

@@ -13,16 +13,27 @@ pytestmark = pytest.mark.gpu
 
 
 def state(m):
-    return [host(t).copy() for t in (m.wq, m.A, m.B, m.y, m.dx, m.dA, m.dB, m.rho)] + \
-        [host(m.sel)[:int(host(m.n_sel)[0])].copy()]
+    ts = [m.wq, m.A, m.B, m.y, m.dx, m.dB, m.rho]
+    ts += [t for t in (m.dA, getattr(m, "u", None), getattr(m, "mB", None),
+                       getattr(m, "vB", None), getattr(m, "adam_state", None)) if t is not None]
+    return [host(t).copy() for t in ts] + [host(m.sel)[:int(host(m.n_sel)[0])].copy()]
 
 
-def test_graph_replay_matches_eager(gpu_lib):
-    announce("graph capture of one step, 3 replays vs eager")
-    spec = wl.LinearSpec("g", d_out=768, d_in=1024, tokens=640, rank=16, dy_std=1e-2)
+# the default step (A trained, SGD, E4M3), and the pages' own setup: A frozen in
+# FP8 (X~A~^T formed in the forward GEMM), 32-bit AdamW whose step count lives
+# on the device, and here an E5M2 gradient
+CONFIGS = {"default": {}, "frozen_fp8_a_adamw_e5m2": dict(fp8_a=True, optimizer="adamw",
+                                                          g_fmt="e5m2")}
+
+
+@pytest.mark.parametrize("cfg", sorted(CONFIGS))
+def test_graph_replay_matches_eager(gpu_lib, cfg):
+    announce(f"graph capture of one step ({cfg}), 3 replays vs eager")
+    spec = wl.LinearSpec("g", d_out=1024, d_in=1024, tokens=640, rank=16, dy_std=1e-2)
     d = wl.make_linear(7, 0, spec)
     batches = [wl.step_activations(7, 0, spec, s) for s in range(3)]
-    mk = lambda: gpu_lib.MeldedLinear(spec.d_out, spec.d_in, spec.rank, spec.tokens)
+    mk = lambda: gpu_lib.MeldedLinear(spec.d_out, spec.d_in, spec.rank, spec.tokens,  # noqa: E731
+                                      **CONFIGS[cfg])
     eager, graphed = mk(), mk()
     for m in (eager, graphed):
         m.init_state(dev(d["W"]), dev(d["A"]), dev(d["B"]))
