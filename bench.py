@@ -152,6 +152,12 @@ def main():
         pc[i][5].elapsed_time(pc[i][6]) for i in range(n_pc) if merges(args.warmup + i)
     ) * 1e3 / max(1, n_merge)
 
+    # Copy-kernel reference (not part of the timed region): a 256 MiB device
+    # copy whose source was evicted from the 256 MB last-level cache by a
+    # 1 GiB write, timed with HIP events; the bandwidth kernels are also
+    # reported as a fraction of this measured rate.
+    copy_gbs = copy_reference_gbs(torch, stream)
+
     # A plain device copy of known size, for scaling the HBM byte counters of
     # a profiler run (not part of the timed region).
     # The source is written, then 1 GiB of other data is written so that the
@@ -246,8 +252,11 @@ def main():
         "fwd_gemm_us_timed": round(gemm_timed_us, 2),
         "quantize_x_GBps": round(quant_gbs, 1),
         "quantize_x_hbm_frac": round(quant_gbs / HBM_PEAK_GBS, 4),
+        "copy_reference_GBps": round(copy_gbs, 1),
+        "quantize_x_frac_of_copy": round(quant_gbs / copy_gbs, 4),
         "proxy_update_GBps": round(proxy_gbs, 1),
         "proxy_update_hbm_frac": round(proxy_gbs / HBM_PEAK_GBS, 4),
+        "proxy_update_frac_of_copy": round(proxy_gbs / copy_gbs, 4),
         "selected_rows_last_step": n_sel,
     }
 
@@ -255,6 +264,30 @@ def main():
         out["cpu_baseline"] = cpu_baseline(spec, d0, args.cpu_tokens, args.optimizer, frozen,
                                            args.grad_format)
     print(json.dumps(out), flush=True)
+
+
+def copy_reference_gbs(torch, stream, mib=256, reps=5):
+    """Bytes read + written per second by a plain device-to-device copy of
+    `mib` MiB whose source is first pushed out of the last-level cache (median
+    of `reps`)."""
+    n = mib << 18
+    src = torch.ones(n, device="cuda")
+    dst = torch.empty_like(src)
+    evict = torch.empty(1 << 28, device="cuda")
+    times = []
+    with torch.cuda.stream(stream):
+        for _ in range(reps):
+            evict.fill_(1.0)
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            dst.copy_(src)
+            b.record(stream)
+            b.synchronize()
+            times.append(a.elapsed_time(b) * 1e-3)
+    del src, dst, evict
+    times.sort()
+    return 2 * n * 4 / times[len(times) // 2] / 1e9
 
 
 GEMM_SOURCES = ("fp8_quantized_lora_amd/csrc/gemm_fp8_kernel.hpp",
