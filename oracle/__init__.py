@@ -9,10 +9,12 @@ from .melded import (fp8_quantize, dequantize, melded_linear_fwd, melded_linear_
                      melded_linear_fwd_frozen_a,
                      melded_linear_bwd_frozen_a, fp8_dequantize, adapter_step, adapter_step_adamw, adamw_scalars, adamw_update,
                      rowwise_proxy_update, row_scores, select_rows,
+                     rowwise_proxy_update_topk_rank, component_scores, select_components,
                      rank_delta, num_threads)
 
 __all__ = ["e4m3", "e5m2", "fp8_quantize", "dequantize", "melded_linear_fwd", "melded_linear_bwd",
            "melded_linear_fwd_frozen_a", "melded_linear_bwd_frozen_a", "fp8_dequantize",
            "adapter_step", "adapter_step_adamw", "adamw_scalars", "adamw_update",
            "rowwise_proxy_update", "row_scores", "select_rows",
+           "rowwise_proxy_update_topk_rank", "component_scores", "select_components",
            "rank_delta", "num_threads"]

@@ -387,3 +387,51 @@ def rowwise_proxy_update(wq: np.ndarray, s_w: float, A: np.ndarray, B: np.ndarra
         wq2[sel] = e4m3.encode(merged)
         B2[sel] = 0.0
     return wq2, B2, sel, rho
+
+
+# ----------------------------------------------------------------------------
+# rank-component top-k: the other reading of the pages' top-k
+# ----------------------------------------------------------------------------
+def component_scores(A: np.ndarray, B: np.ndarray) -> np.ndarray:
+    """Score of rank component j: the largest magnitude in its rank-1 term
+    B[:, j] A[j, :], i.e. max_i |B[i,j]| * max_k |A[j,k]| (the product of two
+    float32 values, exact in float64).  Maxima do not depend on the order of
+    evaluation, so the score, and every decision taken on it, is exact."""
+    A = np.asarray(A, dtype=np.float32)
+    B = np.asarray(B, dtype=np.float32)
+    r = A.shape[0]
+    ma = np.max(np.abs(A), axis=1).astype(np.float64) if A.shape[1] else np.zeros(r)
+    mb = np.max(np.abs(B), axis=0).astype(np.float64) if B.shape[0] else np.zeros(r)
+    return ma * mb
+
+
+def select_components(A: np.ndarray, B: np.ndarray, k: int) -> np.ndarray:
+    """The k rank components with the largest scores, equal scores going to
+    the lower index; returned in ascending index order."""
+    c = component_scores(A, B)
+    order = sorted(range(c.size), key=lambda j: (-float(c[j]), j))
+    return np.array(sorted(order[:k]), dtype=np.int32)
+
+
+def rowwise_proxy_update_topk_rank(wq: np.ndarray, s_w: float, A: np.ndarray, B: np.ndarray,
+                                   k_rank: int, tau: float, k_max: int = 0):
+    """Row-wise proxy update over the top-k rank components ([P4] thread 3,
+    Q1: the top-k selection operates over the r rows of the adapter, r << d,
+    and reduces the update matrix dimension from r to k, lowering the cost of
+    the weight update).
+
+    Reading used: the k components K of largest score (component_scores)
+    form the delta that is merged, u_i = sum over j in K (ascending) of
+    B[i,j] A[j,:] with the same fmaf chain; rows are scored, selected and
+    merged exactly as in rowwise_proxy_update, and a merged row zeroes only
+    B[i, K] (the other components stay pending in the proxy).  With k_rank = r
+    this is rowwise_proxy_update.
+
+    Returns (new codes, new B, selected rows, rho, K)."""
+    K = select_components(A, B, k_rank)
+    A = np.asarray(A, dtype=np.float32)
+    B = np.asarray(B, dtype=np.float32)
+    wq2, BK, sel, rho = rowwise_proxy_update(wq, s_w, A[K], B[:, K], tau, k_max)
+    B2 = np.array(B, copy=True)
+    B2[:, K] = BK
+    return wq2, B2, sel, rho, K
