@@ -45,6 +45,8 @@ def parse():
     ap.add_argument("--adapter", choices=["trained", "frozen-fp8"], default="trained",
                     help="A trained in fp32 (dA computed), or the pages' training setup: A "
                          "frozen in FP8, X~A~^T formed in the forward, no dA")
+    ap.add_argument("--topk-rank", type=int, default=0,
+                    help="merge only the top-k rank components of the proxy (0: all r)")
     ap.add_argument("--grad-format", choices=["e4m3", "e5m2"], default="e4m3",
                     help="FP8 format of the upstream gradient dY")
     ap.add_argument("--merge-every", type=int, default=1,
@@ -82,7 +84,7 @@ def main():
     d0 = wl.make_linear(2, 0, spec, step=0)
     frozen = args.adapter == "frozen-fp8"
     m = fq.MeldedLinear(d_out, d_in, r, T, optimizer=args.optimizer, fp8_a=frozen,
-                        g_fmt=args.grad_format)
+                        g_fmt=args.grad_format, topk_rank=args.topk_rank)
     t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
     m.init_state(t(d0["W"]), t(d0["A"]), t(d0["B"]))
     batches = []
@@ -123,9 +125,8 @@ def main():
                                     fmt=args.grad_format),
             bwd,
             lambda: m.adapter_update(spec.lr, stream=stream),
-            (lambda: fq.rowwise_proxy_update(m.wq, m.s_w, m.A, m.B, spec.tau, spec.k_max, m.sel,
-                                             m.n_sel, rho=m.rho, ws=m.ws_px, stream=stream))
-            if merges(i) else (lambda: None),
+            (lambda: m.merge(spec.tau, spec.k_max, stream=stream)) if merges(i)
+            else (lambda: None),
         ]
 
     for i in range(args.warmup):
@@ -199,10 +200,11 @@ def main():
     gemm_timed_us = sum(a.elapsed_time(b) for a, b in g_ev) * 1e3 / args.steps
     n_sel = int(m.n_sel.cpu()[0])
 
-    # the rank-r row delta B.A is computed on merge steps only
+    # the row delta B.A (rank r, or the top-k components) on merge steps only
     n_merge_timed = sum(merges(args.warmup + n_pc + i) for i in range(args.steps))
-    flops = (wl.step_flops(T, d_in, d_out, r, frozen_a=frozen)
-             - 2 * d_out * d_in * r * (1 - n_merge_timed / args.steps))
+    chain = 2 * d_out * d_in * (args.topk_rank or r)
+    flops = (wl.step_flops(T, d_in, d_out, r, frozen_a=frozen) - 2 * d_out * d_in * r
+             + chain * n_merge_timed / args.steps)
     tflops = flops / (ms_per_step * 1e-3) / 1e12
     tokens_per_s = T / (ms_per_step * 1e-3)
     gemm_flops = 2 * T * d_in * d_out + (2 * T * d_in * r if frozen else 0)
@@ -234,10 +236,13 @@ def main():
                                + ("step" if args.merge_every == 1 else f"{args.merge_every} steps")
                                + (", A frozen in FP8 (X~A~^T formed in the forward, no dA)"
                                   if frozen else "")
-                               + (", dY in E5M2" if args.grad_format == "e5m2" else ""),
+                               + (", dY in E5M2" if args.grad_format == "e5m2" else "")
+                               + (f", proxy merges the top {args.topk_rank} rank components"
+                                  if args.topk_rank else ""),
                    "tokens": T, "d_in": d_in, "d_out": d_out, "rank": r,
                    "optimizer": args.optimizer, "adapter": args.adapter,
                    "merge_every": args.merge_every, "grad_format": args.grad_format,
+                   "topk_rank": args.topk_rank,
                    "parallelism": "single GPU"},
         "tokens_per_s": round(tokens_per_s, 1),
         "roofline": {"kernel": ("melded_linear_fwd_frozen_a call (FP8 GEMM 4096 x 4096 x 4096 "

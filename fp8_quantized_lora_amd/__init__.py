@@ -19,7 +19,8 @@ import torch
 __all__ = ["load", "FalqError", "fp8_quantize", "fp8_quantize_workspace_bytes",
            "melded_linear_fwd", "melded_linear_bwd", "melded_linear_bwd_workspace_bytes",
            "adapter_step", "adapter_step_adamw", "adamw_state", "ADAMW_STATE_BYTES",
-           "rowwise_proxy_update",
+           "rowwise_proxy_update", "rowwise_proxy_update_topk_rank",
+           "rowwise_proxy_update_topk_rank_workspace_bytes",
            "fp8_dequantize", "melded_linear_fwd_frozen_a", "fp8_quantize_fmt",
            "melded_linear_bwd_fmt", "melded_linear_bwd_frozen_a_fmt", "FORMATS",
            "melded_linear_fwd_frozen_a_workspace_bytes", "melded_linear_bwd_frozen_a",
@@ -61,6 +62,10 @@ _SIGS = {
     "melded_linear_bwd_frozen_a": (_i32, [_c_p, _c_p, _c_p, _c_p, _c_p, _i64, _i64, _i64, _i64,
                                           _c_p, _c_p, _c_p, _sz, _c_p]),
     "rowwise_proxy_update_workspace_bytes": (_sz, [_i64, _i64, _i64]),
+    "rowwise_proxy_update_topk_rank_workspace_bytes": (_sz, [_i64, _i64, _i64, _i64]),
+    "rowwise_proxy_update_topk_rank": (_i32, [_c_p, _c_p, _c_p, _c_p, _i64, _i64, _i64, _i64,
+                                              _f32, _i64, _c_p, _c_p, _c_p, _c_p, _c_p, _sz,
+                                              _c_p]),
     "rowwise_proxy_update": (_i32, [_c_p, _c_p, _c_p, _c_p, _i64, _i64, _i64, _f32, _i64, _c_p,
                                     _c_p, _c_p, _c_p, _sz, _c_p]),
 }
@@ -331,6 +336,31 @@ def rowwise_proxy_update(wq, s_w, A, B, tau: float, k_max: int, sel_idx, n_sel, 
     _check(load().rowwise_proxy_update(_ptr(wq), _ptr(s_w), _ptr(A), _ptr(B), d_in, d_out, r, tau,
                                        k_max, _ptr(sel_idx), _ptr(n_sel), _ptr(rho), _ptr(ws),
                                        ws.numel(), _stream(stream)), "rowwise_proxy_update")
+
+
+
+
+def rowwise_proxy_update_topk_rank_workspace_bytes(d_in: int, d_out: int, r: int,
+                                                   k_rank: int) -> int:
+    return int(load().rowwise_proxy_update_topk_rank_workspace_bytes(d_in, d_out, r, k_rank))
+
+
+def rowwise_proxy_update_topk_rank(wq, s_w, A, B, k_rank: int, tau: float, k_max: int, sel_idx,
+                                   n_sel, comp_idx, rho=None, ws=None, stream=None) -> None:
+    """The row-wise proxy update over the k_rank rank components of largest
+    score (comp_idx receives them, ascending)."""
+    d_out, d_in = wq.shape
+    r = A.shape[0]
+    _req(A, torch.float32, (r, d_in), "A")
+    _req(B, torch.float32, (d_out, r), "B")
+    _req(comp_idx, torch.int32, (k_rank,), "comp_idx")
+    need = rowwise_proxy_update_topk_rank_workspace_bytes(d_in, d_out, r, k_rank)
+    if ws is None:
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=wq.device)
+    _check(load().rowwise_proxy_update_topk_rank(
+        _ptr(wq), _ptr(s_w), _ptr(A), _ptr(B), d_in, d_out, r, k_rank, tau, k_max, _ptr(sel_idx),
+        _ptr(n_sel), _ptr(rho), _ptr(comp_idx), _ptr(ws), ws.numel(), _stream(stream)),
+        "rowwise_proxy_update_topk_rank")
 
 
 from .step import MeldedLinear  # noqa: E402  (buffers + the step's call sequence)

@@ -286,4 +286,33 @@ falq_status rowwise_proxy_update(uint8_t* wq, const float* s_w, const float* A, 
                                               n_sel, rho, ws, reinterpret_cast<hipStream_t>(stream)));
 }
 
+size_t rowwise_proxy_update_topk_rank_workspace_bytes(int64_t d_in, int64_t d_out, int64_t r,
+                                                      int64_t k_rank) {
+  if (d_in < 0 || d_out < 0 || r < 0 || k_rank < 0 || k_rank > r) return 0;
+  return falq::proxy_topk_rank_ws_bytes(d_in, d_out, r, k_rank);
+}
+
+falq_status rowwise_proxy_update_topk_rank(uint8_t* wq, const float* s_w, const float* A, float* B,
+                                           int64_t d_in, int64_t d_out, int64_t r,
+                                           int64_t k_rank, float tau, int64_t k_max,
+                                           int32_t* sel_idx, int32_t* n_sel, float* rho,
+                                           int32_t* comp_idx, void* ws, size_t ws_bytes,
+                                           falq_stream stream) {
+  if (!dims_ok(d_in) || d_out < 0 || d_out > ((int64_t)1 << 30) || r < 0 || r > 65536 ||
+      k_rank < 0 || k_rank > r || k_max < 0)
+    return FALQ_EINVAL;
+  if (!scalar(s_w) || !scalar(n_sel)) return FALQ_EINVAL;
+  if (d_out * d_in > 0 && !need(wq)) return FALQ_EINVAL;
+  if (r * d_in > 0 && !need(A)) return FALQ_EINVAL;
+  if (r * d_out > 0 && !need(B)) return FALQ_EINVAL;
+  if (d_out > 0 && !need(sel_idx)) return FALQ_EINVAL;
+  if (k_rank > 0 && (comp_idx == nullptr || !aligned(comp_idx, 4))) return FALQ_EINVAL;
+  if (!opt(rho)) return FALQ_EINVAL;
+  if (!ws_ok(ws, ws_bytes, rowwise_proxy_update_topk_rank_workspace_bytes(d_in, d_out, r, k_rank)))
+    return FALQ_EINVAL;
+  return hip_status(falq::launch_proxy_update_topk_rank(
+      wq, s_w, A, B, d_in, d_out, r, k_rank, tau, k_max, sel_idx, n_sel, rho, comp_idx, ws,
+      reinterpret_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

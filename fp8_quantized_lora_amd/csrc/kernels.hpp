@@ -95,6 +95,21 @@ hipError_t launch_proxy_update(uint8_t* wq, const float* s_w, const float* A, fl
                                int64_t k_max, int32_t* sel_idx, int32_t* n_sel, float* rho,
                                void* ws, hipStream_t s);
 
+// the same with the chain over ranks kidx[0..r) (ascending) of an adapter whose
+// B rows hold rs values (A rows indexed by kidx too)
+hipError_t launch_proxy_update_ranks(uint8_t* wq, const float* s_w, const float* A, float* B,
+                                     int64_t d_in, int64_t d_out, int64_t r, int64_t rs,
+                                     const int32_t* kidx, float tau, int64_t k_max,
+                                     int32_t* sel_idx, int32_t* n_sel, float* rho, void* ws,
+                                     hipStream_t s);
+// proxy update over the top-k rank components (k <= r <= 65536): K [k] int32 output
+size_t proxy_topk_rank_ws_bytes(int64_t d_in, int64_t d_out, int64_t r, int64_t k);
+hipError_t launch_proxy_update_topk_rank(uint8_t* wq, const float* s_w, const float* A, float* B,
+                                         int64_t d_in, int64_t d_out, int64_t r, int64_t k,
+                                         float tau, int64_t k_max, int32_t* sel_idx,
+                                         int32_t* n_sel, float* rho, int32_t* comp_idx,
+                                         void* ws, hipStream_t s);
+
 // ---- misc -----------------------------------------------------------------
 hipError_t launch_fill_f32(float* p, int64_t n, float v, hipStream_t s);
 

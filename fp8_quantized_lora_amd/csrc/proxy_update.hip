@@ -65,11 +65,15 @@ __device__ __forceinline__ float inv_step_of_code(uint32_t c) {
   return __uint_as_float((uint32_t)(127 + 10 - e) << 23);
 }
 
+// IDX: the chain runs over the r ranks kidx[0..r) (ascending) of an adapter
+// whose B rows hold rs values; otherwise over ranks 0..r-1 and rs = r
+template <bool IDX>
 __global__ __launch_bounds__(kThreads) void proxy_score(const uint8_t* __restrict__ wq,
                                                         const float* __restrict__ s_w_ptr,
                                                         const float* __restrict__ A,
                                                         const float* __restrict__ B, int d_in,
-                                                        int d_out, int r,
+                                                        int d_out, int r, int rs,
+                                                        const int32_t* __restrict__ kidx,
                                                         uint32_t* __restrict__ tmax_part,
                                                         uint32_t* __restrict__ cmax_part,
                                                         uint8_t* __restrict__ staged) {
@@ -91,7 +95,8 @@ __global__ __launch_bounds__(kThreads) void proxy_score(const uint8_t* __restric
   // results are discarded)
   const float* brow[PRW];
 #pragma unroll
-  for (int i = 0; i < PRW; ++i) brow[i] = B + (int64_t)min(wrow0 + i, d_out - 1) * r;
+  for (int i = 0; i < PRW; ++i) brow[i] = B + (int64_t)min(wrow0 + i, d_out - 1) * (IDX ? rs : r);
+  auto rk = [&](int k) { return IDX ? kidx[k] : k; };      // rank of chain position k
 
   // stage `buf` <- A[k0 .. k0+KC) x [col0, col0+512): 16 half rows of 1 KB,
   // four per wave; rows past r and columns past d_in are clamped into A
@@ -100,7 +105,7 @@ __global__ __launch_bounds__(kThreads) void proxy_score(const uint8_t* __restric
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int c = w * 4 + j, kk = c >> 1, h = c & 1;
-      const int gk = min(k0 + kk, r - 1);
+      const int gk = rk(min(k0 + kk, r - 1));
       const int gc = min(col0 + h * 256 + lane * 4, d_in - 4);
       load16_to_lds(A + (int64_t)gk * d_in + gc, __builtin_amdgcn_readfirstlane(lbase + c * 1024));
     }
@@ -135,14 +140,14 @@ __global__ __launch_bounds__(kThreads) void proxy_score(const uint8_t* __restric
 #pragma unroll
       for (int u = 0; u < KG; ++u)
 #pragma unroll
-        for (int i = 0; i < PRW; ++i) bq[u][i] = brow[i][k0 + kk + u];
+        for (int i = 0; i < PRW; ++i) bq[u][i] = brow[i][rk(k0 + kk + u)];
 #pragma unroll
       for (int u = 0; u < KG; ++u) rank(bq[u], buf, kk + u);
     }
     for (; kk < kn; ++kk) {
       float bv[PRW];
 #pragma unroll
-      for (int i = 0; i < PRW; ++i) bv[i] = brow[i][k0 + kk];
+      for (int i = 0; i < PRW; ++i) bv[i] = brow[i][rk(k0 + kk)];
       rank(bv, buf, kk);
     }
   }
@@ -345,9 +350,12 @@ __global__ __launch_bounds__(kSelThreads) void proxy_select(const uint32_t* __re
 }
 
 // one selected row per wave: copy the staged codes, zero the B row
+// zeroes B[row][kidx[k]] for k < r (IDX; B rows hold rs values), else B[row][0..r)
+template <bool IDX>
 __global__ __launch_bounds__(kThreads) void proxy_apply(uint8_t* __restrict__ wq,
                                                         const uint8_t* __restrict__ staged,
                                                         float* __restrict__ B, int d_in, int r,
+                                                        int rs, const int32_t* __restrict__ kidx,
                                                         const int32_t* __restrict__ sel,
                                                         const int32_t* __restrict__ n_sel) {
   const int n = *n_sel;
@@ -358,7 +366,7 @@ __global__ __launch_bounds__(kThreads) void proxy_apply(uint8_t* __restrict__ wq
   const uint4* src = reinterpret_cast<const uint4*>(staged + row * d_in);
   uint4* dst = reinterpret_cast<uint4*>(wq + row * d_in);
   for (int j = lane; j < d_in / 16; j += 64) dst[j] = src[j];
-  for (int k = lane; k < r; k += 64) B[row * r + k] = 0.0f;
+  for (int k = lane; k < r; k += 64) B[row * (IDX ? rs : r) + (IDX ? kidx[k] : k)] = 0.0f;
 }
 
 // p <- fl(p - fl(lr * g)) for two tensors in one launch: float4 slots
@@ -417,6 +425,15 @@ hipError_t launch_proxy_update(uint8_t* wq, const float* s_w, const float* A, fl
                                int64_t d_in, int64_t d_out, int64_t r, float tau, int64_t k_max,
                                int32_t* sel_idx, int32_t* n_sel, float* rho, void* ws,
                                hipStream_t s) {
+  return launch_proxy_update_ranks(wq, s_w, A, B, d_in, d_out, r, r, nullptr, tau, k_max, sel_idx,
+                                   n_sel, rho, ws, s);
+}
+
+hipError_t launch_proxy_update_ranks(uint8_t* wq, const float* s_w, const float* A, float* B,
+                                     int64_t d_in, int64_t d_out, int64_t r, int64_t rs,
+                                     const int32_t* kidx, float tau, int64_t k_max,
+                                     int32_t* sel_idx, int32_t* n_sel, float* rho, void* ws,
+                                     hipStream_t s) {
   const ProxyWs L = proxy_layout(d_in, d_out);
   uint8_t* base = reinterpret_cast<uint8_t*>(ws);
   uint32_t* tmax = reinterpret_cast<uint32_t*>(base + L.off_tmax);
@@ -425,15 +442,24 @@ hipError_t launch_proxy_update(uint8_t* wq, const float* s_w, const float* A, fl
   uint8_t* staged = base + L.off_staged;
   if (d_out > 0 && d_in > 0) {
     dim3 grid((unsigned)((d_out + PRB - 1) / PRB), (unsigned)L.ncb);
-    proxy_score<<<grid, kThreads, 0, s>>>(wq, s_w, A, B, (int)d_in, (int)d_out, (int)r, tmax,
-                                          cmax, staged);
+    if (kidx)
+      proxy_score<true><<<grid, kThreads, 0, s>>>(wq, s_w, A, B, (int)d_in, (int)d_out, (int)r,
+                                                  (int)rs, kidx, tmax, cmax, staged);
+    else
+      proxy_score<false><<<grid, kThreads, 0, s>>>(wq, s_w, A, B, (int)d_in, (int)d_out, (int)r,
+                                                   (int)rs, nullptr, tmax, cmax, staged);
   }
   proxy_select<<<1, kSelThreads, 0, s>>>(tmax, cmax, L.ncb, rr, (int)d_out, tau, (int)k_max,
                                          sel_idx, n_sel);
   if (d_out > 0) {
     const int rows_per_block = kThreads / 64;
-    proxy_apply<<<(unsigned)((d_out + rows_per_block - 1) / rows_per_block), kThreads, 0, s>>>(
-        wq, staged, B, (int)d_in, (int)r, sel_idx, n_sel);
+    const unsigned g = (unsigned)((d_out + rows_per_block - 1) / rows_per_block);
+    if (kidx)
+      proxy_apply<true><<<g, kThreads, 0, s>>>(wq, staged, B, (int)d_in, (int)r, (int)rs, kidx,
+                                               sel_idx, n_sel);
+    else
+      proxy_apply<false><<<g, kThreads, 0, s>>>(wq, staged, B, (int)d_in, (int)r, (int)rs,
+                                                nullptr, sel_idx, n_sel);
   }
   return hipGetLastError();
 }

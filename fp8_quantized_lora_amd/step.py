@@ -27,24 +27,29 @@ from . import (fp8_quantize, fp8_quantize_workspace_bytes, fp8_dequantize, melde
                melded_linear_bwd, melded_linear_bwd_workspace_bytes, melded_linear_fwd_frozen_a,
                melded_linear_fwd_frozen_a_workspace_bytes, melded_linear_bwd_frozen_a,
                melded_linear_bwd_frozen_a_workspace_bytes, adapter_step, adapter_step_adamw,
-               adamw_state,
-               rowwise_proxy_update, rowwise_proxy_update_workspace_bytes)
+               adamw_state, rowwise_proxy_update, rowwise_proxy_update_workspace_bytes,
+               rowwise_proxy_update_topk_rank, rowwise_proxy_update_topk_rank_workspace_bytes)
 
 
 class MeldedLinear:
     def __init__(self, d_out: int, d_in: int, rank: int, tokens: int, device="cuda",
                  x_dtype=torch.float32, train_a: bool = True, optimizer: str = "sgd",
-                 adamw: Optional[dict] = None, fp8_a: bool = False, g_fmt: str = "e4m3"):
+                 adamw: Optional[dict] = None, fp8_a: bool = False, g_fmt: str = "e4m3",
+                 topk_rank: int = 0):
         """optimizer "sgd" (adapter_step) or "adamw" (adapter_step_adamw, with
         hyper-parameters `adamw`: beta1, beta2, eps, weight_decay); fp8_a
         freezes A in FP8 (implies train_a=False); g_fmt is the FP8 format of the
-        upstream gradient dY ("e4m3" or "e5m2")."""
+        upstream gradient dY ("e4m3" or "e5m2"); topk_rank > 0 merges only the
+        top-k rank components of the proxy (rowwise_proxy_update_topk_rank)."""
         if optimizer not in ("sgd", "adamw"):
             raise ValueError(f"optimizer must be 'sgd' or 'adamw', not {optimizer!r}")
         if fp8_a:
             train_a = False
         self.fp8_a = fp8_a
         self.g_fmt = g_fmt
+        if not 0 <= topk_rank <= rank:
+            raise ValueError("topk_rank must be in [0, rank]")
+        self.topk_rank = topk_rank
         self.d_out, self.d_in, self.r, self.T = d_out, d_in, rank, tokens
         self.train_a = train_a
         self.optimizer = optimizer
@@ -89,8 +94,12 @@ class MeldedLinear:
         else:
             bw = melded_linear_bwd_workspace_bytes(tokens, d_in, d_out, rank)
         self.ws_bwd = torch.empty(max(1, bw), dtype=u8, device=dev)
-        self.ws_px = torch.empty(max(1, rowwise_proxy_update_workspace_bytes(d_in, d_out, rank)),
-                                 dtype=u8, device=dev)
+        if topk_rank:
+            self.comp_idx = torch.empty(topk_rank, dtype=i32, device=dev)
+            px = rowwise_proxy_update_topk_rank_workspace_bytes(d_in, d_out, rank, topk_rank)
+        else:
+            px = rowwise_proxy_update_workspace_bytes(d_in, d_out, rank)
+        self.ws_px = torch.empty(max(1, px), dtype=u8, device=dev)
 
     def init_state(self, W: torch.Tensor, A: torch.Tensor, B: torch.Tensor, stream=None):
         """W~ = E4M3(W * s_w), s_w = 448 / max|W| (the initial quantization
@@ -131,8 +140,13 @@ class MeldedLinear:
                                self.vB, self.adam_state, lr, stream=stream, **self.adamw)
 
     def merge(self, tau: float, k_max: int = 0, stream=None):
-        rowwise_proxy_update(self.wq, self.s_w, self.A, self.B, tau, k_max, self.sel, self.n_sel,
-                             rho=self.rho, ws=self.ws_px, stream=stream)
+        if self.topk_rank:
+            rowwise_proxy_update_topk_rank(self.wq, self.s_w, self.A, self.B, self.topk_rank, tau,
+                                           k_max, self.sel, self.n_sel, self.comp_idx,
+                                           rho=self.rho, ws=self.ws_px, stream=stream)
+        else:
+            rowwise_proxy_update(self.wq, self.s_w, self.A, self.B, tau, k_max, self.sel,
+                                 self.n_sel, rho=self.rho, ws=self.ws_px, stream=stream)
 
     def update(self, lr: float, tau: float, k_max: int = 0, stream=None, merge: bool = True):
         """Adapter step, then (if `merge`) the row-wise proxy update.  Between

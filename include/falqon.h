@@ -317,6 +317,33 @@ falq_status rowwise_proxy_update(uint8_t *wq, const float *s_w, const float *A, 
                                  int32_t *sel_idx, int32_t *n_sel, float *rho,
                                  void *ws, size_t ws_bytes, falq_stream stream);
 
+/*
+ * rowwise_proxy_update_topk_rank — the row-wise proxy update restricted to
+ * the top k_rank rank components of the adapter ([rebuttal] thread 3 Q1: the
+ * top-k selection runs over the r rows of the adapter, r << d, and reduces
+ * the update from rank r to rank k, lowering the weight-update cost).
+ * Reading: component j's score is the largest magnitude in its rank-1 term,
+ *     c_j = max_i |B[i,j]| * max_k |A[j,k]|   (product formed in double),
+ * and K is the k_rank components of largest score, equal scores going to the
+ * lower index.  With u_i = sum over j in K, ascending, of B[i,j] A[j,:] (the
+ * same fmaf chain), rows are scored, selected and merged as in
+ * rowwise_proxy_update; a merged row zeroes only B[i, K] — the other
+ * components stay pending.  k_rank = r is rowwise_proxy_update.
+ *
+ *   as rowwise_proxy_update, plus
+ *   k_rank    0 <= k_rank <= r; r <= 65536 here (the ranking is O(r^2))
+ *   comp_idx  [k_rank] int32, device (output): K in ascending order
+ *   ws        workspace of rowwise_proxy_update_topk_rank_workspace_bytes
+ */
+size_t rowwise_proxy_update_topk_rank_workspace_bytes(int64_t d_in, int64_t d_out, int64_t r,
+                                                      int64_t k_rank);
+falq_status rowwise_proxy_update_topk_rank(uint8_t *wq, const float *s_w, const float *A,
+                                           float *B, int64_t d_in, int64_t d_out, int64_t r,
+                                           int64_t k_rank, float tau, int64_t k_max,
+                                           int32_t *sel_idx, int32_t *n_sel, float *rho,
+                                           int32_t *comp_idx, void *ws, size_t ws_bytes,
+                                           falq_stream stream);
+
 #ifdef __cplusplus
 }
 #endif
