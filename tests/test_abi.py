@@ -131,6 +131,19 @@ def test_frozen_a_calls_reject_bad_arguments():
         assert lib.melded_linear_bwd_frozen_a(*a) == EINVAL, idx
 
 
+def test_topk_rank_proxy_rejects_bad_arguments():
+    lib = fq.load()
+    ws = fq.rowwise_proxy_update_topk_rank_workspace_bytes(32, 32, 8, 3)
+    assert ws >= fq.rowwise_proxy_update_workspace_bytes(32, 32, 3)
+    assert fq.rowwise_proxy_update_topk_rank_workspace_bytes(32, 32, 8, 9) == 0     # k > r
+    ok = [P, P, P, P, 32, 32, 8, 3, 0.5, 0, P, P, None, P, P, ws, None]
+    for idx, val in [(7, 9), (7, -1), (6, 70000), (13, None), (4, 20), (15, ws - 1), (1, None),
+                     (10, None)]:
+        a = list(ok)
+        a[idx] = val
+        assert lib.rowwise_proxy_update_topk_rank(*a) == EINVAL, idx
+
+
 def test_proxy_rejects_bad_arguments():
     lib = fq.load()
     ws = fq.rowwise_proxy_update_workspace_bytes(32, 32, 4)

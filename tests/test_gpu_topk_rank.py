@@ -49,8 +49,10 @@ def problem(seed, d_out, d_in, r, b_scale=1e-3):
     return wq, s_w, A, B
 
 
+# r > 1024 takes the three-kernel selection (scores, ranks, compaction)
 @pytest.mark.parametrize("d_out,d_in,r,k", [(256, 512, 16, 4), (300, 48, 7, 3), (512, 256, 64, 64),
-                                             (128, 128, 300, 17), (96, 64, 5, 0)])
+                                             (128, 128, 300, 17), (96, 64, 5, 0),
+                                             (160, 64, 2100, 101)])
 def test_topk_rank_bit_exact(gpu_lib, d_out, d_in, r, k):
     announce(f"proxy update top-{k} of r {r}: {d_out} x {d_in}")
     wq, s_w, A, B = problem(d_out + r + k, d_out, d_in, r)
