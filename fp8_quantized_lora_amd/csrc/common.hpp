@@ -49,6 +49,14 @@ __device__ __forceinline__ uint32_t enc4(float a, float b, float c, float d) {
   return nan_patch((uint32_t)w, a, b, c, d);
 }
 
+// enc4 without the NaN patch, converting over `old` (both halves are
+// rewritten; passing a live register saves zeroing one)
+__device__ __forceinline__ uint32_t enc4_nonan(float a, float b, float c, float d, uint32_t old) {
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(clamp448(a), clamp448(b), (int)old, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(clamp448(c), clamp448(d), w, true);
+  return (uint32_t)w;
+}
+
 // one float -> one E4M3 code
 __device__ __forceinline__ uint32_t enc1(float a) {
   int w = __builtin_amdgcn_cvt_pk_fp8_f32(clamp448(a), 0.0f, 0, false);

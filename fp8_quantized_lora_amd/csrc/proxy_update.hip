@@ -22,15 +22,25 @@
 //  proxy_apply    selected rows only: copy the staged codes into the backbone
 //                 and zero the row of B.
 //
-// proxy_score tiles 32 rows x 512 columns per workgroup: each wave owns 8
-// rows, each lane 8 columns (two groups of 4, 256 apart), so a lane keeps 64
-// accumulators.  A reaches LDS by direct global->LDS loads in stages of 8
-// ranks and is read as two float4 per rank; B is wave-uniform (a wave's rows
-// are the same for all its lanes), so its values come through the scalar
-// cache into SGPRs and feed v_fmac as the scalar operand.  That is 64 fused
-// multiply-adds per 32 bytes of LDS traffic, and no VGPRs or LDS broadcasts
-// for B: the kernel is bound by fp32 VALU issue (2 r flops per backbone
-// byte), which is what the exact, ordered chain costs.
+// proxy_score runs the chain on the matrix cores: the fp32 MFMA with K = 1
+// (v_mfma_f32_32x32x1_2b_f32) adds the outer product of a 64-lane column
+// operand and a 64-lane row operand into two 32 x 32 accumulator blocks,
+// each element with one rounding, i.e. exactly fmaf(b, a, acc).  Fed ranks
+// in ascending order from +0 accumulators, a chain of these MFMAs gives the
+// same bits as the scalar fmaf chain, at twice the rate of unpacked fp32 VALU
+// fmas.  The product is formed transposed: the MFMA's rows are backbone
+// columns (operand A[k, cols]) and its columns are backbone rows (operand
+// B[rows, k]), so that one lane ends up holding 4 consecutive columns of one
+// backbone row per accumulator group (a whole 4-byte code word).
+//
+// Workgroup tile 64 rows x 512 columns, 4 waves of 32 rows x 256 columns.
+// Four MFMAs per rank cover a wave's tile: MFMA m takes column 4L + m of
+// the wave's 256 at lane L (one ds_read_b128 per rank feeds all four) and
+// row L % 32 of B.  Lane l then holds row l % 32 and, per block b and group
+// g, the 16 columns 128b + 32g + 16(l / 32) + [0, 16): one 16-byte code
+// load and one 16-byte staged store each.  A reaches LDS by direct
+// global->LDS loads in stages of KC ranks; B's values (one per lane and rank)
+// are loaded a stage ahead into registers.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -39,36 +49,38 @@
 namespace falq {
 namespace {
 
+typedef float f32x32 __attribute__((ext_vector_type(32)));
+
 constexpr int kThreads = 256;
 constexpr int kSelThreads = 1024;
 constexpr int kSelRhoLds = 16384;  // rows whose scores proxy_select keeps in LDS
-constexpr int PRW = 8;           // rows per wave
-constexpr int PRB = 4 * PRW;     // rows per score workgroup
-constexpr int PCB = 512;         // columns per score workgroup (8 per lane)
+constexpr int PRB = 64;          // rows per score workgroup (two waves of 32)
+constexpr int PCB = 512;         // columns per score workgroup (two waves of 256)
 constexpr int KC = 8;            // ranks per LDS stage
-constexpr int KG = 4;            // ranks per batch of scalar B loads
 
-__device__ __forceinline__ uint32_t max_code_mag(uint32_t w, uint32_t m) {
-  const uint32_t a = w & 0x7F7F7F7Fu;
-  const uint32_t b0 = a & 0xFF, b1 = (a >> 8) & 0xFF, b2 = (a >> 16) & 0xFF, b3 = a >> 24;
-  m = m > b0 ? m : b0;
-  m = m > b1 ? m : b1;
-  m = m > b2 ? m : b2;
-  return m > b3 ? m : b3;
+// max(|x|, |y|, m) in one instruction: fmaxf on values the compiler cannot
+// prove canonical costs a canonicalizing max per operand first.  NaN
+// operands are skipped, as by fmaxf.  Only for VALU results (no MFMA result
+// may be read here: the compiler does not see this operand's producer).
+__device__ __forceinline__ float max3_abs(float x, float y, float m) {
+  float r;
+  asm("v_max3_f32 %0, |%1|, |%2|, %3" : "=v"(r) : "v"(x), "v"(y), "v"(m));
+  return r;
 }
 
-// 1 / E4M3 spacing at the magnitude of code c (0..0x7E): 2^9 for exponent
-// field 0 or 1, else 2^(10 - E)
-__device__ __forceinline__ float inv_step_of_code(uint32_t c) {
-  int e = (int)(c >> 3);
-  e = e < 1 ? 1 : e;
-  return __uint_as_float((uint32_t)(127 + 10 - e) << 23);
+// 1 / E4M3 spacing at magnitude m (the bits of a float >= 0, the largest
+// |dec(code)| of a row): 2^9 below 2^-6 (exponent field 0 or 1), else
+// 2^(3 - E) for m in [2^E, 2^(E+1))
+__device__ __forceinline__ float inv_step_of_mag(uint32_t mbits) {
+  if (mbits < 0x3C800000u) return 512.0f;
+  const int e = (int)(mbits >> 23) - 127;
+  return __uint_as_float((uint32_t)(127 + 3 - e) << 23);
 }
 
 // IDX: the chain runs over the r ranks kidx[0..r) (ascending) of an adapter
 // whose B rows hold rs values; otherwise over ranks 0..r-1 and rs = r
 template <bool IDX>
-__global__ __launch_bounds__(kThreads) void proxy_score(const uint8_t* __restrict__ wq,
+__global__ __launch_bounds__(kThreads, 2) void proxy_score(const uint8_t* __restrict__ wq,
                                                         const float* __restrict__ s_w_ptr,
                                                         const float* __restrict__ A,
                                                         const float* __restrict__ B, int d_in,
@@ -78,133 +90,175 @@ __global__ __launch_bounds__(kThreads) void proxy_score(const uint8_t* __restric
                                                         uint32_t* __restrict__ cmax_part,
                                                         uint8_t* __restrict__ staged) {
   __shared__ __attribute__((aligned(1024))) float sA[2][KC][PCB];       // 32 KB
+  __shared__ uint32_t red_t[4][32], red_c[4][32];
   const int tid = threadIdx.x, lane = tid & 63;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wrow0 = blockIdx.x * PRB + w * PRW;            // this wave's first row
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6), wr = w >> 1, wc = w & 1;
+  const int row0 = blockIdx.x * PRB + wr * 32;             // this wave's first row
   const int col0 = blockIdx.y * PCB;
-  const int c0 = col0 + lane * 4, c1 = c0 + 256;           // this lane's two column groups
-  const bool ok0 = c0 < d_in, ok1 = c1 < d_in;
+  const int colw = col0 + wc * 256;                        // this wave's first column
 
-  float acc[PRW][8];
+  f32x32 acc[4];
 #pragma unroll
-  for (int i = 0; i < PRW; ++i)
+  for (int m = 0; m < 4; ++m)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc[i][e] = 0.0f;
+    for (int v = 0; v < 32; ++v) acc[m][v] = 0.0f;
 
-  // B row pointers of this wave (rows past d_out read the last row; their
-  // results are discarded)
-  const float* brow[PRW];
-#pragma unroll
-  for (int i = 0; i < PRW; ++i) brow[i] = B + (int64_t)min(wrow0 + i, d_out - 1) * (IDX ? rs : r);
+  // this lane's B row (rows past d_out read the last row; their results are
+  // discarded)
+  const float* brow = B + (int64_t)min(row0 + (lane & 31), d_out - 1) * (IDX ? rs : r);
   auto rk = [&](int k) { return IDX ? kidx[k] : k; };      // rank of chain position k
 
   // stage `buf` <- A[k0 .. k0+KC) x [col0, col0+512): 16 half rows of 1 KB,
-  // four per wave; rows past r and columns past d_in are clamped into A
+  // four per wave, by direct loads (columns past d_in are clamped into A).
+  // Chain positions past r are padding: their LDS rows are written +0 and
+  // their B operand is -0 (selected where it is used, so that the B loads
+  // are not waited for early), so their MFMAs add fl(-0 * +0) = -0 to every
+  // accumulator, which leaves each one (signed zeros included) unchanged.
   auto issue = [&](int buf, int k0) {
     const uint32_t lbase = lds_offset(&sA[buf][0][0]);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int c = w * 4 + j, kk = c >> 1, h = c & 1;
-      const int gk = rk(min(k0 + kk, r - 1));
-      const int gc = min(col0 + h * 256 + lane * 4, d_in - 4);
-      load16_to_lds(A + (int64_t)gk * d_in + gc, __builtin_amdgcn_readfirstlane(lbase + c * 1024));
+      if (k0 + kk < r) {
+        const int gc = min(col0 + h * 256 + lane * 4, d_in - 4);
+        load16_to_lds(A + (int64_t)rk(k0 + kk) * d_in + gc,
+                      __builtin_amdgcn_readfirstlane(lbase + c * 1024));
+      } else {
+        *reinterpret_cast<float4*>(&sA[buf][kk][h * 256 + lane * 4]) =
+            make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+      }
     }
   };
-  auto rank = [&](const float (&bv)[PRW], int buf, int kk) {
-    const float4 a0 = *reinterpret_cast<const float4*>(&sA[buf][kk][lane * 4]);
-    const float4 a1 = *reinterpret_cast<const float4*>(&sA[buf][kk][256 + lane * 4]);
+  auto load_b = [&](float (&bv)[KC], int k0) {
 #pragma unroll
-    for (int i = 0; i < PRW; ++i) {
-      acc[i][0] = __builtin_fmaf(bv[i], a0.x, acc[i][0]);
-      acc[i][1] = __builtin_fmaf(bv[i], a0.y, acc[i][1]);
-      acc[i][2] = __builtin_fmaf(bv[i], a0.z, acc[i][2]);
-      acc[i][3] = __builtin_fmaf(bv[i], a0.w, acc[i][3]);
-      acc[i][4] = __builtin_fmaf(bv[i], a1.x, acc[i][4]);
-      acc[i][5] = __builtin_fmaf(bv[i], a1.y, acc[i][5]);
-      acc[i][6] = __builtin_fmaf(bv[i], a1.z, acc[i][6]);
-      acc[i][7] = __builtin_fmaf(bv[i], a1.w, acc[i][7]);
-    }
+    for (int u = 0; u < KC; ++u) bv[u] = brow[rk(min(k0 + u, r - 1))];
   };
 
-  const int nslab = (r + KC - 1) / KC;
-  if (nslab > 0) issue(0, 0);
-  for (int s = 0; s < nslab; ++s) {
+  // one stage: wait for it, start the next one (A into the other LDS buffer,
+  // its B values into `nxt`), then KC ranks of four MFMAs each
+  // this lane's eight 16-byte code chunks (see the epilogue), loaded under
+  // the last stage's MFMAs; addresses are clamped into the backbone and out
+  // of range chunks are not used
+  const int row = row0 + (lane & 31);
+  const int64_t rbase = (int64_t)min(row, d_out - 1) * d_in;
+  uint4 codes[8];
+  auto load_codes = [&]() {
+#pragma unroll
+    for (int bg = 0; bg < 8; ++bg)
+      codes[bg] = *reinterpret_cast<const uint4*>(
+          wq + rbase + min(colw + 32 * bg + 16 * (lane >> 5), d_in - 16));
+  };
+
+  // stage s: wait until this wave's part of it landed (direct loads, padding
+  // stores, B values), then the barrier: all of it landed, and stage s-1 is
+  // no longer read, so its buffer can take stage s+1
+  auto wait_stage = [&]() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0x0070);                      // vmcnt(0) lgkmcnt(0)
+    barrier_no_drain();
+  };
+  auto compute = [&](int s, const float (&cur)[KC]) {       // KC ranks, four MFMAs each
     const int buf = s & 1, k0 = s * KC;
-    wait_vmem(0);                  // this wave's part of stage s has landed
-    barrier_no_drain();            // all of stage s landed; stage s-1 no longer read
-    if (s + 1 < nslab) issue(buf ^ 1, k0 + KC);
-    const int kn = min(KC, r - k0);                          // ranks of this stage, ascending
-    int kk = 0;
-    for (; kk + KG <= kn; kk += KG) {
-      float bq[KG][PRW];
 #pragma unroll
-      for (int u = 0; u < KG; ++u)
-#pragma unroll
-        for (int i = 0; i < PRW; ++i) bq[u][i] = brow[i][rk(k0 + kk + u)];
-#pragma unroll
-      for (int u = 0; u < KG; ++u) rank(bq[u], buf, kk + u);
+    for (int kk = 0; kk < KC; ++kk) {
+      const float4 a = *reinterpret_cast<const float4*>(&sA[buf][kk][wc * 256 + lane * 4]);
+      const float b = k0 + kk < r ? cur[kk] : -0.0f;         // padding: -0
+      acc[0] = __builtin_amdgcn_mfma_f32_32x32x1f32(a.x, b, acc[0], 0, 0, 0);
+      acc[1] = __builtin_amdgcn_mfma_f32_32x32x1f32(a.y, b, acc[1], 0, 0, 0);
+      acc[2] = __builtin_amdgcn_mfma_f32_32x32x1f32(a.z, b, acc[2], 0, 0, 0);
+      acc[3] = __builtin_amdgcn_mfma_f32_32x32x1f32(a.w, b, acc[3], 0, 0, 0);
     }
-    for (; kk < kn; ++kk) {
-      float bv[PRW];
+  };
+  // B values alternate between two register sets; the last stage is peeled
+  // so that the prefetched codes are live only there
+  const int nslab = (r + KC - 1) / KC, last = nslab - 1;
+  float b0[KC], b1[KC];
+  if (nslab > 0) {
+    issue(0, 0);
+    load_b(b0, 0);
+  }
+  int s = 0;
+  for (; s + 1 < last; s += 2) {
+    wait_stage();
+    issue((s + 1) & 1, (s + 1) * KC);
+    load_b(b1, (s + 1) * KC);
+    compute(s, b0);
+    wait_stage();
+    issue(s & 1, (s + 2) * KC);
+    load_b(b0, (s + 2) * KC);
+    compute(s + 1, b1);
+  }
+  if (s < last) {
+    wait_stage();
+    issue((s + 1) & 1, (s + 1) * KC);
+    load_b(b1, (s + 1) * KC);
+    compute(s, b0);
 #pragma unroll
-      for (int i = 0; i < PRW; ++i) bv[i] = brow[i][rk(k0 + kk)];
-      rank(bv, buf, kk);
-    }
+    for (int u = 0; u < KC; ++u) b0[u] = b1[u];
+    ++s;
+  }
+  if (nslab > 0) {
+    wait_stage();
+    load_codes();
+    compute(s, b0);
+  } else {
+    load_codes();
   }
 
-  // Epilogue.  Per row this lane has max |t| and the largest code magnitude
-  // of its 8 columns; the row maxima over the 64 lanes go through LDS (the A
-  // stages are free once every wave has passed the barrier below): every
-  // lane writes its 8 pairs, then lanes 0..7 reduce one row each.
-  __syncthreads();
+  // Epilogue.  Accumulator m, register v = 4bg + q of lane l holds column
+  // colw + 32bg + 16(l / 32) + 4q + m of row row0 + l % 32 (bg = 0..7 spans
+  // the two MFMA blocks and their four register groups): code chunk bg.
   const float s_w = *s_w_ptr;
-  float* red_t = &sA[0][0][0] + w * (2 * PRW * 64);               // [8 rows][64 lanes]
-  uint32_t* red_c = reinterpret_cast<uint32_t*>(red_t + PRW * 64);
+  float tm = 0.0f, cmf = 0.0f;           // max |t| and max |dec(code)| of this lane's columns
 #pragma unroll
-  for (int i = 0; i < PRW; ++i) {
-    const int row = wrow0 + i;
-    float tm = 0.0f;
-    uint32_t cm = 0;
-    if (row < d_out) {
+  for (int bg = 0; bg < 8; ++bg) {
+    const int c = colw + 32 * bg + 16 * (lane >> 5);
+    if (row >= d_out || c >= d_in) continue;                 // d_in is a multiple of 16
+    const uint32_t cw[4] = {codes[bg].x, codes[bg].y, codes[bg].z, codes[bg].w};
+    float sum[4][4];
+    uint32_t out[4];
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int c = h ? c1 : c0;
-        if (!(h ? ok1 : ok0)) continue;
-        const uint32_t codes = *reinterpret_cast<const uint32_t*>(wq + (int64_t)row * d_in + c);
-        const float t0 = s_w * acc[i][4 * h + 0], t1 = s_w * acc[i][4 * h + 1];
-        const float t2 = s_w * acc[i][4 * h + 2], t3 = s_w * acc[i][4 * h + 3];
-        tm = fmaxf(tm, fmaxf(fmaxf(fabsf(t0), fabsf(t1)), fmaxf(fabsf(t2), fabsf(t3))));
-        cm = max_code_mag(codes, cm);
-        const float2 lo = dec2(codes, false), hi = dec2(codes, true);
-        *reinterpret_cast<uint32_t*>(staged + (int64_t)row * d_in + c) =
-            enc4(lo.x + t0, lo.y + t1, hi.x + t2, hi.y + t3);
-      }
+    for (int q = 0; q < 4; ++q) {
+      const int v = 4 * bg + q;
+      const float t0 = s_w * acc[0][v], t1 = s_w * acc[1][v];
+      const float t2 = s_w * acc[2][v], t3 = s_w * acc[3][v];
+      tm = max3_abs(t2, t3, max3_abs(t0, t1, tm));
+      const float2 lo = dec2(cw[q], false), hi = dec2(cw[q], true);
+      cmf = max3_abs(hi.x, hi.y, max3_abs(lo.x, lo.y, cmf));
+      sum[q][0] = lo.x + t0;
+      sum[q][1] = lo.y + t1;
+      sum[q][2] = hi.x + t2;
+      sum[q][3] = hi.y + t3;
+      out[q] = enc4_nonan(sum[q][0], sum[q][1], sum[q][2], sum[q][3], cw[q]);
     }
-    // 16-byte chunk of row i rotated by i: the per-row float4 reads below
-    // then touch 16 distinct chunk positions (no bank conflicts)
-    const int slot = i * 64 + ((((lane >> 2) ^ i) << 2) | (lane & 3));
-    red_t[slot] = tm;
-    red_c[slot] = cm;
-  }
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  if (lane < PRW) {
-    const int row = wrow0 + lane;
-    if (row < d_out) {
-      const float4* rt = reinterpret_cast<const float4*>(red_t + lane * 64);
-      const uint4* rc = reinterpret_cast<const uint4*>(red_c + lane * 64);
-      uint32_t tb = 0, cb = 0;                               // |t| >= 0: bit order = value order
+    bool nan = false;
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const float4 x = rt[j ^ lane];
-        const uint4 y = rc[j ^ lane];
-        tb = max(tb, max(max(__float_as_uint(x.x), __float_as_uint(x.y)),
-                         max(__float_as_uint(x.z), __float_as_uint(x.w))));
-        cb = max(cb, max(max(y.x, y.y), max(y.z, y.w)));
-      }
-      tmax_part[(int64_t)blockIdx.y * d_out + row] = tb;    // this column block's share
-      cmax_part[(int64_t)blockIdx.y * d_out + row] = cb;
+    for (int q = 0; q < 4; ++q)
+      nan |= __builtin_isnan(sum[q][0]) | __builtin_isnan(sum[q][1]) |
+             __builtin_isnan(sum[q][2]) | __builtin_isnan(sum[q][3]);
+    if (__builtin_expect(nan, 0)) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) out[q] = nan_patch(out[q], sum[q][0], sum[q][1], sum[q][2], sum[q][3]);
+    }
+    *reinterpret_cast<uint4*>(staged + (int64_t)row * d_in + c) =
+        make_uint4(out[0], out[1], out[2], out[3]);
+  }
+  uint32_t cm = __float_as_uint(cmf);
+  // row maxima: lanes l and l + 32 share a row; then the two waves of the
+  // same rows meet in LDS (|t| >= 0: bit order = value order)
+  uint32_t tb = __float_as_uint(tm);
+  tb = max(tb, (uint32_t)__shfl_xor((int)tb, 32, 64));
+  cm = max(cm, (uint32_t)__shfl_xor((int)cm, 32, 64));
+  if (lane < 32) {
+    red_t[w][lane] = tb;
+    red_c[w][lane] = cm;
+  }
+  __syncthreads();
+  if (tid < PRB) {
+    const int half = tid >> 5, i = tid & 31, rr = blockIdx.x * PRB + tid;
+    if (rr < d_out) {
+      tmax_part[(int64_t)blockIdx.y * d_out + rr] = max(red_t[2 * half][i], red_t[2 * half + 1][i]);
+      cmax_part[(int64_t)blockIdx.y * d_out + rr] = max(red_c[2 * half][i], red_c[2 * half + 1][i]);
     }
   }
 }
@@ -274,7 +328,7 @@ __global__ __launch_bounds__(kSelThreads) void proxy_select(const uint32_t* __re
     for (int j = 0; j < 4; ++j) {
       const int i = i0 + j * kSelThreads;
       if (i < d_out) {
-        const float x = __uint_as_float(tb[j]) * inv_step_of_code(cb[j]);
+        const float x = __uint_as_float(tb[j]) * inv_step_of_mag(cb[j]);
         rho[i] = x;
         if (rv != rho) rv[i] = x;
       }
