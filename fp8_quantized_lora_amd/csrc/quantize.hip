@@ -28,12 +28,23 @@ constexpr int kThreads = 256;
 constexpr int kUnroll = 8;
 constexpr int kAmaxUnroll = 16;
 
+// x is streamed with nontemporal loads: both passes read each byte once, and
+// a load that allocates in the caches has to write back the dirty lines that
+// earlier kernels' outputs left there first (measured on a bf16 4096 x 4096
+// tensor after a large write: 20 us for the amax pass with ordinary loads,
+// 10 us with nontemporal ones)
+__device__ __forceinline__ uint4 stream16(const void* x, int64_t i) {
+  const v4i t = __builtin_nontemporal_load(reinterpret_cast<const v4i*>(x) + i);
+  return make_uint4((uint32_t)t[0], (uint32_t)t[1], (uint32_t)t[2], (uint32_t)t[3]);
+}
+
 template <int DT> struct Vec;
 template <> struct Vec<0> {  // float32: 4 elements per 16-byte load
   static constexpr int N = 4;
   __device__ static void load(const void* x, int64_t i, float (&v)[8]) {
-    float4 f = reinterpret_cast<const float4*>(x)[i];
-    v[0] = f.x; v[1] = f.y; v[2] = f.z; v[3] = f.w;
+    const uint4 u = stream16(x, i);
+    v[0] = __uint_as_float(u.x); v[1] = __uint_as_float(u.y);
+    v[2] = __uint_as_float(u.z); v[3] = __uint_as_float(u.w);
   }
   __device__ static float scalar(const void* x, int64_t i) {
     return reinterpret_cast<const float*>(x)[i];
@@ -42,7 +53,7 @@ template <> struct Vec<0> {  // float32: 4 elements per 16-byte load
 template <> struct Vec<1> {  // bfloat16: 8 elements per 16-byte load
   static constexpr int N = 8;
   __device__ static void load(const void* x, int64_t i, float (&v)[8]) {
-    uint4 u = reinterpret_cast<const uint4*>(x)[i];
+    const uint4 u = stream16(x, i);
     uint32_t w[4] = {u.x, u.y, u.z, u.w};
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
