@@ -96,3 +96,23 @@ def test_proxy_large_rank(gpu_lib):
     announce("proxy 1024 x 4096, r=2048")
     wq, s_w, A, B = proxy_problem(13, 1024, 4096, 2048, b_scale=0.0005)
     check(gpu_lib, wq, s_w, A, B)
+
+
+@pytest.mark.parametrize("r", [5, 8, 9])
+def test_proxy_signed_zero_accumulators(gpu_lib, r):
+    """Rows whose every product underflows to -0 end the chain at -0, so
+    their -0 codes (0x80) stay -0 when merged (dec + t = -0 + -0); ranks that
+    pad the chain to a whole stage on the GPU must not turn such an
+    accumulator into +0.  tau = 0 merges every row."""
+    announce(f"proxy signed-zero accumulators r={r}")
+    rng = np.random.default_rng(100 + r)
+    d_out, d_in = 72, 48
+    wq = rng.integers(0, 0x7F, size=(d_out, d_in)).astype(np.uint8)
+    wq[rng.random(wq.shape) < 0.3] = 0x80
+    wq[rng.random(wq.shape) < 0.1] = 0x00
+    A = (rng.uniform(1.0, 2.0, (r, d_in)) * 1e-20).astype(np.float32)
+    B = (rng.standard_normal((d_out, r)) * 1e-3).astype(np.float32)
+    B[::2] = (-rng.uniform(1.0, 2.0, (d_out // 2, r)) * 1e-30).astype(np.float32)
+    r_wq = oracle.rowwise_proxy_update(wq, np.float32(0.01), A, B, 0.0, 0)[0]
+    assert np.count_nonzero(r_wq[::2] == 0x80) > 0, "fixture keeps no -0 code"
+    check(gpu_lib, wq, np.float32(0.01), A, B, tau=0.0)
