@@ -25,7 +25,7 @@ __all__ = ["load", "FalqError", "fp8_quantize", "fp8_quantize_workspace_bytes",
            "melded_linear_bwd_fmt", "melded_linear_bwd_frozen_a_fmt", "FORMATS",
            "melded_linear_fwd_frozen_a_workspace_bytes", "melded_linear_bwd_frozen_a",
            "melded_linear_bwd_frozen_a_workspace_bytes", "rowwise_proxy_update_workspace_bytes",
-           "version", "LIB_PATH"]
+           "fp4_quantize", "melded_linear_fwd_fp4", "version", "LIB_PATH"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfalqon.so")
 _lib = None
@@ -68,6 +68,8 @@ _SIGS = {
                                               _c_p]),
     "rowwise_proxy_update": (_i32, [_c_p, _c_p, _c_p, _c_p, _i64, _i64, _i64, _f32, _i64, _c_p,
                                     _c_p, _c_p, _c_p, _sz, _c_p]),
+    "fp4_quantize": (_i32, [_c_p, _i32, _i64, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _sz, _c_p]),
+    "melded_linear_fwd_fp4": (_i32, [_c_p, _c_p, _c_p, _c_p, _i64, _i64, _i64, _c_p, _c_p]),
 }
 
 
@@ -182,6 +184,44 @@ def melded_linear_fwd(xq: torch.Tensor, s_x: torch.Tensor, wq: torch.Tensor, s_w
     _req(y, torch.float32, (T, d_out), "y")
     _check(load().melded_linear_fwd(_ptr(xq), _ptr(s_x), _ptr(wq), _ptr(s_w), T, d_in, d_out,
                                     _ptr(y), _stream(stream)), "melded_linear_fwd")
+
+
+def fp4_quantize(x: torch.Tensor, q: torch.Tensor, scale: torch.Tensor,
+                 scale_in: Optional[torch.Tensor] = None, amax: Optional[torch.Tensor] = None,
+                 nonfinite: Optional[torch.Tensor] = None, ws: Optional[torch.Tensor] = None,
+                 stream=None) -> None:
+    """q = FP4 E2M1(x * s), s = 6 / amax(x), two codes per byte along the last
+    axis (q has the shape of x with the last axis halved)."""
+    lib = load()
+    if x.dtype == torch.float32:
+        dt = 0
+    elif x.dtype == torch.bfloat16:
+        dt = 1
+    else:
+        raise FalqError("fp4_quantize: x must be float32 or bfloat16")
+    if x.dim() == 0 or x.shape[-1] % 2:
+        raise FalqError("fp4_quantize: the last axis of x must have even length")
+    n = x.numel()
+    _req(q, torch.uint8, tuple(x.shape[:-1]) + (x.shape[-1] // 2,), "q")
+    wsb = fp8_quantize_workspace_bytes(n)
+    if ws is None:
+        ws = torch.empty(wsb, dtype=torch.uint8, device=x.device)
+    _check(lib.fp4_quantize(_ptr(x), dt, n, _ptr(scale_in), _ptr(q), _ptr(scale), _ptr(amax),
+                            _ptr(nonfinite), _ptr(ws), ws.numel(), _stream(stream)),
+           "fp4_quantize")
+
+
+def melded_linear_fwd_fp4(xq: torch.Tensor, s_x: torch.Tensor, wq: torch.Tensor,
+                          s_w: torch.Tensor, y: torch.Tensor, stream=None) -> None:
+    """y = dec(xq) dec(wq)^T / (s_x s_w) with FP4 E2M1 operands (two codes per
+    byte: xq [T x d_in/2], wq [d_out x d_in/2])."""
+    T, half = xq.shape
+    d_in = 2 * half
+    d_out = wq.shape[0]
+    _req(wq, torch.uint8, (d_out, half), "wq")
+    _req(y, torch.float32, (T, d_out), "y")
+    _check(load().melded_linear_fwd_fp4(_ptr(xq), _ptr(s_x), _ptr(wq), _ptr(s_w), T, d_in, d_out,
+                                        _ptr(y), _stream(stream)), "melded_linear_fwd_fp4")
 
 
 def melded_linear_bwd_workspace_bytes(T: int, d_in: int, d_out: int, r: int) -> int:

@@ -86,6 +86,35 @@ falq_status fp8_quantize_fmt(const void* x, int dtype, int64_t n, int fmt, const
                                           ws, reinterpret_cast<hipStream_t>(stream)));
 }
 
+falq_status fp4_quantize(const void* x, int dtype, int64_t n, const float* scale_in, uint8_t* q,
+                         float* scale, float* amax, int32_t* nonfinite, void* ws, size_t ws_bytes,
+                         falq_stream stream) {
+  if (n < 0 || n % 2 != 0 || (dtype != FALQ_F32 && dtype != FALQ_BF16)) return FALQ_EINVAL;
+  if (n > 0 && (!need(x) || !need(q))) return FALQ_EINVAL;
+  if (!scalar(scale) || (scale_in && !aligned(scale_in, 4)) || (amax && !aligned(amax, 4)) ||
+      (nonfinite && !aligned(nonfinite, 4)))
+    return FALQ_EINVAL;
+  if (!ws_ok(ws, ws_bytes, falq::quantize_ws_bytes())) return FALQ_EINVAL;
+  return hip_status(falq::launch_quantize(x, dtype, 2, n, scale_in, q, scale, amax, nonfinite, ws,
+                                          reinterpret_cast<hipStream_t>(stream)));
+}
+
+falq_status melded_linear_fwd_fp4(const uint8_t* xq, const float* s_x, const uint8_t* wq,
+                                  const float* s_w, int64_t T, int64_t d_in, int64_t d_out,
+                                  float* y, falq_stream stream) {
+  if (T < 0 || T > ((int64_t)1 << 30) || !dims_ok(d_in) || d_in % 256 != 0 || !dims_ok(d_out))
+    return FALQ_EINVAL;
+  if (!scalar(s_x) || !scalar(s_w)) return FALQ_EINVAL;
+  if (T * d_in > 0 && !need(xq)) return FALQ_EINVAL;
+  if (d_out * d_in > 0 && !need(wq)) return FALQ_EINVAL;
+  if (T * d_out > 0 && !need(y)) return FALQ_EINVAL;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (T == 0 || d_out == 0) return FALQ_OK;
+  if (d_in == 0) return hip_status(falq::launch_fill_f32(y, T * d_out, 0.0f, s));
+  return hip_status(falq::launch_gemm_fp4_nt(xq, d_in / 2, wq, d_in / 2, y, d_out, T, d_out,
+                                             d_in / 2, s_x, s_w, s));
+}
+
 falq_status melded_linear_fwd(const uint8_t* xq, const float* s_x, const uint8_t* wq,
                               const float* s_w, int64_t T, int64_t d_in, int64_t d_out, float* y,
                               falq_stream stream) {

@@ -14,6 +14,7 @@ typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
 
 constexpr float kE4M3Max = 448.0f;
 constexpr float kE5M2Max = 57344.0f;      // OCP E5M2: 1.75 * 2^15 (0x7B)
+constexpr float kE2M1Max = 6.0f;          // OCP FP4 E2M1: 1.5 * 2^2
 
 // ---------------------------------------------------------------------------
 // E4M3 (OCP e4m3fn) conversions on the gfx950 conversion unit.
@@ -55,6 +56,19 @@ __device__ __forceinline__ uint32_t enc4_nonan(float a, float b, float c, float 
   int w = __builtin_amdgcn_cvt_pk_fp8_f32(clamp448(a), clamp448(b), (int)old, false);
   w = __builtin_amdgcn_cvt_pk_fp8_f32(clamp448(c), clamp448(d), w, true);
   return (uint32_t)w;
+}
+
+// one float -> one FP4 E2M1 code (0..15): nearest, ties to the even code,
+// |v| > 6 and infinities saturate to 6, NaN (every comparison false) gives a
+// zero; the sign bit is kept.  The seven midpoints of the magnitudes
+// 0, .5, 1, 1.5, 2, 3, 4, 6 are exact: a tie goes to the code with mantissa
+// bit 0, hence > at 0.25, 1.25, 2.5, 5 and >= at 0.75, 1.75, 3.5
+__device__ __forceinline__ uint32_t enc1_e2m1(float v) {
+  const float a = fabsf(v);
+  const uint32_t c = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
+                     (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) +
+                     (uint32_t)(a > 5.0f);
+  return c | ((__float_as_uint(v) >> 31) << 3);
 }
 
 // one float -> one E4M3 code

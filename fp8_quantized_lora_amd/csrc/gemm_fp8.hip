@@ -97,6 +97,18 @@ hipError_t launch_gemm_fp8_nt(const uint8_t* A, int64_t lda, const uint8_t* B, i
                     : gemm_nt<1>(A, lda, B, ldb, C, ldc, M, N, K, sa, sb, s);
 }
 
+hipError_t launch_gemm_fp4_nt(const uint8_t* A, int64_t lda, const uint8_t* B, int64_t ldb,
+                              float* C, int64_t ldc, int64_t M, int64_t N, int64_t Kb,
+                              const float* sa, const float* sb, hipStream_t s) {
+  if (M == 0 || N == 0) return hipSuccess;
+  if (Kb <= 0 || Kb % gemm::dma::BK != 0) return hipErrorInvalidValue;
+  const int tM = (int)((M + gemm::dma::BM - 1) / gemm::dma::BM);
+  const int tN = (int)((N + gemm::dma::BN - 1) / gemm::dma::BN);
+  gemm::dma::gemm_fp8_nt_dma<false, 4><<<tM * tN, gemm::dma::kThreads, 0, s>>>(
+      A, lda, B, ldb, C, ldc, (int)M, (int)N, (int)Kb, sa, sb, tM, tN, gemm::dma::SecondB{});
+  return hipGetLastError();
+}
+
 bool gemm_fp8_nt_fuses_second(int64_t N, int64_t K, int64_t R) {
   if (R <= 0 || K <= 0 || K % gemm::dma::BK != 0) return false;
   const int64_t tN = (N + gemm::dma::BN - 1) / gemm::dma::BN;

@@ -210,7 +210,8 @@ struct SecondB {
   const float* sb;
 };
 
-// FA: format of the A codes (0 = E4M3, 1 = E5M2); B (and the second B) E4M3
+// FA: format of the A codes (0 = E4M3, 1 = E5M2; B and the second B are
+// E4M3), or 4: both operands FP4 E2M1, two codes per byte (K counts bytes)
 template <bool FU, int FA>
 __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_nt_dma(
     const uint8_t* __restrict__ A, int64_t lda, const uint8_t* __restrict__ B, int64_t ldb,
@@ -280,8 +281,22 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_nt_dma(
   const int sw = swz(r16);
   const int o0 = ((2 * g) ^ sw) * 16, o1 = ((2 * g + 1) ^ sw) * 16;
   const int offA = (wm * WTM + r16) * BK, offB = BM * BK + (wn * WTN + r16) * BK;
+  // FP4 (FA == 4): a 128-byte row holds 256 values, two MFMA K-halves of
+  // 128; lane group g reads its 16 bytes of each half (chunks g and g + 4),
+  // joined so that the register layout matches the FP8 path
+  const int p0 = FA == 4 ? (g ^ sw) * 16 : o0, p1 = FA == 4 ? ((g + 4) ^ sw) * 16 : o1;
   auto frag = [&](const uint8_t* p) {
-    return join(*reinterpret_cast<const uint4*>(p + o0), *reinterpret_cast<const uint4*>(p + o1));
+    return join(*reinterpret_cast<const uint4*>(p + p0), *reinterpret_cast<const uint4*>(p + p1));
+  };
+  auto mma = [&](const v8i& a, const v8i& b, v4f c) {
+    if constexpr (FA == 4) {
+      const v8i alo = {a[0], a[1], a[2], a[3], 0, 0, 0, 0}, ahi = {a[4], a[5], a[6], a[7], 0, 0, 0, 0};
+      const v8i blo = {b[0], b[1], b[2], b[3], 0, 0, 0, 0}, bhi = {b[4], b[5], b[6], b[7], 0, 0, 0, 0};
+      c = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(alo, blo, c, 4, 4, 0, 0, 0, 0);
+      return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ahi, bhi, c, 4, 4, 0, 0, 0, 0);
+    } else {
+      return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, FA, 0, 0, 0, 0, 0);
+    }
   };
   // No scalar load may be pending when the loop starts: the compiler then
   // treats each step's LDS reads as returning in order and waits only for the
@@ -316,9 +331,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_nt_dma(
       if (i + 1 < MB) af[(i + 1) & 1] = frag(st + offA + (i + 1) * 16 * BK);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int j = 0; j < NB; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[i & 1], bf[j], acc[i][j], FA,
-                                                                     0, 0, 0, 0, 0);
+      for (int j = 0; j < NB; ++j) acc[i][j] = mma(af[i & 1], bf[j], acc[i][j]);
       if (FU && wave_u && i == iu)
         accu = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[i & 1], bu, accu, FA, 0, 0, 0, 0,
                                                                 0);

@@ -11,7 +11,8 @@ namespace falq {
 // ---- fp8_quantize: amax partials + cast ---------------------------------
 constexpr int kQzMaxParts = 2048;
 size_t quantize_ws_bytes();
-// fmt 0: E4M3 (s = 448 / amax), 1: E5M2 (s = 57344 / amax)
+// fmt 0: E4M3 (s = 448 / amax), 1: E5M2 (s = 57344 / amax), 2: FP4 E2M1
+// (s = 6 / amax; two codes per byte, the lower index in the low nibble; n even)
 hipError_t launch_quantize(const void* x, int dtype, int fmt, int64_t n, const float* scale_in,
                            uint8_t* q, float* scale, float* amax, int32_t* nonfinite,
                            void* ws, hipStream_t s);
@@ -26,6 +27,11 @@ hipError_t launch_dequantize(const uint8_t* q, int64_t n, const float* s, float*
 hipError_t launch_gemm_fp8_nt(const uint8_t* A, int64_t lda, const uint8_t* B, int64_t ldb,
                               float* C, int64_t ldc, int64_t M, int64_t N, int64_t K,
                               const float* sa, const float* sb, hipStream_t s, int a_fmt = 0);
+// FP4 E2M1 operands, two codes per byte: C = dec(A) . dec(B)^T / (sa * sb),
+// Kb = bytes per row (a multiple of 128: 256 values)
+hipError_t launch_gemm_fp4_nt(const uint8_t* A, int64_t lda, const uint8_t* B, int64_t ldb,
+                              float* C, int64_t ldc, int64_t M, int64_t N, int64_t Kb,
+                              const float* sa, const float* sb, hipStream_t s);
 // The same product plus Cu[M x R] = dec(A) . dec(Bu)[R x K]^T / (sa * sbu) in
 // the same launch (the DMA kernel's extra units); only where
 // gemm_fp8_nt_fuses_second(N, K, R) holds

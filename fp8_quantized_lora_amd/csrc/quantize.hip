@@ -128,6 +128,14 @@ __device__ __forceinline__ uint32_t enc4f(float a, float b, float c, float d) {
 template <int DT, int F>
 __device__ __forceinline__ void store_codes(uint8_t* __restrict__ q, int64_t i, const float (&v)[8],
                                             float s) {
+  if (F == 2) {                          // FP4 E2M1: two codes per byte, low nibble first
+    uint32_t w = 0;
+#pragma unroll
+    for (int e = 0; e < (DT == 0 ? 4 : 8); ++e) w |= enc1_e2m1(v[e] * s) << (4 * e);
+    if (DT == 0) reinterpret_cast<uint16_t*>(q)[i] = (uint16_t)w;
+    else reinterpret_cast<uint32_t*>(q)[i] = w;
+    return;
+  }
   if (DT == 0) {
     reinterpret_cast<uint32_t*>(q)[i] = enc4f<F>(v[0] * s, v[1] * s, v[2] * s, v[3] * s);
   } else {
@@ -207,7 +215,8 @@ __global__ __launch_bounds__(kThreads) void qz_cast(const void* __restrict__ x, 
 #pragma unroll
   for (int u = 0; u < kUnroll; ++u)
     if (i0 + u * kThreads < b1) V::load(x, i0 + u * kThreads, v[u]);
-  const float s = fold_scale(part_max, part_bad, nparts, F == 0 ? kE4M3Max : kE5M2Max, scale_in,
+  const float s = fold_scale(part_max, part_bad, nparts,
+                             F == 0 ? kE4M3Max : (F == 1 ? kE5M2Max : kE2M1Max), scale_in,
                              scale_out, amax_out, nonfinite_out);
   while (true) {
 #pragma unroll
@@ -221,9 +230,16 @@ __global__ __launch_bounds__(kThreads) void qz_cast(const void* __restrict__ x, 
     for (int u = 0; u < kUnroll; ++u)
       if (i0 + u * kThreads < b1) V::load(x, i0 + u * kThreads, v[u]);
   }
-  if (blockIdx.x == 0)
-    for (int64_t i = nvec * V::N + threadIdx.x; i < n; i += kThreads)
-      q[i] = (uint8_t)(F == 0 ? enc1(V::scalar(x, i) * s) : enc1_e5m2(V::scalar(x, i) * s));
+  if (blockIdx.x == 0) {
+    if (F == 2) {                        // n is even: the tail in whole bytes
+      for (int64_t i = nvec * V::N + 2 * threadIdx.x; i + 1 < n; i += 2 * kThreads)
+        q[i / 2] = (uint8_t)(enc1_e2m1(V::scalar(x, i) * s) |
+                             (enc1_e2m1(V::scalar(x, i + 1) * s) << 4));
+    } else {
+      for (int64_t i = nvec * V::N + threadIdx.x; i < n; i += kThreads)
+        q[i] = (uint8_t)(F == 0 ? enc1(V::scalar(x, i) * s) : enc1_e5m2(V::scalar(x, i) * s));
+    }
+  }
 }
 
 int blocks_for(int64_t nvec, int unroll, int cap) {
@@ -285,9 +301,11 @@ hipError_t launch_quantize(const void* x, int dtype, int fmt, int64_t n, const f
   qz_cast<DT, F><<<g2, kThreads, 0, s>>>(x, n, part_max, part_bad, g1, scale_in, q, scale, amax, \
                                          nonfinite)
   if (dtype == 0 && fmt == 0) FALQ_CAST(0, 0);
-  else if (dtype == 0) FALQ_CAST(0, 1);
+  else if (dtype == 0 && fmt == 1) FALQ_CAST(0, 1);
+  else if (dtype == 0) FALQ_CAST(0, 2);
   else if (fmt == 0) FALQ_CAST(1, 0);
-  else FALQ_CAST(1, 1);
+  else if (fmt == 1) FALQ_CAST(1, 1);
+  else FALQ_CAST(1, 2);
 #undef FALQ_CAST
   return hipGetLastError();
 }

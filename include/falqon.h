@@ -125,6 +125,41 @@ falq_status fp8_quantize_fmt(const void *x, int dtype, int64_t n, int fmt,
                              falq_stream stream);
 
 /*
+ * fp4_quantize — the per-tensor current-scaled cast of fp8_quantize into FP4
+ * E2M1 codes (the pages estimate an FP4 variant only from the FP4/FP8 matrix
+ * throughput ratio, [rebuttal] thread 2 W2, Table R3; they give no FP4
+ * recipe, so the FP8 one is kept): s = 6 / amax over the finite elements
+ * (amax == 0: s = 1; a quotient that overflows: FLT_MAX), unless scale_in
+ * is given; code = E2M1(fl(x * s)): magnitudes 0, .5, 1, 1.5, 2, 3, 4, 6,
+ * nearest with ties to the code whose mantissa bit is 0, |v| > 6 and
+ * infinities saturate to 6, NaN (no E2M1 encoding) becomes a zero, the sign
+ * bit is kept.  Two codes per byte: element 2j in the low nibble of byte j.
+ *
+ *   x, dtype, n, scale_in, scale, amax, nonfinite, ws, ws_bytes: as fp8_quantize
+ *   q   n / 2 bytes, device (output); n must be even (FALQ_EINVAL otherwise)
+ * Workspace: fp8_quantize_workspace_bytes(n).
+ */
+falq_status fp4_quantize(const void *x, int dtype, int64_t n, const float *scale_in, uint8_t *q,
+                         float *scale, float *amax, int32_t *nonfinite, void *ws,
+                         size_t ws_bytes, falq_stream stream);
+
+/*
+ * melded_linear_fwd_fp4 — melded_linear_fwd with FP4 E2M1 operands on the
+ * gfx950 FP4 matrix cores (the measurement the pages' Table R3 estimates):
+ *     Y[t,o] = (sum_k dec(xq[t,k]) * dec(wq[o,k])) / (s_x * s_w)
+ *
+ *   xq  [T x d_in/2]     E2M1 codes of X as fp4_quantize writes them, device
+ *   wq  [d_out x d_in/2] E2M1 codes of the backbone, device
+ *   s_x, s_w             device floats
+ *   y   [T x d_out]      float32, device (output)
+ * d_in must be a multiple of 256 and d_out a multiple of 16 (FALQ_EINVAL
+ * otherwise); T any.  No workspace.
+ */
+falq_status melded_linear_fwd_fp4(const uint8_t *xq, const float *s_x, const uint8_t *wq,
+                                  const float *s_w, int64_t T, int64_t d_in, int64_t d_out,
+                                  float *y, falq_stream stream);
+
+/*
  * melded_linear_fwd — the forward of the melded layer as one FP8 GEMM with
  * no separate LoRA path ([intro] method paragraph; abstract):
  *     Y[t,o] = (sum_k dec(xq[t,k]) * dec(wq[o,k])) / (s_x * s_w)

@@ -170,3 +170,19 @@ def test_melded_linear_buffers_on_host():
     assert fq.MeldedLinear(64, 32, 4, 16, device="cpu").optimizer == "sgd"
     with pytest.raises(ValueError):
         fq.MeldedLinear(64, 32, 4, 16, device="cpu", optimizer="adam")
+
+
+def test_fp4_calls_reject_bad_arguments():
+    lib = fq.load()
+    ws = fq.fp8_quantize_workspace_bytes(16)
+    assert lib.fp4_quantize(P, 0, 15, None, P, P, None, None, P, ws, None) == EINVAL      # odd n
+    assert lib.fp4_quantize(P, 0, -2, None, P, P, None, None, P, ws, None) == EINVAL
+    assert lib.fp4_quantize(P, 3, 16, None, P, P, None, None, P, ws, None) == EINVAL      # dtype
+    assert lib.fp4_quantize(P, 0, 16, None, None, P, None, None, P, ws, None) == EINVAL   # q null
+    assert lib.fp4_quantize(P, 0, 16, None, P, P, None, None, P, ws - 1, None) == EINVAL  # short ws
+    # d_in must be a multiple of 256, d_out of 16
+    assert lib.melded_linear_fwd_fp4(P, P, P, P, 8, 128, 32, P, None) == EINVAL
+    assert lib.melded_linear_fwd_fp4(P, P, P, P, 8, 256, 24, P, None) == EINVAL
+    assert lib.melded_linear_fwd_fp4(P, None, P, P, 8, 256, 32, P, None) == EINVAL        # s_x
+    assert lib.melded_linear_fwd_fp4(P, P, P, P, 8, 256, 32, None, None) == EINVAL        # y
+    assert lib.melded_linear_fwd_fp4(P, P, P, P, 0, 256, 32, P, None) == 0                # T = 0
