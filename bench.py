@@ -55,6 +55,9 @@ def parse():
     ap.add_argument("--optimizer", choices=["sgd", "adamw"], default="sgd",
                     help="adapter optimizer: SGD lr 1e-3 (the workload's) or 32-bit AdamW "
                          "(the pages' training runs)")
+    ap.add_argument("--fp4-gemm", action="store_true",
+                    help="also time the forward product with FP4 E2M1 operands (X and W cast "
+                         "by fp4_quantize) against the FP8 one, alternating launches")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB before the timed steps "
                          "(calibrates the HBM byte counters of a profiler run)")
@@ -265,10 +268,57 @@ def main():
         "selected_rows_last_step": n_sel,
     }
 
+    if args.fp4_gemm:
+        out["fp4_forward"] = fp4_forward(torch, fq, batches[0][0], t(d0["W"]), m, stream)
+
     if not args.no_cpu_baseline and args.cpu_tokens > 0:
         out["cpu_baseline"] = cpu_baseline(spec, d0, args.cpu_tokens, args.optimizer, frozen,
                                            args.grad_format)
     print(json.dumps(out), flush=True)
+
+
+FP4_PEAK_TFLOPS = 10100.0     # MI355X dense FP4 matrix peak
+
+
+def fp4_forward(torch, fq, X, W, m, stream, reps=20):
+    """The forward product with FP4 E2M1 operands (the pages' Table R3
+    estimates an FP4 speed-up from the FP4/FP8 matrix throughput ratio; this
+    measures it): X and W cast by fp4_quantize, melded_linear_fwd_fp4 and the
+    FP8 melded_linear_fwd launched alternately, each between HIP events on
+    the bench stream."""
+    T, d_in = X.shape
+    d_out = W.shape[0]
+    xq4 = torch.empty((T, d_in // 2), dtype=torch.uint8, device="cuda")
+    wq4 = torch.empty((d_out, d_in // 2), dtype=torch.uint8, device="cuda")
+    sx4 = torch.zeros(1, device="cuda")
+    sw4 = torch.zeros(1, device="cuda")
+    y4 = torch.empty((T, d_out), device="cuda")
+    fq.fp4_quantize(X, xq4, sx4, stream=stream)
+    fq.fp4_quantize(W, wq4, sw4, stream=stream)
+    f4 = lambda: fq.melded_linear_fwd_fp4(xq4, sx4, wq4, sw4, y4, stream=stream)  # noqa: E731
+    f8 = lambda: fq.melded_linear_fwd(m.xq, m.s_x, m.wq, m.s_w, m.y, stream=stream)  # noqa: E731
+    for _ in range(3):
+        f4()
+        f8()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(reps)]
+    torch.cuda.synchronize()
+    for e in ev:
+        e[0].record(stream)
+        f4()
+        e[1].record(stream)
+        e[2].record(stream)
+        f8()
+        e[3].record(stream)
+    torch.cuda.synchronize()
+    us4 = sum(e[0].elapsed_time(e[1]) for e in ev) * 1e3 / reps
+    us8 = sum(e[2].elapsed_time(e[3]) for e in ev) * 1e3 / reps
+    flops = 2.0 * T * d_in * d_out
+    tf4 = flops / (us4 * 1e-6) / 1e12
+    return {"gemm_us": round(us4, 2), "achieved_TFLOPs": round(tf4, 1),
+            "peak_TFLOPs": FP4_PEAK_TFLOPS, "frac": round(tf4 / FP4_PEAK_TFLOPS, 4),
+            "fp8_gemm_us_same_run": round(us8, 2),
+            "fp4_over_fp8_speedup": round(us8 / us4, 3),
+            "shape": f"{T} x {d_out} x {d_in}, operands cast to E2M1 by fp4_quantize"}
 
 
 def copy_reference_gbs(torch, stream, mib=256, reps=5):
