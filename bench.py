@@ -33,6 +33,47 @@ FP8_PEAK_TFLOPS = 5000.0      # MI355X dense FP8 MFMA
 HBM_PEAK_GBS = 8000.0         # MI355X HBM3E
 
 
+class TimingEvent:
+    """A HIP event used only for timing, created with
+    hipEventDisableSystemFence: recording it does not write back and
+    invalidate the caches.  An ordinary timing event does, and in a kernel
+    trace of the step each such record left about 6 us of idle GPU after it
+    and lengthened the kernel that followed.  The timestamps are the same GPU
+    clock; read elapsed times only after a device synchronize."""
+
+    _hip = None
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    def __init__(self):
+        import ctypes
+        if TimingEvent._hip is None:
+            # the HIP runtime torch has loaded (the same shared object)
+            TimingEvent._hip = ctypes.CDLL("libamdhip64.so")
+        self._c = ctypes
+        self.ev = ctypes.c_void_p()
+        rc = self._hip.hipEventCreateWithFlags(ctypes.byref(self.ev),
+                                               ctypes.c_uint(self.DISABLE_SYSTEM_FENCE))
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreateWithFlags failed ({rc})")
+
+    def record(self, stream):
+        rc = self._hip.hipEventRecord(self.ev, self._c.c_void_p(stream.cuda_stream))
+        if rc != 0:
+            raise RuntimeError(f"hipEventRecord failed ({rc})")
+
+    def elapsed_time(self, end) -> float:
+        """Milliseconds from this event to `end`."""
+        ms = self._c.c_float()
+        rc = self._hip.hipEventElapsedTime(self._c.byref(ms), self.ev, end.ev)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return ms.value
+
+    def __del__(self):
+        if self._hip is not None and self.ev:
+            self._hip.hipEventDestroy(self.ev)
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -140,7 +181,7 @@ def main():
     # Per-call durations (reported beside the result, not part of the timed
     # region): HIP events between the calls of a few eager steps.
     n_pc = max(3, min(args.steps, 10), args.merge_every)
-    pc = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
+    pc = [[TimingEvent() for _ in range(len(names) + 1)]
           for _ in range(n_pc)]
     for i in range(n_pc):
         for k, c in enumerate(calls(args.warmup + i)):
@@ -181,12 +222,12 @@ def main():
     # Timed region: K steps, launched eagerly on one stream (back-to-back
     # launches keep the GPU busy: a captured-graph replay of the step measured
     # no faster).  The forward FP8 GEMM, the dominant kernel, is bracketed by
-    # HIP events on the stream it runs on, so its launch duration is measured
-    # in the same region.
-    g_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+    # HIP timing events (without the cache-flushing fence) on the stream it
+    # runs on, so its launch duration is measured in the same region.
+    g_ev = [(TimingEvent(), TimingEvent())
             for _ in range(args.steps)]
-    start = torch.cuda.Event(enable_timing=True)
-    stop = torch.cuda.Event(enable_timing=True)
+    start = TimingEvent()
+    stop = TimingEvent()
     torch.cuda.synchronize()
     start.record(stream)
     for i in range(args.steps):
@@ -300,7 +341,7 @@ def fp4_forward(torch, fq, X, W, m, stream, reps=20):
     for _ in range(3):
         f4()
         f8()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(reps)]
+    ev = [[TimingEvent() for _ in range(4)] for _ in range(reps)]
     torch.cuda.synchronize()
     for e in ev:
         e[0].record(stream)
