@@ -19,6 +19,7 @@ a token sample of the same workload.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import json
 import os
 import sys
@@ -99,6 +100,12 @@ def parse():
     ap.add_argument("--fp4-gemm", action="store_true",
                     help="also time the forward product with FP4 E2M1 operands (X and W cast "
                          "by fp4_quantize) against the FP8 one, alternating launches")
+    ap.add_argument("--workload", choices=["attn7b", "mlp7b", "layer13b", "rank-sweep"],
+                    default="attn7b",
+                    help="attn7b: the 7B attention projection (the headline line); mlp7b: the "
+                         "three 7B MLP linears, 8192 bf16 tokens; layer13b: the seven linears of "
+                         "a 13B decoder layer, 4096 tokens; rank-sweep: 4096 x 4096, 8192 "
+                         "tokens, r in 8 .. 8192 (fwd + bwd time and step time per rank)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB before the timed steps "
                          "(calibrates the HBM byte counters of a profiler run)")
@@ -121,6 +128,14 @@ def main():
 
     fq.load()
     torch.cuda.set_device(0)
+    if args.workload != "attn7b":
+        if args.adapter != "trained" or args.topk_rank or args.grad_format != "e4m3" or \
+                args.merge_every != 1 or args.optimizer != "sgd" or args.fp4_gemm:
+            sys.exit("--workload other than attn7b runs the default step only")
+        out = (rank_sweep(args, torch, fq, wl) if args.workload == "rank-sweep"
+               else layer_workload(args, torch, fq, wl))
+        print(json.dumps(out), flush=True)
+        return
     cfg = wl.WORKLOADS[2]
     spec = cfg.linears[0]
     T, d_in, d_out, r = spec.tokens, spec.d_in, spec.d_out, spec.rank
@@ -318,6 +333,187 @@ def main():
     print(json.dumps(out), flush=True)
 
 
+def _upload(torch, np, a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def _linear_state(torch, np, fq, wl, cfg_id, li, spec, rank=None):
+    """A MeldedLinear initialised from the workload's seeded W, A, B, with the
+    step-0 X (bf16 where the workload passes bf16) and dY resident."""
+    r = spec.rank if rank is None else rank
+    d = wl.make_linear(cfg_id, li, spec, step=0, rank=r)
+    x_dtype = torch.bfloat16 if spec.x_bf16 else torch.float32
+    m = fq.MeldedLinear(spec.d_out, spec.d_in, r, spec.tokens, x_dtype=x_dtype)
+    m.init_state(_upload(torch, np, d["W"]), _upload(torch, np, d["A"]),
+                 _upload(torch, np, d["B"]))
+    if spec.x_bf16:
+        X = _upload(torch, np, d["X_bf16"].view(np.int16)).view(torch.bfloat16)
+    else:
+        X = _upload(torch, np, d["X"])
+    dY = _upload(torch, np, d["dY"])
+    return m, X, dY, d
+
+
+def _step_calls(fq, m, X, dY, spec, stream):
+    """The six boundary calls of one melded-linear step."""
+    return [
+        lambda: fq.fp8_quantize(X, m.xq, m.s_x, ws=m.ws_q, stream=stream),
+        lambda: fq.melded_linear_fwd(m.xq, m.s_x, m.wq, m.s_w, m.y, stream=stream),
+        lambda: fq.fp8_quantize(dY, m.gq, m.s_g, ws=m.ws_q, stream=stream),
+        lambda: fq.melded_linear_bwd(m.gq, m.s_g, m.xq, m.s_x, m.wq, m.s_w, m.A, m.B, m.dx,
+                                     m.dA, m.dB, ws=m.ws_bwd, stream=stream),
+        lambda: m.adapter_update(spec.lr, stream=stream),
+        lambda: m.merge(spec.tau, spec.k_max, stream=stream),
+    ]
+
+
+def _timed(torch, steps, warmup, run_step, stream, gemm=True):
+    """Warm-up, then `steps` steps between two timing events.  `run_step(i,
+    ev)` runs step i; with `gemm`, ev is a pair of timing events the step
+    records around its dominant GEMM (None during warm-up).  Returns (ms per
+    step, GEMM us per launch or None)."""
+    for i in range(warmup):
+        run_step(i, None)
+    torch.cuda.synchronize()
+    g_ev = [(TimingEvent(), TimingEvent()) if gemm else None for _ in range(steps)]
+    start, stop = TimingEvent(), TimingEvent()
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(steps):
+        run_step(warmup + i, g_ev[i])
+    stop.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / steps
+    gemm_us = sum(a.elapsed_time(b) for a, b in g_ev) * 1e3 / steps if gemm else None
+    return ms, gemm_us
+
+
+def _run_calls(calls, ev, stream, gemm_index=1):
+    for k, c in enumerate(calls):
+        if ev is not None and k == gemm_index:
+            ev[0].record(stream)
+            c()
+            ev[1].record(stream)
+        else:
+            c()
+
+
+def layer_workload(args, torch, fq, wl):
+    """The 7B MLP (three linears, 8192 bf16 tokens) or the 13B decoder layer
+    (seven linears, 4096 tokens): one step runs every linear's step in turn,
+    each with its own seeded state, X and dY.  The dominant kernel is the
+    forward GEMM of the first linear (the largest shape of both layers)."""
+    import numpy as np
+    cfg_id = 3 if args.workload == "mlp7b" else 4
+    cfg = wl.WORKLOADS[cfg_id]
+    stream = torch.cuda.current_stream()
+    layers = []
+    for li, spec in enumerate(cfg.linears):
+        m, X, dY, d = _linear_state(torch, np, fq, wl, cfg_id, li, spec)
+        layers.append((m, X, dY, spec))
+        if li == 0:
+            d0 = d
+        del d
+    torch.cuda.synchronize()
+
+    def run_step(i, ev):
+        for li, (m, X, dY, spec) in enumerate(layers):
+            _run_calls(_step_calls(fq, m, X, dY, spec, stream), ev if li == 0 else None, stream)
+
+    ms, gemm_us = _timed(torch, args.steps, args.warmup, run_step, stream)
+    flops = sum(wl.step_flops(sp.tokens, sp.d_in, sp.d_out, sp.rank) for _, _, _, sp in layers)
+    s0 = layers[0][3]
+    T = s0.tokens
+    gemm_flops = 2 * T * s0.d_in * s0.d_out
+    gemm_tf = gemm_flops / (gemm_us * 1e-6) / 1e12
+    shapes = ", ".join(f"{sp.name} {sp.d_out}x{sp.d_in}" for _, _, _, sp in layers)
+    out = {
+        "metric": METRIC, "value": round(flops / (ms * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "fp8e4m3",
+        "data": "synthetic",
+        "config": {"workload": ("7B MLP" if cfg_id == 3 else "13B decoder layer")
+                   + f" ({shapes}; W E4M3), {T} tokens"
+                   + (" of bf16 activations" if s0.x_bf16 else "")
+                   + ", rank 64, SGD lr 1e-3, proxy update every step; one step runs every "
+                     "linear once; the same X and dY every step",
+                   "tokens": T, "linears": len(layers), "rank": s0.rank,
+                   "parallelism": "single GPU"},
+        "tokens_per_s": round(T / (ms * 1e-3), 1),
+        "roofline": {"kernel": f"melded_linear_fwd FP8 GEMM ({T} x {s0.d_out} x {s0.d_in}, "
+                               f"{s0.name})",
+                     "bound": "mfma", "achieved": round(gemm_tf, 1), "peak": FP8_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(gemm_tf / FP8_PEAK_TFLOPS, 4),
+                     "traffic": None},
+        "launch": "eager launches on one HIP stream",
+    }
+    if not args.no_cpu_baseline and args.cpu_tokens > 0:
+        out["cpu_baseline"] = cpu_baseline(s0, d0, min(args.cpu_tokens, 512),
+                                           x_note=" (bf16 activations widened exactly)"
+                                           if s0.x_bf16 else "")
+    return out
+
+
+def rank_sweep(args, torch, fq, wl):
+    """W 4096 x 4096, 8192 tokens, r in 8, 64, 512, 2048, 8192: per rank the
+    forward + backward time (quantize X, forward, quantize dY, backward) and
+    the whole step's (plus SGD and the proxy update), each timed over its own
+    eager steps.  The line's value is the step TFLOP/s at r = 64."""
+    import numpy as np
+    cfg = wl.WORKLOADS[5]
+    spec0 = cfg.linears[0]
+    stream = torch.cuda.current_stream()
+    points = []
+    line = None
+    for r in wl.RANK_SWEEP:
+        m, X, dY, d = _linear_state(torch, np, fq, wl, 5, 0, spec0, rank=r)
+        spec = dataclasses.replace(spec0, rank=r)
+        calls = _step_calls(fq, m, X, dY, spec, stream)
+        fb_ms, _ = _timed(torch, args.steps, args.warmup,
+                          lambda i, ev: _run_calls(calls[:4], None, stream), stream, gemm=False)
+        ms, gemm_us = _timed(torch, args.steps, args.warmup,
+                             lambda i, ev: _run_calls(calls, ev, stream), stream)
+        T = spec.tokens
+        fb_flops = 4 * T * spec.d_in * spec.d_out + 4 * T * r * (spec.d_in + spec.d_out)
+        flops = wl.step_flops(T, spec.d_in, spec.d_out, r)
+        n_sel = int(m.n_sel.cpu()[0])
+        points.append({"rank": r, "fwd_bwd_ms": round(fb_ms, 4), "step_ms": round(ms, 4),
+                       "fwd_bwd_TFLOPs": round(fb_flops / (fb_ms * 1e-3) / 1e12, 1),
+                       "step_TFLOPs": round(flops / (ms * 1e-3) / 1e12, 1),
+                       "fwd_gemm_us": round(gemm_us, 2),
+                       "selected_rows_last_step": n_sel})
+        if r == 64:
+            line = (ms, gemm_us, d, spec)
+        del m, X, dY, d, calls
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+    ms, gemm_us, d64, spec64 = line
+    T = spec64.tokens
+    gemm_tf = 2 * T * spec64.d_in * spec64.d_out / (gemm_us * 1e-6) / 1e12
+    out = {
+        "metric": METRIC,
+        "value": round(wl.step_flops(T, spec64.d_in, spec64.d_out, 64) / (ms * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "fp8e4m3", "data": "synthetic",
+        "config": {"workload": "rank sweep: W 4096x4096 E4M3, 8192 tokens, A std 1/sqrt(r), "
+                               "B std 1e-3, SGD lr 1e-3, proxy update every step; the "
+                               "line's value and ms_per_step are the r = 64 point",
+                   "tokens": T, "d_in": spec64.d_in, "d_out": spec64.d_out,
+                   "ranks": list(wl.RANK_SWEEP), "parallelism": "single GPU"},
+        "tokens_per_s": round(T / (ms * 1e-3), 1),
+        "roofline": {"kernel": f"melded_linear_fwd FP8 GEMM ({T} x 4096 x 4096), r = 64 point",
+                     "bound": "mfma", "achieved": round(gemm_tf, 1), "peak": FP8_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(gemm_tf / FP8_PEAK_TFLOPS, 4),
+                     "traffic": None},
+        "sweep": points,
+        "launch": "eager launches on one HIP stream",
+    }
+    if not args.no_cpu_baseline and args.cpu_tokens > 0:
+        out["cpu_baseline"] = cpu_baseline(spec64, d64, min(args.cpu_tokens, 1024))
+    return out
+
+
 FP4_PEAK_TFLOPS = 10100.0     # MI355X dense FP4 matrix peak
 
 
@@ -428,11 +624,11 @@ def gemm_traffic_bytes():
         return None
 
 
-def cpu_baseline(spec, d0, Ts, optimizer="sgd", frozen=False, g_fmt="e4m3"):
+def cpu_baseline(spec, d0, Ts, optimizer="sgd", frozen=False, g_fmt="e4m3", x_note=""):
     """The CPU oracle, as it is, on a token sample of the same workload:
     quantize X and dY, forward, backward (dX, dA, dB; or with A frozen in FP8,
     X~A~^T in the forward and dX, dB), the adapter step (SGD or AdamW) and
-    the proxy update over the full 4096 x 4096 backbone."""
+    the proxy update over the full backbone."""
     import numpy as np
 
     import oracle
@@ -475,7 +671,8 @@ def cpu_baseline(spec, d0, Ts, optimizer="sgd", frozen=False, g_fmt="e4m3"):
     return {"value": round(flops / step_s / 1e12, 5), "unit": "TFLOP/s", "cores": int(max(
         blas_threads, oracle.num_threads())), "kind": "oracle",
         "tokens_per_s": round(Ts / step_s, 1),
-        "sample": f"one step on the first {Ts} of 4096 tokens (full 4096 x 4096 weight, r=64, "
+        "sample": f"one step on the first {Ts} of {spec.tokens} tokens{x_note} (full "
+                  f"{spec.d_out} x {spec.d_in} weight, r={spec.rank}, "
                   f"full proxy update), {step_s:.1f} s; the initial quantization of W"
                   f"{' and A' if frozen else ''} ({t1 - t0:.1f} s) is not part of the step"}
 

@@ -9,6 +9,12 @@
 //
 // Two kernels.  K a multiple of 128 (every shape of the workloads) takes the
 // direct-to-LDS kernel described in gemm_fp8_kernel.hpp (namespace dma).
+// One 256 x 256 tile occupies a CU, so a tile count just past a multiple of
+// the CU count leaves most CUs idle in the last round (4096 x 5120 outputs:
+// 320 tiles, 64 in the second round of 256).  When the last round holds at
+// most half the CUs and K is long, its tiles are split into two K halves,
+// one workgroup each, in a second launch; the halves add into C (zeroed
+// first by zero_tiles_kernel).
 // Other K take the general kernel below:
 //  * workgroup tile BM x BN x BK = 256 x 256 x 128 bytes, 4 waves in 2 x 2,
 //    each wave a 128 x 128 sub-tile of 4 x 4 blocks of
@@ -66,6 +72,64 @@ __global__ __launch_bounds__(256) void transpose_u8_kernel(const uint8_t* __rest
     *reinterpret_cast<uint4*>(out + (c + k) * rows + r) = make_uint4(o[k][0], o[k][1], o[k][2], o[k][3]);
 }
 
+// zero the C blocks of logical tiles [first, first + count): block b clears
+// 16 rows of tile first + b / 16, one 1 KB row segment per 256 threads
+__global__ __launch_bounds__(256) void zero_tiles_kernel(float* __restrict__ C, int64_t ldc, int M,
+                                                         int N, int tilesM, int tilesN, int first) {
+  int tm, tn;
+  gemm::tile_of(first + (int)blockIdx.x / 16, tilesM, tilesN, tm, tn);
+  const int col = tn * gemm::dma::BN + (int)threadIdx.x;
+  const int r0 = tm * gemm::dma::BM + ((int)blockIdx.x % 16) * 16;
+  if (col >= N) return;
+#pragma unroll 4
+  for (int r = r0; r < r0 + 16 && r < M; ++r) C[(int64_t)r * ldc + col] = 0.0f;
+}
+
+// Number of workgroups that take whole tiles: all nt tiles, or, when the last
+// round (nt mod CUs tiles) fills at most half the CUs and K has at least 64
+// steps of 128, the tiles before that round.  With shorter K the zero fill
+// and the atomic adds cost what the split saves (measured: 4096 x 5120 x 5120
+// and 8192 x 11008 x 4096 take the same time either way; 4096 x 5120 x 13824
+// 244 us split, 283 us whole).
+int whole_tiles(int nt, int nk) {
+  int dev = 0, ncu = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      ncu <= 0)
+    return nt;
+  const int rem = nt % ncu;
+  if (rem == 0 || 2 * rem > ncu || nk < 64) return nt;
+  return nt - rem;
+}
+
+// the direct-to-LDS kernel over tM x tN tiles, with the last round split
+template <int FA>
+hipError_t launch_dma(const uint8_t* A, int64_t lda, const uint8_t* B, int64_t ldb, float* C,
+                      int64_t ldc, int64_t M, int64_t N, int64_t K, const float* sa,
+                      const float* sb, hipStream_t s) {
+  const int tM = (int)((M + gemm::dma::BM - 1) / gemm::dma::BM);
+  const int tN = (int)((N + gemm::dma::BN - 1) / gemm::dma::BN);
+  const int nt = tM * tN;
+  const int full = whole_tiles(nt, (int)(K / gemm::dma::BK));
+  if (full < nt) {
+    zero_tiles_kernel<<<(nt - full) * 16, 256, 0, s>>>(C, ldc, (int)M, (int)N, tM, tN, full);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (full > 0) {
+    gemm::dma::gemm_fp8_nt_dma<false, FA><<<full, gemm::dma::kThreads, 0, s>>>(
+        A, lda, B, ldb, C, ldc, (int)M, (int)N, (int)K, sa, sb, tM, tN, full,
+        gemm::dma::SecondB{});
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (full < nt)
+    gemm::dma::gemm_fp8_nt_dma<false, FA, true><<<2 * (nt - full), gemm::dma::kThreads, 0, s>>>(
+        A, lda, B, ldb, C, ldc, (int)M, (int)N, (int)K, sa, sb, tM, tN, full,
+        gemm::dma::SecondB{});
+  return hipGetLastError();
+}
+
 }  // namespace
 
 namespace {
@@ -73,13 +137,7 @@ template <int FA>
 hipError_t gemm_nt(const uint8_t* A, int64_t lda, const uint8_t* B, int64_t ldb, float* C,
                    int64_t ldc, int64_t M, int64_t N, int64_t K, const float* sa, const float* sb,
                    hipStream_t s) {
-  if (K % gemm::dma::BK == 0) {
-    const int tM = (int)((M + gemm::dma::BM - 1) / gemm::dma::BM);
-    const int tN = (int)((N + gemm::dma::BN - 1) / gemm::dma::BN);
-    gemm::dma::gemm_fp8_nt_dma<false, FA><<<tM * tN, gemm::dma::kThreads, 0, s>>>(
-        A, lda, B, ldb, C, ldc, (int)M, (int)N, (int)K, sa, sb, tM, tN, gemm::dma::SecondB{});
-    return hipGetLastError();
-  }
+  if (K % gemm::dma::BK == 0) return launch_dma<FA>(A, lda, B, ldb, C, ldc, M, N, K, sa, sb, s);
   using Cf = gemm::Cfg<256, 256, 128, 2, 2>;
   const int tilesM = (int)((M + Cf::BM - 1) / Cf::BM);
   const int tilesN = (int)((N + Cf::BN - 1) / Cf::BN);
@@ -102,11 +160,7 @@ hipError_t launch_gemm_fp4_nt(const uint8_t* A, int64_t lda, const uint8_t* B, i
                               const float* sa, const float* sb, hipStream_t s) {
   if (M == 0 || N == 0) return hipSuccess;
   if (Kb <= 0 || Kb % gemm::dma::BK != 0) return hipErrorInvalidValue;
-  const int tM = (int)((M + gemm::dma::BM - 1) / gemm::dma::BM);
-  const int tN = (int)((N + gemm::dma::BN - 1) / gemm::dma::BN);
-  gemm::dma::gemm_fp8_nt_dma<false, 4><<<tM * tN, gemm::dma::kThreads, 0, s>>>(
-      A, lda, B, ldb, C, ldc, (int)M, (int)N, (int)Kb, sa, sb, tM, tN, gemm::dma::SecondB{});
-  return hipGetLastError();
+  return launch_dma<4>(A, lda, B, ldb, C, ldc, M, N, Kb, sa, sb, s);
 }
 
 bool gemm_fp8_nt_fuses_second(int64_t N, int64_t K, int64_t R) {
@@ -125,7 +179,7 @@ hipError_t launch_gemm_fp8_nt_second(const uint8_t* A, int64_t lda, const uint8_
   const int tM = (int)((M + gemm::dma::BM - 1) / gemm::dma::BM);
   const int tN = (int)((N + gemm::dma::BN - 1) / gemm::dma::BN);
   gemm::dma::gemm_fp8_nt_dma<true, 0><<<tM * tN, gemm::dma::kThreads, 0, s>>>(
-      A, lda, B, ldb, C, ldc, (int)M, (int)N, (int)K, sa, sb, tM, tN,
+      A, lda, B, ldb, C, ldc, (int)M, (int)N, (int)K, sa, sb, tM, tN, tM * tN,
       gemm::dma::SecondB{Bu, ldbu, (int)R, Cu, ldcu, sbu});
   return hipGetLastError();
 }

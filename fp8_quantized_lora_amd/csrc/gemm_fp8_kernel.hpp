@@ -29,12 +29,10 @@ __device__ __forceinline__ v8i join(uint4 lo, uint4 hi) {
   return r;
 }
 
-__device__ __forceinline__ void tile_coords(int tilesM, int tilesN, int& tm, int& tn) {
-  const int nt = tilesM * tilesN;
-  const int bid = blockIdx.x;
-  const int per = nt / 8;
-  int logical = bid;
-  if (bid < per * 8) logical = (bid % 8) * per + bid / 8;   // 8 XCDs, round-robin dispatch
+// Logical tile order: groups of G tile rows, column by column inside a group,
+// so that a run of consecutive logical tiles shares few A rows and B columns.
+__host__ __device__ __forceinline__ void tile_of(int logical, int tilesM, int tilesN, int& tm,
+                                                 int& tn) {
   constexpr int G = 8;                                       // tile rows per group
   const int gsz = G * tilesN;
   const int g = logical / gsz;
@@ -43,6 +41,18 @@ __device__ __forceinline__ void tile_coords(int tilesM, int tilesN, int& tm, int
   const int rem = logical - g * gsz;
   tm = first + rem % gm;
   tn = rem / gm;
+}
+
+// The dispatcher deals consecutive workgroup ids round-robin to the 8 XCDs;
+// of the first n ids, each XCD gets a contiguous run of logical ids (ids past
+// the last multiple of 8 keep their own).
+__device__ __forceinline__ int xcd_remap(int bid, int n) {
+  const int per = n / 8;
+  return bid < per * 8 ? (bid % 8) * per + bid / 8 : bid;
+}
+
+__device__ __forceinline__ void tile_coords(int tilesM, int tilesN, int& tm, int& tn) {
+  tile_of(xcd_remap(blockIdx.x, tilesM * tilesN), tilesM, tilesN, tm, tn);
 }
 
 // FA: format of the A codes (0 = E4M3, 1 = E5M2: the MFMA's A-format field);
@@ -211,16 +221,30 @@ struct SecondB {
 };
 
 // FA: format of the A codes (0 = E4M3, 1 = E5M2; B and the second B are
-// E4M3), or 4: both operands FP4 E2M1, two codes per byte (K counts bytes)
-template <bool FU, int FA>
+// E4M3), or 4: both operands FP4 E2M1, two codes per byte (K counts bytes).
+// HALF = false: workgroup b takes the whole logical tile xcd_remap(b, tiles)
+// (tiles = the number of workgroups).  HALF = true: workgroups 2j and 2j + 1
+// take the two K halves of logical tile first + j and add them into C with
+// float atomics (C zeroed beforehand): exactly two addends meet a zero per
+// element, and the sum of two floats does not depend on their order, so the
+// result is the same on every run.
+template <bool FU, int FA, bool HALF = false>
 __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_nt_dma(
     const uint8_t* __restrict__ A, int64_t lda, const uint8_t* __restrict__ B, int64_t ldb,
     float* __restrict__ C, int64_t ldc, int M, int N, int K, const float* __restrict__ sa,
-    const float* __restrict__ sb, int tilesM, int tilesN, SecondB u) {
+    const float* __restrict__ sb, int tilesM, int tilesN, int tiles_or_first, SecondB u) {
+  static_assert(!(FU && HALF), "the second product is not split");
   constexpr int SB = FU ? STAGE_U : STAGE;                 // bytes per LDS stage
   __shared__ __attribute__((aligned(1024))) uint8_t smem[S * SB];
-  int tm, tn;
-  tile_coords(tilesM, tilesN, tm, tn);
+  int tm, tn, k_lo = 0, nk = K / BK;
+  if constexpr (HALF) {
+    const int j = blockIdx.x, h = j & 1;
+    tile_of(tiles_or_first + (j >> 1), tilesM, tilesN, tm, tn);
+    k_lo = h ? nk / 2 : 0;
+    nk = h ? nk - nk / 2 : nk / 2;
+  } else {
+    tile_of(xcd_remap(blockIdx.x, tiles_or_first), tilesM, tilesN, tm, tn);
+  }
   const int m0 = tm * BM, n0 = tn * BN;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, wm = w / WGN, wn = w % WGN;
   // second product: this tile's unit (block ub, quarter uq), if any
@@ -246,19 +270,20 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_nt_dma(
 #pragma unroll
   for (int j = 0; j < AI; ++j) {
     const int row = (w * AI + j) * 8 + lrow;
-    gA[j] = A + (int64_t)min(m0 + row, M - 1) * lda + ((lslot ^ swz(row)) * 16);
+    gA[j] = A + (int64_t)min(m0 + row, M - 1) * lda + k_lo * BK + ((lslot ^ swz(row)) * 16);
   }
 #pragma unroll
   for (int j = 0; j < BI; ++j) {
     const int row = (w * BI + j) * 8 + lrow;
-    gB[j] = B + (int64_t)min(n0 + row, N - 1) * ldb + ((lslot ^ swz(row)) * 16);
+    gB[j] = B + (int64_t)min(n0 + row, N - 1) * ldb + k_lo * BK + ((lslot ^ swz(row)) * 16);
   }
   // the 16 rank rows of the unit's block: waves 0 and 1 load 8 rows each
   const bool load_u = __builtin_amdgcn_readfirstlane((int)(has_u && w < 2)) != 0;
   const uint8_t* gU = nullptr;
   if (FU && load_u) {
     const int row = w * 8 + lrow;
-    gU = u.B + (int64_t)min(ub * UR + row, u.R - 1) * u.ldb + ((lslot ^ swz(row)) * 16);
+    gU = u.B + (int64_t)min(ub * UR + row, u.R - 1) * u.ldb + k_lo * BK +
+         ((lslot ^ swz(row)) * 16);
   }
   auto issue = [&](int stage, int k0) {
     const uint32_t base = lds_offset(smem + stage * SB);
@@ -272,7 +297,6 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_nt_dma(
       load16_to_lds(gU + k0, __builtin_amdgcn_readfirstlane(base + (BM + BN) * BK + w * 1024));
   };
 
-  const int nk = K / BK;
 #pragma unroll
   for (int s = 0; s < S - 1; ++s)
     if (s < nk) issue(s, s * BK);
@@ -355,7 +379,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_nt_dma(
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const int row = rbase + i * 16 + v;
-        if (row < M) C[(int64_t)row * ldc + col] = acc[i][j][v] * scale;
+        if (row >= M) continue;
+        if constexpr (HALF)
+          unsafeAtomicAdd(C + (int64_t)row * ldc + col, acc[i][j][v] * scale);
+        else
+          C[(int64_t)row * ldc + col] = acc[i][j][v] * scale;
       }
     }
   if (FU && wave_u) {

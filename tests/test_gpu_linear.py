@@ -172,3 +172,35 @@ def test_backward_is_deterministic(gpu_lib):
     b = gpu_bwd(gpu_lib, p)
     for u, v in zip(a, b):
         assert np.array_equal(u.view(np.uint32), v.view(np.uint32))
+
+
+def test_split_last_round_parity_and_determinism(gpu_lib):
+    """A tile count just past the CU count (16 x 17 = 272 tiles of 256 x 256
+    on 256 CUs) with a long K (8192 = 64 steps): the 16 tiles of the last
+    round run as two K halves added into a zeroed output.  Y in full against
+    the oracle, bitwise equal over two runs.  Then a dX product whose four
+    tiles are all split, with an odd number of K steps (8320 = 65: halves of
+    32 and 33).  Outputs are NaN-filled beforehand, so an element left
+    unwritten shows."""
+    announce("fwd 4096 x 8192 -> 4352 (split last round), full Y")
+    p = quantized_problem(21, 4096, 8192, 4352, 1)
+    T, d_out = 4096, 4352
+
+    def fwd():
+        y = torch.full((T, d_out), np.nan, dtype=torch.float32, device="cuda")
+        gpu_lib.melded_linear_fwd(dev(p["xq"]), scalar(p["s_x"]), dev(p["wq"]),
+                                  scalar(p["s_w"]), y)
+        return host(y)
+    y1, y2 = fwd(), fwd()
+    ry = oracle.melded_linear_fwd(p["xq"], p["s_x"], p["wq"], p["s_w"])
+    assert np.isfinite(y1).all() and rel_l2(y1, ry) <= TOL
+    assert np.array_equal(y1.view(np.uint32), y2.view(np.uint32))
+    del p
+    announce("bwd 256 x 8320 -> 1024 (every dX tile split, odd K steps)")
+    q = quantized_problem(22, 256, 1024, 8320, 3)
+    dx1, _, dB1 = gpu_bwd(gpu_lib, q, want_da=False)
+    dx2, _, _ = gpu_bwd(gpu_lib, q, want_da=False)
+    rdx, _, rdB = oracle.melded_linear_bwd(q["gq"], q["s_g"], q["xq"], q["s_x"], q["wq"],
+                                           q["s_w"], q["A"], q["B"], want_da=False)
+    assert np.isfinite(dx1).all() and rel_l2(dx1, rdx) <= TOL and rel_l2(dB1, rdB) <= TOL
+    assert np.array_equal(dx1.view(np.uint32), dx2.view(np.uint32))
