@@ -48,6 +48,11 @@
  *   - FP8 is OCP E4M3 ("e4m3fn": bias 7, max 448, no infinities, NaN 0x7F /
  *     0xFF).  Casts round to nearest even and saturate to +-448.
  *   - Output floats are fp32; products of FP8 values accumulate in fp32.
+ *     The GEMM outputs (Y, dX) must be ordinary device memory (hipMalloc):
+ *     on shapes whose last round of 256 x 256 tiles is split into two K
+ *     halves, those tiles are summed with device float atomics, which
+ *     fine-grained (host-coherent) memory does not support.  Results are
+ *     bitwise the same on every run either way.
  */
 #ifndef FALQON_H
 #define FALQON_H
