@@ -6,7 +6,9 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
+#include <cstdint>
 
 namespace {
 
@@ -22,6 +24,15 @@ inline bool opt(const void* p) { return p == nullptr || aligned(p, 16); }
 inline bool scalar(const void* p) { return p != nullptr && aligned(p, 4); }
 
 inline bool dims_ok(int64_t d) { return d >= 0 && d % 16 == 0 && d <= (int64_t)1 << 30; }
+
+// T, d_in, d_out of a melded linear layer: the GEMMs (T x d_out and T x d_in
+// outputs) launch one workgroup per 256 x 256 tile, two per split tile, on a
+// 32-bit grid
+inline bool gemm_dims_ok(int64_t T, int64_t d_in, int64_t d_out) {
+  if (T < 0 || T > ((int64_t)1 << 30) || !dims_ok(d_in) || !dims_ok(d_out)) return false;
+  const int64_t tiles = ((T + 255) / 256) * ((std::max(d_in, d_out) + 255) / 256);
+  return 2 * tiles <= INT32_MAX;
+}
 
 inline falq_status hip_status(hipError_t e) { return e == hipSuccess ? FALQ_OK : FALQ_EHIP; }
 
@@ -102,7 +113,7 @@ falq_status fp4_quantize(const void* x, int dtype, int64_t n, const float* scale
 falq_status melded_linear_fwd_fp4(const uint8_t* xq, const float* s_x, const uint8_t* wq,
                                   const float* s_w, int64_t T, int64_t d_in, int64_t d_out,
                                   float* y, falq_stream stream) {
-  if (T < 0 || T > ((int64_t)1 << 30) || !dims_ok(d_in) || d_in % 256 != 0 || !dims_ok(d_out))
+  if (!gemm_dims_ok(T, d_in, d_out) || d_in % 256 != 0)
     return FALQ_EINVAL;
   if (!scalar(s_x) || !scalar(s_w)) return FALQ_EINVAL;
   if (T * d_in > 0 && !need(xq)) return FALQ_EINVAL;
@@ -118,7 +129,7 @@ falq_status melded_linear_fwd_fp4(const uint8_t* xq, const float* s_x, const uin
 falq_status melded_linear_fwd(const uint8_t* xq, const float* s_x, const uint8_t* wq,
                               const float* s_w, int64_t T, int64_t d_in, int64_t d_out, float* y,
                               falq_stream stream) {
-  if (T < 0 || T > ((int64_t)1 << 30) || !dims_ok(d_in) || !dims_ok(d_out)) return FALQ_EINVAL;
+  if (!gemm_dims_ok(T, d_in, d_out)) return FALQ_EINVAL;
   if (!scalar(s_x) || !scalar(s_w)) return FALQ_EINVAL;
   if (T * d_in > 0 && !need(xq)) return FALQ_EINVAL;
   if (d_out * d_in > 0 && !need(wq)) return FALQ_EINVAL;
@@ -151,7 +162,7 @@ falq_status melded_linear_bwd_fmt(const uint8_t* gq, int g_fmt, const float* s_g
                                   int64_t d_in, int64_t d_out, int64_t r, float* dx, float* dA,
                                   float* dB, void* ws, size_t ws_bytes, falq_stream stream) {
   if (!fmt_ok(g_fmt)) return FALQ_EINVAL;
-  if (T < 0 || T > ((int64_t)1 << 30) || !dims_ok(d_in) || !dims_ok(d_out) || r < 0 ||
+  if (!gemm_dims_ok(T, d_in, d_out) || r < 0 ||
       r > ((int64_t)1 << 20))
     return FALQ_EINVAL;
   if (!scalar(s_g) || !scalar(s_x) || !scalar(s_w)) return FALQ_EINVAL;
@@ -199,7 +210,7 @@ falq_status melded_linear_fwd_frozen_a(const uint8_t* xq, const float* s_x, cons
                                        int64_t T, int64_t d_in, int64_t d_out, int64_t r,
                                        float* y, float* u, void* ws, size_t ws_bytes,
                                        falq_stream stream) {
-  if (T < 0 || T > ((int64_t)1 << 30) || !dims_ok(d_in) || !dims_ok(d_out) || r < 0 ||
+  if (!gemm_dims_ok(T, d_in, d_out) || r < 0 ||
       r > ((int64_t)1 << 20))
     return FALQ_EINVAL;
   if (!scalar(s_a)) return FALQ_EINVAL;
@@ -240,7 +251,7 @@ falq_status melded_linear_bwd_frozen_a_fmt(const uint8_t* gq, int g_fmt, const f
                                            float* dx, float* dB, void* ws, size_t ws_bytes,
                                            falq_stream stream) {
   if (!fmt_ok(g_fmt)) return FALQ_EINVAL;
-  if (T < 0 || T > ((int64_t)1 << 30) || !dims_ok(d_in) || !dims_ok(d_out) || r < 0 ||
+  if (!gemm_dims_ok(T, d_in, d_out) || r < 0 ||
       r > ((int64_t)1 << 20))
     return FALQ_EINVAL;
   if (!scalar(s_g) || !scalar(s_w)) return FALQ_EINVAL;

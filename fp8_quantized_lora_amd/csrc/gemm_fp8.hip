@@ -34,6 +34,7 @@
 // slice; B is loaded the same way, so whatever order the matrix core pairs K
 // elements in, both operands present the same K index in the same slot.
 #include "common.hpp"
+#include <cstdint>
 #include "gemm_fp8_kernel.hpp"
 #include "kernels.hpp"
 
@@ -147,10 +148,18 @@ hipError_t gemm_nt(const uint8_t* A, int64_t lda, const uint8_t* B, int64_t ldb,
 }
 }  // namespace
 
+// the kernels index tiles, rows and K with 32-bit ints and launch one
+// workgroup per tile (or two per split tile) on a 1-D grid
+static bool gemm_shape_ok(int64_t M, int64_t N, int64_t K) {
+  const int64_t tiles = ((M + 255) / 256) * ((N + 255) / 256);
+  return M <= INT32_MAX && N <= INT32_MAX && K <= INT32_MAX && 2 * tiles <= INT32_MAX;
+}
+
 hipError_t launch_gemm_fp8_nt(const uint8_t* A, int64_t lda, const uint8_t* B, int64_t ldb,
                               float* C, int64_t ldc, int64_t M, int64_t N, int64_t K,
                               const float* sa, const float* sb, hipStream_t s, int a_fmt) {
   if (M == 0 || N == 0) return hipSuccess;
+  if (!gemm_shape_ok(M, N, K)) return hipErrorInvalidValue;
   return a_fmt == 0 ? gemm_nt<0>(A, lda, B, ldb, C, ldc, M, N, K, sa, sb, s)
                     : gemm_nt<1>(A, lda, B, ldb, C, ldc, M, N, K, sa, sb, s);
 }
@@ -159,7 +168,7 @@ hipError_t launch_gemm_fp4_nt(const uint8_t* A, int64_t lda, const uint8_t* B, i
                               float* C, int64_t ldc, int64_t M, int64_t N, int64_t Kb,
                               const float* sa, const float* sb, hipStream_t s) {
   if (M == 0 || N == 0) return hipSuccess;
-  if (Kb <= 0 || Kb % gemm::dma::BK != 0) return hipErrorInvalidValue;
+  if (Kb <= 0 || Kb % gemm::dma::BK != 0 || !gemm_shape_ok(M, N, Kb)) return hipErrorInvalidValue;
   return launch_dma<4>(A, lda, B, ldb, C, ldc, M, N, Kb, sa, sb, s);
 }
 
@@ -175,7 +184,7 @@ hipError_t launch_gemm_fp8_nt_second(const uint8_t* A, int64_t lda, const uint8_
                                      int64_t ldbu, int64_t R, float* Cu, int64_t ldcu,
                                      const float* sbu, hipStream_t s) {
   if (M == 0) return hipSuccess;
-  if (!gemm_fp8_nt_fuses_second(N, K, R)) return hipErrorInvalidValue;
+  if (!gemm_fp8_nt_fuses_second(N, K, R) || !gemm_shape_ok(M, N, K)) return hipErrorInvalidValue;
   const int tM = (int)((M + gemm::dma::BM - 1) / gemm::dma::BM);
   const int tN = (int)((N + gemm::dma::BN - 1) / gemm::dma::BN);
   gemm::dma::gemm_fp8_nt_dma<true, 0><<<tM * tN, gemm::dma::kThreads, 0, s>>>(

@@ -83,6 +83,8 @@ def test_linear_rejects_bad_arguments():
     assert lib.melded_linear_fwd(P, P, P, P, -1, 32, 32, P, None) == EINVAL
     assert lib.melded_linear_fwd(P, None, P, P, 8, 32, 32, P, None) == EINVAL             # s_x
     assert lib.melded_linear_fwd(P, P, P, P, 8, 32, 32, None, None) == EINVAL             # y
+    # more 256 x 256 output tiles than a 32-bit grid holds
+    assert lib.melded_linear_fwd(P, P, P, P, 1 << 30, 32, 1 << 30, P, None) == EINVAL
     ws = fq.melded_linear_bwd_workspace_bytes(8, 32, 32, 4)
     args = [P, P, P, P, P, P, P, P, 8, 32, 32, 4, P, P, P, P, ws, None]
     bad_r = list(args); bad_r[11] = -1
