@@ -26,6 +26,7 @@
 // U and V are T x r: a few MiB, consumed at once, cache resident.
 #include "common.hpp"
 #include "kernels.hpp"
+#include "transpose_u8.hpp"
 
 #include <algorithm>
 
@@ -339,11 +340,9 @@ struct Split {
   int tx, ty;          // tiles along cols, rows
 };
 
-__global__ __launch_bounds__(256) void split_bf16_kernel(Split p0, Split p1) {
-  const Split p = blockIdx.z == 0 ? p0 : p1;
-  if ((int)blockIdx.x >= p.tx * p.ty) return;
-  __shared__ float t[32][33];
-  const int r0 = ((int)blockIdx.x / p.tx) * 32, c0 = ((int)blockIdx.x % p.tx) * 32;
+// one 32 x 32 tile of a Split (256 threads; t: 32 x 33 floats of LDS)
+__device__ __forceinline__ void split_tile(const Split& p, int tile, float (*t)[33]) {
+  const int r0 = (tile / p.tx) * 32, c0 = (tile % p.tx) * 32;
   const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;   // 32 x 8
   if (!p.transpose) {
     for (int rr = ty; rr < 32; rr += 8) {
@@ -371,6 +370,34 @@ __global__ __launch_bounds__(256) void split_bf16_kernel(Split p0, Split p1) {
       p.lo[(int64_t)c * p.ld_out + r] = bf16_rne(x - bf16_to_f32(h));
     }
   }
+}
+
+__global__ __launch_bounds__(256) void split_bf16_kernel(Split p0, Split p1) {
+  const Split p = blockIdx.z == 0 ? p0 : p1;
+  if ((int)blockIdx.x >= p.tx * p.ty) return;
+  __shared__ float t[32][33];
+  split_tile(p, (int)blockIdx.x, t);
+}
+
+// The backward's preparation in one launch (each part alone is too small to
+// fill the GPU, and every launch costs a few microseconds of ramp): workgroups
+// [0, n_tr) transpose W~ for the dX product (128 x 128 tiles, tr_tx per tile
+// row), the next sa.tx * sa.ty split A, the rest split B (transposed).
+__global__ __launch_bounds__(256) void bwd_prep_kernel(const uint8_t* __restrict__ wq,
+                                                       int64_t d_out, int64_t d_in,
+                                                       uint8_t* __restrict__ wt, int n_tr,
+                                                       int tr_tx, Split sa, Split sb) {
+  __shared__ float t[32][33];
+  const int b = blockIdx.x;
+  if (b < n_tr) {
+    transpose_u8_tile(wq, d_out, d_in, wt, b % tr_tx, b / tr_tx);
+    return;
+  }
+  const int na = sa.tx * sa.ty;
+  if (b - n_tr < na)
+    split_tile(sa, b - n_tr, t);
+  else
+    split_tile(sb, b - n_tr - na, t);
 }
 
 // out = sum_s P[s] / (*sc * *sc2) with P[s] of shape [M x N] (a null sc or
@@ -672,10 +699,43 @@ hipError_t launch_fill_f32(float* p, int64_t n, float v, hipStream_t s) {
   return hipGetLastError();
 }
 
+// the two float-operand splits of the adapter gradients (A as is; B
+// transposed, only when dA is wanted)
+namespace {
+void make_splits(const Plan& pl, uint8_t* base, const float* A, const float* B, int64_t d_in,
+                 int64_t d_out, int64_t r, Split& sa, Split& sb) {
+  auto u16 = [&](size_t off) { return reinterpret_cast<uint16_t*>(base + off); };
+  sa = Split{A, (int)r, (int)d_in, false, d_in, u16(pl.off_ahi), u16(pl.off_alo),
+             ceil_div(d_in, 32), ceil_div(r, 32)};
+  sb = Split{B, (int)d_out, (int)r, true, d_out, u16(pl.off_bhi), u16(pl.off_blo),
+             ceil_div(r, 32), ceil_div(d_out, 32)};
+}
+}  // namespace
+
+hipError_t launch_bwd_prep(const uint8_t* wq, uint8_t* wt, const float* A, const float* B,
+                           int64_t T, int64_t d_in, int64_t d_out, int64_t r, bool want_da,
+                           void* ws, hipStream_t s) {
+  const bool tr = wt != nullptr && d_in > 0 && d_out > 0;
+  const bool sp = r > 0 && T > 0 && d_in > 0 && d_out > 0;
+  if (!tr && !sp) return hipSuccess;
+  if (tr && (d_in % 16 != 0 || d_out % 16 != 0)) return hipErrorInvalidValue;
+  const int tr_tx = tr ? ceil_div(d_in, 128) : 1;
+  const int n_tr = tr ? tr_tx * ceil_div(d_out, 128) : 0;
+  Split sa{}, sb{};
+  if (sp) {
+    make_splits(make_plan(T, d_in, d_out, r), reinterpret_cast<uint8_t*>(ws), A, B, d_in, d_out,
+                r, sa, sb);
+    if (!want_da) sb.tx = sb.ty = 0;
+  }
+  const int grid = n_tr + sa.tx * sa.ty + sb.tx * sb.ty;
+  bwd_prep_kernel<<<grid, 256, 0, s>>>(wq, d_out, d_in, wt, n_tr, tr_tx, sa, sb);
+  return hipGetLastError();
+}
+
 hipError_t launch_adapter_grads(const uint8_t* gq, const float* s_g, const uint8_t* xq,
                                 const float* s_x, const float* A, const float* B, int64_t T,
                                 int64_t d_in, int64_t d_out, int64_t r, float* dA, float* dB,
-                                void* ws, hipStream_t s, int g_fmt) {
+                                void* ws, hipStream_t s, int g_fmt, bool presplit) {
   if (r == 0) return hipSuccess;
   if (T == 0) {
     hipError_t e = launch_fill_f32(dB, d_out * r, 0.0f, s);
@@ -689,11 +749,10 @@ hipError_t launch_adapter_grads(const uint8_t* gq, const float* s_g, const uint8
   const bool want_da = dA != nullptr;
 
   // 0. float operands -> bf16 hi/lo: A as is [r x d_in]; B transposed [r x d_out]
-  {
-    Split sa{A, (int)r, (int)d_in, false, d_in, u16(pl.off_ahi), u16(pl.off_alo),
-             ceil_div(d_in, 32), ceil_div(r, 32)};
-    Split sb{B, (int)d_out, (int)r, true, d_out, u16(pl.off_bhi), u16(pl.off_blo),
-             ceil_div(r, 32), ceil_div(d_out, 32)};
+  //    (done already by launch_bwd_prep when presplit)
+  if (!presplit) {
+    Split sa, sb;
+    make_splits(pl, base, A, B, d_in, d_out, r, sa, sb);
     const int tiles = std::max(sa.tx * sa.ty, want_da ? sb.tx * sb.ty : 0);
     split_bf16_kernel<<<dim3(tiles, 1, want_da ? 2 : 1), 256, 0, s>>>(sa, sb);
   }

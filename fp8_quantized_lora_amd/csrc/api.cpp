@@ -178,16 +178,26 @@ falq_status melded_linear_bwd_fmt(const uint8_t* gq, int g_fmt, const float* s_g
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   uint8_t* base = reinterpret_cast<uint8_t*>(ws);
   const size_t wt_bytes = align_up((size_t)d_in * (size_t)d_out, 256);
-  hipError_t e = hipSuccess;
-  if (dx && run_dx(gq, g_fmt, s_g, wq, s_w, T, d_in, d_out, dx, base, s) != hipSuccess)
+  // W~^T (for dX) and the adapter operands' bf16 splits in one launch
+  const bool gemm_dx = dx && T * d_in > 0 && d_out > 0;
+  const bool grads = r > 0 && T > 0 && d_in > 0 && d_out > 0;
+  if (falq::launch_bwd_prep(wq, gemm_dx ? base : nullptr, A, B, T, d_in, d_out, grads ? r : 0,
+                            dA != nullptr, base + wt_bytes, s) != hipSuccess)
     return FALQ_EHIP;
+  hipError_t e = hipSuccess;
+  if (gemm_dx)
+    e = falq::launch_gemm_fp8_nt(gq, d_out, base, d_out, dx, d_in, T, d_in, d_out, s_g, s_w, s,
+                                 g_fmt);
+  else if (dx && T * d_in > 0)                                 // d_out == 0
+    e = falq::launch_fill_f32(dx, T * d_in, 0.0f, s);
+  if (e != hipSuccess) return FALQ_EHIP;
   if (r > 0) {
     if (d_in == 0 || d_out == 0) {
       if (d_out > 0) e = falq::launch_fill_f32(dB, d_out * r, 0.0f, s);
       if (e == hipSuccess && dA && d_in > 0) e = falq::launch_fill_f32(dA, r * d_in, 0.0f, s);
     } else {
       e = falq::launch_adapter_grads(gq, s_g, xq, s_x, A, B, T, d_in, d_out, r, dA, dB,
-                                     base + wt_bytes, s, g_fmt);
+                                     base + wt_bytes, s, g_fmt, /*presplit=*/grads);
     }
   }
   return hip_status(e);

@@ -50,7 +50,15 @@ size_t adapter_grad_ws_bytes(int64_t T, int64_t d_in, int64_t d_out, int64_t r);
 hipError_t launch_adapter_grads(const uint8_t* gq, const float* s_g, const uint8_t* xq,
                                 const float* s_x, const float* A, const float* B,
                                 int64_t T, int64_t d_in, int64_t d_out, int64_t r,
-                                float* dA, float* dB, void* ws, hipStream_t s, int g_fmt = 0);
+                                float* dA, float* dB, void* ws, hipStream_t s, int g_fmt = 0,
+                                bool presplit = false);
+// The backward's preparation in one launch: W~^T into wt (skipped when wt is
+// null) and, when r, T, d_in and d_out are all positive, the adapter
+// gradients' float-operand splits into their workspace ws (B's only with
+// want_da); launch_adapter_grads with presplit then skips its own split.
+hipError_t launch_bwd_prep(const uint8_t* wq, uint8_t* wt, const float* A, const float* B,
+                           int64_t T, int64_t d_in, int64_t d_out, int64_t r, bool want_da,
+                           void* ws, hipStream_t s);
 
 // frozen FP8 factor A~: u [T x r] = dec(X~) dec(A~)^T / (s_x s_a)
 size_t frozen_u_ws_bytes(int64_t T, int64_t d_in, int64_t r);
