@@ -23,13 +23,18 @@ def state(m):
 # FP8 (X~A~^T formed in the forward GEMM), 32-bit AdamW whose step count lives
 # on the device, and here an E5M2 gradient
 CONFIGS = {"default": {}, "frozen_fp8_a_adamw_e5m2": dict(fp8_a=True, optimizer="adamw",
-                                                          g_fmt="e5m2")}
+                                                          g_fmt="e5m2"),
+           "split_k_halves": {}}
+# 8192 features: K = 8192 in both FP8 products, so their 256 x 256 tiles
+# (96 in each) run as two K halves added into a zeroed output
+SHAPES = {"split_k_halves": (8192, 8192)}
 
 
 @pytest.mark.parametrize("cfg", sorted(CONFIGS))
 def test_graph_replay_matches_eager(gpu_lib, cfg):
     announce(f"graph capture of one step ({cfg}), 3 replays vs eager")
-    spec = wl.LinearSpec("g", d_out=1024, d_in=1024, tokens=640, rank=16, dy_std=1e-2)
+    d_out, d_in = SHAPES.get(cfg, (1024, 1024))
+    spec = wl.LinearSpec("g", d_out=d_out, d_in=d_in, tokens=640, rank=16, dy_std=1e-2)
     d = wl.make_linear(7, 0, spec)
     batches = [wl.step_activations(7, 0, spec, s) for s in range(3)]
     mk = lambda: gpu_lib.MeldedLinear(spec.d_out, spec.d_in, spec.rank, spec.tokens,  # noqa: E731
