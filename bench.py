@@ -81,7 +81,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--batches", type=int, default=4, help="distinct (X, dY) batches cycled")
-    ap.add_argument("--cpu-tokens", type=int, default=2048,
+    ap.add_argument("--cpu-tokens", type=int, default=4096,
                     help="token sample for the CPU-oracle baseline (0 = skip)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--adapter", choices=["trained", "frozen-fp8"], default="trained",
@@ -624,11 +624,13 @@ def gemm_traffic_bytes():
         return None
 
 
-def cpu_baseline(spec, d0, Ts, optimizer="sgd", frozen=False, g_fmt="e4m3", x_note=""):
+def cpu_baseline(spec, d0, Ts, optimizer="sgd", frozen=False, g_fmt="e4m3", x_note="",
+                 min_seconds=10.0):
     """The CPU oracle, as it is, on a token sample of the same workload:
     quantize X and dY, forward, backward (dX, dA, dB; or with A frozen in FP8,
     X~A~^T in the forward and dX, dB), the adapter step (SGD or AdamW) and
-    the proxy update over the full backbone."""
+    the proxy update over the full backbone; the step is repeated on the same
+    inputs until `min_seconds` have passed, and the mean is reported."""
     import numpy as np
 
     import oracle
@@ -643,24 +645,15 @@ def cpu_baseline(spec, d0, Ts, optimizer="sgd", frozen=False, g_fmt="e4m3", x_no
         aq, s_a, _, _ = oracle.fp8_quantize(A0)
         A0 = oracle.fp8_dequantize(aq, s_a)
     t1 = time.perf_counter()
-    xq, s_x, _, _ = oracle.fp8_quantize(X)
-    gq, s_g, _, _ = oracle.fp8_quantize(dY, fmt=g_fmt)
-    if frozen:
-        _, U = oracle.melded_linear_fwd_frozen_a(xq, s_x, wq, s_w, aq, s_a)
-        _, dB = oracle.melded_linear_bwd_frozen_a(gq, s_g, wq, s_w, U, g_fmt=g_fmt)
-        dA = None
-    else:
-        oracle.melded_linear_fwd(xq, s_x, wq, s_w)
-        _, dA, dB = oracle.melded_linear_bwd(gq, s_g, xq, s_x, wq, s_w, A0, d0["B"], g_fmt=g_fmt)
-    if optimizer == "sgd":
-        A, B = oracle.adapter_step(A0, d0["B"], dA, dB, spec.lr)
-    else:
-        z = [np.zeros_like(A0), np.zeros_like(d0["B"])]
-        A, B, _, _, _, _ = oracle.adapter_step_adamw(A0, d0["B"], dA, dB, z[0], z[0], z[1],
-                                                     z[1], spec.lr, 0.9, 0.999, 1e-8, 0.0, 1)
-    oracle.rowwise_proxy_update(wq, s_w, A, B, spec.tau, spec.k_max)
+    reps = 0
+    while True:
+        _oracle_step(oracle, np, spec, X, dY, wq, s_w, A0, d0["B"], aq if frozen else None,
+                     s_a if frozen else None, optimizer, frozen, g_fmt)
+        reps += 1
+        if time.perf_counter() - t1 >= min_seconds:
+            break
     t2 = time.perf_counter()
-    step_s = t2 - t1
+    step_s = (t2 - t1) / reps
     flops = wl.step_flops(Ts, spec.d_in, spec.d_out, spec.rank, frozen_a=frozen)
     try:
         import threadpoolctl
@@ -671,10 +664,31 @@ def cpu_baseline(spec, d0, Ts, optimizer="sgd", frozen=False, g_fmt="e4m3", x_no
     return {"value": round(flops / step_s / 1e12, 5), "unit": "TFLOP/s", "cores": int(max(
         blas_threads, oracle.num_threads())), "kind": "oracle",
         "tokens_per_s": round(Ts / step_s, 1),
-        "sample": f"one step on the first {Ts} of {spec.tokens} tokens{x_note} (full "
-                  f"{spec.d_out} x {spec.d_in} weight, r={spec.rank}, "
-                  f"full proxy update), {step_s:.1f} s; the initial quantization of W"
-                  f"{' and A' if frozen else ''} ({t1 - t0:.1f} s) is not part of the step"}
+        "sample": f"the step on the first {Ts} of {spec.tokens} tokens{x_note} (full "
+                  f"{spec.d_out} x {spec.d_in} weight, r={spec.rank}, full proxy update), "
+                  f"{reps} repetition{'s' if reps > 1 else ''} in {t2 - t1:.1f} s, mean "
+                  f"{step_s:.2f} s; the initial quantization of W{' and A' if frozen else ''} "
+                  f"({t1 - t0:.1f} s) is not part of the step"}
+
+
+def _oracle_step(oracle, np, spec, X, dY, wq, s_w, A0, B0, aq, s_a, optimizer, frozen, g_fmt):
+    """one step of the oracle from the given state (nothing is kept)"""
+    xq, s_x, _, _ = oracle.fp8_quantize(X)
+    gq, s_g, _, _ = oracle.fp8_quantize(dY, fmt=g_fmt)
+    if frozen:
+        _, U = oracle.melded_linear_fwd_frozen_a(xq, s_x, wq, s_w, aq, s_a)
+        _, dB = oracle.melded_linear_bwd_frozen_a(gq, s_g, wq, s_w, U, g_fmt=g_fmt)
+        dA = None
+    else:
+        oracle.melded_linear_fwd(xq, s_x, wq, s_w)
+        _, dA, dB = oracle.melded_linear_bwd(gq, s_g, xq, s_x, wq, s_w, A0, B0, g_fmt=g_fmt)
+    if optimizer == "sgd":
+        A, B = oracle.adapter_step(A0, B0, dA, dB, spec.lr)
+    else:
+        z = [np.zeros_like(A0), np.zeros_like(B0)]
+        A, B, _, _, _, _ = oracle.adapter_step_adamw(A0, B0, dA, dB, z[0], z[0], z[1],
+                                                     z[1], spec.lr, 0.9, 0.999, 1e-8, 0.0, 1)
+    oracle.rowwise_proxy_update(wq, s_w, A, B, spec.tau, spec.k_max)
 
 
 if __name__ == "__main__":
