@@ -71,7 +71,10 @@ def run_fwd(fq, xq, s_x, wq, s_w):
 
 
 @pytest.mark.parametrize("T,d_in,d_out", [(256, 256, 256), (300, 512, 272), (1, 256, 16),
-                                          (513, 1024, 528)])
+                                          (513, 1024, 528),
+                                          # 16640 values = 8320 bytes = 65 K steps: both
+                                          # tiles run as two K halves (32 and 33 steps)
+                                          (256, 16640, 304)])
 def test_fp4_forward_parity(gpu_lib, T, d_in, d_out):
     announce(f"fp4 forward T={T} d_in={d_in} d_out={d_out}")
     rng = np.random.default_rng(T + d_in + d_out)
