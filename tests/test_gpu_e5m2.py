@@ -76,9 +76,10 @@ def problem(seed, T, d_in, d_out, r):
 
 
 # K = d_out: 512 and 1024 take the direct-load GEMM (K % 128 == 0), 80 and 272
-# the register-staged one
+# the register-staged one; 8320 (65 K steps) splits the dX tiles into two K halves
 @pytest.mark.parametrize("T,d_in,d_out,r", [(256, 512, 512, 16), (257, 400, 272, 5),
-                                            (600, 1040, 1024, 64), (33, 48, 80, 70)])
+                                            (600, 1040, 1024, 64), (33, 48, 80, 70),
+                                            (256, 1024, 8320, 3)])
 def test_e5m2_backward(gpu_lib, T, d_in, d_out, r):
     announce(f"bwd with E5M2 dY: T {T} d_in {d_in} d_out {d_out} r {r}")
     wq, s_w, xq, s_x, gq, s_g, A, B = problem(T + r, T, d_in, d_out, r)
