@@ -1,0 +1,36 @@
+"""Host-side parts of bench.py (no GPU): the one-GPU guard, the traffic
+record's source check, and the argument surface."""
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+
+
+def test_more_than_one_gpu_exits_with_a_message():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120, cwd=ROOT)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr and r.stdout == ""
+
+
+def test_traffic_is_reported_only_for_the_measured_sources(monkeypatch):
+    # the committed summary records the digest of the GEMM sources it was
+    # measured on; any other digest (changed sources) gives no traffic figure
+    measured = bench.gemm_traffic_bytes()
+    assert measured is None or measured > 96 * 2**20      # at least the algorithmic bytes
+    monkeypatch.setattr(bench, "gemm_sources_digest", lambda: "0" * 64)
+    assert bench.gemm_traffic_bytes() is None
+
+
+@pytest.mark.parametrize("argv", [["--workload", "mlp7b"], ["--workload", "rank-sweep"],
+                                  ["--fp4-gemm"], ["--merge-every", "4"], ["--topk-rank", "16"]])
+def test_options_parse(monkeypatch, argv):
+    monkeypatch.setattr(sys, "argv", ["bench.py"] + argv)
+    a = bench.parse()
+    assert a.gpus == 1 and a.steps > 0 and a.warmup >= 0
