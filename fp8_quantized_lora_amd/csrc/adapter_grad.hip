@@ -34,7 +34,6 @@ namespace falq {
 namespace {
 
 constexpr int TM = 256, TN = 64, TK = 128;     // skinny tile: M x N outputs, K step
-constexpr int kThreads = 256;                  // split / reduce kernels
 constexpr int kSkThreads = 512;                // skinny kernel: 8 waves, 64 x 32 outputs each
 
 __device__ __forceinline__ uint16_t bf16_rne(float f) {

@@ -126,8 +126,9 @@ __device__ __forceinline__ float2 dec2(uint32_t w, bool hi) {
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
 
 __device__ __forceinline__ void load16_to_lds(const void* g, uint32_t lds_addr) {
-  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(lds_addr)
-               : "memory", "m0");
+  // "{m0}": the compiler itself places the LDS address in m0 (a register
+  // it reserves, so it may not be named as a clobber)
+  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(lds_addr) : "memory");
 }
 __device__ __forceinline__ uint32_t lds_offset(const void* p) {
   return (uint32_t)(uintptr_t)(const lds_u8*)p;

@@ -134,7 +134,7 @@ __global__ __launch_bounds__(1024) void comp_compact_kernel(const int* __restric
     sums[threadIdx.x] = f;
     __syncthreads();
     for (int off = 1; off < 1024; off <<= 1) {         // inclusive scan
-      const int v = threadIdx.x >= off ? sums[threadIdx.x - off] : 0;
+      const int v = (int)threadIdx.x >= off ? sums[threadIdx.x - off] : 0;
       __syncthreads();
       sums[threadIdx.x] += v;
       __syncthreads();
