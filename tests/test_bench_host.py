@@ -34,3 +34,15 @@ def test_options_parse(monkeypatch, argv):
     monkeypatch.setattr(sys, "argv", ["bench.py"] + argv)
     a = bench.parse()
     assert a.gpus == 1 and a.steps > 0 and a.warmup >= 0
+
+
+def test_cpu_baseline_reports_the_oracle_step():
+    """cpu_baseline times the oracle as it is on a token sample of the
+    workload (one repetition here) and reports what it ran."""
+    import workloads as wl
+    spec = wl.WORKLOADS[1].linears[0]                 # the 512 x 512 single linear
+    d0 = wl.make_linear(1, 0, spec, step=0)
+    r = bench.cpu_baseline(spec, d0, 64, min_seconds=0.0)
+    assert r["kind"] == "oracle" and r["unit"] == "TFLOP/s" and r["value"] > 0
+    assert r["cores"] >= 1 and r["tokens_per_s"] > 0
+    assert "first 64 of 256 tokens" in r["sample"] and "1 repetition " in r["sample"]
