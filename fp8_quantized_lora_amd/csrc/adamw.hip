@@ -11,11 +11,14 @@
 //     p'  = decay*p - step_size*(m'/den)
 // with sqrt and the division correctly rounded.  The step-dependent scalars
 // come from a 64-byte optimizer state in device memory, advanced by a
-// one-thread kernel before the update: step t, the running float64 products
-// beta1^t and beta2^t, and the float32 scalars of the step (decay =
-// 1 - lr*wd, step_size = lr / (1 - beta1^t), inv_bc2 = 1 / sqrt(1 -
-// beta2^t), each computed in float64 and rounded once).  Nothing comes from
-// the host per step, so a captured graph replays consecutive steps.
+// one-thread kernel before the update: step t, then the float32 scalars of
+// step t (decay = 1 - lr*wd, step_size = lr / (1 - beta1^t), inv_bc2 =
+// 1 / sqrt(1 - beta2^t), omb = 1 - beta), each the value of its formula
+// rounded once to float32.  The formulas are evaluated in double-double
+// arithmetic (about 104 significant bits; beta^t by repeated squaring from
+// t), so the single rounding to float32 is the correct one unless the exact
+// value lies within ~2^-95 of a float32 rounding boundary.  Nothing comes
+// from the host per step, so a captured graph replays consecutive steps.
 // Memory: 16 bytes read and 12 bytes written per element, float4 at a time.
 #include "common.hpp"
 #include "kernels.hpp"
@@ -27,24 +30,91 @@ namespace {
 
 constexpr int kThreads = 256;
 
+// ---- double-double arithmetic (value = hi + lo, |lo| <= ulp(hi) / 2) ------
+// Error-free transformations: a + b = s + e exactly (Knuth's two-sum), and
+// a * b = p + e exactly (the product's error from one fused multiply-add).
+// The library is built without fp contraction, so the compiler neither fuses
+// nor reassociates these sums.
+struct dd {
+  double hi, lo;
+};
+__device__ dd two_sum(double a, double b) {
+  const double s = a + b, bb = s - a;
+  return {s, (a - (s - bb)) + (b - bb)};
+}
+__device__ dd fast_two_sum(double a, double b) {      // |a| >= |b|
+  const double s = a + b;
+  return {s, b - (s - a)};
+}
+__device__ dd dd_add(dd a, dd b) {
+  dd s = two_sum(a.hi, b.hi);
+  const dd t = two_sum(a.lo, b.lo);
+  s = fast_two_sum(s.hi, s.lo + t.hi);
+  return fast_two_sum(s.hi, s.lo + t.lo);
+}
+__device__ dd dd_neg(dd a) { return {-a.hi, -a.lo}; }
+__device__ dd dd_mul(dd a, dd b) {
+  const double p = a.hi * b.hi, e = fma(a.hi, b.hi, -p);
+  return fast_two_sum(p, e + (a.hi * b.lo + a.lo * b.hi));
+}
+// a / b by long division: three quotient digits, each from the remainder
+__device__ dd dd_div(dd a, dd b) {
+  const double q1 = a.hi / b.hi;
+  dd r = dd_add(a, dd_neg(dd_mul(b, {q1, 0.0})));
+  const double q2 = r.hi / b.hi;
+  r = dd_add(r, dd_neg(dd_mul(b, {q2, 0.0})));
+  const double q3 = r.hi / b.hi;
+  return dd_add(fast_two_sum(q1, q2), {q3, 0.0});
+}
+// sqrt(a), a > 0: one Newton correction of the double square root
+__device__ dd dd_sqrt(dd a) {
+  const double x = sqrt(a.hi);
+  const dd r = dd_add(a, dd_neg(dd_mul({x, 0.0}, {x, 0.0})));
+  return fast_two_sum(x, r.hi / (2.0 * x));
+}
+// b^t, t >= 0, by repeated squaring
+__device__ dd dd_pow(double b, int64_t t) {
+  dd r{1.0, 0.0}, p{b, 0.0};
+  while (t > 0) {
+    if (t & 1) r = dd_mul(r, p);
+    p = dd_mul(p, p);
+    t >>= 1;
+  }
+  return r;
+}
+// hi + lo rounded once to float32.  (float)hi is the nearest float to hi; it
+// can differ from the nearest float to hi + lo only when hi sits exactly on
+// a midpoint between two floats (|lo| is below hi's double spacing), where
+// the sign of lo decides.
+__device__ float dd_to_f32(dd a) {
+  const float f = (float)a.hi;
+  if (a.lo != 0.0 && __builtin_isfinite(f)) {
+    const float below = nextafterf(f, -__builtin_inff()), above = nextafterf(f, __builtin_inff());
+    if (a.hi == 0.5 * ((double)below + (double)f) && a.lo < 0.0) return below;
+    if (a.hi == 0.5 * ((double)f + (double)above) && a.lo > 0.0) return above;
+  }
+  return f;
+}
+
 // the optimizer state (AdamWState in kernels.hpp): all zero = before step 1
 __global__ void adamw_advance_kernel(AdamWState* st, float lr, float beta1, float beta2, float eps,
                                      float wd) {
-  const bool first = st->t == 0;
-  const double p1 = (first ? 1.0 : st->pow1) * (double)beta1;
-  const double p2 = (first ? 1.0 : st->pow2) * (double)beta2;
-  st->t += 1;
-  st->pow1 = p1;
-  st->pow2 = p2;
+  const int64_t t = st->t + 1;
+  const dd one{1.0, 0.0};
+  const dd p1 = dd_pow((double)beta1, t), p2 = dd_pow((double)beta2, t);
+  st->t = t;
+  st->pow1 = p1.hi;
+  st->pow2 = p2.hi;
   AdamWScalars c;
   c.b1 = beta1;
   c.b2 = beta2;
-  c.omb1 = (float)(1.0 - (double)beta1);
-  c.omb2 = (float)(1.0 - (double)beta2);
+  c.omb1 = dd_to_f32(two_sum(1.0, -(double)beta1));
+  c.omb2 = dd_to_f32(two_sum(1.0, -(double)beta2));
   c.eps = eps;
-  c.decay = (float)(1.0 - (double)lr * (double)wd);
-  c.step_size = (float)((double)lr / (1.0 - p1));
-  c.inv_bc2 = (float)(1.0 / sqrt(1.0 - p2));
+  // lr * wd is exact in double (two 24-bit significands)
+  c.decay = dd_to_f32(two_sum(1.0, -((double)lr * (double)wd)));
+  c.step_size = dd_to_f32(dd_div({(double)lr, 0.0}, dd_add(one, dd_neg(p1))));
+  c.inv_bc2 = dd_to_f32(dd_div(one, dd_sqrt(dd_add(one, dd_neg(p2)))));
   st->sc = c;
 }
 

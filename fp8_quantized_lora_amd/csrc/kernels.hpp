@@ -92,7 +92,7 @@ struct AdamWTensor {
 // optimizer state in device memory (64 bytes; all zero before the first step)
 struct AdamWState {
   int64_t t;             // steps taken
-  double pow1, pow2;     // beta1^t, beta2^t (running products)
+  double pow1, pow2;     // beta1^t, beta2^t (leading double of each; informational)
   AdamWScalars sc;       // the float32 scalars of step t
   uint32_t pad[2];
 };

@@ -299,11 +299,12 @@ falq_status adapter_step(float *A, float *B, const float *dA, const float *dB,
  *
  * `state` is FALQ_ADAMW_STATE_BYTES of device memory (8-byte aligned) that
  * the caller zero-fills once before the first step and then leaves to the
- * library: each call first advances it (step t = t + 1; P1 = beta1^t and
- * P2 = beta2^t as running float64 products, starting from 1) and derives,
- * in float64 from the float arguments, each rounded to float once:
+ * library: each call first advances it (step t = t + 1) and derives from t
+ * and the float arguments the step's float32 scalars, each the exact value
+ * of its formula rounded once to the nearest float32 (evaluated in
+ * double-double arithmetic, beta^t by repeated squaring):
  *     omb1 = 1 - beta1, omb2 = 1 - beta2, decay = 1 - lr*weight_decay,
- *     step_size = lr / (1 - P1), inv_bc2 = 1 / sqrt(1 - P2)
+ *     step_size = lr / (1 - beta1^t), inv_bc2 = 1 / sqrt(1 - beta2^t)
  * then per element, every float operation rounded on its own (no fused
  * multiply-add; sqrt and division correctly rounded):
  *     m <- beta1*m + omb1*g

@@ -26,8 +26,9 @@ arithmetic or an independent library routine.
 from __future__ import annotations
 
 import ctypes
-import math
 import os
+from decimal import Decimal, localcontext
+from fractions import Fraction
 from typing import Optional, Tuple
 
 import numpy as np
@@ -284,30 +285,68 @@ def adapter_step(A: np.ndarray, B: np.ndarray, dA: Optional[np.ndarray], dB: np.
     return A2, B2
 
 
+def _nearest_f32(x: Fraction) -> np.float32:
+    """The float32 nearest to the exact rational x, ties to the even
+    significand.  float(x) is within half a float64 spacing of x, so the
+    nearest float32 is that value's float32 or one of its two neighbours;
+    the choice among the three is made on exact rationals."""
+    c = np.float32(float(x))
+    cands = [np.nextafter(c, np.float32(-np.inf)), c, np.nextafter(c, np.float32(np.inf))]
+    best = None
+    for k in cands:
+        if not np.isfinite(k):
+            continue
+        d = abs(Fraction(float(k)) - x)
+        if best is None or d < best[0] or (d == best[0] and int(k.view(np.uint32)) % 2 == 0):
+            best = (d, k)
+    return np.float32(best[1])
+
+
+def _nearest_f32_guarded(x: Decimal, digits: int) -> np.float32:
+    """_nearest_f32 of a value known to `digits` significant digits: raises
+    if the value lies so close to a float32 rounding boundary that the
+    rounding could depend on the digits not computed."""
+    xf = Fraction(x)
+    c = _nearest_f32(xf)
+    side = np.float32(np.inf) if xf > Fraction(float(c)) else np.float32(-np.inf)
+    mid = (Fraction(float(c)) + Fraction(float(np.nextafter(c, side)))) / 2
+    if abs(xf - mid) <= abs(xf) * Fraction(10) ** (5 - digits):
+        raise ArithmeticError("AdamW scalar too close to a float32 rounding boundary")
+    return c
+
+
 def adamw_scalars(lr: float, beta1: float, beta2: float, eps: float, weight_decay: float,
                   step: int) -> dict:
-    """The float32 scalars of AdamW step number `step` (>= 1).  Each is computed
-    in float64 from the float32 values of the arguments and rounded to float32
-    once:
+    """The float32 scalars of AdamW step number `step` (>= 1), each the exact
+    value of its definition (from the float32 values of the arguments)
+    rounded once to the nearest float32:
         decay     = 1 - lr*wd                     (decoupled weight decay)
-        step_size = lr / (1 - P1)                 (first-moment bias correction)
-        inv_bc2   = 1 / sqrt(1 - P2)              (second-moment bias correction)
+        step_size = lr / (1 - beta1**step)        (first-moment bias correction)
+        inv_bc2   = 1 / sqrt(1 - beta2**step)     (second-moment bias correction)
         omb1, omb2 = 1 - beta1, 1 - beta2
-    where P = beta**step is formed as the running float64 product of beta over
-    the steps (one rounding per step: the value an optimizer state carries
-    from step to step, so that the step count can live in device memory).
+    decay and the omb are rational and computed exactly; the two bias
+    corrections are computed to 120 significant digits, and the rounding is
+    refused (ArithmeticError) should the value lie within 1e-115 (relative)
+    of a float32 rounding boundary, where those digits could not decide it.
     """
+    t = int(step)
+    if t < 1:
+        raise ValueError("step counts from 1")
     lr, b1, b2, eps, wd = (float(np.float32(v)) for v in (lr, beta1, beta2, eps, weight_decay))
-    p1 = p2 = 1.0
-    for _ in range(int(step)):
-        p1 *= b1
-        p2 *= b2
+    F = Fraction
+    digits = 120
+    with localcontext() as ctx:
+        ctx.prec = digits
+        p1 = Decimal(b1) ** t
+        p2 = Decimal(b2) ** t
+        step_size = Decimal(lr) / (1 - p1)
+        inv_bc2 = 1 / (1 - p2).sqrt()
     return {
         "b1": np.float32(b1), "b2": np.float32(b2), "eps": np.float32(eps),
-        "omb1": np.float32(1.0 - b1), "omb2": np.float32(1.0 - b2),
-        "decay": np.float32(1.0 - lr * wd),
-        "step_size": np.float32(lr / (1.0 - p1)),
-        "inv_bc2": np.float32(1.0 / math.sqrt(1.0 - p2)),
+        "omb1": _nearest_f32(1 - F(b1)), "omb2": _nearest_f32(1 - F(b2)),
+        "decay": _nearest_f32(1 - F(lr) * F(wd)),
+        "step_size": _nearest_f32_guarded(step_size, digits),
+        "inv_bc2": _nearest_f32_guarded(inv_bc2, digits),
     }
 
 

@@ -12,18 +12,12 @@ from tests.gpu_util import announce, dev, host
 pytestmark = pytest.mark.gpu
 
 
-def state_at(gpu_lib, t, beta1, beta2):
-    """An AdamW state after t steps: t and the running float64 products of the
-    float32 betas (the scalar fields are rewritten by the next call)."""
+def state_at(gpu_lib, t, beta1=None, beta2=None):
+    """An AdamW state after t steps: the next call takes step t + 1 (the
+    library derives every step scalar from the step count alone)."""
     st = gpu_lib.adamw_state()
-    b1, b2 = float(np.float32(beta1)), float(np.float32(beta2))
-    p1 = p2 = 1.0
-    for _ in range(t):
-        p1 *= b1
-        p2 *= b2
     h = np.zeros(8, np.int64)
     h[0] = t
-    h[1:3] = np.array([p1, p2], np.float64).view(np.int64)
     st.copy_(torch.from_numpy(h))
     return st
 
@@ -95,3 +89,35 @@ def test_adamw_empty(gpu_lib):
     state = gpu_lib.adamw_state()
     gpu_lib.adapter_step_adamw(z, zb, z, zb, z, z, zb, zb, state, lr=1e-3)
     assert int(host(state)[0]) == 1                 # the step is counted
+
+
+@pytest.mark.parametrize("hp,steps", [
+    (dict(lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.01), 10000),
+    (dict(lr=3e-4, beta1=0.8, beta2=0.95, eps=1e-6, weight_decay=0.1), 2000),
+    # lr * wd = 2^-25 (1 + 574 2^-47): 1 - lr*wd rounded through float64
+    # would tie to 1.0; the exact value rounds to 1 - 2^-24
+    (dict(lr=11854442 * 2.0 ** -36, beta1=0.5, beta2=0.75, eps=1e-8,
+          weight_decay=11872131 * 2.0 ** -36), 200)])
+def test_adamw_step_scalars_trace(gpu_lib, hp, steps):
+    """The float32 step scalars the state holds after each of `steps`
+    consecutive calls (tiny tensors), bit for bit against the oracle's
+    exact-definition values: decay, 1 - beta, lr / (1 - beta1^t) and
+    1 / sqrt(1 - beta2^t)."""
+    announce(f"adapter_step_adamw scalar trace, {steps} steps, {hp}")
+    z = torch.zeros((1, 16), device="cuda")
+    zb = torch.zeros((16, 1), device="cuda")
+    state = gpu_lib.adamw_state()
+    hist = torch.empty((steps, 8), dtype=torch.int64, device="cuda")
+    for i in range(steps):
+        gpu_lib.adapter_step_adamw(z, zb, z, zb, z, z, zb, zb, state, **hp)
+        hist[i].copy_(state)
+    h = host(hist)
+    assert np.array_equal(h[:, 0], np.arange(1, steps + 1))
+    sc = h[:, 3:7].copy().view(np.float32)          # b1 b2 omb1 omb2 eps decay step inv
+    names = ["b1", "b2", "omb1", "omb2", "eps", "decay", "step_size", "inv_bc2"]
+    for i in range(steps):
+        ref = oracle.adamw_scalars(hp["lr"], hp["beta1"], hp["beta2"], hp["eps"],
+                                   hp["weight_decay"], i + 1)
+        got = dict(zip(names, sc[i]))
+        for k in names:
+            assert bits(got[k]) == bits(ref[k]), (i + 1, k, got[k], ref[k])

@@ -93,3 +93,25 @@ def test_quantize_is_deterministic(gpu_lib):
     a = run_gpu(gpu_lib, x)
     b = run_gpu(gpu_lib, x)
     assert np.array_equal(a[0], b[0]) and a[1] == b[1]
+
+
+def test_quantize_double_rounding_golden(gpu_lib):
+    """The golden cases whose fl32(x*s) lands exactly on an E4M3 midpoint that
+    the exact product misses (tests/golden/fp8_double_rounding.txt, derived on
+    exact rationals): the GPU cast gives the fixture's two-rounding code,
+    with the scale given and with the scale from the tensor's amax."""
+    from tests.test_oracle_linear import load_double_rounding_golden
+    announce("quantize double-rounding golden cases")
+    rows = load_double_rounding_golden()
+    x = np.array([r[0] for r in rows], np.float32)
+    s_all = np.array([r[1] for r in rows], np.float32)
+    want = np.array([r[2] for r in rows], np.uint8)
+    for s in np.unique(s_all):
+        k = s_all == s
+        q, s_out, _, _ = run_gpu(gpu_lib, x[k], scale_in=s)
+        assert s_out == s and np.array_equal(q, want[k]), (s, q, want[k])
+    for amax in (np.float32(3.1), np.float32(0.0731)):
+        s = np.float32(448.0) / amax
+        k = s_all == s
+        q, s_out, a_out, _ = run_gpu(gpu_lib, np.concatenate([[amax], x[k]]).astype(np.float32))
+        assert s_out == s and a_out == amax and np.array_equal(q[1:], want[k])

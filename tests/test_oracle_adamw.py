@@ -150,13 +150,71 @@ def test_each_rounding_exact_rationals():
         assert p2[0] == np.float32(ep)
 
 
-def test_scalars_from_definitions():
-    for t in (1, 2, 10, 1000):
-        sc = oracle.adamw_scalars(2e-4, 0.9, 0.95, 1e-6, 0.05, t)
-        lr, b1, b2, wd = (float(np.float32(x)) for x in (2e-4, 0.9, 0.95, 0.05))
-        assert abs(float(sc["step_size"]) - lr / (1 - b1 ** t)) <= 1e-7 * lr / (1 - b1 ** t)
-        assert abs(float(sc["inv_bc2"]) * math.sqrt(1 - b2 ** t) - 1) < 1e-7
-        assert sc["decay"] == np.float32(1 - lr * wd)
+ADAMW_HP = [(1e-3, 0.9, 0.999, 1e-8, 0.01), (2e-4, 0.9, 0.95, 1e-6, 0.05),
+            (3e-4, 0.8, 0.95, 1e-6, 0.1)]
+STEPS = list(range(1, 41)) + [64, 100, 333, 1000, 4096, 10000]
+
+
+def _neighbours(c):
+    c = np.float32(c)
+    return (Fraction(float(np.nextafter(c, np.float32(-np.inf)))), Fraction(float(c)),
+            Fraction(float(np.nextafter(c, np.float32(np.inf)))))
+
+
+@pytest.mark.parametrize("hp", ADAMW_HP)
+def test_scalars_exact_definition(hp):
+    """Every step scalar against its definition on exact rationals, with
+    beta**t formed as an exact rational power: step_size and decay rounded by
+    tests/exact.round_to_f32; inv_bc2 = 1/sqrt(1 - beta2**t) checked by
+    bracketing it between the midpoints to its float32 neighbours (exact
+    squares, no square root taken)."""
+    lr, b1, b2, eps, wd = (Fraction(float(np.float32(v))) for v in hp)
+    for t in STEPS:
+        sc = oracle.adamw_scalars(*hp, t)
+        assert float(sc["step_size"]) == round_to_f32(lr / (1 - b1 ** t)), t
+        assert float(sc["decay"]) == round_to_f32(1 - lr * wd)
+        assert float(sc["omb1"]) == round_to_f32(1 - b1)
+        assert float(sc["omb2"]) == round_to_f32(1 - b2)
+        q = 1 - b2 ** t
+        lo, c, hi = _neighbours(sc["inv_bc2"])
+        # 1/sqrt(q) lies between the midpoints (lo+c)/2 and (c+hi)/2
+        assert ((lo + c) / 2) ** 2 * q <= 1 <= ((c + hi) / 2) ** 2 * q, t
+
+
+def test_scalars_limits():
+    """Closed forms: at t = 1 the bias-corrected step is lr/(1 - beta1) and
+    inv_bc2 = 1/sqrt(1 - beta2); the step size falls monotonically towards lr
+    and inv_bc2 towards 1; once beta**t is far below float32 resolution both
+    are exactly lr and 1."""
+    sc1 = oracle.adamw_scalars(1e-3, 0.5, 0.75, 1e-8, 0.0, 1)
+    assert sc1["step_size"] == np.float32(2e-3)        # 0.5 is exact: lr / 0.5
+    assert sc1["inv_bc2"] == np.float32(2.0)           # 1/sqrt(0.25)
+    prev = None
+    for t in (1, 2, 3, 5, 10, 30, 100, 300, 1000):
+        sc = oracle.adamw_scalars(1e-3, 0.9, 0.999, 1e-8, 0.0, t)
+        if prev is not None:
+            assert sc["step_size"] <= prev["step_size"] and sc["inv_bc2"] <= prev["inv_bc2"]
+        prev = sc
+    far = oracle.adamw_scalars(1e-3, 0.9, 0.99, 1e-8, 0.0, 20000)
+    assert far["step_size"] == np.float32(1e-3) and far["inv_bc2"] == np.float32(1.0)
+
+
+def test_scalars_single_rounding_not_float64():
+    """The scalars are the exact values rounded once, not a float64 value
+    rounded again to float32: with the float32 lr = 11854442 * 2**-36 and
+    wd = 11872131 * 2**-36, lr*wd = 2**-25 * (1 + 574 * 2**-47) (the integer
+    product is 2**47 + 574).  1 - lr*wd then lies just below 1 - 2**-25, the
+    midpoint between the float32 values 1 - 2**-24 and 1: float64 rounds it
+    onto the midpoint and float32 then ties it to 1, while the exact value
+    rounds down to 1 - 2**-24."""
+    lr, wd = 11854442 * 2.0 ** -36, 11872131 * 2.0 ** -36
+    assert np.float32(lr) == lr and np.float32(wd) == wd
+    assert 11854442 * 11872131 == 2 ** 47 + 574
+    exact = 1 - Fraction(lr) * Fraction(wd)
+    assert 1 - Fraction(1, 2 ** 24) < exact < 1 - Fraction(1, 2 ** 25)
+    assert np.float32(1.0 - lr * wd) == np.float32(1.0)     # float64 then float32
+    sc = oracle.adamw_scalars(lr, 0.9, 0.999, 1e-8, wd, 1)
+    assert float(sc["decay"]) == 1.0 - 2.0 ** -24 == round_to_f32(exact)
 
 
 def test_frozen_a_keeps_a_and_its_moments():

@@ -99,6 +99,68 @@ def test_quantize_static_scale_and_bf16():
     assert np.array_equal(qa, qb) and sa == sb
 
 
+def load_double_rounding_golden():
+    """tests/golden/fp8_double_rounding.txt: (x, s, code of the two-rounding
+    quantize, code of one rounding of the exact product)."""
+    import os
+    path = os.path.join(os.path.dirname(__file__), "golden", "fp8_double_rounding.txt")
+    rows = []
+    with open(path) as fh:
+        for line in fh:
+            if line.startswith("#") or not line.strip():
+                continue
+            f = line.split()
+            rows.append((np.float32(float.fromhex(f[0])), np.float32(float.fromhex(f[1])),
+                         int(f[2], 16), int(f[3], 16)))
+    return rows
+
+
+def test_quantize_double_rounding_golden():
+    """The cast rounds twice: v = fl32(x*s), then E4M3 of v (the rebuttal's
+    thread 2, reply W2 multiplies by the per-tensor scale and rounds the
+    product to FP8; the reading is an fp32 multiply, then the cast).  Each
+    golden case (derived on exact rationals from the OCP E4M3 definition by
+    tests/golden/make_fp8_double_rounding.py) has fl32(x*s) exactly on an E4M3
+    midpoint that the exact product misses, with non-power-of-two scales, so
+    the two readings give different codes.  Checked with the scale given and
+    with the scale derived from the tensor's amax (s = fl32(448 / amax))."""
+    rows = load_double_rounding_golden()
+    assert len(rows) >= 20
+    x = np.array([r[0] for r in rows], np.float32)
+    s_all = np.array([r[1] for r in rows], np.float32)
+    want = np.array([r[2] for r in rows], np.uint8)
+    for s in np.unique(s_all):
+        k = s_all == s
+        q, s_out, _, _ = oracle.fp8_quantize(x[k], scale_in=s)
+        assert s_out == s and np.array_equal(q, want[k]), (s, q, want[k])
+    # current scaling: a tensor whose amax gives the fixture's scale
+    for amax in (np.float32(3.1), np.float32(0.0731)):
+        s = np.float32(448.0) / amax
+        k = s_all == s
+        assert k.sum() >= 6
+        q, s_out, a_out, _ = oracle.fp8_quantize(np.concatenate([[amax], x[k]]).astype(np.float32))
+        assert s_out == s and a_out == amax and q[0] == 0x7E
+        assert np.array_equal(q[1:], want[k])
+
+
+def test_quantize_double_rounding_golden_rejects_single_rounding():
+    """The planted other reading -- one rounding of the exact product x*s to
+    the nearest E4M3 value (x*s is exact in float64) -- disagrees with every
+    golden case."""
+    rows = load_double_rounding_golden()
+    mags = DEC[:0x7F]                                   # codes 0x00..0x7E, ascending
+    for xv, s, code2, code1 in rows:
+        p = float(xv) * float(s)                        # exact (24 x 24 bits)
+        a = min(abs(p), 448.0)
+        d = np.abs(mags - a)
+        best = int(np.flatnonzero(d == d.min())[-1] if d.min() > 0 else np.argmin(d))
+        cands = np.flatnonzero(d == d.min())
+        if cands.size > 1:                              # a tie: the even code
+            best = int(cands[cands % 2 == 0][0])
+        single = best | (0x80 if p < 0 else 0)
+        assert single == code1 != code2
+
+
 # ----------------------------------------------------------------- forward --
 def test_forward_exact_rationals_tiny():
     rng = np.random.default_rng(5)
