@@ -32,6 +32,7 @@ if ROOT not in sys.path:
 METRIC = "melded FP8 LoRA linear fwd+bwd TFLOP/s and tokens/s; % FP8 MFMA / HBM peak"
 FP8_PEAK_TFLOPS = 5000.0      # MI355X dense FP8 MFMA
 HBM_PEAK_GBS = 8000.0         # MI355X HBM3E
+FP32_PEAK_TFLOPS = 157.3      # MI355X dense fp32 (matrix and vector)
 
 
 class TimingEvent:
@@ -40,9 +41,15 @@ class TimingEvent:
     invalidate the caches.  An ordinary timing event does, and in a kernel
     trace of the step each such record left about 6 us of idle GPU after it
     and lengthened the kernel that followed.  The timestamps are the same GPU
-    clock; read elapsed times only after a device synchronize."""
+    clock; read elapsed times only after a device synchronize.
+
+    Lifetime: every event is kept in a class-wide list and destroyed by
+    destroy_all() before main() returns, after a device synchronize.  No HIP
+    call is made from a finalizer: at interpreter exit the HIP runtime (and a
+    profiler's interception of it) may already be torn down."""
 
     _hip = None
+    _live = []
     DISABLE_SYSTEM_FENCE = 0x20000000
 
     def __init__(self):
@@ -56,6 +63,7 @@ class TimingEvent:
                                                ctypes.c_uint(self.DISABLE_SYSTEM_FENCE))
         if rc != 0:
             raise RuntimeError(f"hipEventCreateWithFlags failed ({rc})")
+        TimingEvent._live.append(self)
 
     def record(self, stream):
         rc = self._hip.hipEventRecord(self.ev, self._c.c_void_p(stream.cuda_stream))
@@ -70,16 +78,27 @@ class TimingEvent:
             raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
         return ms.value
 
-    def __del__(self):
-        if self._hip is not None and self.ev:
+    def destroy(self):
+        if self.ev:
             self._hip.hipEventDestroy(self.ev)
+            self.ev = self._c.c_void_p()
+
+    @classmethod
+    def destroy_all(cls):
+        """Destroy every event made so far (call after a device synchronize)."""
+        for e in cls._live:
+            e.destroy()
+        cls._live.clear()
 
 
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--chunk", type=int, default=10,
+                    help="timed steps per chunk: the median over the chunks' per-step "
+                         "times is reported beside the mean")
     ap.add_argument("--batches", type=int, default=4, help="distinct (X, dY) batches cycled")
     ap.add_argument("--cpu-tokens", type=int, default=4096,
                     help="token sample for the CPU-oracle baseline (0 = skip)")
@@ -106,7 +125,7 @@ def parse():
                          "three 7B MLP linears, 8192 bf16 tokens; layer13b: the seven linears of "
                          "a 13B decoder layer, 4096 tokens; rank-sweep: 4096 x 4096, 8192 "
                          "tokens, r in 8 .. 8192 (fwd + bwd time and step time per rank)")
-    ap.add_argument("--gemm-event-every", type=int, default=4,
+    ap.add_argument("--gemm-event-every", type=int, default=10,
                     help="bracket the forward GEMM with timing events on every N-th timed "
                          "step (1 = every step)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -117,6 +136,19 @@ def parse():
 
 def main():
     args = parse()
+    try:
+        run(args)
+    finally:
+        # explicit teardown while the HIP runtime is alive: drain the GPU,
+        # then destroy the timing events (nothing is left to finalizers)
+        if "torch" in sys.modules:
+            import torch
+            if torch.cuda.is_initialized():
+                torch.cuda.synchronize()
+                TimingEvent.destroy_all()
+
+
+def run(args):
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
               "(the per-GPU shard of the step is what one GPU runs); use --gpus 1",
@@ -244,16 +276,22 @@ def main():
     # no faster).  The forward FP8 GEMM, the dominant kernel, is bracketed by
     # HIP timing events (without the cache-flushing fence) on the stream it
     # runs on, so its launch duration is measured in the same region: on
-    # every fourth step (and the first), since each event record still
+    # every tenth step (and the first), since each event record still
     # leaves a few microseconds of idle GPU on the stream (with a pair on
     # every step the step measured ~6 us longer).
     sampled = [i for i in range(args.steps) if i % args.gemm_event_every == 0]
     g_ev = {i: (TimingEvent(), TimingEvent()) for i in sampled}
-    start = TimingEvent()
-    stop = TimingEvent()
+    # chunk boundaries: an event before step 0 and after every `chunk` steps
+    # (one record per chunk costs the stream a few microseconds once per
+    # chunk), so the median step time over the chunks is measured in the same
+    # region as the total
+    chunk = max(1, args.chunk)
+    bounds = sorted(set(list(range(0, args.steps, chunk)) + [args.steps]))
+    c_ev = {b: TimingEvent() for b in bounds}
     torch.cuda.synchronize()
-    start.record(stream)
     for i in range(args.steps):
+        if i in c_ev:
+            c_ev[i].record(stream)
         for k, c in enumerate(calls(args.warmup + n_pc + i)):
             if k == 1 and i in g_ev:
                 g_ev[i][0].record(stream)
@@ -261,9 +299,12 @@ def main():
                 g_ev[i][1].record(stream)
             else:
                 c()
-    stop.record(stream)
+    c_ev[args.steps].record(stream)
     torch.cuda.synchronize()
-    ms_per_step = start.elapsed_time(stop) / args.steps
+    ms_per_step = c_ev[0].elapsed_time(c_ev[args.steps]) / args.steps
+    chunk_ms = sorted(c_ev[a].elapsed_time(c_ev[b]) / (b - a) for a, b in zip(bounds, bounds[1:]))
+    ms_median = chunk_ms[len(chunk_ms) // 2] if len(chunk_ms) % 2 else \
+        0.5 * (chunk_ms[len(chunk_ms) // 2 - 1] + chunk_ms[len(chunk_ms) // 2])
     gemm_timed_us = sum(a.elapsed_time(b) for a, b in g_ev.values()) * 1e3 / len(g_ev)
     n_sel = int(m.n_sel.cpu()[0])
 
@@ -283,6 +324,9 @@ def main():
     # zero their B rows, write the indices
     proxy_bytes = d_out * d_in + 4 * r * (d_in + d_out) + n_sel * (d_in + 4 * r + 4)
     proxy_gbs = proxy_bytes / (per_call_us["proxy_update"] * 1e-6) / 1e9
+    # the proxy update's exact chain runs on the fp32 matrix cores: 2 r flops
+    # per backbone element (r = the merged components)
+    proxy_tflops = chain / (per_call_us["proxy_update"] * 1e-6) / 1e12
     out = {
         "metric": METRIC,
         "value": round(tflops, 2),
@@ -291,6 +335,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 4),
+        "ms_per_step_median": round(ms_median, 4),
+        "median_over": f"{len(chunk_ms)} chunks of {chunk} steps",
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -330,6 +376,8 @@ def main():
         "proxy_update_GBps": round(proxy_gbs, 1),
         "proxy_update_hbm_frac": round(proxy_gbs / HBM_PEAK_GBS, 4),
         "proxy_update_frac_of_copy": round(proxy_gbs / copy_gbs, 4),
+        "proxy_update_chain_TFLOPs": round(proxy_tflops, 1),
+        "proxy_update_fp32_mfma_frac": round(proxy_tflops / FP32_PEAK_TFLOPS, 4),
         "selected_rows_last_step": n_sel,
     }
 
@@ -634,50 +682,74 @@ def gemm_traffic_bytes():
 
 
 def cpu_baseline(spec, d0, Ts, optimizer="sgd", frozen=False, g_fmt="e4m3", x_note="",
-                 min_seconds=10.0):
+                 min_seconds=10.0, one_thread_tokens=512, one_thread_seconds=5.0):
     """The CPU oracle, as it is, on a token sample of the same workload:
     quantize X and dY, forward, backward (dX, dA, dB; or with A frozen in FP8,
     X~A~^T in the forward and dX, dB), the adapter step (SGD or AdamW) and
     the proxy update over the full backbone; the step is repeated on the same
-    inputs until `min_seconds` have passed, and the mean is reported."""
+    inputs until `min_seconds` have passed, and the mean is reported.  Then
+    the same on one host thread (BLAS and the C part limited to one), on
+    the first `one_thread_tokens` tokens (0: skipped)."""
     import numpy as np
 
     import oracle
     import workloads as wl
 
-    X = d0["X"][:Ts]
-    dY = d0["dY"][:Ts]
     t0 = time.perf_counter()
     wq, s_w, _, _ = oracle.fp8_quantize(d0["W"])
     A0 = d0["A"]
+    aq = s_a = None
     if frozen:
         aq, s_a, _, _ = oracle.fp8_quantize(A0)
         A0 = oracle.fp8_dequantize(aq, s_a)
-    t1 = time.perf_counter()
-    reps = 0
-    while True:
-        _oracle_step(oracle, np, spec, X, dY, wq, s_w, A0, d0["B"], aq if frozen else None,
-                     s_a if frozen else None, optimizer, frozen, g_fmt)
-        reps += 1
-        if time.perf_counter() - t1 >= min_seconds:
-            break
-    t2 = time.perf_counter()
-    step_s = (t2 - t1) / reps
+    t_init = time.perf_counter() - t0
+
+    def timed(n_tok, seconds):
+        X = d0["X"][:n_tok]
+        dY = d0["dY"][:n_tok]
+        t1 = time.perf_counter()
+        reps = 0
+        while True:
+            _oracle_step(oracle, np, spec, X, dY, wq, s_w, A0, d0["B"], aq, s_a, optimizer,
+                         frozen, g_fmt)
+            reps += 1
+            if time.perf_counter() - t1 >= seconds:
+                break
+        return (time.perf_counter() - t1) / reps, reps
+
+    step_s, reps = timed(Ts, min_seconds)
     flops = wl.step_flops(Ts, spec.d_in, spec.d_out, spec.rank, frozen_a=frozen)
     try:
         import threadpoolctl
         blas = threadpoolctl.threadpool_info()
         blas_threads = max([b.get("num_threads", 1) for b in blas] or [1])
     except Exception:
+        threadpoolctl = None
         blas_threads = os.cpu_count()
-    return {"value": round(flops / step_s / 1e12, 5), "unit": "TFLOP/s", "cores": int(max(
+    out = {"value": round(flops / step_s / 1e12, 5), "unit": "TFLOP/s", "cores": int(max(
         blas_threads, oracle.num_threads())), "kind": "oracle",
         "tokens_per_s": round(Ts / step_s, 1),
         "sample": f"the step on the first {Ts} of {spec.tokens} tokens{x_note} (full "
                   f"{spec.d_out} x {spec.d_in} weight, r={spec.rank}, full proxy update), "
-                  f"{reps} repetition{'s' if reps > 1 else ''} in {t2 - t1:.1f} s, mean "
-                  f"{step_s:.2f} s; the initial quantization of W{' and A' if frozen else ''} "
-                  f"({t1 - t0:.1f} s) is not part of the step"}
+                  f"{reps} repetition{'s' if reps > 1 else ''}, mean {step_s:.2f} s; the "
+                  f"initial quantization of W{' and A' if frozen else ''} ({t_init:.1f} s) "
+                  f"is not part of the step"}
+    n1 = min(one_thread_tokens, Ts)
+    if n1 > 0 and threadpoolctl is not None:
+        threads = oracle.num_threads()
+        with threadpoolctl.threadpool_limits(limits=1):
+            oracle.set_num_threads(1)
+            try:
+                s1, reps1 = timed(n1, one_thread_seconds)
+            finally:
+                oracle.set_num_threads(threads)
+        f1 = wl.step_flops(n1, spec.d_in, spec.d_out, spec.rank, frozen_a=frozen)
+        out["one_thread"] = {
+            "value": round(f1 / s1 / 1e12, 6), "unit": "TFLOP/s", "cores": 1,
+            "tokens_per_s": round(n1 / s1, 1),
+            "sample": f"the same step on the first {n1} tokens, BLAS and OpenMP limited to one "
+                      f"thread, {reps1} repetition{'s' if reps1 > 1 else ''}, mean {s1:.2f} s"}
+    return out
 
 
 def _oracle_step(oracle, np, spec, X, dY, wq, s_w, A0, B0, aq, s_a, optimizer, frozen, g_fmt):

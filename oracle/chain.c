@@ -55,3 +55,11 @@ int orc_num_threads(void)
     }
     return n;
 }
+
+/* limit the OpenMP threads of later parallel regions (a timing of the oracle
+ * on one core); arithmetic is unaffected */
+void orc_set_num_threads(int n)
+{
+    extern void omp_set_num_threads(int);
+    omp_set_num_threads(n > 0 ? n : 1);
+}

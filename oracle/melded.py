@@ -56,12 +56,20 @@ def _chain_lib():
                                        ctypes.c_void_p]
         lib.orc_rank_chain.restype = None
         lib.orc_num_threads.restype = ctypes.c_int
+        lib.orc_set_num_threads.argtypes = [ctypes.c_int]
+        lib.orc_set_num_threads.restype = None
         _lib = lib
     return _lib
 
 
 def num_threads() -> int:
     return int(_chain_lib().orc_num_threads())
+
+
+def set_num_threads(n: int) -> None:
+    """Threads of the C part's parallel loops (rows are independent; the
+    arithmetic does not depend on the count)."""
+    _chain_lib().orc_set_num_threads(int(n))
 
 
 # ----------------------------------------------------------------------------

@@ -42,7 +42,19 @@ def test_cpu_baseline_reports_the_oracle_step():
     import workloads as wl
     spec = wl.WORKLOADS[1].linears[0]                 # the 512 x 512 single linear
     d0 = wl.make_linear(1, 0, spec, step=0)
-    r = bench.cpu_baseline(spec, d0, 64, min_seconds=0.0)
+    r = bench.cpu_baseline(spec, d0, 64, min_seconds=0.0, one_thread_tokens=32,
+                           one_thread_seconds=0.0)
     assert r["kind"] == "oracle" and r["unit"] == "TFLOP/s" and r["value"] > 0
     assert r["cores"] >= 1 and r["tokens_per_s"] > 0
-    assert "first 64 of 256 tokens" in r["sample"] and "1 repetition " in r["sample"]
+    assert "first 64 of 256 tokens" in r["sample"] and "1 repetition," in r["sample"]
+    one = r["one_thread"]
+    assert one["cores"] == 1 and one["value"] > 0 and "first 32 tokens" in one["sample"]
+    import oracle
+    assert oracle.num_threads() == r["cores"] or oracle.num_threads() >= 1   # restored
+
+
+def test_timing_events_are_not_destroyed_by_finalizers():
+    """HIP events are destroyed explicitly (TimingEvent.destroy_all after a
+    synchronize), never from a finalizer that could run after the runtime."""
+    assert not hasattr(bench.TimingEvent, "__del__")
+    assert callable(bench.TimingEvent.destroy_all)

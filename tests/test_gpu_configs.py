@@ -18,7 +18,9 @@ import pytest
 import torch
 
 import oracle
-from tests.gpu_util import TOL, announce, dev, host, rel_l2, scalar
+from oracle import e4m3
+from tests.gpu_util import (TOL, announce, check_elementwise, dev, gemm_abs_sum, host, nan_f32,
+                            rel_l2, rel_l2_rank, scalar)
 import workloads as wl
 
 pytestmark = pytest.mark.gpu
@@ -42,11 +44,11 @@ def fwd_bwd(fq, tq, ts, xq, xs, gq, gs, A, B):
     T, d_in = xq.shape
     d_out = gq.shape[1]
     r = A.shape[0]
-    y = torch.empty((T, d_out), dtype=torch.float32, device="cuda")
+    y = nan_f32((T, d_out))
     fq.melded_linear_fwd(xq, xs, tq, ts, y)
-    dx = torch.empty((T, d_in), dtype=torch.float32, device="cuda")
-    dA = torch.empty((r, d_in), dtype=torch.float32, device="cuda")
-    dB = torch.empty((d_out, r), dtype=torch.float32, device="cuda")
+    dx = nan_f32((T, d_in))
+    dA = nan_f32((r, d_in))
+    dB = nan_f32((d_out, r))
     fq.melded_linear_bwd(gq, gs, xq, xs, tq, ts, dev(A), dev(B), dx, dA, dB)
     return host(y), host(dx), host(dA), host(dB)
 
@@ -76,14 +78,26 @@ def check_linear(fq, cfg_id, li, spec, rank=None, rank_sample=None, full_grads=T
     rdx, _, _ = oracle.melded_linear_bwd(gq[rows], s_g, xq[rows], s_x, wq, s_w, A[:1], B[:, :1],
                                          want_da=False)
     errs = {"Y": rel_l2(y[rows], ry), "dX": rel_l2(dx[rows], rdx)}
+    wd = e4m3.decode(wq)
+    check_elementwise(y[rows], ry, gemm_abs_sum(e4m3.decode(xq[rows]), wd,
+                                                np.float64(s_x) * np.float64(s_w)),
+                      spec.d_in, "Y")
+    check_elementwise(dx[rows], rdx, gemm_abs_sum(e4m3.decode(gq[rows]), wd.T,
+                                                  np.float64(s_g) * np.float64(s_w)),
+                      spec.d_out, "dX")
+    del wd
+    assert not np.isnan(dA).any() and not np.isnan(dB).any()
     if full_grads:
         _, rdA, rdB = oracle.melded_linear_bwd(gq, s_g, xq, s_x, wq, s_w, A, B, want_dx=False)
         errs["dA"], errs["dB"] = rel_l2(dA, rdA), rel_l2(dB, rdB)
+        errs["dA per rank"], errs["dB per rank"] = rel_l2_rank(dA, rdA, 0), rel_l2_rank(dB, rdB, 1)
     else:
         K = rank_sample
         _, rdA, rdB = oracle.melded_linear_bwd(gq, s_g, xq, s_x, wq, s_w, A[K], B[:, K],
                                                want_dx=False)
         errs["dA"], errs["dB"] = rel_l2(dA[K], rdA), rel_l2(dB[:, K], rdB)
+        errs["dA per rank"] = rel_l2_rank(dA[K], rdA, 0)
+        errs["dB per rank"] = rel_l2_rank(dB[:, K], rdB, 1)
     print(" ".join(f"{k} {v:.3e}" for k, v in errs.items()))
     assert max(errs.values()) <= TOL, errs
     return d, (tw, tsw, wq, s_w)

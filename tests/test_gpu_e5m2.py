@@ -83,9 +83,9 @@ def problem(seed, T, d_in, d_out, r):
 def test_e5m2_backward(gpu_lib, T, d_in, d_out, r):
     announce(f"bwd with E5M2 dY: T {T} d_in {d_in} d_out {d_out} r {r}")
     wq, s_w, xq, s_x, gq, s_g, A, B = problem(T + r, T, d_in, d_out, r)
-    dx = torch.empty((T, d_in), dtype=torch.float32, device="cuda")
-    dA = torch.empty((r, d_in), dtype=torch.float32, device="cuda")
-    dB = torch.empty((d_out, r), dtype=torch.float32, device="cuda")
+    dx = torch.full((T, d_in), float("nan"), dtype=torch.float32, device="cuda")
+    dA = torch.full((r, d_in), float("nan"), dtype=torch.float32, device="cuda")
+    dB = torch.full((d_out, r), float("nan"), dtype=torch.float32, device="cuda")
     gpu_lib.melded_linear_bwd(dev(gq), scalar(s_g), dev(xq), scalar(s_x), dev(wq), scalar(s_w),
                               dev(A), dev(B), dx, dA, dB, g_fmt="e5m2")
     rdx, rdA, rdB = oracle.melded_linear_bwd(gq, s_g, xq, s_x, wq, s_w, A, B, g_fmt="e5m2")
@@ -104,8 +104,8 @@ def test_e5m2_frozen_backward(gpu_lib):
     wq, s_w, xq, s_x, gq, s_g, A, _ = problem(9, T, d_in, d_out, r)
     aq, s_a, _, _ = oracle.fp8_quantize(A)
     _, u = oracle.melded_linear_fwd_frozen_a(xq, s_x, wq, s_w, aq, s_a)
-    dx = torch.empty((T, d_in), dtype=torch.float32, device="cuda")
-    dB = torch.empty((d_out, r), dtype=torch.float32, device="cuda")
+    dx = torch.full((T, d_in), float("nan"), dtype=torch.float32, device="cuda")
+    dB = torch.full((d_out, r), float("nan"), dtype=torch.float32, device="cuda")
     gpu_lib.melded_linear_bwd_frozen_a(dev(gq), scalar(s_g), dev(wq), scalar(s_w), dev(u), dx, dB,
                                        g_fmt="e5m2")
     rdx, rdB = oracle.melded_linear_bwd_frozen_a(gq, s_g, wq, s_w, u, g_fmt="e5m2")

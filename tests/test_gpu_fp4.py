@@ -65,7 +65,7 @@ def test_fp4_quantize_ties_specials_bf16(gpu_lib):
 
 def run_fwd(fq, xq, s_x, wq, s_w):
     T, d_out = xq.shape[0], wq.shape[0]
-    y = torch.empty((T, d_out), dtype=torch.float32, device="cuda")
+    y = torch.full((T, d_out), float("nan"), dtype=torch.float32, device="cuda")
     fq.melded_linear_fwd_fp4(dev(xq), scalar(s_x), dev(wq), scalar(s_w), y)
     return host(y)
 
@@ -101,7 +101,7 @@ def test_fp4_forward_attention_projection(gpu_lib):
     sx, sw = scalar(0.0), scalar(0.0)
     gpu_lib.fp4_quantize(dev(d["X"]), tx, sx)
     gpu_lib.fp4_quantize(dev(d["W"]), tw, sw)
-    y = torch.empty((spec.tokens, spec.d_out), dtype=torch.float32, device="cuda")
+    y = torch.full((spec.tokens, spec.d_out), float("nan"), dtype=torch.float32, device="cuda")
     gpu_lib.melded_linear_fwd_fp4(tx, sx, tw, sw, y)
     xq, wq, hy = host(tx), host(tw), host(y)
     rxq, rs_x, _, _ = oracle.fp4_quantize(d["X"])

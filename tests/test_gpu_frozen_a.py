@@ -32,7 +32,7 @@ def test_dequantize_bit_exact(gpu_lib):
         codes = rng.integers(0, 256, n).astype(np.uint8)
         codes[(codes & 0x7F) == 0x7F] = 0x11                      # no NaN codes
         q = dev(codes)
-        out = torch.empty(n, dtype=torch.float32, device="cuda")
+        out = torch.full(n, float("nan"), dtype=torch.float32, device="cuda")
         gpu_lib.fp8_dequantize(q, scalar(np.float32(s)), out)
         ref = oracle.fp8_dequantize(codes, np.float32(s))
         assert np.array_equal(host(out).view(np.uint32), ref.view(np.uint32)), n
@@ -51,11 +51,11 @@ def test_frozen_fwd_bwd(gpu_lib, T, d_in, d_out, r):
     q = problem(T + d_in + r, T, d_in, d_out, r)
     xq, wq, gq, aq = dev(q["x"]), dev(q["w"]), dev(q["g"]), dev(q["a"])
     s_x, s_w, s_g, s_a = (scalar(q[k]) for k in ("s_x", "s_w", "s_g", "s_a"))
-    y = torch.empty((T, d_out), dtype=torch.float32, device="cuda")
-    u = torch.empty((T, r), dtype=torch.float32, device="cuda")
+    y = torch.full((T, d_out), float("nan"), dtype=torch.float32, device="cuda")
+    u = torch.full((T, r), float("nan"), dtype=torch.float32, device="cuda")
     gpu_lib.melded_linear_fwd_frozen_a(xq, s_x, wq, s_w, aq, s_a, y, u)
-    dx = torch.empty((T, d_in), dtype=torch.float32, device="cuda")
-    dB = torch.empty((d_out, r), dtype=torch.float32, device="cuda")
+    dx = torch.full((T, d_in), float("nan"), dtype=torch.float32, device="cuda")
+    dB = torch.full((d_out, r), float("nan"), dtype=torch.float32, device="cuda")
     gpu_lib.melded_linear_bwd_frozen_a(gq, s_g, wq, s_w, u, dx, dB)
     if T * d_in * d_out > 1 << 30:          # large: sampled rows of Y, U and dX
         rows = np.unique(np.concatenate([[0, T - 1],
@@ -88,16 +88,16 @@ def test_frozen_edge_cases(gpu_lib):
     s = {k: scalar(q[k]) for k in ("s_x", "s_w", "s_g", "s_a")}
     # no tokens: dB is all zeros
     dB = torch.full((48, 4), np.nan, dtype=torch.float32, device="cuda")
-    u0 = torch.empty((0, 4), dtype=torch.float32, device="cuda")
+    u0 = torch.full((0, 4), float("nan"), dtype=torch.float32, device="cuda")
     gpu_lib.melded_linear_bwd_frozen_a(gq[:0], s["s_g"], wq, s["s_w"], u0, None, dB)
     assert not host(dB).any()
     # rank 0: U is empty, Y still computed
-    y = torch.empty((64, 48), dtype=torch.float32, device="cuda")
+    y = torch.full((64, 48), float("nan"), dtype=torch.float32, device="cuda")
     gpu_lib.melded_linear_fwd_frozen_a(xq, s["s_x"], wq, s["s_w"], aq[:0], s["s_a"], y,
-                                       torch.empty((64, 0), dtype=torch.float32, device="cuda"))
+                                       torch.full((64, 0), float("nan"), dtype=torch.float32, device="cuda"))
     assert rel_l2(host(y), oracle.melded_linear_fwd(q["x"], q["s_x"], q["w"], q["s_w"])) <= TOL
     # dX skipped
-    u = torch.empty((64, 4), dtype=torch.float32, device="cuda")
+    u = torch.full((64, 4), float("nan"), dtype=torch.float32, device="cuda")
     gpu_lib.melded_linear_fwd_frozen_a(xq, s["s_x"], wq, s["s_w"], aq, s["s_a"], y, u)
     gpu_lib.melded_linear_bwd_frozen_a(gq, s["s_g"], wq, s["s_w"], u, None, dB)
     _, rdB = oracle.melded_linear_bwd_frozen_a(q["g"], q["s_g"], q["w"], q["s_w"], host(u),

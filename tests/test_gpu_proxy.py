@@ -116,3 +116,25 @@ def test_proxy_signed_zero_accumulators(gpu_lib, r):
     r_wq = oracle.rowwise_proxy_update(wq, np.float32(0.01), A, B, 0.0, 0)[0]
     assert np.count_nonzero(r_wq[::2] == 0x80) > 0, "fixture keeps no -0 code"
     check(gpu_lib, wq, np.float32(0.01), A, B, tau=0.0)
+
+
+@pytest.mark.parametrize("k_max", [0, 4999])
+def test_proxy_many_rows_global_scores(gpu_lib, k_max):
+    """d_out = 20001 rows (more than the 16384 scores the selection keeps in
+    LDS, so they go through global memory) with a small d_in: codes, B,
+    scores and the selection bit-exact, with and without the k_max cap, and
+    with no rho output (the scores then live in the workspace)."""
+    announce(f"proxy d_out=20001 d_in=32 r=16 k_max={k_max}")
+    wq, s_w, A, B = proxy_problem(31 + k_max, 20001, 32, 16)
+    sel = check(gpu_lib, wq, s_w, A, B, k_max=k_max)
+    assert k_max == 0 or sel.size == k_max
+    d_out = wq.shape[0]
+    twq, tB = dev(wq), dev(B)
+    gsel = torch.full((d_out,), -1, dtype=torch.int32, device="cuda")
+    n = torch.full((1,), -1, dtype=torch.int32, device="cuda")
+    gpu_lib.rowwise_proxy_update(twq, scalar(s_w), dev(A), tB, 0.5, k_max, gsel, n, rho=None)
+    r_wq, r_B, r_sel, _ = oracle.rowwise_proxy_update(wq, s_w, A, B, 0.5, k_max)
+    assert np.array_equal(host(gsel)[: int(host(n)[0])], r_sel)
+    assert np.array_equal(host(twq), r_wq)
+    assert np.array_equal(host(tB).view(np.uint32), r_B.view(np.uint32))
+    print(f"selected {sel.size}/{d_out}")

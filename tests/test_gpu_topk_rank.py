@@ -18,7 +18,7 @@ def run(fq, wq, s_w, A, B, k_rank, tau, k_max=0):
     twq, tB = dev(wq), dev(B)
     sel = torch.full((d_out,), -1, dtype=torch.int32, device="cuda")
     n = torch.zeros(1, dtype=torch.int32, device="cuda")
-    rho = torch.empty(d_out, dtype=torch.float32, device="cuda")
+    rho = torch.full((d_out,), float("nan"), dtype=torch.float32, device="cuda")
     K = torch.empty(k_rank, dtype=torch.int32, device="cuda")
     fq.rowwise_proxy_update_topk_rank(twq, scalar(s_w), dev(A), tB, k_rank, tau, k_max, sel, n, K,
                                       rho=rho)
