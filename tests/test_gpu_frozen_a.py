@@ -32,7 +32,7 @@ def test_dequantize_bit_exact(gpu_lib):
         codes = rng.integers(0, 256, n).astype(np.uint8)
         codes[(codes & 0x7F) == 0x7F] = 0x11                      # no NaN codes
         q = dev(codes)
-        out = torch.full(n, float("nan"), dtype=torch.float32, device="cuda")
+        out = torch.full((n,), float("nan"), dtype=torch.float32, device="cuda")
         gpu_lib.fp8_dequantize(q, scalar(np.float32(s)), out)
         ref = oracle.fp8_dequantize(codes, np.float32(s))
         assert np.array_equal(host(out).view(np.uint32), ref.view(np.uint32)), n
