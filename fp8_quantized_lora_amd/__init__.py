@@ -25,7 +25,11 @@ __all__ = ["load", "FalqError", "fp8_quantize", "fp8_quantize_workspace_bytes",
            "melded_linear_bwd_fmt", "melded_linear_bwd_frozen_a_fmt", "FORMATS",
            "melded_linear_fwd_frozen_a_workspace_bytes", "melded_linear_bwd_frozen_a",
            "melded_linear_bwd_frozen_a_workspace_bytes", "rowwise_proxy_update_workspace_bytes",
-           "fp4_quantize", "melded_linear_fwd_fp4", "version", "LIB_PATH"]
+           "fp4_quantize", "melded_linear_fwd_fp4", "version", "LIB_PATH",
+           "fp8_quantize_noalloc", "QUANTIZE_SCRATCH_BYTES"]
+
+#: bytes of the per-device scratch array behind fp8_quantize_noalloc
+QUANTIZE_SCRATCH_BYTES = 16384
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfalqon.so")
 _lib = None
@@ -69,6 +73,7 @@ _SIGS = {
     "rowwise_proxy_update": (_i32, [_c_p, _c_p, _c_p, _c_p, _i64, _i64, _i64, _f32, _i64, _c_p,
                                     _c_p, _c_p, _c_p, _sz, _c_p]),
     "fp4_quantize": (_i32, [_c_p, _i32, _i64, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _sz, _c_p]),
+    "fp8_quantize_noalloc": (_i32, [_c_p, _i32, _i64, _i32, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p]),
     "melded_linear_fwd_fp4": (_i32, [_c_p, _c_p, _c_p, _c_p, _i64, _i64, _i64, _c_p, _c_p]),
 }
 
@@ -174,6 +179,26 @@ def fp8_quantize(x: torch.Tensor, q: torch.Tensor, scale: torch.Tensor,
 
 def fp8_quantize_fmt(x, q, scale, fmt: str, **kw) -> None:
     fp8_quantize(x, q, scale, fmt=fmt, **kw)
+
+
+def fp8_quantize_noalloc(x: torch.Tensor, q: torch.Tensor, scale: torch.Tensor,
+                         scale_in: Optional[torch.Tensor] = None,
+                         amax: Optional[torch.Tensor] = None,
+                         nonfinite: Optional[torch.Tensor] = None, stream=None,
+                         fmt: str = "e4m3") -> None:
+    """fp8_quantize with no workspace: the library's per-device scratch array
+    holds the amax partials (for callers that cannot allocate).  Calls that
+    overlap on one GPU race on that array."""
+    if x.dtype == torch.float32:
+        dt = 0
+    elif x.dtype == torch.bfloat16:
+        dt = 1
+    else:
+        raise FalqError("fp8_quantize_noalloc: x must be float32 or bfloat16")
+    _req(q, torch.uint8, x.shape, "q")
+    _check(load().fp8_quantize_noalloc(_ptr(x), dt, x.numel(), _fmt(fmt), _ptr(scale_in),
+                                       _ptr(q), _ptr(scale), _ptr(amax), _ptr(nonfinite),
+                                       _stream(stream)), "fp8_quantize_noalloc")
 
 
 def melded_linear_fwd(xq: torch.Tensor, s_x: torch.Tensor, wq: torch.Tensor, s_w: torch.Tensor,

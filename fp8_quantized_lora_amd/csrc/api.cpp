@@ -56,6 +56,9 @@ hipError_t run_dx(const uint8_t* gq, int g_fmt, const float* s_g, const uint8_t*
 
 inline bool fmt_ok(int f) { return f == FALQ_E4M3 || f == FALQ_E5M2; }
 
+static_assert(falq::kQuantizeScratchBytes == FALQ_QUANTIZE_SCRATCH_BYTES,
+              "the scratch size the header states");
+
 }  // namespace
 
 extern "C" {
@@ -93,6 +96,22 @@ falq_status fp8_quantize_fmt(const void* x, int dtype, int64_t n, int fmt, const
       (nonfinite && !aligned(nonfinite, 4)))
     return FALQ_EINVAL;
   if (!ws_ok(ws, ws_bytes, falq::quantize_ws_bytes())) return FALQ_EINVAL;
+  return hip_status(falq::launch_quantize(x, dtype, fmt, n, scale_in, q, scale, amax, nonfinite,
+                                          ws, reinterpret_cast<hipStream_t>(stream)));
+}
+
+falq_status fp8_quantize_noalloc(const void* x, int dtype, int64_t n, int fmt,
+                                 const float* scale_in, uint8_t* q, float* scale, float* amax,
+                                 int32_t* nonfinite, falq_stream stream) {
+  if (n < 0 || (dtype != FALQ_F32 && dtype != FALQ_BF16) || !fmt_ok(fmt)) return FALQ_EINVAL;
+  if (n > 0 && (!need(x) || !need(q))) return FALQ_EINVAL;
+  if (!scalar(scale) || (scale_in && !aligned(scale_in, 4)) || (amax && !aligned(amax, 4)) ||
+      (nonfinite && !aligned(nonfinite, 4)))
+    return FALQ_EINVAL;
+  // the scratch need does not grow with n (at most kQzMaxParts partials)
+  if (falq::quantize_ws_bytes() > falq::quantize_scratch_bytes()) return FALQ_EUNSUPPORTED;
+  void* ws = nullptr;
+  if (falq::quantize_scratch(&ws) != hipSuccess || ws == nullptr) return FALQ_EHIP;
   return hip_status(falq::launch_quantize(x, dtype, fmt, n, scale_in, q, scale, amax, nonfinite,
                                           ws, reinterpret_cast<hipStream_t>(stream)));
 }

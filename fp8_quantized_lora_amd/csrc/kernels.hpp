@@ -11,6 +11,11 @@ namespace falq {
 // ---- fp8_quantize: amax partials + cast ---------------------------------
 constexpr int kQzMaxParts = 2048;
 size_t quantize_ws_bytes();
+// the device address of this device's file-scope scratch array (looked up once
+// per device with hipGetSymbolAddress) and its size; quantize_ws_bytes() fits
+constexpr size_t kQuantizeScratchBytes = (size_t)kQzMaxParts * 8;
+size_t quantize_scratch_bytes();
+hipError_t quantize_scratch(void** out);
 // fmt 0: E4M3 (s = 448 / amax), 1: E5M2 (s = 57344 / amax), 2: FP4 E2M1
 // (s = 6 / amax; two codes per byte, the lower index in the low nibble; n even)
 hipError_t launch_quantize(const void* x, int dtype, int fmt, int64_t n, const float* scale_in,

@@ -22,6 +22,8 @@
 
 #include <float.h>
 
+#include <mutex>
+
 namespace falq {
 namespace {
 
@@ -308,6 +310,44 @@ hipError_t launch_quantize(const void* x, int dtype, int fmt, int64_t n, const f
   else FALQ_CAST(1, 2);
 #undef FALQ_CAST
   return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Scratch for callers that cannot allocate (fp8_quantize_noalloc): the amax
+// partials live in a file-scope device array instead of a caller workspace.
+// Each GPU the library runs on holds its own copy (kQzMaxParts * 8 bytes) for
+// the life of the process.  In host code `scratch` names a host-side stand-in,
+// not device memory: its device address comes from hipGetSymbolAddress, once
+// per device with that device current, and only that address is passed on.
+// Every call on a GPU shares that GPU's array, so calls that overlap on one
+// GPU (concurrent streams) race; stream-ordered calls do not.  Nothing in it
+// needs to start at zero: every amax workgroup writes its partial before the
+// cast launch reads it.
+// ---------------------------------------------------------------------------
+namespace {
+static __device__ __align__(256) uint8_t scratch[kQuantizeScratchBytes];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+size_t quantize_scratch_bytes() { return sizeof(scratch); }
+
+hipError_t quantize_scratch(void** out) {
+  *out = nullptr;
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 }  // namespace falq

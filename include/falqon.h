@@ -130,6 +130,26 @@ falq_status fp8_quantize_fmt(const void *x, int dtype, int64_t n, int fmt,
                              falq_stream stream);
 
 /*
+ * fp8_quantize_noalloc — fp8_quantize_fmt with no workspace argument, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc).  The amax partials
+ * live in a file-scope device array of FALQ_QUANTIZE_SCRATCH_BYTES that each
+ * GPU the library runs on holds until the process ends; the call itself
+ * allocates nothing (no hipMalloc, no hipFree).  The scratch need does not
+ * grow with n (at most 2048 partials whatever the size), so every n >= 0 that
+ * fp8_quantize accepts fits; FALQ_EUNSUPPORTED would report a build whose
+ * partials exceed the array.  All calls on one GPU share that GPU's array:
+ * calls that overlap on one GPU (concurrent streams) race; stream-ordered
+ * calls do not.  Nothing in the array needs clearing between calls.
+ * Arguments and errors as fp8_quantize_fmt; FALQ_EHIP if the device address
+ * of the array cannot be obtained.
+ */
+#define FALQ_QUANTIZE_SCRATCH_BYTES 16384
+falq_status fp8_quantize_noalloc(const void *x, int dtype, int64_t n, int fmt,
+                                 const float *scale_in, uint8_t *q, float *scale, float *amax,
+                                 int32_t *nonfinite, falq_stream stream);
+
+/*
  * fp4_quantize — the per-tensor current-scaled cast of fp8_quantize into FP4
  * E2M1 codes (the pages estimate an FP4 variant only from the FP4/FP8 matrix
  * throughput ratio, [rebuttal] thread 2 W2, Table R3; they give no FP4

@@ -188,3 +188,15 @@ def test_fp4_calls_reject_bad_arguments():
     assert lib.melded_linear_fwd_fp4(P, None, P, P, 8, 256, 32, P, None) == EINVAL        # s_x
     assert lib.melded_linear_fwd_fp4(P, P, P, P, 8, 256, 32, None, None) == EINVAL        # y
     assert lib.melded_linear_fwd_fp4(P, P, P, P, 0, 256, 32, P, None) == 0                # T = 0
+
+
+def test_quantize_noalloc_argument_errors():
+    """fp8_quantize_noalloc validates like fp8_quantize before any HIP call."""
+    lib = fq.load()
+    fake = ctypes.c_void_p(1 << 20)                 # never dereferenced
+    assert lib.fp8_quantize_noalloc(fake, 0, -1, 0, None, fake, fake, None, None, None) == EINVAL
+    assert lib.fp8_quantize_noalloc(fake, 7, 16, 0, None, fake, fake, None, None, None) == EINVAL
+    assert lib.fp8_quantize_noalloc(fake, 0, 16, 9, None, fake, fake, None, None, None) == EINVAL
+    assert lib.fp8_quantize_noalloc(None, 0, 16, 0, None, fake, fake, None, None, None) == EINVAL
+    assert lib.fp8_quantize_noalloc(fake, 0, 16, 0, None, fake, None, None, None, None) == EINVAL
+    assert fq.QUANTIZE_SCRATCH_BYTES >= fq.fp8_quantize_workspace_bytes(1 << 30)
