@@ -312,14 +312,17 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_nt_dma(
   auto frag = [&](const uint8_t* p) {
     return join(*reinterpret_cast<const uint4*>(p + p0), *reinterpret_cast<const uint4*>(p + p1));
   };
+  // The product is formed transposed, D = B A^T per 16 x 16 block (the
+  // MFMA's rows are C's columns), so that each lane ends with four
+  // consecutive columns of one row of C: one 16-byte store per block.
   auto mma = [&](const v8i& a, const v8i& b, v4f c) {
     if constexpr (FA == 4) {
       const v8i alo = {a[0], a[1], a[2], a[3], 0, 0, 0, 0}, ahi = {a[4], a[5], a[6], a[7], 0, 0, 0, 0};
       const v8i blo = {b[0], b[1], b[2], b[3], 0, 0, 0, 0}, bhi = {b[4], b[5], b[6], b[7], 0, 0, 0, 0};
-      c = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(alo, blo, c, 4, 4, 0, 0, 0, 0);
-      return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(ahi, bhi, c, 4, 4, 0, 0, 0, 0);
+      c = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(blo, alo, c, 4, 4, 0, 0, 0, 0);
+      return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bhi, ahi, c, 4, 4, 0, 0, 0, 0);
     } else {
-      return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, FA, 0, 0, 0, 0, 0);
+      return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(b, a, c, 0, FA, 0, 0, 0, 0);
     }
   };
   // No scalar load may be pending when the loop starts: the compiler then
@@ -368,24 +371,28 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_nt_dma(
     }
   }
 
-  const int rbase = m0 + wm * WTM + 4 * (lane >> 4);
-  const int cbase = n0 + wn * WTN + (lane & 15);
+  // lane l holds row r16 = l % 16 of each 16 x 16 block and its columns
+  // 4 (l / 16) .. 4 (l / 16) + 3
+  const int row0 = m0 + wm * WTM + r16;
+  const int col0 = n0 + wn * WTN + 4 * g;
 #pragma unroll
-  for (int i = 0; i < MB; ++i)
+  for (int i = 0; i < MB; ++i) {
+    const int row = row0 + i * 16;
+    if (row >= M) continue;
+    float* crow = C + (int64_t)row * ldc;
 #pragma unroll
     for (int j = 0; j < NB; ++j) {
-      const int col = cbase + j * 16;
-      if (col >= N) continue;
+      const int col = col0 + j * 16;
+      if (col >= N) continue;                 // N is a multiple of 16: all four or none
+      const v4f v = acc[i][j] * scale;
+      if constexpr (HALF) {
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int row = rbase + i * 16 + v;
-        if (row >= M) continue;
-        if constexpr (HALF)
-          unsafeAtomicAdd(C + (int64_t)row * ldc + col, acc[i][j][v] * scale);
-        else
-          C[(int64_t)row * ldc + col] = acc[i][j][v] * scale;
+        for (int e = 0; e < 4; ++e) unsafeAtomicAdd(crow + col + e, v[e]);
+      } else {
+        *reinterpret_cast<v4f*>(crow + col) = v;
       }
     }
+  }
   if (FU && wave_u) {
     const int rank = ub * UR + (lane & 15);
     if (rank < u.R) {
