@@ -125,6 +125,10 @@ def parse():
                          "three 7B MLP linears, 8192 bf16 tokens; layer13b: the seven linears of "
                          "a 13B decoder layer, 4096 tokens; rank-sweep: 4096 x 4096, 8192 "
                          "tokens, r in 8 .. 8192 (fwd + bwd time and step time per rank)")
+    ap.add_argument("--compare-paths", action="store_true",
+                    help="with --workload rank-sweep: also time the separate-path FP8 LoRA "
+                         "layer and the bf16 LoRA layer at every rank (fwd + bwd), and the FP8 "
+                         "backbone alone")
     ap.add_argument("--gemm-event-every", type=int, default=10,
                     help="bracket the forward GEMM with timing events on every N-th timed "
                          "step (1 = every step)")
@@ -511,6 +515,49 @@ def layer_workload(args, torch, fq, wl):
     return out
 
 
+def compare_paths(torch, fq, m, X, dY, args, stream, melded_ms):
+    """fwd+bwd times of the FP8 backbone alone, of the separate-path FP8 LoRA
+    layer and of the bf16 LoRA layer, on the melded layer m's inputs."""
+    T, d_in, d_out, r = m.T, m.d_in, m.d_out, m.r
+    dev = m.wq.device
+    u8, f32 = torch.uint8, torch.float32
+    e_in = torch.empty((0, d_in), dtype=f32, device=dev)
+    e_out = torch.empty((d_out, 0), dtype=f32, device=dev)
+    qx = lambda: fq.fp8_quantize(X, m.xq, m.s_x, ws=m.ws_q, stream=stream)  # noqa: E731
+    qg = lambda: fq.fp8_quantize(dY, m.gq, m.s_g, ws=m.ws_q, stream=stream)  # noqa: E731
+    fwd = lambda: fq.melded_linear_fwd(m.xq, m.s_x, m.wq, m.s_w, m.y, stream=stream)  # noqa: E731
+    base = [qx, fwd, qg, lambda: fq.melded_linear_bwd(m.gq, m.s_g, m.xq, m.s_x, m.wq, m.s_w,
+                                                       e_in, e_out, m.dx, e_in, e_out,
+                                                       ws=m.ws_bwd, stream=stream)]
+    sv = torch.empty(fq.lora_separate_fp8_saved_bytes(T, d_in, d_out, r), dtype=u8, device=dev)
+    wsv = torch.empty(fq.lora_separate_fp8_workspace_bytes(T, d_in, d_out, r), dtype=u8,
+                      device=dev)
+    sep = [qx, lambda: fq.lora_separate_fp8_fwd(m.xq, m.s_x, m.wq, m.s_w, m.A, m.B, m.y, sv,
+                                                ws=wsv, stream=stream),
+           qg, lambda: fq.lora_separate_fp8_bwd(m.gq, m.s_g, m.xq, m.s_x, m.wq, m.s_w, sv, r,
+                                                m.dx, m.dA, m.dB, ws=wsv, stream=stream)]
+    Xf = X.float() if X.dtype != torch.float32 else X
+    sb = torch.empty(fq.lora_bf16_saved_bytes(T, d_in, d_out, r), dtype=u8, device=dev)
+    wsb = torch.empty(fq.lora_bf16_workspace_bytes(T, d_in, d_out, r), dtype=u8, device=dev)
+    bf = [qx, lambda: fq.lora_bf16_fwd(Xf, m.xq, m.s_x, m.wq, m.s_w, m.A, m.B, m.y, sb, ws=wsb,
+                                       stream=stream),
+          qg, lambda: fq.lora_bf16_bwd(dY, m.gq, m.s_g, Xf, m.wq, m.s_w, m.A, m.B, sb, m.dx,
+                                       m.dA, m.dB, ws=wsb, stream=stream)]
+    res = {}
+    for name, cl in (("backbone", base), ("separate_fp8", sep), ("bf16", bf)):
+        ms, _ = _timed(torch, args.steps, args.warmup,
+                       lambda i, ev: _run_calls(cl, None, stream), stream, gemm=False)
+        res[name] = ms
+    del sv, wsv, sb, wsb
+    return {"backbone_fwd_bwd_ms": round(res["backbone"], 4),
+            "separate_fp8_fwd_bwd_ms": round(res["separate_fp8"], 4),
+            "bf16_fwd_bwd_ms": round(res["bf16"], 4),
+            "melded_adapter_ms": round(melded_ms - res["backbone"], 4),
+            "separate_fp8_adapter_ms": round(res["separate_fp8"] - res["backbone"], 4),
+            "bf16_adapter_ms": round(res["bf16"] - res["backbone"], 4),
+            "melded_over_separate_speedup": round(res["separate_fp8"] / melded_ms, 3)}
+
+
 def rank_sweep(args, torch, fq, wl):
     """W 4096 x 4096, 8192 tokens, r in 8, 64, 512, 2048, 8192: per rank the
     forward + backward time (quantize X, forward, quantize dY, backward) and
@@ -534,16 +581,24 @@ def rank_sweep(args, torch, fq, wl):
         fb_flops = 4 * T * spec.d_in * spec.d_out + 4 * T * r * (spec.d_in + spec.d_out)
         flops = wl.step_flops(T, spec.d_in, spec.d_out, r)
         n_sel = int(m.n_sel.cpu()[0])
-        points.append({"rank": r, "fwd_bwd_ms": round(fb_ms, 4), "step_ms": round(ms, 4),
-                       "fwd_bwd_TFLOPs": round(fb_flops / (fb_ms * 1e-3) / 1e12, 1),
-                       "step_TFLOPs": round(flops / (ms * 1e-3) / 1e12, 1),
-                       "fwd_gemm_us": round(gemm_us, 2),
-                       "selected_rows_last_step": n_sel})
+        point = {"rank": r, "fwd_bwd_ms": round(fb_ms, 4), "step_ms": round(ms, 4),
+                 "fwd_bwd_TFLOPs": round(fb_flops / (fb_ms * 1e-3) / 1e12, 1),
+                 "step_TFLOPs": round(flops / (ms * 1e-3) / 1e12, 1),
+                 "fwd_gemm_us": round(gemm_us, 2),
+                 "selected_rows_last_step": n_sel}
+        if args.compare_paths:
+            point.update(compare_paths(torch, fq, m, X, dY, args, stream, fb_ms))
+        points.append(point)
         if r == 64:
             line = (ms, gemm_us, d, spec)
         del m, X, dY, d, calls
         torch.cuda.synchronize()
         torch.cuda.empty_cache()
+    if args.compare_paths:
+        # the smallest rank from which the FP8 branch (separate path) costs
+        # less than the bf16 one
+        tp = [q["rank"] for q in points if q["separate_fp8_adapter_ms"] < q["bf16_adapter_ms"]]
+        turning = tp[0] if tp else None
     ms, gemm_us, d64, spec64 = line
     T = spec64.tokens
     gemm_tf = 2 * T * spec64.d_in * spec64.d_out / (gemm_us * 1e-6) / 1e12
@@ -566,6 +621,14 @@ def rank_sweep(args, torch, fq, wl):
         "sweep": points,
         "launch": "eager launches on one HIP stream",
     }
+    if args.compare_paths:
+        out["fp8_vs_bf16_adapter_turning_rank"] = turning
+        out["compare_paths_note"] = (
+            "fwd+bwd of one layer (both quantizes, forward, backward) on the same inputs: "
+            "melded (the adapter inside the FP8 backbone), separate-path FP8 LoRA (adapter "
+            "branch with its own E4M3 quantizes, FP8 matrix cores) and bf16 LoRA (adapter "
+            "branch in bfloat16); *_adapter_ms = the path's time minus the FP8 backbone alone "
+            "(quantizes, forward GEMM, dX)")
     if not args.no_cpu_baseline and args.cpu_tokens > 0:
         out["cpu_baseline"] = cpu_baseline(spec64, d64, min(args.cpu_tokens, 1024))
     return out

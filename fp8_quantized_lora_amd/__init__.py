@@ -26,7 +26,10 @@ __all__ = ["load", "FalqError", "fp8_quantize", "fp8_quantize_workspace_bytes",
            "melded_linear_fwd_frozen_a_workspace_bytes", "melded_linear_bwd_frozen_a",
            "melded_linear_bwd_frozen_a_workspace_bytes", "rowwise_proxy_update_workspace_bytes",
            "fp4_quantize", "melded_linear_fwd_fp4", "version", "LIB_PATH",
-           "fp8_quantize_noalloc", "QUANTIZE_SCRATCH_BYTES"]
+           "fp8_quantize_noalloc", "QUANTIZE_SCRATCH_BYTES",
+           "lora_separate_fp8_saved_bytes", "lora_separate_fp8_workspace_bytes",
+           "lora_separate_fp8_fwd", "lora_separate_fp8_bwd", "lora_bf16_saved_bytes",
+           "lora_bf16_workspace_bytes", "lora_bf16_fwd", "lora_bf16_bwd"]
 
 #: bytes of the per-device scratch array behind fp8_quantize_noalloc
 QUANTIZE_SCRATCH_BYTES = 16384
@@ -75,6 +78,18 @@ _SIGS = {
     "fp4_quantize": (_i32, [_c_p, _i32, _i64, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _sz, _c_p]),
     "fp8_quantize_noalloc": (_i32, [_c_p, _i32, _i64, _i32, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p]),
     "melded_linear_fwd_fp4": (_i32, [_c_p, _c_p, _c_p, _c_p, _i64, _i64, _i64, _c_p, _c_p]),
+    "lora_separate_fp8_saved_bytes": (_sz, [_i64, _i64, _i64, _i64]),
+    "lora_separate_fp8_workspace_bytes": (_sz, [_i64, _i64, _i64, _i64]),
+    "lora_separate_fp8_fwd": (_i32, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _i64, _i64, _i64, _i64,
+                                     _c_p, _c_p, _sz, _c_p, _sz, _c_p]),
+    "lora_separate_fp8_bwd": (_i32, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _sz, _i64, _i64,
+                                     _i64, _i64, _c_p, _c_p, _c_p, _c_p, _sz, _c_p]),
+    "lora_bf16_saved_bytes": (_sz, [_i64, _i64, _i64, _i64]),
+    "lora_bf16_workspace_bytes": (_sz, [_i64, _i64, _i64, _i64]),
+    "lora_bf16_fwd": (_i32, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _i64, _i64, _i64, _i64,
+                             _c_p, _c_p, _sz, _c_p, _sz, _c_p]),
+    "lora_bf16_bwd": (_i32, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _sz, _i64,
+                             _i64, _i64, _i64, _c_p, _c_p, _c_p, _c_p, _sz, _c_p]),
 }
 
 
@@ -426,6 +441,101 @@ def rowwise_proxy_update_topk_rank(wq, s_w, A, B, k_rank: int, tau: float, k_max
         _ptr(wq), _ptr(s_w), _ptr(A), _ptr(B), d_in, d_out, r, k_rank, tau, k_max, _ptr(sel_idx),
         _ptr(n_sel), _ptr(rho), _ptr(comp_idx), _ptr(ws), ws.numel(), _stream(stream)),
         "rowwise_proxy_update_topk_rank")
+
+
+# ---------------------------------------------------------------------------
+# the baselines: LoRA with a separate adapter branch (separate-path FP8, bf16)
+def lora_separate_fp8_saved_bytes(T: int, d_in: int, d_out: int, r: int) -> int:
+    return int(load().lora_separate_fp8_saved_bytes(T, d_in, d_out, r))
+
+
+def lora_separate_fp8_workspace_bytes(T: int, d_in: int, d_out: int, r: int) -> int:
+    return int(load().lora_separate_fp8_workspace_bytes(T, d_in, d_out, r))
+
+
+def lora_bf16_saved_bytes(T: int, d_in: int, d_out: int, r: int) -> int:
+    return int(load().lora_bf16_saved_bytes(T, d_in, d_out, r))
+
+
+def lora_bf16_workspace_bytes(T: int, d_in: int, d_out: int, r: int) -> int:
+    return int(load().lora_bf16_workspace_bytes(T, d_in, d_out, r))
+
+
+def _buf(t, nbytes, device, name):
+    if t is None:
+        return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+    if t.numel() * t.element_size() < nbytes:
+        raise FalqError(f"{name}: needs {nbytes} bytes")
+    return t
+
+
+def lora_separate_fp8_fwd(xq, s_x, wq, s_w, A, B, y, saved, ws=None, stream=None) -> None:
+    """Y = X^ W^^T + Q(X^ Q(A)^T)^ Q(B)^^T: the layer with a separate FP8 LoRA
+    branch; `saved` (lora_separate_fp8_saved_bytes, uint8) keeps A~, B~, U~
+    and their scales for the backward."""
+    T, d_in = xq.shape
+    d_out = wq.shape[0]
+    r = A.shape[0]
+    _req(wq, torch.uint8, (d_out, d_in), "wq")
+    _req(A, torch.float32, (r, d_in), "A")
+    _req(B, torch.float32, (d_out, r), "B")
+    _req(y, torch.float32, (T, d_out), "y")
+    ws = _buf(ws, lora_separate_fp8_workspace_bytes(T, d_in, d_out, r), xq.device, "ws")
+    _check(load().lora_separate_fp8_fwd(_ptr(xq), _ptr(s_x), _ptr(wq), _ptr(s_w), _ptr(A),
+                                        _ptr(B), T, d_in, d_out, r, _ptr(y), _ptr(saved),
+                                        saved.numel() * saved.element_size(), _ptr(ws),
+                                        ws.numel(), _stream(stream)), "lora_separate_fp8_fwd")
+
+
+def lora_separate_fp8_bwd(gq, s_g, xq, s_x, wq, s_w, saved, r: int, dx, dA, dB, ws=None,
+                          stream=None) -> None:
+    """dX, dA, dB of the separate-path FP8 LoRA layer from the forward's `saved`."""
+    T, d_out = gq.shape
+    d_in = xq.shape[1]
+    _req(dx, torch.float32, (T, d_in), "dx")
+    _req(dA, torch.float32, (r, d_in), "dA")
+    _req(dB, torch.float32, (d_out, r), "dB")
+    ws = _buf(ws, lora_separate_fp8_workspace_bytes(T, d_in, d_out, r), gq.device, "ws")
+    _check(load().lora_separate_fp8_bwd(_ptr(gq), _ptr(s_g), _ptr(xq), _ptr(s_x), _ptr(wq),
+                                        _ptr(s_w), _ptr(saved),
+                                        saved.numel() * saved.element_size(), T, d_in, d_out, r,
+                                        _ptr(dx), _ptr(dA), _ptr(dB), _ptr(ws), ws.numel(),
+                                        _stream(stream)), "lora_separate_fp8_bwd")
+
+
+def lora_bf16_fwd(x, xq, s_x, wq, s_w, A, B, y, saved, ws=None, stream=None) -> None:
+    """Y = X^ W^^T + bf(bf(X) bf(A)^T) bf(B)^T: the FP8 backbone with a bf16
+    LoRA branch; `saved` (lora_bf16_saved_bytes) keeps bf(U)."""
+    T, d_in = xq.shape
+    d_out = wq.shape[0]
+    r = A.shape[0]
+    _req(x, torch.float32, (T, d_in), "x")
+    _req(A, torch.float32, (r, d_in), "A")
+    _req(B, torch.float32, (d_out, r), "B")
+    _req(y, torch.float32, (T, d_out), "y")
+    ws = _buf(ws, lora_bf16_workspace_bytes(T, d_in, d_out, r), xq.device, "ws")
+    _check(load().lora_bf16_fwd(_ptr(x), _ptr(xq), _ptr(s_x), _ptr(wq), _ptr(s_w), _ptr(A),
+                                _ptr(B), T, d_in, d_out, r, _ptr(y), _ptr(saved),
+                                saved.numel() * saved.element_size(), _ptr(ws), ws.numel(),
+                                _stream(stream)), "lora_bf16_fwd")
+
+
+def lora_bf16_bwd(dy, gq, s_g, x, wq, s_w, A, B, saved, dx, dA, dB, ws=None,
+                  stream=None) -> None:
+    """dX, dA, dB of the bf16 LoRA layer from the forward's `saved`."""
+    T, d_out = gq.shape
+    d_in = x.shape[1]
+    r = A.shape[0]
+    _req(dy, torch.float32, (T, d_out), "dy")
+    _req(dx, torch.float32, (T, d_in), "dx")
+    _req(dA, torch.float32, (r, d_in), "dA")
+    _req(dB, torch.float32, (d_out, r), "dB")
+    ws = _buf(ws, lora_bf16_workspace_bytes(T, d_in, d_out, r), gq.device, "ws")
+    _check(load().lora_bf16_bwd(_ptr(dy), _ptr(gq), _ptr(s_g), _ptr(x), _ptr(wq), _ptr(s_w),
+                                _ptr(A), _ptr(B), _ptr(saved),
+                                saved.numel() * saved.element_size(), T, d_in, d_out, r,
+                                _ptr(dx), _ptr(dA), _ptr(dB), _ptr(ws), ws.numel(),
+                                _stream(stream)), "lora_bf16_bwd")
 
 
 from .step import MeldedLinear  # noqa: E402  (buffers + the step's call sequence)

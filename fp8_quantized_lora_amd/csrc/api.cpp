@@ -163,7 +163,9 @@ falq_status melded_linear_fwd(const uint8_t* xq, const float* s_x, const uint8_t
 size_t melded_linear_bwd_workspace_bytes(int64_t T, int64_t d_in, int64_t d_out, int64_t r) {
   if (T < 0 || d_in < 0 || d_out < 0 || r < 0) return 0;
   const size_t wt = align_up((size_t)d_in * (size_t)d_out, 256);      // W~^T for dX
-  return wt + falq::adapter_grad_ws_bytes(T, d_in, d_out, r);
+  return wt + (falq::adapter_wide_route(T, d_in, d_out, r)
+                   ? falq::adapter_wide_ws_bytes(T, d_in, d_out, r)
+                   : falq::adapter_grad_ws_bytes(T, d_in, d_out, r));
 }
 
 falq_status melded_linear_bwd(const uint8_t* gq, const float* s_g, const uint8_t* xq,
@@ -200,8 +202,11 @@ falq_status melded_linear_bwd_fmt(const uint8_t* gq, int g_fmt, const float* s_g
   // W~^T (for dX) and the adapter operands' bf16 splits in one launch
   const bool gemm_dx = dx && T * d_in > 0 && d_out > 0;
   const bool grads = r > 0 && T > 0 && d_in > 0 && d_out > 0;
-  if (falq::launch_bwd_prep(wq, gemm_dx ? base : nullptr, A, B, T, d_in, d_out, grads ? r : 0,
-                            dA != nullptr, base + wt_bytes, s) != hipSuccess)
+  // large ranks contract through the full weight gradient instead
+  const bool wide = grads && falq::adapter_wide_route(T, d_in, d_out, r);
+  if (falq::launch_bwd_prep(wq, gemm_dx ? base : nullptr, A, B, T, d_in, d_out,
+                            grads && !wide ? r : 0, dA != nullptr, base + wt_bytes,
+                            s) != hipSuccess)
     return FALQ_EHIP;
   hipError_t e = hipSuccess;
   if (gemm_dx)
@@ -214,6 +219,9 @@ falq_status melded_linear_bwd_fmt(const uint8_t* gq, int g_fmt, const float* s_g
     if (d_in == 0 || d_out == 0) {
       if (d_out > 0) e = falq::launch_fill_f32(dB, d_out * r, 0.0f, s);
       if (e == hipSuccess && dA && d_in > 0) e = falq::launch_fill_f32(dA, r * d_in, 0.0f, s);
+    } else if (wide) {
+      e = falq::launch_adapter_grads_wide(gq, g_fmt, s_g, xq, s_x, A, B, T, d_in, d_out, r, dA,
+                                          dB, base + wt_bytes, s);
     } else {
       e = falq::launch_adapter_grads(gq, s_g, xq, s_x, A, B, T, d_in, d_out, r, dA, dB,
                                      base + wt_bytes, s, g_fmt, /*presplit=*/grads);
@@ -382,6 +390,132 @@ falq_status rowwise_proxy_update_topk_rank(uint8_t* wq, const float* s_w, const 
   return hip_status(falq::launch_proxy_update_topk_rank(
       wq, s_w, A, B, d_in, d_out, r, k_rank, tau, k_max, sel_idx, n_sel, rho, comp_idx, ws,
       reinterpret_cast<hipStream_t>(stream)));
+}
+
+// ---- the baselines: LoRA with a separate adapter branch ----------------------
+
+namespace {
+bool sep_dims_ok(int64_t T, int64_t d_in, int64_t d_out, int64_t r) {
+  const int64_t r16 = (r + 15) / 16 * 16;      // the rank padded to 16 in the products
+  return gemm_dims_ok(T, d_in, d_out) && T % 16 == 0 && r >= 0 && r % 8 == 0 &&
+         r <= ((int64_t)1 << 20) && gemm_dims_ok(T, d_in, r16) && gemm_dims_ok(T, r16, d_out);
+}
+bool bf16_dims_ok(int64_t T, int64_t d_in, int64_t d_out, int64_t r) {
+  return sep_dims_ok(T, d_in, d_out, r) && T % 64 == 0 && d_in % 64 == 0 && d_out % 64 == 0;
+}
+}  // namespace
+
+size_t lora_separate_fp8_saved_bytes(int64_t T, int64_t d_in, int64_t d_out, int64_t r) {
+  if (!sep_dims_ok(T, d_in, d_out, r)) return 0;
+  return falq::lora_sep_saved_bytes(T, d_in, d_out, r);
+}
+
+size_t lora_separate_fp8_workspace_bytes(int64_t T, int64_t d_in, int64_t d_out, int64_t r) {
+  if (!sep_dims_ok(T, d_in, d_out, r)) return 0;
+  return falq::lora_sep_ws_bytes(T, d_in, d_out, r);
+}
+
+falq_status lora_separate_fp8_fwd(const uint8_t* xq, const float* s_x, const uint8_t* wq,
+                                  const float* s_w, const float* A, const float* B, int64_t T,
+                                  int64_t d_in, int64_t d_out, int64_t r, float* y, void* saved,
+                                  size_t saved_bytes, void* ws, size_t ws_bytes,
+                                  falq_stream stream) {
+  if (!sep_dims_ok(T, d_in, d_out, r)) return FALQ_EINVAL;
+  if (!scalar(s_x) || !scalar(s_w)) return FALQ_EINVAL;
+  if (T * d_in > 0 && !need(xq)) return FALQ_EINVAL;
+  if (d_out * d_in > 0 && !need(wq)) return FALQ_EINVAL;
+  if (T * d_out > 0 && !need(y)) return FALQ_EINVAL;
+  if (r * d_in > 0 && !need(A)) return FALQ_EINVAL;
+  if (r * d_out > 0 && !need(B)) return FALQ_EINVAL;
+  if (!ws_ok(saved, saved_bytes, falq::lora_sep_saved_bytes(T, d_in, d_out, r)) ||
+      !ws_ok(ws, ws_bytes, falq::lora_sep_ws_bytes(T, d_in, d_out, r)))
+    return FALQ_EINVAL;
+  if (T == 0 || d_out == 0 || d_in == 0) return melded_linear_fwd(xq, s_x, wq, s_w, T, d_in, d_out, y, stream);
+  return hip_status(falq::launch_lora_sep_fwd(xq, s_x, wq, s_w, A, B, T, d_in, d_out, r, y,
+                                              saved, ws, reinterpret_cast<hipStream_t>(stream)));
+}
+
+falq_status lora_separate_fp8_bwd(const uint8_t* gq, const float* s_g, const uint8_t* xq,
+                                  const float* s_x, const uint8_t* wq, const float* s_w,
+                                  void* saved, size_t saved_bytes, int64_t T, int64_t d_in,
+                                  int64_t d_out, int64_t r, float* dx, float* dA, float* dB,
+                                  void* ws, size_t ws_bytes, falq_stream stream) {
+  if (!sep_dims_ok(T, d_in, d_out, r)) return FALQ_EINVAL;
+  if (!scalar(s_g) || !scalar(s_x) || !scalar(s_w)) return FALQ_EINVAL;
+  if (T * d_out > 0 && !need(gq)) return FALQ_EINVAL;
+  if (T * d_in > 0 && (!need(xq) || !need(dx))) return FALQ_EINVAL;
+  if (d_out * d_in > 0 && !need(wq)) return FALQ_EINVAL;
+  if (r * d_in > 0 && !need(dA)) return FALQ_EINVAL;
+  if (r * d_out > 0 && !need(dB)) return FALQ_EINVAL;
+  if (!ws_ok(saved, saved_bytes, falq::lora_sep_saved_bytes(T, d_in, d_out, r)) ||
+      !ws_ok(ws, ws_bytes, falq::lora_sep_ws_bytes(T, d_in, d_out, r)))
+    return FALQ_EINVAL;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (T == 0 || d_in == 0 || d_out == 0) {
+    hipError_t e = hipSuccess;
+    if (T * d_in > 0) e = falq::launch_fill_f32(dx, T * d_in, 0.0f, s);
+    if (e == hipSuccess) e = falq::launch_fill_f32(dA, r * d_in, 0.0f, s);
+    if (e == hipSuccess) e = falq::launch_fill_f32(dB, d_out * r, 0.0f, s);
+    return hip_status(e);
+  }
+  return hip_status(falq::launch_lora_sep_bwd(gq, s_g, xq, s_x, wq, s_w, saved, T, d_in, d_out, r,
+                                              dx, dA, dB, ws, s));
+}
+
+size_t lora_bf16_saved_bytes(int64_t T, int64_t d_in, int64_t d_out, int64_t r) {
+  if (!bf16_dims_ok(T, d_in, d_out, r)) return 0;
+  return falq::lora_bf16_saved_bytes(T, r);
+}
+
+size_t lora_bf16_workspace_bytes(int64_t T, int64_t d_in, int64_t d_out, int64_t r) {
+  if (!bf16_dims_ok(T, d_in, d_out, r)) return 0;
+  return falq::lora_bf16_ws_bytes(T, d_in, d_out, r);
+}
+
+falq_status lora_bf16_fwd(const float* x, const uint8_t* xq, const float* s_x, const uint8_t* wq,
+                          const float* s_w, const float* A, const float* B, int64_t T,
+                          int64_t d_in, int64_t d_out, int64_t r, float* y, void* saved,
+                          size_t saved_bytes, void* ws, size_t ws_bytes, falq_stream stream) {
+  if (!bf16_dims_ok(T, d_in, d_out, r)) return FALQ_EINVAL;
+  if (!scalar(s_x) || !scalar(s_w)) return FALQ_EINVAL;
+  if (T * d_in > 0 && (!need(xq) || !need(x))) return FALQ_EINVAL;
+  if (d_out * d_in > 0 && !need(wq)) return FALQ_EINVAL;
+  if (T * d_out > 0 && !need(y)) return FALQ_EINVAL;
+  if (r * d_in > 0 && !need(A)) return FALQ_EINVAL;
+  if (r * d_out > 0 && !need(B)) return FALQ_EINVAL;
+  if (!ws_ok(saved, saved_bytes, falq::lora_bf16_saved_bytes(T, r)) ||
+      !ws_ok(ws, ws_bytes, falq::lora_bf16_ws_bytes(T, d_in, d_out, r)))
+    return FALQ_EINVAL;
+  if (T == 0 || d_out == 0 || d_in == 0) return melded_linear_fwd(xq, s_x, wq, s_w, T, d_in, d_out, y, stream);
+  return hip_status(falq::launch_lora_bf16_fwd(x, xq, s_x, wq, s_w, A, B, T, d_in, d_out, r, y,
+                                               saved, ws, reinterpret_cast<hipStream_t>(stream)));
+}
+
+falq_status lora_bf16_bwd(const float* dy, const uint8_t* gq, const float* s_g, const float* x,
+                          const uint8_t* wq, const float* s_w, const float* A, const float* B,
+                          const void* saved, size_t saved_bytes, int64_t T, int64_t d_in,
+                          int64_t d_out, int64_t r, float* dx, float* dA, float* dB, void* ws,
+                          size_t ws_bytes, falq_stream stream) {
+  if (!bf16_dims_ok(T, d_in, d_out, r)) return FALQ_EINVAL;
+  if (!scalar(s_g) || !scalar(s_w)) return FALQ_EINVAL;
+  if (T * d_out > 0 && (!need(gq) || !need(dy))) return FALQ_EINVAL;
+  if (T * d_in > 0 && (!need(x) || !need(dx))) return FALQ_EINVAL;
+  if (d_out * d_in > 0 && !need(wq)) return FALQ_EINVAL;
+  if (r * d_in > 0 && (!need(A) || !need(dA))) return FALQ_EINVAL;
+  if (r * d_out > 0 && (!need(B) || !need(dB))) return FALQ_EINVAL;
+  if (!ws_ok(saved, saved_bytes, falq::lora_bf16_saved_bytes(T, r)) ||
+      !ws_ok(ws, ws_bytes, falq::lora_bf16_ws_bytes(T, d_in, d_out, r)))
+    return FALQ_EINVAL;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (T == 0 || d_in == 0 || d_out == 0) {
+    hipError_t e = hipSuccess;
+    if (T * d_in > 0) e = falq::launch_fill_f32(dx, T * d_in, 0.0f, s);
+    if (e == hipSuccess) e = falq::launch_fill_f32(dA, r * d_in, 0.0f, s);
+    if (e == hipSuccess) e = falq::launch_fill_f32(dB, d_out * r, 0.0f, s);
+    return hip_status(e);
+  }
+  return hip_status(falq::launch_lora_bf16_bwd(dy, gq, s_g, x, wq, s_w, A, B, saved, T, d_in,
+                                               d_out, r, dx, dA, dB, ws, s));
 }
 
 }  // extern "C"

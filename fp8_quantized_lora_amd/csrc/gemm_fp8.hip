@@ -34,6 +34,7 @@
 // slice; B is loaded the same way, so whatever order the matrix core pairs K
 // elements in, both operands present the same K index in the same slot.
 #include "common.hpp"
+#include <algorithm>
 #include <cstdint>
 #include "gemm_fp8_kernel.hpp"
 #include "kernels.hpp"
@@ -80,15 +81,84 @@ int whole_tiles(int nt, int nk) {
   return nt - rem;
 }
 
-// the direct-to-LDS kernel over tM x tN tiles, with the last round split
+// C (+)= scale * sum of the S partial planes P[s] (M x N, row stride ldp,
+// plane stride M * ldp), added in plane order; scale = 1 / (sa * sb), or 1
+// without scales
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ P, int S,
+                                                            int M, int N, int64_t ldp,
+                                                            float* __restrict__ C, int64_t ldc,
+                                                            const float* __restrict__ sa,
+                                                            const float* __restrict__ sb,
+                                                            int acc) {
+  const float scale = sa ? 1.0f / (sa[0] * sb[0]) : 1.0f;
+  const int64_t n4 = N / 4, total = (int64_t)M * n4;
+  const int64_t plane = (int64_t)M * ldp;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t m = i / n4, c = (i % n4) * 4;
+    const float* p = P + m * ldp + c;
+    v4f v = *reinterpret_cast<const v4f*>(p);
+    for (int sp = 1; sp < S; ++sp) v = v + *reinterpret_cast<const v4f*>(p + sp * plane);
+    v = v * scale;
+    float* cp = C + m * ldc + c;
+    if (acc) v = *reinterpret_cast<const v4f*>(cp) + v;
+    *reinterpret_cast<v4f*>(cp) = v;
+  }
+}
+
+// split-K plan of an output with nt tiles and nk K steps: the number of
+// splits (1: none) so that about one workgroup per CU runs, each split at
+// least 4 K steps
+struct SplitK {
+  int S, kc;
+};
+SplitK splitk_plan(int nt, int nk) {
+  int S = 1;
+  while (nt * S * 2 <= 256 && nk / (S * 2) >= 4) S *= 2;
+  return {S, (nk + S - 1) / S};
+}
+
+}  // namespace
+
+size_t gemm_splitk_ws_bytes(int64_t M, int64_t N, int64_t K_bytes) {
+  if (M <= 0 || N <= 0 || K_bytes <= 0 || K_bytes % gemm::dma::BK != 0) return 0;
+  const int nt = (int)(((M + gemm::dma::BM - 1) / gemm::dma::BM) *
+                       ((N + gemm::dma::BN - 1) / gemm::dma::BN));
+  const SplitK sk = splitk_plan(nt, (int)(K_bytes / gemm::dma::BK));
+  if (sk.S == 1) return 0;
+  return (size_t)sk.S * (size_t)M * (size_t)align_up((size_t)N, 4) * 4;
+}
+
+namespace {
+
+// the direct-to-LDS kernel over tM x tN tiles, with the last round split, or
+// (given a workspace of gemm_splitk_ws_bytes) split over K when the tiles
+// alone would leave most CUs idle
 template <int FA>
 hipError_t launch_dma(const uint8_t* A, int64_t lda, const uint8_t* B, int64_t ldb, float* C,
                       int64_t ldc, int64_t M, int64_t N, int64_t K, const float* sa,
-                      const float* sb, hipStream_t s) {
+                      const float* sb, hipStream_t s, int acc = 0, float* splitk_ws = nullptr) {
   const int tM = (int)((M + gemm::dma::BM - 1) / gemm::dma::BM);
   const int tN = (int)((N + gemm::dma::BN - 1) / gemm::dma::BN);
   const int nt = tM * tN;
-  const int full = whole_tiles(nt, (int)(K / gemm::dma::BK));
+  if (splitk_ws) {
+    const SplitK sk = splitk_plan(nt, (int)(K / gemm::dma::BK));
+    if (sk.S > 1) {
+      const int64_t ldp = (int64_t)align_up((size_t)N, 4);
+      gemm::dma::gemm_fp8_nt_dma<false, FA, 2><<<nt * sk.S, gemm::dma::kThreads, 0, s>>>(
+          A, lda, B, ldb, splitk_ws, ldp, (int)M, (int)N, (int)K, sa, sb, tM, tN, nt,
+          gemm::dma::SecondB{}, sk.kc);
+      hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      const int64_t items = M * (N / 4);
+      const int blocks = (int)std::min<int64_t>((items + 255) / 256, 2048);
+      splitk_reduce_kernel<<<blocks, 256, 0, s>>>(splitk_ws, sk.S, (int)M, (int)N, ldp, C, ldc,
+                                                  FA == 5 ? nullptr : sa, sb, acc);
+      return hipGetLastError();
+    }
+  }
+  // an accumulating product keeps whole tiles (a split would add three terms)
+  const int full = acc ? nt : whole_tiles(nt, (int)(K / gemm::dma::BK));
   if (full < nt) {
     zero_tiles_kernel<<<(nt - full) * 16, 256, 0, s>>>(C, ldc, (int)M, (int)N, tM, tN, full);
     const hipError_t e = hipGetLastError();
@@ -97,14 +167,14 @@ hipError_t launch_dma(const uint8_t* A, int64_t lda, const uint8_t* B, int64_t l
   if (full > 0) {
     gemm::dma::gemm_fp8_nt_dma<false, FA><<<full, gemm::dma::kThreads, 0, s>>>(
         A, lda, B, ldb, C, ldc, (int)M, (int)N, (int)K, sa, sb, tM, tN, full,
-        gemm::dma::SecondB{});
+        gemm::dma::SecondB{}, acc);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (full < nt)
-    gemm::dma::gemm_fp8_nt_dma<false, FA, true><<<2 * (nt - full), gemm::dma::kThreads, 0, s>>>(
+    gemm::dma::gemm_fp8_nt_dma<false, FA, 1><<<2 * (nt - full), gemm::dma::kThreads, 0, s>>>(
         A, lda, B, ldb, C, ldc, (int)M, (int)N, (int)K, sa, sb, tM, tN, full,
-        gemm::dma::SecondB{});
+        gemm::dma::SecondB{}, 0);
   return hipGetLastError();
 }
 
@@ -114,13 +184,15 @@ namespace {
 template <int FA>
 hipError_t gemm_nt(const uint8_t* A, int64_t lda, const uint8_t* B, int64_t ldb, float* C,
                    int64_t ldc, int64_t M, int64_t N, int64_t K, const float* sa, const float* sb,
-                   hipStream_t s) {
-  if (K % gemm::dma::BK == 0) return launch_dma<FA>(A, lda, B, ldb, C, ldc, M, N, K, sa, sb, s);
+                   hipStream_t s, int acc, float* splitk_ws) {
+  if (K % gemm::dma::BK == 0)
+    return launch_dma<FA>(A, lda, B, ldb, C, ldc, M, N, K, sa, sb, s, acc,
+                          N % 4 == 0 ? splitk_ws : nullptr);
   using Cf = gemm::Cfg<256, 256, 128, 2, 2>;
   const int tilesM = (int)((M + Cf::BM - 1) / Cf::BM);
   const int tilesN = (int)((N + Cf::BN - 1) / Cf::BN);
   gemm::gemm_fp8_nt_kernel<Cf, FA><<<tilesM * tilesN, Cf::kThreads, 0, s>>>(
-      A, lda, B, ldb, C, ldc, (int)M, (int)N, (int)K, sa, sb, tilesM, tilesN);
+      A, lda, B, ldb, C, ldc, (int)M, (int)N, (int)K, sa, sb, tilesM, tilesN, acc);
   return hipGetLastError();
 }
 }  // namespace
@@ -134,11 +206,23 @@ static bool gemm_shape_ok(int64_t M, int64_t N, int64_t K) {
 
 hipError_t launch_gemm_fp8_nt(const uint8_t* A, int64_t lda, const uint8_t* B, int64_t ldb,
                               float* C, int64_t ldc, int64_t M, int64_t N, int64_t K,
-                              const float* sa, const float* sb, hipStream_t s, int a_fmt) {
+                              const float* sa, const float* sb, hipStream_t s, int a_fmt,
+                              int acc, float* splitk_ws) {
   if (M == 0 || N == 0) return hipSuccess;
   if (!gemm_shape_ok(M, N, K)) return hipErrorInvalidValue;
-  return a_fmt == 0 ? gemm_nt<0>(A, lda, B, ldb, C, ldc, M, N, K, sa, sb, s)
-                    : gemm_nt<1>(A, lda, B, ldb, C, ldc, M, N, K, sa, sb, s);
+  return a_fmt == 0 ? gemm_nt<0>(A, lda, B, ldb, C, ldc, M, N, K, sa, sb, s, acc, splitk_ws)
+                    : gemm_nt<1>(A, lda, B, ldb, C, ldc, M, N, K, sa, sb, s, acc, splitk_ws);
+}
+
+hipError_t launch_gemm_bf16_nt(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb,
+                               float* C, int64_t ldc, int64_t M, int64_t N, int64_t K,
+                               hipStream_t s, int acc, float* splitk_ws) {
+  if (M == 0 || N == 0) return hipSuccess;
+  // the direct-to-LDS kernel over K in bytes: 64 bf16 per 128-byte step
+  if (K <= 0 || K % 64 != 0 || !gemm_shape_ok(M, N, 2 * K)) return hipErrorInvalidValue;
+  return launch_dma<5>(reinterpret_cast<const uint8_t*>(A), 2 * lda,
+                       reinterpret_cast<const uint8_t*>(B), 2 * ldb, C, ldc, M, N, 2 * K, nullptr,
+                       nullptr, s, acc, N % 4 == 0 ? splitk_ws : nullptr);
 }
 
 hipError_t launch_gemm_fp4_nt(const uint8_t* A, int64_t lda, const uint8_t* B, int64_t ldb,
@@ -166,7 +250,7 @@ hipError_t launch_gemm_fp8_nt_second(const uint8_t* A, int64_t lda, const uint8_
   const int tN = (int)((N + gemm::dma::BN - 1) / gemm::dma::BN);
   gemm::dma::gemm_fp8_nt_dma<true, 0><<<tM * tN, gemm::dma::kThreads, 0, s>>>(
       A, lda, B, ldb, C, ldc, (int)M, (int)N, (int)K, sa, sb, tM, tN, tM * tN,
-      gemm::dma::SecondB{Bu, ldbu, (int)R, Cu, ldcu, sbu});
+      gemm::dma::SecondB{Bu, ldbu, (int)R, Cu, ldcu, sbu}, 0);
   return hipGetLastError();
 }
 

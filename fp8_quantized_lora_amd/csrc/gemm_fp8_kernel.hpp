@@ -56,12 +56,12 @@ __device__ __forceinline__ void tile_coords(int tilesM, int tilesN, int& tm, int
 }
 
 // FA: format of the A codes (0 = E4M3, 1 = E5M2: the MFMA's A-format field);
-// B is E4M3
+// B is E4M3.  acc_c != 0 adds the product onto C.
 template <class C, int FA>
 __global__ __launch_bounds__(C::kThreads, 1) void gemm_fp8_nt_kernel(
     const uint8_t* __restrict__ A, int64_t lda, const uint8_t* __restrict__ B, int64_t ldb,
     float* __restrict__ Cm, int64_t ldc, int M, int N, int K, const float* __restrict__ sa,
-    const float* __restrict__ sb, int tilesM, int tilesN) {
+    const float* __restrict__ sb, int tilesM, int tilesN, int acc_c) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[C::LDS_BYTES];
   uint8_t* sA = smem;
   uint8_t* sB = smem + 2 * C::BM * C::ROW;
@@ -166,7 +166,10 @@ __global__ __launch_bounds__(C::kThreads, 1) void gemm_fp8_nt_kernel(
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int row = rbase + i * 32 + 8 * (v >> 2) + (v & 3);
-        if (row < M) Cm[(int64_t)row * ldc + col] = acc[i][j][v] * scale;
+        if (row < M) {
+          float* c = Cm + (int64_t)row * ldc + col;
+          *c = acc_c ? *c + acc[i][j][v] * scale : acc[i][j][v] * scale;
+        }
       }
     }
 }
@@ -221,19 +224,29 @@ struct SecondB {
 };
 
 // FA: format of the A codes (0 = E4M3, 1 = E5M2; B and the second B are
-// E4M3), or 4: both operands FP4 E2M1, two codes per byte (K counts bytes).
-// HALF = false: workgroup b takes the whole logical tile xcd_remap(b, tiles)
-// (tiles = the number of workgroups).  HALF = true: workgroups 2j and 2j + 1
+// E4M3), or 4: both operands FP4 E2M1, two codes per byte, or 5: both
+// operands bfloat16 (K counts bytes throughout; bf16 takes no scales: sa and
+// sb are ignored).  acc != 0 adds the product onto C instead of overwriting
+// it (whole tiles only).
+// MODE 0: workgroup b takes the whole logical tile xcd_remap(b, tiles)
+// (tiles = the number of workgroups).  MODE 1: workgroups 2j and 2j + 1
 // take the two K halves of logical tile first + j and add them into C with
 // float atomics (C zeroed beforehand): exactly two addends meet a zero per
 // element, and the sum of two floats does not depend on their order, so the
-// result is the same on every run.
-template <bool FU, int FA, bool HALF = false>
+// result is the same on every run.  MODE 2 (split K, for outputs with too few
+// tiles to fill the GPU): workgroup b takes tile b % tiles over K steps
+// [s * acc_c, (s + 1) * acc_c), s = b / tiles, and writes its unscaled partial
+// sums to plane s of C (planes of M * ldc floats); a reduction adds the
+// planes in a fixed order.
+template <bool FU, int FA, int MODE = 0>
 __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_nt_dma(
     const uint8_t* __restrict__ A, int64_t lda, const uint8_t* __restrict__ B, int64_t ldb,
     float* __restrict__ C, int64_t ldc, int M, int N, int K, const float* __restrict__ sa,
-    const float* __restrict__ sb, int tilesM, int tilesN, int tiles_or_first, SecondB u) {
-  static_assert(!(FU && HALF), "the second product is not split");
+    const float* __restrict__ sb, int tilesM, int tilesN, int tiles_or_first, SecondB u,
+    int acc_c) {
+  static_assert(!(FU && MODE != 0), "the second product is not split");
+  constexpr bool HALF = MODE == 1;
+  static_assert(FA != 5 || !FU, "no second product with bf16 operands");
   constexpr int SB = FU ? STAGE_U : STAGE;                 // bytes per LDS stage
   __shared__ __attribute__((aligned(1024))) uint8_t smem[S * SB];
   int tm, tn, k_lo = 0, nk = K / BK;
@@ -242,6 +255,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_nt_dma(
     tile_of(tiles_or_first + (j >> 1), tilesM, tilesN, tm, tn);
     k_lo = h ? nk / 2 : 0;
     nk = h ? nk - nk / 2 : nk / 2;
+  } else if constexpr (MODE == 2) {
+    const int b = blockIdx.x, sp = b / tiles_or_first;
+    tile_of(b % tiles_or_first, tilesM, tilesN, tm, tn);
+    k_lo = sp * acc_c;
+    nk = min(nk - k_lo, acc_c);
+    C += (int64_t)sp * M * ldc;
   } else {
     tile_of(xcd_remap(blockIdx.x, tiles_or_first), tilesM, tilesN, tm, tn);
   }
@@ -307,8 +326,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_nt_dma(
   const int offA = (wm * WTM + r16) * BK, offB = BM * BK + (wn * WTN + r16) * BK;
   // FP4 (FA == 4): a 128-byte row holds 256 values, two MFMA K-halves of
   // 128; lane group g reads its 16 bytes of each half (chunks g and g + 4),
-  // joined so that the register layout matches the FP8 path
-  const int p0 = FA == 4 ? (g ^ sw) * 16 : o0, p1 = FA == 4 ? ((g + 4) ^ sw) * 16 : o1;
+  // joined so that the register layout matches the FP8 path.  bf16 (FA == 5):
+  // a row holds 64 values, two K-halves of the 16 x 16 x 32 bf16 MFMA, whose
+  // lane group g takes elements 8g .. 8g + 7 of its half: chunks g and g + 4
+  // again.
+  constexpr bool HALVES = FA == 4 || FA == 5;
+  const int p0 = HALVES ? (g ^ sw) * 16 : o0, p1 = HALVES ? ((g + 4) ^ sw) * 16 : o1;
   auto frag = [&](const uint8_t* p) {
     return join(*reinterpret_cast<const uint4*>(p + p0), *reinterpret_cast<const uint4*>(p + p1));
   };
@@ -321,6 +344,13 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_nt_dma(
       const v8i blo = {b[0], b[1], b[2], b[3], 0, 0, 0, 0}, bhi = {b[4], b[5], b[6], b[7], 0, 0, 0, 0};
       c = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(blo, alo, c, 4, 4, 0, 0, 0, 0);
       return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(bhi, ahi, c, 4, 4, 0, 0, 0, 0);
+    } else if constexpr (FA == 5) {
+      const v4i alo = {a[0], a[1], a[2], a[3]}, ahi = {a[4], a[5], a[6], a[7]};
+      const v4i blo = {b[0], b[1], b[2], b[3]}, bhi = {b[4], b[5], b[6], b[7]};
+      c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, blo),
+                                                  __builtin_bit_cast(v8bf, alo), c, 0, 0, 0);
+      return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, bhi),
+                                                     __builtin_bit_cast(v8bf, ahi), c, 0, 0, 0);
     } else {
       return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(b, a, c, 0, FA, 0, 0, 0, 0);
     }
@@ -328,7 +358,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_nt_dma(
   // No scalar load may be pending when the loop starts: the compiler then
   // treats each step's LDS reads as returning in order and waits only for the
   // fragments the next MFMA needs.
-  const float scale = 1.0f / (sa[0] * sb[0]);
+  const float scale = (FA == 5 || MODE == 2) ? 1.0f : 1.0f / (sa[0] * sb[0]);
   const float scale_u = FU ? 1.0f / (sa[0] * u.sb[0]) : 0.0f;
   v4f accu;
 #pragma unroll
@@ -384,11 +414,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_nt_dma(
     for (int j = 0; j < NB; ++j) {
       const int col = col0 + j * 16;
       if (col >= N) continue;                 // N is a multiple of 16: all four or none
-      const v4f v = acc[i][j] * scale;
+      v4f v = acc[i][j] * scale;
       if constexpr (HALF) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) unsafeAtomicAdd(crow + col + e, v[e]);
       } else {
+        if (MODE == 0 && acc_c) v = *reinterpret_cast<const v4f*>(crow + col) + v;
         *reinterpret_cast<v4f*>(crow + col) = v;
       }
     }

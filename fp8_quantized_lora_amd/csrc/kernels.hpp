@@ -31,7 +31,40 @@ hipError_t launch_dequantize(const uint8_t* q, int64_t n, const float* s, float*
 // A in E4M3 (a_fmt 0) or E5M2 (a_fmt 1), B in E4M3
 hipError_t launch_gemm_fp8_nt(const uint8_t* A, int64_t lda, const uint8_t* B, int64_t ldb,
                               float* C, int64_t ldc, int64_t M, int64_t N, int64_t K,
-                              const float* sa, const float* sb, hipStream_t s, int a_fmt = 0);
+                              const float* sa, const float* sb, hipStream_t s, int a_fmt = 0,
+                              int acc = 0, float* splitk_ws = nullptr);
+// bytes of split-K partials a product of M x N outputs over K_bytes needs
+// (0: it runs unsplit); splitk_ws = nullptr never splits
+size_t gemm_splitk_ws_bytes(int64_t M, int64_t N, int64_t K_bytes);
+// C (+)= A B^T with bfloat16 operands (K-contiguous, strides and K in
+// elements; K a multiple of 64), fp32 accumulation and output; acc != 0 adds
+// onto C
+hipError_t launch_gemm_bf16_nt(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb,
+                               float* C, int64_t ldc, int64_t M, int64_t N, int64_t K,
+                               hipStream_t s, int acc = 0, float* splitk_ws = nullptr);
+
+// ---- LoRA layers with a separate adapter branch (the baselines) ------------
+size_t lora_sep_saved_bytes(int64_t T, int64_t d_in, int64_t d_out, int64_t r);
+size_t lora_sep_ws_bytes(int64_t T, int64_t d_in, int64_t d_out, int64_t r);
+size_t lora_bf16_saved_bytes(int64_t T, int64_t r);
+size_t lora_bf16_ws_bytes(int64_t T, int64_t d_in, int64_t d_out, int64_t r);
+hipError_t launch_lora_sep_fwd(const uint8_t* xq, const float* s_x, const uint8_t* wq,
+                               const float* s_w, const float* A, const float* B, int64_t T,
+                               int64_t d_in, int64_t d_out, int64_t r, float* y, void* saved,
+                               void* ws, hipStream_t s);
+hipError_t launch_lora_sep_bwd(const uint8_t* gq, const float* s_g, const uint8_t* xq,
+                               const float* s_x, const uint8_t* wq, const float* s_w,
+                               void* saved, int64_t T, int64_t d_in, int64_t d_out, int64_t r,
+                               float* dx, float* dA, float* dB, void* ws, hipStream_t s);
+hipError_t launch_lora_bf16_fwd(const float* x, const uint8_t* xq, const float* s_x,
+                                const uint8_t* wq, const float* s_w, const float* A,
+                                const float* B, int64_t T, int64_t d_in, int64_t d_out, int64_t r,
+                                float* y, void* saved, void* ws, hipStream_t s);
+hipError_t launch_lora_bf16_bwd(const float* dy, const uint8_t* gq, const float* s_g,
+                                const float* x, const uint8_t* wq, const float* s_w,
+                                const float* A, const float* B, const void* saved, int64_t T,
+                                int64_t d_in, int64_t d_out, int64_t r, float* dx, float* dA,
+                                float* dB, void* ws, hipStream_t s);
 // FP4 E2M1 operands, two codes per byte: C = dec(A) . dec(B)^T / (sa * sb),
 // Kb = bytes per row (a multiple of 128: 256 values)
 hipError_t launch_gemm_fp4_nt(const uint8_t* A, int64_t lda, const uint8_t* B, int64_t ldb,
@@ -52,6 +85,13 @@ hipError_t launch_transpose_u8(const uint8_t* in, int64_t rows, int64_t cols, ui
 
 // ---- adapter gradients ----------------------------------------------------
 size_t adapter_grad_ws_bytes(int64_t T, int64_t d_in, int64_t d_out, int64_t r);
+// large ranks: through the full weight gradient M = G^^T X^ (adapter_grad_wide.hip)
+bool adapter_wide_route(int64_t T, int64_t d_in, int64_t d_out, int64_t r);
+size_t adapter_wide_ws_bytes(int64_t T, int64_t d_in, int64_t d_out, int64_t r);
+hipError_t launch_adapter_grads_wide(const uint8_t* gq, int g_fmt, const float* s_g,
+                                     const uint8_t* xq, const float* s_x, const float* A,
+                                     const float* B, int64_t T, int64_t d_in, int64_t d_out,
+                                     int64_t r, float* dA, float* dB, void* ws, hipStream_t s);
 hipError_t launch_adapter_grads(const uint8_t* gq, const float* s_g, const uint8_t* xq,
                                 const float* s_x, const float* A, const float* B,
                                 int64_t T, int64_t d_in, int64_t d_out, int64_t r,

@@ -405,6 +405,65 @@ falq_status rowwise_proxy_update_topk_rank(uint8_t *wq, const float *s_w, const 
                                            int32_t *comp_idx, void *ws, size_t ws_bytes,
                                            falq_stream stream);
 
+/*
+ * ---- Baselines: LoRA with a separate adapter branch -------------------------
+ * The two layers the melded layer is measured against ([intro] abstract and
+ * method paragraph: the melded layer removes the quantization overhead of a
+ * separate LoRA computational path; [rebuttal] thread 1, Q2 and Table R1: FP8
+ * against FP16 LoRA adapter compute, turning point near rank 8192).  Both
+ * keep the FP8 backbone product of melded_linear_fwd / _bwd and add the
+ * adapter as its own branch.  With ^ the dequantized value (code / scale):
+ *
+ * lora_separate_fp8_*: every adapter factor and rank-r intermediate is
+ * quantized per tensor to E4M3 on each step (as fp8_quantize), every product
+ * runs on the FP8 matrix cores:
+ *     A~ = Q(A), B~ = Q(B), U = X^ A^^T, U~ = Q(U), Y = X^ W^^T + U^ B^^T
+ *     V = G^ B^, V~ = Q(V), dX = G^ W^ + V^ A^, dB = G^^T U^, dA = V^^T X^
+ * lora_bf16_*: the adapter branch in bfloat16 (bf = nearest-even bfloat16)
+ * with fp32 accumulation, from the unquantized X and dY:
+ *     U = bf(X) bf(A)^T, Y = X^ W^^T + bf(U) bf(B)^T
+ *     V = bf(dY) bf(B), dX = G^ W^ + bf(V) bf(A), dB = bf(dY)^T bf(U),
+ *     dA = bf(V)^T bf(X)
+ * (U and V themselves are fp32 products rounded once to bfloat16.)
+ *
+ * Shapes: r a multiple of 8; T a multiple of 16 (FP8) or 64 (bf16); d_in and
+ * d_out multiples of 16 (FP8) or 64 (bf16).  FALQ_EINVAL otherwise, and for
+ * null or misaligned pointers or short buffers.  The forward writes into
+ * `saved` what the backward needs (caller-owned, *_saved_bytes, 256-byte
+ * aligned); `ws` is scratch of *_workspace_bytes.  Layout of the FP8 path's
+ * `saved` (each part at the next multiple of 256 bytes): A~ [r x d_in], B~
+ * [d_out x r], U~ [T x r16] (r16 = r rounded up to 16; columns past r are
+ * zero codes), four floats s_a, s_b, s_u, s_v, then V~ [T x r16]; the
+ * forward writes all but V~ and s_v, which the backward adds (the backward
+ * reads the rest).  The bf16 path's `saved` is
+ * bf(U) as [T x r64] bfloat16 (r64 = r rounded up to 64, zero past r).
+ * Other arguments as melded_linear_fwd / melded_linear_bwd; x and dy are the
+ * float32 X [T x d_in] and dY [T x d_out] that xq and gq were quantized from.
+ */
+size_t lora_separate_fp8_saved_bytes(int64_t T, int64_t d_in, int64_t d_out, int64_t r);
+size_t lora_separate_fp8_workspace_bytes(int64_t T, int64_t d_in, int64_t d_out, int64_t r);
+falq_status lora_separate_fp8_fwd(const uint8_t *xq, const float *s_x, const uint8_t *wq,
+                                  const float *s_w, const float *A, const float *B, int64_t T,
+                                  int64_t d_in, int64_t d_out, int64_t r, float *y, void *saved,
+                                  size_t saved_bytes, void *ws, size_t ws_bytes,
+                                  falq_stream stream);
+falq_status lora_separate_fp8_bwd(const uint8_t *gq, const float *s_g, const uint8_t *xq,
+                                  const float *s_x, const uint8_t *wq, const float *s_w,
+                                  void *saved, size_t saved_bytes, int64_t T, int64_t d_in,
+                                  int64_t d_out, int64_t r, float *dx, float *dA, float *dB,
+                                  void *ws, size_t ws_bytes, falq_stream stream);
+size_t lora_bf16_saved_bytes(int64_t T, int64_t d_in, int64_t d_out, int64_t r);
+size_t lora_bf16_workspace_bytes(int64_t T, int64_t d_in, int64_t d_out, int64_t r);
+falq_status lora_bf16_fwd(const float *x, const uint8_t *xq, const float *s_x, const uint8_t *wq,
+                          const float *s_w, const float *A, const float *B, int64_t T,
+                          int64_t d_in, int64_t d_out, int64_t r, float *y, void *saved,
+                          size_t saved_bytes, void *ws, size_t ws_bytes, falq_stream stream);
+falq_status lora_bf16_bwd(const float *dy, const uint8_t *gq, const float *s_g, const float *x,
+                          const uint8_t *wq, const float *s_w, const float *A, const float *B,
+                          const void *saved, size_t saved_bytes, int64_t T, int64_t d_in,
+                          int64_t d_out, int64_t r, float *dx, float *dA, float *dB, void *ws,
+                          size_t ws_bytes, falq_stream stream);
+
 #ifdef __cplusplus
 }
 #endif

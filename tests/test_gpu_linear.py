@@ -54,6 +54,9 @@ SHAPES = [  # (T, d_in, d_out, r): full tiles, ragged tails in every dimension, 
     (1000, 256, 1536, 128),
     (300, 384, 640, 8),      # K % 128 == 0 in both products: fast path with ragged M and N
     (513, 1152, 1280, 64),
+    # ranks large enough that the backward contracts through G^^T X^ first
+    (1024, 512, 512, 256),
+    (512, 256, 384, 512),
 ]
 
 
@@ -256,3 +259,26 @@ def test_fp8_matrix_core_block_truncation(gpu_lib):
         for i, (_, v, pos) in enumerate(rows):
             want = 16384.0 + (np.trunc(v / 2.0) * 2.0 if pos == 1 else v)
             assert y[i, 0] == np.float32(want), (K, pos, v, y[i, 0], want)
+
+
+def test_backward_wide_route_e5m2(gpu_lib):
+    """A large-rank backward (through G^^T X^) with an E5M2 upstream gradient
+    (the FP8 product G~^T X~ then takes the E5M2 operand)."""
+    announce("bwd large rank, E5M2 gradient")
+    rng = np.random.default_rng(41)
+    T, d_in, d_out, r = 1024, 512, 384, 320
+    p = quantized_problem(41, T, d_in, d_out, r)
+    dY = (rng.standard_normal((T, d_out)) * 1e-2).astype(np.float32)
+    gq, s_g, _, _ = oracle.fp8_quantize(dY, fmt="e5m2")
+    dx = torch.full((T, d_in), np.nan, dtype=torch.float32, device="cuda")
+    dA = torch.full((r, d_in), np.nan, dtype=torch.float32, device="cuda")
+    dB = torch.full((d_out, r), np.nan, dtype=torch.float32, device="cuda")
+    gpu_lib.melded_linear_bwd(dev(gq), scalar(s_g), dev(p["xq"]), scalar(p["s_x"]), dev(p["wq"]),
+                              scalar(p["s_w"]), dev(p["A"]), dev(p["B"]), dx, dA, dB,
+                              g_fmt="e5m2")
+    rdx, rdA, rdB = oracle.melded_linear_bwd(gq, s_g, p["xq"], p["s_x"], p["wq"], p["s_w"],
+                                             p["A"], p["B"], g_fmt="e5m2")
+    e = (rel_l2(host(dx), rdx), rel_l2(host(dA), rdA), rel_l2(host(dB), rdB),
+         rel_l2_rank(host(dA), rdA, 0), rel_l2_rank(host(dB), rdB, 1))
+    print("wide E5M2 bwd rel-L2 dX %.2e dA %.2e dB %.2e per rank %.2e %.2e" % e)
+    assert max(e) <= TOL
