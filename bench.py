@@ -207,23 +207,12 @@ def run(args):
         """The step's six boundary calls for batch i, in order (the last one a
         no-op on steps without a merge)."""
         X, dY = batches[i % len(batches)]
-        if frozen:
-            fwd = lambda: fq.melded_linear_fwd_frozen_a(m.xq, m.s_x, m.wq, m.s_w, m.aq, m.s_a,  # noqa: E731
-                                                        m.y, m.u, ws=m.ws_fwd, stream=stream)
-            bwd = lambda: fq.melded_linear_bwd_frozen_a(m.gq, m.s_g, m.wq, m.s_w, m.u, m.dx,  # noqa: E731
-                                                        m.dB, ws=m.ws_bwd, stream=stream,
-                                                        g_fmt=args.grad_format)
-        else:
-            fwd = lambda: fq.melded_linear_fwd(m.xq, m.s_x, m.wq, m.s_w, m.y, stream=stream)  # noqa: E731
-            bwd = lambda: fq.melded_linear_bwd(m.gq, m.s_g, m.xq, m.s_x, m.wq, m.s_w, m.A, m.B,  # noqa: E731
-                                               m.dx, m.dA, m.dB, ws=m.ws_bwd, stream=stream,
-                                               g_fmt=args.grad_format)
         return [
             lambda: fq.fp8_quantize(X, m.xq, m.s_x, ws=m.ws_q, stream=stream),
-            fwd,
+            lambda: m.forward_product(stream),
             lambda: fq.fp8_quantize(dY, m.gq, m.s_g, ws=m.ws_q, stream=stream,
                                     fmt=args.grad_format),
-            bwd,
+            lambda: m.backward_product(stream),
             lambda: m.adapter_update(spec.lr, stream=stream),
             (lambda: m.merge(spec.tau, spec.k_max, stream=stream)) if merges(i)
             else (lambda: None),
@@ -319,7 +308,11 @@ def run(args):
              + chain * n_merge_timed / args.steps)
     tflops = flops / (ms_per_step * 1e-3) / 1e12
     tokens_per_s = T / (ms_per_step * 1e-3)
-    gemm_flops = 2 * T * d_in * d_out + (2 * T * d_in * r if frozen else 0)
+    # the forward call's algorithmic flops: the backbone product, plus the
+    # rank-r product X^ A^T (X~ A~^T with A frozen) where the call forms it
+    # (counted once, at rank r, though the fused route carries A as three
+    # E4M3 pieces)
+    gemm_flops = 2 * T * d_in * d_out + (2 * T * d_in * r if frozen or m.use_xa else 0)
     gemm_us = gemm_timed_us
     gemm_tflops = gemm_flops / (gemm_us * 1e-6) / 1e12
     quant_bytes = T * d_in * 5 + 4                  # fp32 in, E4M3 out, the scale
@@ -364,11 +357,14 @@ def run(args):
         "tokens_per_s": round(tokens_per_s, 1),
         "roofline": {"kernel": ("melded_linear_fwd_frozen_a call (FP8 GEMM 4096 x 4096 x 4096 "
                                 "+ X~A~^T)" if frozen else
+                                "melded_linear_fwd_xa call (A split into three E4M3 pieces, then "
+                                "one FP8 GEMM 4096 x 4096 x 4096 forming X^A^T in the same tiles)"
+                                if m.use_xa else
                                 "melded_linear_fwd FP8 GEMM (4096 x 4096 x 4096)"),
                      "bound": "mfma", "achieved": round(gemm_tflops, 1),
                      "peak": FP8_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(gemm_tflops / FP8_PEAK_TFLOPS, 4),
-                     "traffic": None if frozen else gemm_traffic_bytes()},
+                     "traffic": None if frozen else gemm_traffic_bytes(m.use_xa)},
         "per_call_us": {k: round(v, 2) for k, v in per_call_us.items()},
         "launch": "eager launches on one HIP stream",
         "fwd_gemm_us_timed": round(gemm_timed_us, 2),
@@ -419,10 +415,9 @@ def _step_calls(fq, m, X, dY, spec, stream):
     """The six boundary calls of one melded-linear step."""
     return [
         lambda: fq.fp8_quantize(X, m.xq, m.s_x, ws=m.ws_q, stream=stream),
-        lambda: fq.melded_linear_fwd(m.xq, m.s_x, m.wq, m.s_w, m.y, stream=stream),
+        lambda: m.forward_product(stream),
         lambda: fq.fp8_quantize(dY, m.gq, m.s_g, ws=m.ws_q, stream=stream),
-        lambda: fq.melded_linear_bwd(m.gq, m.s_g, m.xq, m.s_x, m.wq, m.s_w, m.A, m.B, m.dx,
-                                     m.dA, m.dB, ws=m.ws_bwd, stream=stream),
+        lambda: m.backward_product(stream),
         lambda: m.adapter_update(spec.lr, stream=stream),
         lambda: m.merge(spec.tau, spec.k_max, stream=stream),
     ]
@@ -723,10 +718,12 @@ def gemm_sources_digest():
     return h.hexdigest()
 
 
-def gemm_traffic_bytes():
+def gemm_traffic_bytes(fused_xa):
     """HBM bytes per launch of the 4096^3 FP8 GEMM from the committed
     FETCH_SIZE / WRITE_SIZE counter summary, or None when that summary is
-    missing or was taken on other kernel sources than the ones built here."""
+    missing, was taken on other kernel sources than the ones built here, or
+    on the other forward route (`fused_xa`: X^ A^T formed in the GEMM's
+    tiles)."""
     path = os.path.join(ROOT, TRAFFIC_SUMMARY)
     if not os.path.exists(path):
         return None
@@ -737,6 +734,8 @@ def gemm_traffic_bytes():
                 k, v = line[2:].strip().split(": ", 1)
                 vals[k.strip("`")] = v.strip().strip("`")
     if vals.get("sources_sha256") != gemm_sources_digest():
+        return None
+    if vals.get("forward_route") != ("fused_xa" if fused_xa else "plain"):
         return None
     try:
         return int(vals["traffic_bytes_per_launch"])

@@ -27,6 +27,8 @@ __all__ = ["load", "FalqError", "fp8_quantize", "fp8_quantize_workspace_bytes",
            "melded_linear_bwd_frozen_a_workspace_bytes", "rowwise_proxy_update_workspace_bytes",
            "fp4_quantize", "melded_linear_fwd_fp4", "version", "LIB_PATH",
            "fp8_quantize_noalloc", "QUANTIZE_SCRATCH_BYTES",
+           "melded_linear_xa_fused", "melded_linear_fwd_xa", "melded_linear_bwd_xa",
+           "melded_linear_fwd_xa_workspace_bytes", "melded_linear_bwd_xa_workspace_bytes",
            "lora_separate_fp8_saved_bytes", "lora_separate_fp8_workspace_bytes",
            "lora_separate_fp8_fwd", "lora_separate_fp8_bwd", "lora_bf16_saved_bytes",
            "lora_bf16_workspace_bytes", "lora_bf16_fwd", "lora_bf16_bwd"]
@@ -78,6 +80,13 @@ _SIGS = {
     "fp4_quantize": (_i32, [_c_p, _i32, _i64, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _sz, _c_p]),
     "fp8_quantize_noalloc": (_i32, [_c_p, _i32, _i64, _i32, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p]),
     "melded_linear_fwd_fp4": (_i32, [_c_p, _c_p, _c_p, _c_p, _i64, _i64, _i64, _c_p, _c_p]),
+    "melded_linear_xa_fused": (_i32, [_i64, _i64, _i64, _i64]),
+    "melded_linear_fwd_xa_workspace_bytes": (_sz, [_i64, _i64, _i64, _i64]),
+    "melded_linear_fwd_xa": (_i32, [_c_p, _c_p, _c_p, _c_p, _c_p, _i64, _i64, _i64, _i64, _c_p,
+                                    _c_p, _c_p, _sz, _c_p]),
+    "melded_linear_bwd_xa_workspace_bytes": (_sz, [_i64, _i64, _i64, _i64]),
+    "melded_linear_bwd_xa": (_i32, [_c_p, _i32, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p,
+                                    _i64, _i64, _i64, _i64, _c_p, _c_p, _c_p, _c_p, _sz, _c_p]),
     "lora_separate_fp8_saved_bytes": (_sz, [_i64, _i64, _i64, _i64]),
     "lora_separate_fp8_workspace_bytes": (_sz, [_i64, _i64, _i64, _i64]),
     "lora_separate_fp8_fwd": (_i32, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _i64, _i64, _i64, _i64,
@@ -441,6 +450,58 @@ def rowwise_proxy_update_topk_rank(wq, s_w, A, B, k_rank: int, tau: float, k_max
         _ptr(wq), _ptr(s_w), _ptr(A), _ptr(B), d_in, d_out, r, k_rank, tau, k_max, _ptr(sel_idx),
         _ptr(n_sel), _ptr(rho), _ptr(comp_idx), _ptr(ws), ws.numel(), _stream(stream)),
         "rowwise_proxy_update_topk_rank")
+
+
+# ---------------------------------------------------------------------------
+# X^ A^T formed with the forward product, G^ B with the dX product
+def melded_linear_xa_fused(T: int, d_in: int, d_out: int, r: int) -> bool:
+    """Whether X^ A^T and G^ B ride in the FP8 products for this shape."""
+    return bool(load().melded_linear_xa_fused(T, d_in, d_out, r))
+
+
+def melded_linear_fwd_xa_workspace_bytes(T: int, d_in: int, d_out: int, r: int) -> int:
+    return int(load().melded_linear_fwd_xa_workspace_bytes(T, d_in, d_out, r))
+
+
+def melded_linear_bwd_xa_workspace_bytes(T: int, d_in: int, d_out: int, r: int) -> int:
+    return int(load().melded_linear_bwd_xa_workspace_bytes(T, d_in, d_out, r))
+
+
+def melded_linear_fwd_xa(xq, s_x, wq, s_w, A, y, xa, ws=None, stream=None) -> None:
+    """y = X~ W~^T / (s_x s_w) and xa = X^ A^T (the factor dB needs)."""
+    T, d_in = xq.shape
+    d_out = wq.shape[0]
+    r = A.shape[0]
+    _req(wq, torch.uint8, (d_out, d_in), "wq")
+    _req(A, torch.float32, (r, d_in), "A")
+    _req(y, torch.float32, (T, d_out), "y")
+    _req(xa, torch.float32, (T, r), "xa")
+    ws = _buf(ws, melded_linear_fwd_xa_workspace_bytes(T, d_in, d_out, r), xq.device, "ws")
+    _check(load().melded_linear_fwd_xa(_ptr(xq), _ptr(s_x), _ptr(wq), _ptr(s_w), _ptr(A), T, d_in,
+                                       d_out, r, _ptr(y), _ptr(xa), _ptr(ws), ws.numel(),
+                                       _stream(stream)), "melded_linear_fwd_xa")
+
+
+def melded_linear_bwd_xa(gq, s_g, xq, s_x, wq, s_w, A, B, xa, dx, dA, dB, ws=None, stream=None,
+                         g_fmt: str = "e4m3") -> None:
+    """dx, dA = (G^ B)^T X^ and dB = G^^T xa, with xa from melded_linear_fwd_xa."""
+    T, d_out = gq.shape
+    d_in = xq.shape[1]
+    r = A.shape[0]
+    _req(wq, torch.uint8, (d_out, d_in), "wq")
+    _req(A, torch.float32, (r, d_in), "A")
+    _req(B, torch.float32, (d_out, r), "B")
+    _req(xa, torch.float32, (T, r), "xa")
+    _req(dB, torch.float32, (d_out, r), "dB")
+    if dx is not None:
+        _req(dx, torch.float32, (T, d_in), "dx")
+    if dA is not None:
+        _req(dA, torch.float32, (r, d_in), "dA")
+    ws = _buf(ws, melded_linear_bwd_xa_workspace_bytes(T, d_in, d_out, r), gq.device, "ws")
+    _check(load().melded_linear_bwd_xa(_ptr(gq), _fmt(g_fmt), _ptr(s_g), _ptr(xq), _ptr(s_x),
+                                       _ptr(wq), _ptr(s_w), _ptr(A), _ptr(B), _ptr(xa), T, d_in,
+                                       d_out, r, _ptr(dx), _ptr(dA), _ptr(dB), _ptr(ws),
+                                       ws.numel(), _stream(stream)), "melded_linear_bwd_xa")
 
 
 # ---------------------------------------------------------------------------

@@ -26,6 +26,7 @@
 // U and V are T x r: a few MiB, consumed at once, cache resident.
 #include "common.hpp"
 #include "kernels.hpp"
+#include "pieces.hpp"
 #include "transpose_u8.hpp"
 
 #include <algorithm>
@@ -797,6 +798,291 @@ hipError_t launch_adapter_grads(const uint8_t* gq, const float* s_g, const uint8
     launch_reduce(rb, want_da ? &ra : nullptr, s);
   }
   return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// U = X^ A^T formed with the forward product, V = G^ B with the dX product
+// (melded_linear_fwd_xa / melded_linear_bwd_xa): the float factor enters the
+// FP8 matrix cores as three E4M3 pieces per element with one scale per rank,
+// sum_p dec(P_p[j, k]) ~ F[j, k] * s_j (s_j = 448 / max_k |F[j, k]|; each
+// piece the E4M3 rounding of what the previous ones left, so the residual
+// after three is about 2^-12 of the element or less).  The GEMM then adds
+// three MFMAs per K step in the four waves that hold the tile's unit
+// (gemm_fp8_kernel.hpp, SecondB), and the skinny row-wise pass, its
+// partials and their reduction disappear.  Shapes whose tile grid has too
+// few columns for the units (gemm_fp8_nt_fuses_second) form U or V with the
+// skinny kernel instead.
+// ---------------------------------------------------------------------------
+namespace {
+
+// one row j of the operand per workgroup: element k is F[j * rs + k * cs]
+// (A: rs = K, cs = 1; B^T read from B [K x R]: rs = 1, cs = R)
+constexpr int kPieceThreads = 1024, kPieceHold = 16;
+
+__global__ __launch_bounds__(kPieceThreads) void pieces_kernel(const float* __restrict__ F,
+                                                               int64_t K, int64_t rs, int64_t cs,
+                                                               uint8_t* __restrict__ P,
+                                                               int64_t plane,
+                                                               float* __restrict__ sp) {
+  const int64_t j = blockIdx.x;
+  piece_row<kPieceThreads, kPieceHold>(F + j * rs, cs, K, K, P + j * K, plane, sp + j);
+}
+
+// rows [0, rows) of a float operand F (element k of row j at F[j * rs +
+// k * cs], k < K) as pieces P[j * prow + k] (planes `plane` apart, zero for
+// K <= k < Kp) and scales sp[j]; rows [rows, rows_p) zero pieces
+struct PieceJob {
+  const float* f;
+  int64_t rs, cs, K, Kp;
+  uint8_t* P;
+  int64_t prow, plane;
+  float* sp;
+  int rows, rows_p;
+};
+
+__device__ __forceinline__ void piece_job(const PieceJob& q, int row) {
+  if (row < q.rows)
+    piece_row<256, 32>(q.f + row * q.rs, q.cs, q.K, q.Kp, q.P + row * q.prow, q.plane, q.sp + row);
+  else
+    piece_row_zero<256>(q.Kp, q.P + row * q.prow, q.plane, q.sp + row);
+}
+
+// The fused backward's preparation in one launch (each part alone is too
+// small to fill the GPU): workgroups [0, n_tr) transpose W~ for the dX
+// product (128 x 128 tiles, tr_tx per tile row), the next jb.rows_p form the
+// pieces of B^T (one rank per workgroup) for the dX product that also forms
+// G^ B, the rest those of U = X^ A^T for the token-contracting dB.
+__global__ __launch_bounds__(256) void xa_prep_kernel(const uint8_t* __restrict__ wq,
+                                                      int64_t d_out, int64_t d_in,
+                                                      uint8_t* __restrict__ wt, int n_tr,
+                                                      int tr_tx, PieceJob jb, PieceJob ju) {
+  int b = blockIdx.x;
+  if (b < n_tr) {
+    transpose_u8_tile(wq, d_out, d_in, wt, b % tr_tx, b / tr_tx);
+    return;
+  }
+  b -= n_tr;
+  if (b < jb.rows_p)
+    piece_job(jb, b);
+  else
+    piece_job(ju, b - jb.rows_p);
+}
+
+// one skinny product Out [M x R] = dec(Q) F^T / s_q with F [R x K] float,
+// split into bf16 hi/lo (row-wise Q, K contiguous in both)
+struct OnePlan {
+  int S, kc;
+  size_t hi, lo, p, total;
+};
+
+OnePlan one_plan(int64_t M, int64_t K, int64_t R) {
+  OnePlan p{};
+  const int64_t tiles = (int64_t)ceil_div(M, TM) * ceil_div(R, TN);
+  p.S = pick_splits(tiles, K, M * R * 4, 256ll << 20);
+  p.kc = chunk_for(K, p.S);
+  size_t o = 0;
+  auto take = [&](size_t bytes) { size_t at = o; o = align_up(o + bytes, 256); return at; };
+  p.hi = take((size_t)(R * K * 2));
+  p.lo = take((size_t)(R * K * 2));
+  p.p = take((size_t)p.S * M * R * 4);
+  p.total = o;
+  return p;
+}
+
+// F = A [R x K] (trans = false) or B^T with B [K x R] (trans = true)
+hipError_t launch_one_skinny(const uint8_t* q, int64_t ldq, int qf, const float* s_q,
+                             const float* F, bool trans, int64_t M, int64_t K, int64_t R,
+                             float* out, void* ws, hipStream_t s) {
+  const OnePlan pl = one_plan(M, K, R);
+  uint8_t* base = reinterpret_cast<uint8_t*>(ws);
+  uint16_t* hi = reinterpret_cast<uint16_t*>(base + pl.hi);
+  uint16_t* lo = reinterpret_cast<uint16_t*>(base + pl.lo);
+  float* part = reinterpret_cast<float*>(base + pl.p);
+  const Split sp = trans ? Split{F, (int)K, (int)R, true, K, hi, lo, ceil_div(R, 32), ceil_div(K, 32)}
+                         : Split{F, (int)R, (int)K, false, K, hi, lo, ceil_div(K, 32), ceil_div(R, 32)};
+  split_bf16_kernel<<<dim3(sp.tx * sp.ty, 1, 1), 256, 0, s>>>(sp, sp);
+  const Prob pr = prob(q, ldq, hi, lo, K, part, M, R, K, pl.kc);
+  const int tiles = pr.tilesM * pr.tilesN;
+  if (qf == 0)
+    skinny_kernel<false, 2, 0, 0><<<tiles * pl.S, kSkThreads, 0, s>>>(pr, pr, tiles, pl.S);
+  else
+    skinny_kernel<false, 2, 1, 1><<<tiles * pl.S, kSkThreads, 0, s>>>(pr, pr, tiles, pl.S);
+  launch_reduce(red(part, pl.S, M, R, M, s_q, 0, out, R, nullptr, nullptr), nullptr, s);
+  return hipGetLastError();
+}
+
+// the token-contracting half from U, V [T x r] (fp32, fully scaled):
+// U^T, V^T as bf16 hi/lo [r x Tp], then dB = G^^T U, dA = (X^^T V)^T
+struct UvPlan {
+  int64_t Tp;
+  int S2, kc2;
+  size_t uhi, ulo, vhi, vlo, p2b, p2a, total;
+};
+
+UvPlan uv_plan(int64_t T, int64_t d_in, int64_t d_out, int64_t r) {
+  UvPlan p{};
+  p.Tp = (T + TK - 1) / TK * TK;
+  const int64_t nT = ceil_div(r, TN);
+  const int64_t tiles2 = ((int64_t)ceil_div(d_in, TM) + ceil_div(d_out, TM)) * nT;
+  p.S2 = pick_splits(tiles2, T, (d_in + d_out) * r * 4, 256ll << 20);
+  p.kc2 = chunk_for(T, p.S2);
+  size_t o = 0;
+  auto take = [&](size_t bytes) { size_t at = o; o = align_up(o + bytes, 256); return at; };
+  p.uhi = take((size_t)r * p.Tp * 2);
+  p.ulo = take((size_t)r * p.Tp * 2);
+  p.vhi = take((size_t)r * p.Tp * 2);
+  p.vlo = take((size_t)r * p.Tp * 2);
+  p.p2b = take((size_t)p.S2 * d_out * r * 4);
+  p.p2a = take((size_t)p.S2 * d_in * r * 4);
+  p.total = o;
+  return p;
+}
+
+hipError_t launch_grads_from_uv(const uint8_t* gq, int g_fmt, const float* s_g, const uint8_t* xq,
+                                const float* s_x, const float* u, const float* v, int64_t T,
+                                int64_t d_in, int64_t d_out, int64_t r, float* dA, float* dB,
+                                void* ws, hipStream_t s) {
+  const UvPlan pl = uv_plan(T, d_in, d_out, r);
+  uint8_t* base = reinterpret_cast<uint8_t*>(ws);
+  auto u16 = [&](size_t off) { return reinterpret_cast<uint16_t*>(base + off); };
+  auto f32 = [&](size_t off) { return reinterpret_cast<float*>(base + off); };
+  const bool want_da = dA != nullptr;
+  {
+    const Red ru = red(u, 1, T, r, pl.Tp, nullptr, 2, nullptr, pl.Tp, u16(pl.uhi), u16(pl.ulo));
+    const Red rv = red(v, 1, T, r, pl.Tp, nullptr, 2, nullptr, pl.Tp, u16(pl.vhi), u16(pl.vlo));
+    launch_reduce(ru, want_da ? &rv : nullptr, s);
+  }
+  Prob pb = prob(gq, d_out, u16(pl.uhi), u16(pl.ulo), pl.Tp, f32(pl.p2b), d_out, r, T, pl.kc2);
+  Prob pa = prob(xq, d_in, u16(pl.vhi), u16(pl.vlo), pl.Tp, f32(pl.p2a), d_in, r, T, pl.kc2);
+  {
+    const int tiles = std::max(pb.tilesM * pb.tilesN, want_da ? pa.tilesM * pa.tilesN : 0);
+    const int grid = tiles * pl.S2 * (want_da ? 2 : 1);
+    if (g_fmt == 0)
+      skinny_kernel<true, 2, 0, 0><<<grid, kSkThreads, 0, s>>>(pb, pa, tiles, pl.S2);
+    else
+      skinny_kernel<true, 2, 1, 0><<<grid, kSkThreads, 0, s>>>(pb, pa, tiles, pl.S2);
+  }
+  {
+    const Red rb = red(f32(pl.p2b), pl.S2, d_out, r, d_out, s_g, 0, dB, r, nullptr, nullptr);
+    const Red ra = red(f32(pl.p2a), pl.S2, d_in, r, d_in, s_x, 1, dA, d_in, nullptr, nullptr);
+    launch_reduce(rb, want_da ? &ra : nullptr, s);
+  }
+  return hipGetLastError();
+}
+
+struct PiecesPlan {
+  size_t p, sp, total;
+};
+PiecesPlan pieces_plan(int64_t R, int64_t K) {
+  PiecesPlan q{};
+  size_t o = 0;
+  auto take = [&](size_t bytes) { size_t at = o; o = align_up(o + bytes, 256); return at; };
+  q.p = take((size_t)(3 * R * K));
+  q.sp = take((size_t)(R * 4));
+  q.total = o;
+  return q;
+}
+
+// the part of the backward's workspace that forms V (pieces of B^T for the
+// fused product, or the skinny product's splits and partials)
+size_t v_region_bytes(int64_t T, int64_t d_out, int64_t r) {
+  return std::max(pieces_plan(r, d_out).total, one_plan(T, d_out, r).total);
+}
+
+}  // namespace
+
+size_t fwd_xa_ws_bytes(int64_t T, int64_t d_in, int64_t d_out, int64_t r) {
+  if (r <= 0 || T <= 0 || d_in <= 0) return 0;
+  if (gemm_fp8_nt_fuses_second(d_out, d_in, r)) return pieces_plan(r, d_in).total;
+  return one_plan(T, d_in, r).total;
+}
+
+hipError_t launch_fwd_xa(const uint8_t* xq, const float* s_x, const uint8_t* wq, const float* s_w,
+                         const float* A, int64_t T, int64_t d_in, int64_t d_out, int64_t r,
+                         float* y, float* xa, void* ws, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  if (d_in == 0) {
+    hipError_t e = d_out > 0 ? launch_fill_f32(y, T * d_out, 0.0f, s) : hipSuccess;
+    return e == hipSuccess && r > 0 ? launch_fill_f32(xa, T * r, 0.0f, s) : e;
+  }
+  if (r > 0 && gemm_fp8_nt_fuses_second(d_out, d_in, r)) {
+    const PiecesPlan pp = pieces_plan(r, d_in);
+    uint8_t* base = reinterpret_cast<uint8_t*>(ws);
+    float* sp = reinterpret_cast<float*>(base + pp.sp);
+    pieces_kernel<<<(unsigned)r, kPieceThreads, 0, s>>>(A, d_in, d_in, 1, base + pp.p, r * d_in, sp);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return launch_gemm_fp8_nt_pieces(xq, d_in, wq, d_in, y, d_out, T, d_out, d_in, s_x, s_w,
+                                     base + pp.p, d_in, r * d_in, r, sp, xa, r, s, 0);
+  }
+  hipError_t e = d_out > 0 ? launch_gemm_fp8_nt(xq, d_in, wq, d_in, y, d_out, T, d_out, d_in, s_x,
+                                                s_w, s)
+                           : hipSuccess;
+  if (e != hipSuccess || r == 0) return e;
+  return launch_one_skinny(xq, d_in, 0, s_x, A, false, T, d_in, r, xa, ws, s);
+}
+
+// V = G^ B: [T x r], or [r x T4] (rank-major, T4 = T rounded up to 4) when
+// the dX product forms it for the token-contracting kernel
+size_t bwd_xa_ws_bytes(int64_t T, int64_t d_in, int64_t d_out, int64_t r) {
+  if (r <= 0 || T <= 0 || d_in <= 0 || d_out <= 0) return 0;
+  size_t o = align_up((size_t)r * (size_t)((T + 3) / 4 * 4) * 4, 256);   // V
+  o += v_region_bytes(T, d_out, r);
+  return o + (token_grads_ok(T, d_in, d_out, r) ? token_grads_ws_bytes(T, d_in, d_out, r)
+                                                : uv_plan(T, d_in, d_out, r).total);
+}
+
+hipError_t launch_bwd_xa(const uint8_t* gq, int g_fmt, const float* s_g, const uint8_t* xq,
+                         const float* s_x, const uint8_t* wq, uint8_t* wt, const float* s_w,
+                         const float* B, const float* xa, int64_t T, int64_t d_in, int64_t d_out,
+                         int64_t r, float* dx, float* dA, float* dB, void* ws, hipStream_t s) {
+  const int64_t T4 = (T + 3) / 4 * 4;
+  uint8_t* base = reinterpret_cast<uint8_t*>(ws);
+  float* v = reinterpret_cast<float*>(base);
+  uint8_t* vreg = base + align_up((size_t)r * (size_t)T4 * 4, 256);
+  uint8_t* rest = vreg + v_region_bytes(T, d_out, r);
+  const bool want_v = dA != nullptr && r > 0;
+  const bool tr = dx != nullptr && d_in > 0 && d_out > 0;
+  // the dX product with V formed in the same tiles when both are wanted and
+  // the grid allows; the token-contracting kernel when the shape allows
+  const bool fuse = want_v && tr && gemm_fp8_nt_fuses_second(d_in, d_out, r);
+  const bool tok = r > 0 && token_grads_ok(T, d_in, d_out, r);
+  if (tr && (d_in % 16 != 0 || d_out % 16 != 0)) return hipErrorInvalidValue;
+  const PiecesPlan pp = pieces_plan(r, d_out);
+  float* spb = reinterpret_cast<float*>(vreg + pp.sp);
+  PieceJob jb{}, ju{};
+  if (fuse) jb = PieceJob{B, 1, r, d_out, d_out, vreg + pp.p, d_out, r * d_out, spb, (int)r, (int)r};
+  if (tok) {
+    uint8_t* P;
+    float* sp;
+    int64_t Rp, Tp;
+    token_grads_u_pieces(rest, T, d_in, d_out, r, &P, &sp, &Rp, &Tp);
+    ju = PieceJob{xa, 1, r, T, Tp, P, Tp, Rp * Tp, sp, (int)r, (int)Rp};
+  }
+  const int tr_tx = tr ? ceil_div(d_in, 128) : 1;
+  const int n_tr = tr ? tr_tx * ceil_div(d_out, 128) : 0;
+  const int grid = n_tr + jb.rows_p + ju.rows_p;
+  if (grid > 0) {
+    xa_prep_kernel<<<grid, 256, 0, s>>>(wq, d_out, d_in, wt, n_tr, tr_tx, jb, ju);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  hipError_t e = hipSuccess;
+  if (fuse) {
+    e = launch_gemm_fp8_nt_pieces(gq, d_out, wt, d_out, dx, d_in, T, d_in, d_out, s_g, s_w,
+                                  vreg + pp.p, d_out, r * d_out, r, spb, v, tok ? T4 : r, s, g_fmt,
+                                  tok);
+  } else {
+    if (tr) e = launch_gemm_fp8_nt(gq, d_out, wt, d_out, dx, d_in, T, d_in, d_out, s_g, s_w, s,
+                                   g_fmt);
+    if (e == hipSuccess && want_v)
+      e = launch_one_skinny(gq, d_out, g_fmt, s_g, B, true, T, d_out, r, v, vreg, s);
+  }
+  if (e != hipSuccess || r == 0) return e;
+  if (tok)
+    return launch_token_grads(gq, g_fmt, s_g, xq, s_x, xa, 1, r, true, v, fuse ? T4 : 1,
+                              fuse ? 1 : r, T, d_in, d_out, r, dA, dB, rest, s);
+  return launch_grads_from_uv(gq, g_fmt, s_g, xq, s_x, xa, v, T, d_in, d_out, r, dA, dB, rest, s);
 }
 
 }  // namespace falq

@@ -518,4 +518,93 @@ falq_status lora_bf16_bwd(const float* dy, const uint8_t* gq, const float* s_g, 
                                                d_out, r, dx, dA, dB, ws, s));
 }
 
+// ---- U formed with the forward product, V with the dX product ----------------
+
+int melded_linear_xa_fused(int64_t T, int64_t d_in, int64_t d_out, int64_t r) {
+  if (!gemm_dims_ok(T, d_in, d_out) || T <= 0 || r <= 0 || r > ((int64_t)1 << 20)) return 0;
+  return falq::gemm_fp8_nt_fuses_second(d_out, d_in, r) &&
+         falq::gemm_fp8_nt_fuses_second(d_in, d_out, r) &&
+         !falq::adapter_wide_route(T, d_in, d_out, r);
+}
+
+size_t melded_linear_fwd_xa_workspace_bytes(int64_t T, int64_t d_in, int64_t d_out, int64_t r) {
+  if (T < 0 || d_in < 0 || d_out < 0 || r < 0) return 0;
+  return falq::fwd_xa_ws_bytes(T, d_in, d_out, r);
+}
+
+falq_status melded_linear_fwd_xa(const uint8_t* xq, const float* s_x, const uint8_t* wq,
+                                 const float* s_w, const float* A, int64_t T, int64_t d_in,
+                                 int64_t d_out, int64_t r, float* y, float* xa, void* ws,
+                                 size_t ws_bytes, falq_stream stream) {
+  if (!gemm_dims_ok(T, d_in, d_out) || r < 0 || r > ((int64_t)1 << 20)) return FALQ_EINVAL;
+  if (!scalar(s_x) || !scalar(s_w)) return FALQ_EINVAL;
+  if (T * d_in > 0 && !need(xq)) return FALQ_EINVAL;
+  if (d_out * d_in > 0 && !need(wq)) return FALQ_EINVAL;
+  if (T * d_out > 0 && !need(y)) return FALQ_EINVAL;
+  if (r * d_in > 0 && !need(A)) return FALQ_EINVAL;
+  if (T * r > 0 && !need(xa)) return FALQ_EINVAL;
+  if (!ws_ok(ws, ws_bytes, falq::fwd_xa_ws_bytes(T, d_in, d_out, r))) return FALQ_EINVAL;
+  return hip_status(falq::launch_fwd_xa(xq, s_x, wq, s_w, A, T, d_in, d_out, r, y, xa, ws,
+                                        reinterpret_cast<hipStream_t>(stream)));
+}
+
+size_t melded_linear_bwd_xa_workspace_bytes(int64_t T, int64_t d_in, int64_t d_out, int64_t r) {
+  if (T < 0 || d_in < 0 || d_out < 0 || r < 0) return 0;
+  const size_t wt = align_up((size_t)d_in * (size_t)d_out, 256);      // W~^T for dX
+  return wt + (falq::adapter_wide_route(T, d_in, d_out, r)
+                   ? falq::adapter_wide_ws_bytes(T, d_in, d_out, r)
+                   : falq::bwd_xa_ws_bytes(T, d_in, d_out, r));
+}
+
+falq_status melded_linear_bwd_xa(const uint8_t* gq, int g_fmt, const float* s_g,
+                                 const uint8_t* xq, const float* s_x, const uint8_t* wq,
+                                 const float* s_w, const float* A, const float* B,
+                                 const float* xa, int64_t T, int64_t d_in, int64_t d_out,
+                                 int64_t r, float* dx, float* dA, float* dB, void* ws,
+                                 size_t ws_bytes, falq_stream stream) {
+  if (!fmt_ok(g_fmt)) return FALQ_EINVAL;
+  if (!gemm_dims_ok(T, d_in, d_out) || r < 0 || r > ((int64_t)1 << 20)) return FALQ_EINVAL;
+  if (!scalar(s_g) || !scalar(s_x) || !scalar(s_w)) return FALQ_EINVAL;
+  if (T * d_out > 0 && !need(gq)) return FALQ_EINVAL;
+  if (T * d_in > 0 && !need(xq)) return FALQ_EINVAL;
+  if (d_out * d_in > 0 && dx && !need(wq)) return FALQ_EINVAL;
+  if (!opt(dx) || !opt(dA)) return FALQ_EINVAL;
+  if (r * d_in > 0 && !need(A)) return FALQ_EINVAL;
+  if (r * d_out > 0 && (!need(B) || !need(dB))) return FALQ_EINVAL;
+  if (T * r > 0 && !need(xa)) return FALQ_EINVAL;
+  if (!ws_ok(ws, ws_bytes, melded_linear_bwd_xa_workspace_bytes(T, d_in, d_out, r)))
+    return FALQ_EINVAL;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  uint8_t* base = reinterpret_cast<uint8_t*>(ws);
+  const size_t wt_bytes = align_up((size_t)d_in * (size_t)d_out, 256);
+  const bool grads = r > 0 && T > 0 && d_in > 0 && d_out > 0;
+  const bool wide = grads && falq::adapter_wide_route(T, d_in, d_out, r);
+  const bool gemm_dx = dx && T * d_in > 0 && d_out > 0;
+  hipError_t e = hipSuccess;
+  if (gemm_dx && (!grads || wide)) e = falq::launch_transpose_u8(wq, d_out, d_in, base, s);
+  if (e != hipSuccess) return FALQ_EHIP;
+  if (!grads) {
+    if (gemm_dx) e = falq::launch_gemm_fp8_nt(gq, d_out, base, d_out, dx, d_in, T, d_in, d_out,
+                                              s_g, s_w, s, g_fmt);
+    else if (dx && T * d_in > 0) e = falq::launch_fill_f32(dx, T * d_in, 0.0f, s);
+    if (e == hipSuccess && r > 0) {
+      if (d_out > 0) e = falq::launch_fill_f32(dB, d_out * r, 0.0f, s);
+      if (e == hipSuccess && dA && d_in > 0) e = falq::launch_fill_f32(dA, r * d_in, 0.0f, s);
+    }
+    return hip_status(e);
+  }
+  if (wide) {
+    if (gemm_dx) e = falq::launch_gemm_fp8_nt(gq, d_out, base, d_out, dx, d_in, T, d_in, d_out,
+                                              s_g, s_w, s, g_fmt);
+    if (e == hipSuccess)
+      e = falq::launch_adapter_grads_wide(gq, g_fmt, s_g, xq, s_x, A, B, T, d_in, d_out, r, dA,
+                                          dB, base + wt_bytes, s);
+    return hip_status(e);
+  }
+  // the transpose of W~ runs inside launch_bwd_xa's preparation launch
+  return hip_status(falq::launch_bwd_xa(gq, g_fmt, s_g, xq, s_x, wq, base, s_w, B, xa, T, d_in,
+                                        d_out, r, gemm_dx ? dx : nullptr, dA, dB,
+                                        base + wt_bytes, s));
+}
+
 }  // extern "C"

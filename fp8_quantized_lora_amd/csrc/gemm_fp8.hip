@@ -145,7 +145,7 @@ hipError_t launch_dma(const uint8_t* A, int64_t lda, const uint8_t* B, int64_t l
     const SplitK sk = splitk_plan(nt, (int)(K / gemm::dma::BK));
     if (sk.S > 1) {
       const int64_t ldp = (int64_t)align_up((size_t)N, 4);
-      gemm::dma::gemm_fp8_nt_dma<false, FA, 2><<<nt * sk.S, gemm::dma::kThreads, 0, s>>>(
+      gemm::dma::gemm_fp8_nt_dma<0, FA, 2><<<nt * sk.S, gemm::dma::kThreads, 0, s>>>(
           A, lda, B, ldb, splitk_ws, ldp, (int)M, (int)N, (int)K, sa, sb, tM, tN, nt,
           gemm::dma::SecondB{}, sk.kc);
       hipError_t e = hipGetLastError();
@@ -165,14 +165,14 @@ hipError_t launch_dma(const uint8_t* A, int64_t lda, const uint8_t* B, int64_t l
     if (e != hipSuccess) return e;
   }
   if (full > 0) {
-    gemm::dma::gemm_fp8_nt_dma<false, FA><<<full, gemm::dma::kThreads, 0, s>>>(
+    gemm::dma::gemm_fp8_nt_dma<0, FA><<<full, gemm::dma::kThreads, 0, s>>>(
         A, lda, B, ldb, C, ldc, (int)M, (int)N, (int)K, sa, sb, tM, tN, full,
         gemm::dma::SecondB{}, acc);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (full < nt)
-    gemm::dma::gemm_fp8_nt_dma<false, FA, 1><<<2 * (nt - full), gemm::dma::kThreads, 0, s>>>(
+    gemm::dma::gemm_fp8_nt_dma<0, FA, 1><<<2 * (nt - full), gemm::dma::kThreads, 0, s>>>(
         A, lda, B, ldb, C, ldc, (int)M, (int)N, (int)K, sa, sb, tM, tN, full,
         gemm::dma::SecondB{}, 0);
   return hipGetLastError();
@@ -248,9 +248,30 @@ hipError_t launch_gemm_fp8_nt_second(const uint8_t* A, int64_t lda, const uint8_
   if (!gemm_fp8_nt_fuses_second(N, K, R) || !gemm_shape_ok(M, N, K)) return hipErrorInvalidValue;
   const int tM = (int)((M + gemm::dma::BM - 1) / gemm::dma::BM);
   const int tN = (int)((N + gemm::dma::BN - 1) / gemm::dma::BN);
-  gemm::dma::gemm_fp8_nt_dma<true, 0><<<tM * tN, gemm::dma::kThreads, 0, s>>>(
+  gemm::dma::gemm_fp8_nt_dma<1, 0><<<tM * tN, gemm::dma::kThreads, 0, s>>>(
       A, lda, B, ldb, C, ldc, (int)M, (int)N, (int)K, sa, sb, tM, tN, tM * tN,
-      gemm::dma::SecondB{Bu, ldbu, (int)R, Cu, ldcu, sbu}, 0);
+      gemm::dma::SecondB{Bu, ldbu, 0, (int)R, Cu, ldcu, sbu, nullptr}, 0);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_fp8_nt_pieces(const uint8_t* A, int64_t lda, const uint8_t* B,
+                                     int64_t ldb, float* C, int64_t ldc, int64_t M, int64_t N,
+                                     int64_t K, const float* sa, const float* sb,
+                                     const uint8_t* P, int64_t ldp, int64_t plane, int64_t R,
+                                     const float* sp, float* Cu, int64_t ldcu, hipStream_t s,
+                                     int a_fmt, bool cu_rank_major) {
+  if (M == 0) return hipSuccess;
+  if (!gemm_fp8_nt_fuses_second(N, K, R) || !gemm_shape_ok(M, N, K)) return hipErrorInvalidValue;
+  if (cu_rank_major && ldcu % 4 != 0) return hipErrorInvalidValue;
+  const int tM = (int)((M + gemm::dma::BM - 1) / gemm::dma::BM);
+  const int tN = (int)((N + gemm::dma::BN - 1) / gemm::dma::BN);
+  const gemm::dma::SecondB u{P, ldp, plane, (int)R, Cu, ldcu, nullptr, sp, cu_rank_major ? 1 : 0};
+  if (a_fmt == 0)
+    gemm::dma::gemm_fp8_nt_dma<3, 0><<<tM * tN, gemm::dma::kThreads, 0, s>>>(
+        A, lda, B, ldb, C, ldc, (int)M, (int)N, (int)K, sa, sb, tM, tN, tM * tN, u, 0);
+  else
+    gemm::dma::gemm_fp8_nt_dma<3, 1><<<tM * tN, gemm::dma::kThreads, 0, s>>>(
+        A, lda, B, ldb, C, ldc, (int)M, (int)N, (int)K, sa, sb, tM, tN, tM * tN, u, 0);
   return hipGetLastError();
 }
 

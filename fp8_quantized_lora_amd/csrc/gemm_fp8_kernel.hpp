@@ -202,25 +202,33 @@ __device__ __forceinline__ int swz(int row) { return (row ^ ((row >> 3) & 1)) & 
 constexpr int NW = WGM * WGN, kThreads = NW * 64;
 constexpr int WTM = BM / WGM, WTN = BN / WGN, MB = WTM / 16, NB = WTN / 16;
 constexpr int UR = 16;                                  // rank rows of the second B operand
-constexpr int STAGE = (BM + BN) * BK, STAGE_U = STAGE + UR * BK;
+constexpr int STAGE = (BM + BN) * BK;
+constexpr int MAX_NU = 3;                               // pieces of the second B operand
+static_assert(S * (STAGE + MAX_NU * UR * BK) <= 160 * 1024, "LDS");
 constexpr int AI = BM * BK / 1024 / NW, BI = BN * BK / 1024 / NW;   // DMA instructions / wave / stage
 constexpr int LPS = AI + BI;
-static_assert(S * STAGE_U <= 160 * 1024, "LDS");
 
-// Optional second product against a small second B operand (the frozen
-// adapter factor A~ in the forward: U = dec(X~) dec(A~)^T / (sa * su)).  Its
+// Optional second product against a small second B operand of NU E4M3
+// "pieces" summed on the matrix cores: the frozen adapter factor A~ in the
+// forward (NU = 1: U = dec(X~) dec(A~)^T / (sa * sb)), or a float operand
+// held as NU = 3 E4M3 pieces with one scale per row, sum_p dec(P_p) ~ F * sbv
+// (the trained A in the forward, B^T in the dX product: C2 = dec(A) F^T / sa
+// to within the pieces' residual, about 2^-12 of each element).  Its
 // 16-rank blocks times 64-row quarters of a tile are "units"; the tile in
 // column tn < 4 * ceil(R / 16) takes unit tn: block tn / 4, quarter tn % 4.
 // The quarter's rows are held by the four waves of row group wm = quarter / 2,
-// so each of them issues one more MFMA per K step (on its fragment
-// i = (quarter % 2) * 4 + wn), one per SIMD.
+// so each of them issues NU more MFMAs per K step (on its fragment
+// i = (quarter % 2) * 4 + wn), NU per SIMD.
 struct SecondB {
-  const uint8_t* B;      // [R x K] codes, row stride ldb
+  const uint8_t* B;      // piece 0: [R x K] codes, row stride ldb
   int64_t ldb;
+  int64_t plane;         // bytes from one piece to the next
   int R;
-  float* C;              // [M x R] fp32 output, row stride ldc
-  int64_t ldc;
-  const float* sb;
+  float* C;              // [M x R] fp32 output, row stride ldc; or with ct
+  int64_t ldc;           // [R x M], rank-major, row stride ldc
+  const float* sb;       // one scale for every row (sbv == nullptr)
+  const float* sbv;      // or one scale per row (R of them)
+  int ct;
 };
 
 // FA: format of the A codes (0 = E4M3, 1 = E5M2; B and the second B are
@@ -238,16 +246,18 @@ struct SecondB {
 // [s * acc_c, (s + 1) * acc_c), s = b / tiles, and writes its unscaled partial
 // sums to plane s of C (planes of M * ldc floats); a reduction adds the
 // planes in a fixed order.
-template <bool FU, int FA, int MODE = 0>
+template <int NU, int FA, int MODE = 0>
 __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_nt_dma(
     const uint8_t* __restrict__ A, int64_t lda, const uint8_t* __restrict__ B, int64_t ldb,
     float* __restrict__ C, int64_t ldc, int M, int N, int K, const float* __restrict__ sa,
     const float* __restrict__ sb, int tilesM, int tilesN, int tiles_or_first, SecondB u,
     int acc_c) {
+  constexpr bool FU = NU > 0;
+  static_assert(NU >= 0 && NU <= MAX_NU, "pieces");
   static_assert(!(FU && MODE != 0), "the second product is not split");
   constexpr bool HALF = MODE == 1;
   static_assert(FA != 5 || !FU, "no second product with bf16 operands");
-  constexpr int SB = FU ? STAGE_U : STAGE;                 // bytes per LDS stage
+  constexpr int SB = STAGE + NU * UR * BK;                 // bytes per LDS stage
   __shared__ __attribute__((aligned(1024))) uint8_t smem[S * SB];
   int tm, tn, k_lo = 0, nk = K / BK;
   if constexpr (HALF) {
@@ -296,13 +306,14 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_nt_dma(
     const int row = (w * BI + j) * 8 + lrow;
     gB[j] = B + (int64_t)min(n0 + row, N - 1) * ldb + k_lo * BK + ((lslot ^ swz(row)) * 16);
   }
-  // the 16 rank rows of the unit's block: waves 0 and 1 load 8 rows each
-  const bool load_u = __builtin_amdgcn_readfirstlane((int)(has_u && w < 2)) != 0;
+  // the 16 rank rows of the unit's block in each piece: waves 2p and 2p + 1
+  // load 8 rows each of piece p
+  const bool load_u = __builtin_amdgcn_readfirstlane((int)(has_u && w < 2 * NU)) != 0;
   const uint8_t* gU = nullptr;
   if (FU && load_u) {
-    const int row = w * 8 + lrow;
-    gU = u.B + (int64_t)min(ub * UR + row, u.R - 1) * u.ldb + k_lo * BK +
-         ((lslot ^ swz(row)) * 16);
+    const int row = (w & 1) * 8 + lrow;
+    gU = u.B + (int64_t)(w >> 1) * u.plane + (int64_t)min(ub * UR + row, u.R - 1) * u.ldb +
+         k_lo * BK + ((lslot ^ swz(row)) * 16);
   }
   auto issue = [&](int stage, int k0) {
     const uint32_t base = lds_offset(smem + stage * SB);
@@ -359,7 +370,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_nt_dma(
   // treats each step's LDS reads as returning in order and waits only for the
   // fragments the next MFMA needs.
   const float scale = (FA == 5 || MODE == 2) ? 1.0f : 1.0f / (sa[0] * sb[0]);
-  const float scale_u = FU ? 1.0f / (sa[0] * u.sb[0]) : 0.0f;
+  const float scale_u = (FU && u.sbv == nullptr) ? 1.0f / (sa[0] * u.sb[0]) : 0.0f;
   v4f accu;
 #pragma unroll
   for (int v = 0; v < 4; ++v) accu[v] = 0.0f;
@@ -374,14 +385,17 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_nt_dma(
     // A(i+1) ahead of the MFMAs on A(i)); scheduling barriers keep the
     // compiler from reordering them, so the first MFMA waits for 4 reads,
     // not 12.
-    v8i bf[NB], af[2], bu;
+    v8i bf[NB], af[2], bu[NU > 0 ? NU : 1];
     af[0] = frag(st + offA);
 #pragma unroll
     for (int j = 0; j < NB; ++j) {
       bf[j] = frag(st + offB + j * 16 * BK);
       __builtin_amdgcn_sched_barrier(0);
     }
-    if (FU && wave_u) bu = frag(st + offU);
+    if (FU && wave_u) {
+#pragma unroll
+      for (int p = 0; p < NU; ++p) bu[p] = frag(st + offU + p * UR * BK);
+    }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < MB; ++i) {
@@ -389,9 +403,12 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_nt_dma(
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int j = 0; j < NB; ++j) acc[i][j] = mma(af[i & 1], bf[j], acc[i][j]);
-      if (FU && wave_u && i == iu)
-        accu = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[i & 1], bu, accu, FA, 0, 0, 0, 0,
-                                                                0);
+      if (FU && wave_u && i == iu) {
+#pragma unroll
+        for (int p = 0; p < NU; ++p)
+          accu = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[i & 1], bu[p], accu, FA, 0, 0,
+                                                                  0, 0, 0);
+      }
       __builtin_amdgcn_sched_barrier(0);
       // the next stage's direct loads go out once this step's first
       // fragments are in registers (an inline-asm load ahead of the first
@@ -427,10 +444,18 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_nt_dma(
   if (FU && wave_u) {
     const int rank = ub * UR + (lane & 15);
     if (rank < u.R) {
+      const float su = u.sbv ? 1.0f / (sa[0] * u.sbv[rank]) : scale_u;
+      const int row0 = m0 + uq * 64 + wn * 16 + 4 * (lane >> 4);
+      if (u.ct && row0 + 3 < M) {
+        // rank-major: the lane's four rows are consecutive (ldc a multiple of 4)
+        *reinterpret_cast<v4f*>(u.C + (int64_t)rank * u.ldc + row0) = accu * su;
+      } else {
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int row = m0 + uq * 64 + wn * 16 + 4 * (lane >> 4) + v;
-        if (row < M) u.C[(int64_t)row * u.ldc + rank] = accu[v] * scale_u;
+        for (int v = 0; v < 4; ++v) {
+          const int row = row0 + v;
+          if (row < M)
+            u.C[u.ct ? (int64_t)rank * u.ldc + row : (int64_t)row * u.ldc + rank] = accu[v] * su;
+        }
       }
     }
   }

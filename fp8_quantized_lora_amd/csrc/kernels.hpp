@@ -79,12 +79,49 @@ hipError_t launch_gemm_fp8_nt_second(const uint8_t* A, int64_t lda, const uint8_
                                      const float* sa, const float* sb, const uint8_t* Bu,
                                      int64_t ldbu, int64_t R, float* Cu, int64_t ldcu,
                                      const float* sbu, hipStream_t s);
+// C = dec(A) dec(B)^T / (sa sb) as launch_gemm_fp8_nt, and in the same tiles
+// Cu [M x R] = dec(A) F^T / sa for a float operand F [R x K] held as three
+// E4M3 piece planes P (row stride ldp, planes `plane` bytes apart) with the
+// per-row scales sp: sum_p dec(P_p[j, :]) ~ F[j, :] * sp[j].  Requires
+// gemm_fp8_nt_fuses_second(N, K, R); a_fmt as launch_gemm_fp8_nt.
+hipError_t launch_gemm_fp8_nt_pieces(const uint8_t* A, int64_t lda, const uint8_t* B,
+                                     int64_t ldb, float* C, int64_t ldc, int64_t M, int64_t N,
+                                     int64_t K, const float* sa, const float* sb,
+                                     const uint8_t* P, int64_t ldp, int64_t plane, int64_t R,
+                                     const float* sp, float* Cu, int64_t ldcu, hipStream_t s,
+                                     int a_fmt, bool cu_rank_major = false);
 // out[cols x rows] = in[rows x cols]^T (bytes; rows and cols multiples of 16)
 hipError_t launch_transpose_u8(const uint8_t* in, int64_t rows, int64_t cols, uint8_t* out,
                                hipStream_t s);
 
 // ---- adapter gradients ----------------------------------------------------
 size_t adapter_grad_ws_bytes(int64_t T, int64_t d_in, int64_t d_out, int64_t r);
+// U = X^ A^T with the forward product, V = G^ B with the dX product
+size_t fwd_xa_ws_bytes(int64_t T, int64_t d_in, int64_t d_out, int64_t r);
+hipError_t launch_fwd_xa(const uint8_t* xq, const float* s_x, const uint8_t* wq, const float* s_w,
+                         const float* A, int64_t T, int64_t d_in, int64_t d_out, int64_t r,
+                         float* y, float* xa, void* ws, hipStream_t s);
+// dB = G^^T U and dA = V^T X^ from U, V [T x r] (float32) on the FP8 matrix
+// cores with the LDS transpose read (token_grad.hip); dA may be null.
+// Needs d_in and d_out multiples of 128.
+bool token_grads_ok(int64_t T, int64_t d_in, int64_t d_out, int64_t r);
+size_t token_grads_ws_bytes(int64_t T, int64_t d_in, int64_t d_out, int64_t r);
+// U, V given by strides: element (t, j) at u[j * u_rs + t * u_cs]; with
+// u_ready the U pieces are in place already (token_grads_u_pieces: where).
+hipError_t launch_token_grads(const uint8_t* gq, int g_fmt, const float* s_g, const uint8_t* xq,
+                              const float* s_x, const float* u, int64_t u_rs, int64_t u_cs,
+                              bool u_ready, const float* v, int64_t v_rs, int64_t v_cs,
+                              int64_t T, int64_t d_in, int64_t d_out, int64_t r, float* dA,
+                              float* dB, void* ws, hipStream_t s);
+// the U pieces' place in the workspace: [3][Rp][Tp] codes at *P, scales at *sp
+void token_grads_u_pieces(void* ws, int64_t T, int64_t d_in, int64_t d_out, int64_t r,
+                          uint8_t** P, float** sp, int64_t* Rp, int64_t* Tp);
+size_t bwd_xa_ws_bytes(int64_t T, int64_t d_in, int64_t d_out, int64_t r);
+// wq is transposed into wt (d_in x d_out bytes) when dx is wanted
+hipError_t launch_bwd_xa(const uint8_t* gq, int g_fmt, const float* s_g, const uint8_t* xq,
+                         const float* s_x, const uint8_t* wq, uint8_t* wt, const float* s_w,
+                         const float* B, const float* xa, int64_t T, int64_t d_in, int64_t d_out,
+                         int64_t r, float* dx, float* dA, float* dB, void* ws, hipStream_t s);
 // large ranks: through the full weight gradient M = G^^T X^ (adapter_grad_wide.hip)
 bool adapter_wide_route(int64_t T, int64_t d_in, int64_t d_out, int64_t r);
 size_t adapter_wide_ws_bytes(int64_t T, int64_t d_in, int64_t d_out, int64_t r);

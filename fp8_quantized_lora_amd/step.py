@@ -8,6 +8,12 @@ B [d_out x r] (B doubles as the row-wise proxy).  A step is
     -> melded_linear_bwd -> adapter_step (SGD) or adapter_step_adamw
     -> rowwise_proxy_update
 
+With A trained and a shape whose GEMM tile grid allows it
+(melded_linear_xa_fused), the forward is melded_linear_fwd_xa, which also
+forms X^ A^T inside the forward FP8 product, and the backward
+melded_linear_bwd_xa, which forms G^ B inside the dX product: the skinny
+row-wise pass of melded_linear_bwd is not needed.
+
 With fp8_a=True (the pages' training setup: A frozen and held in FP8), A is
 quantized once to A~ at init, the forward is melded_linear_fwd_frozen_a (Y and
 U = X~ A~^T), the backward melded_linear_bwd_frozen_a (dX and dB from U), and
@@ -24,6 +30,8 @@ from typing import Optional
 import torch
 
 from . import (fp8_quantize, fp8_quantize_workspace_bytes, fp8_dequantize, melded_linear_fwd,
+               melded_linear_xa_fused, melded_linear_fwd_xa, melded_linear_bwd_xa,
+               melded_linear_fwd_xa_workspace_bytes, melded_linear_bwd_xa_workspace_bytes,
                melded_linear_bwd, melded_linear_bwd_workspace_bytes, melded_linear_fwd_frozen_a,
                melded_linear_fwd_frozen_a_workspace_bytes, melded_linear_bwd_frozen_a,
                melded_linear_bwd_frozen_a_workspace_bytes, adapter_step, adapter_step_adamw,
@@ -87,9 +95,17 @@ class MeldedLinear:
         # workspaces
         nq = max(tokens * max(d_in, d_out), d_out * d_in)
         self.ws_q = torch.empty(fp8_quantize_workspace_bytes(nq), dtype=u8, device=dev)
+        # X^ A^T with the forward product, G^ B with the dX product
+        self.use_xa = (not fp8_a and train_a and tokens > 0
+                       and melded_linear_xa_fused(tokens, d_in, d_out, rank))
         if fp8_a:
             fw = melded_linear_fwd_frozen_a_workspace_bytes(tokens, d_in, rank)
             bw = melded_linear_bwd_frozen_a_workspace_bytes(tokens, d_in, d_out, rank)
+            self.ws_fwd = torch.empty(max(1, fw), dtype=u8, device=dev)
+        elif self.use_xa:
+            self.xa = torch.empty((tokens, rank), dtype=f32, device=dev)
+            fw = melded_linear_fwd_xa_workspace_bytes(tokens, d_in, d_out, rank)
+            bw = melded_linear_bwd_xa_workspace_bytes(tokens, d_in, d_out, rank)
             self.ws_fwd = torch.empty(max(1, fw), dtype=u8, device=dev)
         else:
             bw = melded_linear_bwd_workspace_bytes(tokens, d_in, d_out, rank)
@@ -115,22 +131,40 @@ class MeldedLinear:
 
     def forward(self, X: torch.Tensor, stream=None):
         fp8_quantize(X, self.xq, self.s_x, ws=self.ws_q, stream=stream)
+        self.forward_product(stream)
+        return self.y
+
+    def forward_product(self, stream=None):
+        """The forward call on the quantized activations (Y, and X^ A^T or
+        X~ A~^T where the route forms it)."""
         if self.fp8_a:
             melded_linear_fwd_frozen_a(self.xq, self.s_x, self.wq, self.s_w, self.aq, self.s_a,
                                        self.y, self.u, ws=self.ws_fwd, stream=stream)
+        elif self.use_xa:
+            melded_linear_fwd_xa(self.xq, self.s_x, self.wq, self.s_w, self.A, self.y, self.xa,
+                                 ws=self.ws_fwd, stream=stream)
         else:
             melded_linear_fwd(self.xq, self.s_x, self.wq, self.s_w, self.y, stream=stream)
-        return self.y
 
     def backward(self, dY: torch.Tensor, stream=None):
         fp8_quantize(dY, self.gq, self.s_g, ws=self.ws_q, stream=stream, fmt=self.g_fmt)
+        self.backward_product(stream)
+        return self.dx
+
+    def backward_product(self, stream=None):
+        """The backward call on the quantized upstream gradient (dX, dB and,
+        with A trained, dA)."""
         if self.fp8_a:
             melded_linear_bwd_frozen_a(self.gq, self.s_g, self.wq, self.s_w, self.u, self.dx,
                                        self.dB, ws=self.ws_bwd, stream=stream, g_fmt=self.g_fmt)
-            return self.dx
-        melded_linear_bwd(self.gq, self.s_g, self.xq, self.s_x, self.wq, self.s_w, self.A, self.B,
-                          self.dx, self.dA, self.dB, ws=self.ws_bwd, stream=stream, g_fmt=self.g_fmt)
-        return self.dx
+        elif self.use_xa:
+            melded_linear_bwd_xa(self.gq, self.s_g, self.xq, self.s_x, self.wq, self.s_w, self.A,
+                                 self.B, self.xa, self.dx, self.dA, self.dB, ws=self.ws_bwd,
+                                 stream=stream, g_fmt=self.g_fmt)
+        else:
+            melded_linear_bwd(self.gq, self.s_g, self.xq, self.s_x, self.wq, self.s_w, self.A,
+                              self.B, self.dx, self.dA, self.dB, ws=self.ws_bwd, stream=stream,
+                              g_fmt=self.g_fmt)
 
     def adapter_update(self, lr: float, stream=None):
         if self.optimizer == "sgd":

@@ -241,6 +241,42 @@ falq_status melded_linear_bwd_fmt(const uint8_t *gq, int g_fmt, const float *s_g
                                   void *ws, size_t ws_bytes, falq_stream stream);
 
 /*
+ * melded_linear_fwd_xa / melded_linear_bwd_xa — the forward and backward of
+ * melded_linear_fwd / melded_linear_bwd with the x A^T factor of dL/dB formed
+ * in the forward ([rebuttal] thread 4, Q1: unlike dL/dA, that factor can be
+ * computed ahead) and handed to the backward:
+ *     forward:   Y as melded_linear_fwd, and XA = X^ A^T      [T x r]
+ *     backward:  dX as melded_linear_bwd, dB = G^^T XA, dA = (G^ B)^T X^
+ * Results equal melded_linear_fwd / _bwd to within the float32 tolerance
+ * (U and V are the same sums).  Where the GEMM tile grid allows
+ * (melded_linear_xa_fused returns 1: r <= d_out / 64 and r <= d_in / 64, K
+ * multiples of 128, and no large-rank route), X^ A^T is formed inside the
+ * forward FP8 product and G^ B inside the dX product, with the float factor
+ * entering the FP8 matrix cores as three E4M3 pieces per element and one
+ * scale per rank (residual about 2^-12 of an element); otherwise by the
+ * skinny kernels.  For ranks where melded_linear_bwd takes the full weight
+ * gradient route, the backward takes it too and does not read xa.
+ *
+ *   A [r x d_in], B [d_out x r] float32; xa [T x r] float32 (output of the
+ *   forward, input of the backward); g_fmt FALQ_E4M3 or FALQ_E5M2 for gq.
+ *   Other arguments as melded_linear_fwd / melded_linear_bwd_fmt; workspaces
+ *   of the matching *_workspace_bytes.
+ */
+int melded_linear_xa_fused(int64_t T, int64_t d_in, int64_t d_out, int64_t r);
+size_t melded_linear_fwd_xa_workspace_bytes(int64_t T, int64_t d_in, int64_t d_out, int64_t r);
+falq_status melded_linear_fwd_xa(const uint8_t *xq, const float *s_x, const uint8_t *wq,
+                                 const float *s_w, const float *A, int64_t T, int64_t d_in,
+                                 int64_t d_out, int64_t r, float *y, float *xa, void *ws,
+                                 size_t ws_bytes, falq_stream stream);
+size_t melded_linear_bwd_xa_workspace_bytes(int64_t T, int64_t d_in, int64_t d_out, int64_t r);
+falq_status melded_linear_bwd_xa(const uint8_t *gq, int g_fmt, const float *s_g,
+                                 const uint8_t *xq, const float *s_x, const uint8_t *wq,
+                                 const float *s_w, const float *A, const float *B,
+                                 const float *xa, int64_t T, int64_t d_in, int64_t d_out,
+                                 int64_t r, float *dx, float *dA, float *dB, void *ws,
+                                 size_t ws_bytes, falq_stream stream);
+
+/*
  * The pages' training setup: A frozen and held in FP8 ([rebuttal] thread 4,
  * Q1: A is frozen, and the x A^T factor of dL/dB, unlike dL/dA, can be
  * computed ahead; thread 2, W1/W9: Figure 2 joins X~ to W~ and to A~ by

@@ -22,10 +22,12 @@ def test_more_than_one_gpu_exits_with_a_message():
 def test_traffic_is_reported_only_for_the_measured_sources(monkeypatch):
     # the committed summary records the digest of the GEMM sources it was
     # measured on; any other digest (changed sources) gives no traffic figure
-    measured = bench.gemm_traffic_bytes()
-    assert measured is None or measured > 96 * 2**20      # at least the algorithmic bytes
+    # and on the forward route it was measured on
+    measured = [bench.gemm_traffic_bytes(f) for f in (False, True)]
+    assert None in measured                               # one route only
+    assert all(v is None or v > 96 * 2**20 for v in measured)   # >= the algorithmic bytes
     monkeypatch.setattr(bench, "gemm_sources_digest", lambda: "0" * 64)
-    assert bench.gemm_traffic_bytes() is None
+    assert bench.gemm_traffic_bytes(False) is None and bench.gemm_traffic_bytes(True) is None
 
 
 @pytest.mark.parametrize("argv", [["--workload", "mlp7b"], ["--workload", "rank-sweep"],

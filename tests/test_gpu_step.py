@@ -1,19 +1,19 @@
 """Whole steps chained on the GPU (MeldedLinear) against the oracle's chain.
 
 Per call on identical inputs the results are bit-exact (codes, rows) or within
-rel-L2 1e-3 (floats).  Within a step, the oracle's dA/dB differ from the
-GPU's at the 1e-6 level, so after SGD (or AdamW) its B differs by as little, and two
-things may then legitimately differ: a row whose score sits at the threshold
-may be selected by one side only, and a merged element whose dec(q) + t sits
-at a rounding midpoint may round to the neighbouring code.  The test asserts
-that every difference is of one of these two kinds, and that Y, dX, dA, dB
-stay within 1e-3.  Each step restarts the oracle from the GPU's state, so the
-comparison does not compound."""
+rel-L2 1e-3 (floats).  The float gradients dA, dB agree with the oracle's own
+to that bound, not bit for bit, and an adapter moved by a rounding-level
+amount may legitimately flip a row whose score sits at the threshold or a
+merged code whose dec(q) + t sits at a rounding midpoint.  So the oracle's
+optimizer takes the GPU's gradients (checked against the oracle's own, rel-L2
+<= 1e-3), after which the adapters (and AdamW moments), the row scores, the
+selected rows and the backbone codes must agree bit for bit.  Each step
+restarts the oracle from the GPU's state, so the comparison does not
+compound."""
 import numpy as np
 import pytest
 
 import oracle
-from oracle import e4m3
 from tests.gpu_util import TOL, announce, dev, host, rel_l2
 import workloads as wl
 
@@ -60,46 +60,23 @@ def run_chain(fq, cfg_id, steps, optimizer="sgd"):
     for step in range(steps):
         d = wl.step_activations(cfg_id, 0, spec, step)
         m.step(dev(d["X"]), dev(d["dY"]), lr=spec.lr, tau=spec.tau, k_max=spec.k_max)
-        wq_before = st["wq"]
-        # AdamW's first steps move each element by about lr * sign(g), so a
-        # gradient entry within rounding of zero may step either way: its
-        # optimizer takes the GPU's gradients (checked against the oracle's
-        # below), after which the adapters, moments, scores and codes must
-        # agree bit for bit
-        grads = (host(m.dA), host(m.dB)) if optimizer == "adamw" else None
+        grads = (host(m.dA), host(m.dB))
         st, out = oracle_step(st, d["X"], d["dY"], spec.lr, spec.tau, spec.k_max,
                               opt_step=0 if optimizer == "sgd" else step + 1, grads=grads)
         e = (rel_l2(host(m.y), out["y"]), rel_l2(host(m.dx), out["dx"]),
-             rel_l2(host(m.dA), out["dA"]), rel_l2(host(m.dB), out["dB"]))
+             rel_l2(grads[0], out["dA"]), rel_l2(grads[1], out["dB"]))
         n_sel = int(host(m.n_sel)[0])
         g_sel = host(m.sel)[:n_sel]
-        flips = np.setxor1d(g_sel, out["sel"])
-        margin = np.abs(out["rho"][flips] - spec.tau) / spec.tau
-        both = np.intersect1d(g_sel, out["sel"])
         g_wq = host(m.wq)
-        di, dj = np.nonzero(g_wq[both] != st["wq"][both])
-        rows, cols = both[di], dj
-        qg, qo = g_wq[rows, cols], st["wq"][rows, cols]
-        vg, vo = e4m3.DECODE_F64[qg], e4m3.DECODE_F64[qo]
-        v = e4m3.DECODE_F64[wq_before[rows, cols]] + out["t"][rows, cols].astype(np.float64)
-        mid = 0.5 * (vg + vo)
-        step_at = e4m3.step_of(np.abs(mid))
-        adjacent = np.abs(vg - vo) <= step_at * 1.0000001 + 0.0
-        near_mid = np.abs(v - mid) <= 1e-3 * (np.abs(out["t"][rows, cols]) + step_at)
         print(f"step {step}: rel-L2 Y {e[0]:.2e} dX {e[1]:.2e} dA {e[2]:.2e} dB {e[3]:.2e}; "
-              f"selected {n_sel}/{spec.d_out}, threshold flips {flips.size}, midpoint "
-              f"re-roundings {rows.size} in {np.unique(rows).size} rows")
+              f"selected {n_sel}/{spec.d_out}")
         assert max(e) <= TOL
-        assert np.all(margin < 1e-3), (flips, margin)
-        assert np.all(adjacent), "a merged code differs by more than one step"
-        assert np.all(near_mid), "a merged code differs away from a rounding midpoint"
-        assert rows.size <= 1e-4 * max(1, both.size) * spec.d_in
-        if optimizer == "adamw":
-            assert flips.size == 0 and rows.size == 0
-            for k, t in (("A", m.A), ("B", m.B), ("mA", m.mA), ("vA", m.vA), ("mB", m.mB),
-                         ("vB", m.vB)):
-                assert np.array_equal(host(t).view(np.uint32), st[k].view(np.uint32)), k
-            assert np.array_equal(host(m.rho).view(np.uint32), out["rho"].view(np.uint32))
+        assert np.array_equal(g_sel, out["sel"])
+        assert np.array_equal(g_wq, st["wq"])
+        keys = ("A", "B") + (("mA", "vA", "mB", "vB") if optimizer == "adamw" else ())
+        for k in keys:
+            assert np.array_equal(host(getattr(m, k)).view(np.uint32), st[k].view(np.uint32)), k
+        assert np.array_equal(host(m.rho).view(np.uint32), out["rho"].view(np.uint32))
         st = dict(wq=g_wq, s_w=st["s_w"], A=host(m.A), B=host(m.B))
         if optimizer == "adamw":
             st.update(mA=host(m.mA), vA=host(m.vA), mB=host(m.mB), vB=host(m.vB))

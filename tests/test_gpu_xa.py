@@ -1,0 +1,168 @@
+"""melded_linear_fwd_xa / melded_linear_bwd_xa on the GPU against the oracle.
+
+The pair computes what melded_linear_fwd + melded_linear_bwd compute, with
+the rank-r factor X^ A^T formed in the forward call (inside the FP8 product's
+tiles where the shape allows) and handed to the backward call, which forms
+G^ B inside the dX product.  Checked here: Y per element against the FP8
+product bound, X^ A^T against its exact value (rel-L2, per rank column), and
+dX, dA, dB against oracle.melded_linear_bwd (rel-L2 <= 1e-3, per rank
+component for dA and dB), on shapes that take the fused route and on shapes
+that fall back to the separate kernels."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import e4m3
+from tests.gpu_util import (TOL, announce, check_elementwise, dev, gemm_bound, host, nan_f32,
+                            rel_l2, rel_l2_rank, scalar)
+from tests.test_gpu_linear import quantized_problem
+import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+
+def gpu_pair(fq, p, g_fmt="e4m3", gq=None, s_g=None):
+    gq = p["gq"] if gq is None else gq
+    s_g = p["s_g"] if s_g is None else s_g
+    T, d_in = p["xq"].shape
+    d_out = p["wq"].shape[0]
+    r = p["A"].shape[0]
+    xq, wq, A, B = dev(p["xq"]), dev(p["wq"]), dev(p["A"]), dev(p["B"])
+    sx, sw = scalar(p["s_x"]), scalar(p["s_w"])
+    y, xa = nan_f32((T, d_out)), nan_f32((T, r))
+    fq.melded_linear_fwd_xa(xq, sx, wq, sw, A, y, xa)
+    dx, dA, dB = nan_f32((T, d_in)), nan_f32((r, d_in)), nan_f32((d_out, r))
+    fq.melded_linear_bwd_xa(dev(gq), scalar(s_g), xq, sx, wq, sw, A, B, xa, dx, dA, dB,
+                            g_fmt=g_fmt)
+    return host(y), host(xa), host(dx), host(dA), host(dB)
+
+
+def exact_xa(p):
+    return e4m3.decode(p["xq"]) @ np.asarray(p["A"], np.float64).T / np.float64(p["s_x"])
+
+
+XA_SHAPES = [  # (T, d_in, d_out, r, fused)
+    (512, 1024, 1024, 16, True),
+    (600, 1024, 1280, 16, True),      # ragged T and a 5-tile N
+    (1024, 2048, 2048, 32, True),
+    (384, 2048, 1024, 13, True),      # rank not a multiple of the 16-row piece tile
+    (256, 512, 512, 16, False),       # too few column tiles to carry the pieces
+    (257, 400, 272, 5, False),        # K not a multiple of 128
+    (300, 384, 640, 8, False),
+    (512, 512, 384, 100, False),      # two 64-rank tiles, the second ragged
+]
+
+
+@pytest.mark.parametrize("T,d_in,d_out,r,fused", XA_SHAPES)
+def test_xa_pair_parity(gpu_lib, T, d_in, d_out, r, fused):
+    announce(f"fwd_xa/bwd_xa T={T} d_in={d_in} d_out={d_out} r={r}")
+    assert gpu_lib.melded_linear_xa_fused(T, d_in, d_out, r) == fused
+    p = quantized_problem(T + 3 * r, T, d_in, d_out, r, b_std=0.5)
+    y, xa, dx, dA, dB = gpu_pair(gpu_lib, p)
+    ref_y = oracle.melded_linear_fwd(p["xq"], p["s_x"], p["wq"], p["s_w"])
+    worst_y = check_elementwise(
+        y, ref_y, gemm_bound(e4m3.decode(p["xq"]), e4m3.decode(p["wq"]),
+                             np.float64(p["s_x"]) * np.float64(p["s_w"]), ref_y), "Y")
+    xa64 = exact_xa(p)
+    e_xa = (rel_l2(xa, xa64), rel_l2_rank(xa, xa64, 1))
+    rdx, rdA, rdB = oracle.melded_linear_bwd(p["gq"], p["s_g"], p["xq"], p["s_x"], p["wq"],
+                                             p["s_w"], p["A"], p["B"])
+    worst_dx = check_elementwise(
+        dx, rdx, gemm_bound(e4m3.decode(p["gq"]), e4m3.decode(p["wq"]).T,
+                            np.float64(p["s_g"]) * np.float64(p["s_w"]), rdx), "dX")
+    e = (rel_l2(dx, rdx), rel_l2(dA, rdA), rel_l2(dB, rdB), rel_l2_rank(dA, rdA, 0),
+         rel_l2_rank(dB, rdB, 1))
+    print("xa pair: X^A^T rel-L2 %.2e (per rank %.2e); dX %.2e dA %.2e dB %.2e (per rank %.2e "
+          "%.2e); worst / bound Y %.3f dX %.3f" % (e_xa + e + (worst_y, worst_dx)))
+    assert max(e_xa) <= TOL and max(e) <= TOL
+
+
+def test_xa_pair_e5m2_gradient(gpu_lib):
+    """The fused backward with an E5M2 upstream gradient (G~ the E5M2 operand
+    of the dX product that also forms G^ B)."""
+    T, d_in, d_out, r = 512, 1024, 1024, 16
+    announce(f"fwd_xa/bwd_xa E5M2 gradient T={T} d={d_in} r={r}")
+    assert gpu_lib.melded_linear_xa_fused(T, d_in, d_out, r)
+    p = quantized_problem(77, T, d_in, d_out, r, b_std=0.5)
+    dY = (np.random.default_rng(78).standard_normal((T, d_out)) * 1e-2).astype(np.float32)
+    gq, s_g, _, _ = oracle.fp8_quantize(dY, fmt="e5m2")
+    _, _, dx, dA, dB = gpu_pair(gpu_lib, p, g_fmt="e5m2", gq=gq, s_g=s_g)
+    rdx, rdA, rdB = oracle.melded_linear_bwd(gq, s_g, p["xq"], p["s_x"], p["wq"], p["s_w"],
+                                             p["A"], p["B"], g_fmt="e5m2")
+    e = (rel_l2(dx, rdx), rel_l2(dA, rdA), rel_l2(dB, rdB), rel_l2_rank(dA, rdA, 0),
+         rel_l2_rank(dB, rdB, 1))
+    print("xa pair E5M2: dX %.2e dA %.2e dB %.2e (per rank %.2e %.2e)" % e)
+    assert max(e) <= TOL
+
+
+def test_xa_pair_agrees_with_unfused_calls(gpu_lib):
+    """Same inputs through melded_linear_fwd + melded_linear_bwd: Y is the
+    same FP8 product (bit for bit), and the gradients agree to the two
+    routes' rounding."""
+    T, d_in, d_out, r = 512, 1024, 1024, 16
+    announce(f"fwd_xa/bwd_xa against fwd/bwd T={T} d={d_in} r={r}")
+    p = quantized_problem(91, T, d_in, d_out, r, b_std=0.5)
+    y, _, dx, dA, dB = gpu_pair(gpu_lib, p)
+    fq = gpu_lib
+    y1 = nan_f32((T, d_out))
+    fq.melded_linear_fwd(dev(p["xq"]), scalar(p["s_x"]), dev(p["wq"]), scalar(p["s_w"]), y1)
+    dx1, dA1, dB1 = nan_f32((T, d_in)), nan_f32((r, d_in)), nan_f32((d_out, r))
+    fq.melded_linear_bwd(dev(p["gq"]), scalar(p["s_g"]), dev(p["xq"]), scalar(p["s_x"]),
+                         dev(p["wq"]), scalar(p["s_w"]), dev(p["A"]), dev(p["B"]), dx1, dA1, dB1)
+    assert np.array_equal(y, host(y1))
+    assert np.array_equal(dx, host(dx1))
+    assert rel_l2(dA, host(dA1)) <= TOL and rel_l2(dB, host(dB1)) <= TOL
+
+
+def test_xa_pair_degenerate(gpu_lib):
+    announce("fwd_xa/bwd_xa degenerate: r=0, T=0, B=0")
+    p = quantized_problem(5, 100, 64, 48, 0)
+    y, xa, dx, dA, dB = gpu_pair(gpu_lib, p)
+    ref_y = oracle.melded_linear_fwd(p["xq"], p["s_x"], p["wq"], p["s_w"])
+    rdx, _, _ = oracle.melded_linear_bwd(p["gq"], p["s_g"], p["xq"], p["s_x"], p["wq"], p["s_w"],
+                                         p["A"], p["B"])
+    assert xa.size == dA.size == dB.size == 0
+    assert rel_l2(y, ref_y) <= TOL and rel_l2(dx, rdx) <= TOL
+    p = quantized_problem(6, 0, 1024, 1024, 16)
+    y, xa, dx, dA, dB = gpu_pair(gpu_lib, p)
+    assert y.size == 0 and not dA.any() and not dB.any()
+    p = quantized_problem(7, 512, 1024, 1024, 16, b_std=0.0)
+    _, _, _, dA, _ = gpu_pair(gpu_lib, p)
+    assert not dA.any()            # B = 0 => G^ B = 0 => dA = 0 exactly
+
+
+def test_xa_pair_full_size_attention_projection(gpu_lib):
+    """The 7B attention projection (4096 x 4096 weight, 4096 tokens with
+    outlier channels, r = 64) through the fused pair: sampled rows of Y and
+    dX against the oracle row by row (each row depends on its own row of X~
+    or G~ only), X^ A^T and dA, dB complete."""
+    spec = wl.WORKLOADS[2].linears[0]
+    T, d_in, d_out, r = spec.tokens, spec.d_in, spec.d_out, spec.rank
+    announce(f"fwd_xa/bwd_xa full size T={T} d_in={d_in} d_out={d_out} r={r}")
+    assert gpu_lib.melded_linear_xa_fused(T, d_in, d_out, r)
+    d = wl.make_linear(2, 0, spec, step=0)
+    wq, s_w, _, _ = oracle.fp8_quantize(d["W"])
+    xq, s_x, _, _ = oracle.fp8_quantize(d["X"])
+    gq, s_g, _, _ = oracle.fp8_quantize(d["dY"])
+    p = dict(wq=wq, s_w=s_w, xq=xq, s_x=s_x, gq=gq, s_g=s_g, A=d["A"], B=d["B"])
+    y, xa, dx, dA, dB = gpu_pair(gpu_lib, p)
+    rows = np.random.default_rng(12).choice(T, 96, replace=False)
+    ref_y = oracle.melded_linear_fwd(xq[rows], s_x, wq, s_w)
+    check_elementwise(y[rows], ref_y,
+                      gemm_bound(e4m3.decode(xq[rows]), e4m3.decode(wq),
+                                 np.float64(s_x) * np.float64(s_w), ref_y), "Y")
+    rdx, _, _ = oracle.melded_linear_bwd(gq[rows], s_g, xq[rows], s_x, wq, s_w, p["A"], p["B"],
+                                         want_da=False)
+    check_elementwise(dx[rows], rdx,
+                      gemm_bound(e4m3.decode(gq[rows]), e4m3.decode(wq).T,
+                                 np.float64(s_g) * np.float64(s_w), rdx), "dX")
+    xa64 = exact_xa(p)
+    _, rdA, rdB = oracle.melded_linear_bwd(gq, s_g, xq, s_x, wq, s_w, p["A"], p["B"],
+                                           want_dx=False)
+    e = (rel_l2(y[rows], ref_y), rel_l2(dx[rows], rdx), rel_l2(xa, xa64),
+         rel_l2_rank(xa, xa64, 1), rel_l2(dA, rdA), rel_l2(dB, rdB), rel_l2_rank(dA, rdA, 0),
+         rel_l2_rank(dB, rdB, 1))
+    print("full-size xa pair: Y %.2e dX %.2e X^A^T %.2e (per rank %.2e) dA %.2e dB %.2e "
+          "(per rank %.2e %.2e)" % e)
+    assert max(e) <= TOL
