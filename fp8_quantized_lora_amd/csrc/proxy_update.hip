@@ -21,6 +21,8 @@
 //                 lower row), compacted in row order;
 //  proxy_apply    selected rows only: copy the staged codes into the backbone
 //                 and zero the row of B.
+// Without a cap on the number of merged rows (k_max = 0) the last two share
+// one launch (proxy_select_apply): a row's merge depends on its own score.
 //
 // proxy_score runs the chain on the matrix cores: the fp32 MFMA with K = 1
 // (v_mfma_f32_32x32x1_2b_f32) adds the outer product of a 64-lane column
@@ -287,13 +289,13 @@ __device__ int block_excl_scan(int v, int* smem16, int* total) {
 
 // rho_i from the per-column-block maxima, written to rho[] for every row;
 // then the selection.  Thread t owns rows [t*R, t*R + R), R = ceil(d_out/1024),
-// so one block-wide scan orders the uncapped selection.
-__global__ __launch_bounds__(kSelThreads) void proxy_select(const uint32_t* __restrict__ tmax_part,
-                                                            const uint32_t* __restrict__ cmax_part,
-                                                            int ncb, float* __restrict__ rho,
-                                                            int d_out, float tau, int k_max,
-                                                            int32_t* __restrict__ sel,
-                                                            int32_t* __restrict__ n_sel) {
+// so one block-wide scan orders the uncapped selection.  (One workgroup of
+// kSelThreads.)
+__device__ __forceinline__ void select_rows(const uint32_t* __restrict__ tmax_part,
+                                            const uint32_t* __restrict__ cmax_part, int ncb,
+                                            float* __restrict__ rho, int d_out, float tau,
+                                            int k_max, int32_t* __restrict__ sel,
+                                            int32_t* __restrict__ n_sel) {
   __shared__ int hist[256];
   __shared__ int s16[kSelThreads / 64];
   __shared__ uint32_t s_prefix;
@@ -403,6 +405,52 @@ __global__ __launch_bounds__(kSelThreads) void proxy_select(const uint32_t* __re
   if (tid == 0) *n_sel = tk_total;
 }
 
+__global__ __launch_bounds__(kSelThreads) void proxy_select(const uint32_t* __restrict__ tmax_part,
+                                                            const uint32_t* __restrict__ cmax_part,
+                                                            int ncb, float* __restrict__ rho,
+                                                            int d_out, float tau, int k_max,
+                                                            int32_t* __restrict__ sel,
+                                                            int32_t* __restrict__ n_sel) {
+  select_rows(tmax_part, cmax_part, ncb, rho, d_out, tau, k_max, sel, n_sel);
+}
+
+// The uncapped selection (k_max = 0: every row with rho_i >= tau) with the
+// row copies in the same launch.  Whether row i is merged depends on rho_i
+// alone, so the copies need not wait for the compacted list: workgroup 0
+// computes rho and the list as proxy_select does, and every other workgroup
+// takes kSelThreads / 64 rows, one per wave, folds that row's column-block
+// maxima into rho_i with the same operations (the same bits), and when
+// rho_i >= tau copies the staged codes into the backbone and zeroes the B
+// row (B[row][kidx[k]] for k < r with IDX; B rows hold rs values).
+template <bool IDX>
+__global__ __launch_bounds__(kSelThreads) void proxy_select_apply(
+    const uint32_t* __restrict__ tmax_part, const uint32_t* __restrict__ cmax_part, int ncb,
+    float* __restrict__ rho, int d_out, float tau, int32_t* __restrict__ sel,
+    int32_t* __restrict__ n_sel, uint8_t* __restrict__ wq, const uint8_t* __restrict__ staged,
+    float* __restrict__ B, int d_in, int r, int rs, const int32_t* __restrict__ kidx) {
+  if (blockIdx.x == 0) {
+    select_rows(tmax_part, cmax_part, ncb, rho, d_out, tau, 0, sel, n_sel);
+    return;
+  }
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)(blockIdx.x - 1) * (kSelThreads / 64) + (threadIdx.x >> 6);
+  if (row >= d_out) return;
+  uint32_t tb = 0, cb = 0;
+  for (int b = lane; b < ncb; b += 64) {
+    const uint32_t x = tmax_part[(int64_t)b * d_out + row], y = cmax_part[(int64_t)b * d_out + row];
+    tb = x > tb ? x : tb;
+    cb = y > cb ? y : cb;
+  }
+  tb = wave_max_u32(tb);
+  cb = wave_max_u32(cb);
+  const float x = __uint_as_float(tb) * inv_step_of_mag(cb);
+  if (!(x >= tau)) return;
+  const uint4* src = reinterpret_cast<const uint4*>(staged + row * d_in);
+  uint4* dst = reinterpret_cast<uint4*>(wq + row * d_in);
+  for (int j = lane; j < d_in / 16; j += 64) dst[j] = src[j];
+  for (int k = lane; k < r; k += 64) B[row * (IDX ? rs : r) + (IDX ? kidx[k] : k)] = 0.0f;
+}
+
 // one selected row per wave: copy the staged codes, zero the B row
 // zeroes B[row][kidx[k]] for k < r (IDX; B rows hold rs values), else B[row][0..r)
 template <bool IDX>
@@ -502,6 +550,18 @@ hipError_t launch_proxy_update_ranks(uint8_t* wq, const float* s_w, const float*
     else
       proxy_score<false><<<grid, kThreads, 0, s>>>(wq, s_w, A, B, (int)d_in, (int)d_out, (int)r,
                                                    (int)rs, nullptr, tmax, cmax, staged);
+  }
+  if (k_max == 0 && d_out > 0) {
+    const unsigned g = 1 + (unsigned)((d_out + kSelThreads / 64 - 1) / (kSelThreads / 64));
+    if (kidx)
+      proxy_select_apply<true><<<g, kSelThreads, 0, s>>>(tmax, cmax, L.ncb, rr, (int)d_out, tau,
+                                                         sel_idx, n_sel, wq, staged, B, (int)d_in,
+                                                         (int)r, (int)rs, kidx);
+    else
+      proxy_select_apply<false><<<g, kSelThreads, 0, s>>>(tmax, cmax, L.ncb, rr, (int)d_out, tau,
+                                                          sel_idx, n_sel, wq, staged, B,
+                                                          (int)d_in, (int)r, (int)rs, nullptr);
+    return hipGetLastError();
   }
   proxy_select<<<1, kSelThreads, 0, s>>>(tmax, cmax, L.ncb, rr, (int)d_out, tau, (int)k_max,
                                          sel_idx, n_sel);
