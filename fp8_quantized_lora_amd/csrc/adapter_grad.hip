@@ -840,32 +840,43 @@ struct PieceJob {
   int rows, rows_p;
 };
 
+constexpr int kPrepThreads = 1024;    // four 128 x 128 transpose tiles per workgroup
+
 __device__ __forceinline__ void piece_job(const PieceJob& q, int row) {
   if (row < q.rows)
-    piece_row<256, 32>(q.f + row * q.rs, q.cs, q.K, q.Kp, q.P + row * q.prow, q.plane, q.sp + row);
+    piece_row<kPrepThreads, 16>(q.f + row * q.rs, q.cs, q.K, q.Kp, q.P + row * q.prow, q.plane,
+                                q.sp + row);
   else
-    piece_row_zero<256>(q.Kp, q.P + row * q.prow, q.plane, q.sp + row);
+    piece_row_zero<kPrepThreads>(q.Kp, q.P + row * q.prow, q.plane, q.sp + row);
 }
 
 // The fused backward's preparation in one launch (each part alone is too
-// small to fill the GPU): workgroups [0, n_tr) transpose W~ for the dX
-// product (128 x 128 tiles, tr_tx per tile row), the next jb.rows_p form the
-// pieces of B^T (one rank per workgroup) for the dX product that also forms
-// G^ B, the rest those of U = X^ A^T for the token-contracting dB.
-__global__ __launch_bounds__(256) void xa_prep_kernel(const uint8_t* __restrict__ wq,
-                                                      int64_t d_out, int64_t d_in,
-                                                      uint8_t* __restrict__ wt, int n_tr,
-                                                      int tr_tx, PieceJob jb, PieceJob ju) {
+// small to fill the GPU): the first jb.rows_p workgroups form the pieces of
+// B^T (one rank per workgroup) for the dX product that also forms G^ B, the
+// next ju.rows_p those of U = X^ A^T for the token-contracting dB, the rest
+// transpose W~ for the dX product (128 x 128 tiles, tr_tx per tile row, four
+// per workgroup).
+__global__ __launch_bounds__(kPrepThreads) void xa_prep_kernel(const uint8_t* __restrict__ wq,
+                                                               int64_t d_out, int64_t d_in,
+                                                               uint8_t* __restrict__ wt, int n_tr,
+                                                               int tr_tx, PieceJob jb,
+                                                               PieceJob ju) {
+  // the piece jobs take the first workgroup ids, so that they are dispatched
+  // first and their latency overlaps the streaming transpose
   int b = blockIdx.x;
-  if (b < n_tr) {
-    transpose_u8_tile(wq, d_out, d_in, wt, b % tr_tx, b / tr_tx);
+  if (b < jb.rows_p) {
+    piece_job(jb, b);
     return;
   }
-  b -= n_tr;
-  if (b < jb.rows_p)
-    piece_job(jb, b);
-  else
-    piece_job(ju, b - jb.rows_p);
+  b -= jb.rows_p;
+  if (b < ju.rows_p) {
+    piece_job(ju, b);
+    return;
+  }
+  b -= ju.rows_p;
+  const int tile = b * (kPrepThreads / 256) + (int)(threadIdx.x >> 8);
+  if (tile < n_tr)
+    transpose_u8_tile(wq, d_out, d_in, wt, tile % tr_tx, tile / tr_tx, (int)(threadIdx.x & 255));
 }
 
 // one skinny product Out [M x R] = dec(Q) F^T / s_q with F [R x K] float,
@@ -1061,9 +1072,9 @@ hipError_t launch_bwd_xa(const uint8_t* gq, int g_fmt, const float* s_g, const u
   }
   const int tr_tx = tr ? ceil_div(d_in, 128) : 1;
   const int n_tr = tr ? tr_tx * ceil_div(d_out, 128) : 0;
-  const int grid = n_tr + jb.rows_p + ju.rows_p;
+  const int grid = ceil_div(n_tr, kPrepThreads / 256) + jb.rows_p + ju.rows_p;
   if (grid > 0) {
-    xa_prep_kernel<<<grid, 256, 0, s>>>(wq, d_out, d_in, wt, n_tr, tr_tx, jb, ju);
+    xa_prep_kernel<<<grid, kPrepThreads, 0, s>>>(wq, d_out, d_in, wt, n_tr, tr_tx, jb, ju);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -7,14 +7,16 @@
 namespace falq {
 
 // out[cols x rows] = in[rows x cols]^T, the 128 x 128 tile (bx, by) of a
-// matrix whose sizes are multiples of 16; 256 threads.  Each thread loads 16
-// rows x 4 bytes (a wave reads two 128-byte row segments per load),
-// transposes them in registers with byte permutes, and stores 4 output rows
-// x 16 bytes.  No LDS and no barrier: threads past the matrix return.
+// matrix whose sizes are multiples of 16; 256 threads (tid 0 .. 255, by
+// default the workgroup's own).  Each thread loads 16 rows x 4 bytes (a wave
+// reads two 128-byte row segments per load), transposes them in registers
+// with byte permutes, and stores 4 output rows x 16 bytes.  No LDS and no
+// barrier: threads past the matrix return.
 __device__ __forceinline__ void transpose_u8_tile(const uint8_t* __restrict__ in, int64_t rows,
                                                   int64_t cols, uint8_t* __restrict__ out, int bx,
-                                                  int by) {
-  const int tid = threadIdx.x, cg = tid & 31, rg = tid >> 5;
+                                                  int by, int tid = -1) {
+  if (tid < 0) tid = threadIdx.x;
+  const int cg = tid & 31, rg = tid >> 5;
   const int64_t c = (int64_t)bx * 128 + cg * 4;             // 4 input columns
   const int64_t r = (int64_t)by * 128 + rg * 16;            // 16 input rows
   if (c >= cols || r >= rows) return;                       // whole 16 x 4 blocks only
