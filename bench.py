@@ -479,8 +479,11 @@ def layer_workload(args, torch, fq, wl):
     ms, gemm_us = _timed(torch, args.steps, args.warmup, run_step, stream)
     flops = sum(wl.step_flops(sp.tokens, sp.d_in, sp.d_out, sp.rank) for _, _, _, sp in layers)
     s0 = layers[0][3]
+    m0 = layers[0][0]
     T = s0.tokens
-    gemm_flops = 2 * T * s0.d_in * s0.d_out
+    # the timed forward call: the backbone product, plus X^ A^T where the
+    # call forms it in the same tiles (counted once, at rank r)
+    gemm_flops = 2 * T * s0.d_in * s0.d_out + (2 * T * s0.d_in * s0.rank if m0.use_xa else 0)
     gemm_tf = gemm_flops / (gemm_us * 1e-6) / 1e12
     shapes = ", ".join(f"{sp.name} {sp.d_out}x{sp.d_in}" for _, _, _, sp in layers)
     out = {
@@ -496,8 +499,11 @@ def layer_workload(args, torch, fq, wl):
                    "tokens": T, "linears": len(layers), "rank": s0.rank,
                    "parallelism": "single GPU"},
         "tokens_per_s": round(T / (ms * 1e-3), 1),
-        "roofline": {"kernel": f"melded_linear_fwd FP8 GEMM ({T} x {s0.d_out} x {s0.d_in}, "
-                               f"{s0.name})",
+        "roofline": {"kernel": (f"melded_linear_fwd_xa call ({s0.name}: A split into three E4M3 "
+                                f"pieces, then one FP8 GEMM {T} x {s0.d_out} x {s0.d_in} forming "
+                                f"X^A^T in the same tiles)" if m0.use_xa else
+                                f"melded_linear_fwd FP8 GEMM ({T} x {s0.d_out} x {s0.d_in}, "
+                                f"{s0.name})"),
                      "bound": "mfma", "achieved": round(gemm_tf, 1), "peak": FP8_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(gemm_tf / FP8_PEAK_TFLOPS, 4),
                      "traffic": None},

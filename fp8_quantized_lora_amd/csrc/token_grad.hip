@@ -56,10 +56,14 @@ static_assert(TLPS == 4 && TKS == 4, "wait counts below assume four loads per st
 // 128-byte piece rows: 16-byte chunk c of row r at slot c ^ swz8(r) (the
 // FP8 GEMM's pattern: the 16-row fragment reads are conflict-free)
 __device__ __forceinline__ int swz8(int row) { return (row ^ ((row >> 3) & 1)) & 7; }
-// 64-byte FP8 rows: chunk c of token row t at slot c ^ swz4(t); a transpose
-// read takes one chunk of 8 consecutive rows, which then cover 32 distinct
-// banks
-__device__ __forceinline__ int swz4(int row) { return (row >> 2) & 3; }
+// 64-byte FP8 rows: chunk c of token row t at slot c ^ swz4(t).  A transpose
+// read serves 32 lanes at a time: two lane groups, each taking one chunk of 8
+// consecutive rows, rows t0 .. t0 + 7 and t0 + 32 .. t0 + 39.  Row t's chunk
+// lands in bank group 4 (t % 4) + slot, and bits 2 and 5 of t make the four
+// rows that share t % 4 take four different slots: the 16 rows cover all 64
+// banks (SQ_LDS_BANK_CONFLICT 0; with bits 2 and 3 alone, every read paid one
+// conflict cycle, at the same kernel time)
+__device__ __forceinline__ int swz4(int row) { return ((row >> 2) & 1) | (((row >> 5) & 1) << 1); }
 
 __device__ __forceinline__ v8i join8(uint4 lo, uint4 hi) {
   v8i r;
@@ -99,11 +103,23 @@ struct TokArgs {
   int T, Tp, r, Rp, S, kps;   // S = 1, or 2 (atomic adds onto zeroed outputs)
 };
 
-// workgroup: problem, then tile (rank tile, column tile), then split (fastest)
+// The dispatcher deals consecutive workgroup ids round-robin to the 8 XCDs;
+// the id is remapped so that each XCD takes a contiguous run of logical
+// workgroups.  Two neighbouring 64-column tiles read the two halves of the
+// same 128-byte lines of the codes, so on one XCD the second read is served
+// by that XCD's L2 instead of HBM (ids past the last multiple of 8 keep
+// their own).
+__device__ __forceinline__ int tok_xcd_remap(int bid, int n) {
+  const int per = n / 8;
+  return bid < per * 8 ? (bid % 8) * per + bid / 8 : bid;
+}
+
+// logical workgroup: problem, then tile (rank tile, column tile), then split
+// (fastest)
 template <int QF0>
 __global__ __launch_bounds__(kTkThreads, 1) void tok_kernel(TokArgs a) {
   __shared__ __attribute__((aligned(1024))) uint8_t smem[TKS * TSTAGE];
-  int b = blockIdx.x;
+  int b = tok_xcd_remap((int)blockIdx.x, (int)gridDim.x);
   const int pi = b >= a.p[0].blocks ? 1 : 0;
   if (pi) b -= a.p[0].blocks;
   // the problem's fields, selected one by one (no indexing of the argument
