@@ -166,3 +166,17 @@ def test_xa_pair_full_size_attention_projection(gpu_lib):
     print("full-size xa pair: Y %.2e dX %.2e X^A^T %.2e (per rank %.2e) dA %.2e dB %.2e "
           "(per rank %.2e %.2e)" % e)
     assert max(e) <= TOL
+
+
+@pytest.mark.parametrize("T,d_in,d_out,r", [(1024, 2048, 2048, 32), (2048, 4096, 4096, 64)])
+def test_xa_pair_is_deterministic(gpu_lib, T, d_in, d_out, r):
+    """The same inputs twice give the same bits: the first shape splits the
+    token contraction into two halves added with float atomics onto zeroed
+    outputs (two addends on a zero: order-independent), the second runs it
+    as one split with plain stores."""
+    announce(f"fwd_xa/bwd_xa determinism T={T} d={d_in} r={r}")
+    p = quantized_problem(5 + r, T, d_in, d_out, r, b_std=0.5)
+    first = gpu_pair(gpu_lib, p)
+    second = gpu_pair(gpu_lib, p)
+    for a, b in zip(first, second):
+        assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
