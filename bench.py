@@ -311,7 +311,7 @@ def run(args):
     # the forward call's algorithmic flops: the backbone product, plus the
     # rank-r product X^ A^T (X~ A~^T with A frozen) where the call forms it
     # (counted once, at rank r, though the fused route carries A as three
-    # E4M3 pieces)
+    # E4M3 pieces under block scales)
     gemm_flops = 2 * T * d_in * d_out + (2 * T * d_in * r if frozen or m.use_xa else 0)
     gemm_us = gemm_timed_us
     gemm_tflops = gemm_flops / (gemm_us * 1e-6) / 1e12
@@ -357,7 +357,7 @@ def run(args):
         "tokens_per_s": round(tokens_per_s, 1),
         "roofline": {"kernel": ("melded_linear_fwd_frozen_a call (FP8 GEMM 4096 x 4096 x 4096 "
                                 "+ X~A~^T)" if frozen else
-                                "melded_linear_fwd_xa call (A split into three E4M3 pieces, then "
+                                "melded_linear_fwd_xa call (A as block-scaled E4M3 pieces, then "
                                 "one FP8 GEMM 4096 x 4096 x 4096 forming X^A^T in the same tiles)"
                                 if m.use_xa else
                                 "melded_linear_fwd FP8 GEMM (4096 x 4096 x 4096)"),
@@ -499,7 +499,7 @@ def layer_workload(args, torch, fq, wl):
                    "tokens": T, "linears": len(layers), "rank": s0.rank,
                    "parallelism": "single GPU"},
         "tokens_per_s": round(T / (ms * 1e-3), 1),
-        "roofline": {"kernel": (f"melded_linear_fwd_xa call ({s0.name}: A split into three E4M3 "
+        "roofline": {"kernel": (f"melded_linear_fwd_xa call ({s0.name}: A as block-scaled E4M3 "
                                 f"pieces, then one FP8 GEMM {T} x {s0.d_out} x {s0.d_in} forming "
                                 f"X^A^T in the same tiles)" if m0.use_xa else
                                 f"melded_linear_fwd FP8 GEMM ({T} x {s0.d_out} x {s0.d_in}, "

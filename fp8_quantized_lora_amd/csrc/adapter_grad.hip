@@ -803,77 +803,57 @@ hipError_t launch_adapter_grads(const uint8_t* gq, const float* s_g, const uint8
 // ---------------------------------------------------------------------------
 // U = X^ A^T formed with the forward product, V = G^ B with the dX product
 // (melded_linear_fwd_xa / melded_linear_bwd_xa): the float factor enters the
-// FP8 matrix cores as three E4M3 pieces per element with one scale per rank,
-// sum_p dec(P_p[j, k]) ~ F[j, k] * s_j (s_j = 448 / max_k |F[j, k]|; each
-// piece the E4M3 rounding of what the previous ones left, so the residual
-// after three is about 2^-12 of the element or less).  The GEMM then adds
-// three MFMAs per K step in the four waves that hold the tile's unit
-// (gemm_fp8_kernel.hpp, SecondB), and the skinny row-wise pass, its
-// partials and their reduction disappear.  Shapes whose tile grid has too
-// few columns for the units (gemm_fp8_nt_fuses_second) form U or V with the
-// skinny kernel instead.
+// FP8 matrix cores as three E4M3 pieces per element with a power-of-two
+// scale per rank and 32-element block, which the matrix core applies itself
+// (pieces.hpp; the residual after three pieces is about 2^-12 of the element
+// or less).  The GEMM then adds three MFMAs per K step in the four waves that
+// hold the tile's unit (gemm_fp8_kernel.hpp, SecondB), and the dX product
+// writes V straight as the pieces the token-contracting kernel reads.  No
+// piece needs more than its own block, so forming them is one pass over the
+// factor with every lane busy.  Shapes whose tile grid has too few columns
+// for the units (gemm_fp8_nt_fuses_second) form U or V with the skinny
+// kernel instead.
 // ---------------------------------------------------------------------------
 namespace {
 
-// one row j of the operand per workgroup: element k is F[j * rs + k * cs]
-// (A: rs = K, cs = 1; B^T read from B [K x R]: rs = 1, cs = R)
-constexpr int kPieceThreads = 1024, kPieceHold = 16;
+// pieces of A [r x K] (K contiguous) for the forward product
+constexpr int kPieceThreads = 256;
 
-__global__ __launch_bounds__(kPieceThreads) void pieces_kernel(const float* __restrict__ F,
-                                                               int64_t K, int64_t rs, int64_t cs,
-                                                               uint8_t* __restrict__ P,
-                                                               int64_t plane,
-                                                               float* __restrict__ sp) {
-  const int64_t j = blockIdx.x;
-  piece_row<kPieceThreads, kPieceHold>(F + j * rs, cs, K, K, P + j * K, plane, sp + j);
+__global__ __launch_bounds__(kPieceThreads) void pieces_kernel(PieceJob q) {
+  const int64_t gid = (int64_t)blockIdx.x * kPieceThreads + threadIdx.x;
+  // the job's lanes come in whole waves
+  if (gid < piece_job_lanes<true>(q.Rp, q.Kp)) piece_job_lane<true>(q, gid);
 }
-
-// rows [0, rows) of a float operand F (element k of row j at F[j * rs +
-// k * cs], k < K) as pieces P[j * prow + k] (planes `plane` apart, zero for
-// K <= k < Kp) and scales sp[j]; rows [rows, rows_p) zero pieces
-struct PieceJob {
-  const float* f;
-  int64_t rs, cs, K, Kp;
-  uint8_t* P;
-  int64_t prow, plane;
-  float* sp;
-  int rows, rows_p;
-};
 
 constexpr int kPrepThreads = 1024;    // four 128 x 128 transpose tiles per workgroup
 
-__device__ __forceinline__ void piece_job(const PieceJob& q, int row) {
-  if (row < q.rows)
-    piece_row<kPrepThreads, 16>(q.f + row * q.rs, q.cs, q.K, q.Kp, q.P + row * q.prow, q.plane,
-                                q.sp + row);
-  else
-    piece_row_zero<kPrepThreads>(q.Kp, q.P + row * q.prow, q.plane, q.sp + row);
+int64_t prep_blocks(const PieceJob& q) {
+  return q.P == nullptr ? 0 : (piece_job_lanes<false>(q.Rp, q.Kp) + kPrepThreads - 1) / kPrepThreads;
 }
 
 // The fused backward's preparation in one launch (each part alone is too
-// small to fill the GPU): the first jb.rows_p workgroups form the pieces of
-// B^T (one rank per workgroup) for the dX product that also forms G^ B, the
-// next ju.rows_p those of U = X^ A^T for the token-contracting dB, the rest
-// transpose W~ for the dX product (128 x 128 tiles, tr_tx per tile row, four
-// per workgroup).
+// small to fill the GPU): the first nb workgroups form the pieces of B^T
+// (read from B [d_out x r]) for the dX product that also forms G^ B, the
+// next nu those of U = X^ A^T (xa [T x r]) for the token-contracting dB, the
+// rest transpose W~ for the dX product (128 x 128 tiles, tr_tx per tile row,
+// four per workgroup).
 __global__ __launch_bounds__(kPrepThreads) void xa_prep_kernel(const uint8_t* __restrict__ wq,
                                                                int64_t d_out, int64_t d_in,
                                                                uint8_t* __restrict__ wt, int n_tr,
-                                                               int tr_tx, PieceJob jb,
-                                                               PieceJob ju) {
+                                                               int tr_tx, PieceJob jb, int nb,
+                                                               PieceJob ju, int nu) {
   // the piece jobs take the first workgroup ids, so that they are dispatched
   // first and their latency overlaps the streaming transpose
   int b = blockIdx.x;
-  if (b < jb.rows_p) {
-    piece_job(jb, b);
+  if (b < nb + nu) {
+    const bool is_b = b < nb;
+    const PieceJob& q = is_b ? jb : ju;
+    const int64_t gid = (int64_t)(is_b ? b : b - nb) * kPrepThreads + threadIdx.x;
+    // a job's lanes come in whole waves
+    if (gid < piece_job_lanes<false>(q.Rp, q.Kp)) piece_job_lane<false>(q, gid);
     return;
   }
-  b -= jb.rows_p;
-  if (b < ju.rows_p) {
-    piece_job(ju, b);
-    return;
-  }
-  b -= ju.rows_p;
+  b -= nb + nu;
   const int tile = b * (kPrepThreads / 256) + (int)(threadIdx.x >> 8);
   if (tile < n_tr)
     transpose_u8_tile(wq, d_out, d_in, wt, tile % tr_tx, tile / tr_tx, (int)(threadIdx.x & 255));
@@ -981,15 +961,19 @@ hipError_t launch_grads_from_uv(const uint8_t* gq, int g_fmt, const float* s_g, 
   return hipGetLastError();
 }
 
+// pieces of a float operand with R rows and K columns (K a multiple of
+// 128): rows padded to 16
 struct PiecesPlan {
-  size_t p, sp, total;
+  int64_t Rp;
+  size_t p, e, total;
 };
 PiecesPlan pieces_plan(int64_t R, int64_t K) {
   PiecesPlan q{};
+  q.Rp = (R + 15) / 16 * 16;
   size_t o = 0;
   auto take = [&](size_t bytes) { size_t at = o; o = align_up(o + bytes, 256); return at; };
-  q.p = take((size_t)(3 * R * K));
-  q.sp = take((size_t)(R * 4));
+  q.p = take((size_t)(3 * q.Rp * K));
+  q.e = take((size_t)(K / 128 * q.Rp * 4));
   q.total = o;
   return q;
 }
@@ -1019,12 +1003,14 @@ hipError_t launch_fwd_xa(const uint8_t* xq, const float* s_x, const uint8_t* wq,
   if (r > 0 && gemm_fp8_nt_fuses_second(d_out, d_in, r)) {
     const PiecesPlan pp = pieces_plan(r, d_in);
     uint8_t* base = reinterpret_cast<uint8_t*>(ws);
-    float* sp = reinterpret_cast<float*>(base + pp.sp);
-    pieces_kernel<<<(unsigned)r, kPieceThreads, 0, s>>>(A, d_in, d_in, 1, base + pp.p, r * d_in, sp);
+    const PieceJob q{A, d_in, 1, r, d_in, base + pp.p, base + pp.e, pp.Rp, d_in};
+    const int64_t blocks = (piece_job_lanes<true>(pp.Rp, d_in) + kPieceThreads - 1) / kPieceThreads;
+    pieces_kernel<<<(unsigned)blocks, kPieceThreads, 0, s>>>(q);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     return launch_gemm_fp8_nt_pieces(xq, d_in, wq, d_in, y, d_out, T, d_out, d_in, s_x, s_w,
-                                     base + pp.p, d_in, r * d_in, r, sp, xa, r, s, 0);
+                                     base + pp.p, base + pp.e, pp.Rp, r, xa, r, nullptr, nullptr,
+                                     0, 0, s, 0);
   }
   hipError_t e = d_out > 0 ? launch_gemm_fp8_nt(xq, d_in, wq, d_in, y, d_out, T, d_out, d_in, s_x,
                                                 s_w, s)
@@ -1033,11 +1019,10 @@ hipError_t launch_fwd_xa(const uint8_t* xq, const float* s_x, const uint8_t* wq,
   return launch_one_skinny(xq, d_in, 0, s_x, A, false, T, d_in, r, xa, ws, s);
 }
 
-// V = G^ B: [T x r], or [r x T4] (rank-major, T4 = T rounded up to 4) when
-// the dX product forms it for the token-contracting kernel
+// V = G^ B [T x r] (row-major), when no kernel writes it straight as pieces
 size_t bwd_xa_ws_bytes(int64_t T, int64_t d_in, int64_t d_out, int64_t r) {
   if (r <= 0 || T <= 0 || d_in <= 0 || d_out <= 0) return 0;
-  size_t o = align_up((size_t)r * (size_t)((T + 3) / 4 * 4) * 4, 256);   // V
+  size_t o = align_up((size_t)r * (size_t)T * 4, 256);   // V
   o += v_region_bytes(T, d_out, r);
   return o + (token_grads_ok(T, d_in, d_out, r) ? token_grads_ws_bytes(T, d_in, d_out, r)
                                                 : uv_plan(T, d_in, d_out, r).total);
@@ -1047,10 +1032,9 @@ hipError_t launch_bwd_xa(const uint8_t* gq, int g_fmt, const float* s_g, const u
                          const float* s_x, const uint8_t* wq, uint8_t* wt, const float* s_w,
                          const float* B, const float* xa, int64_t T, int64_t d_in, int64_t d_out,
                          int64_t r, float* dx, float* dA, float* dB, void* ws, hipStream_t s) {
-  const int64_t T4 = (T + 3) / 4 * 4;
   uint8_t* base = reinterpret_cast<uint8_t*>(ws);
   float* v = reinterpret_cast<float*>(base);
-  uint8_t* vreg = base + align_up((size_t)r * (size_t)T4 * 4, 256);
+  uint8_t* vreg = base + align_up((size_t)r * (size_t)T * 4, 256);
   uint8_t* rest = vreg + v_region_bytes(T, d_out, r);
   const bool want_v = dA != nullptr && r > 0;
   const bool tr = dx != nullptr && d_in > 0 && d_out > 0;
@@ -1060,29 +1044,31 @@ hipError_t launch_bwd_xa(const uint8_t* gq, int g_fmt, const float* s_g, const u
   const bool tok = r > 0 && token_grads_ok(T, d_in, d_out, r);
   if (tr && (d_in % 16 != 0 || d_out % 16 != 0)) return hipErrorInvalidValue;
   const PiecesPlan pp = pieces_plan(r, d_out);
-  float* spb = reinterpret_cast<float*>(vreg + pp.sp);
   PieceJob jb{}, ju{};
-  if (fuse) jb = PieceJob{B, 1, r, d_out, d_out, vreg + pp.p, d_out, r * d_out, spb, (int)r, (int)r};
+  if (fuse) jb = PieceJob{B, 1, r, r, d_out, vreg + pp.p, vreg + pp.e, pp.Rp, d_out};
+  uint8_t *vp = nullptr, *ve = nullptr;
+  int64_t tRp = 0, tTp = 0;
   if (tok) {
-    uint8_t* P;
-    float* sp;
-    int64_t Rp, Tp;
-    token_grads_u_pieces(rest, T, d_in, d_out, r, &P, &sp, &Rp, &Tp);
-    ju = PieceJob{xa, 1, r, T, Tp, P, Tp, Rp * Tp, sp, (int)r, (int)Rp};
+    uint8_t *up, *ue;
+    token_grads_pieces(rest, T, d_in, d_out, r, 0, &up, &ue, &tRp, &tTp);
+    token_grads_pieces(rest, T, d_in, d_out, r, 1, &vp, &ve, &tRp, &tTp);
+    ju = PieceJob{xa, 1, r, r, T, up, ue, tRp, tTp};
   }
+  const int nb = (int)prep_blocks(jb), nu = (int)prep_blocks(ju);
   const int tr_tx = tr ? ceil_div(d_in, 128) : 1;
   const int n_tr = tr ? tr_tx * ceil_div(d_out, 128) : 0;
-  const int grid = ceil_div(n_tr, kPrepThreads / 256) + jb.rows_p + ju.rows_p;
+  const int grid = ceil_div(n_tr, kPrepThreads / 256) + nb + nu;
   if (grid > 0) {
-    xa_prep_kernel<<<grid, kPrepThreads, 0, s>>>(wq, d_out, d_in, wt, n_tr, tr_tx, jb, ju);
+    xa_prep_kernel<<<grid, kPrepThreads, 0, s>>>(wq, d_out, d_in, wt, n_tr, tr_tx, jb, nb, ju, nu);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   hipError_t e = hipSuccess;
   if (fuse) {
+    // with the token-contracting kernel, V goes straight into its pieces
     e = launch_gemm_fp8_nt_pieces(gq, d_out, wt, d_out, dx, d_in, T, d_in, d_out, s_g, s_w,
-                                  vreg + pp.p, d_out, r * d_out, r, spb, v, tok ? T4 : r, s, g_fmt,
-                                  tok);
+                                  vreg + pp.p, vreg + pp.e, pp.Rp, r, v, r, tok ? vp : nullptr,
+                                  tok ? ve : nullptr, tRp, tTp, s, g_fmt);
   } else {
     if (tr) e = launch_gemm_fp8_nt(gq, d_out, wt, d_out, dx, d_in, T, d_in, d_out, s_g, s_w, s,
                                    g_fmt);
@@ -1091,8 +1077,8 @@ hipError_t launch_bwd_xa(const uint8_t* gq, int g_fmt, const float* s_g, const u
   }
   if (e != hipSuccess || r == 0) return e;
   if (tok)
-    return launch_token_grads(gq, g_fmt, s_g, xq, s_x, xa, 1, r, true, v, fuse ? T4 : 1,
-                              fuse ? 1 : r, T, d_in, d_out, r, dA, dB, rest, s);
+    return launch_token_grads(gq, g_fmt, s_g, xq, s_x, xa, true, v, fuse, T, d_in, d_out, r, dA,
+                              dB, rest, s);
   return launch_grads_from_uv(gq, g_fmt, s_g, xq, s_x, xa, v, T, d_in, d_out, r, dA, dB, rest, s);
 }
 

@@ -135,12 +135,13 @@ __device__ __forceinline__ uint32_t lds_offset(const void* p) {
   return (uint32_t)(uintptr_t)(const lds_u8*)p;
 }
 // wait until at most n vector-memory instructions of this wave are in flight
-// (n in {0, 2, 4, 5, 8, 16, 24}; other values wait for all)
+// (n in {0, 2, 4, 5, 8, 9, 10, 16, 24}; other values wait for all)
 __device__ __forceinline__ void wait_vmem(int n) {
 #define FALQ_WVM(k) \
   case k: __builtin_amdgcn_s_waitcnt(((k) & 0xF) | (((k) >> 4) << 14) | (0x7 << 4) | (0xF << 8)); break;
   switch (n) {
-    FALQ_WVM(0) FALQ_WVM(2) FALQ_WVM(4) FALQ_WVM(5) FALQ_WVM(8) FALQ_WVM(16) FALQ_WVM(24)
+    FALQ_WVM(0) FALQ_WVM(2) FALQ_WVM(4) FALQ_WVM(5) FALQ_WVM(8) FALQ_WVM(9) FALQ_WVM(10)
+    FALQ_WVM(16) FALQ_WVM(24)
     default: __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xF << 8)); break;
   }
 #undef FALQ_WVM

@@ -250,22 +250,27 @@ hipError_t launch_gemm_fp8_nt_second(const uint8_t* A, int64_t lda, const uint8_
   const int tN = (int)((N + gemm::dma::BN - 1) / gemm::dma::BN);
   gemm::dma::gemm_fp8_nt_dma<1, 0><<<tM * tN, gemm::dma::kThreads, 0, s>>>(
       A, lda, B, ldb, C, ldc, (int)M, (int)N, (int)K, sa, sb, tM, tN, tM * tN,
-      gemm::dma::SecondB{Bu, ldbu, 0, (int)R, Cu, ldcu, sbu, nullptr}, 0);
+      gemm::dma::SecondB{Bu, ldbu, 0, (int)R, nullptr, 0, sbu, Cu, ldcu, nullptr, nullptr, 0, 0},
+      0);
   return hipGetLastError();
 }
 
 hipError_t launch_gemm_fp8_nt_pieces(const uint8_t* A, int64_t lda, const uint8_t* B,
                                      int64_t ldb, float* C, int64_t ldc, int64_t M, int64_t N,
                                      int64_t K, const float* sa, const float* sb,
-                                     const uint8_t* P, int64_t ldp, int64_t plane, int64_t R,
-                                     const float* sp, float* Cu, int64_t ldcu, hipStream_t s,
-                                     int a_fmt, bool cu_rank_major) {
+                                     const uint8_t* P, const uint8_t* PE, int64_t prp, int64_t R,
+                                     float* Cu, int64_t ldcu, uint8_t* Po, uint8_t* Eo,
+                                     int64_t po_rp, int64_t po_kp, hipStream_t s, int a_fmt) {
   if (M == 0) return hipSuccess;
   if (!gemm_fp8_nt_fuses_second(N, K, R) || !gemm_shape_ok(M, N, K)) return hipErrorInvalidValue;
-  if (cu_rank_major && ldcu % 4 != 0) return hipErrorInvalidValue;
+  const int64_t r16 = (R + gemm::dma::UR - 1) / gemm::dma::UR * gemm::dma::UR;
+  if (prp < r16 || prp % 16 != 0) return hipErrorInvalidValue;
+  if (Po != nullptr && (po_rp < r16 || po_rp % 16 != 0 || po_kp < M || po_kp % 128 != 0))
+    return hipErrorInvalidValue;
   const int tM = (int)((M + gemm::dma::BM - 1) / gemm::dma::BM);
   const int tN = (int)((N + gemm::dma::BN - 1) / gemm::dma::BN);
-  const gemm::dma::SecondB u{P, ldp, plane, (int)R, Cu, ldcu, nullptr, sp, cu_rank_major ? 1 : 0};
+  const gemm::dma::SecondB u{P,  K,  prp * K, (int)R, PE,    prp,   nullptr,
+                             Cu, ldcu, Po,    Eo,     po_rp, po_kp};
   if (a_fmt == 0)
     gemm::dma::gemm_fp8_nt_dma<3, 0><<<tM * tN, gemm::dma::kThreads, 0, s>>>(
         A, lda, B, ldb, C, ldc, (int)M, (int)N, (int)K, sa, sb, tM, tN, tM * tN, u, 0);

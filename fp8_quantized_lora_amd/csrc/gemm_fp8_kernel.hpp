@@ -3,6 +3,7 @@
 #pragma once
 
 #include "common.hpp"
+#include "pieces.hpp"
 
 namespace falq {
 namespace gemm {
@@ -204,31 +205,45 @@ constexpr int WTM = BM / WGM, WTN = BN / WGN, MB = WTM / 16, NB = WTN / 16;
 constexpr int UR = 16;                                  // rank rows of the second B operand
 constexpr int STAGE = (BM + BN) * BK;
 constexpr int MAX_NU = 3;                               // pieces of the second B operand
-static_assert(S * (STAGE + MAX_NU * UR * BK) <= 160 * 1024, "LDS");
+static_assert(S * (STAGE + MAX_NU * UR * BK + UR * 4) + 4 * UR * 4 <= 160 * 1024, "LDS");
 constexpr int AI = BM * BK / 1024 / NW, BI = BN * BK / 1024 / NW;   // DMA instructions / wave / stage
 constexpr int LPS = AI + BI;
 
 // Optional second product against a small second B operand of NU E4M3
 // "pieces" summed on the matrix cores: the frozen adapter factor A~ in the
 // forward (NU = 1: U = dec(X~) dec(A~)^T / (sa * sb)), or a float operand
-// held as NU = 3 E4M3 pieces with one scale per row, sum_p dec(P_p) ~ F * sbv
-// (the trained A in the forward, B^T in the dX product: C2 = dec(A) F^T / sa
-// to within the pieces' residual, about 2^-12 of each element).  Its
-// 16-rank blocks times 64-row quarters of a tile are "units"; the tile in
-// column tn < 4 * ceil(R / 16) takes unit tn: block tn / 4, quarter tn % 4.
-// The quarter's rows are held by the four waves of row group wm = quarter / 2,
-// so each of them issues NU more MFMAs per K step (on its fragment
-// i = (quarter % 2) * 4 + wn), NU per SIMD.
+// held as NU = 3 E4M3 pieces with a power-of-two scale per row and 32-element
+// K block (pieces.hpp), which the matrix core applies as the operand's E8M0
+// block scale (the trained A in the forward, B^T in the dX product:
+// C2 = dec(A) F^T / sa to within the pieces' residual, about 2^-12 of each
+// element).  Its 16-rank blocks times 64-row quarters of a tile are "units";
+// the tile in column tn < 4 * ceil(R / 16) takes unit tn: block tn / 4,
+// quarter tn % 4.  The quarter's rows are held by the four waves of row group
+// wm = quarter / 2, so each of them issues NU more MFMAs per K step (on its
+// fragment i = (quarter % 2) * 4 + wn), NU per SIMD.  The unit's scale bytes
+// of a K step (16 rows x 4 blocks, 64 contiguous bytes) ride in the LDS
+// stage, loaded by wave 2 NU.
+//
+// The second product goes to C ([M x R] floats), or (P != nullptr) straight
+// into pieces of its transpose for a later contraction over the M rows:
+// rows m of C become the K positions of the pieces (P[p][j][m], scale bytes
+// E[c][j][s]: pieces.hpp's layout with Rp = prp rows and Kp = pkp columns,
+// zero codes for m >= M).  A block of 32 rows spans two waves of the row
+// group (positions 16 wn .. 16 wn + 15 and 16 (wn ^ 2) .. of the quarter),
+// which trade their row maxima through LDS.
 struct SecondB {
   const uint8_t* B;      // piece 0: [R x K] codes, row stride ldb
   int64_t ldb;
   int64_t plane;         // bytes from one piece to the next
   int R;
-  float* C;              // [M x R] fp32 output, row stride ldc; or with ct
-  int64_t ldc;           // [R x M], rank-major, row stride ldc
-  const float* sb;       // one scale for every row (sbv == nullptr)
-  const float* sbv;      // or one scale per row (R of them)
-  int ct;
+  const uint8_t* be;     // NU = 3: scale bytes of B (rows padded to brp, a multiple of 16)
+  int64_t brp;
+  const float* sb;       // NU = 1: one scale for all of B
+  float* C;              // [M x R] fp32 output, row stride ldc
+  int64_t ldc;
+  uint8_t* P;            // or pieces of C^T (rows: prp, multiple of 16; columns: pkp >= M,
+  uint8_t* E;            // a multiple of 128) and their scale bytes
+  int64_t prp, pkp;
 };
 
 // FA: format of the A codes (0 = E4M3, 1 = E5M2; B and the second B are
@@ -257,7 +272,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_nt_dma(
   static_assert(!(FU && MODE != 0), "the second product is not split");
   constexpr bool HALF = MODE == 1;
   static_assert(FA != 5 || !FU, "no second product with bf16 operands");
-  constexpr int SB = STAGE + NU * UR * BK;                 // bytes per LDS stage
+  constexpr bool BS = NU == 3;                             // block-scaled pieces
+  constexpr int SE = BS ? UR * 4 : 0;                      // their scale bytes per stage
+  constexpr int SB = STAGE + NU * UR * BK + SE;            // bytes per LDS stage
   __shared__ __attribute__((aligned(1024))) uint8_t smem[S * SB];
   int tm, tn, k_lo = 0, nk = K / BK;
   if constexpr (HALF) {
@@ -315,6 +332,10 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_nt_dma(
     gU = u.B + (int64_t)(w >> 1) * u.plane + (int64_t)min(ub * UR + row, u.R - 1) * u.ldb +
          k_lo * BK + ((lslot ^ swz(row)) * 16);
   }
+  // the unit's scale bytes: four lanes of wave 2 NU, 16 bytes each
+  const bool load_e = BS && __builtin_amdgcn_readfirstlane((int)(has_u && w == 2 * NU)) != 0;
+  const uint8_t* gE = nullptr;
+  if (BS && load_e) gE = u.be + (int64_t)(k_lo * u.brp + ub * UR) * 4 + (lane & 3) * 16;
   auto issue = [&](int stage, int k0) {
     const uint32_t base = lds_offset(smem + stage * SB);
     const uint32_t la = __builtin_amdgcn_readfirstlane(base + w * AI * 1024);
@@ -325,6 +346,9 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_nt_dma(
     for (int j = 0; j < BI; ++j) load16_to_lds(gB[j] + k0, lb + j * 1024);
     if (FU && load_u)
       load16_to_lds(gU + k0, __builtin_amdgcn_readfirstlane(base + (BM + BN) * BK + w * 1024));
+    if (BS && load_e && lane < 4)
+      load16_to_lds(gE + (int64_t)(k0 / BK) * u.brp * 4,
+                    __builtin_amdgcn_readfirstlane(base + (BM + BN + NU * UR) * BK));
   };
 
 #pragma unroll
@@ -370,11 +394,13 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_nt_dma(
   // treats each step's LDS reads as returning in order and waits only for the
   // fragments the next MFMA needs.
   const float scale = (FA == 5 || MODE == 2) ? 1.0f : 1.0f / (sa[0] * sb[0]);
-  const float scale_u = (FU && u.sbv == nullptr) ? 1.0f / (sa[0] * u.sb[0]) : 0.0f;
+  const float scale_u = BS ? 1.0f / sa[0] : (FU ? 1.0f / (sa[0] * u.sb[0]) : 0.0f);
   v4f accu;
 #pragma unroll
   for (int v = 0; v < 4; ++v) accu[v] = 0.0f;
   const int offU = (BM + BN) * BK + r16 * BK;
+  // the lane's scale byte: row r16 of the unit, block g of the step
+  const int offE = (BM + BN + NU * UR) * BK + r16 * 4 + g;
   __builtin_amdgcn_s_waitcnt(0xC07F);                        // lgkmcnt(0)
   for (int kt = 0; kt < nk; ++kt) {
     // stage kt has landed once at most (stages issued after it) * LPS loads are in flight
@@ -392,9 +418,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_nt_dma(
       bf[j] = frag(st + offB + j * 16 * BK);
       __builtin_amdgcn_sched_barrier(0);
     }
+    int eu = 127;
     if (FU && wave_u) {
 #pragma unroll
       for (int p = 0; p < NU; ++p) bu[p] = frag(st + offU + p * UR * BK);
+      if constexpr (BS) eu = st[offE];
     }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -405,9 +433,14 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_nt_dma(
       for (int j = 0; j < NB; ++j) acc[i][j] = mma(af[i & 1], bf[j], acc[i][j]);
       if (FU && wave_u && i == iu) {
 #pragma unroll
-        for (int p = 0; p < NU; ++p)
-          accu = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[i & 1], bu[p], accu, FA, 0, 0,
-                                                                  0, 0, 0);
+        for (int p = 0; p < NU; ++p) {
+          if constexpr (BS)
+            accu = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[i & 1], bu[p], accu, FA, 0,
+                                                                    0, 127, 0, eu);
+          else
+            accu = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[i & 1], bu[p], accu, FA, 0,
+                                                                    0, 0, 0, 0);
+        }
       }
       __builtin_amdgcn_sched_barrier(0);
       // the next stage's direct loads go out once this step's first
@@ -441,21 +474,46 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_nt_dma(
       }
     }
   }
-  if (FU && wave_u) {
-    const int rank = ub * UR + (lane & 15);
-    if (rank < u.R) {
-      const float su = u.sbv ? 1.0f / (sa[0] * u.sbv[rank]) : scale_u;
-      const int row0 = m0 + uq * 64 + wn * 16 + 4 * (lane >> 4);
-      if (u.ct && row0 + 3 < M) {
-        // rank-major: the lane's four rows are consecutive (ldc a multiple of 4)
-        *reinterpret_cast<v4f*>(u.C + (int64_t)rank * u.ldc + row0) = accu * su;
-      } else {
+  if constexpr (FU) {
+    const int rank = ub * UR + r16;
+    const int urow0 = m0 + uq * 64 + wn * 16 + 4 * g;      // the lane's four rows
+    v4f x = accu * scale_u;
+    if (BS && has_u && u.P != nullptr) {
+      // pieces of the transpose: the block of rows (quarter bit 6, wave bit 4)
+      // spans this wave and wave wn ^ 2 of the row group
+      __shared__ uint32_t xmax[4][UR];
+      uint32_t mx = 0;
+      if (wave_u) {
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-          const int row = row0 + v;
-          if (row < M)
-            u.C[u.ct ? (int64_t)rank * u.ldc + row : (int64_t)row * u.ldc + rank] = accu[v] * su;
+          if (urow0 + v >= M) x[v] = 0.0f;
+          mx = max(mx, finite_mag(x[v]));
         }
+        mx = max(mx, (uint32_t)__shfl_xor((int)mx, 16, 64));
+        mx = max(mx, (uint32_t)__shfl_xor((int)mx, 32, 64));
+        if (g == 0) xmax[wn][r16] = mx;
+      }
+      __syncthreads();
+      if (wave_u && urow0 < u.pkp) {
+        mx = max(mx, xmax[wn ^ 2][r16]);
+        const int e = piece_exp(__uint_as_float(mx));
+        uint32_t q0, q1, q2;
+        pieces4(ldexpf(x[0], e), ldexpf(x[1], e), ldexpf(x[2], e), ldexpf(x[3], e), q0, q1, q2);
+        const int64_t plane = u.prp * u.pkp;
+        uint8_t* p = u.P + (int64_t)rank * u.pkp + urow0;
+        *reinterpret_cast<uint32_t*>(p) = q0;
+        *reinterpret_cast<uint32_t*>(p + plane) = q1;
+        *reinterpret_cast<uint32_t*>(p + 2 * plane) = q2;
+        if (g == 0 && wn < 2) {
+          const int64_t c = (m0 + uq * 64) / 128;
+          u.E[(c * u.prp + rank) * 4 + 2 * (wn & 1) + (uq & 1)] = (uint8_t)(127 - e);
+        }
+      }
+    } else if (wave_u && rank < u.R) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int row = urow0 + v;
+        if (row < M) u.C[(int64_t)row * u.ldc + rank] = x[v];
       }
     }
   }

@@ -80,16 +80,19 @@ hipError_t launch_gemm_fp8_nt_second(const uint8_t* A, int64_t lda, const uint8_
                                      int64_t ldbu, int64_t R, float* Cu, int64_t ldcu,
                                      const float* sbu, hipStream_t s);
 // C = dec(A) dec(B)^T / (sa sb) as launch_gemm_fp8_nt, and in the same tiles
-// Cu [M x R] = dec(A) F^T / sa for a float operand F [R x K] held as three
-// E4M3 piece planes P (row stride ldp, planes `plane` bytes apart) with the
-// per-row scales sp: sum_p dec(P_p[j, :]) ~ F[j, :] * sp[j].  Requires
-// gemm_fp8_nt_fuses_second(N, K, R); a_fmt as launch_gemm_fp8_nt.
+// Cu [M x R] = dec(A) F^T / sa for a float operand F [R x K] held as
+// block-scaled E4M3 pieces (pieces.hpp: planes P [3][prp][K], scale bytes PE,
+// prp >= R rounded up to 16, a multiple of 16).  With Po != nullptr the
+// second product is written instead as pieces of Cu^T [R x M] (Po
+// [3][po_rp][po_kp], scale bytes Eo; po_kp >= M a multiple of 128, zero codes
+// past M).  Requires gemm_fp8_nt_fuses_second(N, K, R); a_fmt as
+// launch_gemm_fp8_nt.
 hipError_t launch_gemm_fp8_nt_pieces(const uint8_t* A, int64_t lda, const uint8_t* B,
                                      int64_t ldb, float* C, int64_t ldc, int64_t M, int64_t N,
                                      int64_t K, const float* sa, const float* sb,
-                                     const uint8_t* P, int64_t ldp, int64_t plane, int64_t R,
-                                     const float* sp, float* Cu, int64_t ldcu, hipStream_t s,
-                                     int a_fmt, bool cu_rank_major = false);
+                                     const uint8_t* P, const uint8_t* PE, int64_t prp, int64_t R,
+                                     float* Cu, int64_t ldcu, uint8_t* Po, uint8_t* Eo,
+                                     int64_t po_rp, int64_t po_kp, hipStream_t s, int a_fmt);
 // out[cols x rows] = in[rows x cols]^T (bytes; rows and cols multiples of 16)
 hipError_t launch_transpose_u8(const uint8_t* in, int64_t rows, int64_t cols, uint8_t* out,
                                hipStream_t s);
@@ -106,16 +109,16 @@ hipError_t launch_fwd_xa(const uint8_t* xq, const float* s_x, const uint8_t* wq,
 // Needs d_in and d_out multiples of 128.
 bool token_grads_ok(int64_t T, int64_t d_in, int64_t d_out, int64_t r);
 size_t token_grads_ws_bytes(int64_t T, int64_t d_in, int64_t d_out, int64_t r);
-// U, V given by strides: element (t, j) at u[j * u_rs + t * u_cs]; with
-// u_ready the U pieces are in place already (token_grads_u_pieces: where).
+// U, V [T x r] row-major floats; with u_ready (v_ready) their pieces are in
+// place already (token_grads_pieces: where) and u (v) is not read.
 hipError_t launch_token_grads(const uint8_t* gq, int g_fmt, const float* s_g, const uint8_t* xq,
-                              const float* s_x, const float* u, int64_t u_rs, int64_t u_cs,
-                              bool u_ready, const float* v, int64_t v_rs, int64_t v_cs,
-                              int64_t T, int64_t d_in, int64_t d_out, int64_t r, float* dA,
-                              float* dB, void* ws, hipStream_t s);
-// the U pieces' place in the workspace: [3][Rp][Tp] codes at *P, scales at *sp
-void token_grads_u_pieces(void* ws, int64_t T, int64_t d_in, int64_t d_out, int64_t r,
-                          uint8_t** P, float** sp, int64_t* Rp, int64_t* Tp);
+                              const float* s_x, const float* u, bool u_ready, const float* v,
+                              bool v_ready, int64_t T, int64_t d_in, int64_t d_out, int64_t r,
+                              float* dA, float* dB, void* ws, hipStream_t s);
+// the pieces' place in the workspace (which = 0: U, 1: V): planes
+// [3][Rp][Tp] at *P, scale bytes [Tp / 128][Rp][4] at *E (pieces.hpp)
+void token_grads_pieces(void* ws, int64_t T, int64_t d_in, int64_t d_out, int64_t r, int which,
+                        uint8_t** P, uint8_t** E, int64_t* Rp, int64_t* Tp);
 size_t bwd_xa_ws_bytes(int64_t T, int64_t d_in, int64_t d_out, int64_t r);
 // wq is transposed into wt (d_in x d_out bytes) when dx is wanted
 hipError_t launch_bwd_xa(const uint8_t* gq, int g_fmt, const float* s_g, const uint8_t* xq,

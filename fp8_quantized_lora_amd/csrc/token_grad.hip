@@ -17,11 +17,12 @@
 //   16 c + d: eight consecutive tokens of one output column.  Four reads
 //   (t0 = 32 g + 8 i for the lane group g) fill the 32-byte operand.
 //
-// The float factor F (U or V) enters as three E4M3 pieces per element with
-// one scale per rank, sum_p dec(P_p[j][t]) ~ F[t][j] * s_j (s_j =
-// 448 / max_t |F[t][j]|; each piece the E4M3 rounding of what the earlier
-// ones left, a residual of about 2^-12 of the element or less), laid out
-// rank-major with the tokens contiguous [3][Rp][Tp] and zero beyond T and r.
+// The float factor F (U or V) enters as three E4M3 pieces per element with a
+// power-of-two scale per rank and 32-token block, applied by the matrix core
+// as the operand's E8M0 block scale (pieces.hpp: planes [3][Rp][Tp] with the
+// tokens contiguous, scale bytes [Tp / 128][Rp][4], zero codes beyond T).
+// The pieces of V come from the dX product's epilogue, those of U (and of V
+// when another kernel formed it) from the float factor (uv_pieces_kernel).
 //
 // Tile: 64 ranks x 64 output columns per workgroup over one split of the
 // tokens, 8 waves (each 16 ranks x 32 columns: 2 blocks x 3 pieces = 6
@@ -29,7 +30,10 @@
 // direct-to-LDS loads (the FP8 tile [128 t][64 n] and the pieces
 // [3][64 j][128 t] per stage, 16-byte chunks XOR-swizzled by row so that
 // both the transpose reads and the piece fragment reads are free of bank
-// conflicts).  With too few tiles to fill half the GPU the tokens are split
+// conflicts).  The kernel is bound by the number of direct-load instructions
+// a CU issues, so the scale bytes (256 per step) come in windows of 16 steps
+// (4 KB, one half-wave load per wave, double-buffered) with the stage that
+// opens the window, not with every stage.  With too few tiles to fill half the GPU the tokens are split
 // in two halves whose results are added with float atomics onto outputs
 // zeroed beforehand: exactly two addends meet a zero, and a + b does not
 // depend on which lands first, so the result is the same on every run.
@@ -47,11 +51,16 @@ constexpr int kTkThreads = TKW * 64;
 constexpr int TQ_BYTES = TKK * TKN;                      // FP8 tile [128 t][64 n]
 constexpr int TP_PLANE = TKR * TKK;                      // one piece [64 j][128 t]
 constexpr int TSTAGE = TQ_BYTES + 3 * TP_PLANE;
+constexpr int TEW = 16;                                  // steps per window of scale bytes
+constexpr int TE_WIN = TEW * TKR * 4;                    // one window: [16 steps][64 j][4]
+constexpr int TE_OFF = TKS * TSTAGE;                     // two windows after the ring
 constexpr int TQ_I = TQ_BYTES / 1024 / TKW, TP_I = 3 * TP_PLANE / 1024 / TKW;
 constexpr int TLPS = TQ_I + TP_I;                        // direct loads per wave per stage
 static_assert(TQ_I * 1024 * TKW == TQ_BYTES && TP_I * 1024 * TKW == 3 * TP_PLANE, "loads");
-static_assert(TKS * TSTAGE <= 160 * 1024, "LDS");
-static_assert(TLPS == 4 && TKS == 4, "wait counts below assume four loads per stage, 4 stages");
+static_assert(TE_WIN == TKW * 32 * 16, "one window: 32 lanes x 16 bytes per wave");
+static_assert(TE_OFF + 2 * TE_WIN <= 160 * 1024, "LDS");
+static_assert(TLPS == 4 && TKS == 4, "wait counts below assume four loads per stage (plus one "
+                                     "on window stages), 4 stages");
 
 // 128-byte piece rows: 16-byte chunk c of row r at slot c ^ swz8(r) (the
 // FP8 GEMM's pattern: the 16-row fragment reads are conflict-free)
@@ -76,16 +85,17 @@ typedef __attribute__((address_space(3))) v2i lds_v2i;
 
 constexpr int TNB = 2;                                   // 16-column blocks per wave
 
-// acc[b] += Q block b (format QF) . piece p (E4M3), p = 0, 1, 2
+// acc[b] += Q block b (format QF) . piece p (E4M3, the lane's scale byte eb:
+// rank r16, block g of the step), p = 0, 1, 2
 template <int QF>
-__device__ __forceinline__ void mma_pieces(const v8i (&qf)[TNB], const v8i (&pf)[3],
+__device__ __forceinline__ void mma_pieces(const v8i (&qf)[TNB], const v8i (&pf)[3], int eb,
                                            v4f (&acc)[TNB]) {
 #pragma unroll
   for (int p = 0; p < 3; ++p)
 #pragma unroll
     for (int b = 0; b < TNB; ++b)
-      acc[b] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qf[b], pf[p], acc[b], QF, 0, 0, 0,
-                                                                0, 0);
+      acc[b] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qf[b], pf[p], acc[b], QF, 0, 0,
+                                                                127, 0, eb);
 }
 
 struct TokProb {
@@ -93,7 +103,7 @@ struct TokProb {
   int64_t ldq;
   const float* sq;       // their scale
   const uint8_t* P;      // pieces [3][Rp][Tp]
-  const float* sp;       // per-rank scale [Rp]
+  const uint8_t* E;      // their scale bytes [Tp / 128][Rp][4]
   float* out;            // [N x r] (n_major) or [r x N]
   int N, n_major, tiles_n, blocks;
 };
@@ -118,7 +128,7 @@ __device__ __forceinline__ int tok_xcd_remap(int bid, int n) {
 // (fastest)
 template <int QF0>
 __global__ __launch_bounds__(kTkThreads, 1) void tok_kernel(TokArgs a) {
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[TKS * TSTAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[TE_OFF + 2 * TE_WIN];
   int b = tok_xcd_remap((int)blockIdx.x, (int)gridDim.x);
   const int pi = b >= a.p[0].blocks ? 1 : 0;
   if (pi) b -= a.p[0].blocks;
@@ -129,7 +139,7 @@ __global__ __launch_bounds__(kTkThreads, 1) void tok_kernel(TokArgs a) {
   pr.ldq = pi ? a.p[1].ldq : a.p[0].ldq;
   pr.sq = pi ? a.p[1].sq : a.p[0].sq;
   pr.P = pi ? a.p[1].P : a.p[0].P;
-  pr.sp = pi ? a.p[1].sp : a.p[0].sp;
+  pr.E = pi ? a.p[1].E : a.p[0].E;
   pr.out = pi ? a.p[1].out : a.p[0].out;
   pr.N = pi ? a.p[1].N : a.p[0].N;
   pr.n_major = pi ? a.p[1].n_major : a.p[0].n_major;
@@ -162,6 +172,16 @@ __global__ __launch_bounds__(kTkThreads, 1) void tok_kernel(TokArgs a) {
     gP[q] = pr.P + (int64_t)(R >> 6) * a.Rp * a.Tp + (int64_t)(j0 + row) * a.Tp + k_lo * TKK +
             ((lslot ^ swz8(row)) * 16);
   }
+  // scale bytes: in the window that opens at step kt, wave w brings steps
+  // kt + 2 w, kt + 2 w + 1 (lanes 0 .. 15, 16 .. 31: 16 bytes each of the
+  // step's 256; steps past the last are clamped to it and never read)
+  const int e_step = 2 * w + ((lane >> 4) & 1);
+  auto issue_e = [&](int kt) {
+    const int64_t c = k_lo + min(kt + e_step, a.Tp / TKK - 1 - k_lo);
+    const uint8_t* src = pr.E + (c * a.Rp + j0) * 4 + (lane & 15) * 16;
+    const uint32_t dst = lds_offset(smem + TE_OFF + ((kt / TEW) & 1) * TE_WIN + w * 512);
+    if (lane < 32) load16_to_lds(src, __builtin_amdgcn_readfirstlane(dst));
+  };
   auto issue = [&](int stage, int kt) {
     const uint32_t base = lds_offset(smem + stage * TSTAGE);
     // token rows advance with kt; a row past T - 1 stays clamped
@@ -177,6 +197,7 @@ __global__ __launch_bounds__(kTkThreads, 1) void tok_kernel(TokArgs a) {
     for (int q = 0; q < TP_I; ++q)
       load16_to_lds(gP[q] + kt * TKK,
                     __builtin_amdgcn_readfirstlane(base + TQ_BYTES + (w * TP_I + q) * 1024));
+    if (kt % TEW == 0) issue_e(kt);
   };
 
   v4f acc[TNB];
@@ -200,11 +221,17 @@ __global__ __launch_bounds__(kTkThreads, 1) void tok_kernel(TokArgs a) {
   for (int kt = 0; kt < nk; ++kt) {
     // stage kt has landed once the loads of the stages issued after it (at
     // most TKS - 2) are all that is left in flight
+    // (a window stage among them carries one load more)
     const int after = min(TKS - 2, nk - 1 - kt);
-    if (after >= 2) wait_vmem(2 * TLPS); else if (after == 1) wait_vmem(TLPS); else wait_vmem(0);
+    const bool win = (after >= 1 && (kt + 1) % TEW == 0) || (after >= 2 && (kt + 2) % TEW == 0);
+    const int pending = after * TLPS + (win ? 1 : 0);
+    if (pending == 9) wait_vmem(9); else if (pending == 8) wait_vmem(8);
+    else if (pending == 5) wait_vmem(5); else if (pending == 4) wait_vmem(4); else wait_vmem(0);
     barrier_no_drain();
     const uint8_t* st = smem + (kt % TKS) * TSTAGE;
     v8i pf[3], qf[TNB];
+    const int eb = smem[TE_OFF + ((kt / TEW) & 1) * TE_WIN + (kt % TEW) * (TKR * 4) +
+                        (rb * 16 + r16) * 4 + g];
 #pragma unroll
     for (int p = 0; p < 3; ++p) {
       const uint8_t* pp = st + offP + p * TP_PLANE;
@@ -224,15 +251,15 @@ __global__ __launch_bounds__(kTkThreads, 1) void tok_kernel(TokArgs a) {
     }
     if (kt + TKS - 1 < nk) issue((kt + TKS - 1) % TKS, kt + TKS - 1);
     if (QF0 == 0 || pi)
-      mma_pieces<0>(qf, pf, acc);
+      mma_pieces<0>(qf, pf, eb, acc);
     else
-      mma_pieces<QF0>(qf, pf, acc);
+      mma_pieces<QF0>(qf, pf, eb, acc);
   }
 
   // lane: rank j0 + rb * 16 + r16, columns n0 + nh * 32 + 16 bb + 4 g .. +3
   const int j = j0 + rb * 16 + r16;
   if (j >= a.r) return;
-  const float inv = 1.0f / (pr.sq[0] * pr.sp[j]);
+  const float inv = 1.0f / pr.sq[0];
 #pragma unroll
   for (int bb = 0; bb < TNB; ++bb) {
     const int n = n0 + nh * 32 + 16 * bb + 4 * g;
@@ -251,54 +278,37 @@ __global__ __launch_bounds__(kTkThreads, 1) void tok_kernel(TokArgs a) {
   }
 }
 
-// Pieces of the problems' float factors (problem blockIdx.y: 0 U for dB, 1 V
-// for dA; element (t, j) at F[j * rs + t * cs]) for rank j = blockIdx.x <
-// Rp, tokens t < Tp (zero past T and for j >= r), for the problems whose bit
-// is set in pmask; the blocks past Rp clear the problem's output (n_out
-// floats) when the two token halves are to be added onto it.
-constexpr int kUvThreads = 1024, kUvHold = 16;
+// Pieces of the problems' float factors F [T x r] (element (t, j) at
+// F[t * r + j]) where no earlier kernel formed them: blocks [0, ub) those of
+// U, [ub, ub + vb) those of V, the rest clear the outputs (n0 floats of z0,
+// n1 of z1) that the two token halves are added onto.
+constexpr int kUvThreads = 1024, kUvZero = 16;
 
-struct UvJob {
-  const float* F;
-  int64_t rs, cs;
-  uint8_t* P;
-  float* sp;
-  float* out;
-  int64_t n_out;
-};
-
-__device__ __forceinline__ void uv_job(const UvJob& q, int64_t j, int64_t T, int64_t r, int64_t Tp,
-                                       int64_t Rp, bool pieces) {
-  if (j >= Rp) {
-    const int64_t base = (j - Rp) * kUvThreads * kUvHold;
-#pragma unroll
-    for (int i = 0; i < kUvHold; ++i) {
-      const int64_t k = base + threadIdx.x + (int64_t)i * kUvThreads;
-      if (k < q.n_out) q.out[k] = 0.0f;
-    }
+__global__ __launch_bounds__(kUvThreads) void uv_pieces_kernel(PieceJob u, int64_t ub, PieceJob v,
+                                                               int64_t vb, float* z0, int64_t n0,
+                                                               float* z1, int64_t n1) {
+  int64_t b = blockIdx.x;
+  if (b < ub + vb) {
+    const bool is_u = b < ub;
+    const PieceJob& q = is_u ? u : v;
+    const int64_t gid = (is_u ? b : b - ub) * kUvThreads + threadIdx.x;
+    // a job's lanes come in whole waves
+    if (gid < piece_job_lanes<false>(q.Rp, q.Kp)) piece_job_lane<false>(q, gid);
     return;
   }
-  if (!pieces) return;
-  if (j < r)
-    piece_row<kUvThreads, kUvHold>(q.F + j * q.rs, q.cs, T, Tp, q.P + j * Tp, Rp * Tp, q.sp + j);
-  else
-    piece_row_zero<kUvThreads>(Tp, q.P + j * Tp, Rp * Tp, q.sp + j);
-}
-
-__global__ __launch_bounds__(kUvThreads) void uv_pieces_kernel(UvJob u, UvJob v, int64_t T,
-                                                               int64_t r, int64_t Tp, int64_t Rp,
-                                                               int pmask) {
-  const int64_t j = blockIdx.x;
-  if (blockIdx.y == 0)
-    uv_job(u, j, T, r, Tp, Rp, pmask & 1);
-  else
-    uv_job(v, j, T, r, Tp, Rp, (pmask >> 1) & 1);
+  b -= ub + vb;
+#pragma unroll
+  for (int i = 0; i < kUvZero; ++i) {
+    const int64_t k = (b * kUvZero + i) * kUvThreads + threadIdx.x;
+    if (k < n0) z0[k] = 0.0f;
+    if (k < n1) z1[k] = 0.0f;
+  }
 }
 
 struct TokPlan {
   int64_t Tp, Rp;
   int S, kps, tiles[2];
-  size_t p[2], sp[2], total;
+  size_t p[2], e[2], total;
 };
 
 TokPlan tok_plan(int64_t T, int64_t d_in, int64_t d_out, int64_t r, bool want_da) {
@@ -320,7 +330,7 @@ TokPlan tok_plan(int64_t T, int64_t d_in, int64_t d_out, int64_t r, bool want_da
   auto take = [&](size_t bytes) { size_t at = o; o = align_up(o + bytes, 256); return at; };
   for (int i = 0; i < 2; ++i) {
     q.p[i] = take((size_t)(3 * q.Rp * q.Tp));
-    q.sp[i] = take((size_t)(q.Rp * 4));
+    q.e[i] = take((size_t)(q.Tp / TKK * q.Rp * 4));
   }
   q.total = o;
   return q;
@@ -338,44 +348,43 @@ size_t token_grads_ws_bytes(int64_t T, int64_t d_in, int64_t d_out, int64_t r) {
   return tok_plan(T, d_in, d_out, r, true).total;
 }
 
-void token_grads_u_pieces(void* ws, int64_t T, int64_t d_in, int64_t d_out, int64_t r,
-                          uint8_t** P, float** sp, int64_t* Rp, int64_t* Tp) {
+void token_grads_pieces(void* ws, int64_t T, int64_t d_in, int64_t d_out, int64_t r, int which,
+                        uint8_t** P, uint8_t** E, int64_t* Rp, int64_t* Tp) {
   const TokPlan q = tok_plan(T, d_in, d_out, r, true);
   uint8_t* base = reinterpret_cast<uint8_t*>(ws);
-  *P = base + q.p[0];
-  *sp = reinterpret_cast<float*>(base + q.sp[0]);
+  *P = base + q.p[which];
+  *E = base + q.e[which];
   *Rp = q.Rp;
   *Tp = q.Tp;
 }
 
 hipError_t launch_token_grads(const uint8_t* gq, int g_fmt, const float* s_g, const uint8_t* xq,
-                              const float* s_x, const float* u, int64_t u_rs, int64_t u_cs,
-                              bool u_ready, const float* v, int64_t v_rs, int64_t v_cs,
-                              int64_t T, int64_t d_in, int64_t d_out, int64_t r, float* dA,
-                              float* dB, void* ws, hipStream_t s) {
+                              const float* s_x, const float* u, bool u_ready, const float* v,
+                              bool v_ready, int64_t T, int64_t d_in, int64_t d_out, int64_t r,
+                              float* dA, float* dB, void* ws, hipStream_t s) {
   const bool want_da = dA != nullptr;
   const TokPlan q = tok_plan(T, d_in, d_out, r, want_da);
   uint8_t* base = reinterpret_cast<uint8_t*>(ws);
-  auto f32 = [&](size_t off) { return reinterpret_cast<float*>(base + off); };
   {
-    // zeroing blocks (two token halves only): kUvThreads * kUvHold floats each
-    const int64_t n_out0 = q.S > 1 ? d_out * r : 0, n_out1 = q.S > 1 && want_da ? r * d_in : 0;
-    const int64_t per = (int64_t)kUvThreads * kUvHold;
-    const int64_t zb = (std::max(n_out0, n_out1) + per - 1) / per;
-    const int pmask = (u_ready ? 0 : 1) | (want_da ? 2 : 0);
-    const UvJob ju{u, u_rs, u_cs, base + q.p[0], f32(q.sp[0]), dB, n_out0};
-    const UvJob jv{v, v_rs, v_cs, base + q.p[1], f32(q.sp[1]), dA, n_out1};
-    if (pmask != 0 || zb > 0) {
-      dim3 grid((unsigned)(q.Rp + zb), want_da ? 2u : 1u);
-      uv_pieces_kernel<<<grid, kUvThreads, 0, s>>>(ju, jv, T, r, q.Tp, q.Rp, pmask);
+    const PieceJob ju{u, 1, r, r, T, base + q.p[0], base + q.e[0], q.Rp, q.Tp};
+    const PieceJob jv{v, 1, r, r, T, base + q.p[1], base + q.e[1], q.Rp, q.Tp};
+    const int64_t jobs = (piece_job_lanes<false>(q.Rp, q.Tp) + kUvThreads - 1) / kUvThreads;
+    const int64_t ub = u_ready ? 0 : jobs, vb = v_ready || !want_da ? 0 : jobs;
+    // clearing blocks (two token halves only): kUvThreads * kUvZero floats each
+    const int64_t n0 = q.S > 1 ? d_out * r : 0, n1 = q.S > 1 && want_da ? r * d_in : 0;
+    const int64_t per = (int64_t)kUvThreads * kUvZero;
+    const int64_t zb = (std::max(n0, n1) + per - 1) / per;
+    if (ub + vb + zb > 0) {
+      uv_pieces_kernel<<<(unsigned)(ub + vb + zb), kUvThreads, 0, s>>>(ju, ub, jv, vb, dB, n0, dA,
+                                                                       n1);
       hipError_t e = hipGetLastError();
       if (e != hipSuccess) return e;
     }
   }
   TokArgs a{};
-  a.p[0] = TokProb{gq, d_out, s_g, base + q.p[0], f32(q.sp[0]), dB, (int)d_out, 1,
+  a.p[0] = TokProb{gq, d_out, s_g, base + q.p[0], base + q.e[0], dB, (int)d_out, 1,
                    (int)(d_out / TKN), q.tiles[0] * q.S};
-  a.p[1] = TokProb{xq, d_in, s_x, base + q.p[1], f32(q.sp[1]), dA, (int)d_in, 0,
+  a.p[1] = TokProb{xq, d_in, s_x, base + q.p[1], base + q.e[1], dA, (int)d_in, 0,
                    (int)(d_in / TKN), q.tiles[1] * q.S};
   a.T = (int)T;
   a.Tp = (int)q.Tp;

@@ -252,9 +252,9 @@ falq_status melded_linear_bwd_fmt(const uint8_t *gq, int g_fmt, const float *s_g
  * (melded_linear_xa_fused returns 1: r <= d_out / 64 and r <= d_in / 64, K
  * multiples of 128, and no large-rank route), X^ A^T is formed inside the
  * forward FP8 product and G^ B inside the dX product, with the float factor
- * entering the FP8 matrix cores as three E4M3 pieces per element and one
- * scale per rank (residual about 2^-12 of an element); otherwise by the
- * skinny kernels.  For ranks where melded_linear_bwd takes the full weight
+ * entering the FP8 matrix cores as three E4M3 pieces per element under a
+ * power-of-two scale per rank and 32-element block (residual about 2^-12 of
+ * an element); otherwise by the skinny kernels.  For ranks where melded_linear_bwd takes the full weight
  * gradient route, the backward takes it too and does not read xa.
  *
  *   A [r x d_in], B [d_out x r] float32; xa [T x r] float32 (output of the

@@ -47,6 +47,8 @@ XA_SHAPES = [  # (T, d_in, d_out, r, fused)
     (600, 1024, 1280, 16, True),      # ragged T and a 5-tile N
     (1024, 2048, 2048, 32, True),
     (384, 2048, 1024, 13, True),      # rank not a multiple of the 16-row piece tile
+    (9000, 1024, 1024, 8, True),      # two token splits of 36 steps: three 16-step windows of
+                                      # scale bytes each (a buffer reused), a clamped last one
     (256, 512, 512, 16, False),       # too few column tiles to carry the pieces
     (257, 400, 272, 5, False),        # K not a multiple of 128
     (300, 384, 640, 8, False),
