@@ -32,8 +32,8 @@
 // both the transpose reads and the piece fragment reads are free of bank
 // conflicts).  The kernel is bound by the number of direct-load instructions
 // a CU issues, so the scale bytes (256 per step) come in windows of 16 steps
-// (4 KB, one half-wave load per wave, double-buffered) with the stage that
-// opens the window, not with every stage.  With too few tiles to fill half the GPU the tokens are split
+// (4 KB, one half-wave load per wave, double-buffered), not with every
+// stage.  With too few tiles to fill half the GPU the tokens are split
 // in two halves whose results are added with float atomics onto outputs
 // zeroed beforehand: exactly two addends meet a zero, and a + b does not
 // depend on which lands first, so the result is the same on every run.
@@ -59,8 +59,7 @@ constexpr int TLPS = TQ_I + TP_I;                        // direct loads per wav
 static_assert(TQ_I * 1024 * TKW == TQ_BYTES && TP_I * 1024 * TKW == 3 * TP_PLANE, "loads");
 static_assert(TE_WIN == TKW * 32 * 16, "one window: 32 lanes x 16 bytes per wave");
 static_assert(TE_OFF + 2 * TE_WIN <= 160 * 1024, "LDS");
-static_assert(TLPS == 4 && TKS == 4, "wait counts below assume four loads per stage (plus one "
-                                     "on window stages), 4 stages");
+static_assert(TLPS == 4 && TKS == 4, "wait counts below assume four loads per stage, 4 stages");
 
 // 128-byte piece rows: 16-byte chunk c of row r at slot c ^ swz8(r) (the
 // FP8 GEMM's pattern: the 16-row fragment reads are conflict-free)
@@ -158,11 +157,13 @@ __global__ __launch_bounds__(kTkThreads, 1) void tok_kernel(TokArgs a) {
 
   // direct-load sources: FP8 rows (tokens, clamped into [0, T): rows past T
   // meet zero pieces), piece rows (ranks of this tile, 3 planes)
+  // (the lane's code row within a step, and its column offset)
+  int qR[TQ_I];
   const uint8_t* gQ[TQ_I];
 #pragma unroll
   for (int q = 0; q < TQ_I; ++q) {
-    const int R = (w * TQ_I + q) * 16 + qrow;
-    gQ[q] = pr.q + (int64_t)min(k_lo * TKK + R, a.T - 1) * pr.ldq + n0 + ((qslot ^ swz4(R)) * 16);
+    qR[q] = k_lo * TKK + (w * TQ_I + q) * 16 + qrow;
+    gQ[q] = pr.q + n0 + ((qslot ^ swz4(qR[q])) * 16);
   }
   const uint8_t* gP[TP_I];
 #pragma unroll
@@ -183,21 +184,24 @@ __global__ __launch_bounds__(kTkThreads, 1) void tok_kernel(TokArgs a) {
     if (lane < 32) load16_to_lds(src, __builtin_amdgcn_readfirstlane(dst));
   };
   auto issue = [&](int stage, int kt) {
+    // the next window rides ahead of the loads of the step that precedes it,
+    // so that waiting for any step also covers its window (at the cost of
+    // waiting for one load more in two steps of sixteen)
+    if ((kt + 1) % TEW == 0) issue_e(kt + 1);
     const uint32_t base = lds_offset(smem + stage * TSTAGE);
-    // token rows advance with kt; a row past T - 1 stays clamped
+    // token rows advance with kt; a row past T - 1 is clamped to it (the
+    // swizzle depends on the row's position in the tile only: bits 2 and 5,
+    // unchanged by whole steps)
 #pragma unroll
     for (int q = 0; q < TQ_I; ++q) {
-      const int R = (w * TQ_I + q) * 16 + qrow;
-      const int64_t t = (int64_t)(k_lo + kt) * TKK + R;
-      const uint8_t* src = t < a.T ? gQ[q] + (int64_t)kt * TKK * pr.ldq
-                                   : pr.q + (int64_t)(a.T - 1) * pr.ldq + n0 + ((qslot ^ swz4(R)) * 16);
-      load16_to_lds(src, __builtin_amdgcn_readfirstlane(base + (w * TQ_I + q) * 1024));
+      const int t = min(qR[q] + kt * TKK, a.T - 1);
+      load16_to_lds(gQ[q] + (int64_t)t * pr.ldq,
+                    __builtin_amdgcn_readfirstlane(base + (w * TQ_I + q) * 1024));
     }
 #pragma unroll
     for (int q = 0; q < TP_I; ++q)
       load16_to_lds(gP[q] + kt * TKK,
                     __builtin_amdgcn_readfirstlane(base + TQ_BYTES + (w * TP_I + q) * 1024));
-    if (kt % TEW == 0) issue_e(kt);
   };
 
   v4f acc[TNB];
@@ -206,6 +210,7 @@ __global__ __launch_bounds__(kTkThreads, 1) void tok_kernel(TokArgs a) {
 #pragma unroll
     for (int v = 0; v < 4; ++v) acc[i][v] = 0.0f;
 
+  if (nk > 0) issue_e(0);
 #pragma unroll
   for (int s = 0; s < TKS - 1; ++s)
     if (s < nk) issue(s, s);
@@ -217,16 +222,11 @@ __global__ __launch_bounds__(kTkThreads, 1) void tok_kernel(TokArgs a) {
   // transpose reads: lane (g, s = r16) reads row 32 g + 8 i + s / 2 of the
   // FP8 tile, bytes 8 (s % 2) .. +7 of its 16-byte column chunk
   const int trow = 32 * g + (r16 >> 1), thalf = 8 * (r16 & 1);
-  __builtin_amdgcn_s_waitcnt(0xC07F);                        // lgkmcnt(0)
-  for (int kt = 0; kt < nk; ++kt) {
-    // stage kt has landed once the loads of the stages issued after it (at
-    // most TKS - 2) are all that is left in flight
-    // (a window stage among them carries one load more)
-    const int after = min(TKS - 2, nk - 1 - kt);
-    const bool win = (after >= 1 && (kt + 1) % TEW == 0) || (after >= 2 && (kt + 2) % TEW == 0);
-    const int pending = after * TLPS + (win ? 1 : 0);
-    if (pending == 9) wait_vmem(9); else if (pending == 8) wait_vmem(8);
-    else if (pending == 5) wait_vmem(5); else if (pending == 4) wait_vmem(4); else wait_vmem(0);
+  // one step: stage kt has landed (with any window issued before it) once
+  // the loads of the `after` stages issued after it are all that is left in
+  // flight; then its operands, the loads of step kt + TKS - 1, the MFMAs
+  auto step = [&](int kt, int after, bool refill) {
+    if (after >= 2) wait_vmem(2 * TLPS); else if (after == 1) wait_vmem(TLPS); else wait_vmem(0);
     barrier_no_drain();
     const uint8_t* st = smem + (kt % TKS) * TSTAGE;
     v8i pf[3], qf[TNB];
@@ -249,12 +249,18 @@ __global__ __launch_bounds__(kTkThreads, 1) void tok_kernel(TokArgs a) {
         qf[bb][2 * i + 1] = x[1];
       }
     }
-    if (kt + TKS - 1 < nk) issue((kt + TKS - 1) % TKS, kt + TKS - 1);
+    if (refill) issue((kt + TKS - 1) % TKS, kt + TKS - 1);
     if (QF0 == 0 || pi)
       mma_pieces<0>(qf, pf, eb, acc);
     else
       mma_pieces<QF0>(qf, pf, eb, acc);
-  }
+  };
+  __builtin_amdgcn_s_waitcnt(0xC07F);                        // lgkmcnt(0)
+  int kt = 0;
+  // steady state: TKS - 2 stages behind each, and one to refill
+  for (; kt + TKS - 1 < nk; ++kt) step(kt, TKS - 2, true);
+  // the last TKS - 1 steps (or fewer)
+  for (; kt < nk; ++kt) step(kt, min(TKS - 2, nk - 1 - kt), false);
 
   // lane: rank j0 + rb * 16 + r16, columns n0 + nh * 32 + 16 bb + 4 g .. +3
   const int j = j0 + rb * 16 + r16;
