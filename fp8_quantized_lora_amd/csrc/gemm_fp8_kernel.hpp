@@ -431,7 +431,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_fp8_nt_dma(
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int j = 0; j < NB; ++j) acc[i][j] = mma(af[i & 1], bf[j], acc[i][j]);
-      if (FU && wave_u && i == iu) {
+      if (FU && wave_u && __builtin_expect(i == iu, 0)) {
 #pragma unroll
         for (int p = 0; p < NU; ++p) {
           if constexpr (BS)

@@ -118,6 +118,18 @@ __global__ __launch_bounds__(kThreads, 2) void proxy_score(const uint8_t* __rest
   // accumulator, which leaves each one (signed zeros included) unchanged.
   auto issue = [&](int buf, int k0) {
     const uint32_t lbase = lds_offset(&sA[buf][0][0]);
+    if (k0 + KC <= r) {
+      // a whole stage of real ranks: no test per load (branches in this
+      // barrier-paced loop cost more than their instructions)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int c = w * 4 + j, kk = c >> 1, h = c & 1;
+        const int gc = min(col0 + h * 256 + lane * 4, d_in - 4);
+        load16_to_lds(A + (int64_t)rk(k0 + kk) * d_in + gc,
+                      __builtin_amdgcn_readfirstlane(lbase + c * 1024));
+      }
+      return;
+    }
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int c = w * 4 + j, kk = c >> 1, h = c & 1;
