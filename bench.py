@@ -357,6 +357,10 @@ def run(args):
         "tokens_per_s": round(tokens_per_s, 1),
         "roofline": {"kernel": ("melded_linear_fwd_frozen_a call (FP8 GEMM 4096 x 4096 x 4096 "
                                 "+ X~A~^T)" if frozen else
+                                "melded_linear_fwd_xa_pieces call (one FP8 GEMM 4096 x 4096 x "
+                                "4096 forming X^A^T in the same tiles from A's block-scaled E4M3 "
+                                "pieces, which the SGD step leaves)"
+                                if m.keep_pieces else
                                 "melded_linear_fwd_xa call (A as block-scaled E4M3 pieces, then "
                                 "one FP8 GEMM 4096 x 4096 x 4096 forming X^A^T in the same tiles)"
                                 if m.use_xa else
@@ -499,7 +503,10 @@ def layer_workload(args, torch, fq, wl):
                    "tokens": T, "linears": len(layers), "rank": s0.rank,
                    "parallelism": "single GPU"},
         "tokens_per_s": round(T / (ms * 1e-3), 1),
-        "roofline": {"kernel": (f"melded_linear_fwd_xa call ({s0.name}: A as block-scaled E4M3 "
+        "roofline": {"kernel": (f"melded_linear_fwd_xa_pieces call ({s0.name}: one FP8 GEMM {T} "
+                                f"x {s0.d_out} x {s0.d_in} forming X^A^T in the same tiles from "
+                                f"A's pieces, which the SGD step leaves)" if m0.keep_pieces else
+                                f"melded_linear_fwd_xa call ({s0.name}: A as block-scaled E4M3 "
                                 f"pieces, then one FP8 GEMM {T} x {s0.d_out} x {s0.d_in} forming "
                                 f"X^A^T in the same tiles)" if m0.use_xa else
                                 f"melded_linear_fwd FP8 GEMM ({T} x {s0.d_out} x {s0.d_in}, "

@@ -28,6 +28,8 @@ __all__ = ["load", "FalqError", "fp8_quantize", "fp8_quantize_workspace_bytes",
            "fp4_quantize", "melded_linear_fwd_fp4", "version", "LIB_PATH",
            "fp8_quantize_noalloc", "QUANTIZE_SCRATCH_BYTES",
            "melded_linear_xa_fused", "melded_linear_fwd_xa", "melded_linear_bwd_xa",
+           "adapter_pieces_bytes", "adapter_pieces", "adapter_step_pieces",
+           "melded_linear_fwd_xa_pieces",
            "melded_linear_fwd_xa_workspace_bytes", "melded_linear_bwd_xa_workspace_bytes",
            "lora_separate_fp8_saved_bytes", "lora_separate_fp8_workspace_bytes",
            "lora_separate_fp8_fwd", "lora_separate_fp8_bwd", "lora_bf16_saved_bytes",
@@ -81,6 +83,12 @@ _SIGS = {
     "fp8_quantize_noalloc": (_i32, [_c_p, _i32, _i64, _i32, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p]),
     "melded_linear_fwd_fp4": (_i32, [_c_p, _c_p, _c_p, _c_p, _i64, _i64, _i64, _c_p, _c_p]),
     "melded_linear_xa_fused": (_i32, [_i64, _i64, _i64, _i64]),
+    "adapter_pieces_bytes": (_sz, [_i64, _i64]),
+    "adapter_pieces": (_i32, [_c_p, _i64, _i64, _c_p, _sz, _c_p]),
+    "adapter_step_pieces": (_i32, [_c_p, _c_p, _c_p, _c_p, _i64, _i64, _i64, _f32, _c_p, _sz,
+                                   _c_p]),
+    "melded_linear_fwd_xa_pieces": (_i32, [_c_p, _c_p, _c_p, _c_p, _c_p, _sz, _i64, _i64, _i64,
+                                           _i64, _c_p, _c_p, _c_p]),
     "melded_linear_fwd_xa_workspace_bytes": (_sz, [_i64, _i64, _i64, _i64]),
     "melded_linear_fwd_xa": (_i32, [_c_p, _c_p, _c_p, _c_p, _c_p, _i64, _i64, _i64, _i64, _c_p,
                                     _c_p, _c_p, _sz, _c_p]),
@@ -480,6 +488,45 @@ def melded_linear_fwd_xa(xq, s_x, wq, s_w, A, y, xa, ws=None, stream=None) -> No
     _check(load().melded_linear_fwd_xa(_ptr(xq), _ptr(s_x), _ptr(wq), _ptr(s_w), _ptr(A), T, d_in,
                                        d_out, r, _ptr(y), _ptr(xa), _ptr(ws), ws.numel(),
                                        _stream(stream)), "melded_linear_fwd_xa")
+
+
+def adapter_pieces_bytes(r: int, d_in: int) -> int:
+    """Bytes of the buffer that holds A's pieces (0: not available)."""
+    return int(load().adapter_pieces_bytes(r, d_in))
+
+
+def adapter_pieces(A, pieces, stream=None) -> None:
+    """A's block-scaled E4M3 pieces into `pieces` (uint8, adapter_pieces_bytes)."""
+    r, d_in = A.shape
+    _req(A, torch.float32, (r, d_in), "A")
+    _check(load().adapter_pieces(_ptr(A), r, d_in, _ptr(pieces), pieces.numel(),
+                                 _stream(stream)), "adapter_pieces")
+
+
+def adapter_step_pieces(A, B, dA, dB, lr: float, pieces, stream=None) -> None:
+    """adapter_step (SGD on A and B), and the pieces of the new A into `pieces`."""
+    r, d_in = A.shape
+    d_out = B.shape[0]
+    _req(A, torch.float32, (r, d_in), "A")
+    _req(dA, torch.float32, (r, d_in), "dA")
+    _req(B, torch.float32, (d_out, r), "B")
+    _req(dB, torch.float32, (d_out, r), "dB")
+    _check(load().adapter_step_pieces(_ptr(A), _ptr(B), _ptr(dA), _ptr(dB), r, d_in, d_out, lr,
+                                      _ptr(pieces), pieces.numel(), _stream(stream)),
+           "adapter_step_pieces")
+
+
+def melded_linear_fwd_xa_pieces(xq, s_x, wq, s_w, pieces, r: int, y, xa, stream=None) -> None:
+    """melded_linear_fwd_xa with A given as its pieces (adapter_pieces / adapter_step_pieces)."""
+    T, d_in = xq.shape
+    d_out = wq.shape[0]
+    _req(wq, torch.uint8, (d_out, d_in), "wq")
+    _req(y, torch.float32, (T, d_out), "y")
+    _req(xa, torch.float32, (T, r), "xa")
+    _check(load().melded_linear_fwd_xa_pieces(_ptr(xq), _ptr(s_x), _ptr(wq), _ptr(s_w),
+                                              _ptr(pieces), pieces.numel(), T, d_in, d_out, r,
+                                              _ptr(y), _ptr(xa), _stream(stream)),
+           "melded_linear_fwd_xa_pieces")
 
 
 def melded_linear_bwd_xa(gq, s_g, xq, s_x, wq, s_w, A, B, xa, dx, dA, dB, ws=None, stream=None,

@@ -1019,6 +1019,106 @@ hipError_t launch_fwd_xa(const uint8_t* xq, const float* s_x, const uint8_t* wq,
   return launch_one_skinny(xq, d_in, 0, s_x, A, false, T, d_in, r, xa, ws, s);
 }
 
+// ---------------------------------------------------------------------------
+// A's pieces kept by the optimizer: A changes only in the adapter step, so
+// the step that moves A can leave the pieces the next forward needs, and the
+// forward then launches no pieces kernel.
+// ---------------------------------------------------------------------------
+namespace {
+
+// blocks [0, na): SGD on A and the pieces of the new A (8 lanes per 32-element
+// block, four consecutive elements each); blocks [na, na + nb): SGD on B.
+// The update is the same as sgd_kernel's, p - lr * g with two roundings.
+__global__ __launch_bounds__(kPieceThreads) void sgd_pieces_kernel(
+    float* __restrict__ A, const float* __restrict__ dA, int64_t r, int64_t d_in,
+    float* __restrict__ B, const float* __restrict__ dB, int64_t nbv, float lr, PieceJob q,
+    int64_t na) {
+  const int64_t b = blockIdx.x;
+  if (b < na) {
+    const int64_t gid = b * kPieceThreads + threadIdx.x;
+    // the job's lanes come in whole waves
+    if (gid >= piece_job_lanes<true>(q.Rp, q.Kp)) return;
+    int64_t j, c;
+    int s, d, t;
+    piece_lane_pos<true>(q.Rp, gid, j, c, s, d, t);
+    float v[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    if (j < r) {
+      float4* pa = reinterpret_cast<float4*>(A + j * d_in + c * 128 + d);
+      float4 a = *pa;
+      const float4 g = *reinterpret_cast<const float4*>(dA + j * d_in + c * 128 + d);
+      a.x = a.x - lr * g.x;
+      a.y = a.y - lr * g.y;
+      a.z = a.z - lr * g.z;
+      a.w = a.w - lr * g.w;
+      *pa = a;
+      v[0] = a.x;
+      v[1] = a.y;
+      v[2] = a.z;
+      v[3] = a.w;
+    }
+    piece_lane_store<true, 4>(v, q.P, q.E, q.Rp, q.Kp, j, c, s, d, t);
+    return;
+  }
+  const int64_t i = (b - na) * kPieceThreads + threadIdx.x;
+  if (i < nbv / 4) {
+    float4 x = reinterpret_cast<float4*>(B)[i];
+    const float4 g = reinterpret_cast<const float4*>(dB)[i];
+    x.x = x.x - lr * g.x;
+    x.y = x.y - lr * g.y;
+    x.z = x.z - lr * g.z;
+    x.w = x.w - lr * g.w;
+    reinterpret_cast<float4*>(B)[i] = x;
+  }
+  if (b == na) {
+    for (int64_t k = nbv / 4 * 4 + threadIdx.x; k < nbv; k += kPieceThreads) B[k] = B[k] - lr * dB[k];
+  }
+}
+
+}  // namespace
+
+bool adapter_pieces_ok(int64_t r, int64_t d_in) {
+  return r > 0 && d_in > 0 && d_in % 128 == 0 && r <= ((int64_t)1 << 20) &&
+         d_in <= ((int64_t)1 << 31);
+}
+
+size_t adapter_pieces_bytes(int64_t r, int64_t d_in) {
+  return adapter_pieces_ok(r, d_in) ? pieces_plan(r, d_in).total : 0;
+}
+
+hipError_t launch_adapter_pieces(const float* A, int64_t r, int64_t d_in, void* pieces,
+                                 hipStream_t s) {
+  const PiecesPlan pp = pieces_plan(r, d_in);
+  uint8_t* base = reinterpret_cast<uint8_t*>(pieces);
+  const PieceJob q{A, d_in, 1, r, d_in, base + pp.p, base + pp.e, pp.Rp, d_in};
+  const int64_t blocks = (piece_job_lanes<true>(pp.Rp, d_in) + kPieceThreads - 1) / kPieceThreads;
+  pieces_kernel<<<(unsigned)blocks, kPieceThreads, 0, s>>>(q);
+  return hipGetLastError();
+}
+
+hipError_t launch_sgd_pieces(float* A, float* B, const float* dA, const float* dB, int64_t r,
+                             int64_t d_in, int64_t d_out, float lr, void* pieces, hipStream_t s) {
+  const PiecesPlan pp = pieces_plan(r, d_in);
+  uint8_t* base = reinterpret_cast<uint8_t*>(pieces);
+  const PieceJob q{A, d_in, 1, r, d_in, base + pp.p, base + pp.e, pp.Rp, d_in};
+  const int64_t na = (piece_job_lanes<true>(pp.Rp, d_in) + kPieceThreads - 1) / kPieceThreads;
+  const int64_t nbv = d_out * r;
+  const int64_t nb = std::max<int64_t>(1, (nbv / 4 + kPieceThreads - 1) / kPieceThreads);
+  sgd_pieces_kernel<<<(unsigned)(na + nb), kPieceThreads, 0, s>>>(A, dA, r, d_in, B, dB, nbv, lr,
+                                                                    q, na);
+  return hipGetLastError();
+}
+
+hipError_t launch_fwd_xa_pieces(const uint8_t* xq, const float* s_x, const uint8_t* wq,
+                                const float* s_w, const void* pieces, int64_t T, int64_t d_in,
+                                int64_t d_out, int64_t r, float* y, float* xa, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  const PiecesPlan pp = pieces_plan(r, d_in);
+  const uint8_t* base = reinterpret_cast<const uint8_t*>(pieces);
+  return launch_gemm_fp8_nt_pieces(xq, d_in, wq, d_in, y, d_out, T, d_out, d_in, s_x, s_w,
+                                   base + pp.p, base + pp.e, pp.Rp, r, xa, r, nullptr, nullptr, 0,
+                                   0, s, 0);
+}
+
 // V = G^ B [T x r] (row-major), when no kernel writes it straight as pieces
 size_t bwd_xa_ws_bytes(int64_t T, int64_t d_in, int64_t d_out, int64_t r) {
   if (r <= 0 || T <= 0 || d_in <= 0 || d_out <= 0) return 0;

@@ -548,6 +548,43 @@ falq_status melded_linear_fwd_xa(const uint8_t* xq, const float* s_x, const uint
                                         reinterpret_cast<hipStream_t>(stream)));
 }
 
+size_t adapter_pieces_bytes(int64_t r, int64_t d_in) { return falq::adapter_pieces_bytes(r, d_in); }
+
+falq_status adapter_pieces(const float* A, int64_t r, int64_t d_in, void* pieces,
+                           size_t pieces_bytes, falq_stream stream) {
+  if (!falq::adapter_pieces_ok(r, d_in) || !need(A)) return FALQ_EINVAL;
+  if (!need(pieces) || pieces_bytes < falq::adapter_pieces_bytes(r, d_in)) return FALQ_EINVAL;
+  return hip_status(
+      falq::launch_adapter_pieces(A, r, d_in, pieces, reinterpret_cast<hipStream_t>(stream)));
+}
+
+falq_status adapter_step_pieces(float* A, float* B, const float* dA, const float* dB, int64_t r,
+                                int64_t d_in, int64_t d_out, float lr, void* pieces,
+                                size_t pieces_bytes, falq_stream stream) {
+  if (!falq::adapter_pieces_ok(r, d_in) || d_out < 0 || d_out > ((int64_t)1 << 31))
+    return FALQ_EINVAL;
+  if (!need(A) || !need(dA)) return FALQ_EINVAL;
+  if (d_out > 0 && (!need(B) || !need(dB))) return FALQ_EINVAL;
+  if (!need(pieces) || pieces_bytes < falq::adapter_pieces_bytes(r, d_in)) return FALQ_EINVAL;
+  return hip_status(falq::launch_sgd_pieces(A, B, dA, dB, r, d_in, d_out, lr, pieces,
+                                            reinterpret_cast<hipStream_t>(stream)));
+}
+
+falq_status melded_linear_fwd_xa_pieces(const uint8_t* xq, const float* s_x, const uint8_t* wq,
+                                        const float* s_w, const void* pieces, size_t pieces_bytes,
+                                        int64_t T, int64_t d_in, int64_t d_out, int64_t r,
+                                        float* y, float* xa, falq_stream stream) {
+  if (!gemm_dims_ok(T, d_in, d_out) || T < 0 || !falq::adapter_pieces_ok(r, d_in))
+    return FALQ_EINVAL;
+  if (!falq::gemm_fp8_nt_fuses_second(d_out, d_in, r)) return FALQ_EINVAL;
+  if (!scalar(s_x) || !scalar(s_w)) return FALQ_EINVAL;
+  if (T > 0 && (!need(xq) || !need(y) || !need(xa))) return FALQ_EINVAL;
+  if (!need(wq)) return FALQ_EINVAL;
+  if (!need(pieces) || pieces_bytes < falq::adapter_pieces_bytes(r, d_in)) return FALQ_EINVAL;
+  return hip_status(falq::launch_fwd_xa_pieces(xq, s_x, wq, s_w, pieces, T, d_in, d_out, r, y, xa,
+                                               reinterpret_cast<hipStream_t>(stream)));
+}
+
 size_t melded_linear_bwd_xa_workspace_bytes(int64_t T, int64_t d_in, int64_t d_out, int64_t r) {
   if (T < 0 || d_in < 0 || d_out < 0 || r < 0) return 0;
   const size_t wt = align_up((size_t)d_in * (size_t)d_out, 256);      // W~^T for dX

@@ -104,6 +104,17 @@ size_t fwd_xa_ws_bytes(int64_t T, int64_t d_in, int64_t d_out, int64_t r);
 hipError_t launch_fwd_xa(const uint8_t* xq, const float* s_x, const uint8_t* wq, const float* s_w,
                          const float* A, int64_t T, int64_t d_in, int64_t d_out, int64_t r,
                          float* y, float* xa, void* ws, hipStream_t s);
+// A's pieces (pieces.hpp layout, rows padded to 16) in a caller's buffer:
+// formed from A, or left by an SGD step on A and B; the forward from them
+bool adapter_pieces_ok(int64_t r, int64_t d_in);
+size_t adapter_pieces_bytes(int64_t r, int64_t d_in);
+hipError_t launch_adapter_pieces(const float* A, int64_t r, int64_t d_in, void* pieces,
+                                 hipStream_t s);
+hipError_t launch_sgd_pieces(float* A, float* B, const float* dA, const float* dB, int64_t r,
+                             int64_t d_in, int64_t d_out, float lr, void* pieces, hipStream_t s);
+hipError_t launch_fwd_xa_pieces(const uint8_t* xq, const float* s_x, const uint8_t* wq,
+                                const float* s_w, const void* pieces, int64_t T, int64_t d_in,
+                                int64_t d_out, int64_t r, float* y, float* xa, hipStream_t s);
 // dB = G^^T U and dA = V^T X^ from U, V [T x r] (float32) on the FP8 matrix
 // cores with the LDS transpose read (token_grad.hip); dA may be null.
 // Needs d_in and d_out multiples of 128.

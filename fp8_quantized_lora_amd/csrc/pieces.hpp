@@ -88,41 +88,36 @@ __host__ __device__ constexpr int64_t piece_job_lanes(int64_t Rp, int64_t Kp) {
   return Rp * Kp / (KC ? 4 : 8);
 }
 
+// where lane gid of a job sits: row j, K step c, block s, its first
+// position d in the step, and t (the lane's index within its block)
 template <bool KC>
-__device__ __forceinline__ void piece_job_lane(const PieceJob& q, int64_t gid) {
-  constexpr int N = KC ? 4 : 8;
-  int64_t j, c;
-  int s, d, t;
+__device__ __forceinline__ void piece_lane_pos(int64_t Rp, int64_t gid, int64_t& j, int64_t& c,
+                                               int& s, int& d, int& t) {
   if constexpr (KC) {
     t = (int)(gid & 7);
     s = (int)((gid >> 3) & 3);
     const int64_t jc = gid >> 5;
-    j = jc % q.Rp;
-    c = jc / q.Rp;
+    j = jc % Rp;
+    c = jc / Rp;
     d = 64 * (s & 1) + 16 * (s >> 1) + 32 * (t >> 2) + 4 * (t & 3);
   } else {
     const int jl = (int)(gid & 15);
     t = (int)((gid >> 4) & 3);
     s = (int)((gid >> 6) & 3);
-    const int64_t jc = gid >> 8, nj = q.Rp / 16;
+    const int64_t jc = gid >> 8, nj = Rp / 16;
     j = (jc % nj) * 16 + jl;
     c = jc / nj;
     d = 64 * (s & 1) + 16 * (s >> 1) + 32 * (t >> 1) + 8 * (t & 1);
   }
-  const int64_t k = c * 128 + d;
-  float v[N];
-  const bool row = j < q.R;
-  const float* src = q.f + (row ? j * q.rs + k * q.cs : 0);
-  if (KC && row && k + 3 < q.K && ((uintptr_t)src & 15) == 0) {
-    const float4 x = *reinterpret_cast<const float4*>(src);
-    v[0] = x.x;
-    v[1] = x.y;
-    v[2] = x.z;
-    v[3] = x.w;
-  } else {
-#pragma unroll
-    for (int i = 0; i < N; ++i) v[i] = row && k + i < q.K ? src[i * q.cs] : 0.0f;
-  }
+}
+
+// the pieces of a lane's N consecutive values v (row j, positions c * 128 +
+// d ..): the block maximum over the block's lanes (wave shuffles), the
+// block's exponent, the codes, the scale byte (by the block's lane t = 0)
+template <bool KC, int N>
+__device__ __forceinline__ void piece_lane_store(const float (&v)[N], uint8_t* __restrict__ P,
+                                                 uint8_t* __restrict__ E, int64_t Rp, int64_t Kp,
+                                                 int64_t j, int64_t c, int s, int d, int t) {
   uint32_t m = 0;
 #pragma unroll
   for (int i = 0; i < N; ++i) m = max(m, finite_mag(v[i]));
@@ -139,8 +134,8 @@ __device__ __forceinline__ void piece_job_lane(const PieceJob& q, int64_t gid) {
   for (int h = 0; h < N / 4; ++h)
     pieces4(ldexpf(v[4 * h], e), ldexpf(v[4 * h + 1], e), ldexpf(v[4 * h + 2], e),
             ldexpf(v[4 * h + 3], e), q0[h], q1[h], q2[h]);
-  uint8_t* p = q.P + j * q.Kp + k;
-  const int64_t plane = q.Rp * q.Kp;
+  uint8_t* p = P + j * Kp + c * 128 + d;
+  const int64_t plane = Rp * Kp;
   if constexpr (N == 4) {
     *reinterpret_cast<uint32_t*>(p) = q0[0];
     *reinterpret_cast<uint32_t*>(p + plane) = q1[0];
@@ -150,7 +145,30 @@ __device__ __forceinline__ void piece_job_lane(const PieceJob& q, int64_t gid) {
     *reinterpret_cast<uint2*>(p + plane) = make_uint2(q1[0], q1[1]);
     *reinterpret_cast<uint2*>(p + 2 * plane) = make_uint2(q2[0], q2[1]);
   }
-  if (t == 0) q.E[(c * q.Rp + j) * 4 + s] = (uint8_t)(127 - e);
+  if (t == 0) E[(c * Rp + j) * 4 + s] = (uint8_t)(127 - e);
+}
+
+template <bool KC>
+__device__ __forceinline__ void piece_job_lane(const PieceJob& q, int64_t gid) {
+  constexpr int N = KC ? 4 : 8;
+  int64_t j, c;
+  int s, d, t;
+  piece_lane_pos<KC>(q.Rp, gid, j, c, s, d, t);
+  const int64_t k = c * 128 + d;
+  float v[N];
+  const bool row = j < q.R;
+  const float* src = q.f + (row ? j * q.rs + k * q.cs : 0);
+  if (KC && row && k + 3 < q.K && ((uintptr_t)src & 15) == 0) {
+    const float4 x = *reinterpret_cast<const float4*>(src);
+    v[0] = x.x;
+    v[1] = x.y;
+    v[2] = x.z;
+    v[3] = x.w;
+  } else {
+#pragma unroll
+    for (int i = 0; i < N; ++i) v[i] = row && k + i < q.K ? src[i * q.cs] : 0.0f;
+  }
+  piece_lane_store<KC, N>(v, q.P, q.E, q.Rp, q.Kp, j, c, s, d, t);
 }
 
 }  // namespace falq

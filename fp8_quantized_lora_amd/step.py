@@ -12,7 +12,10 @@ With A trained and a shape whose GEMM tile grid allows it
 (melded_linear_xa_fused), the forward is melded_linear_fwd_xa, which also
 forms X^ A^T inside the forward FP8 product, and the backward
 melded_linear_bwd_xa, which forms G^ B inside the dX product: the skinny
-row-wise pass of melded_linear_bwd is not needed.
+row-wise pass of melded_linear_bwd is not needed.  With SGD on that route, A's
+pieces (the form in which the forward product takes A) are kept in a buffer:
+formed at init, then left by adapter_step_pieces each time SGD moves A, and
+the forward is melded_linear_fwd_xa_pieces.
 
 With fp8_a=True (the pages' training setup: A frozen and held in FP8), A is
 quantized once to A~ at init, the forward is melded_linear_fwd_frozen_a (Y and
@@ -36,7 +39,9 @@ from . import (fp8_quantize, fp8_quantize_workspace_bytes, fp8_dequantize, melde
                melded_linear_fwd_frozen_a_workspace_bytes, melded_linear_bwd_frozen_a,
                melded_linear_bwd_frozen_a_workspace_bytes, adapter_step, adapter_step_adamw,
                adamw_state, rowwise_proxy_update, rowwise_proxy_update_workspace_bytes,
-               rowwise_proxy_update_topk_rank, rowwise_proxy_update_topk_rank_workspace_bytes)
+               rowwise_proxy_update_topk_rank, rowwise_proxy_update_topk_rank_workspace_bytes,
+               adapter_pieces_bytes, adapter_pieces, adapter_step_pieces,
+               melded_linear_fwd_xa_pieces)
 
 
 class MeldedLinear:
@@ -107,6 +112,12 @@ class MeldedLinear:
             fw = melded_linear_fwd_xa_workspace_bytes(tokens, d_in, d_out, rank)
             bw = melded_linear_bwd_xa_workspace_bytes(tokens, d_in, d_out, rank)
             self.ws_fwd = torch.empty(max(1, fw), dtype=u8, device=dev)
+        # A's pieces for the fused forward, left by the SGD step that moves A
+        # (A changes nowhere else in the step); formed once in init_state
+        pb = adapter_pieces_bytes(rank, d_in) if self.use_xa and optimizer == "sgd" else 0
+        self.keep_pieces = pb > 0
+        if self.keep_pieces:
+            self.a_pieces = torch.empty(pb, dtype=u8, device=dev)
         else:
             bw = melded_linear_bwd_workspace_bytes(tokens, d_in, d_out, rank)
         self.ws_bwd = torch.empty(max(1, bw), dtype=u8, device=dev)
@@ -128,6 +139,13 @@ class MeldedLinear:
             fp8_dequantize(self.aq, self.s_a, self.A, stream=stream)
         else:
             self.A.copy_(A)
+        self.refresh_pieces(stream)
+
+    def refresh_pieces(self, stream=None):
+        """Form A's pieces from A (needed only after A was changed other than by
+        adapter_update)."""
+        if self.keep_pieces:
+            adapter_pieces(self.A, self.a_pieces, stream=stream)
 
     def forward(self, X: torch.Tensor, stream=None):
         fp8_quantize(X, self.xq, self.s_x, ws=self.ws_q, stream=stream)
@@ -140,6 +158,9 @@ class MeldedLinear:
         if self.fp8_a:
             melded_linear_fwd_frozen_a(self.xq, self.s_x, self.wq, self.s_w, self.aq, self.s_a,
                                        self.y, self.u, ws=self.ws_fwd, stream=stream)
+        elif self.keep_pieces:
+            melded_linear_fwd_xa_pieces(self.xq, self.s_x, self.wq, self.s_w, self.a_pieces,
+                                        self.r, self.y, self.xa, stream=stream)
         elif self.use_xa:
             melded_linear_fwd_xa(self.xq, self.s_x, self.wq, self.s_w, self.A, self.y, self.xa,
                                  ws=self.ws_fwd, stream=stream)
@@ -167,7 +188,10 @@ class MeldedLinear:
                               g_fmt=self.g_fmt)
 
     def adapter_update(self, lr: float, stream=None):
-        if self.optimizer == "sgd":
+        if self.keep_pieces:
+            adapter_step_pieces(self.A, self.B, self.dA, self.dB, lr, self.a_pieces,
+                                stream=stream)
+        elif self.optimizer == "sgd":
             adapter_step(self.A, self.B, self.dA, self.dB, lr, stream=stream)
         else:
             adapter_step_adamw(self.A, self.B, self.dA, self.dB, self.mA, self.vA, self.mB,

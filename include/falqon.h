@@ -277,6 +277,34 @@ falq_status melded_linear_bwd_xa(const uint8_t *gq, int g_fmt, const float *s_g,
                                  size_t ws_bytes, falq_stream stream);
 
 /*
+ * A's pieces kept by the optimizer.  The forward above carries A as
+ * block-scaled E4M3 pieces.  In the step, A changes only in the adapter
+ * step: the row-wise proxy update ([summary] key design) merges rows of
+ * B . A into the backbone and clears those rows of B, not of A.  So the
+ * step that moves A can leave the pieces that the next forward needs:
+ *   adapter_pieces          forms them from A;
+ *   adapter_step_pieces     adapter_step (SGD, the same update bit for bit) and
+ *                           the pieces of the new A, in one launch;
+ *   melded_linear_fwd_xa_pieces  melded_linear_fwd_xa from the pieces (the
+ *                           same Y and xa bit for bit as from A; no workspace).
+ * The pieces are an opaque buffer of adapter_pieces_bytes(r, d_in) bytes
+ * (0: not available: r = 0 or d_in not a multiple of 128), owned by the
+ * caller, 16-byte aligned, valid for the A they were formed from.
+ * melded_linear_fwd_xa_pieces needs melded_linear_xa_fused's tile condition
+ * on the forward product (r <= d_out / 64); FALQ_EINVAL otherwise.
+ */
+size_t adapter_pieces_bytes(int64_t r, int64_t d_in);
+falq_status adapter_pieces(const float *A, int64_t r, int64_t d_in, void *pieces,
+                           size_t pieces_bytes, falq_stream stream);
+falq_status adapter_step_pieces(float *A, float *B, const float *dA, const float *dB, int64_t r,
+                                int64_t d_in, int64_t d_out, float lr, void *pieces,
+                                size_t pieces_bytes, falq_stream stream);
+falq_status melded_linear_fwd_xa_pieces(const uint8_t *xq, const float *s_x, const uint8_t *wq,
+                                        const float *s_w, const void *pieces, size_t pieces_bytes,
+                                        int64_t T, int64_t d_in, int64_t d_out, int64_t r,
+                                        float *y, float *xa, falq_stream stream);
+
+/*
  * The pages' training setup: A frozen and held in FP8 ([rebuttal] thread 4,
  * Q1: A is frozen, and the x A^T factor of dL/dB, unlike dL/dA, can be
  * computed ahead; thread 2, W1/W9: Figure 2 joins X~ to W~ and to A~ by

@@ -200,3 +200,30 @@ def test_quantize_noalloc_argument_errors():
     assert lib.fp8_quantize_noalloc(None, 0, 16, 0, None, fake, fake, None, None, None) == EINVAL
     assert lib.fp8_quantize_noalloc(fake, 0, 16, 0, None, fake, None, None, None, None) == EINVAL
     assert fq.QUANTIZE_SCRATCH_BYTES >= fq.fp8_quantize_workspace_bytes(1 << 30)
+
+
+def test_adapter_pieces_calls_reject_bad_arguments():
+    """The calls around A's pieces validate before any HIP call."""
+    lib = fq.load()
+    assert fq.adapter_pieces_bytes(0, 128) == 0
+    assert fq.adapter_pieces_bytes(8, 100) == 0                   # d_in not a multiple of 128
+    nb = fq.adapter_pieces_bytes(13, 256)
+    # three planes of 16 padded rows x 256 codes, and 2 x 16 x 4 scale bytes
+    assert nb >= 3 * 16 * 256 + 2 * 16 * 4
+    assert lib.adapter_pieces(None, 13, 256, P, nb, None) == EINVAL            # A null
+    assert lib.adapter_pieces(P, 13, 256, P, nb - 1, None) == EINVAL           # short buffer
+    assert lib.adapter_pieces(P, 13, 200, P, nb, None) == EINVAL               # d_in
+    assert lib.adapter_pieces(P, 13, 256, MIS, nb, None) == EINVAL             # alignment
+    assert lib.adapter_step_pieces(P, P, None, P, 13, 256, 64, 1e-3, P, nb, None) == EINVAL
+    assert lib.adapter_step_pieces(P, None, P, P, 13, 256, 64, 1e-3, P, nb, None) == EINVAL
+    assert lib.adapter_step_pieces(P, P, P, P, 13, 256, -1, 1e-3, P, nb, None) == EINVAL
+    assert lib.adapter_step_pieces(P, P, P, P, 13, 256, 64, 1e-3, P, nb - 1, None) == EINVAL
+    # the forward from the pieces needs the unit columns: r <= d_out / 64 (4096 / 64 = 64 >= 13)
+    assert lib.melded_linear_fwd_xa_pieces(P, P, P, P, P, nb, 8, 256, 512, 13, P, P,
+                                           None) == EINVAL    # 2 column tiles carry no units
+    assert lib.melded_linear_fwd_xa_pieces(P, None, P, P, P, nb, 8, 256, 1024, 13, P, P,
+                                           None) == EINVAL    # s_x
+    assert lib.melded_linear_fwd_xa_pieces(P, P, P, P, P, nb - 1, 8, 256, 1024, 13, P, P,
+                                           None) == EINVAL    # short buffer
+    assert lib.melded_linear_fwd_xa_pieces(P, P, P, P, P, nb, 8, 256, 1024, 13, None, P,
+                                           None) == EINVAL    # y

@@ -182,3 +182,52 @@ def test_xa_pair_is_deterministic(gpu_lib, T, d_in, d_out, r):
     second = gpu_pair(gpu_lib, p)
     for a, b in zip(first, second):
         assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+def pieces_regions(r, d_in):
+    """Byte ranges of A's pieces buffer that hold data (pieces.hpp's layout:
+    three planes of r rounded up to 16 rows of d_in codes, then, 256-byte
+    aligned, d_in / 128 x rows x 4 scale bytes); the rest is padding."""
+    rp = (r + 15) // 16 * 16
+    planes = 3 * rp * d_in
+    e0 = (planes + 255) // 256 * 256
+    return [(0, planes), (e0, e0 + d_in // 128 * rp * 4)]
+
+
+@pytest.mark.parametrize("T,d_in,d_out,r", [(384, 2048, 1024, 13), (1024, 2048, 2048, 32),
+                                            (4096, 4096, 4096, 64), (64, 256, 301, 13)])
+def test_adapter_pieces_path(gpu_lib, T, d_in, d_out, r):
+    """A's pieces kept by the optimizer: adapter_step_pieces gives A and B bit
+    for bit as adapter_step and the same pieces as adapter_pieces on the new
+    A (every data byte written: the same result over two different
+    prefills), and melded_linear_fwd_xa_pieces gives Y and xa bit for bit as
+    melded_linear_fwd_xa from A.  The last shape has d_out * r not a multiple
+    of 4 (B's tail) and too few column tiles for the fused forward."""
+    fq = gpu_lib
+    announce(f"adapter pieces T={T} d_in={d_in} d_out={d_out} r={r}")
+    p = quantized_problem(211, T, d_in, d_out, r, b_std=0.5)
+    rng = np.random.default_rng(212)
+    gA = dev((rng.standard_normal((r, d_in)) * 1e-2).astype(np.float32))
+    gB = dev((rng.standard_normal((d_out, r)) * 1e-2).astype(np.float32))
+    lr = 0.37
+    nb = fq.adapter_pieces_bytes(r, d_in)
+    assert nb > 0
+    A1, B1, A2, B2 = dev(p["A"]), dev(p["B"]), dev(p["A"]), dev(p["B"])
+    p1 = torch.full((nb,), 0x5A, dtype=torch.uint8, device="cuda")
+    p2 = torch.full((nb,), 0xA5, dtype=torch.uint8, device="cuda")
+    fq.adapter_step(A1, B1, gA, gB, lr)
+    fq.adapter_pieces(A1, p1)
+    fq.adapter_step_pieces(A2, B2, gA, gB, lr, p2)
+    assert np.array_equal(host(A1).view(np.uint32), host(A2).view(np.uint32))
+    assert np.array_equal(host(B1).view(np.uint32), host(B2).view(np.uint32))
+    h1, h2 = host(p1), host(p2)
+    for lo, hi in pieces_regions(r, d_in):
+        assert np.array_equal(h1[lo:hi], h2[lo:hi]), (lo, hi)
+    if not gpu_lib.melded_linear_xa_fused(T, d_in, d_out, r):
+        return
+    xq, wq, sx, sw = dev(p["xq"]), dev(p["wq"]), scalar(p["s_x"]), scalar(p["s_w"])
+    y1, xa1, y2, xa2 = nan_f32((T, d_out)), nan_f32((T, r)), nan_f32((T, d_out)), nan_f32((T, r))
+    fq.melded_linear_fwd_xa(xq, sx, wq, sw, A2, y1, xa1)
+    fq.melded_linear_fwd_xa_pieces(xq, sx, wq, sw, p2, r, y2, xa2)
+    assert np.array_equal(host(y1).view(np.uint32), host(y2).view(np.uint32))
+    assert np.array_equal(host(xa1).view(np.uint32), host(xa2).view(np.uint32))
