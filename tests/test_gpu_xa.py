@@ -231,3 +231,56 @@ def test_adapter_pieces_path(gpu_lib, T, d_in, d_out, r):
     fq.melded_linear_fwd_xa_pieces(xq, sx, wq, sw, p2, r, y2, xa2)
     assert np.array_equal(host(y1).view(np.uint32), host(y2).view(np.uint32))
     assert np.array_equal(host(xa1).view(np.uint32), host(xa2).view(np.uint32))
+
+
+def test_adapter_pieces_encoding(gpu_lib):
+    """The pieces themselves (pieces.hpp's format), decoded on the host with
+    the oracle's E4M3 decoder: for every row j and 32-element block (position
+    d of a 128-wide K step belongs to block 2 bit4(d) + bit6(d)), the scale
+    byte is 127 - e with e the largest integer such that the block's largest
+    magnitude m satisfies m 2^e <= 448 (0 for an all-zero block), and each
+    element v is reproduced by (dec q0 + dec q1 + dec q2) 2^-e to within
+    2^-12 |v| + 2^-10 2^-e (three pieces of 3 significant bits, each rounding
+    what the earlier ones left; 2^-10 is half the E4M3 subnormal spacing).
+    Rows past r hold zero codes and scale byte 127."""
+    fq = gpu_lib
+    r, d_in = 13, 512
+    announce(f"adapter pieces encoding r={r} d_in={d_in}")
+    rng = np.random.default_rng(77)
+    A = (rng.standard_normal((r, d_in)) * 10.0 ** rng.uniform(-3, 3, (r, d_in))).astype(np.float32)
+    A[2] = 0.0                                    # a zero row
+    A[5, 128:160] = 0.0                           # (part of) zero blocks
+    A[7, 3] = 3.0e5                               # one large element in its block
+    nb = fq.adapter_pieces_bytes(r, d_in)
+    buf = torch.full((nb,), 0x77, dtype=torch.uint8, device="cuda")
+    fq.adapter_pieces(dev(A), buf)
+    h = host(buf)
+    rp = (r + 15) // 16 * 16
+    (p_lo, p_hi), (e_lo, e_hi) = pieces_regions(r, d_in)
+    planes = h[p_lo:p_hi].reshape(3, rp, d_in)
+    E = h[e_lo:e_hi].reshape(d_in // 128, rp, 4).astype(np.int64)
+    dec = [e4m3.decode(planes[p]).astype(np.float64) for p in range(3)]
+    k = np.arange(d_in)
+    d = k % 128
+    blk = 2 * ((d >> 4) & 1) + ((d >> 6) & 1)                 # block of each column
+    c = k // 128
+    a64 = A.astype(np.float64)
+    for j in range(rp):
+        e_col = 127 - E[c, j, blk]                            # the exponent each column sees
+        if j >= r:
+            assert not planes[:, j].any() and (E[:, j] == 127).all(), j
+            continue
+        for cc in range(d_in // 128):
+            for s in range(4):
+                cols = np.nonzero((c == cc) & (blk == s))[0]
+                assert cols.size == 32
+                m = np.abs(a64[j, cols]).max()
+                e = 0 if m == 0 else int(np.floor(np.log2(448.0 / m)))
+                if m > 0 and m * 2.0 ** (e + 1) <= 448.0:
+                    e += 1                                    # guard log2's rounding both ways
+                if m > 0 and m * 2.0 ** e > 448.0:
+                    e -= 1
+                assert 127 - E[cc, j, s] == e, (j, cc, s, m)
+        v_hat = (dec[0][j] + dec[1][j] + dec[2][j]) * np.exp2(-e_col.astype(np.float64))
+        bound = 2.0 ** -12 * np.abs(a64[j]) + 2.0 ** -10 * np.exp2(-e_col.astype(np.float64))
+        assert (np.abs(v_hat - a64[j]) <= bound).all(), (j, np.max(np.abs(v_hat - a64[j]) / bound))
