@@ -169,3 +169,24 @@ def test_saturating_merge_and_zero_rank():
     wq3, _, sel, rho = oracle.rowwise_proxy_update(wq, s_w, A[:0], B[:, :0], 0.0)
     assert sel.size == 4 and not rho.any()
     assert np.array_equal(wq3, np.where(wq == 0x80, 0, wq))
+
+
+def test_reading_of_a_spread_decides_whether_rows_merge():
+    """The workloads give A ~ N(0, 1/r) without saying whether 1/r is a
+    variance or a standard deviation.  Read as a variance (std 1/sqrt(r), the
+    reading the workloads use), the proxy update merges a good fraction of
+    the rows at the rank-sweep configuration's initial state (4096^2, r = 8,
+    B ~ N(0, 1e-3), tau = 0.5); read as a standard deviation (std 1/r), the
+    adapter delta stays below half an E4M3 step on every row and nothing
+    would ever merge."""
+    import workloads as wl
+    spec = wl.WORKLOADS[5].linears[0]
+    r = 8
+    d = wl.make_linear(5, 0, spec, rank=r)
+    wq, s_w, _, _ = oracle.fp8_quantize(d["W"])
+    fracs = []
+    for A in (d["A"], (d["A"] / np.float32(np.sqrt(r))).astype(np.float32)):
+        _, _, sel, _ = oracle.rowwise_proxy_update(wq, s_w, A, d["B"], spec.tau)
+        fracs.append(len(sel) / spec.d_out)
+    assert 0.3 < fracs[0] < 0.6, fracs
+    assert fracs[1] == 0.0, fracs
