@@ -26,7 +26,7 @@ __all__ = ["load", "FalqError", "fp8_quantize", "fp8_quantize_workspace_bytes",
            "melded_linear_fwd_frozen_a_workspace_bytes", "melded_linear_bwd_frozen_a",
            "melded_linear_bwd_frozen_a_workspace_bytes", "rowwise_proxy_update_workspace_bytes",
            "fp4_quantize", "melded_linear_fwd_fp4", "version", "LIB_PATH",
-           "fp8_quantize_noalloc", "QUANTIZE_SCRATCH_BYTES",
+           "fp8_quantize_noalloc", "QUANTIZE_SCRATCH_BYTES", "fp8_quantize_wait_ticks",
            "melded_linear_xa_fused", "melded_linear_fwd_xa", "melded_linear_bwd_xa",
            "adapter_pieces_bytes", "adapter_pieces", "adapter_step_pieces",
            "melded_linear_fwd_xa_pieces",
@@ -80,6 +80,7 @@ _SIGS = {
     "rowwise_proxy_update": (_i32, [_c_p, _c_p, _c_p, _c_p, _i64, _i64, _i64, _f32, _i64, _c_p,
                                     _c_p, _c_p, _c_p, _sz, _c_p]),
     "fp4_quantize": (_i32, [_c_p, _i32, _i64, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _sz, _c_p]),
+    "fp8_quantize_wait_ticks": (ctypes.c_uint64, [ctypes.c_uint64]),
     "fp8_quantize_noalloc": (_i32, [_c_p, _i32, _i64, _i32, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p]),
     "melded_linear_fwd_fp4": (_i32, [_c_p, _c_p, _c_p, _c_p, _i64, _i64, _i64, _c_p, _c_p]),
     "melded_linear_xa_fused": (_i32, [_i64, _i64, _i64, _i64]),
@@ -231,6 +232,15 @@ def fp8_quantize_noalloc(x: torch.Tensor, q: torch.Tensor, scale: torch.Tensor,
     _check(load().fp8_quantize_noalloc(_ptr(x), dt, x.numel(), _fmt(fmt), _ptr(scale_in),
                                        _ptr(q), _ptr(scale), _ptr(amax), _ptr(nonfinite),
                                        _stream(stream)), "fp8_quantize_noalloc")
+
+
+def fp8_quantize_wait_ticks(ticks: int) -> int:
+    """Set how long (100 MHz GPU counter ticks) the one-launch quantize waits
+    for the other workgroups' maxima before reading their ranges itself;
+    returns the previous setting."""
+    if ticks < 0:
+        raise FalqError("fp8_quantize_wait_ticks: ticks must be >= 0")
+    return int(load().fp8_quantize_wait_ticks(int(ticks)))
 
 
 def melded_linear_fwd(xq: torch.Tensor, s_x: torch.Tensor, wq: torch.Tensor, s_w: torch.Tensor,

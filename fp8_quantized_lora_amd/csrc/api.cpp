@@ -100,6 +100,8 @@ falq_status fp8_quantize_fmt(const void* x, int dtype, int64_t n, int fmt, const
                                           ws, reinterpret_cast<hipStream_t>(stream)));
 }
 
+uint64_t fp8_quantize_wait_ticks(uint64_t ticks) { return falq::quantize_wait_ticks(ticks); }
+
 falq_status fp8_quantize_noalloc(const void* x, int dtype, int64_t n, int fmt,
                                  const float* scale_in, uint8_t* q, float* scale, float* amax,
                                  int32_t* nonfinite, falq_stream stream) {

@@ -15,6 +15,9 @@ size_t quantize_ws_bytes();
 // per device with hipGetSymbolAddress) and its size; quantize_ws_bytes() fits
 constexpr size_t kQuantizeScratchBytes = (size_t)kQzMaxParts * 8;
 size_t quantize_scratch_bytes();
+// the one-launch route's wait for the exchange words, in ticks of the
+// 100 MHz real-time counter; sets it, returns the previous value
+uint64_t quantize_wait_ticks(uint64_t ticks);
 hipError_t quantize_scratch(void** out);
 // fmt 0: E4M3 (s = 448 / amax), 1: E5M2 (s = 57344 / amax), 2: FP4 E2M1
 // (s = 6 / amax; two codes per byte, the lower index in the low nibble; n even)

@@ -33,7 +33,9 @@
  * Conventions for every call:
  *   - Tensor arguments are DEVICE pointers into memory the caller owns,
  *     row-major and contiguous, 16-byte aligned.  The library allocates
- *     nothing and keeps no state between calls; scratch memory comes from the
+ *     nothing and keeps no state between calls that results depend on (the
+ *     one-launch quantize's exchange array is the only state it keeps, and
+ *     its contents never change a result); scratch memory comes from the
  *     caller (`ws`, at least the size the matching *_workspace_bytes returns,
  *     256-byte aligned).  Scalars that a step produces (scales, counts) stay
  *     on the device, so a step needs no host synchronisation.
@@ -110,11 +112,31 @@ const char *falq_version(void);
  *   ws         workspace of fp8_quantize_workspace_bytes(n) bytes
  * Errors: FALQ_EINVAL for n < 0, a NULL required pointer, misalignment, a
  * bad dtype or a short workspace.
+ * Launches: an x of at most 64 MiB (as many 16-byte vectors as the
+ * resident workgroups hold in registers) on a stream that is not being
+ * captured takes one launch that reads x once and exchanges the partial
+ * maxima through a small device array of the library's own (one per GPU,
+ * each word tagged with the call, so nothing needs clearing); larger x, or a
+ * capturing stream, takes two launches that read x twice.  Both give the
+ * same bits.  Calls that overlap on one GPU stay correct but may make the
+ * one-launch form wait for its deadline (fp8_quantize_wait_ticks) and then
+ * read other workgroups' ranges itself.
  */
 size_t fp8_quantize_workspace_bytes(int64_t n);
 falq_status fp8_quantize(const void *x, int dtype, int64_t n, const float *scale_in,
                          uint8_t *q, float *scale, float *amax, int32_t *nonfinite,
                          void *ws, size_t ws_bytes, falq_stream stream);
+
+/*
+ * fp8_quantize_wait_ticks — how long a workgroup of the one-launch quantize
+ * waits for the others' partial maxima before it reads their ranges itself,
+ * in ticks of the GPU's 100 MHz real-time counter (default 50000 = 500 us;
+ * 0 sends every workgroup but the first straight to that fallback, which is
+ * slow but gives the same bits — the setting that tests the fallback).
+ * Applies to later calls of every quantize entry point in this process; sets
+ * the value and returns the previous one.  Host only, no error.
+ */
+uint64_t fp8_quantize_wait_ticks(uint64_t ticks);
 
 /*
  * fp8_quantize_fmt — fp8_quantize with the code format as an argument:

@@ -202,6 +202,18 @@ def test_quantize_noalloc_argument_errors():
     assert fq.QUANTIZE_SCRATCH_BYTES >= fq.fp8_quantize_workspace_bytes(1 << 30)
 
 
+def test_quantize_wait_ticks_round_trip():
+    """The one-launch quantize's wait setting is host state: set, read back
+    through the previous value, restored (no GPU call)."""
+    lib = fq.load()
+    prev = lib.fp8_quantize_wait_ticks(1234)
+    assert prev == 50000                            # the default: 500 us of the 100 MHz counter
+    assert lib.fp8_quantize_wait_ticks(0) == 1234
+    assert fq.fp8_quantize_wait_ticks(prev) == 0
+    with pytest.raises(fq.FalqError):
+        fq.fp8_quantize_wait_ticks(-1)
+
+
 def test_adapter_pieces_calls_reject_bad_arguments():
     """The calls around A's pieces validate before any HIP call."""
     lib = fq.load()

@@ -115,3 +115,80 @@ def test_quantize_double_rounding_golden(gpu_lib):
         k = s_all == s
         q, s_out, a_out, _ = run_gpu(gpu_lib, np.concatenate([[amax], x[k]]).astype(np.float32))
         assert s_out == s and a_out == amax and np.array_equal(q[1:], want[k])
+
+
+def _quantize_dev(fq, x, fmt="e4m3", stream=None):
+    q = torch.empty(x.shape, dtype=torch.uint8, device="cuda")
+    s, amax = scalar(0.0), scalar(0.0)
+    bad = torch.zeros(1, dtype=torch.int32, device="cuda")
+    fq.fp8_quantize(x, q, s, amax=amax, nonfinite=bad, fmt=fmt, stream=stream)
+    return q, s, amax, bad
+
+
+def test_quantize_across_the_one_launch_limit(gpu_lib):
+    """x of up to 64 MiB takes one launch that reads it once, anything larger
+    the two launches: calls alternating between the two routes and between
+    sizes (so the exchange words of the one-launch form hold an earlier
+    call's values) all match the oracle bit for bit."""
+    rng = np.random.default_rng(31)
+    n_one = 4096 * 4096                 # 1024 workgroups: the largest one-launch fp32 x
+    for n, seed in [(n_one, 1), (n_one + 4, 2), (3 * 4096 + 5, 3), (n_one, 4), (n_one - 4096, 5)]:
+        announce(f"quantize f32 n={n} seed {seed}")
+        x = (rng.standard_normal(n) * (seed + 1)).astype(np.float32)
+        x[rng.integers(0, n, 3)] = [np.inf, np.nan, -np.inf]
+        check(gpu_lib, x)
+
+
+def test_quantize_fallback_reads_missing_ranges(gpu_lib):
+    """With no wait for the other workgroups' maxima, every workgroup of the
+    one-launch form reads the ranges whose maxima it has not seen yet: the
+    slow path that keeps the result exact when workgroups are not resident
+    together.  f32 and bf16, E4M3 and E5M2, with non-finite inputs."""
+    rng = np.random.default_rng(32)
+    prev = gpu_lib.fp8_quantize_wait_ticks(0)
+    try:
+        for shape, fmt in [((1024, 1024), "e4m3"), ((640, 2000), "e5m2")]:
+            announce(f"quantize fallback f32 {shape} {fmt}")
+            x = rng.standard_normal(shape).astype(np.float32)
+            x[3, 7], x[-1, -1] = np.nan, -np.inf
+            q, s, amax, bad = _quantize_dev(gpu_lib, dev(x), fmt=fmt)
+            rq, rs, ramax, rbad = oracle.fp8_quantize(x, fmt=fmt)
+            assert np.float32(host(s)[0]) == np.float32(rs)
+            assert np.float32(host(amax)[0]) == np.float32(ramax) and int(host(bad)[0]) == rbad
+            assert np.array_equal(host(q), rq)
+        announce("quantize fallback bf16 (2048, 1536)")
+        xb = wl.fp32_to_bf16_bits(rng.standard_normal((2048, 1536)).astype(np.float32))
+        check(gpu_lib, xb, dtype="bf16")
+    finally:
+        gpu_lib.fp8_quantize_wait_ticks(prev)
+
+
+def test_quantize_in_a_graph_matches_eager(gpu_lib):
+    """Under graph capture the quantize takes its two-launch form (a replay
+    would repeat the one-launch form's call tag): replays of the captured
+    call, with eager calls and synchronisations between them, give the
+    eager call's bits."""
+    announce("quantize 4096 x 4096 f32: graph replays vs eager")
+    rng = np.random.default_rng(33)
+    x = dev((rng.standard_normal((4096, 4096)) * 2).astype(np.float32))
+    eq, es, ea, eb = _quantize_dev(gpu_lib, x)
+    q = torch.empty(x.shape, dtype=torch.uint8, device="cuda")
+    s, amax = scalar(0.0), scalar(0.0)
+    bad = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ws = torch.empty(gpu_lib.fp8_quantize_workspace_bytes(x.numel()), dtype=torch.uint8,
+                     device="cuda")
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(g, stream=side):
+            gpu_lib.fp8_quantize(x, q, s, amax=amax, nonfinite=bad, ws=ws, stream=side)
+    torch.cuda.current_stream().wait_stream(side)
+    for _ in range(3):
+        q.fill_(0)
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(q, eq) and torch.equal(s, es) and torch.equal(amax, ea)
+        assert torch.equal(bad, eb)
+        _quantize_dev(gpu_lib, x)               # eager one-launch call between replays
+        torch.cuda.synchronize()
