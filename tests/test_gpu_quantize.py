@@ -139,6 +139,19 @@ def test_quantize_across_the_one_launch_limit(gpu_lib):
         check(gpu_lib, x)
 
 
+def test_quantize_bf16_across_the_one_launch_limit(gpu_lib):
+    """bf16 x holds 8 elements per 16-byte vector: 4096 x 8192 (64 MiB, 1024
+    workgroups) is the largest one-launch bf16 tensor, 8 more elements take
+    the two launches; both match the oracle bit for bit."""
+    rng = np.random.default_rng(34)
+    n_one = 4096 * 8192
+    for n in (n_one, n_one + 8):
+        announce(f"quantize bf16 n={n}")
+        x = rng.standard_normal(n).astype(np.float32)
+        x[[5, n // 2]] = [np.nan, -np.inf]
+        check(gpu_lib, wl.fp32_to_bf16_bits(x), dtype="bf16")
+
+
 def test_quantize_fallback_reads_missing_ranges(gpu_lib):
     """With no wait for the other workgroups' maxima, every workgroup of the
     one-launch form reads the ranges whose maxima it has not seen yet: the
