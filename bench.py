@@ -182,7 +182,8 @@ def run(args):
     d0 = wl.make_linear(2, 0, spec, step=0)
     frozen = args.adapter == "frozen-fp8"
     m = fq.MeldedLinear(d_out, d_in, r, T, optimizer=args.optimizer, fp8_a=frozen,
-                        g_fmt=args.grad_format, topk_rank=args.topk_rank)
+                        g_fmt=args.grad_format, topk_rank=args.topk_rank,
+                        merge_every=max(1, args.merge_every))
     t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
     m.init_state(t(d0["W"]), t(d0["A"]), t(d0["B"]))
     batches = []

@@ -28,6 +28,7 @@ __all__ = ["load", "FalqError", "fp8_quantize", "fp8_quantize_workspace_bytes",
            "fp4_quantize", "melded_linear_fwd_fp4", "version", "LIB_PATH",
            "fp8_quantize_noalloc", "QUANTIZE_SCRATCH_BYTES", "fp8_quantize_wait_ticks",
            "melded_linear_xa_fused", "melded_linear_fwd_xa", "melded_linear_bwd_xa",
+           "melded_linear_bwd_xa_t", "rowwise_proxy_update_t", "fp8_transpose",
            "adapter_pieces_bytes", "adapter_pieces", "adapter_step_pieces",
            "melded_linear_fwd_xa_pieces",
            "melded_linear_fwd_xa_workspace_bytes", "melded_linear_bwd_xa_workspace_bytes",
@@ -60,6 +61,7 @@ _SIGS = {
     "adapter_step_adamw": (_i32, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _i64, _i64,
                                   _i64, _f32, _f32, _f32, _f32, _f32, _c_p, _c_p]),
     "fp8_dequantize": (_i32, [_c_p, _c_p, _i64, _c_p, _c_p]),
+    "fp8_transpose": (_i32, [_c_p, _i64, _i64, _c_p, _c_p]),
     "fp8_quantize_fmt": (_i32, [_c_p, _i32, _i64, _i32, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _sz,
                                 _c_p]),
     "melded_linear_bwd_fmt": (_i32, [_c_p, _i32, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _i64,
@@ -79,6 +81,8 @@ _SIGS = {
                                               _c_p]),
     "rowwise_proxy_update": (_i32, [_c_p, _c_p, _c_p, _c_p, _i64, _i64, _i64, _f32, _i64, _c_p,
                                     _c_p, _c_p, _c_p, _sz, _c_p]),
+    "rowwise_proxy_update_t": (_i32, [_c_p, _c_p, _c_p, _c_p, _c_p, _i64, _i64, _i64, _f32, _i64,
+                                      _c_p, _c_p, _c_p, _c_p, _sz, _c_p]),
     "fp4_quantize": (_i32, [_c_p, _i32, _i64, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _sz, _c_p]),
     "fp8_quantize_wait_ticks": (ctypes.c_uint64, [ctypes.c_uint64]),
     "fp8_quantize_noalloc": (_i32, [_c_p, _i32, _i64, _i32, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p]),
@@ -96,6 +100,8 @@ _SIGS = {
     "melded_linear_bwd_xa_workspace_bytes": (_sz, [_i64, _i64, _i64, _i64]),
     "melded_linear_bwd_xa": (_i32, [_c_p, _i32, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p,
                                     _i64, _i64, _i64, _i64, _c_p, _c_p, _c_p, _c_p, _sz, _c_p]),
+    "melded_linear_bwd_xa_t": (_i32, [_c_p, _i32, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p,
+                                      _i64, _i64, _i64, _i64, _c_p, _c_p, _c_p, _c_p, _sz, _c_p]),
     "lora_separate_fp8_saved_bytes": (_sz, [_i64, _i64, _i64, _i64]),
     "lora_separate_fp8_workspace_bytes": (_sz, [_i64, _i64, _i64, _i64]),
     "lora_separate_fp8_fwd": (_i32, [_c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _i64, _i64, _i64, _i64,
@@ -428,6 +434,26 @@ def rowwise_proxy_update_workspace_bytes(d_in: int, d_out: int, r: int) -> int:
     return int(load().rowwise_proxy_update_workspace_bytes(d_in, d_out, r))
 
 
+def rowwise_proxy_update_t(wq, wqT, s_w, A, B, tau: float, k_max: int, sel_idx, n_sel, rho=None,
+                           ws=None, stream=None) -> None:
+    """rowwise_proxy_update that also writes wqT = the updated wq, transposed."""
+    d_out, d_in = wq.shape
+    r = A.shape[0]
+    _req(wqT, torch.uint8, (d_in, d_out), "wqT")
+    _req(A, torch.float32, (r, d_in), "A")
+    _req(B, torch.float32, (d_out, r), "B")
+    _req(sel_idx, torch.int32, (d_out,), "sel_idx")
+    if rho is not None:
+        _req(rho, torch.float32, (d_out,), "rho")
+    wsb = rowwise_proxy_update_workspace_bytes(d_in, d_out, r)
+    if ws is None:
+        ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=wq.device)
+    _check(load().rowwise_proxy_update_t(_ptr(wq), _ptr(wqT), _ptr(s_w), _ptr(A), _ptr(B), d_in,
+                                         d_out, r, tau, k_max, _ptr(sel_idx), _ptr(n_sel),
+                                         _ptr(rho), _ptr(ws), ws.numel(), _stream(stream)),
+           "rowwise_proxy_update_t")
+
+
 def rowwise_proxy_update(wq, s_w, A, B, tau: float, k_max: int, sel_idx, n_sel, rho=None, ws=None,
                          stream=None) -> None:
     d_out, d_in = wq.shape
@@ -540,12 +566,13 @@ def melded_linear_fwd_xa_pieces(xq, s_x, wq, s_w, pieces, r: int, y, xa, stream=
 
 
 def melded_linear_bwd_xa(gq, s_g, xq, s_x, wq, s_w, A, B, xa, dx, dA, dB, ws=None, stream=None,
-                         g_fmt: str = "e4m3") -> None:
-    """dx, dA = (G^ B)^T X^ and dB = G^^T xa, with xa from melded_linear_fwd_xa."""
+                         g_fmt: str = "e4m3", wq_t: bool = False) -> None:
+    """dx, dA = (G^ B)^T X^ and dB = G^^T xa, with xa from melded_linear_fwd_xa.
+    wq_t: wq is the backbone's transpose [d_in x d_out] (melded_linear_bwd_xa_t)."""
     T, d_out = gq.shape
     d_in = xq.shape[1]
     r = A.shape[0]
-    _req(wq, torch.uint8, (d_out, d_in), "wq")
+    _req(wq, torch.uint8, (d_in, d_out) if wq_t else (d_out, d_in), "wqT" if wq_t else "wq")
     _req(A, torch.float32, (r, d_in), "A")
     _req(B, torch.float32, (d_out, r), "B")
     _req(xa, torch.float32, (T, r), "xa")
@@ -555,10 +582,26 @@ def melded_linear_bwd_xa(gq, s_g, xq, s_x, wq, s_w, A, B, xa, dx, dA, dB, ws=Non
     if dA is not None:
         _req(dA, torch.float32, (r, d_in), "dA")
     ws = _buf(ws, melded_linear_bwd_xa_workspace_bytes(T, d_in, d_out, r), gq.device, "ws")
-    _check(load().melded_linear_bwd_xa(_ptr(gq), _fmt(g_fmt), _ptr(s_g), _ptr(xq), _ptr(s_x),
-                                       _ptr(wq), _ptr(s_w), _ptr(A), _ptr(B), _ptr(xa), T, d_in,
-                                       d_out, r, _ptr(dx), _ptr(dA), _ptr(dB), _ptr(ws),
-                                       ws.numel(), _stream(stream)), "melded_linear_bwd_xa")
+    name = "melded_linear_bwd_xa_t" if wq_t else "melded_linear_bwd_xa"
+    _check(getattr(load(), name)(_ptr(gq), _fmt(g_fmt), _ptr(s_g), _ptr(xq), _ptr(s_x),
+                                 _ptr(wq), _ptr(s_w), _ptr(A), _ptr(B), _ptr(xa), T, d_in,
+                                 d_out, r, _ptr(dx), _ptr(dA), _ptr(dB), _ptr(ws),
+                                 ws.numel(), _stream(stream)), name)
+
+
+def melded_linear_bwd_xa_t(gq, s_g, xq, s_x, wqT, s_w, A, B, xa, dx, dA, dB, ws=None,
+                           stream=None, g_fmt: str = "e4m3") -> None:
+    """melded_linear_bwd_xa with the backbone handed in transposed, wqT [d_in x d_out]."""
+    melded_linear_bwd_xa(gq, s_g, xq, s_x, wqT, s_w, A, B, xa, dx, dA, dB, ws=ws, stream=stream,
+                         g_fmt=g_fmt, wq_t=True)
+
+
+def fp8_transpose(q: torch.Tensor, qT: torch.Tensor, stream=None) -> None:
+    """qT = q^T for a byte matrix (rows and columns multiples of 16)."""
+    rows, cols = q.shape
+    _req(q, torch.uint8, (rows, cols), "q")
+    _req(qT, torch.uint8, (cols, rows), "qT")
+    _check(load().fp8_transpose(_ptr(q), rows, cols, _ptr(qT), _stream(stream)), "fp8_transpose")
 
 
 # ---------------------------------------------------------------------------

@@ -1131,7 +1131,8 @@ size_t bwd_xa_ws_bytes(int64_t T, int64_t d_in, int64_t d_out, int64_t r) {
 hipError_t launch_bwd_xa(const uint8_t* gq, int g_fmt, const float* s_g, const uint8_t* xq,
                          const float* s_x, const uint8_t* wq, uint8_t* wt, const float* s_w,
                          const float* B, const float* xa, int64_t T, int64_t d_in, int64_t d_out,
-                         int64_t r, float* dx, float* dA, float* dB, void* ws, hipStream_t s) {
+                         int64_t r, float* dx, float* dA, float* dB, void* ws, hipStream_t s,
+                         const uint8_t* wt_given) {
   uint8_t* base = reinterpret_cast<uint8_t*>(ws);
   float* v = reinterpret_cast<float*>(base);
   uint8_t* vreg = base + align_up((size_t)r * (size_t)T * 4, 256);
@@ -1155,8 +1156,10 @@ hipError_t launch_bwd_xa(const uint8_t* gq, int g_fmt, const float* s_g, const u
     ju = PieceJob{xa, 1, r, r, T, up, ue, tRp, tTp};
   }
   const int nb = (int)prep_blocks(jb), nu = (int)prep_blocks(ju);
-  const int tr_tx = tr ? ceil_div(d_in, 128) : 1;
-  const int n_tr = tr ? tr_tx * ceil_div(d_out, 128) : 0;
+  const bool do_tr = tr && wt_given == nullptr;
+  const uint8_t* wtb = wt_given ? wt_given : wt;        // the dX product's W~^T
+  const int tr_tx = do_tr ? ceil_div(d_in, 128) : 1;
+  const int n_tr = do_tr ? tr_tx * ceil_div(d_out, 128) : 0;
   const int grid = ceil_div(n_tr, kPrepThreads / 256) + nb + nu;
   if (grid > 0) {
     xa_prep_kernel<<<grid, kPrepThreads, 0, s>>>(wq, d_out, d_in, wt, n_tr, tr_tx, jb, nb, ju, nu);
@@ -1166,11 +1169,11 @@ hipError_t launch_bwd_xa(const uint8_t* gq, int g_fmt, const float* s_g, const u
   hipError_t e = hipSuccess;
   if (fuse) {
     // with the token-contracting kernel, V goes straight into its pieces
-    e = launch_gemm_fp8_nt_pieces(gq, d_out, wt, d_out, dx, d_in, T, d_in, d_out, s_g, s_w,
+    e = launch_gemm_fp8_nt_pieces(gq, d_out, wtb, d_out, dx, d_in, T, d_in, d_out, s_g, s_w,
                                   vreg + pp.p, vreg + pp.e, pp.Rp, r, v, r, tok ? vp : nullptr,
                                   tok ? ve : nullptr, tRp, tTp, s, g_fmt);
   } else {
-    if (tr) e = launch_gemm_fp8_nt(gq, d_out, wt, d_out, dx, d_in, T, d_in, d_out, s_g, s_w, s,
+    if (tr) e = launch_gemm_fp8_nt(gq, d_out, wtb, d_out, dx, d_in, T, d_in, d_out, s_g, s_w, s,
                                    g_fmt);
     if (e == hipSuccess && want_v)
       e = launch_one_skinny(gq, d_out, g_fmt, s_g, B, true, T, d_out, r, v, vreg, s);

@@ -365,6 +365,26 @@ falq_status rowwise_proxy_update(uint8_t* wq, const float* s_w, const float* A, 
                                               n_sel, rho, ws, reinterpret_cast<hipStream_t>(stream)));
 }
 
+falq_status rowwise_proxy_update_t(uint8_t* wq, uint8_t* wqT, const float* s_w, const float* A,
+                                   float* B, int64_t d_in, int64_t d_out, int64_t r, float tau,
+                                   int64_t k_max, int32_t* sel_idx, int32_t* n_sel, float* rho,
+                                   void* ws, size_t ws_bytes, falq_stream stream) {
+  // the transpose takes whole 16 x 16 byte blocks: d_out a multiple of 16 too
+  if (!dims_ok(d_in) || !dims_ok(d_out) || r < 0 || r > ((int64_t)1 << 20) || k_max < 0)
+    return FALQ_EINVAL;
+  if (!scalar(s_w) || !scalar(n_sel)) return FALQ_EINVAL;
+  if (d_out * d_in > 0 && (!need(wq) || !need(wqT) || wq == wqT)) return FALQ_EINVAL;
+  if (r * d_in > 0 && !need(A)) return FALQ_EINVAL;
+  if (r * d_out > 0 && !need(B)) return FALQ_EINVAL;
+  if (d_out > 0 && !need(sel_idx)) return FALQ_EINVAL;
+  if (!opt(rho)) return FALQ_EINVAL;
+  if (!ws_ok(ws, ws_bytes, rowwise_proxy_update_workspace_bytes(d_in, d_out, r)))
+    return FALQ_EINVAL;
+  return hip_status(falq::launch_proxy_update_ranks(
+      wq, s_w, A, B, d_in, d_out, r, r, nullptr, tau, k_max, sel_idx, n_sel, rho, ws,
+      reinterpret_cast<hipStream_t>(stream), d_out * d_in > 0 ? wqT : nullptr));
+}
+
 size_t rowwise_proxy_update_topk_rank_workspace_bytes(int64_t d_in, int64_t d_out, int64_t r,
                                                       int64_t k_rank) {
   if (d_in < 0 || d_out < 0 || r < 0 || k_rank < 0 || k_rank > r) return 0;
@@ -595,18 +615,23 @@ size_t melded_linear_bwd_xa_workspace_bytes(int64_t T, int64_t d_in, int64_t d_o
                    : falq::bwd_xa_ws_bytes(T, d_in, d_out, r));
 }
 
-falq_status melded_linear_bwd_xa(const uint8_t* gq, int g_fmt, const float* s_g,
-                                 const uint8_t* xq, const float* s_x, const uint8_t* wq,
-                                 const float* s_w, const float* A, const float* B,
-                                 const float* xa, int64_t T, int64_t d_in, int64_t d_out,
-                                 int64_t r, float* dx, float* dA, float* dB, void* ws,
-                                 size_t ws_bytes, falq_stream stream) {
+}  // extern "C"
+
+namespace {
+
+// melded_linear_bwd_xa (wqT == nullptr: W~^T formed from wq in the workspace)
+// and melded_linear_bwd_xa_t (wq == nullptr: the caller's W~^T)
+falq_status bwd_xa_impl(const uint8_t* gq, int g_fmt, const float* s_g, const uint8_t* xq,
+                        const float* s_x, const uint8_t* wq, const uint8_t* wqT, const float* s_w,
+                        const float* A, const float* B, const float* xa, int64_t T, int64_t d_in,
+                        int64_t d_out, int64_t r, float* dx, float* dA, float* dB, void* ws,
+                        size_t ws_bytes, falq_stream stream) {
   if (!fmt_ok(g_fmt)) return FALQ_EINVAL;
   if (!gemm_dims_ok(T, d_in, d_out) || r < 0 || r > ((int64_t)1 << 20)) return FALQ_EINVAL;
   if (!scalar(s_g) || !scalar(s_x) || !scalar(s_w)) return FALQ_EINVAL;
   if (T * d_out > 0 && !need(gq)) return FALQ_EINVAL;
   if (T * d_in > 0 && !need(xq)) return FALQ_EINVAL;
-  if (d_out * d_in > 0 && dx && !need(wq)) return FALQ_EINVAL;
+  if (d_out * d_in > 0 && dx && !need(wqT ? wqT : wq)) return FALQ_EINVAL;
   if (!opt(dx) || !opt(dA)) return FALQ_EINVAL;
   if (r * d_in > 0 && !need(A)) return FALQ_EINVAL;
   if (r * d_out > 0 && (!need(B) || !need(dB))) return FALQ_EINVAL;
@@ -620,10 +645,12 @@ falq_status melded_linear_bwd_xa(const uint8_t* gq, int g_fmt, const float* s_g,
   const bool wide = grads && falq::adapter_wide_route(T, d_in, d_out, r);
   const bool gemm_dx = dx && T * d_in > 0 && d_out > 0;
   hipError_t e = hipSuccess;
-  if (gemm_dx && (!grads || wide)) e = falq::launch_transpose_u8(wq, d_out, d_in, base, s);
+  // the dX product's W~^T: the caller's, or formed in the workspace
+  const uint8_t* wt = wqT ? wqT : base;
+  if (gemm_dx && (!grads || wide) && !wqT) e = falq::launch_transpose_u8(wq, d_out, d_in, base, s);
   if (e != hipSuccess) return FALQ_EHIP;
   if (!grads) {
-    if (gemm_dx) e = falq::launch_gemm_fp8_nt(gq, d_out, base, d_out, dx, d_in, T, d_in, d_out,
+    if (gemm_dx) e = falq::launch_gemm_fp8_nt(gq, d_out, wt, d_out, dx, d_in, T, d_in, d_out,
                                               s_g, s_w, s, g_fmt);
     else if (dx && T * d_in > 0) e = falq::launch_fill_f32(dx, T * d_in, 0.0f, s);
     if (e == hipSuccess && r > 0) {
@@ -633,7 +660,7 @@ falq_status melded_linear_bwd_xa(const uint8_t* gq, int g_fmt, const float* s_g,
     return hip_status(e);
   }
   if (wide) {
-    if (gemm_dx) e = falq::launch_gemm_fp8_nt(gq, d_out, base, d_out, dx, d_in, T, d_in, d_out,
+    if (gemm_dx) e = falq::launch_gemm_fp8_nt(gq, d_out, wt, d_out, dx, d_in, T, d_in, d_out,
                                               s_g, s_w, s, g_fmt);
     if (e == hipSuccess)
       e = falq::launch_adapter_grads_wide(gq, g_fmt, s_g, xq, s_x, A, B, T, d_in, d_out, r, dA,
@@ -643,7 +670,41 @@ falq_status melded_linear_bwd_xa(const uint8_t* gq, int g_fmt, const float* s_g,
   // the transpose of W~ runs inside launch_bwd_xa's preparation launch
   return hip_status(falq::launch_bwd_xa(gq, g_fmt, s_g, xq, s_x, wq, base, s_w, B, xa, T, d_in,
                                         d_out, r, gemm_dx ? dx : nullptr, dA, dB,
-                                        base + wt_bytes, s));
+                                        base + wt_bytes, s, wqT));
+}
+
+}  // namespace
+
+extern "C" {
+
+falq_status melded_linear_bwd_xa(const uint8_t* gq, int g_fmt, const float* s_g,
+                                 const uint8_t* xq, const float* s_x, const uint8_t* wq,
+                                 const float* s_w, const float* A, const float* B,
+                                 const float* xa, int64_t T, int64_t d_in, int64_t d_out,
+                                 int64_t r, float* dx, float* dA, float* dB, void* ws,
+                                 size_t ws_bytes, falq_stream stream) {
+  return bwd_xa_impl(gq, g_fmt, s_g, xq, s_x, wq, nullptr, s_w, A, B, xa, T, d_in, d_out, r, dx,
+                     dA, dB, ws, ws_bytes, stream);
+}
+
+falq_status melded_linear_bwd_xa_t(const uint8_t* gq, int g_fmt, const float* s_g,
+                                   const uint8_t* xq, const float* s_x, const uint8_t* wqT,
+                                   const float* s_w, const float* A, const float* B,
+                                   const float* xa, int64_t T, int64_t d_in, int64_t d_out,
+                                   int64_t r, float* dx, float* dA, float* dB, void* ws,
+                                   size_t ws_bytes, falq_stream stream) {
+  if (d_out * d_in > 0 && dx && wqT == nullptr) return FALQ_EINVAL;
+  return bwd_xa_impl(gq, g_fmt, s_g, xq, s_x, nullptr, wqT, s_w, A, B, xa, T, d_in, d_out, r, dx,
+                     dA, dB, ws, ws_bytes, stream);
+}
+
+falq_status fp8_transpose(const uint8_t* q, int64_t rows, int64_t cols, uint8_t* qT,
+                          falq_stream stream) {
+  if (!dims_ok(rows) || !dims_ok(cols)) return FALQ_EINVAL;
+  if (rows * cols == 0) return FALQ_OK;
+  if (!need(q) || !need(qT) || q == qT) return FALQ_EINVAL;
+  return hip_status(
+      falq::launch_transpose_u8(q, rows, cols, qT, reinterpret_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

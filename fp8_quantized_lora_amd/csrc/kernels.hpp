@@ -134,11 +134,13 @@ hipError_t launch_token_grads(const uint8_t* gq, int g_fmt, const float* s_g, co
 void token_grads_pieces(void* ws, int64_t T, int64_t d_in, int64_t d_out, int64_t r, int which,
                         uint8_t** P, uint8_t** E, int64_t* Rp, int64_t* Tp);
 size_t bwd_xa_ws_bytes(int64_t T, int64_t d_in, int64_t d_out, int64_t r);
-// wq is transposed into wt (d_in x d_out bytes) when dx is wanted
+// wq is transposed into wt (d_in x d_out bytes) when dx is wanted, unless
+// the caller hands the transpose in as wt_given (then wq and wt are unused)
 hipError_t launch_bwd_xa(const uint8_t* gq, int g_fmt, const float* s_g, const uint8_t* xq,
                          const float* s_x, const uint8_t* wq, uint8_t* wt, const float* s_w,
                          const float* B, const float* xa, int64_t T, int64_t d_in, int64_t d_out,
-                         int64_t r, float* dx, float* dA, float* dB, void* ws, hipStream_t s);
+                         int64_t r, float* dx, float* dA, float* dB, void* ws, hipStream_t s,
+                         const uint8_t* wt_given = nullptr);
 // large ranks: through the full weight gradient M = G^^T X^ (adapter_grad_wide.hip)
 bool adapter_wide_route(int64_t T, int64_t d_in, int64_t d_out, int64_t r);
 size_t adapter_wide_ws_bytes(int64_t T, int64_t d_in, int64_t d_out, int64_t r);
@@ -209,12 +211,14 @@ hipError_t launch_proxy_update(uint8_t* wq, const float* s_w, const float* A, fl
                                void* ws, hipStream_t s);
 
 // the same with the chain over ranks kidx[0..r) (ascending) of an adapter whose
-// B rows hold rs values (A rows indexed by kidx too)
+// B rows hold rs values (A rows indexed by kidx too); with wt != nullptr the
+// update also writes wt [d_in x d_out] = the updated wq^T (d_in, d_out
+// multiples of 16)
 hipError_t launch_proxy_update_ranks(uint8_t* wq, const float* s_w, const float* A, float* B,
                                      int64_t d_in, int64_t d_out, int64_t r, int64_t rs,
                                      const int32_t* kidx, float tau, int64_t k_max,
                                      int32_t* sel_idx, int32_t* n_sel, float* rho, void* ws,
-                                     hipStream_t s);
+                                     hipStream_t s, uint8_t* wt = nullptr);
 // proxy update over the top-k rank components (k <= r <= 65536): K [k] int32 output
 size_t proxy_topk_rank_ws_bytes(int64_t d_in, int64_t d_out, int64_t r, int64_t k);
 hipError_t launch_proxy_update_topk_rank(uint8_t* wq, const float* s_w, const float* A, float* B,

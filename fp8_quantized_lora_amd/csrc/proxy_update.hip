@@ -45,6 +45,7 @@
 // are loaded a stage ahead into registers.
 #include "common.hpp"
 #include "kernels.hpp"
+#include "transpose_u8.hpp"
 
 #include <algorithm>
 
@@ -479,6 +480,83 @@ __global__ __launch_bounds__(kSelThreads) void proxy_select_apply(
   for (int k = lane; k < r; k += 64) B[row * (IDX ? rs : r) + (IDX ? kidx[k] : k)] = 0.0f;
 }
 
+// proxy_select_apply that also leaves the transpose of the updated
+// backbone, wt [d_in x d_out] = wq^T, for the next step's dX product.
+// Workgroup 0 computes rho and the list as proxy_select does; every other
+// workgroup takes four 128 x 128 tiles of the backbone, 256 threads each.
+// A tile first decides its 128 rows from their column-block maxima (the
+// same operations as select_rows, so the same bits), then each thread reads
+// 16 rows x 4 bytes of the new backbone (the staged codes of a merged row,
+// the backbone's own otherwise), writes the merged rows' bytes back, and
+// stores the block's transpose (4 columns x 16 bytes) into wt; the tiles of
+// the first tile column zero the merged rows of B.  Every byte of wq and wt
+// is read or written by exactly one thread.  d_out and d_in are multiples
+// of 16.
+template <bool IDX>
+__global__ __launch_bounds__(kSelThreads) void proxy_select_apply_t(
+    const uint32_t* __restrict__ tmax_part, const uint32_t* __restrict__ cmax_part, int ncb,
+    float* __restrict__ rho, int d_out, float tau, int32_t* __restrict__ sel,
+    int32_t* __restrict__ n_sel, uint8_t* __restrict__ wq, const uint8_t* __restrict__ staged,
+    float* __restrict__ B, int d_in, int r, int rs, const int32_t* __restrict__ kidx,
+    uint8_t* __restrict__ wt, int n_tiles, int tiles_x) {
+  if (blockIdx.x == 0) {
+    select_rows(tmax_part, cmax_part, ncb, rho, d_out, tau, 0, sel, n_sel);
+    return;
+  }
+  __shared__ uint8_t merge[4][128];
+  const int q = threadIdx.x >> 8, t = threadIdx.x & 255;
+  const int tile = (blockIdx.x - 1) * 4 + q;
+  const bool live = tile < n_tiles;
+  const int bx = live ? tile % tiles_x : 0, by = live ? tile / tiles_x : 0;
+  if (live && t < 128) {
+    const int64_t row = (int64_t)by * 128 + t;
+    uint8_t m = 0;
+    if (row < d_out) {
+      uint32_t tb = 0, cb = 0;
+      for (int b0 = 0; b0 < ncb; b0 += 8) {
+        uint32_t x[8], y[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int b = min(b0 + u, ncb - 1);              // clamped repeats fold harmlessly
+          x[u] = tmax_part[(int64_t)b * d_out + row];
+          y[u] = cmax_part[(int64_t)b * d_out + row];
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          tb = x[u] > tb ? x[u] : tb;
+          cb = y[u] > cb ? y[u] : cb;
+        }
+      }
+      m = __uint_as_float(tb) * inv_step_of_mag(cb) >= tau ? 1 : 0;
+    }
+    merge[q][t] = m;
+  }
+  __syncthreads();
+  if (!live) return;
+  if (bx == 0 && t < 128) {
+    const int64_t row = (int64_t)by * 128 + t;
+    if (row < d_out && merge[q][t])
+      for (int k = 0; k < r; ++k) B[row * (IDX ? rs : r) + (IDX ? kidx[k] : k)] = 0.0f;
+  }
+  const int cg = t & 31, rg = t >> 5;
+  const int64_t c = (int64_t)bx * 128 + cg * 4;             // 4 backbone columns
+  const int64_t r0 = (int64_t)by * 128 + rg * 16;           // 16 backbone rows
+  if (c >= d_in || r0 >= d_out) return;
+  uint32_t d[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int64_t at = (r0 + i) * d_in + c;
+    const bool mg = merge[q][rg * 16 + i] != 0;
+    d[i] = *reinterpret_cast<const uint32_t*>((mg ? staged : wq) + at);
+    if (mg) *reinterpret_cast<uint32_t*>(wq + at) = d[i];
+  }
+  uint32_t o[4][4];
+  transpose_16x4(d, o);
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+    *reinterpret_cast<uint4*>(wt + (c + k) * d_out + r0) = make_uint4(o[k][0], o[k][1], o[k][2], o[k][3]);
+}
+
 // one selected row per wave: copy the staged codes, zero the B row
 // zeroes B[row][kidx[k]] for k < r (IDX; B rows hold rs values), else B[row][0..r)
 template <bool IDX>
@@ -563,7 +641,7 @@ hipError_t launch_proxy_update_ranks(uint8_t* wq, const float* s_w, const float*
                                      int64_t d_in, int64_t d_out, int64_t r, int64_t rs,
                                      const int32_t* kidx, float tau, int64_t k_max,
                                      int32_t* sel_idx, int32_t* n_sel, float* rho, void* ws,
-                                     hipStream_t s) {
+                                     hipStream_t s, uint8_t* wt) {
   const ProxyWs L = proxy_layout(d_in, d_out);
   uint8_t* base = reinterpret_cast<uint8_t*>(ws);
   uint32_t* tmax = reinterpret_cast<uint32_t*>(base + L.off_tmax);
@@ -578,6 +656,20 @@ hipError_t launch_proxy_update_ranks(uint8_t* wq, const float* s_w, const float*
     else
       proxy_score<false><<<grid, kThreads, 0, s>>>(wq, s_w, A, B, (int)d_in, (int)d_out, (int)r,
                                                    (int)rs, nullptr, tmax, cmax, staged);
+  }
+  if (wt != nullptr && k_max == 0 && d_out > 0 && d_in > 0) {
+    const int tiles_x = (int)((d_in + 127) / 128);
+    const int n_tiles = tiles_x * (int)((d_out + 127) / 128);
+    const unsigned g = 1 + (unsigned)((n_tiles + 3) / 4);
+    if (kidx)
+      proxy_select_apply_t<true><<<g, kSelThreads, 0, s>>>(
+          tmax, cmax, L.ncb, rr, (int)d_out, tau, sel_idx, n_sel, wq, staged, B, (int)d_in, (int)r,
+          (int)rs, kidx, wt, n_tiles, tiles_x);
+    else
+      proxy_select_apply_t<false><<<g, kSelThreads, 0, s>>>(
+          tmax, cmax, L.ncb, rr, (int)d_out, tau, sel_idx, n_sel, wq, staged, B, (int)d_in, (int)r,
+          (int)rs, nullptr, wt, n_tiles, tiles_x);
+    return hipGetLastError();
   }
   if (k_max == 0 && d_out > 0) {
     const unsigned g = 1 + (unsigned)((d_out + kSelThreads / 64 - 1) / (kSelThreads / 64));
@@ -602,6 +694,12 @@ hipError_t launch_proxy_update_ranks(uint8_t* wq, const float* s_w, const float*
     else
       proxy_apply<false><<<g, kThreads, 0, s>>>(wq, staged, B, (int)d_in, (int)r, (int)rs,
                                                 nullptr, sel_idx, n_sel);
+  }
+  if (wt != nullptr && d_out > 0 && d_in > 0) {
+    // the capped selection: the transpose after the merge, in a launch of its own
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return launch_transpose_u8(wq, d_out, d_in, wt, s);
   }
   return hipGetLastError();
 }

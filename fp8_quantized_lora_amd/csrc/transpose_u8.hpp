@@ -6,6 +6,23 @@
 
 namespace falq {
 
+// A 16 x 4 byte block (d[i] = 4 bytes of row i) as 4 x 16: o[k][g] holds
+// bytes k of rows 4g .. 4g + 3, so that o[k][0..3] is column k's 16 bytes.
+// Byte permutes only.
+__device__ __forceinline__ void transpose_16x4(const uint32_t (&d)[16], uint32_t (&o)[4][4]) {
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {                             // rows 4g .. 4g+3
+    const uint32_t t01a = __builtin_amdgcn_perm(d[4 * g + 1], d[4 * g], 0x05010400u);
+    const uint32_t t01b = __builtin_amdgcn_perm(d[4 * g + 1], d[4 * g], 0x07030602u);
+    const uint32_t t23a = __builtin_amdgcn_perm(d[4 * g + 3], d[4 * g + 2], 0x05010400u);
+    const uint32_t t23b = __builtin_amdgcn_perm(d[4 * g + 3], d[4 * g + 2], 0x07030602u);
+    o[0][g] = __builtin_amdgcn_perm(t23a, t01a, 0x05040100u);
+    o[1][g] = __builtin_amdgcn_perm(t23a, t01a, 0x07060302u);
+    o[2][g] = __builtin_amdgcn_perm(t23b, t01b, 0x05040100u);
+    o[3][g] = __builtin_amdgcn_perm(t23b, t01b, 0x07060302u);
+  }
+}
+
 // out[cols x rows] = in[rows x cols]^T, the 128 x 128 tile (bx, by) of a
 // matrix whose sizes are multiples of 16; 256 threads (tid 0 .. 255, by
 // default the workgroup's own).  Each thread loads 16 rows x 4 bytes (a wave
@@ -24,17 +41,7 @@ __device__ __forceinline__ void transpose_u8_tile(const uint8_t* __restrict__ in
 #pragma unroll
   for (int i = 0; i < 16; ++i) d[i] = *reinterpret_cast<const uint32_t*>(in + (r + i) * cols + c);
   uint32_t o[4][4];                                         // [column][4 rows]
-#pragma unroll
-  for (int g = 0; g < 4; ++g) {                             // rows 4g .. 4g+3
-    const uint32_t t01a = __builtin_amdgcn_perm(d[4 * g + 1], d[4 * g], 0x05010400u);
-    const uint32_t t01b = __builtin_amdgcn_perm(d[4 * g + 1], d[4 * g], 0x07030602u);
-    const uint32_t t23a = __builtin_amdgcn_perm(d[4 * g + 3], d[4 * g + 2], 0x05010400u);
-    const uint32_t t23b = __builtin_amdgcn_perm(d[4 * g + 3], d[4 * g + 2], 0x07030602u);
-    o[0][g] = __builtin_amdgcn_perm(t23a, t01a, 0x05040100u);
-    o[1][g] = __builtin_amdgcn_perm(t23a, t01a, 0x07060302u);
-    o[2][g] = __builtin_amdgcn_perm(t23b, t01b, 0x05040100u);
-    o[3][g] = __builtin_amdgcn_perm(t23b, t01b, 0x07060302u);
-  }
+  transpose_16x4(d, o);
 #pragma unroll
   for (int k = 0; k < 4; ++k)
     *reinterpret_cast<uint4*>(out + (c + k) * rows + r) = make_uint4(o[k][0], o[k][1], o[k][2], o[k][3]);

@@ -15,7 +15,12 @@ melded_linear_bwd_xa, which forms G^ B inside the dX product: the skinny
 row-wise pass of melded_linear_bwd is not needed.  With SGD on that route, A's
 pieces (the form in which the forward product takes A) are kept in a buffer:
 formed at init, then left by adapter_step_pieces each time SGD moves A, and
-the forward is melded_linear_fwd_xa_pieces.
+the forward is melded_linear_fwd_xa_pieces.  When merges are periodic
+(merge_every >= 2) the backbone's transpose W~^T, which the dX product reads,
+is kept on that route too: formed at init by fp8_transpose, then left by
+rowwise_proxy_update_t each time the proxy update rewrites W~ (the backbone
+changes nowhere else in the step), and the backward is
+melded_linear_bwd_xa_t, which does not transpose W~ itself.
 
 With fp8_a=True (the pages' training setup: A frozen and held in FP8), A is
 quantized once to A~ at init, the forward is melded_linear_fwd_frozen_a (Y and
@@ -34,6 +39,7 @@ import torch
 
 from . import (fp8_quantize, fp8_quantize_workspace_bytes, fp8_dequantize, melded_linear_fwd,
                melded_linear_xa_fused, melded_linear_fwd_xa, melded_linear_bwd_xa,
+               melded_linear_bwd_xa_t, rowwise_proxy_update_t, fp8_transpose,
                melded_linear_fwd_xa_workspace_bytes, melded_linear_bwd_xa_workspace_bytes,
                melded_linear_bwd, melded_linear_bwd_workspace_bytes, melded_linear_fwd_frozen_a,
                melded_linear_fwd_frozen_a_workspace_bytes, melded_linear_bwd_frozen_a,
@@ -48,12 +54,14 @@ class MeldedLinear:
     def __init__(self, d_out: int, d_in: int, rank: int, tokens: int, device="cuda",
                  x_dtype=torch.float32, train_a: bool = True, optimizer: str = "sgd",
                  adamw: Optional[dict] = None, fp8_a: bool = False, g_fmt: str = "e4m3",
-                 topk_rank: int = 0):
+                 topk_rank: int = 0, merge_every: int = 1):
         """optimizer "sgd" (adapter_step) or "adamw" (adapter_step_adamw, with
         hyper-parameters `adamw`: beta1, beta2, eps, weight_decay); fp8_a
         freezes A in FP8 (implies train_a=False); g_fmt is the FP8 format of the
         upstream gradient dY ("e4m3" or "e5m2"); topk_rank > 0 merges only the
-        top-k rank components of the proxy (rowwise_proxy_update_topk_rank)."""
+        top-k rank components of the proxy (rowwise_proxy_update_topk_rank);
+        merge_every: how often the caller will merge (update(merge=...)), which
+        decides whether W~^T is kept (worth it from every second step on)."""
         if optimizer not in ("sgd", "adamw"):
             raise ValueError(f"optimizer must be 'sgd' or 'adamw', not {optimizer!r}")
         if fp8_a:
@@ -121,6 +129,15 @@ class MeldedLinear:
         else:
             bw = melded_linear_bwd_workspace_bytes(tokens, d_in, d_out, rank)
         self.ws_bwd = torch.empty(max(1, bw), dtype=u8, device=dev)
+        # W~^T for the dX product, left by the proxy update that rewrites W~
+        # (not with the top-k rank proxy, whose merge leaves no transpose).
+        # 4096^2: the backward's preparation without the transpose takes 4.7
+        # instead of 9.8 us, the merge that writes W~^T 20.5 instead of 10.3,
+        # so W~^T is kept only when merges are at most every second step
+        self.keep_wt = (self.use_xa and not topk_rank and d_out % 16 == 0
+                        and merge_every >= 2)
+        if self.keep_wt:
+            self.wqT = torch.empty((d_in, d_out), dtype=u8, device=dev)
         if topk_rank:
             self.comp_idx = torch.empty(topk_rank, dtype=i32, device=dev)
             px = rowwise_proxy_update_topk_rank_workspace_bytes(d_in, d_out, rank, topk_rank)
@@ -132,6 +149,7 @@ class MeldedLinear:
         """W~ = E4M3(W * s_w), s_w = 448 / max|W| (the initial quantization
         error is the implicit adapter); A and B copied in."""
         fp8_quantize(W, self.wq, self.s_w, ws=self.ws_q, stream=stream)
+        self.refresh_transpose(stream)
         self.B.copy_(B)
         if self.fp8_a:                    # A~ = E4M3(A * s_a); the proxy's A is DQ(A~)
             self.A.copy_(A)
@@ -140,6 +158,12 @@ class MeldedLinear:
         else:
             self.A.copy_(A)
         self.refresh_pieces(stream)
+
+    def refresh_transpose(self, stream=None):
+        """Form W~^T from W~ (needed only after W~ was changed other than by
+        merge)."""
+        if self.keep_wt:
+            fp8_transpose(self.wq, self.wqT, stream=stream)
 
     def refresh_pieces(self, stream=None):
         """Form A's pieces from A (needed only after A was changed other than by
@@ -178,6 +202,10 @@ class MeldedLinear:
         if self.fp8_a:
             melded_linear_bwd_frozen_a(self.gq, self.s_g, self.wq, self.s_w, self.u, self.dx,
                                        self.dB, ws=self.ws_bwd, stream=stream, g_fmt=self.g_fmt)
+        elif self.keep_wt:
+            melded_linear_bwd_xa_t(self.gq, self.s_g, self.xq, self.s_x, self.wqT, self.s_w,
+                                   self.A, self.B, self.xa, self.dx, self.dA, self.dB,
+                                   ws=self.ws_bwd, stream=stream, g_fmt=self.g_fmt)
         elif self.use_xa:
             melded_linear_bwd_xa(self.gq, self.s_g, self.xq, self.s_x, self.wq, self.s_w, self.A,
                                  self.B, self.xa, self.dx, self.dA, self.dB, ws=self.ws_bwd,
@@ -202,6 +230,10 @@ class MeldedLinear:
             rowwise_proxy_update_topk_rank(self.wq, self.s_w, self.A, self.B, self.topk_rank, tau,
                                            k_max, self.sel, self.n_sel, self.comp_idx,
                                            rho=self.rho, ws=self.ws_px, stream=stream)
+        elif self.keep_wt:
+            rowwise_proxy_update_t(self.wq, self.wqT, self.s_w, self.A, self.B, tau, k_max,
+                                   self.sel, self.n_sel, rho=self.rho, ws=self.ws_px,
+                                   stream=stream)
         else:
             rowwise_proxy_update(self.wq, self.s_w, self.A, self.B, tau, k_max, self.sel,
                                  self.n_sel, rho=self.rho, ws=self.ws_px, stream=stream)

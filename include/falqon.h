@@ -299,6 +299,33 @@ falq_status melded_linear_bwd_xa(const uint8_t *gq, int g_fmt, const float *s_g,
                                  size_t ws_bytes, falq_stream stream);
 
 /*
+ * melded_linear_bwd_xa_t — melded_linear_bwd_xa with the backbone handed in
+ * transposed: wqT [d_in x d_out] E4M3 codes (wqT[j][i] = wq[i][j]), as
+ * rowwise_proxy_update_t or fp8_transpose leave it.  The dX product reads it
+ * as its K-contiguous operand, so the call does not transpose W~ (16 MiB read
+ * and 16 MiB written per call at 4096 x 4096).  Outputs equal
+ * melded_linear_bwd_xa's with wq = wqT^T, bit for bit.  Workspace:
+ * melded_linear_bwd_xa_workspace_bytes.  FALQ_EINVAL for a null or
+ * misaligned wqT when dx is wanted.
+ */
+falq_status melded_linear_bwd_xa_t(const uint8_t *gq, int g_fmt, const float *s_g,
+                                   const uint8_t *xq, const float *s_x, const uint8_t *wqT,
+                                   const float *s_w, const float *A, const float *B,
+                                   const float *xa, int64_t T, int64_t d_in, int64_t d_out,
+                                   int64_t r, float *dx, float *dA, float *dB, void *ws,
+                                   size_t ws_bytes, falq_stream stream);
+
+/*
+ * fp8_transpose — qT[j][i] = q[i][j] for a byte matrix q [rows x cols]
+ * (E4M3 codes; any bytes), rows and cols multiples of 16; q and qT device,
+ * 16-byte aligned, not the same buffer.  Forms the backbone's transpose once
+ * before the first melded_linear_bwd_xa_t.  FALQ_EINVAL for other sizes or
+ * pointers.
+ */
+falq_status fp8_transpose(const uint8_t *q, int64_t rows, int64_t cols, uint8_t *qT,
+                          falq_stream stream);
+
+/*
  * A's pieces kept by the optimizer.  The forward above carries A as
  * block-scaled E4M3 pieces.  In the step, A changes only in the adapter
  * step: the row-wise proxy update ([summary] key design) merges rows of
@@ -463,6 +490,26 @@ falq_status rowwise_proxy_update(uint8_t *wq, const float *s_w, const float *A, 
                                  float tau, int64_t k_max,
                                  int32_t *sel_idx, int32_t *n_sel, float *rho,
                                  void *ws, size_t ws_bytes, falq_stream stream);
+
+/*
+ * rowwise_proxy_update_t — rowwise_proxy_update that also leaves the
+ * transpose of the updated backbone, wqT[j][i] = wq[i][j] [d_in x d_out],
+ * for the next backward (melded_linear_bwd_xa_t), which then need not
+ * transpose W~ itself.  The merge rewrites rows of W~ anyway ([summary] key
+ * design: only the selected rows change); without a row cap (k_max = 0) the
+ * transpose is written by the launch that merges, from 128 x 128 tiles whose
+ * rows take their merge decision from the same column-block maxima as the
+ * selection, so W~ is read once for both.  With a cap it follows the merge
+ * in a launch of its own.  Every output of rowwise_proxy_update is the same,
+ * bit for bit; wqT is overwritten whole.
+ *
+ *   wqT  [d_in x d_out] uint8, device (output), not overlapping wq
+ *   d_out a multiple of 16 here; other arguments as rowwise_proxy_update.
+ */
+falq_status rowwise_proxy_update_t(uint8_t *wq, uint8_t *wqT, const float *s_w, const float *A,
+                                   float *B, int64_t d_in, int64_t d_out, int64_t r, float tau,
+                                   int64_t k_max, int32_t *sel_idx, int32_t *n_sel, float *rho,
+                                   void *ws, size_t ws_bytes, falq_stream stream);
 
 /*
  * rowwise_proxy_update_topk_rank — the row-wise proxy update restricted to

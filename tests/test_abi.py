@@ -214,6 +214,38 @@ def test_quantize_wait_ticks_round_trip():
         fq.fp8_quantize_wait_ticks(-1)
 
 
+def test_transpose_calls_reject_bad_arguments():
+    """fp8_transpose, rowwise_proxy_update_t and melded_linear_bwd_xa_t
+    validate before any HIP call (no GPU here: only error paths and the
+    zero-size no-ops run)."""
+    lib = fq.load()
+    P = ctypes.c_void_p(1 << 20)                    # never dereferenced
+    Q = ctypes.c_void_p(1 << 21)
+    assert lib.fp8_transpose(P, 24, 32, Q, None) == EINVAL          # rows not a multiple of 16
+    assert lib.fp8_transpose(P, 32, 8, Q, None) == EINVAL
+    assert lib.fp8_transpose(P, 32, 32, P, None) == EINVAL          # in place
+    assert lib.fp8_transpose(None, 32, 32, Q, None) == EINVAL
+    assert lib.fp8_transpose(P, 32, 32, ctypes.c_void_p((1 << 21) + 4), None) == EINVAL
+    assert lib.fp8_transpose(None, 0, 32, None, None) == 0          # empty: nothing to do
+    n = ctypes.c_void_p(1 << 22)
+    ws = ctypes.c_void_p(1 << 23)
+    big = 1 << 30
+    # d_out must be a multiple of 16 for the transpose (the plain update allows any d_out)
+    assert lib.rowwise_proxy_update_t(P, Q, n, P, P, 32, 24, 4, 0.5, 0, P, n, None, ws, big,
+                                      None) == EINVAL
+    assert lib.rowwise_proxy_update_t(P, P, n, P, P, 32, 32, 4, 0.5, 0, P, n, None, ws, big,
+                                      None) == EINVAL               # wqT == wq
+    assert lib.rowwise_proxy_update_t(P, None, n, P, P, 32, 32, 4, 0.5, 0, P, n, None, ws, big,
+                                      None) == EINVAL
+    assert lib.rowwise_proxy_update_t(P, Q, n, P, P, 32, 32, 4, 0.5, -1, P, n, None, ws, big,
+                                      None) == EINVAL               # k_max
+    # the dX product needs the transpose when dx is wanted
+    f = lib.melded_linear_bwd_xa_t
+    assert f(P, 0, n, P, n, None, n, P, P, P, 64, 64, 64, 4, P, P, P, ws, big, None) == EINVAL
+    assert f(P, 7, n, P, n, Q, n, P, P, P, 64, 64, 64, 4, P, P, P, ws, big, None) == EINVAL
+    assert f(P, 0, n, P, n, Q, n, P, P, P, 64, 60, 64, 4, P, P, P, ws, big, None) == EINVAL
+
+
 def test_adapter_pieces_calls_reject_bad_arguments():
     """The calls around A's pieces validate before any HIP call."""
     lib = fq.load()
