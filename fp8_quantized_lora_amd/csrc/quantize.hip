@@ -4,9 +4,10 @@
 // factor s_X of the FALQON rebuttal, thread 2 reply W2), so every cast
 // depends on one global maximum.
 //
-// One launch where x fits in the registers of the resident workgroups (up
-// to 64 MiB): qz_one.  Every workgroup loads its 64 KB of x once and keeps
-// it in registers, reduces max |x| over its finite elements and counts its
+// One launch where x fits the resident workgroups (up to 100 MiB): qz_one.
+// Every workgroup loads its 64 KB of x once and keeps it in registers (for
+// x above 64 MiB, 36 KB more in LDS by direct loads), reduces max |x| over
+// its finite elements and counts its
 // non-finite ones, and publishes both as 64-bit words tagged with the call's
 // epoch (high half) in a small library-owned device array.  Workgroup 0
 // gathers the words of all workgroups, folds them and publishes the result
@@ -267,7 +268,11 @@ __global__ __launch_bounds__(kThreads) void qz_cast(const void* __restrict__ x, 
 
 // ---- one launch (qz_one) ----------------------------------------------------
 constexpr int kOneR = 16;                                 // 16-byte vectors of x per lane
-constexpr int64_t kOnePer = (int64_t)kOneR * kThreads;    // vectors per workgroup (64 KB)
+// ... plus kOneL more per lane staged in LDS for an x of 64 .. 100 MiB
+// (36 KB per workgroup: four workgroups still fit a CU's 160 KB)
+constexpr int kOneL = 9;
+template <int L>
+constexpr int64_t one_per() { return (int64_t)(kOneR + L) * kThreads; }   // vectors per workgroup
 constexpr int kOneMaxWG = 1024;
 constexpr int kOneSlots = kOneMaxWG / kThreads;           // words gathered per lane of workgroup 0
 // exchange words: (max, non-finite count) of workgroup i at 2 i, 2 i + 1;
@@ -284,15 +289,21 @@ __device__ __forceinline__ uint64_t get_word(uint64_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// a direct global -> LDS load of 16 bytes per lane with the streaming hint
+// (lane l's bytes land at lds_addr + 16 l; lds_addr wave-uniform)
+__device__ __forceinline__ void stream16_to_lds(const void* g, uint32_t lds_addr) {
+  asm volatile("global_load_lds_dwordx4 %0, off nt" ::"v"(g), "{m0}"(lds_addr) : "memory");
+}
+
 // max |x| and the non-finite count of workgroup b's range (and the scalar
 // tail for b = 0), by one lane: the fallback for a range whose words have
 // not arrived
-template <int DT>
+template <int DT, int L>
 __device__ void range_partial(const void* __restrict__ x, int64_t n, int b, uint32_t& m,
                               int& bad) {
   using V = Vec<DT>;
   const int64_t nvec = n / V::N;
-  const int64_t b0 = (int64_t)b * kOnePer, b1 = min(nvec, b0 + kOnePer);
+  const int64_t b0 = (int64_t)b * one_per<L>(), b1 = min(nvec, b0 + one_per<L>());
   // one vector at a time: this runs beside the caller's 64 registers of x
 #pragma unroll 1
   for (int64_t i = b0; i < b1; ++i) {
@@ -321,11 +332,12 @@ __device__ __forceinline__ void block_fold(uint32_t& m, int& bad) {
   }
 }
 
-// x [n] -> q, s with x held in registers: workgroup b owns vectors
-// [b kOnePer, (b + 1) kOnePer); gridDim.x <= kOneMaxWG workgroups, all of
-// which the host has checked fit on the device at once.  `wait` bounds each
-// wait for the exchange words, in ticks of the 100 MHz real-time counter.
-template <int DT, int F>
+// x [n] -> q, s with x held in registers (and, L > 0, L more vectors per
+// lane in LDS): workgroup b owns vectors [b P, (b + 1) P), P = one_per<L>();
+// gridDim.x <= kOneMaxWG workgroups, all of which the host has checked fit
+// on the device at once.  `wait` bounds each wait for the exchange words, in
+// ticks of the 100 MHz real-time counter.
+template <int DT, int F, int L>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void qz_one(const void* __restrict__ x, int64_t n,
                                                    uint64_t* __restrict__ words, uint32_t epoch,
                                                    uint64_t wait,
@@ -338,11 +350,19 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
   const int64_t nvec = n / V::N;
   const int tid = threadIdx.x, G = gridDim.x;
   const bool leader = blockIdx.x == 0;
-  const int64_t i0 = (int64_t)blockIdx.x * kOnePer + tid;
+  const int64_t i0 = (int64_t)blockIdx.x * one_per<L>() + tid;
+  __shared__ __attribute__((aligned(16))) uint4 xs[L > 0 ? L * kThreads : 1];
   uint4 raw[kOneR];
 #pragma unroll
   for (int u = 0; u < kOneR; ++u)
     if (i0 + u * kThreads < nvec) raw[u] = stream16(x, i0 + u * kThreads);
+  // the LDS part: lane l of wave w puts vector kOneR + u at xs[u kThreads + 64 w + l]
+  const int64_t j0 = i0 + (int64_t)kOneR * kThreads;
+#pragma unroll
+  for (int u = 0; u < L; ++u)
+    if (j0 + u * kThreads < nvec)
+      stream16_to_lds(reinterpret_cast<const uint4*>(x) + j0 + u * kThreads,
+                      __builtin_amdgcn_readfirstlane(lds_offset(&xs[u * kThreads + (tid & ~63)])));
   uint32_t m = 0;
   int bad = 0;
 #pragma unroll
@@ -353,6 +373,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
 #pragma unroll
       for (int e = 0; e < V::N; ++e) absorb(v[e], m, bad);
     }
+  if constexpr (L > 0) {
+    wait_vmem(0);                        // this wave's own LDS slots have landed
+#pragma unroll
+    for (int u = 0; u < L; ++u)
+      if (j0 + u * kThreads < nvec) {
+        float v[8];
+        V::unpack(xs[u * kThreads + tid], v);
+#pragma unroll
+        for (int e = 0; e < V::N; ++e) absorb(v[e], m, bad);
+      }
+  }
   if (leader)
     for (int64_t i = nvec * V::N + tid; i < n; i += kThreads) absorb(V::scalar(x, i), m, bad);
   // the floats are formed again from the held words for the cast: keeping
@@ -417,7 +448,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     }
 #pragma unroll 1
     for (int k = 0; k < kOneSlots; ++k)
-      if (((need & ~got) >> k) & 1) range_partial<DT>(x, n, tid + k * kThreads, m, bad);
+      if (((need & ~got) >> k) & 1) range_partial<DT, L>(x, n, tid + k * kThreads, m, bad);
     block_fold(m, bad);
     if (tid == 0) {
       s_amax = m;
@@ -442,6 +473,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) v
     if (i < nvec) {
       float v[8];
       V::unpack(raw[u], v);
+      store_codes<DT, F>(q, i, v, s);
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < L; ++u) {
+    const int64_t i = j0 + u * kThreads;
+    if (i < nvec) {
+      float v[8];
+      V::unpack(xs[u * kThreads + tid], v);
       store_codes<DT, F>(q, i, v, s);
     }
   }
@@ -507,27 +547,30 @@ std::mutex g_one_mu;
 struct OneRoute {
   bool init = false;
   void* words = nullptr;
-  int cap[2][3] = {};                       // resident workgroups of qz_one<DT, F>
+  int cap[2][3][2] = {};                    // resident workgroups of qz_one<DT, F, 0 / kOneL>
 };
 OneRoute g_one[kOneDevices];
 std::atomic<uint32_t> g_epoch{0};
 std::atomic<uint64_t> g_wait_ticks{50000};     // 500 us
 
-template <int DT, int F>
+template <int DT, int F, int L>
 int resident(int ncu) {
   int per_cu = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-          &per_cu, reinterpret_cast<const void*>(qz_one<DT, F>), kThreads, 0) != hipSuccess)
+          &per_cu, reinterpret_cast<const void*>(qz_one<DT, F, L>), kThreads, 0) != hipSuccess)
     return 0;
   return per_cu * ncu;
 }
 
-// the exchange words of the current device when x [nvec vectors] fits the
-// resident workgroups of qz_one<dtype, fmt> and the stream is not being
-// captured; nullptr otherwise
-uint64_t* one_route(int dtype, int fmt, int64_t nvec, hipStream_t s) {
-  const int64_t G = std::max<int64_t>(1, (nvec + kOnePer - 1) / kOnePer);
-  if (G > kOneMaxWG) return nullptr;
+template <int L>
+int64_t one_grid(int64_t nvec) { return std::max<int64_t>(1, (nvec + one_per<L>() - 1) / one_per<L>()); }
+
+// The one-launch route for x [nvec vectors] on the current device: the
+// exchange words, and in *lds whether the LDS-staged instance is needed
+// (x larger than the registers of the resident workgroups hold); nullptr
+// when x does not fit either instance or the stream is being captured
+uint64_t* one_route(int dtype, int fmt, int64_t nvec, hipStream_t s, bool* lds) {
+  if (one_grid<kOneL>(nvec) > kOneMaxWG) return nullptr;
   hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
   if (hipStreamIsCapturing(s, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone)
     return nullptr;
@@ -542,14 +585,19 @@ uint64_t* one_route(int dtype, int fmt, int64_t nvec, hipStream_t s) {
         hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
       return nullptr;                       // r.words stays null: the two-launch route
     r.words = p;
-    r.cap[0][0] = resident<0, 0>(ncu);
-    r.cap[0][1] = resident<0, 1>(ncu);
-    r.cap[0][2] = resident<0, 2>(ncu);
-    r.cap[1][0] = resident<1, 0>(ncu);
-    r.cap[1][1] = resident<1, 1>(ncu);
-    r.cap[1][2] = resident<1, 2>(ncu);
+#define FALQ_CAP(DT, F)                                  \
+  r.cap[DT][F][0] = resident<DT, F, 0>(ncu);             \
+  r.cap[DT][F][1] = resident<DT, F, kOneL>(ncu)
+    FALQ_CAP(0, 0); FALQ_CAP(0, 1); FALQ_CAP(0, 2);
+    FALQ_CAP(1, 0); FALQ_CAP(1, 1); FALQ_CAP(1, 2);
+#undef FALQ_CAP
   }
-  if (r.words == nullptr || G > r.cap[dtype != 0][fmt]) return nullptr;
+  if (r.words == nullptr) return nullptr;
+  const int* cap = r.cap[dtype != 0][fmt];
+  const int64_t g0 = one_grid<0>(nvec), g1 = one_grid<kOneL>(nvec);
+  if (g0 <= std::min(cap[0], kOneMaxWG)) *lds = false;
+  else if (g1 <= std::min(cap[1], kOneMaxWG)) *lds = true;
+  else return nullptr;
   return static_cast<uint64_t*>(r.words);
 }
 }  // namespace
@@ -559,14 +607,22 @@ uint64_t quantize_wait_ticks(uint64_t ticks) { return g_wait_ticks.exchange(tick
 hipError_t launch_quantize(const void* x, int dtype, int fmt, int64_t n, const float* scale_in,
                            uint8_t* q, float* scale, float* amax, int32_t* nonfinite,
                            void* ws, hipStream_t s) {
-  if (uint64_t* words = one_route(dtype, fmt, n / (dtype == 0 ? 4 : 8), s)) {
+  bool lds = false;
+  if (uint64_t* words = one_route(dtype, fmt, n / (dtype == 0 ? 4 : 8), s, &lds)) {
     uint32_t epoch = ++g_epoch;
     if (epoch == 0) epoch = ++g_epoch;      // 0 is the words' initial tag
-    const int G = (int)std::max<int64_t>(1, (n / (dtype == 0 ? 4 : 8) + kOnePer - 1) / kOnePer);
+    const int64_t nvec = n / (dtype == 0 ? 4 : 8);
+    const int G = (int)(lds ? one_grid<kOneL>(nvec) : one_grid<0>(nvec));
     const uint64_t wait = g_wait_ticks.load(std::memory_order_relaxed);
-#define FALQ_ONE(DT, F) \
-  qz_one<DT, F><<<G, kThreads, 0, s>>>(x, n, words, epoch, wait, scale_in, q, scale, amax, \
-                                       nonfinite)
+#define FALQ_ONE(DT, F)                                                                        \
+  do {                                                                                         \
+    if (lds)                                                                                   \
+      qz_one<DT, F, kOneL><<<G, kThreads, 0, s>>>(x, n, words, epoch, wait, scale_in, q, scale, \
+                                                  amax, nonfinite);                            \
+    else                                                                                       \
+      qz_one<DT, F, 0><<<G, kThreads, 0, s>>>(x, n, words, epoch, wait, scale_in, q, scale,     \
+                                              amax, nonfinite);                                \
+  } while (0)
     if (dtype == 0 && fmt == 0) FALQ_ONE(0, 0);
     else if (dtype == 0 && fmt == 1) FALQ_ONE(0, 1);
     else if (dtype == 0) FALQ_ONE(0, 2);

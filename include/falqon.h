@@ -112,9 +112,9 @@ const char *falq_version(void);
  *   ws         workspace of fp8_quantize_workspace_bytes(n) bytes
  * Errors: FALQ_EINVAL for n < 0, a NULL required pointer, misalignment, a
  * bad dtype or a short workspace.
- * Launches: an x of at most 64 MiB (as many 16-byte vectors as the
- * resident workgroups hold in registers) on a stream that is not being
- * captured takes one launch that reads x once and exchanges the partial
+ * Launches: an x of at most 100 MiB (as many 16-byte vectors as the
+ * resident workgroups hold in registers and LDS) on a stream that is not
+ * being captured takes one launch that reads x once and exchanges the partial
  * maxima through a small device array of the library's own (one per GPU,
  * each word tagged with the call, so nothing needs clearing); larger x, or a
  * capturing stream, takes two launches that read x twice.  Both give the

@@ -126,10 +126,10 @@ def _quantize_dev(fq, x, fmt="e4m3", stream=None):
 
 
 def test_quantize_across_the_one_launch_limit(gpu_lib):
-    """x of up to 64 MiB takes one launch that reads it once, anything larger
-    the two launches: calls alternating between the two routes and between
-    sizes (so the exchange words of the one-launch form hold an earlier
-    call's values) all match the oracle bit for bit."""
+    """x of up to 64 MiB takes the one launch with x in registers, a little
+    more the one launch with part of x in LDS: calls alternating between the
+    two and between sizes (so the exchange words of the one-launch form hold
+    an earlier call's values) all match the oracle bit for bit."""
     rng = np.random.default_rng(31)
     n_one = 4096 * 4096                 # 1024 workgroups: the largest one-launch fp32 x
     for n, seed in [(n_one, 1), (n_one + 4, 2), (3 * 4096 + 5, 3), (n_one, 4), (n_one - 4096, 5)]:
@@ -139,10 +139,36 @@ def test_quantize_across_the_one_launch_limit(gpu_lib):
         check(gpu_lib, x)
 
 
+def test_quantize_across_the_lds_staged_limit(gpu_lib):
+    """Above 64 MiB the one launch also stages 9 vectors per lane in LDS (up
+    to 1024 workgroups x 25 x 256 vectors = 100 MiB of fp32); one element
+    group more takes the two launches.  The 13B layer's 4096 x 5120 fp32
+    activations (80 MiB) fall in between.  All bit-exact; one pass with no
+    wait, so that the fallback reads ranges of the LDS-staged layout."""
+    rng = np.random.default_rng(35)
+    n_lds = 1024 * 25 * 256 * 4
+    for n in (4096 * 5120, n_lds, n_lds + 4):
+        announce(f"quantize f32 n={n} (LDS-staged limit)")
+        x = (rng.standard_normal(n) * 1.5).astype(np.float32)
+        x[[1, n // 3, n - 1]] = [np.inf, np.nan, -7e3]
+        check(gpu_lib, x)
+    announce("quantize bf16 n=4096*8192+8 (LDS-staged)")
+    xb = rng.standard_normal(4096 * 8192 + 8).astype(np.float32)
+    check(gpu_lib, wl.fp32_to_bf16_bits(xb), dtype="bf16")
+    prev = gpu_lib.fp8_quantize_wait_ticks(0)
+    try:
+        announce("quantize fallback f32 n=4096*4096+4 (LDS-staged)")
+        x = rng.standard_normal(4096 * 4096 + 4).astype(np.float32)
+        check(gpu_lib, x)
+    finally:
+        gpu_lib.fp8_quantize_wait_ticks(prev)
+
+
 def test_quantize_bf16_across_the_one_launch_limit(gpu_lib):
     """bf16 x holds 8 elements per 16-byte vector: 4096 x 8192 (64 MiB, 1024
-    workgroups) is the largest one-launch bf16 tensor, 8 more elements take
-    the two launches; both match the oracle bit for bit."""
+    workgroups) is the largest bf16 tensor held in registers alone, 8 more
+    elements take the LDS-staged instance; both match the oracle bit for
+    bit."""
     rng = np.random.default_rng(34)
     n_one = 4096 * 8192
     for n in (n_one, n_one + 8):
