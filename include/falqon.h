@@ -154,9 +154,11 @@ falq_status fp8_quantize_fmt(const void *x, int dtype, int64_t n, int fmt,
 /*
  * fp8_quantize_noalloc — fp8_quantize_fmt with no workspace argument, for
  * callers that cannot allocate device memory (code under HIP graph capture,
- * tight serving loops, harnesses that forbid hipMalloc).  The amax partials
- * live in a file-scope device array of FALQ_QUANTIZE_SCRATCH_BYTES that each
- * GPU the library runs on holds until the process ends; the call itself
+ * tight serving loops, harnesses that forbid hipMalloc).  The two-launch
+ * form's amax partials live in a file-scope device array of
+ * FALQ_QUANTIZE_SCRATCH_BYTES that each GPU the library runs on holds until
+ * the process ends (the one-launch form needs no workspace: its exchange
+ * words are the library's own, as for fp8_quantize); the call itself
  * allocates nothing (no hipMalloc, no hipFree).  The scratch need does not
  * grow with n (at most 2048 partials whatever the size), so every n >= 0 that
  * fp8_quantize accepts fits; FALQ_EUNSUPPORTED would report a build whose
