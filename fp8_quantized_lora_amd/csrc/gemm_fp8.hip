@@ -81,6 +81,43 @@ int whole_tiles(int nt, int nk) {
   return nt - rem;
 }
 
+// Tile columns for the fast kernel when an output's 256 x 256 tiles leave a
+// short last round: the first c tile columns fill whole rounds of the CUs,
+// and the remaining columns go to the generic kernel in 128 x 128 tiles,
+// which take ~0.7 of a large tile's time per round (4096 x 1024 x 5120:
+// 44.2 us for 256 small tiles against 58.8 us for 64 large ones) — worth it
+// when they fit in one round.  c >= min_cols keeps the tiles that carry a
+// second product in the fast kernel.  0: no split.
+int tail_split_cols(int64_t M, int64_t N, int min_cols) {
+  int dev = 0, ncu = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      ncu <= 0)
+    return 0;
+  const int64_t tM = (M + gemm::dma::BM - 1) / gemm::dma::BM;
+  const int64_t tN = (N + gemm::dma::BN - 1) / gemm::dma::BN;
+  const int64_t nt = tM * tN, rounds = nt / ncu;
+  if (rounds == 0 || nt % ncu == 0) return 0;
+  const int64_t c = rounds * ncu / tM;
+  if (c < std::max(min_cols, 1) || c >= tN) return 0;
+  const int64_t nt_small = ((M + 127) / 128) * ((N - c * gemm::dma::BN + 127) / 128);
+  return nt_small <= ncu ? (int)c : 0;
+}
+
+// the generic kernel in 128 x 128 tiles over output columns [n0, N)
+template <int FA>
+hipError_t launch_tail(const uint8_t* A, int64_t lda, const uint8_t* B, int64_t ldb, float* C,
+                       int64_t ldc, int64_t M, int64_t N, int64_t K, int64_t n0, const float* sa,
+                       const float* sb, hipStream_t s) {
+  using Cf = gemm::Cfg<128, 128, 128, 2, 2>;
+  const int64_t Nt = N - n0;
+  const int tilesM = (int)((M + Cf::BM - 1) / Cf::BM);
+  const int tilesN = (int)((Nt + Cf::BN - 1) / Cf::BN);
+  gemm::gemm_fp8_nt_kernel<Cf, FA><<<tilesM * tilesN, Cf::kThreads, 0, s>>>(
+      A, lda, B + n0 * ldb, ldb, C + n0, ldc, (int)M, (int)Nt, (int)K, sa, sb, tilesM, tilesN, 0);
+  return hipGetLastError();
+}
+
 // C (+)= scale * sum of the S partial planes P[s] (M x N, row stride ldp,
 // plane stride M * ldp), added in plane order; scale = 1 / (sa * sb), or 1
 // without scales
@@ -159,6 +196,19 @@ hipError_t launch_dma(const uint8_t* A, int64_t lda, const uint8_t* B, int64_t l
   }
   // an accumulating product keeps whole tiles (a split would add three terms)
   const int full = acc ? nt : whole_tiles(nt, (int)(K / gemm::dma::BK));
+  if constexpr (FA == 0 || FA == 1) {
+    // short K: the last round's columns as small tiles instead
+    const int c = acc || full < nt ? 0 : tail_split_cols(M, N, 0);
+    if (c > 0) {
+      gemm::dma::gemm_fp8_nt_dma<0, FA><<<tM * c, gemm::dma::kThreads, 0, s>>>(
+          A, lda, B, ldb, C, ldc, (int)M, c * gemm::dma::BN, (int)K, sa, sb, tM, c, tM * c,
+          gemm::dma::SecondB{}, 0);
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      return launch_tail<FA>(A, lda, B, ldb, C, ldc, M, N, K, (int64_t)c * gemm::dma::BN, sa, sb,
+                             s);
+    }
+  }
   if (full < nt) {
     zero_tiles_kernel<<<(nt - full) * 16, 256, 0, s>>>(C, ldc, (int)M, (int)N, tM, tN, full);
     const hipError_t e = hipGetLastError();
@@ -247,12 +297,18 @@ hipError_t launch_gemm_fp8_nt_second(const uint8_t* A, int64_t lda, const uint8_
   if (M == 0) return hipSuccess;
   if (!gemm_fp8_nt_fuses_second(N, K, R) || !gemm_shape_ok(M, N, K)) return hipErrorInvalidValue;
   const int tM = (int)((M + gemm::dma::BM - 1) / gemm::dma::BM);
-  const int tN = (int)((N + gemm::dma::BN - 1) / gemm::dma::BN);
+  // the tile columns past the ones that carry the second product may go to
+  // the small-tile kernel (tail_split_cols)
+  const int c = tail_split_cols(M, N, 4 * (int)((R + gemm::dma::UR - 1) / gemm::dma::UR));
+  const int tN = c > 0 ? c : (int)((N + gemm::dma::BN - 1) / gemm::dma::BN);
+  const int64_t Nm = c > 0 ? (int64_t)c * gemm::dma::BN : N;
   gemm::dma::gemm_fp8_nt_dma<1, 0><<<tM * tN, gemm::dma::kThreads, 0, s>>>(
-      A, lda, B, ldb, C, ldc, (int)M, (int)N, (int)K, sa, sb, tM, tN, tM * tN,
+      A, lda, B, ldb, C, ldc, (int)M, (int)Nm, (int)K, sa, sb, tM, tN, tM * tN,
       gemm::dma::SecondB{Bu, ldbu, 0, (int)R, nullptr, 0, sbu, Cu, ldcu, nullptr, nullptr, 0, 0},
       0);
-  return hipGetLastError();
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess || c == 0) return e;
+  return launch_tail<0>(A, lda, B, ldb, C, ldc, M, N, K, Nm, sa, sb, s);
 }
 
 hipError_t launch_gemm_fp8_nt_pieces(const uint8_t* A, int64_t lda, const uint8_t* B,
@@ -268,16 +324,23 @@ hipError_t launch_gemm_fp8_nt_pieces(const uint8_t* A, int64_t lda, const uint8_
   if (Po != nullptr && (po_rp < r16 || po_rp % 16 != 0 || po_kp < M || po_kp % 128 != 0))
     return hipErrorInvalidValue;
   const int tM = (int)((M + gemm::dma::BM - 1) / gemm::dma::BM);
-  const int tN = (int)((N + gemm::dma::BN - 1) / gemm::dma::BN);
+  // the tile columns past the ones that carry the pieces' product may go to
+  // the small-tile kernel (tail_split_cols)
+  const int c = tail_split_cols(M, N, (int)(4 * (r16 / gemm::dma::UR)));
+  const int tN = c > 0 ? c : (int)((N + gemm::dma::BN - 1) / gemm::dma::BN);
+  const int64_t Nm = c > 0 ? (int64_t)c * gemm::dma::BN : N;
   const gemm::dma::SecondB u{P,  K,  prp * K, (int)R, PE,    prp,   nullptr,
                              Cu, ldcu, Po,    Eo,     po_rp, po_kp};
   if (a_fmt == 0)
     gemm::dma::gemm_fp8_nt_dma<3, 0><<<tM * tN, gemm::dma::kThreads, 0, s>>>(
-        A, lda, B, ldb, C, ldc, (int)M, (int)N, (int)K, sa, sb, tM, tN, tM * tN, u, 0);
+        A, lda, B, ldb, C, ldc, (int)M, (int)Nm, (int)K, sa, sb, tM, tN, tM * tN, u, 0);
   else
     gemm::dma::gemm_fp8_nt_dma<3, 1><<<tM * tN, gemm::dma::kThreads, 0, s>>>(
-        A, lda, B, ldb, C, ldc, (int)M, (int)N, (int)K, sa, sb, tM, tN, tM * tN, u, 0);
-  return hipGetLastError();
+        A, lda, B, ldb, C, ldc, (int)M, (int)Nm, (int)K, sa, sb, tM, tN, tM * tN, u, 0);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess || c == 0) return e;
+  return a_fmt == 0 ? launch_tail<0>(A, lda, B, ldb, C, ldc, M, N, K, Nm, sa, sb, s)
+                    : launch_tail<1>(A, lda, B, ldb, C, ldc, M, N, K, Nm, sa, sb, s);
 }
 
 hipError_t launch_transpose_u8(const uint8_t* in, int64_t rows, int64_t cols, uint8_t* out,

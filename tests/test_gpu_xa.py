@@ -134,16 +134,20 @@ def test_xa_pair_degenerate(gpu_lib):
     assert not dA.any()            # B = 0 => G^ B = 0 => dA = 0 exactly
 
 
-def test_xa_pair_full_size_attention_projection(gpu_lib):
+@pytest.mark.parametrize("cfg", [2, 4])
+def test_xa_pair_full_size_attention_projection(gpu_lib, cfg):
     """The 7B attention projection (4096 x 4096 weight, 4096 tokens with
-    outlier channels, r = 64) through the fused pair: sampled rows of Y and
-    dX against the oracle row by row (each row depends on its own row of X~
-    or G~ only), X^ A^T and dA, dB complete."""
-    spec = wl.WORKLOADS[2].linears[0]
+    outlier channels, r = 64) and the 13B q projection (5120 x 5120: 320
+    output tiles, so the last four tile columns of the forward and dX
+    products run as 128 x 128 tiles in a launch of their own) through the
+    fused pair: sampled rows of Y and dX against the oracle row by row (each
+    row depends on its own row of X~ or G~ only; every column is checked),
+    X^ A^T and dA, dB complete."""
+    spec = wl.WORKLOADS[cfg].linears[0]
     T, d_in, d_out, r = spec.tokens, spec.d_in, spec.d_out, spec.rank
     announce(f"fwd_xa/bwd_xa full size T={T} d_in={d_in} d_out={d_out} r={r}")
     assert gpu_lib.melded_linear_xa_fused(T, d_in, d_out, r)
-    d = wl.make_linear(2, 0, spec, step=0)
+    d = wl.make_linear(cfg, 0, spec, step=0)
     wq, s_w, _, _ = oracle.fp8_quantize(d["W"])
     xq, s_x, _, _ = oracle.fp8_quantize(d["X"])
     gq, s_g, _, _ = oracle.fp8_quantize(d["dY"])
