@@ -83,10 +83,10 @@ int whole_tiles(int nt, int nk) {
 
 // Tile columns for the fast kernel when an output's 256 x 256 tiles leave a
 // short last round: the first c tile columns fill whole rounds of the CUs,
-// and the remaining columns go to the generic kernel in 128 x 128 tiles,
-// which take ~0.7 of a large tile's time per round (4096 x 1024 x 5120:
-// 44.2 us for 256 small tiles against 58.8 us for 64 large ones) — worth it
-// when they fit in one round.  c >= min_cols keeps the tiles that carry a
+// and the remaining columns go to the generic kernel in 128 x 128 tiles
+// (16 waves of 32 x 32, 256-byte K steps), which take about half of a large
+// tile's time per round (4096 x 1024 x 5120: 33.8 us for 256 small tiles
+// against 58.8 us for 64 large ones) — worth it when they fit in one round.  c >= min_cols keeps the tiles that carry a
 // second product in the fast kernel.  0: no split.
 int tail_split_cols(int64_t M, int64_t N, int min_cols) {
   int dev = 0, ncu = 0;
@@ -104,12 +104,15 @@ int tail_split_cols(int64_t M, int64_t N, int min_cols) {
   return nt_small <= ncu ? (int)c : 0;
 }
 
-// the generic kernel in 128 x 128 tiles over output columns [n0, N)
+// the generic kernel in 128 x 128 tiles over output columns [n0, N) (lab,
+// 4096 x 1024 x 5120: 4 waves and 128-byte K steps 44.7 us, 8 waves 41.4,
+// 16 waves 39.0, 8 waves and 256-byte steps 36.3, 16 waves and 256-byte
+// steps 33.8)
 template <int FA>
 hipError_t launch_tail(const uint8_t* A, int64_t lda, const uint8_t* B, int64_t ldb, float* C,
                        int64_t ldc, int64_t M, int64_t N, int64_t K, int64_t n0, const float* sa,
                        const float* sb, hipStream_t s) {
-  using Cf = gemm::Cfg<128, 128, 128, 2, 2>;
+  using Cf = gemm::Cfg<128, 128, 256, 4, 4>;
   const int64_t Nt = N - n0;
   const int tilesM = (int)((M + Cf::BM - 1) / Cf::BM);
   const int tilesN = (int)((Nt + Cf::BN - 1) / Cf::BN);
