@@ -45,7 +45,7 @@ def test_dequantize_bit_exact(gpu_lib):
 @pytest.mark.parametrize("T,d_in,d_out,r", [(256, 512, 512, 16), (777, 48, 80, 5),
                                             (300, 128, 64, 70), (300, 256, 1024, 13),
                                             (512, 384, 2048, 32), (200, 128, 1040, 16),
-                                            (4096, 4096, 4096, 64)])
+                                            (4096, 4096, 4096, 64), (4096, 5120, 5120, 64)])
 def test_frozen_fwd_bwd(gpu_lib, T, d_in, d_out, r):
     announce(f"frozen-A fwd/bwd T {T} d_in {d_in} d_out {d_out} r {r}")
     q = problem(T + d_in + r, T, d_in, d_out, r)
@@ -79,6 +79,24 @@ def test_frozen_fwd_bwd(gpu_lib, T, d_in, d_out, r):
                 "dB": rel_l2(host(dB), rdB)}
     print(" ".join(f"{k} {v:.2e}" for k, v in errs.items()))
     assert max(errs.values()) <= TOL, errs
+
+
+def test_frozen_forward_y_is_the_plain_forward_13b(gpu_lib):
+    """4096 x 5120 x 5120 (320 output tiles: the last four tile columns run
+    as small tiles in a launch of their own): the frozen-A forward's Y is the
+    plain forward's Y bit for bit — the tiles that also form X~A~^T run the
+    same products in the same order."""
+    announce("frozen-A forward vs plain forward, 4096 x 5120 x 5120")
+    q = problem(77, 4096, 5120, 5120, 64)
+    xq, wq, aq = dev(q["x"]), dev(q["w"]), dev(q["a"])
+    s_x, s_w, s_a = (scalar(q[k]) for k in ("s_x", "s_w", "s_a"))
+    y = torch.full((4096, 5120), float("nan"), dtype=torch.float32, device="cuda")
+    y0 = torch.full((4096, 5120), float("nan"), dtype=torch.float32, device="cuda")
+    u = torch.full((4096, 64), float("nan"), dtype=torch.float32, device="cuda")
+    gpu_lib.melded_linear_fwd_frozen_a(xq, s_x, wq, s_w, aq, s_a, y, u)
+    gpu_lib.melded_linear_fwd(xq, s_x, wq, s_w, y0)
+    assert torch.equal(y.view(torch.int32), y0.view(torch.int32))
+    assert not torch.isnan(u).any()
 
 
 def test_frozen_edge_cases(gpu_lib):
