@@ -129,6 +129,10 @@ def parse():
                     help="with --workload rank-sweep: also time the separate-path FP8 LoRA "
                          "layer and the bf16 LoRA layer at every rank (fwd + bwd), and the FP8 "
                          "backbone alone")
+    ap.add_argument("--ranks", type=str, default="",
+                    help="with --workload rank-sweep: a comma-separated subset of the sweep's "
+                         "ranks (default all); without 64 the line's value is the first "
+                         "rank's point")
     ap.add_argument("--gemm-event-every", type=int, default=10,
                     help="bracket the forward GEMM with timing events on every N-th timed "
                          "step (1 = every step)")
@@ -567,6 +571,18 @@ def compare_paths(torch, fq, m, X, dY, args, stream, melded_ms):
             "melded_over_separate_speedup": round(res["separate_fp8"] / melded_ms, 3)}
 
 
+def sweep_ranks(spec: str, allowed):
+    """The ranks named by --ranks (a comma-separated subset of `allowed`, in
+    the sweep's order), or all of them."""
+    if not spec:
+        return tuple(allowed)
+    want = {int(t) for t in spec.split(",") if t.strip()}
+    bad = sorted(want - set(allowed))
+    if bad or not want:
+        raise SystemExit(f"--ranks: {bad or spec!r} not in the sweep's ranks {tuple(allowed)}")
+    return tuple(r for r in allowed if r in want)
+
+
 def rank_sweep(args, torch, fq, wl):
     """W 4096 x 4096, 8192 tokens, r in 8, 64, 512, 2048, 8192: per rank the
     forward + backward time (quantize X, forward, quantize dY, backward) and
@@ -578,7 +594,9 @@ def rank_sweep(args, torch, fq, wl):
     stream = torch.cuda.current_stream()
     points = []
     line = None
-    for r in wl.RANK_SWEEP:
+    ranks = sweep_ranks(args.ranks, wl.RANK_SWEEP)
+    line_rank = 64 if 64 in ranks else ranks[0]
+    for r in ranks:
         m, X, dY, d = _linear_state(torch, np, fq, wl, 5, 0, spec0, rank=r)
         spec = dataclasses.replace(spec0, rank=r)
         calls = _step_calls(fq, m, X, dY, spec, stream)
@@ -598,8 +616,8 @@ def rank_sweep(args, torch, fq, wl):
         if args.compare_paths:
             point.update(compare_paths(torch, fq, m, X, dY, args, stream, fb_ms))
         points.append(point)
-        if r == 64:
-            line = (ms, gemm_us, d, spec)
+        if r == line_rank:
+            line = (ms, gemm_us, d, spec, m.use_xa)
         del m, X, dY, d, calls
         torch.cuda.synchronize()
         torch.cuda.empty_cache()
@@ -608,22 +626,27 @@ def rank_sweep(args, torch, fq, wl):
         # less than the bf16 one
         tp = [q["rank"] for q in points if q["separate_fp8_adapter_ms"] < q["bf16_adapter_ms"]]
         turning = tp[0] if tp else None
-    ms, gemm_us, d64, spec64 = line
+    ms, gemm_us, d64, spec64, xa64 = line
     T = spec64.tokens
-    gemm_tf = 2 * T * spec64.d_in * spec64.d_out / (gemm_us * 1e-6) / 1e12
+    # the timed forward call: the backbone product, plus X^ A^T where the call
+    # forms it in the same tiles (counted once, at rank r)
+    gemm_flops = 2 * T * spec64.d_in * (spec64.d_out + (line_rank if xa64 else 0))
+    gemm_tf = gemm_flops / (gemm_us * 1e-6) / 1e12
     out = {
         "metric": METRIC,
-        "value": round(wl.step_flops(T, spec64.d_in, spec64.d_out, 64) / (ms * 1e-3) / 1e12, 2),
+        "value": round(wl.step_flops(T, spec64.d_in, spec64.d_out, line_rank) / (ms * 1e-3) / 1e12,
+                       2),
         "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "fp8e4m3", "data": "synthetic",
         "config": {"workload": "rank sweep: W 4096x4096 E4M3, 8192 tokens, A std 1/sqrt(r), "
                                "B std 1e-3, SGD lr 1e-3, proxy update every step; the "
-                               "line's value and ms_per_step are the r = 64 point",
+                               f"line's value and ms_per_step are the r = {line_rank} point",
                    "tokens": T, "d_in": spec64.d_in, "d_out": spec64.d_out,
-                   "ranks": list(wl.RANK_SWEEP), "parallelism": "single GPU"},
+                   "ranks": list(ranks), "parallelism": "single GPU"},
         "tokens_per_s": round(T / (ms * 1e-3), 1),
-        "roofline": {"kernel": f"melded_linear_fwd FP8 GEMM ({T} x 4096 x 4096), r = 64 point",
+        "roofline": {"kernel": f"forward call FP8 GEMM ({T} x 4096 x 4096"
+                               f"{', forming X^A^T' if xa64 else ''}), r = {line_rank} point",
                      "bound": "mfma", "achieved": round(gemm_tf, 1), "peak": FP8_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(gemm_tf / FP8_PEAK_TFLOPS, 4),
                      "traffic": None},

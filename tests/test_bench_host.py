@@ -31,7 +31,8 @@ def test_traffic_is_reported_only_for_the_measured_sources(monkeypatch):
 
 
 @pytest.mark.parametrize("argv", [["--workload", "mlp7b"], ["--workload", "rank-sweep"],
-                                  ["--fp4-gemm"], ["--merge-every", "4"], ["--topk-rank", "16"]])
+                                  ["--fp4-gemm"], ["--merge-every", "4"], ["--topk-rank", "16"],
+                                  ["--workload", "rank-sweep", "--ranks", "8192"]])
 def test_options_parse(monkeypatch, argv):
     monkeypatch.setattr(sys, "argv", ["bench.py"] + argv)
     a = bench.parse()
@@ -60,3 +61,13 @@ def test_timing_events_are_not_destroyed_by_finalizers():
     synchronize), never from a finalizer that could run after the runtime."""
     assert not hasattr(bench.TimingEvent, "__del__")
     assert callable(bench.TimingEvent.destroy_all)
+
+
+def test_rank_subset_of_the_sweep():
+    import workloads as wl
+    assert bench.sweep_ranks("", wl.RANK_SWEEP) == tuple(wl.RANK_SWEEP)
+    # the sweep's order, whatever the order given
+    assert bench.sweep_ranks("8192,512", wl.RANK_SWEEP) == (512, 8192)
+    for bad in ("7", "64,100", ","):
+        with pytest.raises(SystemExit):
+            bench.sweep_ranks(bad, wl.RANK_SWEEP)
