@@ -158,7 +158,7 @@ def main():
 
 def run(args):
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
+        print("bench.py measures one GPU: the library has no multi-GPU path "
               "(the per-GPU shard of the step is what one GPU runs); use --gpus 1",
               file=sys.stderr)
         sys.exit(2)

@@ -68,7 +68,7 @@ const char* falq_status_string(falq_status s) {
     case FALQ_OK: return "FALQ_OK";
     case FALQ_EINVAL: return "FALQ_EINVAL: invalid argument";
     case FALQ_EHIP: return "FALQ_EHIP: HIP launch or runtime error";
-    case FALQ_EUNSUPPORTED: return "FALQ_EUNSUPPORTED: not supported by this build";
+    case FALQ_EUNSUPPORTED: return "FALQ_EUNSUPPORTED: not supported by this library";
   }
   return "unknown falq_status";
 }

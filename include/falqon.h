@@ -70,7 +70,7 @@ typedef enum {
     FALQ_OK = 0,
     FALQ_EINVAL = 1,        /* bad argument: null pointer, size, alignment, workspace */
     FALQ_EHIP = 2,          /* a HIP launch or runtime call failed */
-    FALQ_EUNSUPPORTED = 3   /* valid request this build does not implement */
+    FALQ_EUNSUPPORTED = 3   /* valid request this library does not implement */
 } falq_status;
 
 typedef enum {
